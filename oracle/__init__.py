@@ -1,0 +1,12 @@
+"""fp64 CPU oracle for DropKV eviction scoring (test infrastructure only).
+
+Only the tests, the smoke check and the benchmark's CPU-baseline leg may
+import this package. The HIP library never uses it and must fail loudly when
+its own extension is missing rather than fall back here.
+"""
+from .dropkv_oracle import (  # noqa: F401
+    SINGULAR_REST_MASS, SingularRow, NonFiniteInput, bf16_bits_to_f64, as_f64,
+    window_positions, group_rows, row_attention, head_row_stats, perturbation_sq,
+    head_scores, maxpool1d_same, protect_window, evict_smallest, check_args,
+    dropkv_oracle,
+)

@@ -1,0 +1,54 @@
+"""Delete-and-recompute reference for DropKV scores (tiny inputs only).
+
+Independent of the oracle: for every window query and every visible token j
+it literally removes j, re-normalises the softmax over the remaining visible
+keys, recomputes the attention output and takes the squared norm of the
+change. This is the check the DropKV write-up reports for its own
+implementation (section 结果与独立对照: "actually delete each item and
+re-softmax"), and the definition the core formula's Delta_j is the closed
+form of (section 核心公式: "the change after removing a single item").
+
+Pure Python loops over rows and tokens; numpy only for small vectors.
+"""
+
+from __future__ import annotations
+
+import math
+
+import numpy as np
+
+
+def _softmax_output(logits, values, keep):
+    """Output of softmax attention restricted to the index list `keep`."""
+    top = max(logits[j] for j in keep)
+    weights = [math.exp(logits[j] - top) for j in keep]
+    total = math.fsum(weights)
+    out = np.zeros(values.shape[1])
+    for wgt, j in zip(weights, keep):
+        out += (wgt / total) * values[j]
+    return out
+
+
+def brute_force_scores(q, k, v, n, window, Hq, Hkv):
+    """s[h][j]: sum over window rows of h of ||a^(-j) - a||^2; S[g][j] = mean over the group.
+
+    q [Hq][w][d], k/v [Hkv][n][d] as float64. Row i of the window is at
+    position n - window + i and sees keys 0..n-window+i.
+    """
+    G = Hq // Hkv
+    d = q.shape[2]
+    s = np.zeros((Hq, n))
+    for h in range(Hq):
+        g = h // G
+        for i in range(window):
+            pos = n - window + i
+            visible = list(range(pos + 1))
+            logits = [float(np.dot(q[h, i], k[g, j])) / math.sqrt(d) for j in range(n)]
+            full = _softmax_output(logits, v[g], visible)
+            for j in visible:
+                rest = [t for t in visible if t != j]
+                reduced = _softmax_output(logits, v[g], rest)
+                delta = reduced - full
+                s[h, j] += float(np.dot(delta, delta))
+    S = s.reshape(Hkv, G, n).mean(axis=1)
+    return s, S

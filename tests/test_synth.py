@@ -1,0 +1,57 @@
+"""The seeded input generator: reproducible, bf16 rounding equal to torch's, planted structure."""
+
+import math
+
+import numpy as np
+import pytest
+
+from kv_cache_eviction_pass1_amd import synth
+
+
+def test_bf16_round_matches_torch():
+    torch = pytest.importorskip("torch")
+    rng = np.random.default_rng(0)
+    x = np.concatenate([
+        rng.standard_normal(100000).astype(np.float32) * 10.0,
+        np.array([0.0, -0.0, 1.0, -1.0, np.inf, -np.inf, 3.3895314e38, 1e-40, -1e-42], np.float32),
+        # exact halfway cases (ties to even)
+        (np.arange(1, 2000, dtype=np.uint32) << np.uint32(16) | np.uint32(0x8000)).view(np.float32),
+    ])
+    ours = synth.bf16_round_bits(x)
+    ref = torch.from_numpy(x).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    assert np.array_equal(ours, ref)
+    nan = synth.bf16_round_bits(np.array([np.nan], np.float32))
+    assert np.isnan(synth.bf16_bits_to_float32(nan))[0]
+
+
+def test_generator_is_reproducible_and_seeded():
+    cfg = synth.CONFIGS["llama_4k"]
+    a = synth.make_case(cfg, n=512)
+    b = synth.make_case(cfg, n=512)
+    assert np.array_equal(a.q, b.q) and np.array_equal(a.k, b.k) and np.array_equal(a.v, b.v)
+    c = synth.make_case(cfg, n=512, layer=1)
+    assert not np.array_equal(a.k, c.k)
+    assert a.q.dtype == np.uint16 and a.q.shape == (32, 32, 128) and a.k.shape == (8, 512, 128)
+
+
+def test_planted_sink_and_needles():
+    cfg = synth.CONFIGS["llama_4k"]
+    case = synth.make_gaussian_case(cfg.Hq, cfg.Hkv, cfg.d, 1024, cfg.window, dtype="f32",
+                                    sink=True, needles=16)
+    G, d = case.group, case.d
+    q = case.q
+    for g in range(case.Hkv):
+        mu = q[g * G:(g + 1) * G].reshape(-1, d).astype(np.float64).mean(0)
+        u = mu / np.linalg.norm(mu)
+        assert np.allclose(case.k[g, 0], 3.0 * math.sqrt(d) * u, rtol=1e-5)
+        pos = case.needle_pos[g]
+        assert len(set(pos.tolist())) == 16 and pos.min() >= 1 and pos.max() < 1024 - cfg.window
+        for p in pos:
+            assert np.allclose(case.k[g, p], 2.5 * math.sqrt(d) * u, rtol=1e-5)
+
+
+def test_budget_to_evict_count():
+    assert synth.CONFIGS["llama_4k"].n_evicts() == (3892,)
+    assert synth.CONFIGS["llama_32k"].n_evicts() == (31130, 26215)
+    assert synth.CONFIGS["llama_128k"].n_evicts() == (124519,)
+    assert synth.CONFIGS["tiny"].n_evicts() == (7,)
