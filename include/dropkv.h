@@ -1,0 +1,154 @@
+/*
+ * dropkv.h — DropKV eviction scoring on AMD Instinct MI355X (gfx950).
+ *
+ * One call scores one sequence (one batch element) of one layer: for every
+ * physical KV head it takes the queries of the last `window` positions and the
+ * full causal K/V, and returns per-token eviction scores and the indices of
+ * the tokens to evict.
+ *
+ * What is computed (DropKV, arXiv 2610.22130, as described by the write-up
+ * "DropKV：精确单项输出扰动评分组件", section 核心公式 (core formula) and the
+ * prose after its displayed equation; pipeline figure of section 背景与主要改动):
+ *   for query head h and window row i (sequence position P = n - window + i,
+ *   keys 0..P visible — causal tail alignment, section 代码映射与边界):
+ *     p = softmax(K q / sqrt(d)),   a = sum_j p_j v_j,
+ *     Delta_j = p_j / (1 - p_j) * (a - v_j)      (exact single-token removal),
+ *     s_j(h) = sum over window rows of ||Delta_j||^2;
+ *   S_g(j) = mean of s_j(h) over the query heads h of KV head g (GQA:
+ *            h belongs to g = h / (Hq / Hkv));
+ *   P_g = MaxPool1D(S_g) (odd kernel, stride 1, same padding, over [0, n));
+ *   P_g(j) = +inf for the last `window` positions (recent-window protection);
+ *   evict_g = the n_evict smallest P_g under the order (score, index),
+ *             returned in ascending index order.
+ *   A row whose largest probability rounds to 1 in binary32 (rest mass
+ *   R = sum_{j != argmax} exp(x_j - x_max) <= 2^-24) makes exact single-token
+ *   removal singular and is rejected (DROPKV_ERR_SINGULAR); no epsilon is used.
+ *
+ * Layouts (row-major, contiguous, device memory, one sequence):
+ *   q            [Hq][window][d]   bf16 (as uint16 bit patterns) or fp32
+ *   k, v         [Hkv][n][d]       same dtype as q
+ *   out_scores   [Hkv][n]          fp32: pooled scores, +inf on the window
+ *   out_evict_idx[Hkv][n_evict]    int64, ascending per head
+ * All pointers are device pointers owned by the caller; the library keeps
+ * none of them after the call returns. Batches are scored by one call per
+ * sequence (pointer offsets).
+ *
+ * Errors: every entry point validates its arguments on the host first; an
+ * invalid call launches nothing, leaves the outputs untouched and returns
+ * DROPKV_ERR_INVALID. DROPKV_ERR_SINGULAR / DROPKV_ERR_NONFINITE are found
+ * on the device; after them the outputs are unspecified and must not be used.
+ * DROPKV_ERR_DEVICE covers HIP runtime failures (no device, launch or memory
+ * errors). There is no CPU fallback. dropkv_last_error() describes the most
+ * recent failure of the calling thread.
+ *
+ * Threading: the plain entry points use one library-owned, grow-only
+ * workspace per device behind a mutex; calls from several threads are
+ * serialised. dropkv_score_ex takes caller-owned workspace instead and never
+ * synchronises.
+ */
+#ifndef DROPKV_H
+#define DROPKV_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  DROPKV_OK = 0,
+  DROPKV_ERR_INVALID = -1,   /* bad argument: nothing launched */
+  DROPKV_ERR_SINGULAR = -2,  /* a window row has a probability that rounds to 1 */
+  DROPKV_ERR_NONFINITE = -3, /* NaN/inf in the inputs or the scores */
+  DROPKV_ERR_DEVICE = -4     /* HIP runtime error */
+} dropkv_status;
+
+/* Element type of q, k, v. */
+enum { DROPKV_BF16 = 0, DROPKV_F32 = 1 };
+
+/* Bits of the device status word written by dropkv_score_ex. */
+enum { DROPKV_STATUS_SINGULAR = 1, DROPKV_STATUS_NONFINITE = 2 };
+
+/* Flags for dropkv_score_ex. */
+enum {
+  DROPKV_FLAG_GENERIC = 1 /* force the plain-VALU path even where the MFMA path applies */
+};
+
+/*
+ * Score one sequence, bf16 inputs (uint16 bit patterns). Argument limits:
+ * 1 <= window < n; Hq, Hkv >= 1 and Hq % Hkv == 0; 1 <= d <= 256;
+ * pool_kernel odd and >= 1; 0 <= n_evict <= n - window (out_evict_idx may be
+ * NULL when n_evict == 0). `stream` is a hipStream_t (NULL = default stream).
+ * Enqueues on `stream`, then synchronises that stream to read the status word.
+ */
+int dropkv_score(const void* q, const void* k, const void* v, int64_t n, int32_t window,
+                 int32_t Hq, int32_t Hkv, int32_t d, int32_t pool_kernel, int64_t n_evict,
+                 float* out_scores, int64_t* out_evict_idx, void* stream);
+
+/* Same as dropkv_score with fp32 q, k, v. */
+int dropkv_score_f32(const float* q, const float* k, const float* v, int64_t n, int32_t window,
+                     int32_t Hq, int32_t Hkv, int32_t d, int32_t pool_kernel, int64_t n_evict,
+                     float* out_scores, int64_t* out_evict_idx, void* stream);
+
+/* Bytes of device workspace dropkv_score_ex needs for this shape (0 on invalid shape). */
+size_t dropkv_workspace_bytes(int32_t dtype, int64_t n, int32_t window, int32_t Hq, int32_t Hkv,
+                              int32_t d);
+
+/*
+ * Fully asynchronous form. `workspace` (>= dropkv_workspace_bytes, 256-byte
+ * aligned, device memory owned by the caller) holds all scratch; `d_status`
+ * is a caller-owned device int32 that the call clears and then ORs
+ * DROPKV_STATUS_* bits into. Returns DROPKV_OK once enqueued (or
+ * DROPKV_ERR_INVALID / DROPKV_ERR_DEVICE); device-side errors are visible only
+ * in *d_status after the stream completes. Calls sharing a workspace must be
+ * ordered on one stream.
+ */
+int dropkv_score_ex(int32_t dtype, const void* q, const void* k, const void* v, int64_t n,
+                    int32_t window, int32_t Hq, int32_t Hkv, int32_t d, int32_t pool_kernel,
+                    int64_t n_evict, float* out_scores, int64_t* out_evict_idx, void* workspace,
+                    size_t workspace_bytes, int32_t* d_status, uint32_t flags, void* stream);
+
+/*
+ * Stage export: the GQA-mean scores S [Hkv][n] (fp32) before pooling and
+ * protection. Synchronous like dropkv_score (returns SINGULAR / NONFINITE).
+ */
+int dropkv_raw_scores(int32_t dtype, const void* q, const void* k, const void* v, int64_t n,
+                      int32_t window, int32_t Hq, int32_t Hkv, int32_t d, float* out_S,
+                      uint32_t flags, void* stream);
+
+/*
+ * Stage export: per window row (row index h*window + i) the softmax
+ * statistics after all of n is seen: out_m = largest logit x_max (natural
+ * units, x = q.k / sqrt(d)), out_rest = R = sum_{j != argmax} exp(x_j - x_max),
+ * out_argmax = lowest index attaining x_max (valid where R < 1; -1 where the
+ * path does not track it), and out_a [Hq*window][d] = the attention output a.
+ * Any output pointer may be NULL. Synchronous; returns SINGULAR if a row is.
+ */
+int dropkv_row_stats(int32_t dtype, const void* q, const void* k, const void* v, int64_t n,
+                     int32_t window, int32_t Hq, int32_t Hkv, int32_t d, float* out_m,
+                     float* out_rest, int32_t* out_argmax, float* out_a, uint32_t flags,
+                     void* stream);
+
+/*
+ * The pooling, protection and selection stage alone, on caller-given raw
+ * scores S [Hkv][n] (non-negative fp32): writes out_scores and out_evict_idx
+ * exactly as dropkv_score does. Synchronous; NONFINITE if S holds NaN/inf.
+ */
+int dropkv_select(const float* S, int64_t n, int32_t window, int32_t Hkv, int32_t pool_kernel,
+                  int64_t n_evict, float* out_scores, int64_t* out_evict_idx, void* stream);
+
+/* 1 if (dtype, d) takes the MFMA path by default, 0 if the plain-VALU path. */
+int dropkv_uses_mfma(int32_t dtype, int32_t d);
+
+/* Human-readable description of the calling thread's most recent error ("" if none). */
+const char* dropkv_last_error(void);
+
+/* Library version string. */
+const char* dropkv_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* DROPKV_H */

@@ -1,0 +1,220 @@
+"""ctypes binding of libdropkv (argument marshalling only).
+
+Every step of the scoring runs in the HIP library; this module only checks
+tensor shapes, allocates outputs with torch on the inputs' device and passes
+raw pointers and the current HIP stream. If the library is not built, or no
+GPU is present, calls raise: there is no CPU fallback.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Tuple
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libdropkv.so")
+
+OK, ERR_INVALID, ERR_SINGULAR, ERR_NONFINITE, ERR_DEVICE = 0, -1, -2, -3, -4
+BF16, F32 = 0, 1
+STATUS_SINGULAR, STATUS_NONFINITE = 1, 2
+FLAG_GENERIC = 1
+
+# name -> (restype, argtypes)
+_c = ctypes
+_p, _i32, _i64, _u32, _sz = _c.c_void_p, _c.c_int32, _c.c_int64, _c.c_uint32, _c.c_size_t
+SIGNATURES = {
+    "dropkv_score": (_i32, [_p, _p, _p, _i64, _i32, _i32, _i32, _i32, _i32, _i64, _p, _p, _p]),
+    "dropkv_score_f32": (_i32, [_p, _p, _p, _i64, _i32, _i32, _i32, _i32, _i32, _i64, _p, _p, _p]),
+    "dropkv_workspace_bytes": (_sz, [_i32, _i64, _i32, _i32, _i32, _i32]),
+    "dropkv_score_ex": (_i32, [_i32, _p, _p, _p, _i64, _i32, _i32, _i32, _i32, _i32, _i64, _p, _p,
+                               _p, _sz, _p, _u32, _p]),
+    "dropkv_raw_scores": (_i32, [_i32, _p, _p, _p, _i64, _i32, _i32, _i32, _i32, _p, _u32, _p]),
+    "dropkv_row_stats": (_i32, [_i32, _p, _p, _p, _i64, _i32, _i32, _i32, _i32, _p, _p, _p, _p,
+                                _u32, _p]),
+    "dropkv_select": (_i32, [_p, _i64, _i32, _i32, _i32, _i64, _p, _p, _p]),
+    "dropkv_uses_mfma": (_i32, [_i32, _i32]),
+    "dropkv_last_error": (_c.c_char_p, []),
+    "dropkv_version": (_c.c_char_p, []),
+}
+
+
+class DropKVError(RuntimeError):
+    def __init__(self, code: int, msg: str):
+        super().__init__(f"dropkv error {code}: {msg}")
+        self.code = code
+
+
+class DropKVInvalidError(DropKVError, ValueError):
+    pass
+
+
+class DropKVSingularError(DropKVError):
+    pass
+
+
+class DropKVNonFiniteError(DropKVError):
+    pass
+
+
+class DropKVNotBuiltError(RuntimeError):
+    pass
+
+
+_lib = None
+
+
+def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
+    """Load libdropkv.so (raises DropKVNotBuiltError if it is missing)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise DropKVNotBuiltError(f"{path} is missing: build the HIP library first "
+                                  "(python -m kv_cache_eviction_pass1_amd.build)")
+    lib = ctypes.CDLL(path)
+    for name, (res, args) in SIGNATURES.items():
+        fn = getattr(lib, name)
+        fn.restype, fn.argtypes = res, args
+    _lib = lib
+    return lib
+
+
+def _raise(code: int):
+    if code == OK:
+        return
+    msg = load_library().dropkv_last_error().decode(errors="replace")
+    cls = {ERR_INVALID: DropKVInvalidError, ERR_SINGULAR: DropKVSingularError,
+           ERR_NONFINITE: DropKVNonFiniteError}.get(code, DropKVError)
+    raise cls(code, msg)
+
+
+def _torch():
+    import torch
+    return torch
+
+
+def _stream_handle(stream) -> Optional[int]:
+    torch = _torch()
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return s.cuda_stream
+
+
+def _dtype_code(t) -> int:
+    torch = _torch()
+    if t.dtype == torch.bfloat16:
+        return BF16
+    if t.dtype == torch.float32:
+        return F32
+    raise DropKVInvalidError(ERR_INVALID, f"unsupported dtype {t.dtype}")
+
+
+def _shapes(q, k, v) -> Tuple[int, int, int, int, int]:
+    if q.dim() != 3 or k.dim() != 3 or v.dim() != 3:
+        raise DropKVInvalidError(ERR_INVALID, "q must be [Hq, window, d], k and v [Hkv, n, d]")
+    Hq, w, d = q.shape
+    Hkv, n, dk = k.shape
+    if tuple(v.shape) != (Hkv, n, dk) or dk != d:
+        raise DropKVInvalidError(ERR_INVALID, "q/k/v shapes disagree")
+    if not (q.dtype == k.dtype == v.dtype):
+        raise DropKVInvalidError(ERR_INVALID, "q, k, v must share one dtype")
+    for t in (q, k, v):
+        if not t.is_cuda or not t.is_contiguous():
+            raise DropKVInvalidError(ERR_INVALID, "q, k, v must be contiguous GPU tensors")
+    return Hq, Hkv, d, n, w
+
+
+def score(q, k, v, *, pool_kernel: int, n_evict: int, stream=None):
+    """DropKV scores and evict indices of one sequence.
+
+    q [Hq, window, d], k/v [Hkv, n, d] (bf16 or fp32, contiguous, on the GPU).
+    Returns (scores [Hkv, n] fp32 pooled with +inf on the window,
+    evict_idx [Hkv, n_evict] int64 ascending).
+    """
+    torch = _torch()
+    lib = load_library()
+    Hq, Hkv, d, n, w = _shapes(q, k, v)
+    scores = torch.empty((Hkv, n), dtype=torch.float32, device=q.device)
+    idx = torch.empty((Hkv, max(n_evict, 0)), dtype=torch.int64, device=q.device)
+    fn = lib.dropkv_score if _dtype_code(q) == BF16 else lib.dropkv_score_f32
+    rc = fn(q.data_ptr(), k.data_ptr(), v.data_ptr(), n, w, Hq, Hkv, d, pool_kernel, n_evict,
+            scores.data_ptr(), idx.data_ptr() if n_evict > 0 else None, _stream_handle(stream))
+    _raise(rc)
+    return scores, idx
+
+
+def workspace_bytes(dtype_code: int, n: int, window: int, Hq: int, Hkv: int, d: int) -> int:
+    return int(load_library().dropkv_workspace_bytes(dtype_code, n, window, Hq, Hkv, d))
+
+
+def score_ex(q, k, v, *, pool_kernel: int, n_evict: int, workspace, status, scores=None,
+             evict_idx=None, flags: int = 0, stream=None):
+    """Asynchronous scoring into caller-owned workspace/status/outputs (no synchronisation).
+
+    workspace: uint8 GPU tensor of >= workspace_bytes(...); status: int32 GPU
+    tensor of one element that receives the STATUS_* bits. Returns (scores, evict_idx).
+    """
+    torch = _torch()
+    lib = load_library()
+    Hq, Hkv, d, n, w = _shapes(q, k, v)
+    if scores is None:
+        scores = torch.empty((Hkv, n), dtype=torch.float32, device=q.device)
+    if evict_idx is None:
+        evict_idx = torch.empty((Hkv, max(n_evict, 0)), dtype=torch.int64, device=q.device)
+    rc = lib.dropkv_score_ex(_dtype_code(q), q.data_ptr(), k.data_ptr(), v.data_ptr(), n, w, Hq,
+                             Hkv, d, pool_kernel, n_evict, scores.data_ptr(),
+                             evict_idx.data_ptr() if n_evict > 0 else None, workspace.data_ptr(),
+                             workspace.numel() * workspace.element_size(), status.data_ptr(),
+                             flags, _stream_handle(stream))
+    _raise(rc)
+    return scores, evict_idx
+
+
+def raw_scores(q, k, v, *, flags: int = 0, stream=None):
+    """GQA-mean scores S [Hkv, n] before pooling and protection."""
+    torch = _torch()
+    lib = load_library()
+    Hq, Hkv, d, n, w = _shapes(q, k, v)
+    S = torch.empty((Hkv, n), dtype=torch.float32, device=q.device)
+    rc = lib.dropkv_raw_scores(_dtype_code(q), q.data_ptr(), k.data_ptr(), v.data_ptr(), n, w, Hq,
+                               Hkv, d, S.data_ptr(), flags, _stream_handle(stream))
+    _raise(rc)
+    return S
+
+
+def row_stats(q, k, v, *, flags: int = 0, stream=None):
+    """Per window row (h*window+i): (x_max, rest mass R, argmax or -1, output a [rows, d])."""
+    torch = _torch()
+    lib = load_library()
+    Hq, Hkv, d, n, w = _shapes(q, k, v)
+    rows = Hq * w
+    m = torch.empty(rows, dtype=torch.float32, device=q.device)
+    rest = torch.empty(rows, dtype=torch.float32, device=q.device)
+    arg = torch.empty(rows, dtype=torch.int32, device=q.device)
+    a = torch.empty((rows, d), dtype=torch.float32, device=q.device)
+    rc = lib.dropkv_row_stats(_dtype_code(q), q.data_ptr(), k.data_ptr(), v.data_ptr(), n, w, Hq,
+                              Hkv, d, m.data_ptr(), rest.data_ptr(), arg.data_ptr(), a.data_ptr(),
+                              flags, _stream_handle(stream))
+    _raise(rc)
+    return m, rest, arg, a
+
+
+def select(S, *, window: int, pool_kernel: int, n_evict: int, stream=None):
+    """Pool, protect and select on given raw scores S [Hkv, n] (fp32 GPU tensor)."""
+    torch = _torch()
+    lib = load_library()
+    Hkv, n = S.shape
+    scores = torch.empty((Hkv, n), dtype=torch.float32, device=S.device)
+    idx = torch.empty((Hkv, max(n_evict, 0)), dtype=torch.int64, device=S.device)
+    rc = lib.dropkv_select(S.data_ptr(), n, window, Hkv, pool_kernel, n_evict, scores.data_ptr(),
+                           idx.data_ptr() if n_evict > 0 else None, _stream_handle(stream))
+    _raise(rc)
+    return scores, idx
+
+
+def uses_mfma(dtype_code: int, d: int) -> bool:
+    return bool(load_library().dropkv_uses_mfma(dtype_code, d))
+
+
+def version() -> str:
+    return load_library().dropkv_version().decode()

@@ -1,0 +1,324 @@
+// C-ABI entry points of libdropkv: validation, workspace, dispatch, status.
+#include "../../include/dropkv.h"
+#include "dropkv_common.h"
+
+#include <cstdio>
+#include <cstring>
+#include <mutex>
+#include <string>
+#include <unordered_map>
+
+namespace dropkv {
+
+namespace {
+
+thread_local std::string g_last_error;
+
+int fail(int code, const std::string& msg) {
+  g_last_error = msg;
+  return code;
+}
+
+int fail_hip(hipError_t e, const char* what) {
+  return fail(DROPKV_ERR_DEVICE, std::string(what) + ": " + hipGetErrorString(e));
+}
+
+size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+// Library-owned grow-only workspace per device (plain entry points only).
+struct DeviceWs {
+  void* ptr = nullptr;
+  size_t bytes = 0;
+};
+std::mutex g_ws_mutex;
+std::unordered_map<int, DeviceWs> g_ws;
+
+const char* validate(int dtype, int64_t n, int32_t w, int32_t Hq, int32_t Hkv, int32_t d) {
+  if (dtype != DROPKV_BF16 && dtype != DROPKV_F32) return "dtype must be DROPKV_BF16 or DROPKV_F32";
+  if (n < 2) return "n must be >= 2";
+  if (w < 1 || (int64_t)w >= n) return "need 1 <= window < n";
+  if (Hq < 1 || Hkv < 1) return "need Hq >= 1 and Hkv >= 1";
+  if (Hq % Hkv != 0) return "Hq must be a multiple of Hkv";
+  if (d < 1 || d > 256) return "need 1 <= d <= 256";
+  if (n > ((int64_t)1 << 31) - 1) return "n must fit in int32 token indices";
+  // element counts must fit comfortably in 64-bit byte offsets
+  const double kv_elems = (double)Hkv * (double)n * (double)d;
+  if (kv_elems > 1e15) return "K/V too large";
+  if ((double)Hq * w > 1e8) return "too many window rows";
+  return nullptr;
+}
+
+const char* validate_select(int64_t n, int32_t w, int32_t Hkv, int32_t pool_kernel, int64_t n_evict) {
+  if (pool_kernel < 1 || pool_kernel % 2 == 0) return "pool_kernel must be odd and >= 1";
+  if (n_evict < 0 || n_evict > n - w) return "need 0 <= n_evict <= n - window";
+  (void)Hkv;
+  return nullptr;
+}
+
+bool is_device_ptr(const void* p) {
+  if (!p) return false;
+  hipPointerAttribute_t attr;
+  if (hipPointerGetAttributes(&attr, p) != hipSuccess) {
+    (void)hipGetLastError();
+    return false;
+  }
+  return attr.type == hipMemoryTypeDevice || attr.type == hipMemoryTypeManaged;
+}
+
+bool use_mfma(int dtype, int d, uint32_t flags) {
+  return !(flags & DROPKV_FLAG_GENERIC) && mfma_supported(dtype, d);
+}
+
+// Run the scoring stages up to raw scores (ws.S) and row statistics.
+int run_scores(int dtype, const void* q, const void* k, const void* v, const Shape& s,
+               const Workspace& ws, bool mfma, hipStream_t st) {
+  hipError_t e = launch_clear_status(ws.status, st);
+  if (e != hipSuccess) return fail_hip(e, "clear status");
+  if (mfma) {
+    e = launch_mfma_path(q, k, v, s, ws, st);
+    if (e != hipSuccess) return fail_hip(e, "mfma path");
+  } else {
+    e = launch_generic_rows(dtype, q, k, v, s, ws, st);
+    if (e != hipSuccess) return fail_hip(e, "generic row stats");
+    e = launch_generic_scores(dtype, q, k, v, s, ws, st);
+    if (e != hipSuccess) return fail_hip(e, "generic scores");
+  }
+  return DROPKV_OK;
+}
+
+// A singular row leaves its own scores undefined (often inf/NaN), which the
+// select stage then also reports as non-finite: the singular bit wins.
+int status_to_code(int32_t st_word) {
+  if (st_word & kStatusSingular)
+    return fail(DROPKV_ERR_SINGULAR, "a window row has a probability that rounds to 1 (singular)");
+  if (st_word & kStatusNonFinite) return fail(DROPKV_ERR_NONFINITE, "non-finite inputs or scores");
+  return DROPKV_OK;
+}
+
+// Library-owned workspace for the current device; caller holds g_ws_mutex.
+int get_workspace(size_t need, void** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail_hip(e, "hipGetDevice");
+  DeviceWs& w = g_ws[dev];
+  if (w.bytes < need) {
+    if (w.ptr) {
+      e = hipDeviceSynchronize();
+      if (e != hipSuccess) return fail_hip(e, "hipDeviceSynchronize");
+      (void)hipFree(w.ptr);
+      w.ptr = nullptr;
+      w.bytes = 0;
+    }
+    e = hipMalloc(&w.ptr, need);
+    if (e != hipSuccess) return fail_hip(e, "hipMalloc workspace");
+    w.bytes = need;
+  }
+  *out = w.ptr;
+  return DROPKV_OK;
+}
+
+int sync_status(const Workspace& ws, hipStream_t st) {
+  int32_t word = 0;
+  hipError_t e = hipMemcpyAsync(&word, ws.status, sizeof(word), hipMemcpyDeviceToHost, st);
+  if (e != hipSuccess) return fail_hip(e, "status readback");
+  e = hipStreamSynchronize(st);
+  if (e != hipSuccess) return fail_hip(e, "hipStreamSynchronize");
+  return status_to_code(word);
+}
+
+int check_inputs(const void* q, const void* k, const void* v) {
+  if (!q || !k || !v) return fail(DROPKV_ERR_INVALID, "null input pointer");
+  if (!is_device_ptr(q) || !is_device_ptr(k) || !is_device_ptr(v))
+    return fail(DROPKV_ERR_INVALID, "q, k and v must be device pointers");
+  return DROPKV_OK;
+}
+
+int score_sync(int dtype, const void* q, const void* k, const void* v, int64_t n, int32_t w,
+               int32_t Hq, int32_t Hkv, int32_t d, int32_t pool_kernel, int64_t n_evict,
+               float* out_scores, int64_t* out_idx, hipStream_t st) {
+  g_last_error.clear();
+  if (const char* m = validate(dtype, n, w, Hq, Hkv, d)) return fail(DROPKV_ERR_INVALID, m);
+  if (const char* m = validate_select(n, w, Hkv, pool_kernel, n_evict)) return fail(DROPKV_ERR_INVALID, m);
+  if (int rc = check_inputs(q, k, v)) return rc;
+  if (!out_scores || !is_device_ptr(out_scores)) return fail(DROPKV_ERR_INVALID, "out_scores must be a device pointer");
+  if (n_evict > 0 && (!out_idx || !is_device_ptr(out_idx)))
+    return fail(DROPKV_ERR_INVALID, "out_evict_idx must be a device pointer when n_evict > 0");
+  const Shape s{n, w, Hq, Hkv, d};
+  const bool mfma = use_mfma(dtype, d, 0);
+  std::lock_guard<std::mutex> lock(g_ws_mutex);
+  const size_t need = carve_workspace(nullptr, s, mfma).bytes;
+  void* base = nullptr;
+  if (int rc = get_workspace(need, &base)) return rc;
+  Workspace ws = carve_workspace(base, s, mfma);
+  if (int rc = run_scores(dtype, q, k, v, s, ws, mfma, st)) return rc;
+  hipError_t e = launch_select(ws.S, n, w, Hkv, pool_kernel, n_evict, out_scores, out_idx, ws.status, st);
+  if (e != hipSuccess) return fail_hip(e, "select");
+  return sync_status(ws, st);
+}
+
+}  // namespace
+
+// ----------------------------------------------------------------- workspace layout
+
+Workspace carve_workspace(void* base, const Shape& s, bool mfma) {
+  Workspace ws{};
+  size_t off = 0;
+  char* b = (char*)base;
+  auto take = [&](size_t bytes) -> void* {
+    void* p = b ? (void*)(b + off) : nullptr;
+    off = align_up(off + bytes, 256);
+    return p;
+  };
+  const size_t rows = (size_t)s.rows();
+  ws.status = (int32_t*)take(sizeof(int32_t));
+  ws.S = (float*)take(sizeof(float) * (size_t)s.Hkv * (size_t)s.n);
+  ws.rs.m = (float*)take(sizeof(float) * rows);
+  ws.rs.rest = (float*)take(sizeof(float) * rows);
+  ws.rs.L = (float*)take(sizeof(float) * rows);
+  ws.rs.jstar = (int32_t*)take(sizeof(int32_t) * rows);
+  ws.rs.fixval = (float*)take(sizeof(float) * rows);
+  ws.rs.flag = (int32_t*)take(sizeof(int32_t) * rows);
+  ws.rs.a = (float*)take(sizeof(float) * rows * (size_t)s.d);
+  if (mfma) {
+    ws.rs.a_bf = (uint16_t*)take(sizeof(uint16_t) * rows * (size_t)s.d);
+    ws.rs.na = (float*)take(sizeof(float) * rows);
+    ws.rs.bias = (float*)take(sizeof(float) * rows);
+    ws.nchunks = mfma_chunks(s);
+    ws.part = (float*)take(sizeof(float) * (size_t)ws.nchunks * rows * (size_t)(s.d + 2));
+    ws.flaglist = (int32_t*)take(sizeof(int32_t) * (size_t)s.Hkv * (1 + 2 * (size_t)s.G() * s.w));
+  }
+  ws.bytes = off;
+  return ws;
+}
+
+}  // namespace dropkv
+
+using namespace dropkv;
+
+extern "C" {
+
+int dropkv_score(const void* q, const void* k, const void* v, int64_t n, int32_t window,
+                 int32_t Hq, int32_t Hkv, int32_t d, int32_t pool_kernel, int64_t n_evict,
+                 float* out_scores, int64_t* out_evict_idx, void* stream) {
+  return score_sync(DROPKV_BF16, q, k, v, n, window, Hq, Hkv, d, pool_kernel, n_evict, out_scores,
+                    out_evict_idx, (hipStream_t)stream);
+}
+
+int dropkv_score_f32(const float* q, const float* k, const float* v, int64_t n, int32_t window,
+                     int32_t Hq, int32_t Hkv, int32_t d, int32_t pool_kernel, int64_t n_evict,
+                     float* out_scores, int64_t* out_evict_idx, void* stream) {
+  return score_sync(DROPKV_F32, q, k, v, n, window, Hq, Hkv, d, pool_kernel, n_evict, out_scores,
+                    out_evict_idx, (hipStream_t)stream);
+}
+
+size_t dropkv_workspace_bytes(int32_t dtype, int64_t n, int32_t window, int32_t Hq, int32_t Hkv,
+                              int32_t d) {
+  if (validate(dtype, n, window, Hq, Hkv, d)) return 0;
+  const Shape s{n, window, Hq, Hkv, d};
+  // sized for the larger (MFMA) layout so any flag choice fits
+  return carve_workspace(nullptr, s, mfma_supported(dtype, d)).bytes;
+}
+
+int dropkv_score_ex(int32_t dtype, const void* q, const void* k, const void* v, int64_t n,
+                    int32_t window, int32_t Hq, int32_t Hkv, int32_t d, int32_t pool_kernel,
+                    int64_t n_evict, float* out_scores, int64_t* out_evict_idx, void* workspace,
+                    size_t workspace_bytes, int32_t* d_status, uint32_t flags, void* stream) {
+  g_last_error.clear();
+  if (const char* m = validate(dtype, n, window, Hq, Hkv, d)) return fail(DROPKV_ERR_INVALID, m);
+  if (const char* m = validate_select(n, window, Hkv, pool_kernel, n_evict))
+    return fail(DROPKV_ERR_INVALID, m);
+  if (int rc = check_inputs(q, k, v)) return rc;
+  if (!out_scores || !is_device_ptr(out_scores)) return fail(DROPKV_ERR_INVALID, "out_scores must be a device pointer");
+  if (n_evict > 0 && (!out_evict_idx || !is_device_ptr(out_evict_idx)))
+    return fail(DROPKV_ERR_INVALID, "out_evict_idx must be a device pointer when n_evict > 0");
+  if (!workspace || ((uintptr_t)workspace & 255) || !is_device_ptr(workspace))
+    return fail(DROPKV_ERR_INVALID, "workspace must be a 256-byte aligned device pointer");
+  if (!d_status || !is_device_ptr(d_status)) return fail(DROPKV_ERR_INVALID, "d_status must be a device pointer");
+  const Shape s{n, window, Hq, Hkv, d};
+  const bool mfma = use_mfma(dtype, d, flags);
+  Workspace ws = carve_workspace(workspace, s, mfma);
+  if (ws.bytes > workspace_bytes) return fail(DROPKV_ERR_INVALID, "workspace too small");
+  ws.status = d_status;
+  hipStream_t st = (hipStream_t)stream;
+  if (int rc = run_scores(dtype, q, k, v, s, ws, mfma, st)) return rc;
+  hipError_t e = launch_select(ws.S, n, window, Hkv, pool_kernel, n_evict, out_scores, out_evict_idx,
+                               ws.status, st);
+  if (e != hipSuccess) return fail_hip(e, "select");
+  return DROPKV_OK;
+}
+
+int dropkv_raw_scores(int32_t dtype, const void* q, const void* k, const void* v, int64_t n,
+                      int32_t window, int32_t Hq, int32_t Hkv, int32_t d, float* out_S,
+                      uint32_t flags, void* stream) {
+  g_last_error.clear();
+  if (const char* m = validate(dtype, n, window, Hq, Hkv, d)) return fail(DROPKV_ERR_INVALID, m);
+  if (int rc = check_inputs(q, k, v)) return rc;
+  if (!out_S || !is_device_ptr(out_S)) return fail(DROPKV_ERR_INVALID, "out_S must be a device pointer");
+  const Shape s{n, window, Hq, Hkv, d};
+  const bool mfma = use_mfma(dtype, d, flags);
+  hipStream_t st = (hipStream_t)stream;
+  std::lock_guard<std::mutex> lock(g_ws_mutex);
+  void* base = nullptr;
+  if (int rc = get_workspace(carve_workspace(nullptr, s, mfma).bytes, &base)) return rc;
+  Workspace ws = carve_workspace(base, s, mfma);
+  if (int rc = run_scores(dtype, q, k, v, s, ws, mfma, st)) return rc;
+  hipError_t e = hipMemcpyAsync(out_S, ws.S, sizeof(float) * (size_t)Hkv * n, hipMemcpyDeviceToDevice, st);
+  if (e != hipSuccess) return fail_hip(e, "copy S");
+  return sync_status(ws, st);
+}
+
+int dropkv_row_stats(int32_t dtype, const void* q, const void* k, const void* v, int64_t n,
+                     int32_t window, int32_t Hq, int32_t Hkv, int32_t d, float* out_m,
+                     float* out_rest, int32_t* out_argmax, float* out_a, uint32_t flags,
+                     void* stream) {
+  g_last_error.clear();
+  if (const char* m = validate(dtype, n, window, Hq, Hkv, d)) return fail(DROPKV_ERR_INVALID, m);
+  if (int rc = check_inputs(q, k, v)) return rc;
+  for (const void* p : {(const void*)out_m, (const void*)out_rest, (const void*)out_argmax, (const void*)out_a})
+    if (p && !is_device_ptr(p)) return fail(DROPKV_ERR_INVALID, "outputs must be device pointers");
+  const Shape s{n, window, Hq, Hkv, d};
+  const bool mfma = use_mfma(dtype, d, flags);
+  hipStream_t st = (hipStream_t)stream;
+  std::lock_guard<std::mutex> lock(g_ws_mutex);
+  void* base = nullptr;
+  if (int rc = get_workspace(carve_workspace(nullptr, s, mfma).bytes, &base)) return rc;
+  Workspace ws = carve_workspace(base, s, mfma);
+  if (int rc = run_scores(dtype, q, k, v, s, ws, mfma, st)) return rc;
+  const size_t rows = (size_t)s.rows();
+  hipError_t e = hipSuccess;
+  if (out_m && e == hipSuccess) e = hipMemcpyAsync(out_m, ws.rs.m, 4 * rows, hipMemcpyDeviceToDevice, st);
+  if (out_rest && e == hipSuccess) e = hipMemcpyAsync(out_rest, ws.rs.rest, 4 * rows, hipMemcpyDeviceToDevice, st);
+  if (out_argmax && e == hipSuccess) e = hipMemcpyAsync(out_argmax, ws.rs.jstar, 4 * rows, hipMemcpyDeviceToDevice, st);
+  if (out_a && e == hipSuccess) e = hipMemcpyAsync(out_a, ws.rs.a, 4 * rows * d, hipMemcpyDeviceToDevice, st);
+  if (e != hipSuccess) return fail_hip(e, "copy row stats");
+  return sync_status(ws, st);
+}
+
+int dropkv_select(const float* S, int64_t n, int32_t window, int32_t Hkv, int32_t pool_kernel,
+                  int64_t n_evict, float* out_scores, int64_t* out_evict_idx, void* stream) {
+  g_last_error.clear();
+  if (n < 2 || window < 1 || window >= n || Hkv < 1) return fail(DROPKV_ERR_INVALID, "need n >= 2, 1 <= window < n, Hkv >= 1");
+  if (const char* m = validate_select(n, window, Hkv, pool_kernel, n_evict)) return fail(DROPKV_ERR_INVALID, m);
+  if (!S || !is_device_ptr(S) || !out_scores || !is_device_ptr(out_scores))
+    return fail(DROPKV_ERR_INVALID, "S and out_scores must be device pointers");
+  if (n_evict > 0 && (!out_evict_idx || !is_device_ptr(out_evict_idx)))
+    return fail(DROPKV_ERR_INVALID, "out_evict_idx must be a device pointer when n_evict > 0");
+  hipStream_t st = (hipStream_t)stream;
+  std::lock_guard<std::mutex> lock(g_ws_mutex);
+  void* base = nullptr;
+  if (int rc = get_workspace(256, &base)) return rc;
+  Workspace ws{};
+  ws.status = (int32_t*)base;
+  hipError_t e = launch_clear_status(ws.status, st);
+  if (e == hipSuccess) e = launch_select(S, n, window, Hkv, pool_kernel, n_evict, out_scores, out_evict_idx, ws.status, st);
+  if (e != hipSuccess) return fail_hip(e, "select");
+  return sync_status(ws, st);
+}
+
+int dropkv_uses_mfma(int32_t dtype, int32_t d) { return mfma_supported(dtype, d) ? 1 : 0; }
+
+const char* dropkv_last_error(void) { return g_last_error.c_str(); }
+
+const char* dropkv_version(void) { return "dropkv-gfx950 0.1"; }
+
+}  // extern "C"

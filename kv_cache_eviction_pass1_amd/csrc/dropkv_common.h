@@ -1,0 +1,102 @@
+// Internal declarations shared by the HIP sources of libdropkv (gfx950 only).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+#include <stddef.h>
+
+namespace dropkv {
+
+// Bits of the device status word (same values as DROPKV_STATUS_* in dropkv.h).
+constexpr int kStatusSingular = 1;
+constexpr int kStatusNonFinite = 2;
+
+// A window row is rejected when its rest mass R = sum_{j != argmax} exp(x_j - x_max)
+// is at most 2^-24: then 1/(1+R) rounds to 1 in binary32 (the singular-input rule).
+constexpr float kSingularRest = 5.9604644775390625e-08f;  // 2^-24
+
+constexpr float kLog2e = 1.4426950408889634f;
+
+// Per-window-row statistics, row index r = h * window + i (query head h, window row i).
+struct RowStats {
+  float* m;         // largest logit x_max = max_j q.k_j / sqrt(d)  (natural units)
+  float* rest;      // R = sum_{j != argmax} exp(x_j - x_max)
+  float* L;         // 1 + R (softmax denominator relative to the max)
+  int32_t* jstar;   // argmax (lowest index), or -1 if not tracked
+  float* fixval;    // ||Delta_{argmax}||^2 computed without cancellation (valid where used)
+  int32_t* flag;    // 1: the argmax term of this row comes from fixval, not the main pass
+  float* a;         // [rows][d] attention output a = sum_j p_j v_j (fp32)
+  uint16_t* a_bf;   // [rows][d] a rounded to bf16 (MFMA path)
+  float* na;        // ||a||^2 from the bf16-rounded a (MFMA path)
+  float* bias;      // per-row exponent offset for the score pass (MFMA path, log2 units)
+};
+
+// Device workspace, carved from one caller- or library-owned allocation.
+struct Workspace {
+  int32_t* status;  // OR of kStatus* bits
+  float* S;         // [Hkv][n] GQA-mean raw scores
+  RowStats rs;
+  float* part;      // pass-1 partials (MFMA path)
+  int32_t* flaglist;  // per KV head: count then (row, token) pairs of rows handled by fixval
+  int nchunks;      // pass-1 split count (MFMA path)
+  size_t bytes;     // total bytes used
+};
+
+struct Shape {
+  int64_t n;
+  int32_t w, Hq, Hkv, d;
+  int32_t G() const { return Hq / Hkv; }
+  int64_t rows() const { return (int64_t)Hq * w; }
+};
+
+// Workspace layout for a shape (ws_base may be null to only size it).
+Workspace carve_workspace(void* ws_base, const Shape& s, bool mfma);
+
+// Launchers. Each returns hipSuccess or the launch error.
+hipError_t launch_clear_status(int32_t* status, hipStream_t st);
+hipError_t launch_generic_rows(int dtype, const void* q, const void* k, const void* v,
+                               const Shape& s, const Workspace& ws, hipStream_t st);
+hipError_t launch_generic_scores(int dtype, const void* q, const void* k, const void* v,
+                                 const Shape& s, const Workspace& ws, hipStream_t st);
+hipError_t launch_select(const float* S, int64_t n, int32_t w, int32_t Hkv, int32_t pool_kernel,
+                         int64_t n_evict, float* out_scores, int64_t* out_idx, int32_t* status,
+                         hipStream_t st);
+hipError_t launch_mfma_path(const void* q, const void* k, const void* v, const Shape& s,
+                            const Workspace& ws, hipStream_t st);
+bool mfma_supported(int dtype, int d);
+int mfma_chunks(const Shape& s);
+
+// ------------------------------------------------------------------ device helpers
+
+__device__ __forceinline__ float bf16_to_f32(uint16_t b) {
+  return __uint_as_float(((uint32_t)b) << 16);
+}
+
+template <typename T> struct Elem;
+template <> struct Elem<float> {
+  static __device__ __forceinline__ float get(const float* p, size_t i) { return p[i]; }
+};
+template <> struct Elem<uint16_t> {
+  static __device__ __forceinline__ float get(const uint16_t* p, size_t i) { return bf16_to_f32(p[i]); }
+};
+
+__device__ __forceinline__ bool finite_f(float x) { return (__float_as_uint(x) & 0x7f800000u) != 0x7f800000u; }
+
+// Deterministic block reductions (fixed combination order). `red` must hold
+// blockDim.x entries; every thread of the block must call them.
+template <int NT>
+__device__ __forceinline__ float block_sum(float x, float* red) {
+  const int t = threadIdx.x;
+  red[t] = x;
+  __syncthreads();
+#pragma unroll
+  for (int o = NT / 2; o > 0; o >>= 1) {
+    if (t < o) red[t] = red[t] + red[t + o];
+    __syncthreads();
+  }
+  float r = red[0];
+  __syncthreads();
+  return r;
+}
+
+}  // namespace dropkv

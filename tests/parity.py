@@ -1,0 +1,79 @@
+"""Helpers that compare the HIP library's outputs with the fp64 oracle.
+
+Tolerances: relative 2e-2 on scores for bf16 inputs and 1e-5 for fp32
+inputs, on every finite entry; +inf entries (the protected window) must match
+exactly. Evicted sets must always be the bottom-n_evict of the GPU's own
+pooled scores under (score, index), and must equal the oracle's set exactly
+whenever no oracle score other than the boundary value lies within twice the
+tolerance of it.
+"""
+
+from __future__ import annotations
+
+import numpy as np
+
+import oracle
+
+RTOL = {"bf16": 2e-2, "f32": 1e-5}
+
+
+def to_torch(case, device="cuda"):
+    import torch
+    if case.dtype == "bf16":
+        conv = lambda a: torch.from_numpy(a.view(np.int16).copy()).view(torch.bfloat16)
+    else:
+        conv = lambda a: torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32))
+    return tuple(conv(t).to(device).contiguous() for t in (case.q, case.k, case.v))
+
+
+def run_oracle(case, pool_kernel, n_evict, heads=None):
+    return oracle.dropkv_oracle(case.q, case.k, case.v, n=case.n, window=case.window, Hq=case.Hq,
+                                Hkv=case.Hkv, d=case.d, pool_kernel=pool_kernel, n_evict=n_evict,
+                                dtype=case.dtype, heads=heads)
+
+
+def max_rel_err(gpu, ref, floor_rel=1e-30):
+    gpu = np.asarray(gpu, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    inf_ref = np.isinf(ref)
+    assert np.array_equal(np.isinf(gpu), inf_ref), "+inf positions differ"
+    assert np.all(gpu[inf_ref] > 0), "-inf in GPU scores"
+    fin = ~inf_ref
+    if not fin.any():
+        return 0.0
+    assert np.all(np.isfinite(gpu[fin])), "non-finite GPU score"
+    scale = np.max(np.abs(ref[fin]))
+    floor = max(floor_rel * scale, 1e-300)
+    err = np.abs(gpu[fin] - ref[fin]) / np.maximum(np.abs(ref[fin]), floor)
+    return float(err.max())
+
+
+def own_bottom_k(scores_row, k):
+    return np.sort(np.argsort(scores_row, kind="stable")[:k])
+
+
+def check_evictions(gpu_scores, gpu_idx, ref_P, ref_S, ref_idx, n_evict, rtol):
+    """Returns (n_exact_checked, jaccards). Asserts both eviction rules."""
+    gpu_scores = np.asarray(gpu_scores)
+    gpu_idx = np.asarray(gpu_idx)
+    exact, jac = 0, []
+    n = gpu_scores.shape[1]
+    for g in range(gpu_scores.shape[0]):
+        if n_evict == 0:
+            assert gpu_idx.shape[1] == 0
+            continue
+        own = own_bottom_k(gpu_scores[g], n_evict)
+        assert np.array_equal(gpu_idx[g], own), f"head {g}: not the bottom-k of its own scores"
+        assert np.all(np.diff(gpu_idx[g]) > 0), "indices not strictly ascending"
+        ref = ref_idx[g]
+        inter = np.intersect1d(ref, gpu_idx[g]).size
+        jac.append(inter / max(1, np.union1d(ref, gpu_idx[g]).size))
+        tau = np.sort(ref_P[g])[n_evict - 1]
+        band = 2 * rtol * abs(tau)
+        near_P = np.abs(ref_P[g] - tau) <= band
+        near_S = np.abs(ref_S[g] - tau) <= band
+        ambiguous = np.any(near_P & (ref_P[g] != tau)) or np.any(near_S & (ref_S[g] != tau))
+        if not ambiguous:
+            assert np.array_equal(gpu_idx[g], ref), f"head {g}: evicted set differs from the oracle's"
+            exact += 1
+    return exact, jac
