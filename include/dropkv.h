@@ -138,6 +138,21 @@ int dropkv_row_stats(int32_t dtype, const void* q, const void* k, const void* v,
 int dropkv_select(const float* S, int64_t n, int32_t window, int32_t Hkv, int32_t pool_kernel,
                   int64_t n_evict, float* out_scores, int64_t* out_evict_idx, void* stream);
 
+/*
+ * Measurement form of dropkv_score: runs the whole path once on `stream`
+ * with a HIP event recorded after every kernel, synchronises, and writes the
+ * duration of each stage in milliseconds to out_ms[0..*out_count-1] (at most
+ * 12 stages) and their comma-separated names to out_names (names_bytes
+ * bytes, NUL-terminated; may be NULL). Outputs and return codes are those of
+ * dropkv_score / dropkv_score_f32 for the same dtype; `flags` as in
+ * dropkv_score_ex.
+ */
+int dropkv_stage_times(int32_t dtype, const void* q, const void* k, const void* v, int64_t n,
+                       int32_t window, int32_t Hq, int32_t Hkv, int32_t d, int32_t pool_kernel,
+                       int64_t n_evict, float* out_scores, int64_t* out_evict_idx, uint32_t flags,
+                       float* out_ms, char* out_names, int32_t names_bytes, int32_t* out_count,
+                       void* stream);
+
 /* 1 if (dtype, d) takes the MFMA path by default, 0 if the plain-VALU path. */
 int dropkv_uses_mfma(int32_t dtype, int32_t d);
 

@@ -33,6 +33,8 @@ SIGNATURES = {
     "dropkv_row_stats": (_i32, [_i32, _p, _p, _p, _i64, _i32, _i32, _i32, _i32, _p, _p, _p, _p,
                                 _u32, _p]),
     "dropkv_select": (_i32, [_p, _i64, _i32, _i32, _i32, _i64, _p, _p, _p]),
+    "dropkv_stage_times": (_i32, [_i32, _p, _p, _p, _i64, _i32, _i32, _i32, _i32, _i32, _i64, _p,
+                                  _p, _u32, _p, _p, _i32, _p, _p]),
     "dropkv_uses_mfma": (_i32, [_i32, _i32]),
     "dropkv_last_error": (_c.c_char_p, []),
     "dropkv_version": (_c.c_char_p, []),
@@ -210,6 +212,30 @@ def select(S, *, window: int, pool_kernel: int, n_evict: int, stream=None):
                            idx.data_ptr() if n_evict > 0 else None, _stream_handle(stream))
     _raise(rc)
     return scores, idx
+
+
+def stage_times(q, k, v, *, pool_kernel: int, n_evict: int, flags: int = 0, stream=None):
+    """One scoring call with a HIP event after every kernel.
+
+    Returns (scores, evict_idx, [(stage name, milliseconds), ...]).
+    """
+    torch = _torch()
+    lib = load_library()
+    Hq, Hkv, d, n, w = _shapes(q, k, v)
+    scores = torch.empty((Hkv, n), dtype=torch.float32, device=q.device)
+    idx = torch.empty((Hkv, max(n_evict, 0)), dtype=torch.int64, device=q.device)
+    ms = (ctypes.c_float * 16)()
+    names = ctypes.create_string_buffer(512)
+    count = ctypes.c_int32(0)
+    rc = lib.dropkv_stage_times(_dtype_code(q), q.data_ptr(), k.data_ptr(), v.data_ptr(), n, w, Hq,
+                                Hkv, d, pool_kernel, n_evict, scores.data_ptr(),
+                                idx.data_ptr() if n_evict > 0 else None, flags,
+                                ctypes.cast(ms, ctypes.c_void_p), ctypes.cast(names, ctypes.c_void_p),
+                                512, ctypes.cast(ctypes.pointer(count), ctypes.c_void_p),
+                                _stream_handle(stream))
+    _raise(rc)
+    labels = names.value.decode().split(",") if count.value else []
+    return scores, idx, [(labels[i], float(ms[i])) for i in range(count.value)]
 
 
 def uses_mfma(dtype_code: int, d: int) -> bool:

@@ -71,17 +71,20 @@ bool use_mfma(int dtype, int d, uint32_t flags) {
 
 // Run the scoring stages up to raw scores (ws.S) and row statistics.
 int run_scores(int dtype, const void* q, const void* k, const void* v, const Shape& s,
-               const Workspace& ws, bool mfma, hipStream_t st) {
+               const Workspace& ws, bool mfma, hipStream_t st, StageEvents* se = nullptr) {
   hipError_t e = launch_clear_status(ws.status, st);
   if (e != hipSuccess) return fail_hip(e, "clear status");
   if (mfma) {
-    e = launch_mfma_path(q, k, v, s, ws, st);
+    e = launch_mfma_path(q, k, v, s, ws, st, se);
     if (e != hipSuccess) return fail_hip(e, "mfma path");
   } else {
+    record_stage(se, "start", st);
     e = launch_generic_rows(dtype, q, k, v, s, ws, st);
     if (e != hipSuccess) return fail_hip(e, "generic row stats");
+    record_stage(se, "rows", st);
     e = launch_generic_scores(dtype, q, k, v, s, ws, st);
     if (e != hipSuccess) return fail_hip(e, "generic scores");
+    record_stage(se, "scores", st);
   }
   return DROPKV_OK;
 }
@@ -158,6 +161,23 @@ int score_sync(int dtype, const void* q, const void* k, const void* v, int64_t n
 
 }  // namespace
 
+// ----------------------------------------------------------------- stage events
+
+hipError_t record_stage(StageEvents* se, const char* name, hipStream_t st) {
+  if (!se || se->count > kMaxStages) return hipSuccess;
+  // ev[0] is the start marker; ev[i] (i >= 1) closes stage i-1
+  if (se->count == 0 && name && std::strcmp(name, "start") == 0) {
+    hipError_t e = hipEventRecord(se->ev[0], st);
+    se->count = 0;
+    return e;
+  }
+  if (se->count >= kMaxStages) return hipSuccess;
+  se->names[se->count] = name;
+  hipError_t e = hipEventRecord(se->ev[se->count + 1], st);
+  se->count += 1;
+  return e;
+}
+
 // ----------------------------------------------------------------- workspace layout
 
 Workspace carve_workspace(void* base, const Shape& s, bool mfma) {
@@ -184,8 +204,8 @@ Workspace carve_workspace(void* base, const Shape& s, bool mfma) {
     ws.rs.na = (float*)take(sizeof(float) * rows);
     ws.rs.bias = (float*)take(sizeof(float) * rows);
     ws.nchunks = mfma_chunks(s);
-    ws.part = (float*)take(sizeof(float) * (size_t)ws.nchunks * rows * (size_t)(s.d + 2));
-    ws.flaglist = (int32_t*)take(sizeof(int32_t) * (size_t)s.Hkv * (1 + 2 * (size_t)s.G() * s.w));
+    ws.part = (float*)take(sizeof(float) * (size_t)ws.nchunks * rows * (size_t)(s.d + 4));
+    ws.extra = take(mfma_extra_bytes(s));
   }
   ws.bytes = off;
   return ws;
@@ -313,6 +333,57 @@ int dropkv_select(const float* S, int64_t n, int32_t window, int32_t Hkv, int32_
   if (e == hipSuccess) e = launch_select(S, n, window, Hkv, pool_kernel, n_evict, out_scores, out_evict_idx, ws.status, st);
   if (e != hipSuccess) return fail_hip(e, "select");
   return sync_status(ws, st);
+}
+
+int dropkv_stage_times(int32_t dtype, const void* q, const void* k, const void* v, int64_t n,
+                       int32_t window, int32_t Hq, int32_t Hkv, int32_t d, int32_t pool_kernel,
+                       int64_t n_evict, float* out_scores, int64_t* out_evict_idx, uint32_t flags,
+                       float* out_ms, char* out_names, int32_t names_bytes, int32_t* out_count,
+                       void* stream) {
+  g_last_error.clear();
+  if (const char* m = validate(dtype, n, window, Hq, Hkv, d)) return fail(DROPKV_ERR_INVALID, m);
+  if (const char* m = validate_select(n, window, Hkv, pool_kernel, n_evict)) return fail(DROPKV_ERR_INVALID, m);
+  if (int rc = check_inputs(q, k, v)) return rc;
+  if (!out_scores || !is_device_ptr(out_scores)) return fail(DROPKV_ERR_INVALID, "out_scores must be a device pointer");
+  if (n_evict > 0 && (!out_evict_idx || !is_device_ptr(out_evict_idx)))
+    return fail(DROPKV_ERR_INVALID, "out_evict_idx must be a device pointer when n_evict > 0");
+  if (!out_ms || !out_count) return fail(DROPKV_ERR_INVALID, "out_ms and out_count are required");
+  const Shape s{n, window, Hq, Hkv, d};
+  const bool mfma = use_mfma(dtype, d, flags);
+  hipStream_t st = (hipStream_t)stream;
+  std::lock_guard<std::mutex> lock(g_ws_mutex);
+  void* base = nullptr;
+  if (int rc = get_workspace(carve_workspace(nullptr, s, mfma).bytes, &base)) return rc;
+  Workspace ws = carve_workspace(base, s, mfma);
+  StageEvents se{};
+  for (int i = 0; i <= kMaxStages; ++i) {
+    hipError_t e = hipEventCreate(&se.ev[i]);
+    if (e != hipSuccess) return fail_hip(e, "hipEventCreate");
+  }
+  int rc = run_scores(dtype, q, k, v, s, ws, mfma, st, &se);
+  if (rc == DROPKV_OK) {
+    hipError_t e = launch_select(ws.S, n, window, Hkv, pool_kernel, n_evict, out_scores, out_evict_idx, ws.status, st);
+    if (e != hipSuccess) rc = fail_hip(e, "select");
+    else record_stage(&se, "select", st);
+  }
+  if (rc == DROPKV_OK) rc = sync_status(ws, st);
+  if (rc == DROPKV_OK || rc == DROPKV_ERR_SINGULAR || rc == DROPKV_ERR_NONFINITE) {
+    std::string names;
+    for (int i = 0; i < se.count; ++i) {
+      float ms = 0.f;
+      (void)hipEventElapsedTime(&ms, se.ev[i], se.ev[i + 1]);
+      out_ms[i] = ms;
+      names += se.names[i];
+      names += (i + 1 < se.count) ? "," : "";
+    }
+    *out_count = se.count;
+    if (out_names && names_bytes > 0) {
+      std::strncpy(out_names, names.c_str(), (size_t)names_bytes - 1);
+      out_names[names_bytes - 1] = 0;
+    }
+  }
+  for (int i = 0; i <= kMaxStages; ++i) (void)hipEventDestroy(se.ev[i]);
+  return rc;
 }
 
 int dropkv_uses_mfma(int32_t dtype, int32_t d) { return mfma_supported(dtype, d) ? 1 : 0; }

@@ -37,7 +37,7 @@ struct Workspace {
   float* S;         // [Hkv][n] GQA-mean raw scores
   RowStats rs;
   float* part;      // pass-1 partials (MFMA path)
-  int32_t* flaglist;  // per KV head: count then (row, token) pairs of rows handled by fixval
+  void* extra;      // further MFMA-path buffers (see mfma_extra_bytes)
   int nchunks;      // pass-1 split count (MFMA path)
   size_t bytes;     // total bytes used
 };
@@ -61,10 +61,20 @@ hipError_t launch_generic_scores(int dtype, const void* q, const void* k, const 
 hipError_t launch_select(const float* S, int64_t n, int32_t w, int32_t Hkv, int32_t pool_kernel,
                          int64_t n_evict, float* out_scores, int64_t* out_idx, int32_t* status,
                          hipStream_t st);
+// Stage timing: when `ev` is non-null, an event is recorded on the stream after
+// every kernel of the path; `names` receives the stage names (at most kMaxStages).
+constexpr int kMaxStages = 12;
+struct StageEvents {
+  hipEvent_t ev[kMaxStages + 1];
+  const char* names[kMaxStages];
+  int count;
+};
+hipError_t record_stage(StageEvents* se, const char* name, hipStream_t st);
 hipError_t launch_mfma_path(const void* q, const void* k, const void* v, const Shape& s,
-                            const Workspace& ws, hipStream_t st);
+                            const Workspace& ws, hipStream_t st, StageEvents* se);
 bool mfma_supported(int dtype, int d);
 int mfma_chunks(const Shape& s);
+size_t mfma_extra_bytes(const Shape& s);
 
 // ------------------------------------------------------------------ device helpers
 
