@@ -154,7 +154,7 @@ int score_sync(int dtype, const void* q, const void* k, const void* v, int64_t n
   if (int rc = get_workspace(need, &base)) return rc;
   Workspace ws = carve_workspace(base, s, mfma);
   if (int rc = run_scores(dtype, q, k, v, s, ws, mfma, st)) return rc;
-  hipError_t e = launch_select(ws.S, n, w, Hkv, pool_kernel, n_evict, out_scores, out_idx, ws.status, st);
+  hipError_t e = launch_select(ws.S, n, w, Hkv, pool_kernel, n_evict, out_scores, out_idx, ws.status, ws.sel, st);
   if (e != hipSuccess) return fail_hip(e, "select");
   return sync_status(ws, st);
 }
@@ -199,6 +199,7 @@ Workspace carve_workspace(void* base, const Shape& s, bool mfma) {
   ws.rs.fixval = (float*)take(sizeof(float) * rows);
   ws.rs.flag = (int32_t*)take(sizeof(int32_t) * rows);
   ws.rs.a = (float*)take(sizeof(float) * rows * (size_t)s.d);
+  ws.sel = take(select_scratch_bytes(s.n, s.Hkv));
   if (mfma) {
     ws.rs.a_bf = (uint16_t*)take(sizeof(uint16_t) * rows * (size_t)s.d);
     ws.rs.na = (float*)take(sizeof(float) * rows);
@@ -262,7 +263,7 @@ int dropkv_score_ex(int32_t dtype, const void* q, const void* k, const void* v, 
   hipStream_t st = (hipStream_t)stream;
   if (int rc = run_scores(dtype, q, k, v, s, ws, mfma, st)) return rc;
   hipError_t e = launch_select(ws.S, n, window, Hkv, pool_kernel, n_evict, out_scores, out_evict_idx,
-                               ws.status, st);
+                               ws.status, ws.sel, st);
   if (e != hipSuccess) return fail_hip(e, "select");
   return DROPKV_OK;
 }
@@ -326,11 +327,12 @@ int dropkv_select(const float* S, int64_t n, int32_t window, int32_t Hkv, int32_
   hipStream_t st = (hipStream_t)stream;
   std::lock_guard<std::mutex> lock(g_ws_mutex);
   void* base = nullptr;
-  if (int rc = get_workspace(256, &base)) return rc;
+  if (int rc = get_workspace(256 + select_scratch_bytes(n, Hkv), &base)) return rc;
   Workspace ws{};
   ws.status = (int32_t*)base;
+  ws.sel = (char*)base + 256;
   hipError_t e = launch_clear_status(ws.status, st);
-  if (e == hipSuccess) e = launch_select(S, n, window, Hkv, pool_kernel, n_evict, out_scores, out_evict_idx, ws.status, st);
+  if (e == hipSuccess) e = launch_select(S, n, window, Hkv, pool_kernel, n_evict, out_scores, out_evict_idx, ws.status, ws.sel, st);
   if (e != hipSuccess) return fail_hip(e, "select");
   return sync_status(ws, st);
 }
@@ -362,7 +364,7 @@ int dropkv_stage_times(int32_t dtype, const void* q, const void* k, const void* 
   }
   int rc = run_scores(dtype, q, k, v, s, ws, mfma, st, &se);
   if (rc == DROPKV_OK) {
-    hipError_t e = launch_select(ws.S, n, window, Hkv, pool_kernel, n_evict, out_scores, out_evict_idx, ws.status, st);
+    hipError_t e = launch_select(ws.S, n, window, Hkv, pool_kernel, n_evict, out_scores, out_evict_idx, ws.status, ws.sel, st);
     if (e != hipSuccess) rc = fail_hip(e, "select");
     else record_stage(&se, "select", st);
   }

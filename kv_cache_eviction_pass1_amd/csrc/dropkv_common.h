@@ -38,6 +38,7 @@ struct Workspace {
   RowStats rs;
   float* part;      // pass-1 partials (MFMA path)
   void* extra;      // further MFMA-path buffers (see mfma_extra_bytes)
+  void* sel;        // select-stage scratch (see select_scratch_bytes)
   int nchunks;      // pass-1 split count (MFMA path)
   size_t bytes;     // total bytes used
 };
@@ -60,7 +61,8 @@ hipError_t launch_generic_scores(int dtype, const void* q, const void* k, const 
                                  const Shape& s, const Workspace& ws, hipStream_t st);
 hipError_t launch_select(const float* S, int64_t n, int32_t w, int32_t Hkv, int32_t pool_kernel,
                          int64_t n_evict, float* out_scores, int64_t* out_idx, int32_t* status,
-                         hipStream_t st);
+                         void* scratch, hipStream_t st);
+size_t select_scratch_bytes(int64_t n, int32_t Hkv);
 // Stage timing: when `ev` is non-null, an event is recorded on the stream after
 // every kernel of the path; `names` receives the stage names (at most kMaxStages).
 constexpr int kMaxStages = 12;
