@@ -29,7 +29,7 @@
 // gives lane l column l%32 and rows 8*(v/4) + 4*(l/32) + v%4, v = 0..15.
 // K/V tiles live in LDS as 64 rows of 256 bytes with the 16-byte chunks of
 // row t XOR-permuted by swz(t) (bank-conflict free for both the 16-byte
-// operand reads and the transposing 8-byte reads).
+// operand reads and the transposing 8-byte reads on gfx950's 64-bank LDS).
 #include "dropkv_common.h"
 
 namespace dropkv {
@@ -51,7 +51,11 @@ constexpr int FXSTRIDE = HD + 2;         // floats per fix-up partial (sp, ps, D
 typedef __attribute__((address_space(3))) void lds_void;
 typedef __attribute__((address_space(1))) const void gbl_cvoid;
 
-__device__ __forceinline__ int swz(int t) { return ((t & 3) << 1) | ((t >> 2) & 1); }
+// Chunk permutation of token row t: a bijection on t mod 16 (16 consecutive
+// rows read with ds_read_b128 hit 16 distinct 16-byte bank groups) whose top
+// two bits differ within every aligned group of 4 rows (the 32 lanes of a
+// ds_read_b64_tr_b16 read 4 rows x 64 bytes from 16 distinct bank groups).
+__device__ __forceinline__ int swz(int t) { return ((t & 3) << 2) | ((t >> 2) & 3); }
 
 // byte offset of element d of token row t inside a swizzled tile
 __device__ __forceinline__ int toff(int t, int d) {
@@ -602,25 +606,90 @@ __device__ __forceinline__ void p2_combine(const P2Args& P, float (*red)[TT][2],
   }
 }
 
-__global__ __launch_bounds__(MAXW * 64) void k_pass2(P2Args P) {
-  __shared__ __attribute__((aligned(1024))) char kb0[TILE_BYTES];
-  __shared__ __attribute__((aligned(1024))) char vb0[TILE_BYTES];
-  __shared__ __attribute__((aligned(1024))) char kb1[TILE_BYTES];
-  __shared__ __attribute__((aligned(1024))) char vb1[TILE_BYTES];
-  __shared__ float red[MAXW][TT][2];
+// ---- pass 2, fast path
+//
+// A workgroup has NW waves (2 per SIMD at NW = 8); each wave owns one 32-row
+// block and walks its chunk in 32-token subtiles. K/V tiles of 64 tokens are
+// triple-buffered in LDS (two tiles in flight). Per subtile the wave runs
+// X = Q K^T and C = a V^T on MFMA (the accumulator of C starts at
+// -||a||^2/2) and then the score VALU, in one of three forms chosen per
+// subtile by a wave vote on the largest p = 2^{x c - bias}:
+//   p < 2^-12 everywhere: r^2 = p^2 (1 + 2p + ...) is taken as 2^{2(x c - bias)}
+//                          (relative error < 2p < 5e-4);
+//   p < 2^-7  everywhere: r^2 = p^2 (1 + 2p + 3p^2) (error 4p^3 < 2e-6);
+//   otherwise:            r^2 = (p / (1 - p))^2 with a reciprocal.
+
+enum { kTierSquare = 0, kTierSeries = 1, kTierExact = 2 };
+
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+}
+
+// Workgroup barrier that orders LDS traffic only. __syncthreads() would also
+// wait for every outstanding vector-memory operation (vmcnt(0)), including
+// the direct-to-LDS loads of tiles still in flight; callers wait for the tile
+// they need with wait_vmcnt<N>() first.
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
+// ||v||^2 of the 64 tokens of a tile into LDS (one 4-byte direct-to-LDS load per lane)
+__device__ __forceinline__ void issue_nv(const float* nvh, int64_t tok0, int64_t n, float* lds, int lane) {
+  int64_t tok = tok0 + lane;
+  if (tok >= n) tok = n - 1;
+  __builtin_amdgcn_global_load_lds((gbl_cvoid*)(nvh + tok), (lds_void*)lds, 4, 0, 0);
+}
+
+template <int TIER>
+__device__ __forceinline__ void p2_values(const f32x16& X, const f32x16& C, const float (&bias)[16],
+                                          float c2, float& t1, float& t2) {
+  float a1 = 0.f, a2 = 0.f;
+#pragma unroll
+  for (int vv = 0; vv < 16; ++vv) {
+    const float y = fmaf(X[vv], c2, -bias[vv]);
+    float r2;
+    if (TIER == kTierSquare) {
+      r2 = __builtin_amdgcn_exp2f(y + y);
+    } else {
+      const float p = __builtin_amdgcn_exp2f(y);
+      if (TIER == kTierSeries) {
+        r2 = (p * p) * fmaf(p, fmaf(p, 3.0f, 2.0f), 1.0f);
+      } else {
+        const float r = p * __builtin_amdgcn_rcpf(1.0f - p);
+        r2 = r * r;
+      }
+    }
+    a2 += r2;
+    a1 = fmaf(r2, C[vv], a1);
+  }
+  t1 = a1;
+  t2 = a2;
+}
+
+template <int NW>
+__global__ __launch_bounds__(NW * 64) void k_pass2(P2Args P) {
+  __shared__ __attribute__((aligned(1024))) char kbuf[3][TILE_BYTES];
+  __shared__ __attribute__((aligned(1024))) char vbuf[3][TILE_BYTES];
+  __shared__ float red3[3][NW][TT];
+  __shared__ float nvbuf[3][TT];
+  constexpr int kDmaPerTile = 32 / NW + 1;  // direct-to-LDS instructions per wave per tile
   const int chunk = blockIdx.x, rg = blockIdx.y, g = blockIdx.z;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int h = lane >> 5, l32 = lane & 31;
-  const int rb = rg * P.nw + wave;
+  const int rb = rg * NW + wave;
   const bool active = rb * 32 < P.Rg;
-  int nwa = (P.Rg - rg * P.nw * 32 + 31) / 32;  // active waves of this row group
-  if (nwa > P.nw) nwa = P.nw;
+  int nwa = (P.Rg - rg * NW * 32 + 31) / 32;  // active waves
+  if (nwa > NW) nwa = NW;
   const int64_t t0 = (int64_t)chunk * P.tiles_per_chunk * TT;
   int64_t t1 = t0 + (int64_t)P.tiles_per_chunk * TT;
   if (t1 > P.n) t1 = P.n;
   const int ntiles = (int)((t1 - t0 + TT - 1) / TT);
   const uint16_t* kh = P.k + (size_t)g * P.n * HD;
   const uint16_t* vh = P.v + (size_t)g * P.n * HD;
+  const float* __restrict__ nvg = P.nv + (size_t)g * P.n;
+  float* __restrict__ Sout = P.S + ((size_t)blockIdx.y * P.Hkv + g) * P.n;
   const bool flagged = P.flagcount[g] != 0;
 
   bf16x8 qa[8], aa[8];
@@ -629,12 +698,10 @@ __global__ __launch_bounds__(MAXW * 64) void k_pass2(P2Args P) {
     const int row = rb * 32 + l32;
     const bool ok = row < P.Rg;
     const size_t grow = (size_t)g * P.Rg + (ok ? row : 0);
-    const uint16_t* qr = P.q + grow * HD;
-    const uint16_t* ar = P.rs.a_bf + grow * HD;
 #pragma unroll
     for (int ks = 0; ks < 8; ++ks) {
-      bf16x8 tq = *(const bf16x8*)(qr + ks * 16 + h * 8);
-      bf16x8 ta = *(const bf16x8*)(ar + ks * 16 + h * 8);
+      bf16x8 tq = *(const bf16x8*)(P.q + grow * HD + ks * 16 + h * 8);
+      bf16x8 ta = *(const bf16x8*)(P.rs.a_bf + grow * HD + ks * 16 + h * 8);
       if (!ok) { tq = bf16x8{}; ta = bf16x8{}; }
       qa[ks] = tq;
       aa[ks] = ta;
@@ -650,27 +717,109 @@ __global__ __launch_bounds__(MAXW * 64) void k_pass2(P2Args P) {
   }
 
   if (ntiles > 0) {
-    issue_tile(kh, t0, P.n, kb0, wave, P.nw, lane);
-    issue_tile(vh, t0, P.n, vb0, wave, P.nw, lane);
+    issue_tile(kh, t0, P.n, kbuf[0], wave, NW, lane);
+    issue_tile(vh, t0, P.n, vbuf[0], wave, NW, lane);
   }
-  for (int it = 0; it < ntiles; it += 2) {
-    tile_barrier();
-    if (it + 1 < ntiles) {
-      issue_tile(kh, t0 + (int64_t)(it + 1) * TT, P.n, kb1, wave, P.nw, lane);
-      issue_tile(vh, t0 + (int64_t)(it + 1) * TT, P.n, vb1, wave, P.nw, lane);
+
+  if (flagged) {
+    // per-tile path with the argmax exclusion of flagged rows (double-buffered)
+    float (*red)[TT][2] = (float (*)[TT][2])&red3[0][0][0];
+    static_assert(3 * NW * TT >= NW * TT * 2, "reduction buffer");
+    for (int it = 0; it < ntiles; ++it) {
+      const int b = it & 1;
+      tile_barrier();
+      if (it + 1 < ntiles) {
+        issue_tile(kh, t0 + (int64_t)(it + 1) * TT, P.n, kbuf[b ^ 1], wave, NW, lane);
+        issue_tile(vh, t0 + (int64_t)(it + 1) * TT, P.n, vbuf[b ^ 1], wave, NW, lane);
+      }
+      p2_tile(P, kbuf[b], vbuf[b], t0 + (int64_t)it * TT, lane, active, rb, qa, aa, bias, cinit,
+              true, g, red, wave);
+      __syncthreads();
+      p2_combine(P, red, nwa, t0 + (int64_t)it * TT, t1, g);
     }
-    p2_tile(P, kb0, vb0, t0 + (int64_t)it * TT, lane, active, rb, qa, aa, bias, cinit, flagged, g, red, wave);
-    __syncthreads();
-    p2_combine(P, red, nwa, t0 + (int64_t)it * TT, t1, g);
-    if (it + 1 >= ntiles) break;
-    tile_barrier();
-    if (it + 2 < ntiles) {
-      issue_tile(kh, t0 + (int64_t)(it + 2) * TT, P.n, kb0, wave, P.nw, lane);
-      issue_tile(vh, t0 + (int64_t)(it + 2) * TT, P.n, vb0, wave, P.nw, lane);
+    return;
+  }
+
+  // the fast path's only vector-memory loads are the direct-to-LDS tile loads
+  // (K, V and ||v||^2), so `vmcnt <= one tile's loads` means the older tile landed
+  if (ntiles > 0) issue_nv(nvg, t0, P.n, nvbuf[0], lane);
+  if (ntiles > 1) {
+    issue_tile(kh, t0 + TT, P.n, kbuf[1], wave, NW, lane);
+    issue_tile(vh, t0 + TT, P.n, vbuf[1], wave, NW, lane);
+    issue_nv(nvg, t0 + TT, P.n, nvbuf[1], lane);
+  }
+  const float c2 = P.c2;
+  for (int t = 0; t < ntiles; ++t) {
+    const int64_t tb = t0 + (int64_t)t * TT;
+    if (t + 1 < ntiles) wait_vmcnt<kDmaPerTile>(); else wait_vmcnt<0>();
+    lds_barrier();  // tile t in LDS for every wave; tile t-1's buffer is free
+    if (t >= 1 && threadIdx.x < TT) {
+      // scores of tile t-1 (all waves wrote their partials before this barrier)
+      const int64_t tok = tb - TT + threadIdx.x;
+      if (tok < t1) {
+        float sacc = 0.f;
+        for (int wv = 0; wv < nwa; ++wv) sacc += red3[(t - 1) % 3][wv][threadIdx.x];
+        Sout[tok] = fmaxf(sacc, 0.0f) * P.invG;
+      }
     }
-    p2_tile(P, kb1, vb1, t0 + (int64_t)(it + 1) * TT, lane, active, rb, qa, aa, bias, cinit, flagged, g, red, wave);
-    __syncthreads();
-    p2_combine(P, red, nwa, t0 + (int64_t)(it + 1) * TT, t1, g);
+    if (t + 2 < ntiles) {
+      const int nb = (t + 2) % 3;
+      issue_tile(kh, tb + 2 * TT, P.n, kbuf[nb], wave, NW, lane);
+      issue_tile(vh, tb + 2 * TT, P.n, vbuf[nb], wave, NW, lane);
+      issue_nv(nvg, tb + 2 * TT, P.n, nvbuf[nb], lane);
+    }
+    if (active) {
+      const char* kc = kbuf[t % 3];
+      const char* vc = vbuf[t % 3];
+#pragma unroll
+      for (int sub = 0; sub < 2; ++sub) {
+        const char* kt = kc + sub * 32 * 256;
+        const char* vt = vc + sub * 32 * 256;
+        bf16x8 kb[8], vb[8];
+#pragma unroll
+        for (int ks = 0; ks < 8; ++ks) kb[ks] = ld16(kt + toff(l32, ks * 16 + h * 8));
+#pragma unroll
+        for (int ks = 0; ks < 8; ++ks) vb[ks] = ld16(vt + toff(l32, ks * 16 + h * 8));
+        f32x16 X = {}, C;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) C[i] = cinit[i];
+#pragma unroll
+        for (int ks = 0; ks < 8; ++ks) X = mfma(qa[ks], kb[ks], X);
+#pragma unroll
+        for (int ks = 0; ks < 8; ++ks) C = mfma(aa[ks], vb[ks], C);
+        const int64_t tok = tb + sub * 32 + l32;
+        float xm = -INFINITY;
+        if (tb + sub * 32 + 31 > P.n - P.w) {
+#pragma unroll
+          for (int vv = 0; vv < 16; ++vv) {
+            const int rr = rb * 32 + (vv >> 2) * 8 + 4 * h + (vv & 3);
+            if (tok > P.n - P.w + (rr % P.w)) X[vv] = -INFINITY;
+          }
+        }
+#pragma unroll
+        for (int vv = 0; vv < 16; ++vv) xm = fmaxf(xm, fmaf(X[vv], c2, -bias[vv]));
+        float q1, q2;
+        if (__builtin_amdgcn_ballot_w64(xm > -7.0f))
+          p2_values<kTierExact>(X, C, bias, c2, q1, q2);
+        else if (__builtin_amdgcn_ballot_w64(xm > -12.0f))
+          p2_values<kTierSeries>(X, C, bias, c2, q1, q2);
+        else
+          p2_values<kTierSquare>(X, C, bias, c2, q1, q2);
+        // this wave's rows: sum r^2 (||a||^2 - 2 a.v + ||v||^2) = ||v||^2 q2 - 2 q1
+        const float sw = pair_sum(fmaf(nvbuf[t % 3][sub * 32 + l32], q2, -2.0f * q1));
+        if (h == 0) red3[t % 3][wave][sub * 32 + l32] = sw;
+      }
+    }
+  }
+  __syncthreads();
+  if (ntiles >= 1 && threadIdx.x < TT) {
+    const int tl = ntiles - 1;
+    const int64_t tok = t0 + (int64_t)tl * TT + threadIdx.x;
+    if (tok < t1) {
+      float sacc = 0.f;
+      for (int wv = 0; wv < nwa; ++wv) sacc += red3[tl % 3][wv][threadIdx.x];
+      Sout[tok] = fmaxf(sacc, 0.0f) * P.invG;
+    }
   }
 }
 
@@ -690,6 +839,7 @@ __global__ void k_zero_i32(int32_t* p, int count) {
 
 struct Plan {
   int Rg, RBt, nrg, nw, tiles, tpc1, nch1, tpc2, nch2;
+  int nw2, nrg2;  // pass 2: waves per workgroup (1, 2 or 4; 64 rows each) and row groups
 };
 
 Plan make_plan(const Shape& s) {
@@ -707,7 +857,14 @@ Plan make_plan(const Shape& s) {
   if (p.nch1 < 1) p.nch1 = 1;
   p.tpc1 = (p.tiles + p.nch1 - 1) / p.nch1;
   p.nch1 = (p.tiles + p.tpc1 - 1) / p.tpc1;
-  p.nch2 = (target2 + per - 1) / per;
+  // pass 2: 32 rows per wave, 8 waves (256 rows) per workgroup, or fewer waves
+  // (power of two) when the KV head has fewer row blocks
+  p.nw2 = 8;
+  while (p.nw2 > 1 && p.nw2 / 2 >= p.RBt) p.nw2 /= 2;
+  p.nrg2 = (p.RBt + p.nw2 - 1) / p.nw2;
+  const int per2 = s.Hkv * p.nrg2;
+  (void)target2;
+  p.nch2 = (256 + per2 - 1) / per2;
   if (p.nch2 > p.tiles) p.nch2 = p.tiles;
   if (p.nch2 < 1) p.nch2 = 1;
   p.tpc2 = (p.tiles + p.nch2 - 1) / p.nch2;
@@ -727,7 +884,7 @@ size_t mfma_extra_bytes(const Shape& s) {
   b += sizeof(float) * (size_t)s.Hkv * s.n;                       // ||v||^2
   b += sizeof(float) * (size_t)FXC * s.Hkv * p.Rg * FXSTRIDE;     // fix-up partials
   b += sizeof(int32_t) * (size_t)s.Hkv;                           // flag counts
-  if (p.nrg > 1) b += sizeof(float) * (size_t)p.nrg * s.Hkv * s.n;  // row-group partial S
+  if (p.nrg2 > 1) b += sizeof(float) * (size_t)p.nrg2 * s.Hkv * s.n;  // row-group partial S
   return b + 4 * 256;
 }
 
@@ -740,7 +897,7 @@ hipError_t launch_mfma_path(const void* q, const void* k, const void* v, const S
   float* nv = (float*)take(sizeof(float) * (size_t)s.Hkv * s.n);
   float* fx = (float*)take(sizeof(float) * (size_t)FXC * s.Hkv * p.Rg * FXSTRIDE);
   int32_t* flagcount = (int32_t*)take(sizeof(int32_t) * (size_t)s.Hkv);
-  float* Spart = p.nrg > 1 ? (float*)take(sizeof(float) * (size_t)p.nrg * s.Hkv * s.n) : ws.S;
+  float* Spart = p.nrg2 > 1 ? (float*)take(sizeof(float) * (size_t)p.nrg2 * s.Hkv * s.n) : ws.S;
   const float c2 = kLog2e / sqrtf((float)HD);
 
   k_zero_i32<<<(s.Hkv + 63) / 64, 64, 0, st>>>(flagcount, s.Hkv);
@@ -758,13 +915,19 @@ hipError_t launch_mfma_path(const void* q, const void* k, const void* v, const S
              ws.rs, flagcount, fx};
   k_fixup<<<dim3(FXC, s.Hkv), 256, 0, st>>>(af);
   record_stage(se, "fixup", st);
-  P2Args a2{(const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v, s.n, s.w, p.Rg, p.nw,
+  P2Args a2{(const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v, s.n, s.w, p.Rg, p.nw2,
             p.tpc2, s.Hkv, c2, 1.0f / (float)s.G(), ws.rs, nv, flagcount, Spart};
-  k_pass2<<<dim3(p.nch2, p.nrg, s.Hkv), p.nw * 64, 0, st>>>(a2);
+  const dim3 grid2(p.nch2, p.nrg2, s.Hkv);
+  switch (p.nw2) {
+    case 8: k_pass2<8><<<grid2, 512, 0, st>>>(a2); break;
+    case 4: k_pass2<4><<<grid2, 256, 0, st>>>(a2); break;
+    case 2: k_pass2<2><<<grid2, 128, 0, st>>>(a2); break;
+    default: k_pass2<1><<<grid2, 64, 0, st>>>(a2); break;
+  }
   record_stage(se, "pass2", st);
-  if (p.nrg > 1) {
+  if (p.nrg2 > 1) {
     const int64_t total = (int64_t)s.Hkv * s.n;
-    k_sum_rowgroups<<<(unsigned)((total + 255) / 256), 256, 0, st>>>(Spart, ws.S, total, p.nrg);
+    k_sum_rowgroups<<<(unsigned)((total + 255) / 256), 256, 0, st>>>(Spart, ws.S, total, p.nrg2);
     record_stage(se, "rowgroup_sum", st);
   }
   FoldArgs ao{s.n, p.Rg, s.Hkv, 1.0f / (float)s.G(), ws.rs, flagcount, fx, ws.S, ws.status};
