@@ -72,8 +72,8 @@ bool use_mfma(int dtype, int d, uint32_t flags) {
 // Run the scoring stages up to raw scores (ws.S) and row statistics.
 int run_scores(int dtype, const void* q, const void* k, const void* v, const Shape& s,
                const Workspace& ws, bool mfma, hipStream_t st, StageEvents* se = nullptr) {
-  hipError_t e = launch_clear_status(ws.status, st);
-  if (e != hipSuccess) return fail_hip(e, "clear status");
+  hipError_t e = launch_init(ws.status, ws.flagcount, ws.sel, s.Hkv, st);
+  if (e != hipSuccess) return fail_hip(e, "init");
   if (mfma) {
     e = launch_mfma_path(q, k, v, s, ws, st, se);
     if (e != hipSuccess) return fail_hip(e, "mfma path");
@@ -200,6 +200,7 @@ Workspace carve_workspace(void* base, const Shape& s, bool mfma) {
   ws.rs.flag = (int32_t*)take(sizeof(int32_t) * rows);
   ws.rs.a = (float*)take(sizeof(float) * rows * (size_t)s.d);
   ws.sel = take(select_scratch_bytes(s.n, s.Hkv));
+  ws.flagcount = (int32_t*)take(sizeof(int32_t) * (size_t)s.Hkv);
   if (mfma) {
     ws.rs.a_bf = (uint16_t*)take(sizeof(uint16_t) * rows * (size_t)s.d);
     ws.rs.na = (float*)take(sizeof(float) * rows);
@@ -331,7 +332,7 @@ int dropkv_select(const float* S, int64_t n, int32_t window, int32_t Hkv, int32_
   Workspace ws{};
   ws.status = (int32_t*)base;
   ws.sel = (char*)base + 256;
-  hipError_t e = launch_clear_status(ws.status, st);
+  hipError_t e = launch_init(ws.status, nullptr, ws.sel, Hkv, st);
   if (e == hipSuccess) e = launch_select(S, n, window, Hkv, pool_kernel, n_evict, out_scores, out_evict_idx, ws.status, ws.sel, st);
   if (e != hipSuccess) return fail_hip(e, "select");
   return sync_status(ws, st);

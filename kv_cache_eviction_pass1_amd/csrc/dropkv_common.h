@@ -39,6 +39,7 @@ struct Workspace {
   float* part;      // pass-1 partials (MFMA path)
   void* extra;      // further MFMA-path buffers (see mfma_extra_bytes)
   void* sel;        // select-stage scratch (see select_scratch_bytes)
+  int32_t* flagcount;  // [Hkv] rows per KV head whose argmax term comes from the fix-up
   int nchunks;      // pass-1 split count (MFMA path)
   size_t bytes;     // total bytes used
 };
@@ -54,7 +55,9 @@ struct Shape {
 Workspace carve_workspace(void* ws_base, const Shape& s, bool mfma);
 
 // Launchers. Each returns hipSuccess or the launch error.
-hipError_t launch_clear_status(int32_t* status, hipStream_t st);
+// Zeroes the status word, flagcount[Hkv] (may be null) and the select scratch.
+hipError_t launch_init(int32_t* status, int32_t* flagcount, void* sel_scratch, int32_t Hkv,
+                       hipStream_t st);
 hipError_t launch_generic_rows(int dtype, const void* q, const void* k, const void* v,
                                const Shape& s, const Workspace& ws, hipStream_t st);
 hipError_t launch_generic_scores(int dtype, const void* q, const void* k, const void* v,

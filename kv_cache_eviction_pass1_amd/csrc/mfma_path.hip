@@ -129,37 +129,41 @@ struct P1Args {
   float* nv;         // [Hkv][n]
 };
 
-__device__ __forceinline__ void p1_tile(const P1Args& A, char* kb, char* vb, int64_t tokbase_tile,
-                                        int wave, int lane, bool active, int64_t pos,
-                                        const bf16x8 (&qb)[8], float& m_run, float& l_run, int& best,
-                                        f32x16 (&O)[4], int g, int64_t chunk_end) {
-  const int h = lane >> 5, l32 = lane & 31;
-  // ||v_j||^2 for the tile's tokens (row group 0 only): 8 threads per token
-  if (blockIdx.y == 0) {
-    const int nthr = A.nw * 64;
-    for (int tt = threadIdx.x >> 3; tt < TT; tt += nthr >> 3) {
-      const int sl = threadIdx.x & 7;
-      float acc = 0.f;
+// ||v_j||^2 of one LDS tile, 8 threads per token (row group 0 writes them)
+__device__ __forceinline__ void p1_vnorms(const P1Args& A, const char* vb, int64_t tokbase_tile,
+                                          int g, int64_t chunk_end) {
+  const int nthr = A.nw * 64;
+  for (int tt = threadIdx.x >> 3; tt < TT; tt += nthr >> 3) {
+    const int sl = threadIdx.x & 7;
+    float acc = 0.f;
 #pragma unroll
-      for (int c = 0; c < 2; ++c) {
-        const int d0 = sl * 16 + c * 8;
-        const uint4 raw = *(const uint4*)(vb + toff(tt, d0));
-        const uint32_t wv[4] = {raw.x, raw.y, raw.z, raw.w};
+    for (int c = 0; c < 2; ++c) {
+      const int d0 = sl * 16 + c * 8;
+      const uint4 raw = *(const uint4*)(vb + toff(tt, d0));
+      const uint32_t wv[4] = {raw.x, raw.y, raw.z, raw.w};
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const float lo = __uint_as_float(wv[e] << 16), hi = __uint_as_float(wv[e] & 0xffff0000u);
-          acc = fmaf(lo, lo, acc);
-          acc = fmaf(hi, hi, acc);
-        }
+      for (int e = 0; e < 4; ++e) {
+        const float lo = __uint_as_float(wv[e] << 16), hi = __uint_as_float(wv[e] & 0xffff0000u);
+        acc = fmaf(lo, lo, acc);
+        acc = fmaf(hi, hi, acc);
       }
-      acc += __shfl_xor(acc, 1, 64);
-      acc += __shfl_xor(acc, 2, 64);
-      acc += __shfl_xor(acc, 4, 64);
-      const int64_t tok = tokbase_tile + tt;
-      if (sl == 0 && tok < chunk_end) A.nv[(size_t)g * A.n + tok] = acc;
     }
+    acc += __shfl_xor(acc, 1, 64);
+    acc += __shfl_xor(acc, 2, 64);
+    acc += __shfl_xor(acc, 4, 64);
+    const int64_t tok = tokbase_tile + tt;
+    if (sl == 0 && tok < chunk_end) A.nv[(size_t)g * A.n + tok] = acc;
   }
-  if (!active) return;
+}
+
+// One 64-token tile of pass 1 for this wave's 32 rows (S^T layout: lane = row).
+__device__ __forceinline__ void p1_tile(const P1Args& A, const char* kb, const char* vb,
+                                        int64_t tokbase_tile, int lane, int64_t pos,
+                                        const bf16x8 (&qb)[8], float& m_run, float& l_run, int& best,
+                                        f32x16 (&O)[4]) {
+  const int h = lane >> 5, l32 = lane & 31;
+  const int gi = lane >> 4, srcl = lane & 15;
+  const int dh = gi & 1;
 #pragma unroll
   for (int sub = 0; sub < 2; ++sub) {
     const char* kt = kb + sub * 32 * 256;
@@ -210,8 +214,6 @@ __device__ __forceinline__ void p1_tile(const P1Args& A, char* kb, char* vb, int
       for (int i = 0; i < 8; ++i) pb[s][i] = (__bf16)e[8 * s + i];
     // O^T[d][row] += V^T[d][tok] P^T[tok][row]; k-slot 8h+i of step s is token
     // 16s + 8(i/4) + 4h + i%4 (the order in which X^T left the values in this lane)
-    const int gi = lane >> 4, srcl = lane & 15;
-    const int dh = gi & 1;
     bf16x8 va[2][4];
 #pragma unroll
     for (int s = 0; s < 2; ++s) {
@@ -229,15 +231,25 @@ __device__ __forceinline__ void p1_tile(const P1Args& A, char* kb, char* vb, int
   }
 }
 
-__global__ __launch_bounds__(MAXW * 64) void k_pass1(P1Args A) {
-  __shared__ __attribute__((aligned(1024))) char kb0[TILE_BYTES];
-  __shared__ __attribute__((aligned(1024))) char vb0[TILE_BYTES];
-  __shared__ __attribute__((aligned(1024))) char kb1[TILE_BYTES];
-  __shared__ __attribute__((aligned(1024))) char vb1[TILE_BYTES];
+template <int N>
+__device__ __forceinline__ void p1_wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+}
+
+__device__ __forceinline__ void p1_lds_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
+template <int NW>
+__global__ __launch_bounds__(NW * 64) void k_pass1(P1Args A) {
+  __shared__ __attribute__((aligned(1024))) char kbuf[3][TILE_BYTES];
+  __shared__ __attribute__((aligned(1024))) char vbuf[3][TILE_BYTES];
+  constexpr int kDmaPerTile = 32 / NW;  // direct-to-LDS instructions per wave per tile
   const int chunk = blockIdx.x, rg = blockIdx.y, g = blockIdx.z;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int h = lane >> 5, l32 = lane & 31;
-  const int rb = rg * A.nw + wave;
+  const int rb = rg * NW + wave;
   const int row = rb * 32 + l32;
   const bool active = rb * 32 < A.Rg;
   const bool row_ok = row < A.Rg;
@@ -266,23 +278,29 @@ __global__ __launch_bounds__(MAXW * 64) void k_pass1(P1Args A) {
   for (int db = 0; db < 4; ++db) O[db] = f32x16{};
 
   if (ntiles > 0) {
-    issue_tile(kh, t0, A.n, kb0, wave, A.nw, lane);
-    issue_tile(vh, t0, A.n, vb0, wave, A.nw, lane);
+    issue_tile(kh, t0, A.n, kbuf[0], wave, NW, lane);
+    issue_tile(vh, t0, A.n, vbuf[0], wave, NW, lane);
   }
-  for (int it = 0; it < ntiles; it += 2) {
-    tile_barrier();
-    if (it + 1 < ntiles) {
-      issue_tile(kh, t0 + (int64_t)(it + 1) * TT, A.n, kb1, wave, A.nw, lane);
-      issue_tile(vh, t0 + (int64_t)(it + 1) * TT, A.n, vb1, wave, A.nw, lane);
+  if (ntiles > 1) {
+    issue_tile(kh, t0 + TT, A.n, kbuf[1], wave, NW, lane);
+    issue_tile(vh, t0 + TT, A.n, vbuf[1], wave, NW, lane);
+  }
+  // Per iteration the vector-memory ops are, in issue order: ||v||^2 stores of
+  // tile t, then the loads of tile t+2; so `vmcnt <= one tile's loads` at the
+  // top of iteration t+1 means tile t+1 has landed.
+  for (int t = 0; t < ntiles; ++t) {
+    const int64_t tb = t0 + (int64_t)t * TT;
+    if (t + 1 < ntiles) p1_wait_vmcnt<kDmaPerTile>(); else p1_wait_vmcnt<0>();
+    p1_lds_barrier();  // tile t in LDS for every wave; tile t-1's buffer is free
+    const char* kc = kbuf[t % 3];
+    const char* vc = vbuf[t % 3];
+    if (rg == 0) p1_vnorms(A, vc, tb, g, t1);
+    if (t + 2 < ntiles) {
+      const int nb = (t + 2) % 3;
+      issue_tile(kh, tb + 2 * TT, A.n, kbuf[nb], wave, NW, lane);
+      issue_tile(vh, tb + 2 * TT, A.n, vbuf[nb], wave, NW, lane);
     }
-    p1_tile(A, kb0, vb0, t0 + (int64_t)it * TT, wave, lane, active, pos, qb, m_run, l_run, best, O, g, t1);
-    if (it + 1 >= ntiles) break;
-    tile_barrier();
-    if (it + 2 < ntiles) {
-      issue_tile(kh, t0 + (int64_t)(it + 2) * TT, A.n, kb0, wave, A.nw, lane);
-      issue_tile(vh, t0 + (int64_t)(it + 2) * TT, A.n, vb0, wave, A.nw, lane);
-    }
-    p1_tile(A, kb1, vb1, t0 + (int64_t)(it + 1) * TT, wave, lane, active, pos, qb, m_run, l_run, best, O, g, t1);
+    if (active) p1_tile(A, kc, vc, tb, lane, pos, qb, m_run, l_run, best, O);
   }
   if (!active) return;
   const float l_tot = pair_sum(l_run);
@@ -325,22 +343,56 @@ __global__ __launch_bounds__(256) void k_merge(MergeArgs M) {
   if (row >= rows) return;
   const int g = (int)(row / M.Rg), r = (int)(row % M.Rg);
   const size_t cstride = (size_t)rows * PSTRIDE;
+  const float* prow = M.part + (size_t)row * PSTRIDE;
+  // lane c (< 64) holds chunk c's (m, l, best); more chunks fold in 64 at a time
   float mx = -INFINITY;
   int bt = -1;
-  for (int c = 0; c < M.nchunks; ++c) {
-    const float* pr = M.part + c * cstride + (size_t)row * PSTRIDE;
-    const float mc = pr[HD];
-    if (mc > mx) { mx = mc; bt = __float_as_int(pr[HD + 2]); }
+  for (int c0 = 0; c0 < M.nchunks; c0 += 64) {
+    const int c = c0 + lane;
+    const float mc = c < M.nchunks ? prow[c * cstride + HD] : -INFINITY;
+    float wm = mc;
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) wm = fmaxf(wm, __shfl_xor(wm, o, 64));
+    if (wm > mx) {
+      const unsigned long long hit = __builtin_amdgcn_ballot_w64(mc == wm);
+      const int first = __ffsll((long long)hit) - 1;  // lowest chunk attaining the max
+      const float bf = c < M.nchunks ? prow[c * cstride + HD + 2] : 0.f;
+      bt = __float_as_int(__shfl(bf, first, 64));
+      mx = wm;
+    }
   }
   float l = 0.f, a0 = 0.f, a1 = 0.f;
-  for (int c = 0; c < M.nchunks; ++c) {
-    const float* pr = M.part + c * cstride + (size_t)row * PSTRIDE;
-    const float mc = pr[HD];
-    const float s = (mc == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f((mc - mx) * M.c2);
-    l = fmaf(pr[HD + 1], s, l);
-    const float2 av = *(const float2*)(pr + 2 * lane);
-    a0 = fmaf(av.x, s, a0);
-    a1 = fmaf(av.y, s, a1);
+  for (int c0 = 0; c0 < M.nchunks; c0 += 64) {
+    const int c = c0 + lane;
+    const float mc = c < M.nchunks ? prow[c * cstride + HD] : -INFINITY;
+    const float lc = c < M.nchunks ? prow[c * cstride + HD + 1] : 0.f;
+    const float sc = (mc == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f((mc - mx) * M.c2);
+    float lw = lc * sc;
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) lw += __shfl_xor(lw, o, 64);
+    l += lw;
+    const int cn = (M.nchunks - c0) < 64 ? (M.nchunks - c0) : 64;
+    int cc = 0;
+    for (; cc + 8 <= cn; cc += 8) {
+      float2 av[8];
+      float sv[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        av[u] = *(const float2*)(prow + (size_t)(c0 + cc + u) * cstride + 2 * lane);
+        sv[u] = __shfl(sc, cc + u, 64);
+      }
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        a0 = fmaf(av[u].x, sv[u], a0);
+        a1 = fmaf(av[u].y, sv[u], a1);
+      }
+    }
+    for (; cc < cn; ++cc) {
+      const float2 av = *(const float2*)(prow + (size_t)(c0 + cc) * cstride + 2 * lane);
+      const float sv = __shfl(sc, cc, 64);
+      a0 = fmaf(av.x, sv, a0);
+      a1 = fmaf(av.y, sv, a1);
+    }
   }
   const float inv_l = 1.0f / l;
   const float x0 = a0 * inv_l, x1 = a1 * inv_l;
@@ -832,10 +884,6 @@ __global__ void k_sum_rowgroups(const float* __restrict__ Sp, float* __restrict_
   S[i] = s;
 }
 
-__global__ void k_zero_i32(int32_t* p, int count) {
-  const int i = blockIdx.x * blockDim.x + threadIdx.x;
-  if (i < count) p[i] = 0;
-}
 
 struct Plan {
   int Rg, RBt, nrg, nw, tiles, tpc1, nch1, tpc2, nch2;
@@ -846,8 +894,9 @@ Plan make_plan(const Shape& s) {
   Plan p{};
   p.Rg = s.G() * s.w;
   p.RBt = (p.Rg + 31) / 32;
-  p.nrg = (p.RBt + MAXW - 1) / MAXW;
-  p.nw = (p.RBt + p.nrg - 1) / p.nrg;
+  p.nw = MAXW;  // pass 1: 32 rows per wave, power-of-two waves per workgroup
+  while (p.nw > 1 && p.nw / 2 >= p.RBt) p.nw /= 2;
+  p.nrg = (p.RBt + p.nw - 1) / p.nw;
   p.tiles = (int)((s.n + TT - 1) / TT);
   // pass 1: about one workgroup per CU (partials cost HBM traffic)
   const int target1 = 256, target2 = 512;
@@ -883,7 +932,6 @@ size_t mfma_extra_bytes(const Shape& s) {
   size_t b = 0;
   b += sizeof(float) * (size_t)s.Hkv * s.n;                       // ||v||^2
   b += sizeof(float) * (size_t)FXC * s.Hkv * p.Rg * FXSTRIDE;     // fix-up partials
-  b += sizeof(int32_t) * (size_t)s.Hkv;                           // flag counts
   if (p.nrg2 > 1) b += sizeof(float) * (size_t)p.nrg2 * s.Hkv * s.n;  // row-group partial S
   return b + 4 * 256;
 }
@@ -896,15 +944,22 @@ hipError_t launch_mfma_path(const void* q, const void* k, const void* v, const S
   auto take = [&](size_t bytes) { char* r = extra; extra += (bytes + 255) / 256 * 256; return r; };
   float* nv = (float*)take(sizeof(float) * (size_t)s.Hkv * s.n);
   float* fx = (float*)take(sizeof(float) * (size_t)FXC * s.Hkv * p.Rg * FXSTRIDE);
-  int32_t* flagcount = (int32_t*)take(sizeof(int32_t) * (size_t)s.Hkv);
+  int32_t* flagcount = ws.flagcount;
   float* Spart = p.nrg2 > 1 ? (float*)take(sizeof(float) * (size_t)p.nrg2 * s.Hkv * s.n) : ws.S;
   const float c2 = kLog2e / sqrtf((float)HD);
 
-  k_zero_i32<<<(s.Hkv + 63) / 64, 64, 0, st>>>(flagcount, s.Hkv);
   P1Args a1{(const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v, s.n, s.w, p.Rg, p.nw,
             p.tpc1, s.Hkv, c2, ws.part, nv};
   record_stage(se, "start", st);
-  k_pass1<<<dim3(p.nch1, p.nrg, s.Hkv), p.nw * 64, 0, st>>>(a1);
+  {
+    const dim3 grid1(p.nch1, p.nrg, s.Hkv);
+    switch (p.nw) {
+      case 8: k_pass1<8><<<grid1, 512, 0, st>>>(a1); break;
+      case 4: k_pass1<4><<<grid1, 256, 0, st>>>(a1); break;
+      case 2: k_pass1<2><<<grid1, 128, 0, st>>>(a1); break;
+      default: k_pass1<1><<<grid1, 64, 0, st>>>(a1); break;
+    }
+  }
   record_stage(se, "pass1", st);
   MergeArgs am{(const uint16_t*)q, (const uint16_t*)k, ws.part, s.n, s.w, p.Rg, s.Hkv, p.nch1,
                c2, 1.0f / sqrtf((float)HD), ws.rs, flagcount, ws.status};

@@ -92,20 +92,30 @@ __device__ __forceinline__ bool last_to_arrive(SelState* st, int round, int nblk
 }
 
 // Finds the bin holding rank `rank` (1-based) in a global histogram; updates st.
-__device__ void pick_digit(const uint32_t* h, int bins, int shift, uint32_t digit_mask, SelState* st,
+template <int PER>
+__device__ void pick_digit(const uint32_t* h, int shift, uint32_t digit_mask, SelState* st,
                            int64_t rank, int64_t* wsum, uint32_t* sh_digit, int64_t* sh_rank) {
-  const int per = bins / kT;  // bins per thread (16 or 1)
+  uint32_t c[PER];
   int64_t loc = 0;
-  for (int i = 0; i < per; ++i) loc += ld_relaxed(h + threadIdx.x * per + i);
+#pragma unroll
+  for (int i = 0; i < PER; ++i) {
+    c[i] = ld_relaxed(h + threadIdx.x * PER + i);
+    loc += c[i];
+  }
   int64_t total;
   const int64_t before = wg_exclusive_scan(loc, wsum, total);
   if (before < rank && rank <= before + loc) {
     int64_t r = rank - before;
-    for (int i = 0; i < per; ++i) {
-      const int64_t c = ld_relaxed(h + threadIdx.x * per + i);
-      if (r <= c) { *sh_digit = (uint32_t)(threadIdx.x * per + i); *sh_rank = r; break; }
-      r -= c;
+    uint32_t dg = 0;
+    int64_t rr = r;
+    bool found = false;
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+      if (!found && r <= (int64_t)c[i]) { dg = threadIdx.x * PER + i; rr = r; found = true; }
+      if (!found) r -= c[i];
     }
+    *sh_digit = dg;
+    *sh_rank = rr;
   }
   __syncthreads();
   if (threadIdx.x == 0) {
@@ -121,6 +131,18 @@ __device__ __forceinline__ void load_keys(const SelArgs& A, int g, int b, uint32
 #pragma unroll
   for (int e = 0; e < kPer; ++e) {
     const int64_t j = j0 + e;
+    key[e] = (j < A.n) ? score_key(Pg[j]) : 0xffffffffu;
+  }
+}
+
+// Keys of a workgroup's range in strided order (element base + e*kT + tid):
+// coalesced loads; histogram and counting rounds do not depend on the order.
+__device__ __forceinline__ void load_keys_strided(const SelArgs& A, int g, int b, uint32_t (&key)[kPer]) {
+  const int64_t base = (int64_t)b * kChunk + threadIdx.x;
+  const float* Pg = A.P + (size_t)g * A.n;
+#pragma unroll
+  for (int e = 0; e < kPer; ++e) {
+    const int64_t j = base + (int64_t)e * kT;
     key[e] = (j < A.n) ? score_key(Pg[j]) : 0xffffffffu;
   }
 }
@@ -150,18 +172,18 @@ __global__ __launch_bounds__(kT) void k_sel_pool(SelArgs A) {
   __syncthreads();
   uint32_t key[kPer];
   bool nf = false;
-  const int64_t j0 = base + (int64_t)threadIdx.x * kPer;
 #pragma unroll
   for (int e = 0; e < kPer; ++e) {
-    const int64_t j = j0 + e;
+    const int li = e * kT + threadIdx.x;  // consecutive threads, consecutive tokens
+    const int64_t j = base + li;
     key[e] = 0xffffffffu;
     if (j < A.n) {
       float mx;
       if (in_lds) {
-        const int li = (int)(j - base) + half;
-        mx = sS[li];
+        const int c = li + half;
+        mx = sS[c];
         if (!finite_f(mx)) nf = true;
-        for (int t = li - half; t <= li + half; ++t) mx = fmaxf(mx, sS[t]);
+        for (int t = c - half; t <= c + half; ++t) mx = fmaxf(mx, sS[t]);
       } else {
         mx = Sg[j];
         if (!finite_f(mx)) nf = true;
@@ -189,7 +211,7 @@ __global__ __launch_bounds__(kT) void k_sel_pool(SelArgs A) {
   SelState* st = A.st + g;
   if (last_to_arrive(st, 0, A.nblk, &flag)) {
     if (threadIdx.x == 0) { st->prefix = 0; st->mask = 0; }
-    pick_digit(gh, kBins1, 20, 0xfffu, st, A.n_evict, wsum, &sh_digit, &sh_rank);
+    pick_digit<kBins1 / kT>(gh, 20, 0xfffu, st, A.n_evict, wsum, &sh_digit, &sh_rank);
   }
 }
 
@@ -211,7 +233,7 @@ __global__ __launch_bounds__(kT) void k_sel_refine(SelArgs A) {
   for (int i = threadIdx.x; i < BINS; i += kT) hist[i] = 0;
   __syncthreads();
   uint32_t key[kPer];
-  load_keys(A, g, b, key);
+  load_keys_strided(A, g, b, key);
 #pragma unroll
   for (int e = 0; e < kPer; ++e)
     if (key[e] != 0xffffffffu && (key[e] & mask) == prefix) atomicAdd(&hist[(key[e] >> SHIFT) & DMASK], 1u);
@@ -220,7 +242,7 @@ __global__ __launch_bounds__(kT) void k_sel_refine(SelArgs A) {
   for (int i = threadIdx.x; i < BINS; i += kT)
     if (hist[i]) atomicAdd(gh + i, hist[i]);
   if (last_to_arrive(st, ROUND, A.nblk, &flag)) {
-    pick_digit(gh, BINS, SHIFT, DMASK, st, rank, wsum, &sh_digit, &sh_rank);
+    pick_digit<BINS / kT>(gh, SHIFT, DMASK, st, rank, wsum, &sh_digit, &sh_rank);
     if (ROUND == 2 && threadIdx.x == 0) {
       st->tau = st->prefix;
       st->need = st->rank;
@@ -237,7 +259,7 @@ __global__ __launch_bounds__(kT) void k_sel_count(SelArgs A) {
   SelState* st = A.st + g;
   const uint32_t tau = ld_relaxed(&st->tau);
   uint32_t key[kPer];
-  load_keys(A, g, b, key);
+  load_keys_strided(A, g, b, key);
   int64_t less = 0, eq = 0;
 #pragma unroll
   for (int e = 0; e < kPer; ++e) {
@@ -250,18 +272,25 @@ __global__ __launch_bounds__(kT) void k_sel_count(SelArgs A) {
   int64_t* bcg = A.bc + (size_t)g * A.nblk * 4;
   if (threadIdx.x == 0) { bcg[4 * b] = tl; bcg[4 * b + 1] = te; }
   if (last_to_arrive(st, 3, A.nblk, &flag)) {
-    if (threadIdx.x == 0) {
-      const int64_t need = ld_relaxed64(&st->need);
-      int64_t out = 0, eqb = 0;
-      for (int i = 0; i < A.nblk; ++i) {
-        const int64_t l = ld_relaxed64(bcg + 4 * i), e = ld_relaxed64(bcg + 4 * i + 1);
-        int64_t take_eq = need - eqb;
-        take_eq = take_eq < 0 ? 0 : (take_eq > e ? e : take_eq);
-        bcg[4 * i + 2] = out;
+    // per-workgroup output offsets: taken_i = less_i + clamp(need - eq_before_i, 0, eq_i)
+    const int64_t need = ld_relaxed64(&st->need);
+    int64_t out_carry = 0, eq_carry = 0;
+    for (int i0 = 0; i0 < A.nblk; i0 += kT) {
+      const int i = i0 + threadIdx.x;
+      const int64_t l = i < A.nblk ? ld_relaxed64(bcg + 4 * i) : 0;
+      const int64_t e = i < A.nblk ? ld_relaxed64(bcg + 4 * i + 1) : 0;
+      int64_t etot;
+      const int64_t eqb = eq_carry + wg_exclusive_scan(e, wsum, etot);
+      int64_t take_eq = need - eqb;
+      take_eq = take_eq < 0 ? 0 : (take_eq > e ? e : take_eq);
+      int64_t ttot;
+      const int64_t outb = out_carry + wg_exclusive_scan(l + take_eq, wsum, ttot);
+      if (i < A.nblk) {
+        bcg[4 * i + 2] = outb;
         bcg[4 * i + 3] = eqb;
-        out += l + take_eq;
-        eqb += e;
       }
+      out_carry += ttot;
+      eq_carry += etot;
     }
   }
 }
@@ -302,18 +331,20 @@ __global__ __launch_bounds__(kT) void k_sel_write(SelArgs A) {
     }
 }
 
-__global__ void k_sel_clear(uint32_t* hist, SelState* st, int Hkv) {
+// Zeroes the status word, the per-head flag counts and the select scratch
+// (histograms and per-head selection state) in one launch.
+__global__ void k_init(int32_t* status, int32_t* flagcount, uint32_t* hist, SelState* st, int Hkv) {
   const int g = blockIdx.x;
   uint32_t* h = hist + (size_t)g * (kBins1 + kBins2 + kBins3);
   for (int i = threadIdx.x; i < kBins1 + kBins2 + kBins3; i += blockDim.x) h[i] = 0;
   if (threadIdx.x == 0) {
-    SelState s{};
-    st[g] = s;
+    SelState z{};
+    st[g] = z;
+    if (flagcount) flagcount[g] = 0;
+    if (g == 0) *status = 0;
   }
   (void)Hkv;
 }
-
-__global__ void k_clear_status(int32_t* status) { *status = 0; }
 
 }  // namespace
 
@@ -325,8 +356,31 @@ size_t select_scratch_bytes(int64_t n, int32_t Hkv) {
   return b + 256;
 }
 
-hipError_t launch_clear_status(int32_t* status, hipStream_t st) {
-  k_clear_status<<<1, 1, 0, st>>>(status);
+namespace {
+
+struct SelPtrs {
+  uint32_t* hist;
+  SelState* st;
+  int64_t* bc;
+};
+
+SelPtrs carve_sel(void* scratch, int32_t Hkv) {
+  SelPtrs q;
+  char* p = (char*)scratch;
+  q.hist = (uint32_t*)p;
+  p += (sizeof(uint32_t) * (size_t)Hkv * (kBins1 + kBins2 + kBins3) + 255) / 256 * 256;
+  q.st = (SelState*)p;
+  p += (sizeof(SelState) * (size_t)Hkv + 255) / 256 * 256;
+  q.bc = (int64_t*)p;
+  return q;
+}
+
+}  // namespace
+
+hipError_t launch_init(int32_t* status, int32_t* flagcount, void* sel_scratch, int32_t Hkv,
+                       hipStream_t st) {
+  const SelPtrs q = carve_sel(sel_scratch, Hkv);
+  k_init<<<Hkv, 256, 0, st>>>(status, flagcount, q.hist, q.st, Hkv);
   return hipGetLastError();
 }
 
@@ -342,15 +396,12 @@ hipError_t launch_select(const float* S, int64_t n, int32_t w, int32_t Hkv, int3
   A.w = w;
   A.pool_half = pool_kernel / 2;
   A.nblk = (int)((n + kChunk - 1) / kChunk);
-  char* p = (char*)scratch;
-  A.hist = (uint32_t*)p;
-  p += (sizeof(uint32_t) * (size_t)Hkv * (kBins1 + kBins2 + kBins3) + 255) / 256 * 256;
-  A.st = (SelState*)p;
-  p += (sizeof(SelState) * (size_t)Hkv + 255) / 256 * 256;
-  A.bc = (int64_t*)p;
+  const SelPtrs q = carve_sel(scratch, Hkv);
+  A.hist = q.hist;
+  A.st = q.st;
+  A.bc = q.bc;
   A.status = status;
   const dim3 grid(A.nblk, Hkv);
-  if (n_evict > 0) k_sel_clear<<<Hkv, 256, 0, st>>>(A.hist, A.st, Hkv);
   k_sel_pool<<<grid, kT, 0, st>>>(A);
   if (n_evict > 0) {
     k_sel_refine<1><<<grid, kT, 0, st>>>(A);
