@@ -32,6 +32,8 @@
 // operand reads and the transposing 8-byte reads on gfx950's 64-bank LDS).
 #include "dropkv_common.h"
 
+#include <type_traits>
+
 namespace dropkv {
 
 namespace {
@@ -44,7 +46,7 @@ constexpr int HD = 128;                  // head dim of this path
 constexpr int TT = 64;                   // tokens per LDS tile
 constexpr int TILE_BYTES = TT * HD * 2;  // 16 KiB per tensor per tile
 constexpr int MAXW = 8;                  // waves per workgroup (row blocks of 32)
-constexpr int PSTRIDE = HD + 4;          // floats per pass-1 partial (A[128], m, l, best, pad)
+constexpr int PSTRIDE = HD + 4;          // floats per pass-1 partial (A[128], m, l, best, mref)
 constexpr int FXC = 8;                   // token chunks of the fix-up pass
 constexpr int FXSTRIDE = HD + 2;         // floats per fix-up partial (sp, ps, D[128])
 
@@ -103,10 +105,13 @@ __device__ __forceinline__ uint16_t f32_to_bf16_rne(float x) {
 }
 
 // Issue direct-to-LDS loads of one 64-token tile of one tensor: 16 wave
-// instructions of 1 KiB (4 token rows each); instruction `inst` of `nw` waves.
+// instructions of 1 KiB (4 token rows each), instruction wave + i*NW of NW waves.
+template <int NW>
 __device__ __forceinline__ void issue_tile(const uint16_t* __restrict__ head, int64_t tok0, int64_t n,
-                                           char* lds, int wave, int nw, int lane) {
-  for (int inst = wave; inst < 16; inst += nw) {
+                                           char* lds, int wave, int lane) {
+#pragma unroll
+  for (int i = 0; i < 16 / NW; ++i) {
+    const int inst = wave + i * NW;
     const int row = inst * 4 + (lane >> 4);
     const int c = (lane & 15) ^ swz(row);
     int64_t tok = tok0 + row;
@@ -129,25 +134,52 @@ struct P1Args {
   float* nv;         // [Hkv][n]
 };
 
-// ||v_j||^2 of one LDS tile, 8 threads per token (row group 0 writes them)
+// Per-lane LDS byte offsets inside a tile, for the first 32-token subtile.
+// The swizzle only looks at the token index mod 16, so the second subtile
+// (+32 rows), the second 16-token MFMA step (+16 rows) and the buffer index
+// are plain additive constants that fold into the instructions' offset field.
+struct LdsOff {
+  int k[8];  // 16-byte operand chunks: token l%32, dims 16ks + 8(l/32) .. +7
+  int v[8];  // transposing reads: [2 db + second]
+};
+
+__device__ __forceinline__ LdsOff lds_offsets(int lane) {
+  const int h = lane >> 5, l32 = lane & 31, srcl = lane & 15, dh = (lane >> 4) & 1;
+  LdsOff o;
+#pragma unroll
+  for (int ks = 0; ks < 8; ++ks) o.k[ks] = toff(l32, ks * 16 + h * 8);
+  const int t0 = 4 * h + (srcl >> 2);
+#pragma unroll
+  for (int db = 0; db < 4; ++db) {
+    const int d = 32 * db + 16 * dh + 4 * (srcl & 3);
+    o.v[2 * db] = toff(t0, d);
+    o.v[2 * db + 1] = toff(t0 + 8, d);
+  }
+  return o;
+}
+
+// ||v_j||^2 of one LDS tile: 8 lanes per token, each squares 16 bf16 values
+// with two-term dot products (exact products, fp32 sums).
 __device__ __forceinline__ void p1_vnorms(const P1Args& A, const char* vb, int64_t tokbase_tile,
                                           int g, int64_t chunk_end) {
+  typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
   const int nthr = A.nw * 64;
   for (int tt = threadIdx.x >> 3; tt < TT; tt += nthr >> 3) {
     const int sl = threadIdx.x & 7;
-    float acc = 0.f;
+    float acc0 = 0.f, acc1 = 0.f;
 #pragma unroll
     for (int c = 0; c < 2; ++c) {
-      const int d0 = sl * 16 + c * 8;
-      const uint4 raw = *(const uint4*)(vb + toff(tt, d0));
+      const uint4 raw = *(const uint4*)(vb + toff(tt, sl * 16 + c * 8));
       const uint32_t wv[4] = {raw.x, raw.y, raw.z, raw.w};
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const float lo = __uint_as_float(wv[e] << 16), hi = __uint_as_float(wv[e] & 0xffff0000u);
-        acc = fmaf(lo, lo, acc);
-        acc = fmaf(hi, hi, acc);
+      for (int e = 0; e < 4; e += 2) {
+        const bf16x2 p0 = __builtin_bit_cast(bf16x2, wv[e]);
+        const bf16x2 p1 = __builtin_bit_cast(bf16x2, wv[e + 1]);
+        acc0 = __builtin_amdgcn_fdot2_f32_bf16(p0, p0, acc0, false);
+        acc1 = __builtin_amdgcn_fdot2_f32_bf16(p1, p1, acc1, false);
       }
     }
+    float acc = acc0 + acc1;
     acc += __shfl_xor(acc, 1, 64);
     acc += __shfl_xor(acc, 2, 64);
     acc += __shfl_xor(acc, 4, 64);
@@ -156,57 +188,72 @@ __device__ __forceinline__ void p1_vnorms(const P1Args& A, const char* vb, int64
   }
 }
 
-// One 64-token tile of pass 1 for this wave's 32 rows (S^T layout: lane = row).
-__device__ __forceinline__ void p1_tile(const P1Args& A, const char* kb, const char* vb,
-                                        int64_t tokbase_tile, int lane, int64_t pos,
-                                        const bf16x8 (&qb)[8], float& m_run, float& l_run, int& best,
-                                        f32x16 (&O)[4]) {
-  const int h = lane >> 5, l32 = lane & 31;
-  const int gi = lane >> 4, srcl = lane & 15;
-  const int dh = gi & 1;
+// Online-softmax state of one window row (one lane pair).
+//  m_true : largest logit seen so far (exact running max, for the merge);
+//  mref   : reference exponent (log2 domain) of l and O, i.e. l = sum 2^{x c - mref}.
+// The reference only moves when a logit exceeds it by more than kLazy (a
+// factor 2^8 in p), so the O/l rescale runs a few times per chunk instead of
+// at every new maximum; p stays below 2^8, well inside bf16 and fp32 range.
+constexpr float kLazy = 8.0f;
+
+struct P1State {
+  float m_true, mref, l;
+  int best;  // 32-token block of the first occurrence of m_true
+};
+
+// One 64-token tile of pass 1 for this wave's 32 rows (X^T layout: lane = row).
+template <bool MASK>
+__device__ __forceinline__ void p1_tile(float c2, const char* kb, const char* vb, int64_t tokbase_tile,
+                                        const LdsOff& off, int lane, int64_t pos,
+                                        const bf16x8 (&qb)[8], P1State& st, f32x16 (&O)[4]) {
+  const int h = lane >> 5;
 #pragma unroll
   for (int sub = 0; sub < 2; ++sub) {
     const char* kt = kb + sub * 32 * 256;
     const char* vt = vb + sub * 32 * 256;
     bf16x8 ka[8];
 #pragma unroll
-    for (int ks = 0; ks < 8; ++ks) ka[ks] = ld16(kt + toff(l32, ks * 16 + h * 8));
+    for (int ks = 0; ks < 8; ++ks) ka[ks] = ld16(kt + off.k[ks]);
     f32x16 x = {};
 #pragma unroll
     for (int ks = 0; ks < 8; ++ks) x = mfma(ka[ks], qb[ks], x);
     const int64_t tokbase = tokbase_tile + sub * 32;
-    if (tokbase + 31 > A.n - A.w) {  // causal tail / ragged end: mask invisible keys
+    if (MASK) {  // causal tail / ragged end: hide keys after this row's position
 #pragma unroll
       for (int vv = 0; vv < 16; ++vv) {
         const int64_t tok = tokbase + (vv >> 2) * 8 + 4 * h + (vv & 3);
         if (tok > pos) x[vv] = -INFINITY;
       }
     }
-    float mx = x[0];
+    float mx = fmaxf(fmaxf(x[0], x[1]), x[2]);
 #pragma unroll
-    for (int vv = 1; vv < 16; ++vv) mx = fmaxf(mx, x[vv]);
-    mx = pair_max(mx);
-    const bool up = mx > m_run;
-    if (up) best = (int)(tokbase >> 5);
-    if (__builtin_amdgcn_ballot_w64(up)) {
-      const float m_new = up ? mx : m_run;
-      const float alpha = (m_run == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f((m_run - m_new) * A.c2);
-      if (up) {
-        l_run *= alpha;
+    for (int vv = 3; vv < 15; vv += 2) mx = fmaxf(fmaxf(mx, x[vv]), x[vv + 1]);
+    mx = pair_max(fmaxf(mx, x[15]));
+    if (mx > st.m_true) {
+      st.m_true = mx;
+      st.best = (int)(tokbase >> 5);
+    }
+    if (__builtin_amdgcn_ballot_w64(mx * c2 > st.mref + kLazy)) {
+      const float nref = st.m_true * c2;
+      if (nref > st.mref) {
+        const float alpha = (st.mref == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(st.mref - nref);
+        st.l *= alpha;
 #pragma unroll
         for (int db = 0; db < 4; ++db) O[db] *= alpha;
+        st.mref = nref;
       }
-      m_run = m_new;
     }
-    const float mc = (m_run == -INFINITY) ? 0.f : m_run * A.c2;
+    const float nb = (st.mref == -INFINITY) ? 0.f : -st.mref;
     float e[16];
-    float ls = 0.f;
+    float ls0 = 0.f, ls1 = 0.f;
 #pragma unroll
-    for (int vv = 0; vv < 16; ++vv) {
-      e[vv] = __builtin_amdgcn_exp2f(fmaf(x[vv], A.c2, -mc));
-      ls += e[vv];
+    for (int vv = 0; vv < 16; vv += 2) {
+      e[vv] = __builtin_amdgcn_exp2f(fmaf(x[vv], c2, nb));
+      e[vv + 1] = __builtin_amdgcn_exp2f(fmaf(x[vv + 1], c2, nb));
+      ls0 += e[vv];
+      ls1 += e[vv + 1];
     }
-    l_run += ls;
+    st.l += ls0 + ls1;
     bf16x8 pb[2];
 #pragma unroll
     for (int s = 0; s < 2; ++s)
@@ -216,14 +263,10 @@ __device__ __forceinline__ void p1_tile(const P1Args& A, const char* kb, const c
     // 16s + 8(i/4) + 4h + i%4 (the order in which X^T left the values in this lane)
     bf16x8 va[2][4];
 #pragma unroll
-    for (int s = 0; s < 2; ++s) {
-      const int t0 = 16 * s + 4 * h + (srcl >> 2);
+    for (int s = 0; s < 2; ++s)
 #pragma unroll
-      for (int db = 0; db < 4; ++db) {
-        const int d = 32 * db + 16 * dh + 4 * (srcl & 3);
-        va[s][db] = tr_pair(vt + toff(t0, d), vt + toff(t0 + 8, d));
-      }
-    }
+      for (int db = 0; db < 4; ++db)
+        va[s][db] = tr_pair(vt + s * 16 * 256 + off.v[2 * db], vt + s * 16 * 256 + off.v[2 * db + 1]);
 #pragma unroll
     for (int s = 0; s < 2; ++s)
 #pragma unroll
@@ -232,13 +275,29 @@ __device__ __forceinline__ void p1_tile(const P1Args& A, const char* kb, const c
 }
 
 template <int N>
-__device__ __forceinline__ void p1_wait_vmcnt() {
+__device__ __forceinline__ void wait_vmcnt() {
   static_assert(N >= 0 && N < 64, "vmcnt range");
   __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
 }
 
-__device__ __forceinline__ void p1_lds_barrier() {
+// Workgroup barrier that orders LDS traffic only. __syncthreads() would also
+// wait for every outstanding vector-memory operation (vmcnt(0)), including
+// the direct-to-LDS loads of tiles still in flight; callers wait for the tile
+// they need with wait_vmcnt<N>() first.
+__device__ __forceinline__ void lds_barrier() {
   asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
+template <int B>
+using IntC = std::integral_constant<int, B>;
+
+// Tiles [0, n_clean) of a chunk end at or before the first window position,
+// so no row needs the causal mask there.
+__device__ __forceinline__ int clean_tiles(int64_t n, int w, int64_t t0, int ntiles) {
+  const int64_t lim = n - w + 1 - t0;  // tokens of this chunk visible to every row
+  if (lim <= 0) return 0;
+  const int64_t c = lim / TT;
+  return c < ntiles ? (int)c : ntiles;
 }
 
 template <int NW>
@@ -257,9 +316,12 @@ __global__ __launch_bounds__(NW * 64) void k_pass1(P1Args A) {
   int64_t t1 = t0 + (int64_t)A.tiles_per_chunk * TT;
   if (t1 > A.n) t1 = A.n;
   const int ntiles = (int)((t1 - t0 + TT - 1) / TT);
+  const int nclean = clean_tiles(A.n, A.w, t0, ntiles);
   const uint16_t* kh = A.k + (size_t)g * A.n * HD;
   const uint16_t* vh = A.v + (size_t)g * A.n * HD;
   const int64_t pos = A.n - A.w + ((row_ok ? row : 0) % A.w);
+  const float c2 = A.c2;
+  const LdsOff off = lds_offsets(lane);
 
   bf16x8 qb[8];
   {
@@ -271,39 +333,51 @@ __global__ __launch_bounds__(NW * 64) void k_pass1(P1Args A) {
       qb[ks] = t;
     }
   }
-  float m_run = -INFINITY, l_run = 0.f;
-  int best = -1;
+  P1State st{-INFINITY, -INFINITY, 0.f, -1};
   f32x16 O[4];
 #pragma unroll
   for (int db = 0; db < 4; ++db) O[db] = f32x16{};
 
   if (ntiles > 0) {
-    issue_tile(kh, t0, A.n, kbuf[0], wave, NW, lane);
-    issue_tile(vh, t0, A.n, vbuf[0], wave, NW, lane);
+    issue_tile<NW>(kh, t0, A.n, kbuf[0], wave, lane);
+    issue_tile<NW>(vh, t0, A.n, vbuf[0], wave, lane);
   }
   if (ntiles > 1) {
-    issue_tile(kh, t0 + TT, A.n, kbuf[1], wave, NW, lane);
-    issue_tile(vh, t0 + TT, A.n, vbuf[1], wave, NW, lane);
+    issue_tile<NW>(kh, t0 + TT, A.n, kbuf[1], wave, lane);
+    issue_tile<NW>(vh, t0 + TT, A.n, vbuf[1], wave, lane);
   }
-  // Per iteration the vector-memory ops are, in issue order: ||v||^2 stores of
+  // Per tile the vector-memory ops are, in issue order: ||v||^2 stores of
   // tile t, then the loads of tile t+2; so `vmcnt <= one tile's loads` at the
-  // top of iteration t+1 means tile t+1 has landed.
-  for (int t = 0; t < ntiles; ++t) {
+  // top of tile t+1 means tile t+1 has landed.
+  auto head = [&](int t, const char* vc, char* kn, char* vn) {
     const int64_t tb = t0 + (int64_t)t * TT;
-    if (t + 1 < ntiles) p1_wait_vmcnt<kDmaPerTile>(); else p1_wait_vmcnt<0>();
-    p1_lds_barrier();  // tile t in LDS for every wave; tile t-1's buffer is free
-    const char* kc = kbuf[t % 3];
-    const char* vc = vbuf[t % 3];
+    if (t + 1 < ntiles) wait_vmcnt<kDmaPerTile>(); else wait_vmcnt<0>();
+    lds_barrier();  // tile t in LDS for every wave; tile t-1's buffer is free
     if (rg == 0) p1_vnorms(A, vc, tb, g, t1);
     if (t + 2 < ntiles) {
-      const int nb = (t + 2) % 3;
-      issue_tile(kh, tb + 2 * TT, A.n, kbuf[nb], wave, NW, lane);
-      issue_tile(vh, tb + 2 * TT, A.n, vbuf[nb], wave, NW, lane);
+      issue_tile<NW>(kh, tb + 2 * TT, A.n, kn, wave, lane);
+      issue_tile<NW>(vh, tb + 2 * TT, A.n, vn, wave, lane);
     }
-    if (active) p1_tile(A, kc, vc, tb, lane, pos, qb, m_run, l_run, best, O);
+  };
+  auto clean = [&](auto bc, int t) {
+    constexpr int B = decltype(bc)::value;
+    constexpr int N2 = (B + 2) % 3;
+    head(t, vbuf[B], kbuf[N2], vbuf[N2]);
+    if (active) p1_tile<false>(c2, kbuf[B], vbuf[B], t0 + (int64_t)t * TT, off, lane, pos, qb, st, O);
+  };
+  int t = 0;
+  for (; t + 3 <= nclean; t += 3) {
+    clean(IntC<0>{}, t);
+    clean(IntC<1>{}, t + 1);
+    clean(IntC<2>{}, t + 2);
+  }
+  for (; t < ntiles; ++t) {  // at most two clean tiles, then the masked tail
+    const int b = t % 3, nb = (t + 2) % 3;
+    head(t, vbuf[b], kbuf[nb], vbuf[nb]);
+    if (active) p1_tile<true>(c2, kbuf[b], vbuf[b], t0 + (int64_t)t * TT, off, lane, pos, qb, st, O);
   }
   if (!active) return;
-  const float l_tot = pair_sum(l_run);
+  const float l_tot = pair_sum(st.l);
   if (!row_ok) return;
   float* pr = A.part + ((size_t)chunk * A.Hkv * A.Rg + (size_t)g * A.Rg + row) * PSTRIDE;
   // lane holds O^T rows d = 32db + 8i + 4h + (0..3) of this row's column
@@ -315,9 +389,10 @@ __global__ __launch_bounds__(NW * 64) void k_pass1(P1Args A) {
       *(float4*)(pr + 32 * db + 8 * i + 4 * h) = o;
     }
   if (h == 0) {
-    pr[HD] = m_run;
+    pr[HD] = st.m_true;
     pr[HD + 1] = l_tot;
-    pr[HD + 2] = __int_as_float(best);
+    pr[HD + 2] = __int_as_float(st.best);
+    pr[HD + 3] = st.mref;
   }
 }
 
@@ -364,9 +439,10 @@ __global__ __launch_bounds__(256) void k_merge(MergeArgs M) {
   float l = 0.f, a0 = 0.f, a1 = 0.f;
   for (int c0 = 0; c0 < M.nchunks; c0 += 64) {
     const int c = c0 + lane;
-    const float mc = c < M.nchunks ? prow[c * cstride + HD] : -INFINITY;
+    // chunk c holds l and A relative to its own reference exponent mref
+    const float rc = c < M.nchunks ? prow[c * cstride + HD + 3] : -INFINITY;
     const float lc = c < M.nchunks ? prow[c * cstride + HD + 1] : 0.f;
-    const float sc = (mc == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f((mc - mx) * M.c2);
+    const float sc = (rc == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(rc - mx * M.c2);
     float lw = lc * sc;
 #pragma unroll
     for (int o = 32; o > 0; o >>= 1) lw += __shfl_xor(lw, o, 64);
@@ -673,20 +749,6 @@ __device__ __forceinline__ void p2_combine(const P2Args& P, float (*red)[TT][2],
 
 enum { kTierSquare = 0, kTierSeries = 1, kTierExact = 2 };
 
-template <int N>
-__device__ __forceinline__ void wait_vmcnt() {
-  static_assert(N >= 0 && N < 64, "vmcnt range");
-  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
-}
-
-// Workgroup barrier that orders LDS traffic only. __syncthreads() would also
-// wait for every outstanding vector-memory operation (vmcnt(0)), including
-// the direct-to-LDS loads of tiles still in flight; callers wait for the tile
-// they need with wait_vmcnt<N>() first.
-__device__ __forceinline__ void lds_barrier() {
-  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
-}
-
 // ||v||^2 of the 64 tokens of a tile into LDS (one 4-byte direct-to-LDS load per lane)
 __device__ __forceinline__ void issue_nv(const float* nvh, int64_t tok0, int64_t n, float* lds, int lane) {
   int64_t tok = tok0 + lane;
@@ -694,18 +756,18 @@ __device__ __forceinline__ void issue_nv(const float* nvh, int64_t tok0, int64_t
   __builtin_amdgcn_global_load_lds((gbl_cvoid*)(nvh + tok), (lds_void*)lds, 4, 0, 0);
 }
 
+// Score terms of one subtile from y2 = 2 (x c - bias) = log2 p^2:
+// t1 = sum_rows r^2 C, t2 = sum_rows r^2 with r = p / (1 - p).
 template <int TIER>
-__device__ __forceinline__ void p2_values(const f32x16& X, const f32x16& C, const float (&bias)[16],
-                                          float c2, float& t1, float& t2) {
-  float a1 = 0.f, a2 = 0.f;
+__device__ __forceinline__ void p2_values(const float (&y2)[16], const f32x16& C, float& t1, float& t2) {
+  float a1 = 0.f, a2 = 0.f, b1 = 0.f, b2 = 0.f;
 #pragma unroll
   for (int vv = 0; vv < 16; ++vv) {
-    const float y = fmaf(X[vv], c2, -bias[vv]);
     float r2;
     if (TIER == kTierSquare) {
-      r2 = __builtin_amdgcn_exp2f(y + y);
+      r2 = __builtin_amdgcn_exp2f(y2[vv]);
     } else {
-      const float p = __builtin_amdgcn_exp2f(y);
+      const float p = __builtin_amdgcn_exp2f(0.5f * y2[vv]);
       if (TIER == kTierSeries) {
         r2 = (p * p) * fmaf(p, fmaf(p, 3.0f, 2.0f), 1.0f);
       } else {
@@ -713,11 +775,58 @@ __device__ __forceinline__ void p2_values(const f32x16& X, const f32x16& C, cons
         r2 = r * r;
       }
     }
-    a2 += r2;
-    a1 = fmaf(r2, C[vv], a1);
+    if (vv & 1) {
+      b2 += r2;
+      b1 = fmaf(r2, C[vv], b1);
+    } else {
+      a2 += r2;
+      a1 = fmaf(r2, C[vv], a1);
+    }
   }
-  t1 = a1;
-  t2 = a2;
+  t1 = a1 + b1;
+  t2 = a2 + b2;
+}
+
+// One 32-token subtile of the pass-2 fast path for this wave's 32 rows:
+// returns this wave's share of the score of token l%32 (valid in lanes < 32).
+template <bool MASK>
+__device__ __forceinline__ float p2_sub(const char* kt, const char* vt, float nvj, const LdsOff& off,
+                                        const bf16x8 (&qa)[8], const bf16x8 (&aa)[8],
+                                        const float (&nb2)[16], const float (&cinit)[16], float c2x2,
+                                        int64_t tok, const int (&rpos)[16]) {
+  bf16x8 kb[8], vb[8];
+#pragma unroll
+  for (int ks = 0; ks < 8; ++ks) kb[ks] = ld16(kt + off.k[ks]);
+#pragma unroll
+  for (int ks = 0; ks < 8; ++ks) vb[ks] = ld16(vt + off.k[ks]);
+  f32x16 X = {}, C;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) C[i] = cinit[i];
+#pragma unroll
+  for (int ks = 0; ks < 8; ++ks) X = mfma(qa[ks], kb[ks], X);
+#pragma unroll
+  for (int ks = 0; ks < 8; ++ks) C = mfma(aa[ks], vb[ks], C);
+  float y2[16];
+#pragma unroll
+  for (int vv = 0; vv < 16; ++vv) {
+    y2[vv] = fmaf(X[vv], c2x2, nb2[vv]);
+    if (MASK && tok > (int64_t)rpos[vv]) y2[vv] = -INFINITY;
+  }
+  float ym = fmaxf(fmaxf(y2[0], y2[1]), y2[2]);
+#pragma unroll
+  for (int vv = 3; vv < 15; vv += 2) ym = fmaxf(fmaxf(ym, y2[vv]), y2[vv + 1]);
+  ym = fmaxf(ym, y2[15]);
+  float q1, q2;
+  if (__builtin_amdgcn_ballot_w64(ym > -24.0f)) {
+    if (__builtin_amdgcn_ballot_w64(ym > -14.0f))
+      p2_values<kTierExact>(y2, C, q1, q2);
+    else
+      p2_values<kTierSeries>(y2, C, q1, q2);
+  } else {
+    p2_values<kTierSquare>(y2, C, q1, q2);
+  }
+  // this wave's rows: sum r^2 (||a||^2 - 2 a.v + ||v||^2) = ||v||^2 q2 - 2 q1
+  return pair_sum(fmaf(nvj, q2, -2.0f * q1));
 }
 
 template <int NW>
@@ -769,8 +878,8 @@ __global__ __launch_bounds__(NW * 64) void k_pass2(P2Args P) {
   }
 
   if (ntiles > 0) {
-    issue_tile(kh, t0, P.n, kbuf[0], wave, NW, lane);
-    issue_tile(vh, t0, P.n, vbuf[0], wave, NW, lane);
+    issue_tile<NW>(kh, t0, P.n, kbuf[0], wave, lane);
+    issue_tile<NW>(vh, t0, P.n, vbuf[0], wave, lane);
   }
 
   if (flagged) {
@@ -781,8 +890,8 @@ __global__ __launch_bounds__(NW * 64) void k_pass2(P2Args P) {
       const int b = it & 1;
       tile_barrier();
       if (it + 1 < ntiles) {
-        issue_tile(kh, t0 + (int64_t)(it + 1) * TT, P.n, kbuf[b ^ 1], wave, NW, lane);
-        issue_tile(vh, t0 + (int64_t)(it + 1) * TT, P.n, vbuf[b ^ 1], wave, NW, lane);
+        issue_tile<NW>(kh, t0 + (int64_t)(it + 1) * TT, P.n, kbuf[b ^ 1], wave, lane);
+        issue_tile<NW>(vh, t0 + (int64_t)(it + 1) * TT, P.n, vbuf[b ^ 1], wave, lane);
       }
       p2_tile(P, kbuf[b], vbuf[b], t0 + (int64_t)it * TT, lane, active, rb, qa, aa, bias, cinit,
               true, g, red, wave);
@@ -796,83 +905,79 @@ __global__ __launch_bounds__(NW * 64) void k_pass2(P2Args P) {
   // (K, V and ||v||^2), so `vmcnt <= one tile's loads` means the older tile landed
   if (ntiles > 0) issue_nv(nvg, t0, P.n, nvbuf[0], lane);
   if (ntiles > 1) {
-    issue_tile(kh, t0 + TT, P.n, kbuf[1], wave, NW, lane);
-    issue_tile(vh, t0 + TT, P.n, vbuf[1], wave, NW, lane);
+    issue_tile<NW>(kh, t0 + TT, P.n, kbuf[1], wave, lane);
+    issue_tile<NW>(vh, t0 + TT, P.n, vbuf[1], wave, lane);
     issue_nv(nvg, t0 + TT, P.n, nvbuf[1], lane);
   }
-  const float c2 = P.c2;
-  for (int t = 0; t < ntiles; ++t) {
-    const int64_t tb = t0 + (int64_t)t * TT;
-    if (t + 1 < ntiles) wait_vmcnt<kDmaPerTile>(); else wait_vmcnt<0>();
-    lds_barrier();  // tile t in LDS for every wave; tile t-1's buffer is free
-    if (t >= 1 && threadIdx.x < TT) {
-      // scores of tile t-1 (all waves wrote their partials before this barrier)
-      const int64_t tok = tb - TT + threadIdx.x;
+  const float c2x2 = 2.0f * P.c2;
+  const LdsOff off = lds_offsets(lane);
+  float nb2[16];
+  int rpos[16];  // window position of each of this lane's rows, relative to n - w
+#pragma unroll
+  for (int vv = 0; vv < 16; ++vv) {
+    nb2[vv] = -2.0f * bias[vv];
+    const int rr = rb * 32 + (vv >> 2) * 8 + 4 * h + (vv & 3);
+    rpos[vv] = rr % P.w;
+  }
+  const int nclean = clean_tiles(P.n, P.w, t0, ntiles);
+  // scores of tile t-1 (every wave wrote its partial before the barrier at tile t)
+  auto combine = [&](int tl, const float (*red)[TT]) {
+    if (threadIdx.x < TT) {
+      const int64_t tok = t0 + (int64_t)tl * TT + threadIdx.x;
       if (tok < t1) {
         float sacc = 0.f;
-        for (int wv = 0; wv < nwa; ++wv) sacc += red3[(t - 1) % 3][wv][threadIdx.x];
+        for (int wv = 0; wv < nwa; ++wv) sacc += red[wv][threadIdx.x];
         Sout[tok] = fmaxf(sacc, 0.0f) * P.invG;
       }
     }
+  };
+  auto head = [&](int t, const float (*red_prev)[TT], char* kn, char* vn, float* nvn) {
+    const int64_t tb = t0 + (int64_t)t * TT;
+    if (t + 1 < ntiles) wait_vmcnt<kDmaPerTile>(); else wait_vmcnt<0>();
+    lds_barrier();  // tile t in LDS for every wave; tile t-1's buffer is free
+    if (t >= 1) combine(t - 1, red_prev);
     if (t + 2 < ntiles) {
-      const int nb = (t + 2) % 3;
-      issue_tile(kh, tb + 2 * TT, P.n, kbuf[nb], wave, NW, lane);
-      issue_tile(vh, tb + 2 * TT, P.n, vbuf[nb], wave, NW, lane);
-      issue_nv(nvg, tb + 2 * TT, P.n, nvbuf[nb], lane);
+      issue_tile<NW>(kh, tb + 2 * TT, P.n, kn, wave, lane);
+      issue_tile<NW>(vh, tb + 2 * TT, P.n, vn, wave, lane);
+      issue_nv(nvg, tb + 2 * TT, P.n, nvn, lane);
     }
+  };
+  // token offset of this lane's column relative to n - w, for the causal mask
+  const int64_t tok_rel0 = t0 + l32 - (P.n - P.w);
+  auto clean = [&](auto bc, int t) {
+    constexpr int B = decltype(bc)::value;
+    constexpr int N2 = (B + 2) % 3;
+    head(t, red3[N2], kbuf[N2], vbuf[N2], nvbuf[N2]);
     if (active) {
-      const char* kc = kbuf[t % 3];
-      const char* vc = vbuf[t % 3];
 #pragma unroll
       for (int sub = 0; sub < 2; ++sub) {
-        const char* kt = kc + sub * 32 * 256;
-        const char* vt = vc + sub * 32 * 256;
-        bf16x8 kb[8], vb[8];
+        const float sw = p2_sub<false>(kbuf[B] + sub * 32 * 256, vbuf[B] + sub * 32 * 256,
+                                       nvbuf[B][sub * 32 + l32], off, qa, aa, nb2, cinit, c2x2, 0, rpos);
+        if (h == 0) red3[B][wave][sub * 32 + l32] = sw;
+      }
+    }
+  };
+  int t = 0;
+  for (; t + 3 <= nclean; t += 3) {
+    clean(IntC<0>{}, t);
+    clean(IntC<1>{}, t + 1);
+    clean(IntC<2>{}, t + 2);
+  }
+  for (; t < ntiles; ++t) {  // at most two clean tiles, then the masked tail
+    const int b = t % 3, nb = (t + 2) % 3;
+    head(t, red3[nb], kbuf[nb], vbuf[nb], nvbuf[nb]);
+    if (active) {
 #pragma unroll
-        for (int ks = 0; ks < 8; ++ks) kb[ks] = ld16(kt + toff(l32, ks * 16 + h * 8));
-#pragma unroll
-        for (int ks = 0; ks < 8; ++ks) vb[ks] = ld16(vt + toff(l32, ks * 16 + h * 8));
-        f32x16 X = {}, C;
-#pragma unroll
-        for (int i = 0; i < 16; ++i) C[i] = cinit[i];
-#pragma unroll
-        for (int ks = 0; ks < 8; ++ks) X = mfma(qa[ks], kb[ks], X);
-#pragma unroll
-        for (int ks = 0; ks < 8; ++ks) C = mfma(aa[ks], vb[ks], C);
-        const int64_t tok = tb + sub * 32 + l32;
-        float xm = -INFINITY;
-        if (tb + sub * 32 + 31 > P.n - P.w) {
-#pragma unroll
-          for (int vv = 0; vv < 16; ++vv) {
-            const int rr = rb * 32 + (vv >> 2) * 8 + 4 * h + (vv & 3);
-            if (tok > P.n - P.w + (rr % P.w)) X[vv] = -INFINITY;
-          }
-        }
-#pragma unroll
-        for (int vv = 0; vv < 16; ++vv) xm = fmaxf(xm, fmaf(X[vv], c2, -bias[vv]));
-        float q1, q2;
-        if (__builtin_amdgcn_ballot_w64(xm > -7.0f))
-          p2_values<kTierExact>(X, C, bias, c2, q1, q2);
-        else if (__builtin_amdgcn_ballot_w64(xm > -12.0f))
-          p2_values<kTierSeries>(X, C, bias, c2, q1, q2);
-        else
-          p2_values<kTierSquare>(X, C, bias, c2, q1, q2);
-        // this wave's rows: sum r^2 (||a||^2 - 2 a.v + ||v||^2) = ||v||^2 q2 - 2 q1
-        const float sw = pair_sum(fmaf(nvbuf[t % 3][sub * 32 + l32], q2, -2.0f * q1));
-        if (h == 0) red3[t % 3][wave][sub * 32 + l32] = sw;
+      for (int sub = 0; sub < 2; ++sub) {
+        const int64_t tok = tok_rel0 + (int64_t)t * TT + sub * 32;
+        const float sw = p2_sub<true>(kbuf[b] + sub * 32 * 256, vbuf[b] + sub * 32 * 256,
+                                      nvbuf[b][sub * 32 + l32], off, qa, aa, nb2, cinit, c2x2, tok, rpos);
+        if (h == 0) red3[b][wave][sub * 32 + l32] = sw;
       }
     }
   }
   __syncthreads();
-  if (ntiles >= 1 && threadIdx.x < TT) {
-    const int tl = ntiles - 1;
-    const int64_t tok = t0 + (int64_t)tl * TT + threadIdx.x;
-    if (tok < t1) {
-      float sacc = 0.f;
-      for (int wv = 0; wv < nwa; ++wv) sacc += red3[tl % 3][wv][threadIdx.x];
-      Sout[tok] = fmaxf(sacc, 0.0f) * P.invG;
-    }
-  }
+  if (ntiles >= 1) combine(ntiles - 1, red3[(ntiles - 1) % 3]);
 }
 
 // Sum of the row-group partial scores (only when a KV head has > 8 row blocks).
