@@ -121,6 +121,45 @@ __device__ __forceinline__ void issue_tile(const uint16_t* __restrict__ head, in
   }
 }
 
+// Lane byte offsets of the direct-to-LDS loads of a full tile: load i of wave
+// `wave` fetches token rows 4 (wave + i NW) .. +3, lane l the 16-byte chunk
+// (l%16) ^ swz(row) of row 4 (wave + i NW) + l/16. They do not depend on the
+// tile, so a full tile needs one uniform base address and no per-lane math.
+// (Kept for NW >= 4 only: with fewer waves the offsets would occupy 8-16
+// registers, and those narrow workgroups recompute them per load instead.)
+template <int NW>
+struct DmaOff {
+  static constexpr int kN = NW >= 4 ? 16 / NW : 1;
+  uint32_t g[kN];
+};
+
+template <int NW>
+__device__ __forceinline__ DmaOff<NW> dma_offsets(int wave, int lane) {
+  DmaOff<NW> o;
+#pragma unroll
+  for (int i = 0; i < DmaOff<NW>::kN; ++i) {
+    const int row = (wave + i * NW) * 4 + (lane >> 4);
+    o.g[i] = (uint32_t)(row * 256 + (((lane & 15) ^ swz(row)) << 4));
+  }
+  return o;
+}
+
+// Loads of tile [tok0, tok0 + 64): full tiles take the offset form, a tile
+// that runs past n clamps its rows (issue_tile).
+template <int NW>
+__device__ __forceinline__ void issue_any(const uint16_t* __restrict__ head, int64_t tok0, int64_t n,
+                                          char* lds, int wave, int lane, const DmaOff<NW>& o) {
+  if (NW >= 4 && tok0 + TT <= n) {
+    const char* base = (const char*)(head + tok0 * HD);
+#pragma unroll
+    for (int i = 0; i < DmaOff<NW>::kN; ++i)
+      __builtin_amdgcn_global_load_lds((gbl_cvoid*)(base + o.g[i]), (lds_void*)(lds + (wave + i * NW) * 1024),
+                                       16, 0, 0);
+  } else {
+    issue_tile<NW>(head, tok0, n, lds, wave, lane);
+  }
+}
+
 // ---------------------------------------------------------------------------- pass 1
 
 struct P1Args {
@@ -158,34 +197,54 @@ __device__ __forceinline__ LdsOff lds_offsets(int lane) {
   return o;
 }
 
-// ||v_j||^2 of one LDS tile: 8 lanes per token, each squares 16 bf16 values
-// with two-term dot products (exact products, fp32 sums).
-__device__ __forceinline__ void p1_vnorms(const P1Args& A, const char* vb, int64_t tokbase_tile,
-                                          int g, int64_t chunk_end) {
+// ||v_j||^2 of the tiles, computed by pass 1 while V sits in LDS: NW lanes
+// per token (wave w takes tokens (64/NW) w .. +64/NW-1), each squaring 128/NW
+// dims with two-term dot products (bf16 squares are exact, sums fp32), then
+// a swizzle reduction over the NW lanes. The LDS offsets are per-lane
+// constants.
+// (Narrow workgroups, NW < 4, recompute the offsets instead of keeping 8-16.)
+template <int NW>
+struct VnOff {
+  static constexpr int kN = NW >= 4 ? 16 / NW : 1;
+  int o[kN];
+};
+
+template <int NW>
+__device__ __forceinline__ int vn_offset(int wave, int lane, int c) {
+  return toff(wave * (TT / NW) + lane / NW, (lane % NW) * (HD / NW) + c * 8);
+}
+
+template <int NW>
+__device__ __forceinline__ VnOff<NW> vn_offsets(int wave, int lane) {
+  VnOff<NW> r;
+#pragma unroll
+  for (int c = 0; c < VnOff<NW>::kN; ++c) r.o[c] = vn_offset<NW>(wave, lane, c);
+  return r;
+}
+
+template <int NW>
+__device__ __forceinline__ void p1_vnorms(const char* vb, const VnOff<NW>& vo, float* nvtile, int64_t ntok,
+                                          int wave, int lane) {
   typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-  const int nthr = A.nw * 64;
-  for (int tt = threadIdx.x >> 3; tt < TT; tt += nthr >> 3) {
-    const int sl = threadIdx.x & 7;
-    float acc0 = 0.f, acc1 = 0.f;
+  float a0 = 0.f, a1 = 0.f;
 #pragma unroll
-    for (int c = 0; c < 2; ++c) {
-      const uint4 raw = *(const uint4*)(vb + toff(tt, sl * 16 + c * 8));
-      const uint32_t wv[4] = {raw.x, raw.y, raw.z, raw.w};
-#pragma unroll
-      for (int e = 0; e < 4; e += 2) {
-        const bf16x2 p0 = __builtin_bit_cast(bf16x2, wv[e]);
-        const bf16x2 p1 = __builtin_bit_cast(bf16x2, wv[e + 1]);
-        acc0 = __builtin_amdgcn_fdot2_f32_bf16(p0, p0, acc0, false);
-        acc1 = __builtin_amdgcn_fdot2_f32_bf16(p1, p1, acc1, false);
-      }
-    }
-    float acc = acc0 + acc1;
-    acc += __shfl_xor(acc, 1, 64);
-    acc += __shfl_xor(acc, 2, 64);
-    acc += __shfl_xor(acc, 4, 64);
-    const int64_t tok = tokbase_tile + tt;
-    if (sl == 0 && tok < chunk_end) A.nv[(size_t)g * A.n + tok] = acc;
+  for (int c = 0; c < 16 / NW; ++c) {
+    const int o = NW >= 4 ? vo.o[c < VnOff<NW>::kN ? c : 0] : vn_offset<NW>(wave, lane, c);
+    const uint4 u = *(const uint4*)(vb + o);
+    const bf16x2 p0 = __builtin_bit_cast(bf16x2, u.x), p1 = __builtin_bit_cast(bf16x2, u.y);
+    const bf16x2 p2 = __builtin_bit_cast(bf16x2, u.z), p3 = __builtin_bit_cast(bf16x2, u.w);
+    a0 = __builtin_amdgcn_fdot2_f32_bf16(p0, p0, a0, false);
+    a1 = __builtin_amdgcn_fdot2_f32_bf16(p1, p1, a1, false);
+    a0 = __builtin_amdgcn_fdot2_f32_bf16(p2, p2, a0, false);
+    a1 = __builtin_amdgcn_fdot2_f32_bf16(p3, p3, a1, false);
   }
+  float acc = a0 + a1;
+  // sum over the NW consecutive lanes of a token (swizzle xor within 32 lanes)
+  if (NW >= 2) acc += __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(acc), (1 << 10) | 0x1f));
+  if (NW >= 4) acc += __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(acc), (2 << 10) | 0x1f));
+  if (NW >= 8) acc += __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(acc), (4 << 10) | 0x1f));
+  const int tt = wave * (TT / NW) + lane / NW;
+  if (lane % NW == 0 && tt < ntok) nvtile[tt] = acc;
 }
 
 // Online-softmax state of one window row (one lane pair).
@@ -304,9 +363,11 @@ template <int NW>
 __global__ __launch_bounds__(NW * 64) void k_pass1(P1Args A) {
   __shared__ __attribute__((aligned(1024))) char kbuf[3][TILE_BYTES];
   __shared__ __attribute__((aligned(1024))) char vbuf[3][TILE_BYTES];
-  constexpr int kDmaPerTile = 32 / NW;  // direct-to-LDS instructions per wave per tile
+  // Per tile and wave: 32/NW direct-to-LDS loads, then (row group 0) one
+  // ||v||^2 store. vmcnt counts both, in issue order.
+  constexpr int kDmaPerTile = 32 / NW;
   const int chunk = blockIdx.x, rg = blockIdx.y, g = blockIdx.z;
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
   const int h = lane >> 5, l32 = lane & 31;
   const int rb = rg * NW + wave;
   const int row = rb * 32 + l32;
@@ -319,9 +380,12 @@ __global__ __launch_bounds__(NW * 64) void k_pass1(P1Args A) {
   const int nclean = clean_tiles(A.n, A.w, t0, ntiles);
   const uint16_t* kh = A.k + (size_t)g * A.n * HD;
   const uint16_t* vh = A.v + (size_t)g * A.n * HD;
+  float* nvh = A.nv + (size_t)g * A.n;
   const int64_t pos = A.n - A.w + ((row_ok ? row : 0) % A.w);
   const float c2 = A.c2;
   const LdsOff off = lds_offsets(lane);
+  const DmaOff<NW> doff = dma_offsets<NW>(wave, lane);
+  const VnOff<NW> vno = vn_offsets<NW>(wave, lane);
 
   bf16x8 qb[8];
   {
@@ -339,24 +403,24 @@ __global__ __launch_bounds__(NW * 64) void k_pass1(P1Args A) {
   for (int db = 0; db < 4; ++db) O[db] = f32x16{};
 
   if (ntiles > 0) {
-    issue_tile<NW>(kh, t0, A.n, kbuf[0], wave, lane);
-    issue_tile<NW>(vh, t0, A.n, vbuf[0], wave, lane);
+    issue_any<NW>(kh, t0, A.n, kbuf[0], wave, lane, doff);
+    issue_any<NW>(vh, t0, A.n, vbuf[0], wave, lane, doff);
   }
   if (ntiles > 1) {
-    issue_tile<NW>(kh, t0 + TT, A.n, kbuf[1], wave, lane);
-    issue_tile<NW>(vh, t0 + TT, A.n, vbuf[1], wave, lane);
+    issue_any<NW>(kh, t0 + TT, A.n, kbuf[1], wave, lane, doff);
+    issue_any<NW>(vh, t0 + TT, A.n, vbuf[1], wave, lane, doff);
   }
-  // Per tile the vector-memory ops are, in issue order: ||v||^2 stores of
+  // Per tile the vector-memory ops are, in issue order: the ||v||^2 store of
   // tile t, then the loads of tile t+2; so `vmcnt <= one tile's loads` at the
   // top of tile t+1 means tile t+1 has landed.
   auto head = [&](int t, const char* vc, char* kn, char* vn) {
     const int64_t tb = t0 + (int64_t)t * TT;
     if (t + 1 < ntiles) wait_vmcnt<kDmaPerTile>(); else wait_vmcnt<0>();
     lds_barrier();  // tile t in LDS for every wave; tile t-1's buffer is free
-    if (rg == 0) p1_vnorms(A, vc, tb, g, t1);
+    if (rg == 0) p1_vnorms<NW>(vc, vno, nvh + tb, t1 - tb, wave, lane);
     if (t + 2 < ntiles) {
-      issue_tile<NW>(kh, tb + 2 * TT, A.n, kn, wave, lane);
-      issue_tile<NW>(vh, tb + 2 * TT, A.n, vn, wave, lane);
+      issue_any<NW>(kh, tb + 2 * TT, A.n, kn, wave, lane, doff);
+      issue_any<NW>(vh, tb + 2 * TT, A.n, vn, wave, lane, doff);
     }
   };
   auto clean = [&](auto bc, int t) {
@@ -837,7 +901,7 @@ __global__ __launch_bounds__(NW * 64) void k_pass2(P2Args P) {
   __shared__ float nvbuf[3][TT];
   constexpr int kDmaPerTile = 32 / NW + 1;  // direct-to-LDS instructions per wave per tile
   const int chunk = blockIdx.x, rg = blockIdx.y, g = blockIdx.z;
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
   const int h = lane >> 5, l32 = lane & 31;
   const int rb = rg * NW + wave;
   const bool active = rb * 32 < P.Rg;
@@ -852,6 +916,7 @@ __global__ __launch_bounds__(NW * 64) void k_pass2(P2Args P) {
   const float* __restrict__ nvg = P.nv + (size_t)g * P.n;
   float* __restrict__ Sout = P.S + ((size_t)blockIdx.y * P.Hkv + g) * P.n;
   const bool flagged = P.flagcount[g] != 0;
+  const DmaOff<NW> doff = dma_offsets<NW>(wave, lane);
 
   bf16x8 qa[8], aa[8];
   float bias[16], cinit[16];
@@ -905,8 +970,8 @@ __global__ __launch_bounds__(NW * 64) void k_pass2(P2Args P) {
   // (K, V and ||v||^2), so `vmcnt <= one tile's loads` means the older tile landed
   if (ntiles > 0) issue_nv(nvg, t0, P.n, nvbuf[0], lane);
   if (ntiles > 1) {
-    issue_tile<NW>(kh, t0 + TT, P.n, kbuf[1], wave, lane);
-    issue_tile<NW>(vh, t0 + TT, P.n, vbuf[1], wave, lane);
+    issue_any<NW>(kh, t0 + TT, P.n, kbuf[1], wave, lane, doff);
+    issue_any<NW>(vh, t0 + TT, P.n, vbuf[1], wave, lane, doff);
     issue_nv(nvg, t0 + TT, P.n, nvbuf[1], lane);
   }
   const float c2x2 = 2.0f * P.c2;
@@ -937,8 +1002,8 @@ __global__ __launch_bounds__(NW * 64) void k_pass2(P2Args P) {
     lds_barrier();  // tile t in LDS for every wave; tile t-1's buffer is free
     if (t >= 1) combine(t - 1, red_prev);
     if (t + 2 < ntiles) {
-      issue_tile<NW>(kh, tb + 2 * TT, P.n, kn, wave, lane);
-      issue_tile<NW>(vh, tb + 2 * TT, P.n, vn, wave, lane);
+      issue_any<NW>(kh, tb + 2 * TT, P.n, kn, wave, lane, doff);
+      issue_any<NW>(vh, tb + 2 * TT, P.n, vn, wave, lane, doff);
       issue_nv(nvg, tb + 2 * TT, P.n, nvn, lane);
     }
   };
