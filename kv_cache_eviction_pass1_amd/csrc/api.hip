@@ -320,6 +320,7 @@ int dropkv_select(const float* S, int64_t n, int32_t window, int32_t Hkv, int32_
                   int64_t n_evict, float* out_scores, int64_t* out_evict_idx, void* stream) {
   g_last_error.clear();
   if (n < 2 || window < 1 || window >= n || Hkv < 1) return fail(DROPKV_ERR_INVALID, "need n >= 2, 1 <= window < n, Hkv >= 1");
+  if (n > ((int64_t)1 << 31) - 1) return fail(DROPKV_ERR_INVALID, "n must fit in int32 token indices");
   if (const char* m = validate_select(n, window, Hkv, pool_kernel, n_evict)) return fail(DROPKV_ERR_INVALID, m);
   if (!S || !is_device_ptr(S) || !out_scores || !is_device_ptr(out_scores))
     return fail(DROPKV_ERR_INVALID, "S and out_scores must be device pointers");

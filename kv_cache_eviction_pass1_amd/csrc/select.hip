@@ -8,31 +8,41 @@
 //
 // Scores are non-negative, so the IEEE-754 bit pattern of a pooled score,
 // read as uint32, orders exactly like its value (+inf = 0x7f800000 sorts
-// last). The n_evict-th smallest key tau is found by a radix select over
-// many workgroups per head: digits of 12, 12 and 8 bits; each round builds
-// LDS histograms, adds them into a global histogram, and the last workgroup
-// to arrive picks the digit. Then every workgroup counts its keys below and
-// equal to tau, the last one turns the counts into output offsets, and each
-// workgroup writes its share of the indices in order.
+// last). The n_evict-th smallest key tau is found by a radix select whose
+// digits are key bits 31..20, 19..8 and 7..0. Four kernels, with no
+// device-scope fence inside any of them (on this multi-XCD part a fence
+// writes back the L2, which costs far more than a kernel boundary):
+//   pool     many workgroups: pooled scores -> out_scores, histogram of digit 1;
+//   cand     many workgroups: each derives digit 1 from the histogram, counts
+//            per segment (16+ consecutive keys) the keys below digit 1's bin,
+//            and compacts the keys inside that bin (the candidates) with
+//            their indices, plus their digit-2 histogram;
+//   tau      one workgroup per head: digits 2 and 3 from the candidates give
+//            tau and `need` (how many keys equal to tau are evicted); the
+//            candidates complete the per-segment counts, and a scan turns
+//            them into per-segment output offsets;
+//   write    many workgroups: every segment writes its evicted indices.
 #include "dropkv_common.h"
 
 namespace dropkv {
 
 namespace {
 
-constexpr int kT = 256;           // threads per workgroup
-constexpr int kPer = 16;          // consecutive elements per thread
-constexpr int kChunk = kT * kPer; // elements per workgroup
-constexpr int kMaxHalo = 512;     // pooling halo held in LDS (larger kernels read global memory)
-constexpr int kBins1 = 4096, kBins2 = 4096, kBins3 = 256;
+constexpr int kT = 256;            // threads per workgroup (pool, cand, write)
+constexpr int kPer = 16;           // pool: elements per thread
+constexpr int kChunk = kT * kPer;  // pool: elements per workgroup
+constexpr int kMaxHalo = 512;      // pooling halo held in LDS (larger kernels read global memory)
+constexpr int kBins1 = 4096;       // digit 1: key bits 31..20
+constexpr int kBins2 = 4096;       // digit 2: key bits 19..8
+constexpr int kBins3 = 256;        // digit 3: key bits 7..0
+constexpr int kHistStride = kBins1 + kBins2 + 16;  // per head: hist1, hist2, candidate count
+constexpr int kFT = 1024;          // threads of the tau workgroup
+constexpr int kMaxSeg = 8192;      // segments per head (held in the tau workgroup's LDS)
 
 struct SelState {
-  uint32_t prefix;
-  uint32_t mask;
-  int64_t rank;   // 1-based rank still to find among keys matching prefix/mask
   uint32_t tau;
-  int64_t need;   // keys equal to tau that are evicted (lowest indices first)
-  uint32_t arrive[4];
+  uint32_t pad;
+  int64_t need;  // keys equal to tau that are evicted (lowest indices first)
 };
 
 struct SelArgs {
@@ -41,9 +51,13 @@ struct SelArgs {
   int64_t* idx;    // out_evict_idx
   int64_t n, n_evict;
   int w, pool_half, nblk;
-  uint32_t* hist;  // [Hkv][kBins1 + kBins2 + kBins3]
+  int seg, nseg;   // keys per segment, segments per head
+  bool vec4;       // P rows are 16-byte aligned (n % 4 == 0): vector loads
+  uint32_t* hist;  // [Hkv][kHistStride]: hist1, hist2, candidate count (zeroed by init)
   SelState* st;    // [Hkv]
-  int64_t* bc;     // [Hkv][nblk][4]: less, eq -> out offset, eq before
+  uint2* cand;     // [Hkv][n]: (key, index) of the candidates
+  uint32_t* seg_lt;   // [Hkv][nseg]: keys below digit 1's bin
+  int64_t* seg_off;   // [Hkv][nseg][2]: output offset, tau-equal keys before the segment
   int32_t* status;
 };
 
@@ -52,15 +66,10 @@ __device__ __forceinline__ uint32_t score_key(float x) {
   return (b & 0x80000000u) ? 0u : b;  // -0 (and any negative) sorts as +0
 }
 
-__device__ __forceinline__ uint32_t ld_relaxed(const uint32_t* p) {
-  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ int64_t ld_relaxed64(const int64_t* p) {
-  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-
-// Exclusive prefix sum over the workgroup (kT threads); also returns the total.
+// Exclusive prefix sum over a workgroup of T threads; also returns the total.
+template <int T>
 __device__ __forceinline__ int64_t wg_exclusive_scan(int64_t x, int64_t* wsum, int64_t& total) {
+  constexpr int NWV = T / 64;
   const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
   int64_t v = x;
 #pragma unroll
@@ -70,92 +79,75 @@ __device__ __forceinline__ int64_t wg_exclusive_scan(int64_t x, int64_t* wsum, i
   }
   if (lane == 63) wsum[wid] = v;
   __syncthreads();
-  int64_t before = 0;
-  for (int i = 0; i < wid; ++i) before += wsum[i];
-  total = wsum[0] + wsum[1] + wsum[2] + wsum[3];
+  int64_t before = 0, tot = 0;
+#pragma unroll
+  for (int i = 0; i < NWV; ++i) {
+    const int64_t s = wsum[i];
+    before += (i < wid) ? s : 0;
+    tot += s;
+  }
+  total = tot;
   __syncthreads();
   return before + v - x;
 }
 
-// Returns true in every thread of the last workgroup of head g to finish `round`.
-__device__ __forceinline__ bool last_to_arrive(SelState* st, int round, int nblk, int* flag) {
-  __threadfence();
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    const uint32_t t = atomicAdd(&st->arrive[round], 1u);
-    *flag = (t == (uint32_t)nblk - 1) ? 1 : 0;
-  }
-  __syncthreads();
-  const bool last = *flag != 0;
-  if (last) __threadfence();
-  return last;
-}
-
-// Finds the bin holding rank `rank` (1-based) in a global histogram; updates st.
-template <int PER>
-__device__ void pick_digit(const uint32_t* h, int shift, uint32_t digit_mask, SelState* st,
-                           int64_t rank, int64_t* wsum, uint32_t* sh_digit, int64_t* sh_rank) {
+// Bin of a histogram holding the key of 1-based rank `rank`, and the rank
+// inside that bin; the result is in *bin / *rin for every thread on return.
+template <int T, int NB>
+__device__ __forceinline__ void find_bin(const uint32_t* h, int64_t rank, int64_t* wsum, int* bin,
+                                         int64_t* rin) {
+  constexpr int PER = (NB + T - 1) / T;
   uint32_t c[PER];
   int64_t loc = 0;
 #pragma unroll
   for (int i = 0; i < PER; ++i) {
-    c[i] = ld_relaxed(h + threadIdx.x * PER + i);
+    const int b = threadIdx.x * PER + i;
+    c[i] = b < NB ? h[b] : 0u;
     loc += c[i];
   }
   int64_t total;
-  const int64_t before = wg_exclusive_scan(loc, wsum, total);
+  const int64_t before = wg_exclusive_scan<T>(loc, wsum, total);
   if (before < rank && rank <= before + loc) {
     int64_t r = rank - before;
-    uint32_t dg = 0;
-    int64_t rr = r;
-    bool found = false;
+    int found = -1;
+    int64_t rr = 0;
 #pragma unroll
     for (int i = 0; i < PER; ++i) {
-      if (!found && r <= (int64_t)c[i]) { dg = threadIdx.x * PER + i; rr = r; found = true; }
-      if (!found) r -= c[i];
+      if (found < 0 && r <= (int64_t)c[i]) {
+        found = threadIdx.x * PER + i;
+        rr = r;
+      }
+      if (found < 0) r -= c[i];
     }
-    *sh_digit = dg;
-    *sh_rank = rr;
+    *bin = found;
+    *rin = rr;
   }
   __syncthreads();
-  if (threadIdx.x == 0) {
-    st->prefix |= (*sh_digit & digit_mask) << shift;
-    st->mask |= digit_mask << shift;
-    st->rank = *sh_rank;
-  }
 }
 
-__device__ __forceinline__ void load_keys(const SelArgs& A, int g, int b, uint32_t (&key)[kPer]) {
-  const int64_t j0 = (int64_t)b * kChunk + (int64_t)threadIdx.x * kPer;
-  const float* Pg = A.P + (size_t)g * A.n;
+// Keys [j0, j0 + 16) of a head, 0xffffffff from `end` on.
+__device__ __forceinline__ void load16(const float* Pg, int64_t j0, int64_t end, bool vec4, uint32_t (&key)[16]) {
+  if (vec4 && j0 + 16 <= end) {
 #pragma unroll
-  for (int e = 0; e < kPer; ++e) {
-    const int64_t j = j0 + e;
-    key[e] = (j < A.n) ? score_key(Pg[j]) : 0xffffffffu;
-  }
-}
-
-// Keys of a workgroup's range in strided order (element base + e*kT + tid):
-// coalesced loads; histogram and counting rounds do not depend on the order.
-__device__ __forceinline__ void load_keys_strided(const SelArgs& A, int g, int b, uint32_t (&key)[kPer]) {
-  const int64_t base = (int64_t)b * kChunk + threadIdx.x;
-  const float* Pg = A.P + (size_t)g * A.n;
+    for (int q = 0; q < 4; ++q) {
+      const float4 f = *(const float4*)(Pg + j0 + 4 * q);
+      key[4 * q] = score_key(f.x);
+      key[4 * q + 1] = score_key(f.y);
+      key[4 * q + 2] = score_key(f.z);
+      key[4 * q + 3] = score_key(f.w);
+    }
+  } else {
 #pragma unroll
-  for (int e = 0; e < kPer; ++e) {
-    const int64_t j = base + (int64_t)e * kT;
-    key[e] = (j < A.n) ? score_key(Pg[j]) : 0xffffffffu;
+    for (int e = 0; e < 16; ++e) key[e] = (j0 + e < end) ? score_key(Pg[j0 + e]) : 0xffffffffu;
   }
 }
 
-// Round 1: pool + protect (writes out_scores) and the histogram of key bits 31..20.
+// Pool + protect (writes out_scores) and the histogram of digit 1.
 __global__ __launch_bounds__(kT) void k_sel_pool(SelArgs A) {
   const int b = blockIdx.x, g = blockIdx.y;
   __shared__ float sS[kChunk + 2 * kMaxHalo];
   __shared__ uint32_t hist[kBins1];
-  __shared__ int64_t wsum[4];
-  __shared__ int flag, bad;
-  __shared__ uint32_t sh_digit;
-  __shared__ int64_t sh_rank;
+  __shared__ int bad;
   const float* Sg = A.S + (size_t)g * A.n;
   float* Pg = A.P + (size_t)g * A.n;
   const int64_t base = (int64_t)b * kChunk;
@@ -205,188 +197,233 @@ __global__ __launch_bounds__(kT) void k_sel_pool(SelArgs A) {
   __syncthreads();
   if (threadIdx.x == 0 && bad) atomicOr(A.status, kStatusNonFinite);
   if (A.n_evict <= 0) return;
-  uint32_t* gh = A.hist + (size_t)g * (kBins1 + kBins2 + kBins3);
+  uint32_t* gh = A.hist + (size_t)g * kHistStride;
   for (int i = threadIdx.x; i < kBins1; i += kT)
     if (hist[i]) atomicAdd(gh + i, hist[i]);
-  SelState* st = A.st + g;
-  if (last_to_arrive(st, 0, A.nblk, &flag)) {
-    if (threadIdx.x == 0) { st->prefix = 0; st->mask = 0; }
-    pick_digit<kBins1 / kT>(gh, 20, 0xfffu, st, A.n_evict, wsum, &sh_digit, &sh_rank);
-  }
 }
 
-// Rounds 2 and 3: histogram of the next digit among keys matching the prefix.
-template <int ROUND>
-__global__ __launch_bounds__(kT) void k_sel_refine(SelArgs A) {
-  constexpr int BINS = ROUND == 1 ? kBins2 : kBins3;
-  constexpr int SHIFT = ROUND == 1 ? 8 : 0;
-  constexpr uint32_t DMASK = ROUND == 1 ? 0xfffu : 0xffu;
-  const int b = blockIdx.x, g = blockIdx.y;
-  __shared__ uint32_t hist[BINS];
-  __shared__ int64_t wsum[4];
-  __shared__ int flag;
-  __shared__ uint32_t sh_digit;
-  __shared__ int64_t sh_rank;
-  SelState* st = A.st + g;
-  const uint32_t prefix = ld_relaxed(&st->prefix), mask = ld_relaxed(&st->mask);
-  const int64_t rank = ld_relaxed64(&st->rank);
-  for (int i = threadIdx.x; i < BINS; i += kT) hist[i] = 0;
-  __syncthreads();
-  uint32_t key[kPer];
-  load_keys_strided(A, g, b, key);
+// Per segment: keys below digit 1's bin; the bin's keys become candidates.
+__global__ __launch_bounds__(kT) void k_sel_cand(SelArgs A) {
+  const int g = blockIdx.y;
+  const int s = blockIdx.x * kT + threadIdx.x;
+  __shared__ uint32_t hist2[kBins2];
+  __shared__ int64_t wsum[kT / 64];
+  __shared__ int sh_bin;
+  __shared__ int64_t sh_rin;
+  __shared__ uint32_t sh_base;
+  uint32_t* gh = A.hist + (size_t)g * kHistStride;
+  for (int i = threadIdx.x; i < kBins2; i += kT) hist2[i] = 0;
+  find_bin<kT, kBins1>(gh, A.n_evict, wsum, &sh_bin, &sh_rin);
+  const uint32_t d1 = (uint32_t)sh_bin;
+  const float* Pg = A.P + (size_t)g * A.n;
+  const int64_t j0 = (int64_t)s * A.seg;
+  const int64_t j1 = (s < A.nseg) ? ((j0 + A.seg < A.n) ? j0 + A.seg : A.n) : j0;
+  uint32_t lt = 0, nc = 0;
+  for (int64_t c0 = j0; c0 < j1; c0 += 16) {
+    uint32_t key[16];
+    load16(Pg, c0, j1, A.vec4, key);
 #pragma unroll
-  for (int e = 0; e < kPer; ++e)
-    if (key[e] != 0xffffffffu && (key[e] & mask) == prefix) atomicAdd(&hist[(key[e] >> SHIFT) & DMASK], 1u);
-  __syncthreads();
-  uint32_t* gh = A.hist + (size_t)g * (kBins1 + kBins2 + kBins3) + (ROUND == 1 ? kBins1 : kBins1 + kBins2);
-  for (int i = threadIdx.x; i < BINS; i += kT)
-    if (hist[i]) atomicAdd(gh + i, hist[i]);
-  if (last_to_arrive(st, ROUND, A.nblk, &flag)) {
-    pick_digit<BINS / kT>(gh, SHIFT, DMASK, st, rank, wsum, &sh_digit, &sh_rank);
-    if (ROUND == 2 && threadIdx.x == 0) {
-      st->tau = st->prefix;
-      st->need = st->rank;
-    }
-  }
-}
-
-// Counts keys below / equal to tau per workgroup; the last workgroup turns the
-// counts into per-workgroup output offsets and "equal keys before" counts.
-__global__ __launch_bounds__(kT) void k_sel_count(SelArgs A) {
-  const int b = blockIdx.x, g = blockIdx.y;
-  __shared__ int64_t wsum[4];
-  __shared__ int flag;
-  SelState* st = A.st + g;
-  const uint32_t tau = ld_relaxed(&st->tau);
-  uint32_t key[kPer];
-  load_keys_strided(A, g, b, key);
-  int64_t less = 0, eq = 0;
-#pragma unroll
-  for (int e = 0; e < kPer; ++e) {
-    less += (key[e] < tau) ? 1 : 0;
-    eq += (key[e] == tau) ? 1 : 0;
-  }
-  int64_t tl, te;
-  (void)wg_exclusive_scan(less, wsum, tl);
-  (void)wg_exclusive_scan(eq, wsum, te);
-  int64_t* bcg = A.bc + (size_t)g * A.nblk * 4;
-  if (threadIdx.x == 0) { bcg[4 * b] = tl; bcg[4 * b + 1] = te; }
-  if (last_to_arrive(st, 3, A.nblk, &flag)) {
-    // per-workgroup output offsets: taken_i = less_i + clamp(need - eq_before_i, 0, eq_i)
-    const int64_t need = ld_relaxed64(&st->need);
-    int64_t out_carry = 0, eq_carry = 0;
-    for (int i0 = 0; i0 < A.nblk; i0 += kT) {
-      const int i = i0 + threadIdx.x;
-      const int64_t l = i < A.nblk ? ld_relaxed64(bcg + 4 * i) : 0;
-      const int64_t e = i < A.nblk ? ld_relaxed64(bcg + 4 * i + 1) : 0;
-      int64_t etot;
-      const int64_t eqb = eq_carry + wg_exclusive_scan(e, wsum, etot);
-      int64_t take_eq = need - eqb;
-      take_eq = take_eq < 0 ? 0 : (take_eq > e ? e : take_eq);
-      int64_t ttot;
-      const int64_t outb = out_carry + wg_exclusive_scan(l + take_eq, wsum, ttot);
-      if (i < A.nblk) {
-        bcg[4 * i + 2] = outb;
-        bcg[4 * i + 3] = eqb;
+    for (int e = 0; e < 16; ++e) {
+      if (key[e] == 0xffffffffu) continue;
+      const uint32_t top = key[e] >> 20;
+      lt += top < d1 ? 1u : 0u;
+      if (top == d1) {
+        ++nc;
+        atomicAdd(&hist2[(key[e] >> 8) & 0xfffu], 1u);
       }
-      out_carry += ttot;
-      eq_carry += etot;
     }
+  }
+  if (s < A.nseg) A.seg_lt[(size_t)g * A.nseg + s] = lt;
+  int64_t total;
+  const int64_t before = wg_exclusive_scan<kT>(nc, wsum, total);
+  if (threadIdx.x == 0 && total > 0) sh_base = atomicAdd(gh + kBins1 + kBins2, (uint32_t)total);
+  __syncthreads();
+  if (nc > 0) {
+    uint2* cg = A.cand + (size_t)g * A.n;
+    uint32_t pos = sh_base + (uint32_t)before;
+    for (int64_t c0 = j0; c0 < j1; c0 += 16) {
+      uint32_t key[16];
+      load16(Pg, c0, j1, A.vec4, key);
+#pragma unroll
+      for (int e = 0; e < 16; ++e)
+        if (key[e] != 0xffffffffu && (key[e] >> 20) == d1) cg[pos++] = make_uint2(key[e], (uint32_t)(c0 + e));
+    }
+  }
+  if (total > 0) {
+    uint32_t* gh2 = gh + kBins1;
+    for (int i = threadIdx.x; i < kBins2; i += kT)
+      if (hist2[i]) atomicAdd(gh2 + i, hist2[i]);
   }
 }
 
-// Writes the evicted indices of each workgroup's range, in index order.
-__global__ __launch_bounds__(kT) void k_sel_write(SelArgs A) {
-  const int b = blockIdx.x, g = blockIdx.y;
-  __shared__ int64_t wsum[4];
-  SelState* st = A.st + g;
-  const uint32_t tau = ld_relaxed(&st->tau);
-  const int64_t need = ld_relaxed64(&st->need);
-  const int64_t* bcg = A.bc + (size_t)g * A.nblk * 4;
-  const int64_t out0 = ld_relaxed64(bcg + 4 * b + 2), eq0 = ld_relaxed64(bcg + 4 * b + 3);
-  uint32_t key[kPer];
-  load_keys(A, g, b, key);
-  int64_t eq = 0;
-#pragma unroll
-  for (int e = 0; e < kPer; ++e) eq += (key[e] == tau) ? 1 : 0;
-  int64_t tot;
-  int64_t eq_before = eq0 + wg_exclusive_scan(eq, wsum, tot);
-  bool take[kPer];
-  int64_t nt = 0;
-#pragma unroll
-  for (int e = 0; e < kPer; ++e) {
-    bool t = key[e] < tau;
-    if (key[e] == tau) { t = eq_before < need; ++eq_before; }
-    take[e] = t;
-    nt += t ? 1 : 0;
-  }
-  int64_t pos = out0 + wg_exclusive_scan(nt, wsum, tot);
-  int64_t* og = A.idx + (size_t)g * A.n_evict;
-  const int64_t j0 = (int64_t)b * kChunk + (int64_t)threadIdx.x * kPer;
-#pragma unroll
-  for (int e = 0; e < kPer; ++e)
-    if (take[e]) {
-      if (pos < A.n_evict) og[pos] = j0 + e;
-      ++pos;
-    }
-}
-
-// Zeroes the status word, the per-head flag counts and the select scratch
-// (histograms and per-head selection state) in one launch.
-__global__ void k_init(int32_t* status, int32_t* flagcount, uint32_t* hist, SelState* st, int Hkv) {
+// tau, need and the per-segment output offsets of one head.
+__global__ __launch_bounds__(kFT) void k_sel_tau(SelArgs A) {
   const int g = blockIdx.x;
-  uint32_t* h = hist + (size_t)g * (kBins1 + kBins2 + kBins3);
-  for (int i = threadIdx.x; i < kBins1 + kBins2 + kBins3; i += blockDim.x) h[i] = 0;
+  __shared__ uint32_t slt[kMaxSeg];
+  __shared__ uint32_t seq[kMaxSeg];
+  __shared__ uint32_t hist3[kBins3];
+  __shared__ int64_t wsum[kFT / 64];
+  __shared__ int sh_bin;
+  __shared__ int64_t sh_rin;
+  const uint32_t* gh = A.hist + (size_t)g * kHistStride;
+  find_bin<kFT, kBins1>(gh, A.n_evict, wsum, &sh_bin, &sh_rin);
+  const uint32_t d1 = (uint32_t)sh_bin;
+  const int64_t r1 = sh_rin;
+  for (int i = threadIdx.x; i < kBins3; i += kFT) hist3[i] = 0;
+  find_bin<kFT, kBins2>(gh + kBins1, r1, wsum, &sh_bin, &sh_rin);
+  const uint32_t d2 = (uint32_t)sh_bin;
+  const int64_t r2 = sh_rin;
+  const uint32_t nc = gh[kBins1 + kBins2];
+  const uint2* cg = A.cand + (size_t)g * A.n;
+  for (uint32_t i = threadIdx.x; i < nc; i += kFT) {
+    const uint32_t key = cg[i].x;
+    if (((key >> 8) & 0xfffu) == d2) atomicAdd(&hist3[key & 0xffu], 1u);
+  }
+  __syncthreads();
+  find_bin<kFT, kBins3>(hist3, r2, wsum, &sh_bin, &sh_rin);
+  const uint32_t tau = (d1 << 20) | (d2 << 8) | (uint32_t)sh_bin;
+  const int64_t need = sh_rin;
   if (threadIdx.x == 0) {
-    SelState z{};
-    st[g] = z;
+    A.st[g].tau = tau;
+    A.st[g].need = need;
+  }
+  // per-segment counts: below tau = below digit 1's bin + candidates below tau
+  const uint32_t* sl = A.seg_lt + (size_t)g * A.nseg;
+  for (int s = threadIdx.x; s < A.nseg; s += kFT) {
+    slt[s] = sl[s];
+    seq[s] = 0;
+  }
+  __syncthreads();
+  for (uint32_t i = threadIdx.x; i < nc; i += kFT) {
+    const uint2 c = cg[i];
+    const int s = (int)(c.y / (uint32_t)A.seg);
+    if (c.x < tau) atomicAdd(&slt[s], 1u);
+    else if (c.x == tau) atomicAdd(&seq[s], 1u);
+  }
+  __syncthreads();
+  // thread t owns segments [t spt, (t+1) spt): offsets by one workgroup scan
+  const int spt = (A.nseg + kFT - 1) / kFT;
+  const int s0 = threadIdx.x * spt;
+  int64_t l = 0, e = 0;
+  for (int s = s0; s < s0 + spt && s < A.nseg; ++s) {
+    l += slt[s];
+    e += seq[s];
+  }
+  int64_t tot;
+  // both counts are below 2^31: one scan of (eq << 32 | lt)
+  const int64_t pk = wg_exclusive_scan<kFT>((e << 32) | l, wsum, tot);
+  int64_t lb = pk & 0xffffffffLL, eb = pk >> 32;
+  int64_t* so = A.seg_off + (size_t)g * A.nseg * 2;
+  for (int s = s0; s < s0 + spt && s < A.nseg; ++s) {
+    const int64_t taken_eq = eb < need ? eb : need;
+    so[2 * s] = lb + taken_eq;
+    so[2 * s + 1] = eb;
+    lb += slt[s];
+    eb += seq[s];
+  }
+}
+
+// Writes the evicted indices of each segment, in index order.
+__global__ __launch_bounds__(kT) void k_sel_write(SelArgs A) {
+  const int g = blockIdx.y;
+  const int s = blockIdx.x * kT + threadIdx.x;
+  if (s >= A.nseg) return;
+  const uint32_t tau = A.st[g].tau;
+  const int64_t need = A.st[g].need;
+  const int64_t* so = A.seg_off + ((size_t)g * A.nseg + s) * 2;
+  int64_t pos = so[0], eqb = so[1];
+  const float* Pg = A.P + (size_t)g * A.n;
+  int64_t* og = A.idx + (size_t)g * A.n_evict;
+  const int64_t j0 = (int64_t)s * A.seg;
+  const int64_t j1 = (j0 + A.seg < A.n) ? j0 + A.seg : A.n;
+  for (int64_t c0 = j0; c0 < j1; c0 += 16) {
+    uint32_t key[16];
+    load16(Pg, c0, j1, A.vec4, key);
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      bool take = key[e] < tau;
+      if (key[e] == tau) {
+        take = eqb < need;
+        ++eqb;
+      }
+      if (take) {
+        if (pos < A.n_evict) og[pos] = c0 + e;
+        ++pos;
+      }
+    }
+  }
+}
+
+// Zeroes the status word, the per-head flag counts and the select histograms
+// and candidate counts in one launch.
+__global__ void k_init(int32_t* status, int32_t* flagcount, uint32_t* hist) {
+  const int g = blockIdx.x;
+  uint32_t* h = hist + (size_t)g * kHistStride;
+  for (int i = threadIdx.x; i < kHistStride; i += blockDim.x) h[i] = 0;
+  if (threadIdx.x == 0) {
     if (flagcount) flagcount[g] = 0;
     if (g == 0) *status = 0;
   }
-  (void)Hkv;
 }
 
-}  // namespace
+struct SelGeom {
+  int seg, nseg;
+};
 
-size_t select_scratch_bytes(int64_t n, int32_t Hkv) {
-  const int64_t nblk = (n + kChunk - 1) / kChunk;
-  size_t b = sizeof(uint32_t) * (size_t)Hkv * (kBins1 + kBins2 + kBins3);
-  b = (b + 255) / 256 * 256 + (sizeof(SelState) * (size_t)Hkv + 255) / 256 * 256;
-  b += sizeof(int64_t) * 4 * (size_t)Hkv * nblk;
-  return b + 256;
+SelGeom sel_geom(int64_t n) {
+  int64_t seg = (n + kMaxSeg - 1) / kMaxSeg;
+  seg = (seg + 15) / 16 * 16;
+  if (seg < 16) seg = 16;
+  SelGeom q;
+  q.seg = (int)seg;
+  q.nseg = (int)((n + seg - 1) / seg);
+  return q;
 }
-
-namespace {
 
 struct SelPtrs {
   uint32_t* hist;
   SelState* st;
-  int64_t* bc;
+  uint2* cand;
+  uint32_t* seg_lt;
+  int64_t* seg_off;
+  size_t bytes;
 };
 
-SelPtrs carve_sel(void* scratch, int32_t Hkv) {
-  SelPtrs q;
-  char* p = (char*)scratch;
-  q.hist = (uint32_t*)p;
-  p += (sizeof(uint32_t) * (size_t)Hkv * (kBins1 + kBins2 + kBins3) + 255) / 256 * 256;
-  q.st = (SelState*)p;
-  p += (sizeof(SelState) * (size_t)Hkv + 255) / 256 * 256;
-  q.bc = (int64_t*)p;
-  return q;
+SelPtrs carve_sel(void* scratch, int64_t n, int32_t Hkv) {
+  const SelGeom q = sel_geom(n);
+  SelPtrs r{};
+  char* base = (char*)scratch;
+  size_t off = 0;
+  auto take = [&](size_t b) {
+    char* p = base ? base + off : nullptr;
+    off += (b + 255) / 256 * 256;
+    return p;
+  };
+  r.hist = (uint32_t*)take(sizeof(uint32_t) * (size_t)Hkv * kHistStride);
+  r.st = (SelState*)take(sizeof(SelState) * (size_t)Hkv);
+  r.cand = (uint2*)take(sizeof(uint2) * (size_t)Hkv * (size_t)n);
+  r.seg_lt = (uint32_t*)take(sizeof(uint32_t) * (size_t)Hkv * q.nseg);
+  r.seg_off = (int64_t*)take(sizeof(int64_t) * 2 * (size_t)Hkv * q.nseg);
+  r.bytes = off;
+  return r;
 }
 
 }  // namespace
 
+size_t select_scratch_bytes(int64_t n, int32_t Hkv) { return carve_sel(nullptr, n, Hkv).bytes + 256; }
+
 hipError_t launch_init(int32_t* status, int32_t* flagcount, void* sel_scratch, int32_t Hkv,
                        hipStream_t st) {
-  const SelPtrs q = carve_sel(sel_scratch, Hkv);
-  k_init<<<Hkv, 256, 0, st>>>(status, flagcount, q.hist, q.st, Hkv);
+  // the histogram block sits first in the select scratch for every n
+  k_init<<<Hkv, 256, 0, st>>>(status, flagcount, (uint32_t*)sel_scratch);
   return hipGetLastError();
 }
 
 hipError_t launch_select(const float* S, int64_t n, int32_t w, int32_t Hkv, int32_t pool_kernel,
                          int64_t n_evict, float* out_scores, int64_t* out_idx, int32_t* status,
                          void* scratch, hipStream_t st) {
+  const SelGeom q = sel_geom(n);
+  const SelPtrs p = carve_sel(scratch, n, Hkv);
   SelArgs A{};
   A.S = S;
   A.P = out_scores;
@@ -396,18 +433,21 @@ hipError_t launch_select(const float* S, int64_t n, int32_t w, int32_t Hkv, int3
   A.w = w;
   A.pool_half = pool_kernel / 2;
   A.nblk = (int)((n + kChunk - 1) / kChunk);
-  const SelPtrs q = carve_sel(scratch, Hkv);
-  A.hist = q.hist;
-  A.st = q.st;
-  A.bc = q.bc;
+  A.seg = q.seg;
+  A.nseg = q.nseg;
+  A.vec4 = (n % 4 == 0) && ((uintptr_t)out_scores % 16 == 0);
+  A.hist = p.hist;
+  A.st = p.st;
+  A.cand = p.cand;
+  A.seg_lt = p.seg_lt;
+  A.seg_off = p.seg_off;
   A.status = status;
-  const dim3 grid(A.nblk, Hkv);
-  k_sel_pool<<<grid, kT, 0, st>>>(A);
+  k_sel_pool<<<dim3(A.nblk, Hkv), kT, 0, st>>>(A);
   if (n_evict > 0) {
-    k_sel_refine<1><<<grid, kT, 0, st>>>(A);
-    k_sel_refine<2><<<grid, kT, 0, st>>>(A);
-    k_sel_count<<<grid, kT, 0, st>>>(A);
-    k_sel_write<<<grid, kT, 0, st>>>(A);
+    const dim3 gs((q.nseg + kT - 1) / kT, Hkv);
+    k_sel_cand<<<gs, kT, 0, st>>>(A);
+    k_sel_tau<<<Hkv, kFT, 0, st>>>(A);
+    k_sel_write<<<gs, kT, 0, st>>>(A);
   }
   return hipGetLastError();
 }
