@@ -92,19 +92,14 @@ __device__ __forceinline__ int64_t wg_exclusive_scan(int64_t x, int64_t* wsum, i
 }
 
 // Bin of a histogram holding the key of 1-based rank `rank`, and the rank
-// inside that bin; the result is in *bin / *rin for every thread on return.
-template <int T, int NB>
-__device__ __forceinline__ void find_bin(const uint32_t* h, int64_t rank, int64_t* wsum, int* bin,
-                                         int64_t* rin) {
-  constexpr int PER = (NB + T - 1) / T;
-  uint32_t c[PER];
+// inside that bin, from the counts c[] of bins threadIdx.x * PER + i (loaded
+// by the caller); the result is in *bin / *rin for every thread on return.
+template <int T, int PER>
+__device__ __forceinline__ void find_bin_regs(const uint32_t (&c)[PER], int64_t rank, int64_t* wsum, int* bin,
+                                              int64_t* rin) {
   int64_t loc = 0;
 #pragma unroll
-  for (int i = 0; i < PER; ++i) {
-    const int b = threadIdx.x * PER + i;
-    c[i] = b < NB ? h[b] : 0u;
-    loc += c[i];
-  }
+  for (int i = 0; i < PER; ++i) loc += c[i];
   int64_t total;
   const int64_t before = wg_exclusive_scan<T>(loc, wsum, total);
   if (before < rank && rank <= before + loc) {
@@ -123,6 +118,16 @@ __device__ __forceinline__ void find_bin(const uint32_t* h, int64_t rank, int64_
     *rin = rr;
   }
   __syncthreads();
+}
+
+template <int T, int NB>
+__device__ __forceinline__ void load_bins(const uint32_t* h, uint32_t (&c)[(NB + T - 1) / T]) {
+  constexpr int PER = (NB + T - 1) / T;
+#pragma unroll
+  for (int i = 0; i < PER; ++i) {
+    const int b = threadIdx.x * PER + i;
+    c[i] = b < NB ? h[b] : 0u;
+  }
 }
 
 // Keys [j0, j0 + 16) of a head, 0xffffffff from `end` on.
@@ -156,9 +161,27 @@ __global__ __launch_bounds__(kT) void k_sel_pool(SelArgs A) {
   if (threadIdx.x == 0) bad = 0;
   for (int i = threadIdx.x; i < kBins1; i += kT) hist[i] = 0;
   if (in_lds) {
-    for (int i = threadIdx.x; i < kChunk + 2 * half; i += kT) {
-      const int64_t j = base - half + i;
-      sS[i] = (j >= 0 && j < A.n) ? Sg[j] : 0.0f;  // S >= 0: zero padding = clipping
+    // all loads in flight before the first LDS store (S >= 0: zero padding = clipping)
+    float sv[kPer];
+#pragma unroll
+    for (int e = 0; e < kPer; ++e) {
+      const int64_t j = base + e * kT + threadIdx.x;
+      sv[e] = j < A.n ? Sg[j] : 0.0f;
+    }
+    const int ih = threadIdx.x < half ? threadIdx.x : (int)threadIdx.x - half + kChunk + half;
+    float hv = 0.0f;
+    const bool halo = threadIdx.x < 2 * half;
+    if (halo) {
+      const int64_t j = base - half + ih;
+      hv = (j >= 0 && j < A.n) ? Sg[j] : 0.0f;
+    }
+#pragma unroll
+    for (int e = 0; e < kPer; ++e) sS[half + e * kT + threadIdx.x] = sv[e];
+    if (halo) sS[ih] = hv;
+    for (int i = kT + threadIdx.x; i < 2 * half; i += kT) {  // halves above kT / 2 only
+      const int ii = i < half ? i : i - half + kChunk + half;
+      const int64_t j = base - half + ii;
+      sS[ii] = (j >= 0 && j < A.n) ? Sg[j] : 0.0f;
     }
   }
   __syncthreads();
@@ -212,16 +235,19 @@ __global__ __launch_bounds__(kT) void k_sel_cand(SelArgs A) {
   __shared__ int64_t sh_rin;
   __shared__ uint32_t sh_base;
   uint32_t* gh = A.hist + (size_t)g * kHistStride;
-  for (int i = threadIdx.x; i < kBins2; i += kT) hist2[i] = 0;
-  find_bin<kT, kBins1>(gh, A.n_evict, wsum, &sh_bin, &sh_rin);
-  const uint32_t d1 = (uint32_t)sh_bin;
   const float* Pg = A.P + (size_t)g * A.n;
   const int64_t j0 = (int64_t)s * A.seg;
   const int64_t j1 = (s < A.nseg) ? ((j0 + A.seg < A.n) ? j0 + A.seg : A.n) : j0;
+  // the segment's first 16 keys and the digit-1 counts are loaded together
+  uint32_t key0[16];
+  load16(Pg, j0, j1, A.vec4, key0);
+  uint32_t c1[kBins1 / kT];
+  load_bins<kT, kBins1>(gh, c1);
+  for (int i = threadIdx.x; i < kBins2; i += kT) hist2[i] = 0;
+  find_bin_regs<kT, kBins1 / kT>(c1, A.n_evict, wsum, &sh_bin, &sh_rin);
+  const uint32_t d1 = (uint32_t)sh_bin;
   uint32_t lt = 0, nc = 0;
-  for (int64_t c0 = j0; c0 < j1; c0 += 16) {
-    uint32_t key[16];
-    load16(Pg, c0, j1, A.vec4, key);
+  auto count16 = [&](const uint32_t (&key)[16]) {
 #pragma unroll
     for (int e = 0; e < 16; ++e) {
       if (key[e] == 0xffffffffu) continue;
@@ -232,6 +258,12 @@ __global__ __launch_bounds__(kT) void k_sel_cand(SelArgs A) {
         atomicAdd(&hist2[(key[e] >> 8) & 0xfffu], 1u);
       }
     }
+  };
+  count16(key0);
+  for (int64_t c0 = j0 + 16; c0 < j1; c0 += 16) {
+    uint32_t key[16];
+    load16(Pg, c0, j1, A.vec4, key);
+    count16(key);
   }
   if (s < A.nseg) A.seg_lt[(size_t)g * A.nseg + s] = lt;
   int64_t total;
@@ -241,12 +273,16 @@ __global__ __launch_bounds__(kT) void k_sel_cand(SelArgs A) {
   if (nc > 0) {
     uint2* cg = A.cand + (size_t)g * A.n;
     uint32_t pos = sh_base + (uint32_t)before;
-    for (int64_t c0 = j0; c0 < j1; c0 += 16) {
-      uint32_t key[16];
-      load16(Pg, c0, j1, A.vec4, key);
+    auto emit16 = [&](const uint32_t (&key)[16], int64_t c0) {
 #pragma unroll
       for (int e = 0; e < 16; ++e)
         if (key[e] != 0xffffffffu && (key[e] >> 20) == d1) cg[pos++] = make_uint2(key[e], (uint32_t)(c0 + e));
+    };
+    emit16(key0, j0);
+    for (int64_t c0 = j0 + 16; c0 < j1; c0 += 16) {
+      uint32_t key[16];
+      load16(Pg, c0, j1, A.vec4, key);
+      emit16(key, c0);
     }
   }
   if (total > 0) {
@@ -257,6 +293,8 @@ __global__ __launch_bounds__(kT) void k_sel_cand(SelArgs A) {
 }
 
 // tau, need and the per-segment output offsets of one head.
+constexpr int kCandRegs = 8;  // candidates per thread held in registers (else re-read)
+
 __global__ __launch_bounds__(kFT) void k_sel_tau(SelArgs A) {
   const int g = blockIdx.x;
   __shared__ uint32_t slt[kMaxSeg];
@@ -266,21 +304,53 @@ __global__ __launch_bounds__(kFT) void k_sel_tau(SelArgs A) {
   __shared__ int sh_bin;
   __shared__ int64_t sh_rin;
   const uint32_t* gh = A.hist + (size_t)g * kHistStride;
-  find_bin<kFT, kBins1>(gh, A.n_evict, wsum, &sh_bin, &sh_rin);
-  const uint32_t d1 = (uint32_t)sh_bin;
-  const int64_t r1 = sh_rin;
+  const uint32_t* sl = A.seg_lt + (size_t)g * A.nseg;
+  const uint2* cg = A.cand + (size_t)g * A.n;
+  // every load that does not depend on tau, issued together
+  uint32_t c1[kBins1 / kFT], c2[kBins2 / kFT];
+  load_bins<kFT, kBins1>(gh, c1);
+  load_bins<kFT, kBins2>(gh + kBins1, c2);
+  const uint32_t nc = gh[kBins1 + kBins2];
+  uint32_t lts[kMaxSeg / kFT];
+#pragma unroll
+  for (int i = 0; i < kMaxSeg / kFT; ++i) {
+    const int sg = threadIdx.x + i * kFT;
+    lts[i] = sg < A.nseg ? sl[sg] : 0u;
+  }
+  const bool in_regs = nc <= (uint32_t)(kCandRegs * kFT);
+  uint2 cr[kCandRegs];
+#pragma unroll
+  for (int i = 0; i < kCandRegs; ++i) {
+    const uint32_t ci = threadIdx.x + i * kFT;
+    cr[i] = (in_regs && ci < nc) ? cg[ci] : make_uint2(0xffffffffu, 0u);
+  }
   for (int i = threadIdx.x; i < kBins3; i += kFT) hist3[i] = 0;
-  find_bin<kFT, kBins2>(gh + kBins1, r1, wsum, &sh_bin, &sh_rin);
+#pragma unroll
+  for (int i = 0; i < kMaxSeg / kFT; ++i) {
+    const int sg = threadIdx.x + i * kFT;
+    if (sg < A.nseg) {
+      slt[sg] = lts[i];
+      seq[sg] = 0;
+    }
+  }
+  find_bin_regs<kFT, kBins1 / kFT>(c1, A.n_evict, wsum, &sh_bin, &sh_rin);
+  const uint32_t d1 = (uint32_t)sh_bin;
+  find_bin_regs<kFT, kBins2 / kFT>(c2, sh_rin, wsum, &sh_bin, &sh_rin);
   const uint32_t d2 = (uint32_t)sh_bin;
   const int64_t r2 = sh_rin;
-  const uint32_t nc = gh[kBins1 + kBins2];
-  const uint2* cg = A.cand + (size_t)g * A.n;
-  for (uint32_t i = threadIdx.x; i < nc; i += kFT) {
-    const uint32_t key = cg[i].x;
-    if (((key >> 8) & 0xfffu) == d2) atomicAdd(&hist3[key & 0xffu], 1u);
+  auto digit3 = [&](uint32_t key) {
+    if (key != 0xffffffffu && ((key >> 8) & 0xfffu) == d2) atomicAdd(&hist3[key & 0xffu], 1u);
+  };
+  if (in_regs) {
+#pragma unroll
+    for (int i = 0; i < kCandRegs; ++i) digit3(cr[i].x);
+  } else {
+    for (uint32_t i = threadIdx.x; i < nc; i += kFT) digit3(cg[i].x);
   }
   __syncthreads();
-  find_bin<kFT, kBins3>(hist3, r2, wsum, &sh_bin, &sh_rin);
+  uint32_t c3[1];
+  c3[0] = threadIdx.x < kBins3 ? hist3[threadIdx.x] : 0u;
+  find_bin_regs<kFT, 1>(c3, r2, wsum, &sh_bin, &sh_rin);
   const uint32_t tau = (d1 << 20) | (d2 << 8) | (uint32_t)sh_bin;
   const int64_t need = sh_rin;
   if (threadIdx.x == 0) {
@@ -288,38 +358,38 @@ __global__ __launch_bounds__(kFT) void k_sel_tau(SelArgs A) {
     A.st[g].need = need;
   }
   // per-segment counts: below tau = below digit 1's bin + candidates below tau
-  const uint32_t* sl = A.seg_lt + (size_t)g * A.nseg;
-  for (int s = threadIdx.x; s < A.nseg; s += kFT) {
-    slt[s] = sl[s];
-    seq[s] = 0;
-  }
-  __syncthreads();
-  for (uint32_t i = threadIdx.x; i < nc; i += kFT) {
-    const uint2 c = cg[i];
-    const int s = (int)(c.y / (uint32_t)A.seg);
-    if (c.x < tau) atomicAdd(&slt[s], 1u);
-    else if (c.x == tau) atomicAdd(&seq[s], 1u);
+  auto fix = [&](uint2 c) {
+    if (c.x == 0xffffffffu) return;
+    const int sg = (int)(c.y / (uint32_t)A.seg);
+    if (c.x < tau) atomicAdd(&slt[sg], 1u);
+    else if (c.x == tau) atomicAdd(&seq[sg], 1u);
+  };
+  if (in_regs) {
+#pragma unroll
+    for (int i = 0; i < kCandRegs; ++i) fix(cr[i]);
+  } else {
+    for (uint32_t i = threadIdx.x; i < nc; i += kFT) fix(cg[i]);
   }
   __syncthreads();
   // thread t owns segments [t spt, (t+1) spt): offsets by one workgroup scan
   const int spt = (A.nseg + kFT - 1) / kFT;
   const int s0 = threadIdx.x * spt;
   int64_t l = 0, e = 0;
-  for (int s = s0; s < s0 + spt && s < A.nseg; ++s) {
-    l += slt[s];
-    e += seq[s];
+  for (int sg = s0; sg < s0 + spt && sg < A.nseg; ++sg) {
+    l += slt[sg];
+    e += seq[sg];
   }
   int64_t tot;
   // both counts are below 2^31: one scan of (eq << 32 | lt)
   const int64_t pk = wg_exclusive_scan<kFT>((e << 32) | l, wsum, tot);
   int64_t lb = pk & 0xffffffffLL, eb = pk >> 32;
   int64_t* so = A.seg_off + (size_t)g * A.nseg * 2;
-  for (int s = s0; s < s0 + spt && s < A.nseg; ++s) {
+  for (int sg = s0; sg < s0 + spt && sg < A.nseg; ++sg) {
     const int64_t taken_eq = eb < need ? eb : need;
-    so[2 * s] = lb + taken_eq;
-    so[2 * s + 1] = eb;
-    lb += slt[s];
-    eb += seq[s];
+    so[2 * sg] = lb + taken_eq;
+    so[2 * sg + 1] = eb;
+    lb += slt[sg];
+    eb += seq[sg];
   }
 }
 
