@@ -41,8 +41,10 @@ def parse():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="llama_128k")
-    ap.add_argument("--stage-reps", type=int, default=10)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a plain device copy of 512 MiB (3 times): the reference kernel "
+                         "that scales rocprofv3 FETCH_SIZE / WRITE_SIZE to bytes")
     ap.add_argument("--out", default=None, help="also write the JSON line to this new file")
     return ap.parse_args()
 
@@ -65,6 +67,53 @@ def cpu_model():
     return platform.processor() or None
 
 
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_llama_128k.txt")
+
+
+def source_sha(rel):
+    import hashlib
+    with open(os.path.join(ROOT, rel), "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()
+
+
+def counted_traffic(kernel):
+    """HBM bytes per launch of `kernel` from the committed counter summary, or None.
+
+    The summary records FETCH_SIZE + WRITE_SIZE per dispatch scaled by the same
+    counters on a plain copy of known size, and the SHA-256 of the kernel
+    source they were taken on; a changed source makes the figure stale (None).
+    """
+    try:
+        lines = open(TRAFFIC_FILE).read().splitlines()
+    except OSError:
+        return None
+    vals, shas = {}, {}
+    for ln in lines:
+        parts = ln.split()
+        if len(parts) == 3 and parts[0] == "bytes_per_launch":
+            vals[parts[1]] = float(parts[2])
+        if len(parts) == 3 and parts[0] == "source_sha256":
+            shas[parts[1]] = parts[2]
+    if kernel not in vals or not shas:
+        return None
+    for rel, sha in shas.items():
+        if not os.path.exists(os.path.join(ROOT, rel)) or source_sha(rel) != sha:
+            return None
+    return int(vals[kernel])
+
+
+def copy_calibration():
+    import torch
+    dev = torch.device("cuda:0")
+    nbytes = 512 << 20
+    src = torch.ones(nbytes // 4, dtype=torch.float32, device=dev)
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration_bytes": nbytes, "reps": 3}), flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
@@ -79,6 +128,9 @@ def main():
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
+    if args.copy_calibration:
+        copy_calibration()
+        return
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
 
@@ -101,21 +153,23 @@ def main():
     scores = torch.empty((case.Hkv, case.n), dtype=torch.float32, device=dev)
     evict = torch.empty((case.Hkv, n_evict), dtype=torch.int64, device=dev)
 
-    def step():
+    def step(flags=0):
         K.score_ex(q, k, v, pool_kernel=cfg.pool_kernel, n_evict=n_evict, workspace=ws,
-                   status=status, scores=scores, evict_idx=evict)
+                   status=status, scores=scores, evict_idx=evict, flags=flags)
 
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
     if int(status.item()) != 0:
         raise SystemExit(f"device status {int(status.item())} after warm-up")
+    K.stage_log()  # start the timed region with an empty stage log
 
-    # timed region: K whole-path steps, synchronised on both sides
+    # timed region: K whole-path steps, synchronised on both sides; every step
+    # records a HIP event after each kernel on the library's stream (no sync)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for _ in range(args.steps):
-        step()
+        step(K.FLAG_STAGE_LOG)
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     st_word = int(status.item())
@@ -124,13 +178,9 @@ def main():
     ms_per_step = (t1 - t0) * 1e3 / args.steps
     tokens_per_s = case.n / (ms_per_step * 1e-3)
 
-    # per-kernel durations from HIP events recorded between the library's launches
-    stage_acc = {}
-    for _ in range(max(1, args.stage_reps)):
-        _, _, stages = K.stage_times(q, k, v, pool_kernel=cfg.pool_kernel, n_evict=n_evict)
-        for name, ms in stages:
-            stage_acc.setdefault(name, []).append(ms)
-    stage_ms = {k_: float(np.mean(v_)) for k_, v_ in stage_acc.items()}
+    # per-kernel mean durations over the timed steps, from their HIP events
+    logged, stages = K.stage_log()
+    stage_ms = {name: ms for name, ms in stages}
     kv_bytes_per_pass = case.Hkv * case.n * case.d * 2 * 2  # K and V read once
     passes = [s for s in ("pass1", "pass2") if s in stage_ms]
     if passes:
@@ -143,8 +193,9 @@ def main():
         achieved = 2 * kv_bytes_per_pass / (dom_ms * 1e-3) / 1e9
     roofline = {
         "bound": "hbm", "kernel": dom, "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
-        "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
-        "bytes_per_launch": kv_bytes_per_pass, "avg_ms": round(dom_ms, 4),
+        "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+        "traffic": counted_traffic(dom) if args.workload == "llama_128k" else None,
+        "bytes_per_launch": kv_bytes_per_pass, "avg_ms": round(dom_ms, 4), "timed_launches": logged,
     }
     step_bytes = 2 * kv_bytes_per_pass
     flops = 8 * case.d * case.group * case.window * case.Hkv * case.n

@@ -72,7 +72,9 @@ enum { DROPKV_STATUS_SINGULAR = 1, DROPKV_STATUS_NONFINITE = 2 };
 
 /* Flags for dropkv_score_ex. */
 enum {
-  DROPKV_FLAG_GENERIC = 1 /* force the plain-VALU path even where the MFMA path applies */
+  DROPKV_FLAG_GENERIC = 1, /* force the plain-VALU path even where the MFMA path applies */
+  DROPKV_FLAG_STAGE_LOG = 2 /* dropkv_score_ex only: record a HIP event after every kernel of
+                               the call into the library's stage log (see dropkv_stage_log) */
 };
 
 /*
@@ -152,6 +154,20 @@ int dropkv_stage_times(int32_t dtype, const void* q, const void* k, const void* 
                        int64_t n_evict, float* out_scores, int64_t* out_evict_idx, uint32_t flags,
                        float* out_ms, char* out_names, int32_t names_bytes, int32_t* out_count,
                        void* stream);
+
+/*
+ * Reads the stage log of the current device: calls of dropkv_score_ex made
+ * with DROPKV_FLAG_STAGE_LOG since the last read (at most 64 are kept; later
+ * ones are not logged). Waits for their events, writes the mean duration of
+ * each stage over those calls in milliseconds to out_ms[0..*out_count-1] (at
+ * most 12), their comma-separated names to out_names (names_bytes bytes,
+ * NUL-terminated; may be NULL) and the number of calls to *out_calls, then
+ * empties the log. DROPKV_ERR_INVALID if the logged calls ran different
+ * stage sequences; *out_calls = 0 if nothing was logged. Not thread-safe
+ * against concurrent logged calls on the same device.
+ */
+int dropkv_stage_log(float* out_ms, char* out_names, int32_t names_bytes, int32_t* out_count,
+                     int32_t* out_calls);
 
 /* 1 if (dtype, d) takes the MFMA path by default, 0 if the plain-VALU path. */
 int dropkv_uses_mfma(int32_t dtype, int32_t d);

@@ -19,6 +19,7 @@ OK, ERR_INVALID, ERR_SINGULAR, ERR_NONFINITE, ERR_DEVICE = 0, -1, -2, -3, -4
 BF16, F32 = 0, 1
 STATUS_SINGULAR, STATUS_NONFINITE = 1, 2
 FLAG_GENERIC = 1
+FLAG_STAGE_LOG = 2
 
 # name -> (restype, argtypes)
 _c = ctypes
@@ -35,6 +36,7 @@ SIGNATURES = {
     "dropkv_select": (_i32, [_p, _i64, _i32, _i32, _i32, _i64, _p, _p, _p]),
     "dropkv_stage_times": (_i32, [_i32, _p, _p, _p, _i64, _i32, _i32, _i32, _i32, _i32, _i64, _p,
                                   _p, _u32, _p, _p, _i32, _p, _p]),
+    "dropkv_stage_log": (_i32, [_p, _p, _i32, _p, _p]),
     "dropkv_uses_mfma": (_i32, [_i32, _i32]),
     "dropkv_last_error": (_c.c_char_p, []),
     "dropkv_version": (_c.c_char_p, []),
@@ -236,6 +238,24 @@ def stage_times(q, k, v, *, pool_kernel: int, n_evict: int, flags: int = 0, stre
     _raise(rc)
     labels = names.value.decode().split(",") if count.value else []
     return scores, idx, [(labels[i], float(ms[i])) for i in range(count.value)]
+
+
+def stage_log():
+    """Mean per-stage milliseconds of the calls logged with FLAG_STAGE_LOG since the last read.
+
+    Returns (calls, [(stage name, milliseconds), ...]) and empties the log.
+    """
+    lib = load_library()
+    ms = (ctypes.c_float * 16)()
+    names = ctypes.create_string_buffer(512)
+    count = ctypes.c_int32(0)
+    calls = ctypes.c_int32(0)
+    rc = lib.dropkv_stage_log(ctypes.cast(ms, ctypes.c_void_p), ctypes.cast(names, ctypes.c_void_p), 512,
+                              ctypes.cast(ctypes.pointer(count), ctypes.c_void_p),
+                              ctypes.cast(ctypes.pointer(calls), ctypes.c_void_p))
+    _raise(rc)
+    labels = names.value.decode().split(",") if count.value else []
+    return calls.value, [(labels[i], float(ms[i])) for i in range(count.value)]
 
 
 def uses_mfma(dtype_code: int, d: int) -> bool:

@@ -33,6 +33,34 @@ struct DeviceWs {
 std::mutex g_ws_mutex;
 std::unordered_map<int, DeviceWs> g_ws;
 
+// Stage log: event sets of up to kLogCalls logged dropkv_score_ex calls per device.
+constexpr int kLogCalls = 64;
+struct StageLog {
+  StageEvents slot[kLogCalls];
+  bool created[kLogCalls] = {};
+  int used = 0;
+};
+std::mutex g_log_mutex;
+std::unordered_map<int, StageLog> g_log;
+
+// Next free slot of the current device's log (events created on first use), or null.
+StageEvents* log_slot() {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return nullptr;
+  std::lock_guard<std::mutex> lock(g_log_mutex);
+  StageLog& L = g_log[dev];
+  if (L.used >= kLogCalls) return nullptr;
+  const int i = L.used;
+  if (!L.created[i]) {
+    for (int e = 0; e <= kMaxStages; ++e)
+      if (hipEventCreate(&L.slot[i].ev[e]) != hipSuccess) return nullptr;
+    L.created[i] = true;
+  }
+  L.slot[i].count = 0;
+  L.used += 1;
+  return &L.slot[i];
+}
+
 const char* validate(int dtype, int64_t n, int32_t w, int32_t Hq, int32_t Hkv, int32_t d) {
   if (dtype != DROPKV_BF16 && dtype != DROPKV_F32) return "dtype must be DROPKV_BF16 or DROPKV_F32";
   if (n < 2) return "n must be >= 2";
@@ -262,10 +290,13 @@ int dropkv_score_ex(int32_t dtype, const void* q, const void* k, const void* v, 
   if (ws.bytes > workspace_bytes) return fail(DROPKV_ERR_INVALID, "workspace too small");
   ws.status = d_status;
   hipStream_t st = (hipStream_t)stream;
-  if (int rc = run_scores(dtype, q, k, v, s, ws, mfma, st)) return rc;
+  StageEvents* se = (flags & DROPKV_FLAG_STAGE_LOG) ? log_slot() : nullptr;
+  if (int rc = run_scores(dtype, q, k, v, s, ws, mfma, st, se)) return rc;
   hipError_t e = launch_select(ws.S, n, window, Hkv, pool_kernel, n_evict, out_scores, out_evict_idx,
                                ws.status, ws.sel, st);
   if (e != hipSuccess) return fail_hip(e, "select");
+  e = record_stage(se, "select", st);
+  if (e != hipSuccess) return fail_hip(e, "stage event");
   return DROPKV_OK;
 }
 
@@ -388,6 +419,51 @@ int dropkv_stage_times(int32_t dtype, const void* q, const void* k, const void* 
   }
   for (int i = 0; i <= kMaxStages; ++i) (void)hipEventDestroy(se.ev[i]);
   return rc;
+}
+
+int dropkv_stage_log(float* out_ms, char* out_names, int32_t names_bytes, int32_t* out_count,
+                     int32_t* out_calls) {
+  g_last_error.clear();
+  if (!out_ms || !out_count || !out_calls) return fail(DROPKV_ERR_INVALID, "out_ms, out_count and out_calls are required");
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail_hip(e, "hipGetDevice");
+  std::lock_guard<std::mutex> lock(g_log_mutex);
+  StageLog& L = g_log[dev];
+  const int calls = L.used;
+  L.used = 0;
+  *out_calls = calls;
+  *out_count = 0;
+  if (calls == 0) return DROPKV_OK;
+  const StageEvents& s0 = L.slot[0];
+  for (int c = 0; c < calls; ++c) {
+    const StageEvents& sc = L.slot[c];
+    if (sc.count != s0.count) return fail(DROPKV_ERR_INVALID, "logged calls ran different stages");
+    for (int i = 0; i < sc.count; ++i)
+      if (std::strcmp(sc.names[i], s0.names[i]) != 0)
+        return fail(DROPKV_ERR_INVALID, "logged calls ran different stages");
+    e = hipEventSynchronize(sc.ev[sc.count]);
+    if (e != hipSuccess) return fail_hip(e, "hipEventSynchronize");
+  }
+  std::string names;
+  for (int i = 0; i < s0.count; ++i) {
+    double acc = 0.0;
+    for (int c = 0; c < calls; ++c) {
+      float ms = 0.f;
+      e = hipEventElapsedTime(&ms, L.slot[c].ev[i], L.slot[c].ev[i + 1]);
+      if (e != hipSuccess) return fail_hip(e, "hipEventElapsedTime");
+      acc += ms;
+    }
+    out_ms[i] = (float)(acc / calls);
+    names += s0.names[i];
+    names += (i + 1 < s0.count) ? "," : "";
+  }
+  *out_count = s0.count;
+  if (out_names && names_bytes > 0) {
+    std::strncpy(out_names, names.c_str(), (size_t)names_bytes - 1);
+    out_names[names_bytes - 1] = 0;
+  }
+  return DROPKV_OK;
 }
 
 int dropkv_uses_mfma(int32_t dtype, int32_t d) { return mfma_supported(dtype, d) ? 1 : 0; }

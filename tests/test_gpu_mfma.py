@@ -137,3 +137,30 @@ def test_mfma_nan_in_values_reported():
     q, k, v = to_torch(case)
     with pytest.raises(K.DropKVNonFiniteError):
         K.score(q, k, v, pool_kernel=3, n_evict=100)
+
+
+def test_stage_log_over_async_calls():
+    """Logged dropkv_score_ex calls report every kernel's mean time, in order, and match unlogged outputs."""
+    case = synth.make_gaussian_case(8, 2, 128, 3000, 32, dtype="bf16", seeds=(5, 6, 7), sink=True, needles=4)
+    print(f"[mfma] stage log Hq={case.Hq} Hkv={case.Hkv} n={case.n}", flush=True)
+    q, k, v = to_torch(case)
+    ne = 2000
+    ws = torch.empty(K.workspace_bytes(K.BF16, case.n, case.window, case.Hq, case.Hkv, case.d),
+                     dtype=torch.uint8, device=q.device)
+    st = torch.zeros(1, dtype=torch.int32, device=q.device)
+    K.stage_log()
+    ref_scores, ref_idx = K.score(q, k, v, pool_kernel=7, n_evict=ne)
+    outs = []
+    for _ in range(3):
+        outs.append(K.score_ex(q, k, v, pool_kernel=7, n_evict=ne, workspace=ws, status=st,
+                               flags=K.FLAG_STAGE_LOG))
+    calls, stages = K.stage_log()
+    torch.cuda.synchronize()
+    assert int(st.item()) == 0
+    assert calls == 3
+    names = [s for s, _ in stages]
+    assert names[0] == "pass1" and names[-1] == "select" and "pass2" in names
+    assert all(ms > 0 for _, ms in stages)
+    for sc, ix in outs:
+        assert torch.equal(sc, ref_scores) and torch.equal(ix, ref_idx)
+    assert K.stage_log() == (0, [])
