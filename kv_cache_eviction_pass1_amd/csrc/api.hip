@@ -98,14 +98,21 @@ bool use_mfma(int dtype, int d, uint32_t flags) {
 }
 
 // Run the scoring stages up to raw scores (ws.S) and row statistics.
+// fold: when non-null (scoring calls), the MFMA path leaves the argmax terms
+// of flagged rows for the select stage and describes them here; it stays
+// zero-initialised (nothing to fold) on the generic path.
 int run_scores(int dtype, const void* q, const void* k, const void* v, const Shape& s,
-               const Workspace& ws, bool mfma, hipStream_t st, StageEvents* se = nullptr) {
-  hipError_t e = launch_init(ws.status, ws.flagcount, ws.sel, s.Hkv, st);
-  if (e != hipSuccess) return fail_hip(e, "init");
+               const Workspace& ws, bool mfma, hipStream_t st, StageEvents* se = nullptr,
+               FoldInfo* fold = nullptr) {
+  hipError_t e;
+  if (fold) *fold = FoldInfo{};
   if (mfma) {
-    e = launch_mfma_path(q, k, v, s, ws, st, se);
+    // pass 1 clears the status word, the flag counts and the select state
+    e = launch_mfma_path(q, k, v, s, ws, st, se, fold != nullptr, fold);
     if (e != hipSuccess) return fail_hip(e, "mfma path");
   } else {
+    e = launch_init(ws.status, ws.flagcount, ws.sel, s.Hkv, st);
+    if (e != hipSuccess) return fail_hip(e, "init");
     record_stage(se, "start", st);
     e = launch_generic_rows(dtype, q, k, v, s, ws, st);
     if (e != hipSuccess) return fail_hip(e, "generic row stats");
@@ -181,8 +188,9 @@ int score_sync(int dtype, const void* q, const void* k, const void* v, int64_t n
   void* base = nullptr;
   if (int rc = get_workspace(need, &base)) return rc;
   Workspace ws = carve_workspace(base, s, mfma);
-  if (int rc = run_scores(dtype, q, k, v, s, ws, mfma, st)) return rc;
-  hipError_t e = launch_select(ws.S, n, w, Hkv, pool_kernel, n_evict, out_scores, out_idx, ws.status, ws.sel, st);
+  FoldInfo fold{};
+  if (int rc = run_scores(dtype, q, k, v, s, ws, mfma, st, nullptr, &fold)) return rc;
+  hipError_t e = launch_select(ws.S, n, w, Hkv, pool_kernel, n_evict, out_scores, out_idx, ws.status, &fold, ws.sel, st);
   if (e != hipSuccess) return fail_hip(e, "select");
   return sync_status(ws, st);
 }
@@ -291,9 +299,10 @@ int dropkv_score_ex(int32_t dtype, const void* q, const void* k, const void* v, 
   ws.status = d_status;
   hipStream_t st = (hipStream_t)stream;
   StageEvents* se = (flags & DROPKV_FLAG_STAGE_LOG) ? log_slot() : nullptr;
-  if (int rc = run_scores(dtype, q, k, v, s, ws, mfma, st, se)) return rc;
+  FoldInfo fold{};
+  if (int rc = run_scores(dtype, q, k, v, s, ws, mfma, st, se, &fold)) return rc;
   hipError_t e = launch_select(ws.S, n, window, Hkv, pool_kernel, n_evict, out_scores, out_evict_idx,
-                               ws.status, ws.sel, st);
+                               ws.status, &fold, ws.sel, st);
   if (e != hipSuccess) return fail_hip(e, "select");
   e = record_stage(se, "select", st);
   if (e != hipSuccess) return fail_hip(e, "stage event");
@@ -365,7 +374,9 @@ int dropkv_select(const float* S, int64_t n, int32_t window, int32_t Hkv, int32_
   ws.status = (int32_t*)base;
   ws.sel = (char*)base + 256;
   hipError_t e = launch_init(ws.status, nullptr, ws.sel, Hkv, st);
-  if (e == hipSuccess) e = launch_select(S, n, window, Hkv, pool_kernel, n_evict, out_scores, out_evict_idx, ws.status, ws.sel, st);
+  if (e == hipSuccess)
+    e = launch_select(S, n, window, Hkv, pool_kernel, n_evict, out_scores, out_evict_idx, ws.status, nullptr,
+                      ws.sel, st);
   if (e != hipSuccess) return fail_hip(e, "select");
   return sync_status(ws, st);
 }
@@ -395,9 +406,11 @@ int dropkv_stage_times(int32_t dtype, const void* q, const void* k, const void* 
     hipError_t e = hipEventCreate(&se.ev[i]);
     if (e != hipSuccess) return fail_hip(e, "hipEventCreate");
   }
-  int rc = run_scores(dtype, q, k, v, s, ws, mfma, st, &se);
+  FoldInfo fold{};
+  int rc = run_scores(dtype, q, k, v, s, ws, mfma, st, &se, &fold);
   if (rc == DROPKV_OK) {
-    hipError_t e = launch_select(ws.S, n, window, Hkv, pool_kernel, n_evict, out_scores, out_evict_idx, ws.status, ws.sel, st);
+    hipError_t e = launch_select(ws.S, n, window, Hkv, pool_kernel, n_evict, out_scores, out_evict_idx, ws.status,
+                                 &fold, ws.sel, st);
     if (e != hipSuccess) rc = fail_hip(e, "select");
     else record_stage(&se, "select", st);
   }

@@ -62,10 +62,23 @@ hipError_t launch_generic_rows(int dtype, const void* q, const void* k, const vo
                                const Shape& s, const Workspace& ws, hipStream_t st);
 hipError_t launch_generic_scores(int dtype, const void* q, const void* k, const void* v,
                                  const Shape& s, const Workspace& ws, hipStream_t st);
+// Exact argmax terms of the rows flagged by the MFMA path's merge (rows with
+// p_max > 1/2): per-chunk fix-up partials (sp, ps, D[d]) that the select
+// stage folds into S in row order. flagcount == nullptr: nothing to fold.
+struct FoldInfo {
+  const int32_t* flagcount;  // [Hkv]
+  RowStats rs;
+  const float* fx;           // [nchunk][Hkv * Rg][stride]
+  int Hkv, Rg, nchunk, stride, d;
+  float invG;
+};
+
 hipError_t launch_select(const float* S, int64_t n, int32_t w, int32_t Hkv, int32_t pool_kernel,
                          int64_t n_evict, float* out_scores, int64_t* out_idx, int32_t* status,
-                         void* scratch, hipStream_t st);
+                         const FoldInfo* fold, void* scratch, hipStream_t st);
 size_t select_scratch_bytes(int64_t n, int32_t Hkv);
+// 32-bit words at the start of the select scratch that must be zero before a call.
+size_t select_zero_words(int32_t Hkv);
 // Stage timing: when `ev` is non-null, an event is recorded on the stream after
 // every kernel of the path; `names` receives the stage names (at most kMaxStages).
 constexpr int kMaxStages = 12;
@@ -75,8 +88,17 @@ struct StageEvents {
   int count;
 };
 hipError_t record_stage(StageEvents* se, const char* name, hipStream_t st);
+// MFMA path up to raw scores. Pass 1 also clears the status word, the flag
+// counts and select_zero_words(Hkv) words of ws.sel (no separate init launch).
+// fold_in_select: leave the flagged rows' argmax terms out of ws.S and return
+// their description in *fold for launch_select to add (else *fold is unused
+// and k_fold adds them to ws.S).
 hipError_t launch_mfma_path(const void* q, const void* k, const void* v, const Shape& s,
-                            const Workspace& ws, hipStream_t st, StageEvents* se);
+                            const Workspace& ws, hipStream_t st, StageEvents* se, bool fold_in_select,
+                            FoldInfo* fold);
+// Adds the argmax terms described by `fold` into S [Hkv][n] (one block per head).
+hipError_t launch_fold(const FoldInfo& fold, int64_t n, int32_t Hkv, float* S, int32_t* status,
+                       hipStream_t st);
 bool mfma_supported(int dtype, int d);
 int mfma_chunks(const Shape& s);
 size_t mfma_extra_bytes(const Shape& s);
@@ -112,6 +134,32 @@ __device__ __forceinline__ float block_sum(float x, float* red) {
   float r = red[0];
   __syncthreads();
   return r;
+}
+
+
+// Argmax term ||Delta_{j*}||^2 of flagged row `row` from its fix-up partials
+// (sp = sum_{i != j*} p_i, ps = p_{j*}, D = sum_{i != j*} p_i (v_i - v_{j*})),
+// reduced over the NT threads of the calling block (threads t < F.d add D_t).
+// Every thread returns the same value, R in *R_out and the status bits to
+// raise in *bits (non-finite or singular row: the value must not be used).
+template <int NT>
+__device__ __forceinline__ float fold_value(const FoldInfo& F, int64_t row, float* red, float* R_out,
+                                            int* bits) {
+  const int tid = threadIdx.x;
+  float sp = 0.f, ps = 0.f, D = 0.f;
+  for (int c = 0; c < F.nchunk; ++c) {
+    const float* o = F.fx + ((size_t)c * F.Hkv * F.Rg + row) * F.stride;
+    sp += o[0];
+    ps += o[1];
+    if (tid < F.d) D += o[2 + tid];
+  }
+  const float dn2 = block_sum<NT>(D * D, red);
+  // R = sum_{i != j*} e_i / e_{j*}; ||a - v_{j*}|| = ||D|| / (ps + sp); p/(1-p) = 1/R
+  const float R = sp / ps;
+  const float tot = ps + sp;
+  *R_out = R;
+  *bits = (!(ps > 0.f) || !finite_f(R)) ? kStatusNonFinite : (R <= kSingularRest ? kStatusSingular : 0);
+  return dn2 / (tot * tot) / (R * R);
 }
 
 }  // namespace dropkv

@@ -171,6 +171,10 @@ struct P1Args {
   float c2;          // log2(e) / sqrt(d)
   float* part;       // [chunk][Hkv*Rg][PSTRIDE]
   float* nv;         // [Hkv][n]
+  int32_t* status;   // cleared here (read by later kernels only)
+  int32_t* flagcount;  // [Hkv], cleared here
+  uint32_t* zero;    // select state cleared here
+  int64_t zero_words;
 };
 
 // Per-lane LDS byte offsets inside a tile, for the first 32-token subtile.
@@ -386,6 +390,15 @@ __global__ __launch_bounds__(NW * 64) void k_pass1(P1Args A) {
   const LdsOff off = lds_offsets(lane);
   const DmaOff<NW> doff = dma_offsets<NW>(wave, lane);
   const VnOff<NW> vno = vn_offsets<NW>(wave, lane);
+  {
+    // state of this call that later kernels accumulate into
+    const int64_t wg = blockIdx.x + (int64_t)gridDim.x * (blockIdx.y + (int64_t)gridDim.y * blockIdx.z);
+    const int64_t nthr = (int64_t)gridDim.x * gridDim.y * gridDim.z * blockDim.x;
+    for (int64_t i = wg * blockDim.x + threadIdx.x; i < A.zero_words; i += nthr) A.zero[i] = 0u;
+    if (wg == 0)
+      for (int i = threadIdx.x; i < A.Hkv; i += blockDim.x) A.flagcount[i] = 0;
+    if (wg == 0 && threadIdx.x == 0) *A.status = 0;
+  }
 
   bf16x8 qb[8];
   {
@@ -652,46 +665,36 @@ __global__ __launch_bounds__(256) void k_fixup(FixArgs F) {
 }
 
 struct FoldArgs {
+  FoldInfo f;
   int64_t n;
-  int Rg, Hkv;
-  float invG;
-  RowStats rs;
-  const int32_t* flagcount;
-  const float* fx;
   float* S;
   int32_t* status;
 };
 
-// Adds the argmax terms of flagged rows into S, in row order (deterministic).
+// Adds the argmax terms of flagged rows into S, in row order (deterministic),
+// and records R, L and the term in the row statistics.
 __global__ __launch_bounds__(HD) void k_fold(FoldArgs F) {
   const int g = blockIdx.x;
-  if (F.flagcount[g] == 0) return;
+  if (F.f.flagcount[g] == 0) return;
   const int tid = threadIdx.x;
   __shared__ float red[HD];
-  for (int r = 0; r < F.Rg; ++r) {
-    const int64_t row = (int64_t)g * F.Rg + r;
-    if (!F.rs.flag[row]) continue;
-    float sp = 0.f, ps = 0.f, D = 0.f;
-    for (int c = 0; c < FXC; ++c) {
-      const float* o = F.fx + ((size_t)c * F.Hkv * F.Rg + row) * FXSTRIDE;
-      sp += o[0];
-      ps += o[1];
-      D += o[2 + tid];
-    }
-    const float dn2 = block_sum<HD>(D * D, red);
-    const int js = F.rs.jstar[row];
-    if (tid == 0 && (js < 0 || js >= F.n)) atomicOr(F.status, kStatusNonFinite);
-    if (tid == 0 && js >= 0 && js < F.n) {
-      // R = sum_{i != j*} e_i / e_{j*}; ||a - v_{j*}|| = ||D|| / (ps + sp); p/(1-p) = 1/R
-      const float R = sp / ps;
-      const float tot = ps + sp;
-      const float val = dn2 / (tot * tot) / (R * R);
-      F.rs.rest[row] = R;
-      F.rs.L[row] = 1.0f + R;
-      F.rs.fixval[row] = val;
-      if (!(ps > 0.f) || !finite_f(R)) atomicOr(F.status, kStatusNonFinite);
-      else if (R <= kSingularRest) atomicOr(F.status, kStatusSingular);
-      else F.S[(size_t)g * F.n + js] += val * F.invG;
+  for (int r = 0; r < F.f.Rg; ++r) {
+    const int64_t row = (int64_t)g * F.f.Rg + r;
+    if (!F.f.rs.flag[row]) continue;
+    float R;
+    int bits;
+    const float val = fold_value<HD>(F.f, row, red, &R, &bits);
+    const int js = F.f.rs.jstar[row];
+    if (tid == 0) {
+      if (js < 0 || js >= F.n) {
+        atomicOr(F.status, kStatusNonFinite);
+        continue;
+      }
+      F.f.rs.rest[row] = R;
+      F.f.rs.L[row] = 1.0f + R;
+      F.f.rs.fixval[row] = val;
+      if (bits) atomicOr(F.status, bits);
+      else F.S[(size_t)g * F.n + js] += val * F.f.invG;
     }
   }
 }
@@ -1106,8 +1109,17 @@ size_t mfma_extra_bytes(const Shape& s) {
   return b + 4 * 256;
 }
 
+hipError_t launch_fold(const FoldInfo& fold, int64_t n, int32_t Hkv, float* S, int32_t* status,
+                       hipStream_t st) {
+  if (!fold.flagcount) return hipSuccess;
+  FoldArgs ao{fold, n, S, status};
+  k_fold<<<Hkv, HD, 0, st>>>(ao);
+  return hipGetLastError();
+}
+
 hipError_t launch_mfma_path(const void* q, const void* k, const void* v, const Shape& s,
-                            const Workspace& ws, hipStream_t st, StageEvents* se) {
+                            const Workspace& ws, hipStream_t st, StageEvents* se, bool fold_in_select,
+                            FoldInfo* fold) {
   const Plan p = make_plan(s);
   // carve the path's extra buffers behind the common workspace
   char* extra = (char*)ws.extra;
@@ -1119,7 +1131,8 @@ hipError_t launch_mfma_path(const void* q, const void* k, const void* v, const S
   const float c2 = kLog2e / sqrtf((float)HD);
 
   P1Args a1{(const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v, s.n, s.w, p.Rg, p.nw,
-            p.tpc1, s.Hkv, c2, ws.part, nv};
+            p.tpc1, s.Hkv, c2, ws.part, nv, ws.status, flagcount, (uint32_t*)ws.sel,
+            (int64_t)select_zero_words(s.Hkv)};
   record_stage(se, "start", st);
   {
     const dim3 grid1(p.nch1, p.nrg, s.Hkv);
@@ -1155,9 +1168,14 @@ hipError_t launch_mfma_path(const void* q, const void* k, const void* v, const S
     k_sum_rowgroups<<<(unsigned)((total + 255) / 256), 256, 0, st>>>(Spart, ws.S, total, p.nrg2);
     record_stage(se, "rowgroup_sum", st);
   }
-  FoldArgs ao{s.n, p.Rg, s.Hkv, 1.0f / (float)s.G(), ws.rs, flagcount, fx, ws.S, ws.status};
-  k_fold<<<s.Hkv, HD, 0, st>>>(ao);
-  record_stage(se, "fold", st);
+  FoldInfo fi{flagcount, ws.rs, fx, s.Hkv, p.Rg, FXC, FXSTRIDE, HD, 1.0f / (float)s.G()};
+  if (fold_in_select) {
+    *fold = fi;
+  } else {
+    hipError_t e = launch_fold(fi, s.n, s.Hkv, ws.S, ws.status, st);
+    if (e != hipSuccess) return e;
+    record_stage(se, "fold", st);
+  }
   return hipGetLastError();
 }
 

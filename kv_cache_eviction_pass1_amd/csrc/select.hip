@@ -59,6 +59,7 @@ struct SelArgs {
   uint32_t* seg_lt;   // [Hkv][nseg]: keys below digit 1's bin
   int64_t* seg_off;   // [Hkv][nseg][2]: output offset, tau-equal keys before the segment
   int32_t* status;
+  FoldInfo fold;      // argmax terms of flagged rows to add to S (flagcount null: none)
 };
 
 __device__ __forceinline__ uint32_t score_key(float x) {
@@ -152,6 +153,7 @@ __global__ __launch_bounds__(kT) void k_sel_pool(SelArgs A) {
   const int b = blockIdx.x, g = blockIdx.y;
   __shared__ float sS[kChunk + 2 * kMaxHalo];
   __shared__ uint32_t hist[kBins1];
+  __shared__ float red[kT];
   __shared__ int bad;
   const float* Sg = A.S + (size_t)g * A.n;
   float* Pg = A.P + (size_t)g * A.n;
@@ -185,6 +187,34 @@ __global__ __launch_bounds__(kT) void k_sel_pool(SelArgs A) {
     }
   }
   __syncthreads();
+  if (in_lds && A.fold.flagcount && A.fold.flagcount[g] > 0) {
+    // exact argmax terms of flagged rows, added in row order to this tile's
+    // copy of S (workgroup 0 of the head records them in the row statistics)
+    const FoldInfo& F = A.fold;
+    for (int r = 0; r < F.Rg; ++r) {
+      const int64_t row = (int64_t)g * F.Rg + r;
+      if (!F.rs.flag[row]) continue;
+      float R;
+      int bits;
+      const float val = fold_value<kT>(F, row, red, &R, &bits);
+      const int js = F.rs.jstar[row];
+      if (threadIdx.x == 0) {
+        if (js < 0 || js >= A.n) {
+          if (b == 0) atomicOr(A.status, kStatusNonFinite);
+        } else {
+          if (b == 0) {
+            F.rs.rest[row] = R;
+            F.rs.L[row] = 1.0f + R;
+            F.rs.fixval[row] = val;
+            if (bits) atomicOr(A.status, bits);
+          }
+          const int64_t li = js - (base - half);
+          if (!bits && li >= 0 && li < kChunk + 2 * half) sS[li] += val * F.invG;
+        }
+      }
+    }
+    __syncthreads();
+  }
   uint32_t key[kPer];
   bool nf = false;
 #pragma unroll
@@ -482,6 +512,8 @@ SelPtrs carve_sel(void* scratch, int64_t n, int32_t Hkv) {
 
 size_t select_scratch_bytes(int64_t n, int32_t Hkv) { return carve_sel(nullptr, n, Hkv).bytes + 256; }
 
+size_t select_zero_words(int32_t Hkv) { return (size_t)Hkv * kHistStride; }
+
 hipError_t launch_init(int32_t* status, int32_t* flagcount, void* sel_scratch, int32_t Hkv,
                        hipStream_t st) {
   // the histogram block sits first in the select scratch for every n
@@ -491,8 +523,14 @@ hipError_t launch_init(int32_t* status, int32_t* flagcount, void* sel_scratch, i
 
 hipError_t launch_select(const float* S, int64_t n, int32_t w, int32_t Hkv, int32_t pool_kernel,
                          int64_t n_evict, float* out_scores, int64_t* out_idx, int32_t* status,
-                         void* scratch, hipStream_t st) {
+                         const FoldInfo* fold, void* scratch, hipStream_t st) {
   const SelGeom q = sel_geom(n);
+  if (fold && fold->flagcount && pool_kernel / 2 > kMaxHalo) {
+    // the pool kernel reads S from global memory for such wide kernels: fold first
+    hipError_t e = launch_fold(*fold, n, Hkv, const_cast<float*>(S), status, st);
+    if (e != hipSuccess) return e;
+    fold = nullptr;
+  }
   const SelPtrs p = carve_sel(scratch, n, Hkv);
   SelArgs A{};
   A.S = S;
@@ -512,6 +550,7 @@ hipError_t launch_select(const float* S, int64_t n, int32_t w, int32_t Hkv, int3
   A.seg_lt = p.seg_lt;
   A.seg_off = p.seg_off;
   A.status = status;
+  if (fold) A.fold = *fold;
   k_sel_pool<<<dim3(A.nblk, Hkv), kT, 0, st>>>(A);
   if (n_evict > 0) {
     const dim3 gs((q.nseg + kT - 1) / kT, Hkv);

@@ -113,6 +113,15 @@ def test_mfma_flagged_rows_match_oracle():
     assert np.allclose(rest[fl], rests[fl], rtol=2e-2)
 
 
+@pytest.mark.parametrize("pool", [1, 1031])
+def test_mfma_flagged_rows_pool_widths(pool):
+    """The argmax terms reach the pooled scores both when the pool stage folds
+    them into its LDS tile and when a pool wider than that tile folds them first."""
+    gaps = [0.0, 2.0, 7.0, 8.0, 10.0, 13.0, 16.0, 20.0]
+    case = _dominant_case(gaps, n=3000, seed=3)
+    _compare(case, pool, 1500, f"flagged pool={pool}")
+
+
 def test_mfma_singular_row_rejected():
     gaps = [0.0, 2.0, 30.0, 1.0, 0.5, 0.0, 3.0, 1.0]  # gap 30 -> R ~ 700 e^-30 < 2^-24
     case = _dominant_case(gaps)
