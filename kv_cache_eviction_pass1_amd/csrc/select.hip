@@ -17,11 +17,11 @@
 //            per segment (16+ consecutive keys) the keys below digit 1's bin,
 //            and compacts the keys inside that bin (the candidates) with
 //            their indices, plus their digit-2 histogram;
-//   tau      one workgroup per head: digits 2 and 3 from the candidates give
-//            tau and `need` (how many keys equal to tau are evicted); the
-//            candidates complete the per-segment counts, and a scan turns
-//            them into per-segment output offsets;
-//   write    many workgroups: every segment writes its evicted indices.
+//   write    many workgroups: each derives digits 2 and 3 from the candidates
+//            (tau and `need`, how many keys equal to tau are evicted),
+//            completes the per-segment counts with the candidates, turns the
+//            counts of all earlier segments and its own into output offsets,
+//            and writes its segments' evicted indices.
 #include "dropkv_common.h"
 
 namespace dropkv {
@@ -36,14 +36,8 @@ constexpr int kBins1 = 4096;       // digit 1: key bits 31..20
 constexpr int kBins2 = 4096;       // digit 2: key bits 19..8
 constexpr int kBins3 = 256;        // digit 3: key bits 7..0
 constexpr int kHistStride = kBins1 + kBins2 + 16;  // per head: hist1, hist2, candidate count
-constexpr int kFT = 1024;          // threads of the tau workgroup
-constexpr int kMaxSeg = 8192;      // segments per head (held in the tau workgroup's LDS)
-
-struct SelState {
-  uint32_t tau;
-  uint32_t pad;
-  int64_t need;  // keys equal to tau that are evicted (lowest indices first)
-};
+constexpr int kMaxSeg = 8192;      // segments per head (bounds the prefix each write workgroup sums)
+static_assert(kBins3 == kT, "digit-3 bins: one per thread of the write workgroup");
 
 struct SelArgs {
   const float* S;
@@ -54,10 +48,8 @@ struct SelArgs {
   int seg, nseg;   // keys per segment, segments per head
   bool vec4;       // P rows are 16-byte aligned (n % 4 == 0): vector loads
   uint32_t* hist;  // [Hkv][kHistStride]: hist1, hist2, candidate count (zeroed by init)
-  SelState* st;    // [Hkv]
   uint2* cand;     // [Hkv][n]: (key, index) of the candidates
   uint32_t* seg_lt;   // [Hkv][nseg]: keys below digit 1's bin
-  int64_t* seg_off;   // [Hkv][nseg][2]: output offset, tau-equal keys before the segment
   int32_t* status;
   FoldInfo fold;      // argmax terms of flagged rows to add to S (flagcount null: none)
 };
@@ -67,43 +59,59 @@ __device__ __forceinline__ uint32_t score_key(float x) {
   return (b & 0x80000000u) ? 0u : b;  // -0 (and any negative) sorts as +0
 }
 
-// Exclusive prefix sum over a workgroup of T threads; also returns the total.
+// Inclusive prefix sum over the 64 lanes of a wave with DPP row shifts and
+// row broadcasts (VALU only; lanes without a source read 0).
+__device__ __forceinline__ uint32_t wave_incl_scan(uint32_t x) {
+  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x111, 0xf, 0xf, false);  // row_shr:1
+  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x112, 0xf, 0xf, false);  // row_shr:2
+  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x114, 0xf, 0xf, false);  // row_shr:4
+  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x118, 0xf, 0xf, false);  // row_shr:8
+  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x142, 0xa, 0xf, false);  // row_bcast:15 -> rows 1, 3
+  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x143, 0xc, 0xf, false);  // row_bcast:31 -> rows 2, 3
+  return x;
+}
+
+// Exclusive prefix sums of two values over a workgroup of T threads (one
+// barrier pair for both); totals returned in ta / tb. Sums must stay below 2^32.
 template <int T>
-__device__ __forceinline__ int64_t wg_exclusive_scan(int64_t x, int64_t* wsum, int64_t& total) {
+__device__ __forceinline__ void wg_scan2(uint32_t xa, uint32_t xb, uint32_t (*wsum)[T / 64], uint32_t& ea,
+                                         uint32_t& eb, uint32_t& ta, uint32_t& tb) {
   constexpr int NWV = T / 64;
   const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
-  int64_t v = x;
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    const int64_t y = __shfl_up(v, o, 64);
-    if (lane >= o) v += y;
+  const uint32_t va = wave_incl_scan(xa), vb = wave_incl_scan(xb);
+  if (lane == 63) {
+    wsum[0][wid] = va;
+    wsum[1][wid] = vb;
   }
-  if (lane == 63) wsum[wid] = v;
   __syncthreads();
-  int64_t before = 0, tot = 0;
+  uint32_t ba = 0, bb = 0, sa = 0, sb = 0;
 #pragma unroll
   for (int i = 0; i < NWV; ++i) {
-    const int64_t s = wsum[i];
-    before += (i < wid) ? s : 0;
-    tot += s;
+    const uint32_t wa = wsum[0][i], wb = wsum[1][i];
+    ba += (i < wid) ? wa : 0u;
+    bb += (i < wid) ? wb : 0u;
+    sa += wa;
+    sb += wb;
   }
-  total = tot;
+  ta = sa;
+  tb = sb;
+  ea = ba + va - xa;
+  eb = bb + vb - xb;
   __syncthreads();
-  return before + v - x;
 }
 
 // Bin of a histogram holding the key of 1-based rank `rank`, and the rank
 // inside that bin, from the counts c[] of bins threadIdx.x * PER + i (loaded
 // by the caller); the result is in *bin / *rin for every thread on return.
 template <int T, int PER>
-__device__ __forceinline__ void find_bin_regs(const uint32_t (&c)[PER], int64_t rank, int64_t* wsum, int* bin,
-                                              int64_t* rin) {
-  int64_t loc = 0;
+__device__ __forceinline__ void find_bin_regs(const uint32_t (&c)[PER], int64_t rank, uint32_t (*wsum)[T / 64],
+                                              int* bin, int64_t* rin) {
+  uint32_t loc = 0;
 #pragma unroll
   for (int i = 0; i < PER; ++i) loc += c[i];
-  int64_t total;
-  const int64_t before = wg_exclusive_scan<T>(loc, wsum, total);
-  if (before < rank && rank <= before + loc) {
+  uint32_t before, unused, total, unused2;
+  wg_scan2<T>(loc, 0u, wsum, before, unused, total, unused2);
+  if ((int64_t)before < rank && rank <= (int64_t)before + loc) {
     int64_t r = rank - before;
     int found = -1;
     int64_t rr = 0;
@@ -260,7 +268,7 @@ __global__ __launch_bounds__(kT) void k_sel_cand(SelArgs A) {
   const int g = blockIdx.y;
   const int s = blockIdx.x * kT + threadIdx.x;
   __shared__ uint32_t hist2[kBins2];
-  __shared__ int64_t wsum[kT / 64];
+  __shared__ uint32_t wsum[2][kT / 64];
   __shared__ int sh_bin;
   __shared__ int64_t sh_rin;
   __shared__ uint32_t sh_base;
@@ -296,13 +304,13 @@ __global__ __launch_bounds__(kT) void k_sel_cand(SelArgs A) {
     count16(key);
   }
   if (s < A.nseg) A.seg_lt[(size_t)g * A.nseg + s] = lt;
-  int64_t total;
-  const int64_t before = wg_exclusive_scan<kT>(nc, wsum, total);
-  if (threadIdx.x == 0 && total > 0) sh_base = atomicAdd(gh + kBins1 + kBins2, (uint32_t)total);
+  uint32_t before, unused, total, unused2;
+  wg_scan2<kT>(nc, 0u, wsum, before, unused, total, unused2);
+  if (threadIdx.x == 0 && total > 0) sh_base = atomicAdd(gh + kBins1 + kBins2, total);
   __syncthreads();
   if (nc > 0) {
     uint2* cg = A.cand + (size_t)g * A.n;
-    uint32_t pos = sh_base + (uint32_t)before;
+    uint32_t pos = sh_base + before;
     auto emit16 = [&](const uint32_t (&key)[16], int64_t c0) {
 #pragma unroll
       for (int e = 0; e < 16; ++e)
@@ -322,135 +330,119 @@ __global__ __launch_bounds__(kT) void k_sel_cand(SelArgs A) {
   }
 }
 
-// tau, need and the per-segment output offsets of one head.
-constexpr int kCandRegs = 8;  // candidates per thread held in registers (else re-read)
+// tau, need, the output offsets of this workgroup's segments, and their
+// evicted indices in index order. Every workgroup of a head derives the same
+// tau from the same histograms and candidates. All loads that do not depend
+// on tau are issued together first; the candidates are staged in LDS.
+constexpr int kCandLds = 4096;  // candidates held in LDS (more are re-read from global memory)
 
-__global__ __launch_bounds__(kFT) void k_sel_tau(SelArgs A) {
-  const int g = blockIdx.x;
-  __shared__ uint32_t slt[kMaxSeg];
-  __shared__ uint32_t seq[kMaxSeg];
+__global__ __launch_bounds__(kT) void k_sel_write(SelArgs A) {
+  const int g = blockIdx.y;
+  const int s0 = blockIdx.x * kT;  // first segment of this workgroup
+  const int s = s0 + threadIdx.x;
+  __shared__ uint2 cl[kCandLds];
   __shared__ uint32_t hist3[kBins3];
-  __shared__ int64_t wsum[kFT / 64];
+  __shared__ uint32_t wlt[kT], weq[kT];
+  __shared__ uint32_t wsum[2][kT / 64];
   __shared__ int sh_bin;
   __shared__ int64_t sh_rin;
   const uint32_t* gh = A.hist + (size_t)g * kHistStride;
   const uint32_t* sl = A.seg_lt + (size_t)g * A.nseg;
   const uint2* cg = A.cand + (size_t)g * A.n;
-  // every load that does not depend on tau, issued together
-  uint32_t c1[kBins1 / kFT], c2[kBins2 / kFT];
-  load_bins<kFT, kBins1>(gh, c1);
-  load_bins<kFT, kBins2>(gh + kBins1, c2);
+  const float* Pg = A.P + (size_t)g * A.n;
+  // ---- round 1: histograms, candidate count, segment counts, this segment's first keys
+  uint32_t c1[kBins1 / kT], c2[kBins2 / kT];
+  load_bins<kT, kBins1>(gh, c1);
+  load_bins<kT, kBins2>(gh + kBins1, c2);
   const uint32_t nc = gh[kBins1 + kBins2];
-  uint32_t lts[kMaxSeg / kFT];
+  const uint32_t own_lt = s < A.nseg ? sl[s] : 0u;
+  uint32_t pre[kMaxSeg / kT];  // counts of the segments before this workgroup's
 #pragma unroll
-  for (int i = 0; i < kMaxSeg / kFT; ++i) {
-    const int sg = threadIdx.x + i * kFT;
-    lts[i] = sg < A.nseg ? sl[sg] : 0u;
+  for (int k = 0; k < kMaxSeg / kT; ++k) {
+    const int t = threadIdx.x + k * kT;
+    pre[k] = t < s0 ? sl[t] : 0u;
   }
-  const bool in_regs = nc <= (uint32_t)(kCandRegs * kFT);
-  uint2 cr[kCandRegs];
+  const int64_t j0 = (int64_t)s * A.seg;
+  const int64_t j1 = (s < A.nseg) ? ((j0 + A.seg < A.n) ? j0 + A.seg : A.n) : j0;
+  uint32_t key0[16];
+  load16(Pg, j0, j1, A.vec4, key0);
+  hist3[threadIdx.x] = 0;  // kT == kBins3
+  wlt[threadIdx.x] = 0;
+  weq[threadIdx.x] = 0;
+  // ---- round 2: candidates into LDS
+  const uint32_t ncl = nc < (uint32_t)kCandLds ? nc : (uint32_t)kCandLds;
+  {
+    uint2 c16[kCandLds / kT];
 #pragma unroll
-  for (int i = 0; i < kCandRegs; ++i) {
-    const uint32_t ci = threadIdx.x + i * kFT;
-    cr[i] = (in_regs && ci < nc) ? cg[ci] : make_uint2(0xffffffffu, 0u);
-  }
-  for (int i = threadIdx.x; i < kBins3; i += kFT) hist3[i] = 0;
-#pragma unroll
-  for (int i = 0; i < kMaxSeg / kFT; ++i) {
-    const int sg = threadIdx.x + i * kFT;
-    if (sg < A.nseg) {
-      slt[sg] = lts[i];
-      seq[sg] = 0;
+    for (int k = 0; k < kCandLds / kT; ++k) {
+      const uint32_t i = threadIdx.x + k * kT;
+      c16[k] = i < ncl ? cg[i] : make_uint2(0xffffffffu, 0u);
     }
+#pragma unroll
+    for (int k = 0; k < kCandLds / kT; ++k) cl[threadIdx.x + k * kT] = c16[k];
   }
-  find_bin_regs<kFT, kBins1 / kFT>(c1, A.n_evict, wsum, &sh_bin, &sh_rin);
+  uint32_t before_lt = 0;
+#pragma unroll
+  for (int k = 0; k < kMaxSeg / kT; ++k) before_lt += pre[k];
+  find_bin_regs<kT, kBins1 / kT>(c1, A.n_evict, wsum, &sh_bin, &sh_rin);  // (its barriers also publish cl)
   const uint32_t d1 = (uint32_t)sh_bin;
-  find_bin_regs<kFT, kBins2 / kFT>(c2, sh_rin, wsum, &sh_bin, &sh_rin);
+  find_bin_regs<kT, kBins2 / kT>(c2, sh_rin, wsum, &sh_bin, &sh_rin);
   const uint32_t d2 = (uint32_t)sh_bin;
   const int64_t r2 = sh_rin;
-  auto digit3 = [&](uint32_t key) {
-    if (key != 0xffffffffu && ((key >> 8) & 0xfffu) == d2) atomicAdd(&hist3[key & 0xffu], 1u);
-  };
-  if (in_regs) {
-#pragma unroll
-    for (int i = 0; i < kCandRegs; ++i) digit3(cr[i].x);
-  } else {
-    for (uint32_t i = threadIdx.x; i < nc; i += kFT) digit3(cg[i].x);
+  auto cand = [&](uint32_t i) { return i < (uint32_t)kCandLds ? cl[i] : cg[i]; };
+  for (uint32_t i = threadIdx.x; i < nc; i += kT) {
+    const uint32_t key = cand(i).x;
+    if (((key >> 8) & 0xfffu) == d2) atomicAdd(&hist3[key & 0xffu], 1u);
   }
   __syncthreads();
   uint32_t c3[1];
-  c3[0] = threadIdx.x < kBins3 ? hist3[threadIdx.x] : 0u;
-  find_bin_regs<kFT, 1>(c3, r2, wsum, &sh_bin, &sh_rin);
+  c3[0] = hist3[threadIdx.x];
+  find_bin_regs<kT, 1>(c3, r2, wsum, &sh_bin, &sh_rin);
   const uint32_t tau = (d1 << 20) | (d2 << 8) | (uint32_t)sh_bin;
   const int64_t need = sh_rin;
-  if (threadIdx.x == 0) {
-    A.st[g].tau = tau;
-    A.st[g].need = need;
-  }
-  // per-segment counts: below tau = below digit 1's bin + candidates below tau
-  auto fix = [&](uint2 c) {
-    if (c.x == 0xffffffffu) return;
+  // candidates below / equal to tau: before this workgroup's segments, or in one of them
+  uint32_t cb_lt = 0, cb_eq = 0;
+  for (uint32_t i = threadIdx.x; i < nc; i += kT) {
+    const uint2 c = cand(i);
+    if (c.x > tau) continue;
     const int sg = (int)(c.y / (uint32_t)A.seg);
-    if (c.x < tau) atomicAdd(&slt[sg], 1u);
-    else if (c.x == tau) atomicAdd(&seq[sg], 1u);
-  };
-  if (in_regs) {
-#pragma unroll
-    for (int i = 0; i < kCandRegs; ++i) fix(cr[i]);
-  } else {
-    for (uint32_t i = threadIdx.x; i < nc; i += kFT) fix(cg[i]);
+    if (c.x < tau) {
+      if (sg < s0) ++cb_lt;
+      else if (sg < s0 + kT) atomicAdd(&wlt[sg - s0], 1u);
+    } else {
+      if (sg < s0) ++cb_eq;
+      else if (sg < s0 + kT) atomicAdd(&weq[sg - s0], 1u);
+    }
   }
-  __syncthreads();
-  // thread t owns segments [t spt, (t+1) spt): offsets by one workgroup scan
-  const int spt = (A.nseg + kFT - 1) / kFT;
-  const int s0 = threadIdx.x * spt;
-  int64_t l = 0, e = 0;
-  for (int sg = s0; sg < s0 + spt && sg < A.nseg; ++sg) {
-    l += slt[sg];
-    e += seq[sg];
-  }
-  int64_t tot;
-  // both counts are below 2^31: one scan of (eq << 32 | lt)
-  const int64_t pk = wg_exclusive_scan<kFT>((e << 32) | l, wsum, tot);
-  int64_t lb = pk & 0xffffffffLL, eb = pk >> 32;
-  int64_t* so = A.seg_off + (size_t)g * A.nseg * 2;
-  for (int sg = s0; sg < s0 + spt && sg < A.nseg; ++sg) {
-    const int64_t taken_eq = eb < need ? eb : need;
-    so[2 * sg] = lb + taken_eq;
-    so[2 * sg + 1] = eb;
-    lb += slt[sg];
-    eb += seq[sg];
-  }
-}
-
-// Writes the evicted indices of each segment, in index order.
-__global__ __launch_bounds__(kT) void k_sel_write(SelArgs A) {
-  const int g = blockIdx.y;
-  const int s = blockIdx.x * kT + threadIdx.x;
+  // counts below 2^31 (n fits in int32): 32-bit scans
+  uint32_t x0, x1, tot_lt, tot_eq;
+  wg_scan2<kT>((uint32_t)(before_lt + cb_lt), (uint32_t)cb_eq, wsum, x0, x1, tot_lt, tot_eq);
+  uint32_t lpre, epre, t0, t1;
+  wg_scan2<kT>(own_lt + wlt[threadIdx.x], weq[threadIdx.x], wsum, lpre, epre, t0, t1);
+  const int64_t lb = (int64_t)tot_lt + lpre;
+  int64_t eqb = (int64_t)tot_eq + epre;
   if (s >= A.nseg) return;
-  const uint32_t tau = A.st[g].tau;
-  const int64_t need = A.st[g].need;
-  const int64_t* so = A.seg_off + ((size_t)g * A.nseg + s) * 2;
-  int64_t pos = so[0], eqb = so[1];
-  const float* Pg = A.P + (size_t)g * A.n;
+  int64_t pos = lb + (eqb < need ? eqb : need);
   int64_t* og = A.idx + (size_t)g * A.n_evict;
-  const int64_t j0 = (int64_t)s * A.seg;
-  const int64_t j1 = (j0 + A.seg < A.n) ? j0 + A.seg : A.n;
-  for (int64_t c0 = j0; c0 < j1; c0 += 16) {
-    uint32_t key[16];
-    load16(Pg, c0, j1, A.vec4, key);
+  auto emit16 = [&](const uint32_t (&key)[16], int64_t q0) {
 #pragma unroll
-    for (int e = 0; e < 16; ++e) {
-      bool take = key[e] < tau;
-      if (key[e] == tau) {
+    for (int k = 0; k < 16; ++k) {
+      bool take = key[k] < tau;
+      if (key[k] == tau) {
         take = eqb < need;
         ++eqb;
       }
       if (take) {
-        if (pos < A.n_evict) og[pos] = c0 + e;
+        if (pos < A.n_evict) og[pos] = q0 + k;
         ++pos;
       }
     }
+  };
+  emit16(key0, j0);
+  for (int64_t q0 = j0 + 16; q0 < j1; q0 += 16) {
+    uint32_t key[16];
+    load16(Pg, q0, j1, A.vec4, key);
+    emit16(key, q0);
   }
 }
 
@@ -482,10 +474,8 @@ SelGeom sel_geom(int64_t n) {
 
 struct SelPtrs {
   uint32_t* hist;
-  SelState* st;
   uint2* cand;
   uint32_t* seg_lt;
-  int64_t* seg_off;
   size_t bytes;
 };
 
@@ -500,10 +490,8 @@ SelPtrs carve_sel(void* scratch, int64_t n, int32_t Hkv) {
     return p;
   };
   r.hist = (uint32_t*)take(sizeof(uint32_t) * (size_t)Hkv * kHistStride);
-  r.st = (SelState*)take(sizeof(SelState) * (size_t)Hkv);
   r.cand = (uint2*)take(sizeof(uint2) * (size_t)Hkv * (size_t)n);
   r.seg_lt = (uint32_t*)take(sizeof(uint32_t) * (size_t)Hkv * q.nseg);
-  r.seg_off = (int64_t*)take(sizeof(int64_t) * 2 * (size_t)Hkv * q.nseg);
   r.bytes = off;
   return r;
 }
@@ -545,17 +533,14 @@ hipError_t launch_select(const float* S, int64_t n, int32_t w, int32_t Hkv, int3
   A.nseg = q.nseg;
   A.vec4 = (n % 4 == 0) && ((uintptr_t)out_scores % 16 == 0);
   A.hist = p.hist;
-  A.st = p.st;
   A.cand = p.cand;
   A.seg_lt = p.seg_lt;
-  A.seg_off = p.seg_off;
   A.status = status;
   if (fold) A.fold = *fold;
   k_sel_pool<<<dim3(A.nblk, Hkv), kT, 0, st>>>(A);
   if (n_evict > 0) {
     const dim3 gs((q.nseg + kT - 1) / kT, Hkv);
     k_sel_cand<<<gs, kT, 0, st>>>(A);
-    k_sel_tau<<<Hkv, kFT, 0, st>>>(A);
     k_sel_write<<<gs, kT, 0, st>>>(A);
   }
   return hipGetLastError();
