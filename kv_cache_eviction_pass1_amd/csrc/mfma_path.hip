@@ -278,8 +278,12 @@ __device__ __forceinline__ void p1_tile(float c2, const char* kb, const char* vb
 #pragma unroll
     for (int ks = 0; ks < 8; ++ks) ka[ks] = ld16(kt + off.k[ks]);
     f32x16 x = {};
+    // Raised issue priority over each MFMA group: the wave sharing this SIMD
+    // then tends to be in its VALU phase meanwhile (measured ~3% faster).
+    __builtin_amdgcn_s_setprio(1);
 #pragma unroll
     for (int ks = 0; ks < 8; ++ks) x = mfma(ka[ks], qb[ks], x);
+    __builtin_amdgcn_s_setprio(0);
     const int64_t tokbase = tokbase_tile + sub * 32;
     if (MASK) {  // causal tail / ragged end: hide keys after this row's position
 #pragma unroll
@@ -330,10 +334,12 @@ __device__ __forceinline__ void p1_tile(float c2, const char* kb, const char* vb
 #pragma unroll
       for (int db = 0; db < 4; ++db)
         va[s][db] = tr_pair(vt + s * 16 * 256 + off.v[2 * db], vt + s * 16 * 256 + off.v[2 * db + 1]);
+    __builtin_amdgcn_s_setprio(1);
 #pragma unroll
     for (int s = 0; s < 2; ++s)
 #pragma unroll
       for (int db = 0; db < 4; ++db) O[db] = mfma(va[s][db], pb[s], O[db]);
+    __builtin_amdgcn_s_setprio(0);
   }
 }
 
