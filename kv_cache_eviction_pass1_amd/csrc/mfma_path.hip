@@ -532,16 +532,16 @@ __global__ __launch_bounds__(256) void k_merge(MergeArgs M) {
     l += lw;
     const int cn = (M.nchunks - c0) < 64 ? (M.nchunks - c0) : 64;
     int cc = 0;
-    for (; cc + 8 <= cn; cc += 8) {
-      float2 av[8];
-      float sv[8];
+    for (; cc + 16 <= cn; cc += 16) {  // sixteen chunk rows in flight
+      float2 av[16];
+      float sv[16];
 #pragma unroll
-      for (int u = 0; u < 8; ++u) {
+      for (int u = 0; u < 16; ++u) {
         av[u] = *(const float2*)(prow + (size_t)(c0 + cc + u) * cstride + 2 * lane);
         sv[u] = __shfl(sc, cc + u, 64);
       }
 #pragma unroll
-      for (int u = 0; u < 8; ++u) {
+      for (int u = 0; u < 16; ++u) {
         a0 = fmaf(av[u].x, sv[u], a0);
         a1 = fmaf(av[u].y, sv[u], a1);
       }
@@ -616,12 +616,14 @@ struct FixArgs {
 };
 
 // Per flagged row and token chunk: sp = sum_{i != j*} p_i, ps = p_{j*} and
-// D = sum_{i != j*} p_i (v_i - v_{j*}), with p_i = 2^{x_i c - bias}.
-__global__ __launch_bounds__(256) void k_fixup(FixArgs F) {
-  const int c = blockIdx.x, g = blockIdx.y;
+// D = sum_{i != j*} p_i (v_i - v_{j*}), with p_i = 2^{x_i c - bias}; for a
+// workgroup of T >= 128 threads (T/128 threads per dimension of D).
+template <int T>
+__device__ __forceinline__ void fixup_chunk(const FixArgs& F, int c, int g) {
+  static_assert(T >= HD && T % HD == 0, "fix-up needs a multiple of 128 threads");
   if (F.flagcount[g] == 0) return;
   const int tid = threadIdx.x;
-  __shared__ float qs[HD], vstar[HD], ptile[256], red[256], redD[256];
+  __shared__ float qs[HD], vstar[HD], ptile[T], red[T], redD[T];
   const int64_t cs = (F.n + FXC - 1) / FXC;
   const int64_t c0 = c * cs;
   const int64_t c1 = (c0 + cs < F.n) ? c0 + cs : F.n;
@@ -640,8 +642,8 @@ __global__ __launch_bounds__(256) void k_fixup(FixArgs F) {
     }
     __syncthreads();
     float sp = 0.f, ps = 0.f, Dacc = 0.f;
-    const int dim = tid & (HD - 1), sub = tid >> 7;
-    for (int64_t b = c0; b < hi; b += 256) {
+    const int dim = tid & (HD - 1), sub = tid / HD;
+    for (int64_t b = c0; b < hi; b += T) {
       const int64_t j = b + tid;
       float p = 0.f;
       if (j < hi) {
@@ -654,21 +656,27 @@ __global__ __launch_bounds__(256) void k_fixup(FixArgs F) {
       }
       ptile[tid] = p;
       __syncthreads();
-      const int cnt = (int)((hi - b) < 256 ? (hi - b) : 256);
-      for (int t = sub; t < cnt; t += 2) {
+      const int cnt = (int)((hi - b) < T ? (hi - b) : T);
+      for (int t = sub; t < cnt; t += T / HD) {
         const float vv = bf16_to_f32(F.v[((size_t)g * F.n + b + t) * HD + dim]);
         Dacc = fmaf(ptile[t], vv - vstar[dim], Dacc);
       }
       __syncthreads();
     }
     redD[tid] = Dacc;
-    const float spt = block_sum<256>(sp, red);
-    const float pst = block_sum<256>(ps, red);
+    const float spt = block_sum<T>(sp, red);
+    const float pst = block_sum<T>(ps, red);
     float* o = F.fx + ((size_t)c * F.Hkv * F.Rg + row) * FXSTRIDE;
-    if (tid < HD) o[2 + tid] = redD[tid] + redD[tid + HD];
+    if (tid < HD) {
+      float d = 0.f;
+      for (int q = 0; q < T / HD; ++q) d += redD[q * HD + tid];
+      o[2 + tid] = d;
+    }
     if (tid == 0) { o[0] = spt; o[1] = pst; }
   }
 }
+
+__global__ __launch_bounds__(256) void k_fixup(FixArgs F) { fixup_chunk<256>(F, blockIdx.x, blockIdx.y); }
 
 struct FoldArgs {
   FoldInfo f;
@@ -903,7 +911,14 @@ __device__ __forceinline__ float p2_sub(const char* kt, const char* vt, float nv
 }
 
 template <int NW>
-__global__ __launch_bounds__(NW * 64) void k_pass2(P2Args P) {
+__global__ __launch_bounds__(NW * 64) void k_pass2(P2Args P, FixArgs F) {
+  if (NW >= 2 && blockIdx.x >= gridDim.x - (NW >= 2 ? FXC : 0)) {
+    // the argmax fix-up (independent of pass 2) runs as FXC extra workgroups per head
+    if constexpr (NW >= 2) {
+      if (blockIdx.y == 0) fixup_chunk<NW * 64>(F, blockIdx.x - (gridDim.x - FXC), blockIdx.z);
+    }
+    return;
+  }
   __shared__ __attribute__((aligned(1024))) char kbuf[3][TILE_BYTES];
   __shared__ __attribute__((aligned(1024))) char vbuf[3][TILE_BYTES];
   __shared__ float red3[3][NW][TT];
@@ -1157,16 +1172,18 @@ hipError_t launch_mfma_path(const void* q, const void* k, const void* v, const S
   record_stage(se, "merge", st);
   FixArgs af{(const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v, s.n, s.w, p.Rg, s.Hkv, c2,
              ws.rs, flagcount, fx};
-  k_fixup<<<dim3(FXC, s.Hkv), 256, 0, st>>>(af);
-  record_stage(se, "fixup", st);
+  if (p.nw2 < 2) {  // wider workgroups run the fix-up inside pass 2
+    k_fixup<<<dim3(FXC, s.Hkv), 256, 0, st>>>(af);
+    record_stage(se, "fixup", st);
+  }
   P2Args a2{(const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v, s.n, s.w, p.Rg, p.nw2,
             p.tpc2, s.Hkv, c2, 1.0f / (float)s.G(), ws.rs, nv, flagcount, Spart};
-  const dim3 grid2(p.nch2, p.nrg2, s.Hkv);
+  const dim3 grid2(p.nch2 + (p.nw2 >= 2 ? FXC : 0), p.nrg2, s.Hkv);
   switch (p.nw2) {
-    case 8: k_pass2<8><<<grid2, 512, 0, st>>>(a2); break;
-    case 4: k_pass2<4><<<grid2, 256, 0, st>>>(a2); break;
-    case 2: k_pass2<2><<<grid2, 128, 0, st>>>(a2); break;
-    default: k_pass2<1><<<grid2, 64, 0, st>>>(a2); break;
+    case 8: k_pass2<8><<<grid2, 512, 0, st>>>(a2, af); break;
+    case 4: k_pass2<4><<<grid2, 256, 0, st>>>(a2, af); break;
+    case 2: k_pass2<2><<<grid2, 128, 0, st>>>(a2, af); break;
+    default: k_pass2<1><<<grid2, 64, 0, st>>>(a2, af); break;
   }
   record_stage(se, "pass2", st);
   if (p.nrg2 > 1) {
