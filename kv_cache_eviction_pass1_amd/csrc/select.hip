@@ -9,12 +9,14 @@
 // Scores are non-negative, so the IEEE-754 bit pattern of a pooled score,
 // read as uint32, orders exactly like its value (+inf = 0x7f800000 sorts
 // last). The n_evict-th smallest key tau is found by a radix select whose
-// digits are key bits 31..20, 19..8 and 7..0. Four kernels, with no
+// digits are key bits 31..20, 19..8 and 7..0. Three kernels, with no
 // device-scope fence inside any of them (on this multi-XCD part a fence
-// writes back the L2, which costs far more than a kernel boundary):
+// writes back the L2, which costs far more than a kernel boundary); the
+// histograms and the candidate count start at zero (cleared by the first
+// kernel of the scoring path, or by an init launch):
 //   pool     many workgroups: pooled scores -> out_scores, histogram of digit 1;
 //   cand     many workgroups: each derives digit 1 from the histogram, counts
-//            per segment (16+ consecutive keys) the keys below digit 1's bin,
+//            per segment (8+ consecutive keys) the keys below digit 1's bin,
 //            and compacts the keys inside that bin (the candidates) with
 //            their indices, plus their digit-2 histogram;
 //   write    many workgroups: each derives digits 2 and 3 from the candidates
@@ -22,22 +24,32 @@
 //            completes the per-segment counts with the candidates, turns the
 //            counts of all earlier segments and its own into output offsets,
 //            and writes its segments' evicted indices.
+#include <type_traits>
+
 #include "dropkv_common.h"
 
 namespace dropkv {
 
 namespace {
 
-constexpr int kT = 256;            // threads per workgroup (pool, cand, write)
-constexpr int kPer = 16;           // pool: elements per thread
-constexpr int kChunk = kT * kPer;  // pool: elements per workgroup
+// 512 threads: two waves per SIMD hide part of the latency of these short,
+// one-pass kernels (one workgroup per CU at the 128K shape)
+constexpr int kT = 512;            // threads per workgroup (pool, cand, write)
+constexpr int kChunk = 4096;       // pool: elements per workgroup
+constexpr int kPer = kChunk / kT;  // pool: elements per thread
+constexpr int kKeys = 8;           // cand / write: keys per load group (segments are multiples of it)
 constexpr int kMaxHalo = 512;      // pooling halo held in LDS (larger kernels read global memory)
 constexpr int kBins1 = 4096;       // digit 1: key bits 31..20
 constexpr int kBins2 = 4096;       // digit 2: key bits 19..8
 constexpr int kBins3 = 256;        // digit 3: key bits 7..0
 constexpr int kHistStride = kBins1 + kBins2 + 16;  // per head: hist1, hist2, candidate count
-constexpr int kMaxSeg = 8192;      // segments per head (bounds the prefix each write workgroup sums)
-static_assert(kBins3 == kT, "digit-3 bins: one per thread of the write workgroup");
+constexpr int kBinsPer = kBins1 / kT;  // digit-1 and digit-2 bins per thread
+constexpr int kMaxWg = 32;         // cand / write workgroups per head
+constexpr int kMaxSeg = kMaxWg * kT;  // segments per head
+static_assert(kBins1 == kBins2 && kBinsPer % 4 == 0, "load_bins: whole 16-byte groups per thread");
+static_assert(kChunk % kT == 0 && kKeys % 4 == 0, "pool and key groups");
+static_assert(kMaxWg <= kT, "write: one earlier workgroup per thread");
+static_assert(kBins3 <= kT, "digit-3 bins: at most one per thread of the write workgroup");
 
 struct SelArgs {
   const float* S;
@@ -50,6 +62,7 @@ struct SelArgs {
   uint32_t* hist;  // [Hkv][kHistStride]: hist1, hist2, candidate count (zeroed by init)
   uint2* cand;     // [Hkv][n]: (key, index) of the candidates
   uint32_t* seg_lt;   // [Hkv][nseg]: keys below digit 1's bin
+  uint32_t* wg_lt;    // [Hkv][kMaxWg]: the same, summed over each cand workgroup's segments
   int32_t* status;
   FoldInfo fold;      // argmax terms of flagged rows to add to S (flagcount null: none)
 };
@@ -129,21 +142,26 @@ __device__ __forceinline__ void find_bin_regs(const uint32_t (&c)[PER], int64_t 
   __syncthreads();
 }
 
-template <int T, int NB>
-__device__ __forceinline__ void load_bins(const uint32_t* h, uint32_t (&c)[(NB + T - 1) / T]) {
-  constexpr int PER = (NB + T - 1) / T;
+// Counts of bins kBinsPer * threadIdx.x .. + kBinsPer - 1 of a 16-byte
+// aligned histogram of kBins1 bins, in 16-byte loads.
+__device__ __forceinline__ void load_bins(const uint32_t* h, uint32_t (&c)[kBinsPer]) {
+  const uint4* p = reinterpret_cast<const uint4*>(h) + threadIdx.x * (kBinsPer / 4);
 #pragma unroll
-  for (int i = 0; i < PER; ++i) {
-    const int b = threadIdx.x * PER + i;
-    c[i] = b < NB ? h[b] : 0u;
+  for (int q = 0; q < kBinsPer / 4; ++q) {
+    const uint4 v = p[q];
+    c[4 * q] = v.x;
+    c[4 * q + 1] = v.y;
+    c[4 * q + 2] = v.z;
+    c[4 * q + 3] = v.w;
   }
 }
 
-// Keys [j0, j0 + 16) of a head, 0xffffffff from `end` on.
-__device__ __forceinline__ void load16(const float* Pg, int64_t j0, int64_t end, bool vec4, uint32_t (&key)[16]) {
-  if (vec4 && j0 + 16 <= end) {
+// Keys [j0, j0 + kKeys) of a head, 0xffffffff from `end` on.
+__device__ __forceinline__ void load_keys(const float* Pg, int64_t j0, int64_t end, bool vec4,
+                                          uint32_t (&key)[kKeys]) {
+  if (vec4 && j0 + kKeys <= end) {
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
+    for (int q = 0; q < kKeys / 4; ++q) {
       const float4 f = *(const float4*)(Pg + j0 + 4 * q);
       key[4 * q] = score_key(f.x);
       key[4 * q + 1] = score_key(f.y);
@@ -152,7 +170,7 @@ __device__ __forceinline__ void load16(const float* Pg, int64_t j0, int64_t end,
     }
   } else {
 #pragma unroll
-    for (int e = 0; e < 16; ++e) key[e] = (j0 + e < end) ? score_key(Pg[j0 + e]) : 0xffffffffu;
+    for (int e = 0; e < kKeys; ++e) key[e] = (j0 + e < end) ? score_key(Pg[j0 + e]) : 0xffffffffu;
   }
 }
 
@@ -168,6 +186,8 @@ __global__ __launch_bounds__(kT) void k_sel_pool(SelArgs A) {
   const int64_t base = (int64_t)b * kChunk;
   const int half = A.pool_half;
   const bool in_lds = half <= kMaxHalo;
+  // issued first: its latency overlaps the loads of the tile
+  const int flagged = (in_lds && A.fold.flagcount) ? A.fold.flagcount[g] : 0;
   if (threadIdx.x == 0) bad = 0;
   for (int i = threadIdx.x; i < kBins1; i += kT) hist[i] = 0;
   if (in_lds) {
@@ -195,7 +215,7 @@ __global__ __launch_bounds__(kT) void k_sel_pool(SelArgs A) {
     }
   }
   __syncthreads();
-  if (in_lds && A.fold.flagcount && A.fold.flagcount[g] > 0) {
+  if (flagged > 0) {
     // exact argmax terms of flagged rows, added in row order to this tile's
     // copy of S (workgroup 0 of the head records them in the row statistics)
     const FoldInfo& F = A.fold;
@@ -223,28 +243,41 @@ __global__ __launch_bounds__(kT) void k_sel_pool(SelArgs A) {
     }
     __syncthreads();
   }
-  uint32_t key[kPer];
+  // token base + e * kT + threadIdx.x: consecutive threads, consecutive tokens
+  float mx[kPer];
   bool nf = false;
+  if (in_lds) {
 #pragma unroll
-  for (int e = 0; e < kPer; ++e) {
-    const int li = e * kT + threadIdx.x;  // consecutive threads, consecutive tokens
-    const int64_t j = base + li;
-    key[e] = 0xffffffffu;
-    if (j < A.n) {
-      float mx;
-      if (in_lds) {
-        const int c = li + half;
-        mx = sS[c];
-        if (!finite_f(mx)) nf = true;
-        for (int t = c - half; t <= c + half; ++t) mx = fmaxf(mx, sS[t]);
-      } else {
-        mx = Sg[j];
-        if (!finite_f(mx)) nf = true;
+    for (int e = 0; e < kPer; ++e) {
+      mx[e] = sS[half + e * kT + threadIdx.x];
+      if (base + e * kT + threadIdx.x < A.n && !finite_f(mx[e])) nf = true;  // max() would hide a NaN
+    }
+    // one window offset at a time: the kPer LDS reads of a step are independent
+    for (int t = 0; t <= 2 * half; ++t) {
+#pragma unroll
+      for (int e = 0; e < kPer; ++e) mx[e] = fmaxf(mx[e], sS[t + e * kT + threadIdx.x]);
+    }
+  } else {
+#pragma unroll
+    for (int e = 0; e < kPer; ++e) {
+      const int64_t j = base + e * kT + threadIdx.x;
+      mx[e] = 0.0f;
+      if (j < A.n) {
+        mx[e] = Sg[j];
+        if (!finite_f(mx[e])) nf = true;
         const int64_t lo = j - half < 0 ? 0 : j - half;
         const int64_t hi = j + half >= A.n ? A.n - 1 : j + half;
-        for (int64_t t = lo; t <= hi; ++t) mx = fmaxf(mx, Sg[t]);
+        for (int64_t t = lo; t <= hi; ++t) mx[e] = fmaxf(mx[e], Sg[t]);
       }
-      const float p = (j >= A.n - A.w) ? INFINITY : mx;
+    }
+  }
+  uint32_t key[kPer];
+#pragma unroll
+  for (int e = 0; e < kPer; ++e) {
+    const int64_t j = base + e * kT + threadIdx.x;
+    key[e] = 0xffffffffu;
+    if (j < A.n) {
+      const float p = (j >= A.n - A.w) ? INFINITY : mx[e];
       Pg[j] = p;
       key[e] = score_key(p);
     }
@@ -276,18 +309,18 @@ __global__ __launch_bounds__(kT) void k_sel_cand(SelArgs A) {
   const float* Pg = A.P + (size_t)g * A.n;
   const int64_t j0 = (int64_t)s * A.seg;
   const int64_t j1 = (s < A.nseg) ? ((j0 + A.seg < A.n) ? j0 + A.seg : A.n) : j0;
-  // the segment's first 16 keys and the digit-1 counts are loaded together
-  uint32_t key0[16];
-  load16(Pg, j0, j1, A.vec4, key0);
-  uint32_t c1[kBins1 / kT];
-  load_bins<kT, kBins1>(gh, c1);
+  // the segment's first keys and the digit-1 counts are loaded together
+  uint32_t key0[kKeys];
+  load_keys(Pg, j0, j1, A.vec4, key0);
+  uint32_t c1[kBinsPer];
+  load_bins(gh, c1);
   for (int i = threadIdx.x; i < kBins2; i += kT) hist2[i] = 0;
-  find_bin_regs<kT, kBins1 / kT>(c1, A.n_evict, wsum, &sh_bin, &sh_rin);
+  find_bin_regs<kT, kBinsPer>(c1, A.n_evict, wsum, &sh_bin, &sh_rin);
   const uint32_t d1 = (uint32_t)sh_bin;
   uint32_t lt = 0, nc = 0;
-  auto count16 = [&](const uint32_t (&key)[16]) {
+  auto count_keys = [&](const uint32_t (&key)[kKeys]) {
 #pragma unroll
-    for (int e = 0; e < 16; ++e) {
+    for (int e = 0; e < kKeys; ++e) {
       if (key[e] == 0xffffffffu) continue;
       const uint32_t top = key[e] >> 20;
       lt += top < d1 ? 1u : 0u;
@@ -297,152 +330,220 @@ __global__ __launch_bounds__(kT) void k_sel_cand(SelArgs A) {
       }
     }
   };
-  count16(key0);
-  for (int64_t c0 = j0 + 16; c0 < j1; c0 += 16) {
-    uint32_t key[16];
-    load16(Pg, c0, j1, A.vec4, key);
-    count16(key);
+  count_keys(key0);
+  for (int64_t c0 = j0 + kKeys; c0 < j1; c0 += kKeys) {
+    uint32_t key[kKeys];
+    load_keys(Pg, c0, j1, A.vec4, key);
+    count_keys(key);
   }
   if (s < A.nseg) A.seg_lt[(size_t)g * A.nseg + s] = lt;
-  uint32_t before, unused, total, unused2;
-  wg_scan2<kT>(nc, 0u, wsum, before, unused, total, unused2);
-  if (threadIdx.x == 0 && total > 0) sh_base = atomicAdd(gh + kBins1 + kBins2, total);
-  __syncthreads();
-  if (nc > 0) {
-    uint2* cg = A.cand + (size_t)g * A.n;
-    uint32_t pos = sh_base + before;
-    auto emit16 = [&](const uint32_t (&key)[16], int64_t c0) {
-#pragma unroll
-      for (int e = 0; e < 16; ++e)
-        if (key[e] != 0xffffffffu && (key[e] >> 20) == d1) cg[pos++] = make_uint2(key[e], (uint32_t)(c0 + e));
-    };
-    emit16(key0, j0);
-    for (int64_t c0 = j0 + 16; c0 < j1; c0 += 16) {
-      uint32_t key[16];
-      load16(Pg, c0, j1, A.vec4, key);
-      emit16(key, c0);
-    }
+  uint32_t before, unused, total, total_lt;
+  wg_scan2<kT>(nc, lt, wsum, before, unused, total, total_lt);
+  if (threadIdx.x == 0) {
+    A.wg_lt[(size_t)g * kMaxWg + blockIdx.x] = total_lt;
+    if (total > 0) sh_base = atomicAdd(gh + kBins1 + kBins2, total);
   }
-  if (total > 0) {
+  if (total > 0) {  // digit-2 counts (the barrier of the scan made hist2 complete)
     uint32_t* gh2 = gh + kBins1;
     for (int i = threadIdx.x; i < kBins2; i += kT)
       if (hist2[i]) atomicAdd(gh2 + i, hist2[i]);
+  }
+  __syncthreads();  // sh_base
+  if (nc > 0) {
+    uint2* cg = A.cand + (size_t)g * A.n;
+    uint32_t pos = sh_base + before;
+    auto emit_keys = [&](const uint32_t (&key)[kKeys], int64_t c0) {
+#pragma unroll
+      for (int e = 0; e < kKeys; ++e)
+        if (key[e] != 0xffffffffu && (key[e] >> 20) == d1) cg[pos++] = make_uint2(key[e], (uint32_t)(c0 + e));
+    };
+    emit_keys(key0, j0);
+    for (int64_t c0 = j0 + kKeys; c0 < j1; c0 += kKeys) {
+      uint32_t key[kKeys];
+      load_keys(Pg, c0, j1, A.vec4, key);
+      emit_keys(key, c0);
+    }
   }
 }
 
 // tau, need, the output offsets of this workgroup's segments, and their
 // evicted indices in index order. Every workgroup of a head derives the same
-// tau from the same histograms and candidates. All loads that do not depend
-// on tau are issued together first; the candidates are staged in LDS.
-constexpr int kCandLds = 4096;  // candidates held in LDS (more are re-read from global memory)
+// tau from the same histograms and candidates. Everything that does not
+// depend on tau is loaded in one round, the first kCandLds candidate slots
+// included (read before their count is known; slots past it are ignored).
+constexpr int kCandLds = 4096;        // candidates held in LDS (more are re-read from global memory)
+constexpr int kTie = 1024;            // candidates sharing tau's digits 1 and 2, listed (more: a second pass)
+constexpr int kStage = 2 * kCandLds;  // evicted indices staged per workgroup, as int32 over the candidate buffer
 
 __global__ __launch_bounds__(kT) void k_sel_write(SelArgs A) {
   const int g = blockIdx.y;
   const int s0 = blockIdx.x * kT;  // first segment of this workgroup
   const int s = s0 + threadIdx.x;
-  __shared__ uint2 cl[kCandLds];
+  __shared__ uint2 cl[kCandLds + kT / 2];  // candidates; later kStage + kT staged uint32 slots
+  __shared__ uint2 tie[kTie];
   __shared__ uint32_t hist3[kBins3];
   __shared__ uint32_t wlt[kT], weq[kT];
   __shared__ uint32_t wsum[2][kT / 64];
   __shared__ int sh_bin;
   __shared__ int64_t sh_rin;
+  __shared__ uint32_t ntie;
   const uint32_t* gh = A.hist + (size_t)g * kHistStride;
   const uint32_t* sl = A.seg_lt + (size_t)g * A.nseg;
   const uint2* cg = A.cand + (size_t)g * A.n;
   const float* Pg = A.P + (size_t)g * A.n;
-  // ---- round 1: histograms, candidate count, segment counts, this segment's first keys
-  uint32_t c1[kBins1 / kT], c2[kBins2 / kT];
-  load_bins<kT, kBins1>(gh, c1);
-  load_bins<kT, kBins2>(gh + kBins1, c2);
+  // ---- the one round of loads
+  uint32_t c1[kBinsPer], c2[kBinsPer];
+  load_bins(gh, c1);
+  load_bins(gh + kBins1, c2);
   const uint32_t nc = gh[kBins1 + kBins2];
   const uint32_t own_lt = s < A.nseg ? sl[s] : 0u;
-  uint32_t pre[kMaxSeg / kT];  // counts of the segments before this workgroup's
-#pragma unroll
-  for (int k = 0; k < kMaxSeg / kT; ++k) {
-    const int t = threadIdx.x + k * kT;
-    pre[k] = t < s0 ? sl[t] : 0u;
-  }
+  // keys below digit 1's bin in the workgroups of segments before this one's
+  const uint32_t prev_lt = (int)threadIdx.x < (int)blockIdx.x ? A.wg_lt[(size_t)g * kMaxWg + threadIdx.x] : 0u;
   const int64_t j0 = (int64_t)s * A.seg;
   const int64_t j1 = (s < A.nseg) ? ((j0 + A.seg < A.n) ? j0 + A.seg : A.n) : j0;
-  uint32_t key0[16];
-  load16(Pg, j0, j1, A.vec4, key0);
-  hist3[threadIdx.x] = 0;  // kT == kBins3
-  wlt[threadIdx.x] = 0;
-  weq[threadIdx.x] = 0;
-  // ---- round 2: candidates into LDS
-  const uint32_t ncl = nc < (uint32_t)kCandLds ? nc : (uint32_t)kCandLds;
+  uint32_t key0[kKeys];
+  load_keys(Pg, j0, j1, A.vec4, key0);
+  const int64_t nspec = A.n < kCandLds ? A.n : kCandLds;
   {
     uint2 c16[kCandLds / kT];
 #pragma unroll
     for (int k = 0; k < kCandLds / kT; ++k) {
-      const uint32_t i = threadIdx.x + k * kT;
-      c16[k] = i < ncl ? cg[i] : make_uint2(0xffffffffu, 0u);
+      const int i = threadIdx.x + k * kT;
+      c16[k] = i < nspec ? cg[i] : make_uint2(0xffffffffu, 0u);
     }
+    if (threadIdx.x < kBins3) hist3[threadIdx.x] = 0;
+    wlt[threadIdx.x] = 0;
+    weq[threadIdx.x] = 0;
+    if (threadIdx.x == 0) ntie = 0;
 #pragma unroll
     for (int k = 0; k < kCandLds / kT; ++k) cl[threadIdx.x + k * kT] = c16[k];
   }
-  uint32_t before_lt = 0;
-#pragma unroll
-  for (int k = 0; k < kMaxSeg / kT; ++k) before_lt += pre[k];
-  find_bin_regs<kT, kBins1 / kT>(c1, A.n_evict, wsum, &sh_bin, &sh_rin);  // (its barriers also publish cl)
+  find_bin_regs<kT, kBinsPer>(c1, A.n_evict, wsum, &sh_bin, &sh_rin);  // (its barriers also publish cl)
   const uint32_t d1 = (uint32_t)sh_bin;
-  find_bin_regs<kT, kBins2 / kT>(c2, sh_rin, wsum, &sh_bin, &sh_rin);
+  find_bin_regs<kT, kBinsPer>(c2, sh_rin, wsum, &sh_bin, &sh_rin);
   const uint32_t d2 = (uint32_t)sh_bin;
   const int64_t r2 = sh_rin;
   auto cand = [&](uint32_t i) { return i < (uint32_t)kCandLds ? cl[i] : cg[i]; };
-  for (uint32_t i = threadIdx.x; i < nc; i += kT) {
-    const uint32_t key = cand(i).x;
-    if (((key >> 8) & 0xfffu) == d2) atomicAdd(&hist3[key & 0xffu], 1u);
+  // counts of keys below tau (cb_lt) / equal to it (cb_eq) before this
+  // workgroup's segments; wlt / weq: in each of its segments
+  uint32_t cb_lt = 0, cb_eq = 0;
+  auto count_lt = [&](uint32_t tok) {
+    const int sg = (int)(tok / (uint32_t)A.seg);
+    if (sg < s0) ++cb_lt;
+    else if (sg < s0 + kT) atomicAdd(&wlt[sg - s0], 1u);
+  };
+  auto count_eq = [&](uint32_t tok) {
+    const int sg = (int)(tok / (uint32_t)A.seg);
+    if (sg < s0) ++cb_eq;
+    else if (sg < s0 + kT) atomicAdd(&weq[sg - s0], 1u);
+  };
+  // one pass: digit 2 below d2 means below tau; equal goes to the digit-3
+  // histogram and the tie list (every candidate has digit 1 == d1)
+  auto sort_cand = [&](uint2 c) {
+    const uint32_t dg = (c.x >> 8) & 0xfffu;
+    if (dg < d2) {
+      count_lt(c.y);
+    } else if (dg == d2) {
+      atomicAdd(&hist3[c.x & 0xffu], 1u);
+      const uint32_t t = atomicAdd(&ntie, 1u);
+      if (t < (uint32_t)kTie) tie[t] = c;
+    }
+  };
+  const uint32_t ncl = nc < (uint32_t)kCandLds ? nc : (uint32_t)kCandLds;
+  for (uint32_t i0 = 0; i0 < ncl; i0 += 4 * kT) {  // four LDS reads in flight
+    uint2 c[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const uint32_t i = i0 + k * kT + threadIdx.x;
+      c[k] = i < ncl ? cl[i] : make_uint2(0xffffffffu, 0u);
+    }
+#pragma unroll
+    for (int k = 0; k < 4; ++k)
+      if (i0 + k * kT + threadIdx.x < ncl) sort_cand(c[k]);
   }
+  for (uint32_t i = ncl + threadIdx.x; i < nc; i += kT) sort_cand(cg[i]);
   __syncthreads();
   uint32_t c3[1];
-  c3[0] = hist3[threadIdx.x];
+  c3[0] = threadIdx.x < kBins3 ? hist3[threadIdx.x] : 0u;
   find_bin_regs<kT, 1>(c3, r2, wsum, &sh_bin, &sh_rin);
   const uint32_t tau = (d1 << 20) | (d2 << 8) | (uint32_t)sh_bin;
   const int64_t need = sh_rin;
-  // candidates below / equal to tau: before this workgroup's segments, or in one of them
-  uint32_t cb_lt = 0, cb_eq = 0;
-  for (uint32_t i = threadIdx.x; i < nc; i += kT) {
-    const uint2 c = cand(i);
-    if (c.x > tau) continue;
-    const int sg = (int)(c.y / (uint32_t)A.seg);
-    if (c.x < tau) {
-      if (sg < s0) ++cb_lt;
-      else if (sg < s0 + kT) atomicAdd(&wlt[sg - s0], 1u);
-    } else {
-      if (sg < s0) ++cb_eq;
-      else if (sg < s0 + kT) atomicAdd(&weq[sg - s0], 1u);
+  const uint32_t nt = ntie;
+  auto count_tie = [&](uint2 c) {
+    if (c.x < tau) count_lt(c.y);
+    else if (c.x == tau) count_eq(c.y);
+  };
+  if (nt <= (uint32_t)kTie) {
+    for (uint32_t i = threadIdx.x; i < nt; i += kT) count_tie(tie[i]);
+  } else {
+    for (uint32_t i = threadIdx.x; i < nc; i += kT) {
+      const uint2 c = cand(i);
+      if (((c.x >> 8) & 0xfffu) == d2) count_tie(c);
     }
   }
   // counts below 2^31 (n fits in int32): 32-bit scans
   uint32_t x0, x1, tot_lt, tot_eq;
-  wg_scan2<kT>((uint32_t)(before_lt + cb_lt), (uint32_t)cb_eq, wsum, x0, x1, tot_lt, tot_eq);
-  uint32_t lpre, epre, t0, t1;
-  wg_scan2<kT>(own_lt + wlt[threadIdx.x], weq[threadIdx.x], wsum, lpre, epre, t0, t1);
-  const int64_t lb = (int64_t)tot_lt + lpre;
-  int64_t eqb = (int64_t)tot_eq + epre;
-  if (s >= A.nseg) return;
-  int64_t pos = lb + (eqb < need ? eqb : need);
+  wg_scan2<kT>(prev_lt + cb_lt, cb_eq, wsum, x0, x1, tot_lt, tot_eq);
+  uint32_t lpre, epre, in_lt, in_eq;
+  wg_scan2<kT>(own_lt + wlt[threadIdx.x], weq[threadIdx.x], wsum, lpre, epre, in_lt, in_eq);
+  // this workgroup's evictions fill og[base, base + cnt)
+  const int64_t taken0 = (int64_t)tot_eq < need ? (int64_t)tot_eq : need;
+  const int64_t taken1 = (int64_t)tot_eq + in_eq < need ? (int64_t)tot_eq + in_eq : need;
+  const int64_t base = (int64_t)tot_lt + taken0;
+  const int64_t cnt = (int64_t)in_lt + (taken1 - taken0);
+  const bool staged = cnt <= kStage;  // same for every thread
+  uint32_t* stg = reinterpret_cast<uint32_t*>(cl);  // kStage slots, then one spare slot per thread
   int64_t* og = A.idx + (size_t)g * A.n_evict;
-  auto emit16 = [&](const uint32_t (&key)[16], int64_t q0) {
+  // token indices, counts and positions fit in 32 bits (n < 2^31)
+  const uint32_t need32 = (uint32_t)need;
+  const uint32_t base32 = (uint32_t)base, cnt32 = (uint32_t)cnt;
+  auto emit = [&](auto to_lds) {
+    if (s >= A.nseg) return;
+    uint32_t eqb = tot_eq + epre;
+    uint32_t pos = tot_lt + lpre + (eqb < need32 ? eqb : need32);
+    auto emit_keys = [&](const uint32_t (&key)[kKeys], uint32_t q0) {
 #pragma unroll
-    for (int k = 0; k < 16; ++k) {
-      bool take = key[k] < tau;
-      if (key[k] == tau) {
-        take = eqb < need;
-        ++eqb;
+      for (int k = 0; k < kKeys; ++k) {
+        const bool eq = key[k] == tau;
+        const bool take = key[k] < tau || (eq && eqb < need32);
+        eqb += eq ? 1u : 0u;
+        if constexpr (decltype(to_lds)::value) {
+          // no branch: a key not taken is written to this thread's spare slot
+          const uint32_t r = pos - base32;  // wraps above cnt32 if ever below base
+          stg[(take && r < cnt32) ? r : (uint32_t)(kStage + threadIdx.x)] = q0 + k;
+        } else {
+          if (take && pos < (uint32_t)A.n_evict) og[pos] = (int64_t)(q0 + k);
+        }
+        pos += take ? 1u : 0u;
       }
-      if (take) {
-        if (pos < A.n_evict) og[pos] = q0 + k;
-        ++pos;
-      }
+    };
+    emit_keys(key0, (uint32_t)j0);
+    for (int64_t q0 = j0 + kKeys; q0 < j1; q0 += kKeys) {
+      uint32_t key[kKeys];
+      load_keys(Pg, q0, j1, A.vec4, key);
+      emit_keys(key, (uint32_t)q0);
     }
   };
-  emit16(key0, j0);
-  for (int64_t q0 = j0 + 16; q0 < j1; q0 += 16) {
-    uint32_t key[16];
-    load16(Pg, q0, j1, A.vec4, key);
-    emit16(key, q0);
+  if (!staged) {
+    emit(std::false_type{});
+    return;
+  }
+  emit(std::true_type{});
+  __syncthreads();
+  // consecutive threads, consecutive output slots; the LDS reads first (slot
+  // i0 + k * kT + threadIdx.x < i0 + kOutPer * kT <= kStage while i0 < cnt32)
+  constexpr int kOutPer = kStage / kT / 2;
+  static_assert(kStage % (kOutPer * kT) == 0, "whole rounds of output slots");
+  const int64_t lim = A.n_evict - base;  // >= cnt for consistent scores
+  for (uint32_t i0 = 0; i0 < cnt32; i0 += kOutPer * kT) {
+    uint32_t v[kOutPer];
+#pragma unroll
+    for (int k = 0; k < kOutPer; ++k) v[k] = stg[i0 + k * kT + threadIdx.x];
+#pragma unroll
+    for (int k = 0; k < kOutPer; ++k) {
+      const uint32_t i = i0 + k * kT + threadIdx.x;
+      if (i < cnt32 && (int64_t)i < lim) og[base + i] = (int64_t)v[k];
+    }
   }
 }
 
@@ -464,8 +565,8 @@ struct SelGeom {
 
 SelGeom sel_geom(int64_t n) {
   int64_t seg = (n + kMaxSeg - 1) / kMaxSeg;
-  seg = (seg + 15) / 16 * 16;
-  if (seg < 16) seg = 16;
+  seg = (seg + kKeys - 1) / kKeys * kKeys;
+  if (seg < kKeys) seg = kKeys;
   SelGeom q;
   q.seg = (int)seg;
   q.nseg = (int)((n + seg - 1) / seg);
@@ -476,6 +577,7 @@ struct SelPtrs {
   uint32_t* hist;
   uint2* cand;
   uint32_t* seg_lt;
+  uint32_t* wg_lt;
   size_t bytes;
 };
 
@@ -492,6 +594,7 @@ SelPtrs carve_sel(void* scratch, int64_t n, int32_t Hkv) {
   r.hist = (uint32_t*)take(sizeof(uint32_t) * (size_t)Hkv * kHistStride);
   r.cand = (uint2*)take(sizeof(uint2) * (size_t)Hkv * (size_t)n);
   r.seg_lt = (uint32_t*)take(sizeof(uint32_t) * (size_t)Hkv * q.nseg);
+  r.wg_lt = (uint32_t*)take(sizeof(uint32_t) * (size_t)Hkv * kMaxWg);
   r.bytes = off;
   return r;
 }
@@ -535,6 +638,7 @@ hipError_t launch_select(const float* S, int64_t n, int32_t w, int32_t Hkv, int3
   A.hist = p.hist;
   A.cand = p.cand;
   A.seg_lt = p.seg_lt;
+  A.wg_lt = p.wg_lt;
   A.status = status;
   if (fold) A.fold = *fold;
   k_sel_pool<<<dim3(A.nblk, Hkv), kT, 0, st>>>(A);

@@ -144,7 +144,13 @@ def test_bitwise_repeatable():
 # ------------------------------------------------------------ select stage ---
 
 @pytest.mark.parametrize("n,w,k,ne", [(50, 6, 3, 20), (4097, 64, 7, 3000), (1000, 10, 1, 990),
-                                      (300, 5, 5, 0), (64, 1, 3, 63)])
+                                      (300, 5, 5, 0), (64, 1, 3, 63),
+                                      # thousands of keys tied with tau: candidates beyond the
+                                      # on-chip buffer, ties beyond the tie list
+                                      (40000, 64, 7, 30000),
+                                      # segments of 24 keys: several load groups per segment and
+                                      # workgroups with more evictions than their staging area
+                                      (300000, 64, 9, 250000)])
 def test_select_matches_stable_argsort(n, w, k, ne):
     rng = np.random.default_rng(n + ne)
     S = rng.integers(0, 7, size=(3, n)).astype(np.float32) * np.float32(0.25)  # many exact ties
