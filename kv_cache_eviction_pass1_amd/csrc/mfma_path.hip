@@ -243,10 +243,11 @@ __device__ __forceinline__ void p1_vnorms(const char* vb, const VnOff<NW>& vo, f
     a1 = __builtin_amdgcn_fdot2_f32_bf16(p3, p3, a1, false);
   }
   float acc = a0 + a1;
-  // sum over the NW consecutive lanes of a token (swizzle xor within 32 lanes)
-  if (NW >= 2) acc += __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(acc), (1 << 10) | 0x1f));
-  if (NW >= 4) acc += __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(acc), (2 << 10) | 0x1f));
-  if (NW >= 8) acc += __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(acc), (4 << 10) | 0x1f));
+  // sum over the NW consecutive lanes of a token, in DPP lane moves (no LDS
+  // round trip): quad_perm [1,0,3,2], quad_perm [2,3,0,1], row_half_mirror
+  if (NW >= 2) acc += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(acc), 0xB1, 0xf, 0xf, false));
+  if (NW >= 4) acc += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(acc), 0x4E, 0xf, 0xf, false));
+  if (NW >= 8) acc += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(acc), 0x141, 0xf, 0xf, false));
   const int tt = wave * (TT / NW) + lane / NW;
   if (lane % NW == 0 && tt < ntok) nvtile[tt] = acc;
 }
@@ -284,6 +285,17 @@ __device__ __forceinline__ void p1_tile(float c2, const char* kb, const char* vb
 #pragma unroll
     for (int ks = 0; ks < 8; ++ks) x = mfma(ka[ks], qb[ks], x);
     __builtin_amdgcn_s_setprio(0);
+    // O^T[d][row] += V^T[d][tok] P^T[tok][row]; k-slot 8h+i of step s is token
+    // 16s + 8(i/4) + 4h + i%4 (the order in which X^T left the values in this
+    // lane). The transposing reads are issued here, so that their latency
+    // passes under the softmax below.
+    bf16x8 va[2][4];
+#pragma unroll
+    for (int s = 0; s < 2; ++s)
+#pragma unroll
+      for (int db = 0; db < 4; ++db)
+        va[s][db] = tr_pair(vt + s * 16 * 256 + off.v[2 * db], vt + s * 16 * 256 + off.v[2 * db + 1]);
+    __builtin_amdgcn_sched_barrier(0);
     const int64_t tokbase = tokbase_tile + sub * 32;
     if (MASK) {  // causal tail / ragged end: hide keys after this row's position
 #pragma unroll
@@ -326,14 +338,6 @@ __device__ __forceinline__ void p1_tile(float c2, const char* kb, const char* vb
     for (int s = 0; s < 2; ++s)
 #pragma unroll
       for (int i = 0; i < 8; ++i) pb[s][i] = (__bf16)e[8 * s + i];
-    // O^T[d][row] += V^T[d][tok] P^T[tok][row]; k-slot 8h+i of step s is token
-    // 16s + 8(i/4) + 4h + i%4 (the order in which X^T left the values in this lane)
-    bf16x8 va[2][4];
-#pragma unroll
-    for (int s = 0; s < 2; ++s)
-#pragma unroll
-      for (int db = 0; db < 4; ++db)
-        va[s][db] = tr_pair(vt + s * 16 * 256 + off.v[2 * db], vt + s * 16 * 256 + off.v[2 * db + 1]);
     __builtin_amdgcn_s_setprio(1);
 #pragma unroll
     for (int s = 0; s < 2; ++s)
