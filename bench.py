@@ -38,8 +38,10 @@ MFMA_BF16_PEAK_TFLOPS = 2500.0
 def parse():
     ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=3)
+    # The GPU needs ~60 back-to-back steps (~25 ms) before its clocks settle; the
+    # default warm-up covers that, so the timed steps measure the steady state.
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=100)
     ap.add_argument("--workload", default="llama_128k")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",

@@ -157,7 +157,7 @@ int dropkv_stage_times(int32_t dtype, const void* q, const void* k, const void* 
 
 /*
  * Reads the stage log of the current device: calls of dropkv_score_ex made
- * with DROPKV_FLAG_STAGE_LOG since the last read (at most 64 are kept; later
+ * with DROPKV_FLAG_STAGE_LOG since the last read (at most 256 are kept; later
  * ones are not logged). Waits for their events, writes the mean duration of
  * each stage over those calls in milliseconds to out_ms[0..*out_count-1] (at
  * most 12), their comma-separated names to out_names (names_bytes bytes,

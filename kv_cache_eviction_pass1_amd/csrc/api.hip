@@ -34,7 +34,7 @@ std::mutex g_ws_mutex;
 std::unordered_map<int, DeviceWs> g_ws;
 
 // Stage log: event sets of up to kLogCalls logged dropkv_score_ex calls per device.
-constexpr int kLogCalls = 64;
+constexpr int kLogCalls = 256;
 struct StageLog {
   StageEvents slot[kLogCalls];
   bool created[kLogCalls] = {};
@@ -52,8 +52,9 @@ StageEvents* log_slot() {
   if (L.used >= kLogCalls) return nullptr;
   const int i = L.used;
   if (!L.created[i]) {
+    // timing-only events: no system-scope fence (and its cache writeback) per record
     for (int e = 0; e <= kMaxStages; ++e)
-      if (hipEventCreate(&L.slot[i].ev[e]) != hipSuccess) return nullptr;
+      if (hipEventCreateWithFlags(&L.slot[i].ev[e], hipEventDisableSystemFence) != hipSuccess) return nullptr;
     L.created[i] = true;
   }
   L.slot[i].count = 0;
@@ -403,8 +404,8 @@ int dropkv_stage_times(int32_t dtype, const void* q, const void* k, const void* 
   Workspace ws = carve_workspace(base, s, mfma);
   StageEvents se{};
   for (int i = 0; i <= kMaxStages; ++i) {
-    hipError_t e = hipEventCreate(&se.ev[i]);
-    if (e != hipSuccess) return fail_hip(e, "hipEventCreate");
+    hipError_t e = hipEventCreateWithFlags(&se.ev[i], hipEventDisableSystemFence);
+    if (e != hipSuccess) return fail_hip(e, "hipEventCreateWithFlags");
   }
   FoldInfo fold{};
   int rc = run_scores(dtype, q, k, v, s, ws, mfma, st, &se, &fold);

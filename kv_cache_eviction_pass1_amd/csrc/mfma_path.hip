@@ -878,12 +878,14 @@ template <bool MASK>
 __device__ __forceinline__ float p2_sub(const char* kt, const char* vt, float nvj, const LdsOff& off,
                                         const bf16x8 (&qa)[8], const bf16x8 (&aa)[8],
                                         const float (&nb2)[16], const float (&cinit)[16], float c2x2,
-                                        int64_t tok, const int (&rpos)[16]) {
+                                        int64_t tok, int rbase, int w) {
   bf16x8 kb[8], vb[8];
 #pragma unroll
   for (int ks = 0; ks < 8; ++ks) kb[ks] = ld16(kt + off.k[ks]);
 #pragma unroll
   for (int ks = 0; ks < 8; ++ks) vb[ks] = ld16(vt + off.k[ks]);
+  // all sixteen operand reads in flight before the first MFMA waits on one
+  __builtin_amdgcn_sched_barrier(0);
   f32x16 X = {}, C;
 #pragma unroll
   for (int i = 0; i < 16; ++i) C[i] = cinit[i];
@@ -895,7 +897,10 @@ __device__ __forceinline__ float p2_sub(const char* kt, const char* vt, float nv
 #pragma unroll
   for (int vv = 0; vv < 16; ++vv) {
     y2[vv] = fmaf(X[vv], c2x2, nb2[vv]);
-    if (MASK && tok > (int64_t)rpos[vv]) y2[vv] = -INFINITY;
+    if (MASK) {  // row rbase + 8(vv/4) + vv%4 sits at window position row % w
+      const int rpos = (rbase + (vv >> 2) * 8 + (vv & 3)) % w;
+      if (tok > (int64_t)rpos) y2[vv] = -INFINITY;
+    }
   }
   float ym = fmaxf(fmaxf(y2[0], y2[1]), y2[2]);
 #pragma unroll
@@ -1005,13 +1010,9 @@ __global__ __launch_bounds__(NW * 64) void k_pass2(P2Args P, FixArgs F) {
   const float c2x2 = 2.0f * P.c2;
   const LdsOff off = lds_offsets(lane);
   float nb2[16];
-  int rpos[16];  // window position of each of this lane's rows, relative to n - w
 #pragma unroll
-  for (int vv = 0; vv < 16; ++vv) {
-    nb2[vv] = -2.0f * bias[vv];
-    const int rr = rb * 32 + (vv >> 2) * 8 + 4 * h + (vv & 3);
-    rpos[vv] = rr % P.w;
-  }
+  for (int vv = 0; vv < 16; ++vv) nb2[vv] = -2.0f * bias[vv];
+  const int rbase = rb * 32 + 4 * h;  // first row of this lane's 16 (masked tiles only)
   const int nclean = clean_tiles(P.n, P.w, t0, ntiles);
   // scores of tile t-1 (every wave wrote its partial before the barrier at tile t)
   auto combine = [&](int tl, const float (*red)[TT]) {
@@ -1045,7 +1046,7 @@ __global__ __launch_bounds__(NW * 64) void k_pass2(P2Args P, FixArgs F) {
 #pragma unroll
       for (int sub = 0; sub < 2; ++sub) {
         const float sw = p2_sub<false>(kbuf[B] + sub * 32 * 256, vbuf[B] + sub * 32 * 256,
-                                       nvbuf[B][sub * 32 + l32], off, qa, aa, nb2, cinit, c2x2, 0, rpos);
+                                       nvbuf[B][sub * 32 + l32], off, qa, aa, nb2, cinit, c2x2, 0, rbase, P.w);
         if (h == 0) red3[B][wave][sub * 32 + l32] = sw;
       }
     }
@@ -1064,7 +1065,7 @@ __global__ __launch_bounds__(NW * 64) void k_pass2(P2Args P, FixArgs F) {
       for (int sub = 0; sub < 2; ++sub) {
         const int64_t tok = tok_rel0 + (int64_t)t * TT + sub * 32;
         const float sw = p2_sub<true>(kbuf[b] + sub * 32 * 256, vbuf[b] + sub * 32 * 256,
-                                      nvbuf[b][sub * 32 + l32], off, qa, aa, nb2, cinit, c2x2, tok, rpos);
+                                      nvbuf[b][sub * 32 + l32], off, qa, aa, nb2, cinit, c2x2, tok, rbase, P.w);
         if (h == 0) red3[b][wave][sub * 32 + l32] = sw;
       }
     }
