@@ -67,8 +67,9 @@ typedef enum {
 /* Element type of q, k, v. */
 enum { DROPKV_BF16 = 0, DROPKV_F32 = 1 };
 
-/* Bits of the device status word written by dropkv_score_ex. */
-enum { DROPKV_STATUS_SINGULAR = 1, DROPKV_STATUS_NONFINITE = 2 };
+/* Bits of the device status word written by dropkv_score_ex (and, for
+ * DROPKV_STATUS_BAD_INDEX, by dropkv_compact). */
+enum { DROPKV_STATUS_SINGULAR = 1, DROPKV_STATUS_NONFINITE = 2, DROPKV_STATUS_BAD_INDEX = 4 };
 
 /* Flags for dropkv_score_ex. */
 enum {
@@ -168,6 +169,29 @@ int dropkv_stage_times(int32_t dtype, const void* q, const void* k, const void* 
  */
 int dropkv_stage_log(float* out_ms, char* out_names, int32_t names_bytes, int32_t* out_count,
                      int32_t* out_calls);
+
+/*
+ * Cache compaction, the step after scoring (write-up section 代码映射与边界:
+ * the scorer returns per-head eviction indices and the caller drops those
+ * tokens from its cache). Copies the rows of k and v [Hkv][n][d] (dtype
+ * DROPKV_BF16 or DROPKV_F32) whose token index is not in evict_idx
+ * [Hkv][n_evict] (int64, strictly increasing per head, inside [0, n), as
+ * dropkv_score returns it) to out_k, out_v [Hkv][n - n_evict][d], in
+ * ascending token order: kept token j of head g becomes row
+ * j - #{evicted indices of g below j}. Bitwise copies.
+ * Limits: 1 <= n < 2^31, Hkv >= 1, 1 <= d <= 4096, 0 <= n_evict <= n; every
+ * pointer is a device pointer (evict_idx may be NULL when n_evict == 0,
+ * out_k / out_v when n_evict == n); outputs must not overlap the inputs.
+ * Asynchronous on `stream`: the call ORs DROPKV_STATUS_BAD_INDEX into the
+ * caller-owned device int32 `d_status` (which the caller clears beforehand;
+ * the call does not, so that it is one kernel launch) if some head's list is
+ * not strictly increasing inside [0, n); the outputs are then unspecified,
+ * but no write falls outside out_k / out_v. Returns DROPKV_OK once enqueued,
+ * DROPKV_ERR_INVALID (nothing launched) or DROPKV_ERR_DEVICE.
+ */
+int dropkv_compact(int32_t dtype, const void* k, const void* v, int64_t n, int32_t Hkv, int32_t d,
+                   const int64_t* evict_idx, int64_t n_evict, void* out_k, void* out_v,
+                   int32_t* d_status, void* stream);
 
 /* 1 if (dtype, d) takes the MFMA path by default, 0 if the plain-VALU path. */
 int dropkv_uses_mfma(int32_t dtype, int32_t d);

@@ -17,7 +17,7 @@ LIB_PATH = os.path.join(_HERE, "libdropkv.so")
 
 OK, ERR_INVALID, ERR_SINGULAR, ERR_NONFINITE, ERR_DEVICE = 0, -1, -2, -3, -4
 BF16, F32 = 0, 1
-STATUS_SINGULAR, STATUS_NONFINITE = 1, 2
+STATUS_SINGULAR, STATUS_NONFINITE, STATUS_BAD_INDEX = 1, 2, 4
 FLAG_GENERIC = 1
 FLAG_STAGE_LOG = 2
 
@@ -37,6 +37,7 @@ SIGNATURES = {
     "dropkv_stage_times": (_i32, [_i32, _p, _p, _p, _i64, _i32, _i32, _i32, _i32, _i32, _i64, _p,
                                   _p, _u32, _p, _p, _i32, _p, _p]),
     "dropkv_stage_log": (_i32, [_p, _p, _i32, _p, _p]),
+    "dropkv_compact": (_i32, [_i32, _p, _p, _i64, _i32, _i32, _p, _i64, _p, _p, _p, _p]),
     "dropkv_uses_mfma": (_i32, [_i32, _i32]),
     "dropkv_last_error": (_c.c_char_p, []),
     "dropkv_version": (_c.c_char_p, []),
@@ -214,6 +215,44 @@ def select(S, *, window: int, pool_kernel: int, n_evict: int, stream=None):
                            idx.data_ptr() if n_evict > 0 else None, _stream_handle(stream))
     _raise(rc)
     return scores, idx
+
+
+def compact(k, v, evict_idx, *, status=None, out_k=None, out_v=None, stream=None):
+    """Cache compaction: the rows of k, v [Hkv, n, d] not listed in evict_idx
+    [Hkv, n_evict] (int64, increasing per head) as out_k, out_v [Hkv, n - n_evict, d].
+
+    With `status` (a device int32 tensor, cleared by the caller) the call is
+    asynchronous and ORs STATUS_BAD_INDEX into it for an invalid list; without
+    it the call synchronises and raises DropKVInvalidError for one.
+    """
+    torch = _torch()
+    lib = load_library()
+    if k.dim() != 3 or tuple(v.shape) != tuple(k.shape) or k.dtype != v.dtype:
+        raise DropKVInvalidError(ERR_INVALID, "k and v must both be [Hkv, n, d] of one dtype")
+    for t in (k, v, evict_idx):
+        if not t.is_cuda or not t.is_contiguous():
+            raise DropKVInvalidError(ERR_INVALID, "k, v and evict_idx must be contiguous GPU tensors")
+    Hkv, n, d = k.shape
+    if evict_idx.dtype != torch.int64 or evict_idx.dim() != 2 or evict_idx.shape[0] != Hkv:
+        raise DropKVInvalidError(ERR_INVALID, "evict_idx must be int64 [Hkv, n_evict]")
+    n_evict = evict_idx.shape[1]
+    n_keep = n - n_evict
+    if out_k is None:
+        out_k = torch.empty((Hkv, max(n_keep, 0), d), dtype=k.dtype, device=k.device)
+    if out_v is None:
+        out_v = torch.empty((Hkv, max(n_keep, 0), d), dtype=k.dtype, device=k.device)
+    sync = status is None
+    if sync:
+        status = torch.zeros(1, dtype=torch.int32, device=k.device)
+    rc = lib.dropkv_compact(_dtype_code(k), k.data_ptr(), v.data_ptr(), n, Hkv, d,
+                            evict_idx.data_ptr() if n_evict > 0 else None, n_evict,
+                            out_k.data_ptr() if n_keep > 0 else None,
+                            out_v.data_ptr() if n_keep > 0 else None, status.data_ptr(),
+                            _stream_handle(stream))
+    _raise(rc)
+    if sync and int(status.item()) & STATUS_BAD_INDEX:
+        raise DropKVInvalidError(ERR_INVALID, "evict_idx is not strictly increasing inside [0, n)")
+    return out_k, out_v
 
 
 def stage_times(q, k, v, *, pool_kernel: int, n_evict: int, flags: int = 0, stream=None):

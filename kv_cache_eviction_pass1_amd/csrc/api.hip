@@ -480,6 +480,26 @@ int dropkv_stage_log(float* out_ms, char* out_names, int32_t names_bytes, int32_
   return DROPKV_OK;
 }
 
+int dropkv_compact(int32_t dtype, const void* k, const void* v, int64_t n, int32_t Hkv, int32_t d,
+                   const int64_t* evict_idx, int64_t n_evict, void* out_k, void* out_v,
+                   int32_t* d_status, void* stream) {
+  g_last_error.clear();
+  if (dtype != DROPKV_BF16 && dtype != DROPKV_F32) return fail(DROPKV_ERR_INVALID, "dtype must be DROPKV_BF16 or DROPKV_F32");
+  if (n < 1 || n > ((int64_t)1 << 31) - 1) return fail(DROPKV_ERR_INVALID, "need 1 <= n < 2^31");
+  if (Hkv < 1 || d < 1 || d > 4096) return fail(DROPKV_ERR_INVALID, "need Hkv >= 1 and 1 <= d <= 4096");
+  if (n_evict < 0 || n_evict > n) return fail(DROPKV_ERR_INVALID, "need 0 <= n_evict <= n");
+  if (!k || !v || !is_device_ptr(k) || !is_device_ptr(v)) return fail(DROPKV_ERR_INVALID, "k and v must be device pointers");
+  if (n_evict > 0 && (!evict_idx || !is_device_ptr(evict_idx)))
+    return fail(DROPKV_ERR_INVALID, "evict_idx must be a device pointer when n_evict > 0");
+  if (n_evict < n && (!out_k || !out_v || !is_device_ptr(out_k) || !is_device_ptr(out_v)))
+    return fail(DROPKV_ERR_INVALID, "out_k and out_v must be device pointers when tokens are kept");
+  if (!d_status || !is_device_ptr(d_status)) return fail(DROPKV_ERR_INVALID, "d_status must be a device pointer");
+  hipError_t e = launch_compact(dtype, k, v, n, Hkv, d, evict_idx, n_evict, out_k, out_v, d_status,
+                                (hipStream_t)stream);
+  if (e != hipSuccess) return fail_hip(e, "compact");
+  return DROPKV_OK;
+}
+
 int dropkv_uses_mfma(int32_t dtype, int32_t d) { return mfma_supported(dtype, d) ? 1 : 0; }
 
 const char* dropkv_last_error(void) { return g_last_error.c_str(); }

@@ -10,6 +10,7 @@ namespace dropkv {
 // Bits of the device status word (same values as DROPKV_STATUS_* in dropkv.h).
 constexpr int kStatusSingular = 1;
 constexpr int kStatusNonFinite = 2;
+constexpr int kStatusBadIndex = 4;  // cache compaction: eviction list not increasing inside [0, n)
 
 // A window row is rejected when its rest mass R = sum_{j != argmax} exp(x_j - x_max)
 // is at most 2^-24: then 1/(1+R) rounds to 1 in binary32 (the singular-input rule).
@@ -55,6 +56,13 @@ struct Shape {
 Workspace carve_workspace(void* ws_base, const Shape& s, bool mfma);
 
 // Launchers. Each returns hipSuccess or the launch error.
+// Cache compaction (compact.hip): ORs kStatusBadIndex into *status for an
+// invalid list, and copies the rows of k, v
+// [Hkv][n][d] not listed in evict_idx [Hkv][n_evict] to out_k, out_v
+// [Hkv][n - n_evict][d]; dtype 0 = bf16, 1 = fp32.
+hipError_t launch_compact(int dtype, const void* k, const void* v, int64_t n, int32_t Hkv, int32_t d,
+                          const int64_t* evict_idx, int64_t n_evict, void* out_k, void* out_v,
+                          int32_t* status, hipStream_t st);
 // Zeroes the status word, flagcount[Hkv] (may be null) and the select scratch.
 hipError_t launch_init(int32_t* status, int32_t* flagcount, void* sel_scratch, int32_t Hkv,
                        hipStream_t st);

@@ -8,5 +8,5 @@ from .dropkv_oracle import (  # noqa: F401
     SINGULAR_REST_MASS, SingularRow, NonFiniteInput, bf16_bits_to_f64, as_f64,
     window_positions, group_rows, row_attention, head_row_stats, perturbation_sq,
     head_scores, maxpool1d_same, protect_window, evict_smallest, check_args,
-    dropkv_oracle,
+    dropkv_oracle, compact_cache,
 )

@@ -206,6 +206,34 @@ def evict_smallest(P: np.ndarray, n_evict: int) -> np.ndarray:
     return out
 
 
+def compact_cache(k: np.ndarray, v: np.ndarray, evict: np.ndarray):
+    """Cache compaction, the step after scoring.
+
+    Write-up section 代码映射与边界 (code map): the scorer hands back, per
+    physical KV head, the indices of the tokens to drop, and the caller removes
+    them from its cache. Per head g, the result holds the rows k[g, j], v[g, j]
+    of every j that evict[g] does not list, in ascending j (the order of the
+    cache). The rows are copied as they are (bit patterns included).
+    Raises ValueError unless each evict[g] is strictly increasing inside [0, n).
+    """
+    evict = np.asarray(evict, dtype=np.int64).reshape(k.shape[0], -1)
+    Hkv, n = k.shape[0], k.shape[1]
+    if v.shape != k.shape:
+        raise ValueError("k and v must have one shape")
+    n_keep = n - evict.shape[1]
+    ok = np.empty((Hkv, n_keep) + k.shape[2:], dtype=k.dtype)
+    ov = np.empty((Hkv, n_keep) + v.shape[2:], dtype=v.dtype)
+    for g in range(Hkv):
+        e = evict[g]
+        if e.size and (e[0] < 0 or e[-1] >= n or np.any(np.diff(e) <= 0)):
+            raise ValueError("eviction list must be strictly increasing inside [0, n)")
+        keep = np.ones(n, dtype=bool)
+        keep[e] = False
+        ok[g] = k[g][keep]
+        ov[g] = v[g][keep]
+    return ok, ov
+
+
 def check_args(n: int, window: int, Hq: int, Hkv: int, d: int, pool_kernel: int, n_evict: int) -> None:
     w = window
     if not (1 <= w < n):

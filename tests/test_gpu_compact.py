@@ -1,0 +1,174 @@
+"""Cache compaction on the GPU (dropkv_compact) against the oracle, bit for bit.
+
+Covers the three copy widths (16-, 4- and 2-byte units, chosen from the row
+size and the pointers' alignment), ragged token counts around the 1024-token
+block, empty and full eviction lists, invalid lists (status bit, and no write
+outside the outputs: guard rows around them stay untouched), and the
+score -> compact pipeline on a full-size layer.
+"""
+
+import numpy as np
+import pytest
+
+import oracle
+import kv_cache_eviction_pass1_amd as K
+from kv_cache_eviction_pass1_amd import synth
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+GUARD = 3  # guard rows on each side of every output
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.fail("GPU tests need a GPU")
+    K.load_library()
+    yield
+
+
+def _bits(t):
+    """Host copy of a tensor's bit patterns."""
+    a = t.detach().cpu()
+    if a.dtype == torch.bfloat16:
+        return a.view(torch.int16).numpy()
+    return a.view(torch.int32).numpy()
+
+
+def _guarded_outputs(Hkv, n_keep, d, dtype, dev):
+    """Outputs as views into larger buffers whose guard rows hold a fill pattern."""
+    bufs, views = [], []
+    for _ in range(2):
+        b = torch.full((Hkv * n_keep * d + 2 * GUARD * d,), -7.0, dtype=dtype, device=dev)
+        bufs.append(b)
+        views.append(b[GUARD * d: GUARD * d + Hkv * n_keep * d].view(Hkv, n_keep, d))
+    return bufs, views
+
+
+def _check_guards(bufs, Hkv, n_keep, d):
+    for b in bufs:
+        head = b[: GUARD * d].float().cpu()
+        tail = b[GUARD * d + Hkv * n_keep * d:].float().cpu()
+        assert torch.all(head == -7.0) and torch.all(tail == -7.0), "write outside the output"
+
+
+def _evict_lists(rng, Hkv, n, ne, kind):
+    rows = []
+    for g in range(Hkv):
+        if kind == "random":
+            e = np.sort(rng.choice(n, size=ne, replace=False))
+        elif kind == "runs":  # long runs of kept and evicted tokens
+            starts = np.sort(rng.choice(max(n - 1, 1), size=max(1, ne // 50), replace=False))
+            e = np.unique(np.concatenate([np.arange(s, min(n, s + 50)) for s in starts]))[:ne]
+            if e.size < ne:
+                rest = np.setdiff1d(np.arange(n), e)
+                e = np.sort(np.concatenate([e, rng.choice(rest, size=ne - e.size, replace=False)]))
+        else:  # every other token, from g
+            e = np.arange(g % 2, n, 2)[:ne]
+            if e.size < ne:
+                rest = np.setdiff1d(np.arange(n), e)
+                e = np.sort(np.concatenate([e, rest[: ne - e.size]]))
+        rows.append(e.astype(np.int64))
+    return np.stack(rows) if rows else np.zeros((Hkv, 0), np.int64)
+
+
+def _run(k, v, ev, misalign=False):
+    Hkv, n, d = k.shape
+    n_keep = n - ev.shape[1]
+    bufs, (ok, ov) = _guarded_outputs(Hkv, n_keep, d, k.dtype, k.device)
+    if misalign:  # inputs one element past an aligned base: forces the 2-byte / 4-byte copy
+        kb = torch.empty(k.numel() + 1, dtype=k.dtype, device=k.device)
+        vb = torch.empty(v.numel() + 1, dtype=v.dtype, device=v.device)
+        kb[1:].copy_(k.reshape(-1))
+        vb[1:].copy_(v.reshape(-1))
+        k, v = kb[1:].view(Hkv, n, d), vb[1:].view(Hkv, n, d)
+    st = torch.zeros(1, dtype=torch.int32, device=k.device)
+    K.compact(k, v, torch.from_numpy(ev).to(k.device), status=st, out_k=ok, out_v=ov)
+    torch.cuda.synchronize()
+    return ok, ov, int(st.item()), bufs
+
+
+@pytest.mark.parametrize("dtype,d", [("bf16", 128), ("bf16", 7), ("f32", 3), ("f32", 64), ("bf16", 256)])
+@pytest.mark.parametrize("n", [1, 5, 1023, 1024, 1025, 3000])
+def test_compact_matches_oracle(dtype, d, n):
+    rng = np.random.default_rng(n * 31 + d)
+    Hkv = 3
+    tdt = torch.bfloat16 if dtype == "bf16" else torch.float32
+    k = torch.randn(Hkv, n, d).to(tdt).cuda()
+    v = torch.randn(Hkv, n, d).to(tdt).cuda()
+    for ne, kind in ((0, "random"), (n, "random"), (n // 2, "random"), (n - n // 7, "runs"), (n // 3, "alt")):
+        ev = _evict_lists(rng, Hkv, n, ne, kind)
+        print(f"[compact] {dtype} d={d} n={n} evict={ne} {kind}", flush=True)
+        ok, ov, st, bufs = _run(k, v, ev)
+        assert st == 0
+        rk, rv = oracle.compact_cache(_bits(k), _bits(v), ev)
+        assert np.array_equal(_bits(ok), rk) and np.array_equal(_bits(ov), rv)
+        _check_guards(bufs, Hkv, n - ne, d)
+
+
+@pytest.mark.parametrize("dtype,d", [("bf16", 128), ("f32", 32)])
+def test_compact_unaligned_inputs(dtype, d):
+    rng = np.random.default_rng(5)
+    Hkv, n = 2, 2500
+    tdt = torch.bfloat16 if dtype == "bf16" else torch.float32
+    k = torch.randn(Hkv, n, d).to(tdt).cuda()
+    v = torch.randn(Hkv, n, d).to(tdt).cuda()
+    ev = _evict_lists(rng, Hkv, n, 1900, "random")
+    print(f"[compact] unaligned {dtype} d={d}", flush=True)
+    ok, ov, st, bufs = _run(k, v, ev, misalign=True)
+    assert st == 0
+    rk, rv = oracle.compact_cache(_bits(k), _bits(v), ev)
+    assert np.array_equal(_bits(ok), rk) and np.array_equal(_bits(ov), rv)
+    _check_guards(bufs, Hkv, n - 1900, d)
+
+
+@pytest.mark.parametrize("bad", ["unsorted", "duplicate", "too_large", "negative"])
+def test_compact_bad_lists_flagged_and_contained(bad):
+    Hkv, n, d = 2, 3000, 16
+    k = torch.randn(Hkv, n, d).cuda()
+    v = torch.randn(Hkv, n, d).cuda()
+    rng = np.random.default_rng(9)
+    ev = _evict_lists(rng, Hkv, n, 1000, "random")
+    if bad == "unsorted":
+        ev[1, 10], ev[1, 500] = ev[1, 500], ev[1, 10]
+    elif bad == "duplicate":
+        ev[0, 700] = ev[0, 699]
+    elif bad == "too_large":
+        ev[1, -1] = n + 5
+    else:
+        ev[0, 0] = -3
+    print(f"[compact] bad list: {bad}", flush=True)
+    ok, ov, st, bufs = _run(k, v, ev)
+    assert st & K.STATUS_BAD_INDEX
+    _check_guards(bufs, Hkv, n - 1000, d)
+    with pytest.raises(K.DropKVInvalidError):
+        K.compact(k, v, torch.from_numpy(ev).cuda())
+
+
+def test_compact_invalid_arguments_launch_nothing():
+    k = torch.randn(2, 100, 8).cuda()
+    ev = torch.zeros((2, 101), dtype=torch.int64, device="cuda")
+    with pytest.raises(K.DropKVInvalidError):
+        K.compact(k, k.clone(), ev)  # more evictions than tokens
+    with pytest.raises(K.DropKVInvalidError):
+        K.compact(k, k.clone(), torch.zeros((3, 4), dtype=torch.int64, device="cuda"))
+
+
+def test_score_then_compact_full_layer():
+    """The step after scoring: the 32K Llama layer, scored, then its cache compacted."""
+    cfg = synth.CONFIGS["llama_32k"]
+    case = synth.make_case(cfg)
+    to_t = lambda a: torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).cuda()
+    q, k, v = to_t(case.q), to_t(case.k), to_t(case.v)
+    ne = cfg.n_evicts()[0]
+    print(f"[compact] score -> compact llama_32k evict={ne}", flush=True)
+    _, idx = K.score(q, k, v, pool_kernel=cfg.pool_kernel, n_evict=ne)
+    ok, ov = K.compact(k, v, idx)
+    torch.cuda.synchronize()
+    rk, rv = oracle.compact_cache(case.k, case.v, idx.cpu().numpy())
+    assert ok.shape == (case.Hkv, case.n - ne, case.d)
+    assert np.array_equal(_bits(ok), rk.view(np.int16)) and np.array_equal(_bits(ov), rv.view(np.int16))
+    # the protected window is always kept, at the end of every head
+    assert np.array_equal(_bits(ok)[:, -case.window:], case.k[:, -case.window:].view(np.int16))
