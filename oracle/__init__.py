@@ -10,3 +10,4 @@ from .dropkv_oracle import (  # noqa: F401
     head_scores, maxpool1d_same, protect_window, evict_smallest, check_args,
     dropkv_oracle, compact_cache,
 )
+from .joint import joint_objective, approx_ratio  # noqa: F401
