@@ -235,6 +235,34 @@ def main():
         "device": torch.cuda.get_device_name(dev),
     }
 
+    # Scoring from given row statistics (no pass 1; the step a prefill kernel's
+    # statistics would allow), timed apart from the scoring steps above.
+    if K.uses_mfma(dcode, case.d):
+        m_, rest_, arg_, a_ = (t.contiguous() for t in K.row_stats(q, k, v))
+        fs_sc = torch.empty_like(scores)
+        fs_ix = torch.empty_like(evict)
+
+        def fs_step():
+            K.score_from_stats(q, k, v, m_, rest_, arg_, a_, pool_kernel=cfg.pool_kernel,
+                               n_evict=n_evict, workspace=ws, status=status, scores=fs_sc,
+                               evict_idx=fs_ix)
+        for _ in range(args.warmup):
+            fs_step()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(args.steps):
+            fs_step()
+        e1.record()
+        torch.cuda.synchronize()
+        if int(status.item()) != 0:
+            raise SystemExit(f"device status {int(status.item())} scoring from statistics")
+        fs_ms = e0.elapsed_time(e1) / args.steps
+        rec["from_stats"] = {
+            "ms_per_step": round(fs_ms, 4), "tokens_per_s": round(case.n / (fs_ms * 1e-3), 1),
+            "speedup_vs_step": round(ms_per_step / fs_ms, 3),
+            "evict_equal": bool(torch.equal(fs_ix, evict)),
+        }
+
     # Cache compaction (the step after scoring), timed apart from the scoring
     # steps above: copies each head's kept rows of K and V into a compact cache.
     if n_evict < case.n:

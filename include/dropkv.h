@@ -171,6 +171,39 @@ int dropkv_stage_log(float* out_ms, char* out_names, int32_t names_bytes, int32_
                      int32_t* out_calls);
 
 /*
+ * Scoring from given window-row statistics, without pass 1: when a prefill
+ * attention kernel has already seen the window rows, its per-row statistics
+ * replace the first of the two streams over K and V (the step before the
+ * path; the atlas summary of the paper, Experimental setup, lists
+ * FlashAttention-2 among the work it builds on). Inputs as dropkv_score
+ * (bf16 with d = 128 only, the MFMA path), plus per window row r = h*window + i
+ * of query head h (device pointers, fp32 unless stated):
+ *   m      [Hq*window]     largest logit x_max, x = q.k / sqrt(d) (natural units)
+ *   rest   [Hq*window]     R = sum_{j != argmax} exp(x_j - x_max)
+ *   argmax [Hq*window]     int32, lowest index attaining x_max (read where R < 1)
+ *   a      [Hq*window][d]  attention output sum_j p_j v_j
+ * exactly what dropkv_row_stats exports. Outputs and errors as dropkv_score
+ * (NONFINITE also for non-finite statistics or an argmax outside [0, n) on a
+ * row with R < 1). Synchronous.
+ */
+int dropkv_score_from_stats(const void* q, const void* k, const void* v, int64_t n, int32_t window,
+                            int32_t Hq, int32_t Hkv, int32_t d, int32_t pool_kernel, int64_t n_evict,
+                            const float* m, const float* rest, const int32_t* argmax, const float* a,
+                            float* out_scores, int64_t* out_evict_idx, void* stream);
+
+/*
+ * Asynchronous form of dropkv_score_from_stats, with caller-owned workspace
+ * (>= dropkv_workspace_bytes(DROPKV_BF16, ...), 256-byte aligned) and device
+ * status word, as dropkv_score_ex (which it mirrors; the status word is
+ * cleared by the call).
+ */
+int dropkv_score_from_stats_ex(const void* q, const void* k, const void* v, int64_t n, int32_t window,
+                               int32_t Hq, int32_t Hkv, int32_t d, int32_t pool_kernel, int64_t n_evict,
+                               const float* m, const float* rest, const int32_t* argmax, const float* a,
+                               float* out_scores, int64_t* out_evict_idx, void* workspace,
+                               size_t workspace_bytes, int32_t* d_status, void* stream);
+
+/*
  * Cache compaction, the step after scoring (write-up section 代码映射与边界:
  * the scorer returns per-head eviction indices and the caller drops those
  * tokens from its cache). Copies the rows of k and v [Hkv][n][d] (dtype

@@ -10,14 +10,16 @@ from .binding import (  # noqa: F401
     BF16, F32, FLAG_GENERIC, FLAG_STAGE_LOG, STATUS_BAD_INDEX, STATUS_NONFINITE, STATUS_SINGULAR,
     DropKVError,
     DropKVInvalidError, DropKVNonFiniteError, DropKVNotBuiltError, DropKVSingularError, LIB_PATH,
-    compact, load_library, raw_scores, row_stats, score, score_ex, select, stage_log, stage_times,
+    compact, load_library, raw_scores, row_stats, score, score_ex, score_from_stats, select,
+    stage_log, stage_times,
     uses_mfma,
     version,
     workspace_bytes,
 )
 
 __all__ = [
-    "score", "score_ex", "raw_scores", "row_stats", "select", "compact", "stage_times", "stage_log",
+    "score", "score_ex", "score_from_stats", "raw_scores", "row_stats", "select", "compact",
+    "stage_times", "stage_log",
     "workspace_bytes",
     "uses_mfma",
     "load_library", "version", "DropKVError", "DropKVInvalidError", "DropKVSingularError",

@@ -37,6 +37,10 @@ SIGNATURES = {
     "dropkv_stage_times": (_i32, [_i32, _p, _p, _p, _i64, _i32, _i32, _i32, _i32, _i32, _i64, _p,
                                   _p, _u32, _p, _p, _i32, _p, _p]),
     "dropkv_stage_log": (_i32, [_p, _p, _i32, _p, _p]),
+    "dropkv_score_from_stats": (_i32, [_p, _p, _p, _i64, _i32, _i32, _i32, _i32, _i32, _i64, _p, _p,
+                                       _p, _p, _p, _p, _p]),
+    "dropkv_score_from_stats_ex": (_i32, [_p, _p, _p, _i64, _i32, _i32, _i32, _i32, _i32, _i64, _p,
+                                          _p, _p, _p, _p, _p, _p, _sz, _p, _p]),
     "dropkv_compact": (_i32, [_i32, _p, _p, _i64, _i32, _i32, _p, _i64, _p, _p, _p, _p]),
     "dropkv_uses_mfma": (_i32, [_i32, _i32]),
     "dropkv_last_error": (_c.c_char_p, []),
@@ -215,6 +219,40 @@ def select(S, *, window: int, pool_kernel: int, n_evict: int, stream=None):
                            idx.data_ptr() if n_evict > 0 else None, _stream_handle(stream))
     _raise(rc)
     return scores, idx
+
+
+def score_from_stats(q, k, v, m, rest, argmax, a, *, pool_kernel: int, n_evict: int, stream=None,
+                     workspace=None, status=None, scores=None, evict_idx=None):
+    """Scores and evict indices from given window-row statistics (no pass 1):
+    m, rest [Hq*window] fp32, argmax [Hq*window] int32, a [Hq*window, d] fp32,
+    as row_stats returns them. bf16 q, k, v with d = 128. With `workspace`
+    and `status` (device tensors, as for score_ex) the call is asynchronous."""
+    torch = _torch()
+    lib = load_library()
+    Hq, Hkv, d, n, w = _shapes(q, k, v)
+    if _dtype_code(q) != BF16:
+        raise DropKVInvalidError(ERR_INVALID, "score_from_stats takes bf16 q, k, v")
+    rows = Hq * w
+    for t, dt, shape in ((m, torch.float32, (rows,)), (rest, torch.float32, (rows,)),
+                         (argmax, torch.int32, (rows,)), (a, torch.float32, (rows, d))):
+        if t.dtype != dt or tuple(t.shape) != shape or not t.is_cuda or not t.is_contiguous():
+            raise DropKVInvalidError(ERR_INVALID, "row statistics must be contiguous GPU tensors "
+                                     "m, rest [rows] fp32, argmax [rows] int32, a [rows, d] fp32")
+    if scores is None:
+        scores = torch.empty((Hkv, n), dtype=torch.float32, device=q.device)
+    if evict_idx is None:
+        evict_idx = torch.empty((Hkv, max(n_evict, 0)), dtype=torch.int64, device=q.device)
+    ptrs = (q.data_ptr(), k.data_ptr(), v.data_ptr(), n, w, Hq, Hkv, d, pool_kernel, n_evict,
+            m.data_ptr(), rest.data_ptr(), argmax.data_ptr(), a.data_ptr(), scores.data_ptr(),
+            evict_idx.data_ptr() if n_evict > 0 else None)
+    if workspace is not None:
+        rc = lib.dropkv_score_from_stats_ex(*ptrs, workspace.data_ptr(),
+                                            workspace.numel() * workspace.element_size(),
+                                            status.data_ptr(), _stream_handle(stream))
+    else:
+        rc = lib.dropkv_score_from_stats(*ptrs, _stream_handle(stream))
+    _raise(rc)
+    return scores, evict_idx
 
 
 def compact(k, v, evict_idx, *, status=None, out_k=None, out_v=None, stream=None):

@@ -172,6 +172,36 @@ int check_inputs(const void* q, const void* k, const void* v) {
   return DROPKV_OK;
 }
 
+int check_from_stats(const void* q, const void* k, const void* v, int64_t n, int32_t window, int32_t Hq,
+                     int32_t Hkv, int32_t d, int32_t pool_kernel, int64_t n_evict, const float* m,
+                     const float* rest, const int32_t* argmax, const float* a, float* out_scores,
+                     int64_t* out_evict_idx) {
+  if (const char* msg = validate(DROPKV_BF16, n, window, Hq, Hkv, d)) return fail(DROPKV_ERR_INVALID, msg);
+  if (!mfma_supported(DROPKV_BF16, d)) return fail(DROPKV_ERR_INVALID, "scoring from statistics needs bf16 inputs with d = 128");
+  if (const char* msg = validate_select(n, window, Hkv, pool_kernel, n_evict)) return fail(DROPKV_ERR_INVALID, msg);
+  if (int rc = check_inputs(q, k, v)) return rc;
+  if (!m || !rest || !argmax || !a || !is_device_ptr(m) || !is_device_ptr(rest) || !is_device_ptr(argmax) ||
+      !is_device_ptr(a))
+    return fail(DROPKV_ERR_INVALID, "m, rest, argmax and a must be device pointers");
+  if (!out_scores || !is_device_ptr(out_scores)) return fail(DROPKV_ERR_INVALID, "out_scores must be a device pointer");
+  if (n_evict > 0 && (!out_evict_idx || !is_device_ptr(out_evict_idx)))
+    return fail(DROPKV_ERR_INVALID, "out_evict_idx must be a device pointer when n_evict > 0");
+  return DROPKV_OK;
+}
+
+int enqueue_from_stats(const void* q, const void* k, const void* v, const Shape& s, const Workspace& ws,
+                       int32_t pool_kernel, int64_t n_evict, const float* m, const float* rest,
+                       const int32_t* argmax, const float* a, float* out_scores, int64_t* out_evict_idx,
+                       hipStream_t st) {
+  FoldInfo fold{};
+  hipError_t e = launch_mfma_from_stats(q, k, v, s, ws, st, m, rest, argmax, a, &fold);
+  if (e != hipSuccess) return fail_hip(e, "score from statistics");
+  e = launch_select(ws.S, s.n, s.w, s.Hkv, pool_kernel, n_evict, out_scores, out_evict_idx, ws.status, &fold,
+                    ws.sel, st);
+  if (e != hipSuccess) return fail_hip(e, "select");
+  return DROPKV_OK;
+}
+
 int score_sync(int dtype, const void* q, const void* k, const void* v, int64_t n, int32_t w,
                int32_t Hq, int32_t Hkv, int32_t d, int32_t pool_kernel, int64_t n_evict,
                float* out_scores, int64_t* out_idx, hipStream_t st) {
@@ -478,6 +508,46 @@ int dropkv_stage_log(float* out_ms, char* out_names, int32_t names_bytes, int32_
     out_names[names_bytes - 1] = 0;
   }
   return DROPKV_OK;
+}
+
+int dropkv_score_from_stats(const void* q, const void* k, const void* v, int64_t n, int32_t window,
+                            int32_t Hq, int32_t Hkv, int32_t d, int32_t pool_kernel, int64_t n_evict,
+                            const float* m, const float* rest, const int32_t* argmax, const float* a,
+                            float* out_scores, int64_t* out_evict_idx, void* stream) {
+  g_last_error.clear();
+  if (int rc = check_from_stats(q, k, v, n, window, Hq, Hkv, d, pool_kernel, n_evict, m, rest, argmax, a,
+                                out_scores, out_evict_idx))
+    return rc;
+  const Shape s{n, window, Hq, Hkv, d};
+  hipStream_t st = (hipStream_t)stream;
+  std::lock_guard<std::mutex> lock(g_ws_mutex);
+  void* base = nullptr;
+  if (int rc = get_workspace(carve_workspace(nullptr, s, true).bytes, &base)) return rc;
+  Workspace ws = carve_workspace(base, s, true);
+  if (int rc = enqueue_from_stats(q, k, v, s, ws, pool_kernel, n_evict, m, rest, argmax, a, out_scores,
+                                  out_evict_idx, st))
+    return rc;
+  return sync_status(ws, st);
+}
+
+int dropkv_score_from_stats_ex(const void* q, const void* k, const void* v, int64_t n, int32_t window,
+                               int32_t Hq, int32_t Hkv, int32_t d, int32_t pool_kernel, int64_t n_evict,
+                               const float* m, const float* rest, const int32_t* argmax, const float* a,
+                               float* out_scores, int64_t* out_evict_idx, void* workspace,
+                               size_t workspace_bytes, int32_t* d_status, void* stream) {
+  g_last_error.clear();
+  if (int rc = check_from_stats(q, k, v, n, window, Hq, Hkv, d, pool_kernel, n_evict, m, rest, argmax, a,
+                                out_scores, out_evict_idx))
+    return rc;
+  if (!workspace || ((uintptr_t)workspace & 255) || !is_device_ptr(workspace))
+    return fail(DROPKV_ERR_INVALID, "workspace must be a 256-byte aligned device pointer");
+  if (!d_status || !is_device_ptr(d_status)) return fail(DROPKV_ERR_INVALID, "d_status must be a device pointer");
+  const Shape s{n, window, Hq, Hkv, d};
+  Workspace ws = carve_workspace(workspace, s, true);
+  if (ws.bytes > workspace_bytes) return fail(DROPKV_ERR_INVALID, "workspace too small");
+  ws.status = d_status;
+  return enqueue_from_stats(q, k, v, s, ws, pool_kernel, n_evict, m, rest, argmax, a, out_scores,
+                            out_evict_idx, (hipStream_t)stream);
 }
 
 int dropkv_compact(int32_t dtype, const void* k, const void* v, int64_t n, int32_t Hkv, int32_t d,

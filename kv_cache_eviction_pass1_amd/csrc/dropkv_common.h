@@ -105,6 +105,13 @@ hipError_t launch_mfma_path(const void* q, const void* k, const void* v, const S
                             const Workspace& ws, hipStream_t st, StageEvents* se, bool fold_in_select,
                             FoldInfo* fold);
 // Adds the argmax terms described by `fold` into S [Hkv][n] (one block per head).
+// MFMA path from caller-given row statistics (m, R, argmax, a per window row,
+// row r = h * window + i): no pass 1; clears the status word, flag counts and
+// select histograms itself; *fold as with fold_in_select.
+hipError_t launch_mfma_from_stats(const void* q, const void* k, const void* v, const Shape& s,
+                                  const Workspace& ws, hipStream_t st, const float* m,
+                                  const float* rest, const int32_t* argmax, const float* a,
+                                  FoldInfo* fold);
 hipError_t launch_fold(const FoldInfo& fold, int64_t n, int32_t Hkv, float* S, int32_t* status,
                        hipStream_t st);
 bool mfma_supported(int dtype, int d);

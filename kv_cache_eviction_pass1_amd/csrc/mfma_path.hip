@@ -78,6 +78,25 @@ __device__ __forceinline__ float pair_sum(float x) {
   return __uint_as_float(s[0]) + __uint_as_float(s[1]);
 }
 
+// ||v_j||^2 of token l%32 of a subtile from the V operand of C = a V^T (lane l
+// holds dims 16ks + 8(l/32) .. +7 of that token): two-term bf16 dot products
+// (exact squares, fp32 sums) over the lane's half of the dims, plus the other
+// half-lane's. Used when no ||v||^2 array from pass 1 exists.
+__device__ __forceinline__ float vnorm_from_operand(const bf16x8 (&vb)[8]) {
+  typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+  float a0 = 0.f, a1 = 0.f;
+#pragma unroll
+  for (int ks = 0; ks < 8; ++ks) {
+    const bf16x2 p0 = {vb[ks][0], vb[ks][1]}, p1 = {vb[ks][2], vb[ks][3]};
+    const bf16x2 p2 = {vb[ks][4], vb[ks][5]}, p3 = {vb[ks][6], vb[ks][7]};
+    a0 = __builtin_amdgcn_fdot2_f32_bf16(p0, p0, a0, false);
+    a1 = __builtin_amdgcn_fdot2_f32_bf16(p1, p1, a1, false);
+    a0 = __builtin_amdgcn_fdot2_f32_bf16(p2, p2, a0, false);
+    a1 = __builtin_amdgcn_fdot2_f32_bf16(p3, p3, a1, false);
+  }
+  return pair_sum(a0 + a1);
+}
+
 __device__ __forceinline__ bf16x8 ld16(const char* p) { return *(const bf16x8*)p; }
 
 // Wait until this wave's direct-to-LDS loads have landed, then barrier: after
@@ -801,8 +820,10 @@ __device__ __forceinline__ void p2_tile(const P2Args& P, const char* kb, const c
   }
 }
 
+template <bool NVC>
 __device__ __forceinline__ void p2_combine(const P2Args& P, float (*red)[TT][2], int nwa,
-                                           int64_t tokbase_tile, int64_t chunk_end, int g) {
+                                           int64_t tokbase_tile, int64_t chunk_end, int g,
+                                           const char* vtile) {
   if (threadIdx.x < TT) {
     const int64_t tok = tokbase_tile + threadIdx.x;
     if (tok < chunk_end) {
@@ -812,10 +833,72 @@ __device__ __forceinline__ void p2_combine(const P2Args& P, float (*red)[TT][2],
         T2 += red[wv][threadIdx.x][1];
       }
       // sum_rows r^2 (||a||^2 - 2 a.v + ||v||^2) = ||v||^2 T2 - 2 T1
-      const float nvj = P.nv[(size_t)g * P.n + tok];
+      float nvj;
+      if constexpr (NVC) {  // from the tile's V row (bf16 squares are exact, fp32 sums)
+        float acc = 0.f;
+        for (int c = 0; c < HD; c += 8) {
+          const bf16x8 x = ld16(vtile + toff((int)threadIdx.x, c));
+#pragma unroll
+          for (int i = 0; i < 8; ++i) acc = fmaf((float)x[i], (float)x[i], acc);
+        }
+        nvj = acc;
+      } else {
+        nvj = P.nv[(size_t)g * P.n + tok];
+      }
       const float s = fmaxf(fmaf(nvj, T2, -2.0f * T1), 0.0f) * P.invG;
       P.S[((size_t)blockIdx.y * P.Hkv + g) * P.n + tok] = s;
     }
+  }
+}
+
+// ---- row state from given statistics (no pass 1)
+
+struct ImportArgs {
+  const float* m;         // [rows] largest logit, natural units (x = q.k / sqrt(d))
+  const float* rest;      // [rows] R = sum_{j != argmax} exp(x_j - x_max)
+  const int32_t* argmax;  // [rows] lowest index attaining x_max (read where R < 1)
+  const float* a;         // [rows][HD] attention output
+  int64_t n, rows;
+  int Rg;
+  RowStats rs;
+  int32_t* flagcount;
+  int32_t* status;
+};
+
+// One wave per window row: what the merge would leave for pass 2 (bias, a in
+// bf16 and ||a_bf16||^2, the flag of rows with p_max > 1/2 and their argmax),
+// computed from statistics supplied by the caller, e.g. by a prefill
+// attention kernel that saw the same rows.
+__global__ __launch_bounds__(256) void k_import(ImportArgs I) {
+  const int lane = threadIdx.x & 63;
+  const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (row >= I.rows) return;
+  const int g = (int)(row / I.Rg);
+  const float2 av = *(const float2*)(I.a + (size_t)row * HD + 2 * lane);
+  const uint16_t b0 = f32_to_bf16_rne(av.x), b1 = f32_to_bf16_rne(av.y);
+  const float f0 = bf16_to_f32(b0), f1 = bf16_to_f32(b1);
+  float na = fmaf(f0, f0, f1 * f1);
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) na += __shfl_xor(na, o, 64);
+  *(float2*)(I.rs.a + (size_t)row * HD + 2 * lane) = av;
+  *(uint32_t*)(I.rs.a_bf + (size_t)row * HD + 2 * lane) = (uint32_t)b0 | ((uint32_t)b1 << 16);
+  const float m = I.m[row], R = I.rest[row];
+  bool bad = !finite_f(av.x) || !finite_f(av.y);
+  bad = __builtin_amdgcn_ballot_w64(bad) != 0 || !finite_f(m) || !finite_f(R) || !(R >= 0.f);
+  const bool flagged = !bad && R < 1.0f;
+  const int js = flagged ? I.argmax[row] : -1;
+  if (lane == 0) {
+    const float L = 1.0f + R;
+    I.rs.m[row] = m;
+    I.rs.L[row] = L;
+    I.rs.rest[row] = R;
+    I.rs.na[row] = na;
+    I.rs.bias[row] = m * kLog2e + __log2f(L);
+    I.rs.jstar[row] = js;
+    I.rs.flag[row] = flagged ? 1 : 0;
+    I.rs.fixval[row] = 0.f;
+    if (bad || (flagged && (js < 0 || js >= I.n))) atomicOr(I.status, kStatusNonFinite);
+    else if (flagged) atomicAdd(&I.flagcount[g], 1);
   }
 }
 
@@ -874,7 +957,7 @@ __device__ __forceinline__ void p2_values(const float (&y2)[16], const f32x16& C
 
 // One 32-token subtile of the pass-2 fast path for this wave's 32 rows:
 // returns this wave's share of the score of token l%32 (valid in lanes < 32).
-template <bool MASK>
+template <bool MASK, bool NVC>
 __device__ __forceinline__ float p2_sub(const char* kt, const char* vt, float nvj, const LdsOff& off,
                                         const bf16x8 (&qa)[8], const bf16x8 (&aa)[8],
                                         const float (&nb2)[16], const float (&cinit)[16], float c2x2,
@@ -886,6 +969,7 @@ __device__ __forceinline__ float p2_sub(const char* kt, const char* vt, float nv
   for (int ks = 0; ks < 8; ++ks) vb[ks] = ld16(vt + off.k[ks]);
   // all sixteen operand reads in flight before the first MFMA waits on one
   __builtin_amdgcn_sched_barrier(0);
+  if constexpr (NVC) nvj = vnorm_from_operand(vb);
   f32x16 X = {}, C;
 #pragma unroll
   for (int i = 0; i < 16; ++i) C[i] = cinit[i];
@@ -919,7 +1003,9 @@ __device__ __forceinline__ float p2_sub(const char* kt, const char* vt, float nv
   return pair_sum(fmaf(nvj, q2, -2.0f * q1));
 }
 
-template <int NW>
+// NVC: ||v_j||^2 comes from the V operands in registers instead of the array
+// pass 1 writes (the path that starts from given row statistics).
+template <int NW, bool NVC>
 __global__ __launch_bounds__(NW * 64) void k_pass2(P2Args P, FixArgs F) {
   if (NW >= 2 && blockIdx.x >= gridDim.x - (NW >= 2 ? FXC : 0)) {
     // the argmax fix-up (independent of pass 2) runs as FXC extra workgroups per head
@@ -932,7 +1018,7 @@ __global__ __launch_bounds__(NW * 64) void k_pass2(P2Args P, FixArgs F) {
   __shared__ __attribute__((aligned(1024))) char vbuf[3][TILE_BYTES];
   __shared__ float red3[3][NW][TT];
   __shared__ float nvbuf[3][TT];
-  constexpr int kDmaPerTile = 32 / NW + 1;  // direct-to-LDS instructions per wave per tile
+  constexpr int kDmaPerTile = 32 / NW + (NVC ? 0 : 1);  // direct-to-LDS instructions per wave per tile
   const int chunk = blockIdx.x, rg = blockIdx.y, g = blockIdx.z;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
   const int h = lane >> 5, l32 = lane & 31;
@@ -946,7 +1032,7 @@ __global__ __launch_bounds__(NW * 64) void k_pass2(P2Args P, FixArgs F) {
   const int ntiles = (int)((t1 - t0 + TT - 1) / TT);
   const uint16_t* kh = P.k + (size_t)g * P.n * HD;
   const uint16_t* vh = P.v + (size_t)g * P.n * HD;
-  const float* __restrict__ nvg = P.nv + (size_t)g * P.n;
+  const float* __restrict__ nvg = NVC ? nullptr : P.nv + (size_t)g * P.n;
   float* __restrict__ Sout = P.S + ((size_t)blockIdx.y * P.Hkv + g) * P.n;
   const bool flagged = P.flagcount[g] != 0;
   const DmaOff<NW> doff = dma_offsets<NW>(wave, lane);
@@ -994,18 +1080,18 @@ __global__ __launch_bounds__(NW * 64) void k_pass2(P2Args P, FixArgs F) {
       p2_tile(P, kbuf[b], vbuf[b], t0 + (int64_t)it * TT, lane, active, rb, qa, aa, bias, cinit,
               true, g, red, wave);
       __syncthreads();
-      p2_combine(P, red, nwa, t0 + (int64_t)it * TT, t1, g);
+      p2_combine<NVC>(P, red, nwa, t0 + (int64_t)it * TT, t1, g, vbuf[b]);
     }
     return;
   }
 
   // the fast path's only vector-memory loads are the direct-to-LDS tile loads
   // (K, V and ||v||^2), so `vmcnt <= one tile's loads` means the older tile landed
-  if (ntiles > 0) issue_nv(nvg, t0, P.n, nvbuf[0], lane);
+  if (!NVC && ntiles > 0) issue_nv(nvg, t0, P.n, nvbuf[0], lane);
   if (ntiles > 1) {
     issue_any<NW>(kh, t0 + TT, P.n, kbuf[1], wave, lane, doff);
     issue_any<NW>(vh, t0 + TT, P.n, vbuf[1], wave, lane, doff);
-    issue_nv(nvg, t0 + TT, P.n, nvbuf[1], lane);
+    if (!NVC) issue_nv(nvg, t0 + TT, P.n, nvbuf[1], lane);
   }
   const float c2x2 = 2.0f * P.c2;
   const LdsOff off = lds_offsets(lane);
@@ -1033,7 +1119,7 @@ __global__ __launch_bounds__(NW * 64) void k_pass2(P2Args P, FixArgs F) {
     if (t + 2 < ntiles) {
       issue_any<NW>(kh, tb + 2 * TT, P.n, kn, wave, lane, doff);
       issue_any<NW>(vh, tb + 2 * TT, P.n, vn, wave, lane, doff);
-      issue_nv(nvg, tb + 2 * TT, P.n, nvn, lane);
+      if (!NVC) issue_nv(nvg, tb + 2 * TT, P.n, nvn, lane);
     }
   };
   // token offset of this lane's column relative to n - w, for the causal mask
@@ -1045,7 +1131,7 @@ __global__ __launch_bounds__(NW * 64) void k_pass2(P2Args P, FixArgs F) {
     if (active) {
 #pragma unroll
       for (int sub = 0; sub < 2; ++sub) {
-        const float sw = p2_sub<false>(kbuf[B] + sub * 32 * 256, vbuf[B] + sub * 32 * 256,
+        const float sw = p2_sub<false, NVC>(kbuf[B] + sub * 32 * 256, vbuf[B] + sub * 32 * 256,
                                        nvbuf[B][sub * 32 + l32], off, qa, aa, nb2, cinit, c2x2, 0, rbase, P.w);
         if (h == 0) red3[B][wave][sub * 32 + l32] = sw;
       }
@@ -1064,7 +1150,7 @@ __global__ __launch_bounds__(NW * 64) void k_pass2(P2Args P, FixArgs F) {
 #pragma unroll
       for (int sub = 0; sub < 2; ++sub) {
         const int64_t tok = tok_rel0 + (int64_t)t * TT + sub * 32;
-        const float sw = p2_sub<true>(kbuf[b] + sub * 32 * 256, vbuf[b] + sub * 32 * 256,
+        const float sw = p2_sub<true, NVC>(kbuf[b] + sub * 32 * 256, vbuf[b] + sub * 32 * 256,
                                       nvbuf[b][sub * 32 + l32], off, qa, aa, nb2, cinit, c2x2, tok, rbase, P.w);
         if (h == 0) red3[b][wave][sub * 32 + l32] = sw;
       }
@@ -1185,10 +1271,10 @@ hipError_t launch_mfma_path(const void* q, const void* k, const void* v, const S
             p.tpc2, s.Hkv, c2, 1.0f / (float)s.G(), ws.rs, nv, flagcount, Spart};
   const dim3 grid2(p.nch2 + (p.nw2 >= 2 ? FXC : 0), p.nrg2, s.Hkv);
   switch (p.nw2) {
-    case 8: k_pass2<8><<<grid2, 512, 0, st>>>(a2, af); break;
-    case 4: k_pass2<4><<<grid2, 256, 0, st>>>(a2, af); break;
-    case 2: k_pass2<2><<<grid2, 128, 0, st>>>(a2, af); break;
-    default: k_pass2<1><<<grid2, 64, 0, st>>>(a2, af); break;
+    case 8: k_pass2<8, false><<<grid2, 512, 0, st>>>(a2, af); break;
+    case 4: k_pass2<4, false><<<grid2, 256, 0, st>>>(a2, af); break;
+    case 2: k_pass2<2, false><<<grid2, 128, 0, st>>>(a2, af); break;
+    default: k_pass2<1, false><<<grid2, 64, 0, st>>>(a2, af); break;
   }
   record_stage(se, "pass2", st);
   if (p.nrg2 > 1) {
@@ -1204,6 +1290,43 @@ hipError_t launch_mfma_path(const void* q, const void* k, const void* v, const S
     if (e != hipSuccess) return e;
     record_stage(se, "fold", st);
   }
+  return hipGetLastError();
+}
+
+hipError_t launch_mfma_from_stats(const void* q, const void* k, const void* v, const Shape& s,
+                                  const Workspace& ws, hipStream_t st, const float* m,
+                                  const float* rest, const int32_t* argmax, const float* a,
+                                  FoldInfo* fold) {
+  const Plan p = make_plan(s);
+  char* extra = (char*)ws.extra;  // the same carve as launch_mfma_path (nv stays unused)
+  auto take = [&](size_t bytes) { char* r = extra; extra += (bytes + 255) / 256 * 256; return r; };
+  (void)take(sizeof(float) * (size_t)s.Hkv * s.n);
+  float* fx = (float*)take(sizeof(float) * (size_t)FXC * s.Hkv * p.Rg * FXSTRIDE);
+  int32_t* flagcount = ws.flagcount;
+  float* Spart = p.nrg2 > 1 ? (float*)take(sizeof(float) * (size_t)p.nrg2 * s.Hkv * s.n) : ws.S;
+  const float c2 = kLog2e / sqrtf((float)HD);
+  hipError_t e = launch_init(ws.status, flagcount, ws.sel, s.Hkv, st);
+  if (e != hipSuccess) return e;
+  const int64_t rows = (int64_t)s.Hkv * p.Rg;
+  ImportArgs ai{m, rest, argmax, a, s.n, rows, p.Rg, ws.rs, flagcount, ws.status};
+  k_import<<<(unsigned)((rows + 3) / 4), 256, 0, st>>>(ai);
+  FixArgs af{(const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v, s.n, s.w, p.Rg, s.Hkv, c2,
+             ws.rs, flagcount, fx};
+  if (p.nw2 < 2) k_fixup<<<dim3(FXC, s.Hkv), 256, 0, st>>>(af);
+  P2Args a2{(const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v, s.n, s.w, p.Rg, p.nw2,
+            p.tpc2, s.Hkv, c2, 1.0f / (float)s.G(), ws.rs, nullptr, flagcount, Spart};
+  const dim3 grid2(p.nch2 + (p.nw2 >= 2 ? FXC : 0), p.nrg2, s.Hkv);
+  switch (p.nw2) {
+    case 8: k_pass2<8, true><<<grid2, 512, 0, st>>>(a2, af); break;
+    case 4: k_pass2<4, true><<<grid2, 256, 0, st>>>(a2, af); break;
+    case 2: k_pass2<2, true><<<grid2, 128, 0, st>>>(a2, af); break;
+    default: k_pass2<1, true><<<grid2, 64, 0, st>>>(a2, af); break;
+  }
+  if (p.nrg2 > 1) {
+    const int64_t total = (int64_t)s.Hkv * s.n;
+    k_sum_rowgroups<<<(unsigned)((total + 255) / 256), 256, 0, st>>>(Spart, ws.S, total, p.nrg2);
+  }
+  *fold = FoldInfo{flagcount, ws.rs, fx, s.Hkv, p.Rg, FXC, FXSTRIDE, HD, 1.0f / (float)s.G()};
   return hipGetLastError();
 }
 
