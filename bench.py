@@ -44,6 +44,8 @@ def parse():
     ap.add_argument("--warmup", type=int, default=100)
     ap.add_argument("--workload", default="llama_128k")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-sweep", action="store_true",
+                    help="skip the Qwen2.5-7B-shaped 28-layer x 2-sequence sweep timing")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain device copy of 512 MiB (3 times): the reference kernel "
                          "that scales rocprofv3 FETCH_SIZE / WRITE_SIZE to bytes")
@@ -262,6 +264,46 @@ def main():
             "speedup_vs_step": round(ms_per_step / fs_ms, 3),
             "evict_equal": bool(torch.equal(fs_ix, evict)),
         }
+
+    # The Qwen2.5-7B-shaped sweep (28 layers x 2 sequences of one 128K layer
+    # shape, G = 7), back to back on one stream; MFMA-bound by its arithmetic
+    # intensity. One generated layer's tensors serve every call (the throughput
+    # does not depend on the values; parity of this shape is a test's job).
+    if args.workload == "llama_128k" and not args.no_sweep:
+        qcfg = synth.CONFIGS["qwen_128k_sweep"]
+        qc = synth.make_case(qcfg)
+        qq, qk, qv = (to_dev(t).contiguous() for t in (qc.q, qc.k, qc.v))
+        qne = qcfg.n_evicts()[0]
+        qws = torch.empty(K.workspace_bytes(K.BF16, qc.n, qc.window, qc.Hq, qc.Hkv, qc.d),
+                          dtype=torch.uint8, device=dev)
+        qst = torch.zeros(1, dtype=torch.int32, device=dev)
+        qsc = torch.empty((qc.Hkv, qc.n), dtype=torch.float32, device=dev)
+        qix = torch.empty((qc.Hkv, qne), dtype=torch.int64, device=dev)
+        calls = qcfg.layers * qcfg.batch
+
+        def q_step():
+            K.score_ex(qq, qk, qv, pool_kernel=qcfg.pool_kernel, n_evict=qne, workspace=qws,
+                       status=qst, scores=qsc, evict_idx=qix)
+        for _ in range(args.warmup):
+            q_step()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(calls):
+            q_step()
+        e1.record()
+        torch.cuda.synchronize()
+        if int(qst.item()) != 0:
+            raise SystemExit(f"device status {int(qst.item())} in the Qwen sweep")
+        q_ms = e0.elapsed_time(e1)
+        q_flop = calls * 8 * qc.d * qc.group * qc.window * qc.Hkv * qc.n
+        rec["qwen_sweep"] = {
+            "workload": "Qwen2.5-7B-shaped layer (Hq 28, Hkv 4, d 128, n 131072, w 64), 28 layers x 2 sequences",
+            "calls": calls, "ms": round(q_ms, 3), "ms_per_call": round(q_ms / calls, 4),
+            "tokens_per_s": round(calls * qc.n / (q_ms * 1e-3), 1),
+            "mfma_TFLOPs": round(q_flop / (q_ms * 1e-3) / 1e12, 1),
+            "mfma_frac": round(q_flop / (q_ms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),
+        }
+        del qq, qk, qv, qws
 
     # Cache compaction (the step after scoring), timed apart from the scoring
     # steps above: copies each head's kept rows of K and V into a compact cache.
