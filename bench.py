@@ -44,8 +44,9 @@ def parse():
     ap.add_argument("--warmup", type=int, default=100)
     ap.add_argument("--workload", default="llama_128k")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--no-sweep", action="store_true",
-                    help="skip the Qwen2.5-7B-shaped 28-layer x 2-sequence sweep timing")
+    ap.add_argument("--no-extras", action="store_true",
+                    help="time only the headline step: skip the scoring-from-statistics, "
+                         "Qwen2.5-7B sweep and cache-compaction timings that follow it")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain device copy of 512 MiB (3 times): the reference kernel "
                          "that scales rocprofv3 FETCH_SIZE / WRITE_SIZE to bytes")
@@ -239,7 +240,7 @@ def main():
 
     # Scoring from given row statistics (no pass 1; the step a prefill kernel's
     # statistics would allow), timed apart from the scoring steps above.
-    if K.uses_mfma(dcode, case.d):
+    if K.uses_mfma(dcode, case.d) and not args.no_extras:
         m_, rest_, arg_, a_ = (t.contiguous() for t in K.row_stats(q, k, v))
         fs_sc = torch.empty_like(scores)
         fs_ix = torch.empty_like(evict)
@@ -269,7 +270,7 @@ def main():
     # shape, G = 7), back to back on one stream; MFMA-bound by its arithmetic
     # intensity. One generated layer's tensors serve every call (the throughput
     # does not depend on the values; parity of this shape is a test's job).
-    if args.workload == "llama_128k" and not args.no_sweep:
+    if args.workload == "llama_128k" and not args.no_extras:
         qcfg = synth.CONFIGS["qwen_128k_sweep"]
         qc = synth.make_case(qcfg)
         qq, qk, qv = (to_dev(t).contiguous() for t in (qc.q, qc.k, qc.v))
@@ -307,7 +308,7 @@ def main():
 
     # Cache compaction (the step after scoring), timed apart from the scoring
     # steps above: copies each head's kept rows of K and V into a compact cache.
-    if n_evict < case.n:
+    if n_evict < case.n and not args.no_extras:
         n_keep = case.n - n_evict
         out_k = torch.empty((case.Hkv, n_keep, case.d), dtype=k.dtype, device=dev)
         out_v = torch.empty_like(out_k)
