@@ -11,3 +11,4 @@ from .dropkv_oracle import (  # noqa: F401
     dropkv_oracle, compact_cache,
 )
 from .joint import joint_objective, approx_ratio  # noqa: F401
+from .decode import decode_init, decode_step, decode_scratch, decode_select  # noqa: F401
