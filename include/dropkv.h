@@ -226,6 +226,71 @@ int dropkv_compact(int32_t dtype, const void* k, const void* v, int64_t n, int32
                    const int64_t* evict_idx, int64_t n_evict, void* out_k, void* out_v,
                    int32_t* d_status, void* stream);
 
+/*
+ * Decode-time rescoring with a sliding observation window.
+ *
+ * The pages leave a decode-time scorer to future work and call per-step decode
+ * bandwidth-bound (atlas summary, Limitations). These calls keep the raw score
+ * S of the core formula (write-up section 核心公式: the sum over the window
+ * queries of ||Delta_j||^2, averaged over the query heads of each KV head;
+ * before pooling) up to date while tokens are appended one at a time, the
+ * window always being the last `window` query positions: a step adds the
+ * terms of the new position's query rows and subtracts those of the rows that
+ * leave the window (a row's terms depend only on the keys it sees, which
+ * appending does not change). S is kept in fp64 and the subtracted terms are
+ * bit for bit the added ones, so the maintained S matches scoring the grown
+ * cache from scratch to the path's own accuracy. After an eviction the
+ * cache's softmaxes change: compact, then start again with dropkv_decode_init.
+ *
+ * Inputs are bf16 with d = 128. k and v are the caller's cache, [Hkv][n_max][d]
+ * (head stride n_max token rows), of which the first n rows of each head are
+ * valid; q is [Hq][window][d] (the last `window` positions' query rows, head
+ * major), q_new [Hq][d] (the appended position's query rows). The caller owns
+ * `state`: device memory of dropkv_decode_state_bytes(...) bytes, 256-byte
+ * aligned, used only through these calls (layout: fp64 S [Hkv][n_max] first,
+ * then the window's rows). All calls are asynchronous on `stream` and return
+ * DROPKV_OK once enqueued, DROPKV_ERR_INVALID (nothing launched: shape, count
+ * or pointer checks) or DROPKV_ERR_DEVICE. Device-side findings go to the
+ * caller's device int32 `d_status` as DROPKV_STATUS_* bits: a window row whose
+ * rest mass is <= 2^-24 (SINGULAR) or non-finite values (NONFINITE) make S
+ * unspecified until the next init. Limits: window >= 1, Hq a multiple of Hkv,
+ * n_max < 2^31. Calls on one state must not overlap.
+ */
+size_t dropkv_decode_state_bytes(int64_t n_max, int32_t window, int32_t Hq, int32_t Hkv, int32_t d);
+
+/* Score the first n tokens (window < n <= n_max) and fill the state; clears
+ * *d_status first. The window rows' statistics come from the same pass 1 and
+ * merge as dropkv_score. */
+int dropkv_decode_init(const void* q, const void* k, const void* v, int64_t n, int64_t n_max, int32_t window,
+                       int32_t Hq, int32_t Hkv, int32_t d, void* state, size_t state_bytes, int32_t* d_status,
+                       void* stream);
+
+/* One appended token: the caller has written its key and value at row n - 1
+ * of every head, and n counts it (window + 2 <= n <= n_max, and the state
+ * holds n - 1 tokens: one call per token, in order). ORs status bits. */
+int dropkv_decode_step(const void* q_new, const void* k, const void* v, int64_t n, int64_t n_max,
+                       int32_t window, int32_t Hq, int32_t Hkv, int32_t d, void* state, size_t state_bytes,
+                       int32_t* d_status, void* stream);
+
+/* Recompute S from the window rows kept in the state (no new statistics):
+ * equal to the incrementally kept S up to fp64 rounding. ORs status bits. */
+int dropkv_decode_rebuild(const void* k, const void* v, int64_t n, int64_t n_max, int32_t window, int32_t Hq,
+                          int32_t Hkv, int32_t d, void* state, size_t state_bytes, int32_t* d_status,
+                          void* stream);
+
+/* The kept raw score S rounded to fp32 into out_S [Hkv][n]. */
+int dropkv_decode_scores(const void* state, size_t state_bytes, int64_t n, int64_t n_max, int32_t window,
+                         int32_t Hq, int32_t Hkv, int32_t d, float* out_S, void* stream);
+
+/* Re-eviction on the kept score: max-pool (odd pool_kernel, stride 1, same
+ * padding), +inf on the last `window` positions, the n_evict smallest per head
+ * under (score, index) ascending, exactly as dropkv_score does after its own
+ * raw scores (0 <= n_evict <= n - window). out_scores [Hkv][n] fp32,
+ * out_evict_idx [Hkv][n_evict] int64. ORs status bits. */
+int dropkv_decode_select(void* state, size_t state_bytes, int64_t n, int64_t n_max, int32_t window, int32_t Hq,
+                         int32_t Hkv, int32_t d, int32_t pool_kernel, int64_t n_evict, float* out_scores,
+                         int64_t* out_evict_idx, int32_t* d_status, void* stream);
+
 /* 1 if (dtype, d) takes the MFMA path by default, 0 if the plain-VALU path. */
 int dropkv_uses_mfma(int32_t dtype, int32_t d);
 

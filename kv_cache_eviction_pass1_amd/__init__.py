@@ -8,7 +8,7 @@ load the library; the first call does, and fails loudly if it is not built.
 
 from .binding import (  # noqa: F401
     BF16, F32, FLAG_GENERIC, FLAG_STAGE_LOG, STATUS_BAD_INDEX, STATUS_NONFINITE, STATUS_SINGULAR,
-    DropKVError,
+    DecodeScorer, DropKVError,
     DropKVInvalidError, DropKVNonFiniteError, DropKVNotBuiltError, DropKVSingularError, LIB_PATH,
     compact, load_library, raw_scores, row_stats, score, score_ex, score_from_stats, select,
     stage_log, stage_times,
@@ -18,7 +18,7 @@ from .binding import (  # noqa: F401
 )
 
 __all__ = [
-    "score", "score_ex", "score_from_stats", "raw_scores", "row_stats", "select", "compact",
+    "score", "score_ex", "score_from_stats", "raw_scores", "row_stats", "select", "compact", "DecodeScorer",
     "stage_times", "stage_log",
     "workspace_bytes",
     "uses_mfma",

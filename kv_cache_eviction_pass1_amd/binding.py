@@ -42,6 +42,13 @@ SIGNATURES = {
     "dropkv_score_from_stats_ex": (_i32, [_p, _p, _p, _i64, _i32, _i32, _i32, _i32, _i32, _i64, _p,
                                           _p, _p, _p, _p, _p, _p, _sz, _p, _p]),
     "dropkv_compact": (_i32, [_i32, _p, _p, _i64, _i32, _i32, _p, _i64, _p, _p, _p, _p]),
+    "dropkv_decode_state_bytes": (_sz, [_i64, _i32, _i32, _i32, _i32]),
+    "dropkv_decode_init": (_i32, [_p, _p, _p, _i64, _i64, _i32, _i32, _i32, _i32, _p, _sz, _p, _p]),
+    "dropkv_decode_step": (_i32, [_p, _p, _p, _i64, _i64, _i32, _i32, _i32, _i32, _p, _sz, _p, _p]),
+    "dropkv_decode_rebuild": (_i32, [_p, _p, _i64, _i64, _i32, _i32, _i32, _i32, _p, _sz, _p, _p]),
+    "dropkv_decode_scores": (_i32, [_p, _sz, _i64, _i64, _i32, _i32, _i32, _i32, _p, _p]),
+    "dropkv_decode_select": (_i32, [_p, _sz, _i64, _i64, _i32, _i32, _i32, _i32, _i32, _i64, _p, _p, _p,
+                                    _p]),
     "dropkv_uses_mfma": (_i32, [_i32, _i32]),
     "dropkv_last_error": (_c.c_char_p, []),
     "dropkv_version": (_c.c_char_p, []),
@@ -291,6 +298,99 @@ def compact(k, v, evict_idx, *, status=None, out_k=None, out_v=None, stream=None
     if sync and int(status.item()) & STATUS_BAD_INDEX:
         raise DropKVInvalidError(ERR_INVALID, "evict_idx is not strictly increasing inside [0, n)")
     return out_k, out_v
+
+
+class DecodeScorer:
+    """Decode-time rescoring of one sequence's cache (dropkv_decode_* calls).
+
+    The cache is the caller's k, v [Hkv, n_max, d] bf16 tensors, of which the
+    first n token rows of each head are valid; the scorer owns the device
+    state (sized for n_max) and a device status word. Calls are asynchronous
+    on the current stream; check() synchronises and raises on a recorded
+    singular / non-finite row.
+    """
+
+    def __init__(self, *, n_max: int, window: int, Hq: int, Hkv: int, d: int, device=None):
+        torch = _torch()
+        self.lib = load_library()
+        self.n_max, self.window, self.Hq, self.Hkv, self.d = n_max, window, Hq, Hkv, d
+        nbytes = self.lib.dropkv_decode_state_bytes(n_max, window, Hq, Hkv, d)
+        if nbytes == 0:
+            raise DropKVInvalidError(ERR_INVALID, "unsupported decode shape (bf16, d = 128)")
+        self.state = torch.empty(nbytes, dtype=torch.uint8, device=device or "cuda")
+        self.status = torch.zeros(1, dtype=torch.int32, device=self.state.device)
+        self.n = 0
+
+    def _kv(self, k, v):
+        torch = _torch()
+        want = (self.Hkv, self.n_max, self.d)
+        for t in (k, v):
+            if tuple(t.shape) != want or t.dtype != torch.bfloat16 or not t.is_cuda or not t.is_contiguous():
+                raise DropKVInvalidError(ERR_INVALID, f"k and v must be contiguous bf16 GPU tensors {list(want)}")
+
+    def _args(self):
+        return (self.n_max, self.window, self.Hq, self.Hkv, self.d)
+
+    def init(self, q, k, v, n: int, stream=None):
+        """Score the first n tokens; q [Hq, window, d] are the last window positions' query rows."""
+        self._kv(k, v)
+        if tuple(q.shape) != (self.Hq, self.window, self.d) or q.dtype != k.dtype or not q.is_contiguous():
+            raise DropKVInvalidError(ERR_INVALID, "q must be contiguous bf16 [Hq, window, d]")
+        _raise(self.lib.dropkv_decode_init(q.data_ptr(), k.data_ptr(), v.data_ptr(), n, *self._args(),
+                                           self.state.data_ptr(), self.state.numel(), self.status.data_ptr(),
+                                           _stream_handle(stream)))
+        self.n = n
+
+    def step(self, q_new, k, v, stream=None):
+        """Append one token: its key and value are already at row self.n of k and v; q_new [Hq, d]."""
+        self._kv(k, v)
+        if tuple(q_new.shape) != (self.Hq, self.d) or q_new.dtype != k.dtype or not q_new.is_contiguous():
+            raise DropKVInvalidError(ERR_INVALID, "q_new must be contiguous bf16 [Hq, d]")
+        n = self.n + 1
+        _raise(self.lib.dropkv_decode_step(q_new.data_ptr(), k.data_ptr(), v.data_ptr(), n, *self._args(),
+                                           self.state.data_ptr(), self.state.numel(), self.status.data_ptr(),
+                                           _stream_handle(stream)))
+        self.n = n
+
+    def rebuild(self, k, v, stream=None):
+        """Recompute the kept score from the stored window rows."""
+        self._kv(k, v)
+        _raise(self.lib.dropkv_decode_rebuild(k.data_ptr(), v.data_ptr(), self.n, *self._args(),
+                                              self.state.data_ptr(), self.state.numel(), self.status.data_ptr(),
+                                              _stream_handle(stream)))
+
+    def raw_scores(self, stream=None):
+        """The kept raw score as fp32 [Hkv, n]."""
+        torch = _torch()
+        out = torch.empty((self.Hkv, self.n), dtype=torch.float32, device=self.state.device)
+        _raise(self.lib.dropkv_decode_scores(self.state.data_ptr(), self.state.numel(), self.n, *self._args(),
+                                             out.data_ptr(), _stream_handle(stream)))
+        return out
+
+    def raw_scores_f64(self):
+        """The kept fp64 score [Hkv, n] (a view into the state: S64 comes first in its layout)."""
+        torch = _torch()
+        S64 = self.state[: 8 * self.Hkv * self.n_max].view(torch.float64).view(self.Hkv, self.n_max)
+        return S64[:, : self.n]
+
+    def select(self, *, pool_kernel: int, n_evict: int, stream=None):
+        """Re-eviction on the kept score: (pooled scores [Hkv, n], evict_idx [Hkv, n_evict])."""
+        torch = _torch()
+        scores = torch.empty((self.Hkv, self.n), dtype=torch.float32, device=self.state.device)
+        idx = torch.empty((self.Hkv, max(n_evict, 0)), dtype=torch.int64, device=self.state.device)
+        _raise(self.lib.dropkv_decode_select(self.state.data_ptr(), self.state.numel(), self.n, *self._args(),
+                                             pool_kernel, n_evict, scores.data_ptr(),
+                                             idx.data_ptr() if n_evict > 0 else None, self.status.data_ptr(),
+                                             _stream_handle(stream)))
+        return scores, idx
+
+    def check(self):
+        """Synchronise and raise if a call recorded a singular or non-finite row."""
+        word = int(self.status.item())
+        if word & STATUS_SINGULAR:
+            raise DropKVSingularError(ERR_SINGULAR, "a window row has a probability that rounds to 1 (singular)")
+        if word & STATUS_NONFINITE:
+            raise DropKVNonFiniteError(ERR_NONFINITE, "non-finite inputs or scores")
 
 
 def stage_times(q, k, v, *, pool_kernel: int, n_evict: int, flags: int = 0, stream=None):

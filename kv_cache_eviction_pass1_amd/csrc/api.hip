@@ -172,6 +172,24 @@ int check_inputs(const void* q, const void* k, const void* v) {
   return DROPKV_OK;
 }
 
+// Decode-time rescoring: shape checks shared by its entry points. `n` is the
+// current token count; need_n is the smallest count the call accepts.
+int check_decode(int64_t n, int64_t need_n, int64_t n_max, int32_t window, int32_t Hq, int32_t Hkv, int32_t d,
+                 const void* state, size_t state_bytes) {
+  if (d != 128) return fail(DROPKV_ERR_INVALID, "decode rescoring needs bf16 inputs with d = 128");
+  if (window < 1) return fail(DROPKV_ERR_INVALID, "need window >= 1");
+  if (Hq < 1 || Hkv < 1 || Hq % Hkv != 0) return fail(DROPKV_ERR_INVALID, "need Hq a positive multiple of Hkv >= 1");
+  if (n_max > ((int64_t)1 << 31) - 1) return fail(DROPKV_ERR_INVALID, "n_max must fit in int32 token indices");
+  if (n < need_n || n > n_max) return fail(DROPKV_ERR_INVALID, "token count out of range for this call (see dropkv.h)");
+  if ((double)Hkv * (double)n_max * 128.0 > 1e15 || (double)Hq * window > 1e8)
+    return fail(DROPKV_ERR_INVALID, "shape too large");
+  if (!state || ((uintptr_t)state & 255) || !is_device_ptr(state))
+    return fail(DROPKV_ERR_INVALID, "state must be a 256-byte aligned device pointer");
+  if (carve_decode_state(nullptr, n_max, window, Hq, Hkv).bytes > state_bytes)
+    return fail(DROPKV_ERR_INVALID, "state too small (dropkv_decode_state_bytes)");
+  return DROPKV_OK;
+}
+
 int check_from_stats(const void* q, const void* k, const void* v, int64_t n, int32_t window, int32_t Hq,
                      int32_t Hkv, int32_t d, int32_t pool_kernel, int64_t n_evict, const float* m,
                      const float* rest, const int32_t* argmax, const float* a, float* out_scores,
@@ -567,6 +585,80 @@ int dropkv_compact(int32_t dtype, const void* k, const void* v, int64_t n, int32
   hipError_t e = launch_compact(dtype, k, v, n, Hkv, d, evict_idx, n_evict, out_k, out_v, d_status,
                                 (hipStream_t)stream);
   if (e != hipSuccess) return fail_hip(e, "compact");
+  return DROPKV_OK;
+}
+
+size_t dropkv_decode_state_bytes(int64_t n_max, int32_t window, int32_t Hq, int32_t Hkv, int32_t d) {
+  if (d != 128 || window < 1 || Hq < 1 || Hkv < 1 || Hq % Hkv != 0 || n_max < 2 ||
+      n_max > ((int64_t)1 << 31) - 1)
+    return 0;
+  return carve_decode_state(nullptr, n_max, window, Hq, Hkv).bytes;
+}
+
+int dropkv_decode_init(const void* q, const void* k, const void* v, int64_t n, int64_t n_max, int32_t window,
+                       int32_t Hq, int32_t Hkv, int32_t d, void* state, size_t state_bytes, int32_t* d_status,
+                       void* stream) {
+  g_last_error.clear();
+  if (int rc = check_decode(n, (int64_t)window + 1, n_max, window, Hq, Hkv, d, state, state_bytes)) return rc;
+  if (int rc = check_inputs(q, k, v)) return rc;
+  if (!d_status || !is_device_ptr(d_status)) return fail(DROPKV_ERR_INVALID, "d_status must be a device pointer");
+  const DecState S = carve_decode_state(state, n_max, window, Hq, Hkv);
+  hipError_t e = launch_decode_init(q, k, v, n, n_max, window, Hq, Hkv, S, d_status, (hipStream_t)stream);
+  if (e != hipSuccess) return fail_hip(e, "decode init");
+  return DROPKV_OK;
+}
+
+int dropkv_decode_step(const void* q_new, const void* k, const void* v, int64_t n, int64_t n_max,
+                       int32_t window, int32_t Hq, int32_t Hkv, int32_t d, void* state, size_t state_bytes,
+                       int32_t* d_status, void* stream) {
+  g_last_error.clear();
+  if (int rc = check_decode(n, (int64_t)window + 2, n_max, window, Hq, Hkv, d, state, state_bytes)) return rc;
+  if (int rc = check_inputs(q_new, k, v)) return rc;
+  if (!d_status || !is_device_ptr(d_status)) return fail(DROPKV_ERR_INVALID, "d_status must be a device pointer");
+  const DecState S = carve_decode_state(state, n_max, window, Hq, Hkv);
+  hipError_t e = launch_decode_step(q_new, k, v, n, n_max, window, Hq, Hkv, S, d_status, (hipStream_t)stream);
+  if (e != hipSuccess) return fail_hip(e, "decode step");
+  return DROPKV_OK;
+}
+
+int dropkv_decode_rebuild(const void* k, const void* v, int64_t n, int64_t n_max, int32_t window, int32_t Hq,
+                          int32_t Hkv, int32_t d, void* state, size_t state_bytes, int32_t* d_status,
+                          void* stream) {
+  g_last_error.clear();
+  if (int rc = check_decode(n, (int64_t)window + 1, n_max, window, Hq, Hkv, d, state, state_bytes)) return rc;
+  if (!k || !v || !is_device_ptr(k) || !is_device_ptr(v)) return fail(DROPKV_ERR_INVALID, "k and v must be device pointers");
+  if (!d_status || !is_device_ptr(d_status)) return fail(DROPKV_ERR_INVALID, "d_status must be a device pointer");
+  const DecState S = carve_decode_state(state, n_max, window, Hq, Hkv);
+  hipError_t e = launch_decode_rebuild(k, v, n, n_max, window, Hq, Hkv, S, d_status, (hipStream_t)stream);
+  if (e != hipSuccess) return fail_hip(e, "decode rebuild");
+  return DROPKV_OK;
+}
+
+int dropkv_decode_scores(const void* state, size_t state_bytes, int64_t n, int64_t n_max, int32_t window,
+                         int32_t Hq, int32_t Hkv, int32_t d, float* out_S, void* stream) {
+  g_last_error.clear();
+  if (int rc = check_decode(n, (int64_t)window + 1, n_max, window, Hq, Hkv, d, state, state_bytes)) return rc;
+  if (!out_S || !is_device_ptr(out_S)) return fail(DROPKV_ERR_INVALID, "out_S must be a device pointer");
+  const DecState S = carve_decode_state(const_cast<void*>(state), n_max, window, Hq, Hkv);
+  hipError_t e = launch_decode_scores(S, n, n_max, Hkv, out_S, (hipStream_t)stream);
+  if (e != hipSuccess) return fail_hip(e, "decode scores");
+  return DROPKV_OK;
+}
+
+int dropkv_decode_select(void* state, size_t state_bytes, int64_t n, int64_t n_max, int32_t window, int32_t Hq,
+                         int32_t Hkv, int32_t d, int32_t pool_kernel, int64_t n_evict, float* out_scores,
+                         int64_t* out_evict_idx, int32_t* d_status, void* stream) {
+  g_last_error.clear();
+  if (int rc = check_decode(n, (int64_t)window + 1, n_max, window, Hq, Hkv, d, state, state_bytes)) return rc;
+  if (const char* m = validate_select(n, window, Hkv, pool_kernel, n_evict)) return fail(DROPKV_ERR_INVALID, m);
+  if (!out_scores || !is_device_ptr(out_scores)) return fail(DROPKV_ERR_INVALID, "out_scores must be a device pointer");
+  if (n_evict > 0 && (!out_evict_idx || !is_device_ptr(out_evict_idx)))
+    return fail(DROPKV_ERR_INVALID, "out_evict_idx must be a device pointer when n_evict > 0");
+  if (!d_status || !is_device_ptr(d_status)) return fail(DROPKV_ERR_INVALID, "d_status must be a device pointer");
+  const DecState S = carve_decode_state(state, n_max, window, Hq, Hkv);
+  hipError_t e = launch_decode_select(S, n, n_max, window, Hq, Hkv, pool_kernel, n_evict, out_scores, out_evict_idx,
+                                      d_status, (hipStream_t)stream);
+  if (e != hipSuccess) return fail_hip(e, "decode select");
   return DROPKV_OK;
 }
 

@@ -1,0 +1,786 @@
+// Decode-time rescoring: the raw DropKV score of a growing cache, kept up to
+// date as tokens are appended, with the observation window sliding over the
+// last w query positions.
+//
+// Pages: the atlas summary (Limitations) leaves a decode-time kernel to future
+// work and calls per-step decode bandwidth-bound; the write-up's core formula
+// (核心公式) sums ||Delta_j||^2 over the window queries and averages over the
+// query heads of a KV head. A window row's terms depend only on the keys it
+// sees, which appending does not change, so one step is: add the terms of the
+// G new rows of each KV head (position n - 1), subtract those of the G rows
+// leaving the window (position n - 1 - w).
+//
+// Exactness of the subtraction. The raw score is kept in fp64, and a row's
+// terms are always produced by the same kernel from the same stored row state
+// (query, a, exponent bias, ...), so the terms subtracted when a row leaves are
+// bit for bit the ones added when it entered; the fp64 sums then cancel them
+// to rounding far below fp32, however much larger they were than what stays.
+//
+// Kernels (bf16, d = 128):
+//   k_dec_stats / k_dec_merge  new rows' attention: max logit, exact rest mass
+//       R = sum_{j != argmax} 2^{x_j - m}, argmax, a (VALU; 16 lanes per token)
+//   k_dec_contrib  signed terms r^2 ||a - v_j||^2 of a list of rows for every
+//       token (X = Q K^T and C = a V^T on MFMA, one wave per 32 tokens, K and V
+//       read straight into the MFMA operands), added into the fp64 score
+//   k_dec_star     argmax terms of rows with p_max > 1/2 (kept per row, so the
+//       exact value added is the one later removed) and the commit of the new
+//       rows into the window's ring of row slots
+// The first window comes from the MFMA pass 1 + merge + argmax fix-up.
+#include "dropkv_common.h"
+
+namespace dropkv {
+
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+constexpr int HD = 128;
+constexpr int kRowBatch = 8;       // new rows per k_dec_stats launch
+constexpr int kDecPart = HD + 4;   // floats per stats partial (A[128], m, R, j*, pad)
+constexpr int kContribRows = 1024; // rows per k_dec_contrib launch (LDS tables)
+constexpr int kTokPerWg = 1024;    // tokens per k_dec_contrib workgroup (4 waves x 8 subtiles)
+constexpr int kStatsTok = 2048;    // tokens per k_dec_stats workgroup
+
+__device__ __forceinline__ f32x16 mfma(bf16x8 a, bf16x8 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ uint16_t rne_bf16(float x) {
+  uint32_t b = __float_as_uint(x);
+  if ((b & 0x7f800000u) == 0x7f800000u) return (uint16_t)((b >> 16) | ((b & 0xffffu) ? 0x40u : 0u));
+  b += 0x7fffu + ((b >> 16) & 1u);
+  return (uint16_t)(b >> 16);
+}
+
+// sum over the 16 lanes of a DPP row, result in every lane of the row
+__device__ __forceinline__ float row16_sum(float x) {
+  x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0xB1, 0xf, 0xf, false));   // quad_perm 1,0,3,2
+  x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x4E, 0xf, 0xf, false));   // quad_perm 2,3,0,1
+  x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x141, 0xf, 0xf, false));  // row_half_mirror
+  x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x140, 0xf, 0xf, false));  // row_mirror
+  return x;
+}
+
+// ---------------------------------------------------------------------------- row table
+
+// Row table index of query head h (of KV head g's G) in slot `slot` (slot w
+// is the staging slot of the position being appended).
+__device__ __forceinline__ int64_t trow(int g, int slot, int h, int w, int G) {
+  return ((int64_t)g * (w + 1) + slot) * G + h;
+}
+
+// State derived from (m, L, a) once, when a row is stored: a in bf16 for the
+// MFMA, C's start value -||a_bf16||^2 / 2 and the exponent bias
+// m log2(e) + log2(L), so that p_j = 2^{x_j log2(e)/sqrt(d) - bias}. One wave
+// per row, lane = 2 dims.
+__device__ __forceinline__ void derive_row(const DecRows& T, int64_t r, float m, float L, int lane) {
+  const float2 av = *(const float2*)(T.a + r * HD + 2 * lane);
+  const uint16_t b0 = rne_bf16(av.x), b1 = rne_bf16(av.y);
+  const float f0 = bf16_to_f32(b0), f1 = bf16_to_f32(b1);
+  float na = fmaf(f0, f0, f1 * f1);
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) na += __shfl_xor(na, o, 64);
+  *(uint32_t*)(T.a_bf + r * HD + 2 * lane) = (uint32_t)b0 | ((uint32_t)b1 << 16);
+  if (lane == 0) {
+    T.cinit[r] = -0.5f * na;
+    T.bias[r] = m * kLog2e + __log2f(L);
+  }
+}
+
+struct LoadArgs {
+  const uint16_t* q;  // [Hq][w][d] window queries
+  RowStats rs;        // window rows r = h * w + i
+  DecRows T;
+  double* S64;
+  int64_t n, n_max;
+  int w, Hq, Hkv;
+};
+
+// Window rows of the first scoring into their slots (slot = position mod w),
+// and the fp64 score cleared. One wave per row; the score is cleared by a
+// grid-stride loop.
+__global__ __launch_bounds__(256) void k_dec_load(LoadArgs A) {
+  const int lane = threadIdx.x & 63;
+  const int G = A.Hq / A.Hkv;
+  {
+    const int64_t tot = (int64_t)A.Hkv * A.n_max;
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < tot; i += (int64_t)gridDim.x * blockDim.x)
+      A.S64[i] = 0.0;
+  }
+  const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (row >= (int64_t)A.Hq * A.w) return;
+  const int h = (int)(row / A.w), i = (int)(row % A.w);
+  const int g = h / G, hl = h % G;
+  const int64_t pos = A.n - A.w + i;
+  const int64_t r = trow(g, (int)(pos % A.w), hl, A.w, G);
+  *(uint32_t*)(A.T.q + r * HD + 2 * lane) = *(const uint32_t*)(A.q + row * HD + 2 * lane);
+  *(float2*)(A.T.a + r * HD + 2 * lane) = *(const float2*)(A.rs.a + row * HD + 2 * lane);
+  const float m = A.rs.m[row], L = A.rs.L[row];
+  if (lane == 0) {
+    A.T.m[r] = m;
+    A.T.L[r] = L;
+    A.T.R[r] = A.rs.rest[row];
+    A.T.jstar[r] = A.rs.flag[row] ? A.rs.jstar[row] : -1;
+    A.T.cstar[r] = 0.f;
+  }
+  derive_row(A.T, r, m, L, lane);
+}
+
+// ---------------------------------------------------------------------------- argmax terms
+
+struct StarInitArgs {
+  FoldInfo f;
+  DecRows T;
+  double* S64;
+  int64_t n, n_max;
+  int w;
+  int32_t* status;
+};
+
+// First window: the argmax terms of flagged rows from the fix-up partials
+// (exact rest mass and ||a - v_j*||^2 without cancellation), added to the
+// score in row order and kept in the row slots. One block per KV head.
+__global__ __launch_bounds__(HD) void k_dec_star_init(StarInitArgs A) {
+  const int g = blockIdx.x;
+  if (A.f.flagcount[g] == 0) return;
+  const int G = A.f.Rg / A.w;
+  __shared__ float red[HD];
+  for (int rr = 0; rr < A.f.Rg; ++rr) {
+    const int64_t row = (int64_t)g * A.f.Rg + rr;
+    if (!A.f.rs.flag[row]) continue;
+    float R;
+    int bits;
+    const float val = fold_value<HD>(A.f, row, red, &R, &bits);
+    const int js = A.f.rs.jstar[row];
+    if (threadIdx.x == 0) {
+      const int hl = rr / A.w, i = rr % A.w;
+      const int64_t r = trow(g, (int)((A.n - A.w + i) % A.w), hl, A.w, G);
+      if (js < 0 || js >= A.n) {
+        atomicOr(A.status, kStatusNonFinite);
+      } else if (bits) {
+        atomicOr(A.status, bits);
+      } else {
+        A.T.R[r] = R;
+        A.T.cstar[r] = val;
+        A.S64[(size_t)g * A.n_max + js] += (double)val / (double)G;
+      }
+    }
+  }
+}
+
+struct StarStepArgs {
+  const uint16_t* v;  // [Hkv][n_max][d]
+  DecRows T;
+  double* S64;
+  int64_t n, n_max;
+  int w, G;
+  int commit;         // 1: step (new rows in the staging slot, commit them); 0: rebuild (all slots)
+  int32_t* status;
+};
+
+// One block per KV head. Step: the new rows' argmax terms (rows with R < 1:
+// ||a - v_j*||^2 / R^2, computed directly) are added and kept, the leaving
+// rows' kept terms are subtracted, then the new rows replace the leaving ones
+// in their slot. Rebuild: every window slot's kept term is added.
+__global__ __launch_bounds__(HD) void k_dec_star(StarStepArgs A) {
+  const int g = blockIdx.x, tid = threadIdx.x;
+  __shared__ float red[HD];
+  const double invG = 1.0 / (double)A.G;
+  double* S = A.S64 + (size_t)g * A.n_max;
+  if (!A.commit) {
+    for (int slot = 0; slot < A.w; ++slot)
+      for (int h = 0; h < A.G; ++h) {
+        const int64_t r = trow(g, slot, h, A.w, A.G);
+        const int js = A.T.jstar[r];
+        if (tid == 0 && js >= 0 && js < A.n) S[js] += (double)A.T.cstar[r] * invG;
+      }
+    return;
+  }
+  const int so = (int)((A.n - 1) % A.w);  // slot of the leaving rows, and of the new ones after the commit
+  for (int h = 0; h < A.G; ++h) {
+    const int64_t rn = trow(g, A.w, h, A.w, A.G);
+    const int js = A.T.jstar[rn];  // uniform
+    if (js >= 0) {
+      const float d = A.T.a[rn * HD + tid] - bf16_to_f32(A.v[((size_t)g * A.n_max + js) * HD + tid]);
+      const float dist = block_sum<HD>(d * d, red);
+      if (tid == 0) {
+        const float R = A.T.R[rn];
+        const float val = dist / (R * R);
+        A.T.cstar[rn] = val;
+        S[js] += (double)val * invG;
+      }
+    } else if (tid == 0) {
+      A.T.cstar[rn] = 0.f;
+    }
+    if (tid == 0) {
+      const int64_t ro = trow(g, so, h, A.w, A.G);
+      const int jo = A.T.jstar[ro];
+      if (jo >= 0 && jo < A.n) S[jo] -= (double)A.T.cstar[ro] * invG;
+    }
+  }
+  __syncthreads();
+  // commit: staging rows into the leaving rows' slot
+  for (int h = 0; h < A.G; ++h) {
+    const int64_t rn = trow(g, A.w, h, A.w, A.G), ro = trow(g, so, h, A.w, A.G);
+    A.T.q[ro * HD + tid] = A.T.q[rn * HD + tid];
+    A.T.a[ro * HD + tid] = A.T.a[rn * HD + tid];
+    A.T.a_bf[ro * HD + tid] = A.T.a_bf[rn * HD + tid];
+    if (tid == 0) {
+      A.T.m[ro] = A.T.m[rn];
+      A.T.L[ro] = A.T.L[rn];
+      A.T.R[ro] = A.T.R[rn];
+      A.T.jstar[ro] = A.T.jstar[rn];
+      A.T.cstar[ro] = A.T.cstar[rn];
+      A.T.bias[ro] = A.T.bias[rn];
+      A.T.cinit[ro] = A.T.cinit[rn];
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------- new rows
+
+struct StatsArgs {
+  const uint16_t* qn;  // [Hq][d] query rows of the appended position
+  const uint16_t* k;   // [Hkv][n_max][d]
+  const uint16_t* v;
+  float* part;         // [nch][Hkv][G][kDecPart]
+  int64_t n, n_max;
+  int G, Hkv, nch, r0, nr;  // rows r0 .. r0 + nr - 1 of each KV head's G (nr <= kRowBatch)
+  float c2;                 // log2(e) / sqrt(d)
+};
+
+// Online state of one row over a set of tokens: largest logit m (log2 units),
+// rest mass R = sum over the other tokens of 2^{x - m}, argmax j (lowest index
+// among equal maxima) and A = sum 2^{x - m} v over all tokens.
+struct OnState {
+  float m, R;
+  int j;
+};
+
+// (m1, R1, j1, A1) merged with (m2, R2, j2, A2); A is the caller's (8 dims per lane)
+__device__ __forceinline__ void on_merge(OnState& s1, float (&A1)[8], OnState s2, const float (&A2)[8]) {
+  if (s2.m == -INFINITY) return;
+  if (s1.m == -INFINITY) {
+    s1 = s2;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) A1[i] = A2[i];
+    return;
+  }
+  const bool win1 = s1.m > s2.m || (s1.m == s2.m && s1.j < s2.j);
+  const float mx = fmaxf(s1.m, s2.m);
+  const float f1 = __builtin_amdgcn_exp2f(s1.m - mx), f2 = __builtin_amdgcn_exp2f(s2.m - mx);
+  s1.R = win1 ? s1.R + (s2.R + 1.0f) * f2 : s2.R + (s1.R + 1.0f) * f1;
+  s1.j = win1 ? s1.j : s2.j;
+  s1.m = mx;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) A1[i] = A1[i] * f1 + A2[i] * f2;
+}
+
+// Per (token chunk, KV head): 16 lanes per token (lane l%16 holds dims
+// 8(l%16) .. +7, so a wave instruction reads 4 whole token rows), rows held
+// in registers; the 16 lane groups of the workgroup are merged through lane
+// shuffles and LDS into one partial per row.
+__global__ __launch_bounds__(256) void k_dec_stats(StatsArgs A) {
+  const int chunk = blockIdx.x, g = blockIdx.y;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int li = lane & 15, grp = lane >> 4;
+  const int nr = A.nr;
+  const int64_t t0 = (int64_t)chunk * kStatsTok;
+  int64_t t1 = t0 + kStatsTok;
+  if (t1 > A.n) t1 = A.n;
+  uint32_t q[kRowBatch][4];
+#pragma unroll
+  for (int r = 0; r < kRowBatch; ++r) {
+    const int rr = r < nr ? r : 0;
+    const uint4 u = *(const uint4*)(A.qn + ((size_t)(g * A.G + A.r0 + rr)) * HD + 8 * li);
+    q[r][0] = u.x; q[r][1] = u.y; q[r][2] = u.z; q[r][3] = u.w;
+  }
+  OnState st[kRowBatch];
+  float acc[kRowBatch][8];
+#pragma unroll
+  for (int r = 0; r < kRowBatch; ++r) {
+    st[r] = OnState{-INFINITY, 0.f, -1};
+#pragma unroll
+    for (int i = 0; i < 8; ++i) acc[r][i] = 0.f;
+  }
+  const uint16_t* kh = A.k + (size_t)g * A.n_max * HD;
+  const uint16_t* vh = A.v + (size_t)g * A.n_max * HD;
+  for (int64_t tb = t0; tb < t1; tb += 16) {
+    const int64_t tok = tb + wave * 4 + grp;
+    const bool ok = tok < t1;
+    const int64_t tr = ok ? tok : t1 - 1;
+    const uint4 ku = *(const uint4*)(kh + tr * HD + 8 * li);
+    const uint4 vu = *(const uint4*)(vh + tr * HD + 8 * li);
+    const uint32_t kw[4] = {ku.x, ku.y, ku.z, ku.w};
+    const uint32_t vw[4] = {vu.x, vu.y, vu.z, vu.w};
+    float vf[8];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      vf[2 * i] = __uint_as_float(vw[i] << 16);
+      vf[2 * i + 1] = __uint_as_float(vw[i] & 0xffff0000u);
+    }
+#pragma unroll
+    for (int r = 0; r < kRowBatch; ++r) {
+      if (r >= nr) break;
+      float d = 0.f;
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        d = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, q[r][i]), __builtin_bit_cast(bf16x2, kw[i]),
+                                            d, false);
+      const float x = row16_sum(d) * A.c2;
+      if (!ok) continue;
+      const float mx = fmaxf(st[r].m, x);
+      const float so = __builtin_amdgcn_exp2f(st[r].m - mx);  // 0 while the state is empty
+      const float e = __builtin_amdgcn_exp2f(x - mx);
+      const bool gt = x > st[r].m;
+      st[r].R = gt ? (st[r].R + 1.0f) * so : st[r].R + e;
+      if (st[r].m == -INFINITY) st[r].R = 0.f;
+      st[r].j = gt ? (int)tok : st[r].j;
+      st[r].m = mx;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) acc[r][i] = fmaf(acc[r][i], so, e * vf[i]);
+    }
+  }
+  // merge the four lane groups of the wave (lanes li, li + 16, li + 32, li + 48)
+#pragma unroll
+  for (int r = 0; r < kRowBatch; ++r) {
+    if (r >= nr) break;
+#pragma unroll
+    for (int o = 16; o < 64; o <<= 1) {
+      OnState s2{__shfl_xor(st[r].m, o, 64), __shfl_xor(st[r].R, o, 64), __shfl_xor(st[r].j, o, 64)};
+      float a2[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) a2[i] = __shfl_xor(acc[r][i], o, 64);
+      // both lanes of a pair merge in the same order (lower lane group first), so they agree bit for bit
+      if (lane & o) {
+        OnState s1 = s2;
+        float a1[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) a1[i] = a2[i];
+        on_merge(s1, a1, st[r], acc[r]);
+        st[r] = s1;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) acc[r][i] = a1[i];
+      } else {
+        on_merge(st[r], acc[r], s2, a2);
+      }
+    }
+  }
+  // then the four waves, in wave order
+  __shared__ float ws[4][kRowBatch][kDecPart];
+  if (grp == 0) {
+#pragma unroll
+    for (int r = 0; r < kRowBatch; ++r) {
+      if (r >= nr) break;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) ws[wave][r][8 * li + i] = acc[r][i];
+      if (li == 0) {
+        ws[wave][r][HD] = st[r].m;
+        ws[wave][r][HD + 1] = st[r].R;
+        ws[wave][r][HD + 2] = __int_as_float(st[r].j);
+      }
+    }
+  }
+  __syncthreads();
+  if (wave == 0 && grp == 0) {
+#pragma unroll
+    for (int r = 0; r < kRowBatch; ++r) {
+      if (r >= nr) break;
+      OnState s1{ws[0][r][HD], ws[0][r][HD + 1], __float_as_int(ws[0][r][HD + 2])};
+      float a1[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) a1[i] = ws[0][r][8 * li + i];
+      for (int wv = 1; wv < 4; ++wv) {
+        OnState s2{ws[wv][r][HD], ws[wv][r][HD + 1], __float_as_int(ws[wv][r][HD + 2])};
+        float a2[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) a2[i] = ws[wv][r][8 * li + i];
+        on_merge(s1, a1, s2, a2);
+      }
+      float* o = A.part + (((size_t)chunk * A.Hkv + g) * A.G + A.r0 + r) * kDecPart;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) o[8 * li + i] = a1[i];
+      if (li == 0) {
+        o[HD] = s1.m;
+        o[HD + 1] = s1.R;
+        o[HD + 2] = __int_as_float(s1.j);
+      }
+    }
+  }
+}
+
+struct DMergeArgs {
+  const float* part;
+  const uint16_t* qn;
+  DecRows T;
+  int64_t n;
+  int G, Hkv, w, nch;
+  int32_t* status;
+};
+
+// One wave per new row: the chunk partials merged in chunk order, the row
+// stored in the staging slot (query, a, m, L = 1 + R, R, argmax of rows with
+// R < 1, derived state). Rejects R <= 2^-24 (singular) and non-finite rows.
+__global__ __launch_bounds__(256) void k_dec_merge(DMergeArgs A) {
+  const int lane = threadIdx.x & 63;
+  const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (row >= (int64_t)A.Hkv * A.G) return;
+  const int g = (int)(row / A.G), h = (int)(row % A.G);
+  float m = -INFINITY, R = 0.f, a0 = 0.f, a1 = 0.f;
+  int j = -1;
+  for (int c = 0; c < A.nch; ++c) {
+    const float* o = A.part + (((size_t)c * A.Hkv + g) * A.G + h) * kDecPart;
+    const float m2 = o[HD], R2 = o[HD + 1];
+    const int j2 = __float_as_int(o[HD + 2]);
+    const float2 a2 = *(const float2*)(o + 2 * lane);
+    if (m2 == -INFINITY) continue;
+    if (m == -INFINITY) { m = m2; R = R2; j = j2; a0 = a2.x; a1 = a2.y; continue; }
+    const bool win1 = m > m2 || (m == m2 && j < j2);
+    const float mx = fmaxf(m, m2);
+    const float f1 = __builtin_amdgcn_exp2f(m - mx), f2 = __builtin_amdgcn_exp2f(m2 - mx);
+    R = win1 ? R + (R2 + 1.0f) * f2 : R2 + (R + 1.0f) * f1;
+    j = win1 ? j : j2;
+    m = mx;
+    a0 = a0 * f1 + a2.x * f2;
+    a1 = a1 * f1 + a2.y * f2;
+  }
+  const float L = 1.0f + R;
+  const float x0 = a0 / L, x1 = a1 / L;
+  const int64_t r = trow(g, A.w, h, A.w, A.G);
+  *(float2*)(A.T.a + r * HD + 2 * lane) = make_float2(x0, x1);
+  *(uint32_t*)(A.T.q + r * HD + 2 * lane) = *(const uint32_t*)(A.qn + row * HD + 2 * lane);
+  bool bad = !finite_f(m) || !finite_f(R) || !finite_f(x0) || !finite_f(x1);
+  bad = __builtin_amdgcn_ballot_w64(bad) != 0;
+  const float m_nat = m / kLog2e;
+  if (lane == 0) {
+    A.T.m[r] = m_nat;
+    A.T.L[r] = L;
+    A.T.R[r] = R;
+    A.T.jstar[r] = (!bad && R < 1.0f) ? j : -1;
+    A.T.cstar[r] = 0.f;
+    if (bad) atomicOr(A.status, kStatusNonFinite);
+    else if (R <= kSingularRest) atomicOr(A.status, kStatusSingular);
+  }
+  derive_row(A.T, r, m_nat, L, lane);
+}
+
+// ---------------------------------------------------------------------------- signed terms
+
+struct ContribArgs {
+  const uint16_t* k;  // [Hkv][n_max][d]
+  const uint16_t* v;
+  DecRows T;
+  double* S64;        // [Hkv][n_max]
+  int64_t n, n_max;
+  int w, G;
+  int mode;           // 0: window entries e0 .. e1-1 (rows at n - w + e); 1: step (new rows +, leaving rows -)
+  int e0, e1;
+  float c2;           // log2(e) / sqrt(d)
+};
+
+// Row rr of this launch's list (per KV head): entry e = rr / G, query head rr % G.
+__device__ __forceinline__ void entry_of(const ContribArgs& A, int e, int& slot, int64_t& pos, float& sign) {
+  if (A.mode == 0) {
+    pos = A.n - A.w + e;
+    slot = (int)(pos % A.w);
+    sign = 1.0f;
+  } else if (e == 0) {
+    slot = A.w;
+    pos = A.n - 1;
+    sign = 1.0f;
+  } else {
+    slot = (int)((A.n - 1) % A.w);
+    pos = A.n - 1 - A.w;
+    sign = -1.0f;
+  }
+}
+
+// Operand layout (32x32x16 bf16 MFMA): lane l holds row / token l%32 and, at
+// step ks, dims 64 (l/32) + 8 ks .. +7 (a fixed permutation of the 128 dims,
+// the same for every operand, so each lane's loads are 128 contiguous bytes).
+__device__ __forceinline__ int opdim(int lane, int ks) { return 64 * (lane >> 5) + 8 * ks; }
+
+// Per (chunk of kTokPerWg tokens, KV head): each wave takes 32-token subtiles;
+// per subtile and 32-row block X = Q K^T and C = a V^T - ||a||^2/2 on MFMA,
+// then per (row, token) the term r^2 ||a - v_j||^2 with r = p / (1 - p), for
+// tokens the row sees other than its kept argmax, summed with the row's sign
+// in fp64 and added to the score.
+template <bool ONEBLOCK>
+__global__ __launch_bounds__(256) void k_dec_contrib(ContribArgs A) {
+  const int chunk = blockIdx.x, g = blockIdx.y;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int h = lane >> 5, l32 = lane & 31;
+  const int nrows = (A.e1 - A.e0) * A.G;
+  const int nb = (nrows + 31) / 32;
+  __shared__ __attribute__((aligned(16))) float s_bias[kContribRows];
+  __shared__ __attribute__((aligned(16))) float s_cinit[kContribRows];
+  __shared__ __attribute__((aligned(16))) float s_sign[kContribRows];
+  __shared__ __attribute__((aligned(16))) int s_pos[kContribRows];
+  __shared__ __attribute__((aligned(16))) int s_js[kContribRows];
+  __shared__ int64_t s_row[kContribRows];
+  for (int rr = threadIdx.x; rr < nb * 32; rr += blockDim.x) {
+    if (rr < nrows) {
+      int slot;
+      int64_t pos;
+      float sign;
+      entry_of(A, A.e0 + rr / A.G, slot, pos, sign);
+      const int64_t r = trow(g, slot, rr % A.G, A.w, A.G);
+      s_row[rr] = r;
+      s_bias[rr] = A.T.bias[r];
+      s_cinit[rr] = A.T.cinit[r];
+      s_sign[rr] = sign;
+      s_pos[rr] = (int)pos;
+      s_js[rr] = A.T.jstar[r];
+    } else {  // padding rows: p = 0
+      s_row[rr] = -1;
+      s_bias[rr] = INFINITY;
+      s_cinit[rr] = 0.f;
+      s_sign[rr] = 0.f;
+      s_pos[rr] = -1;
+      s_js[rr] = -1;
+    }
+  }
+  __syncthreads();
+  const uint16_t* kh = A.k + (size_t)g * A.n_max * HD;
+  const uint16_t* vh = A.v + (size_t)g * A.n_max * HD;
+  const double invG = 1.0 / (double)A.G;
+  double* S = A.S64 + (size_t)g * A.n_max;
+  const int64_t t0 = (int64_t)chunk * kTokPerWg;
+
+  auto load_rows = [&](int b, bf16x8 (&qa)[8], bf16x8 (&aa)[8]) {
+    const int64_t r = s_row[32 * b + l32];
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks) {
+      if (r >= 0) {
+        qa[ks] = *(const bf16x8*)(A.T.q + r * HD + opdim(lane, ks));
+        aa[ks] = *(const bf16x8*)(A.T.a_bf + r * HD + opdim(lane, ks));
+      } else {
+        qa[ks] = bf16x8{};
+        aa[ks] = bf16x8{};
+      }
+    }
+  };
+  // signed fp64 sum of the block's 16 terms of this lane's token
+  auto block_terms = [&](int b, const bf16x8 (&qa)[8], const bf16x8 (&aa)[8], const bf16x8 (&kb)[8],
+                         const bf16x8 (&vb)[8], float nvj, int tok, double& acc) {
+    f32x16 X = {}, C;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const float4 c4 = *(const float4*)(&s_cinit[32 * b + 8 * j + 4 * h]);
+      C[4 * j] = c4.x;
+      C[4 * j + 1] = c4.y;
+      C[4 * j + 2] = c4.z;
+      C[4 * j + 3] = c4.w;
+    }
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks) X = mfma(qa[ks], kb[ks], X);
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks) C = mfma(aa[ks], vb[ks], C);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int base = 32 * b + 8 * j + 4 * h;
+      const float4 bi = *(const float4*)(&s_bias[base]);
+      const float4 sg = *(const float4*)(&s_sign[base]);
+      const int4 ps = *(const int4*)(&s_pos[base]);
+      const int4 js = *(const int4*)(&s_js[base]);
+      const float bv[4] = {bi.x, bi.y, bi.z, bi.w}, sv[4] = {sg.x, sg.y, sg.z, sg.w};
+      const int pv[4] = {ps.x, ps.y, ps.z, ps.w}, jv[4] = {js.x, js.y, js.z, js.w};
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int vv = 4 * j + i;
+        float c = 0.f;
+        if (tok <= pv[i] && tok != jv[i]) {
+          const float p = __builtin_amdgcn_exp2f(fmaf(X[vv], A.c2, -bv[i]));
+          const float r = p * __builtin_amdgcn_rcpf(1.0f - p);
+          c = r * r * fmaxf(fmaf(-2.0f, C[vv], nvj), 0.0f);
+        }
+        acc += (double)(sv[i] * c);
+      }
+    }
+  };
+
+  bf16x8 qa1[8], aa1[8];
+  if (ONEBLOCK) load_rows(0, qa1, aa1);
+  for (int sub = wave; sub < kTokPerWg / 32; sub += 4) {
+    const int64_t tb = t0 + (int64_t)sub * 32;
+    if (tb >= A.n) break;
+    int64_t tok = tb + l32;
+    const int64_t tr = tok < A.n ? tok : A.n - 1;
+    bf16x8 kb[8], vb[8];
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks) {
+      kb[ks] = *(const bf16x8*)(kh + tr * HD + opdim(lane, ks));
+      vb[ks] = *(const bf16x8*)(vh + tr * HD + opdim(lane, ks));
+    }
+    // ||v_j||^2: exact bf16 squares, fp32 sums over this lane's 64 dims, then the pair
+    float n0 = 0.f, n1 = 0.f;
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks) {
+      const bf16x2 p0 = {vb[ks][0], vb[ks][1]}, p1 = {vb[ks][2], vb[ks][3]};
+      const bf16x2 p2 = {vb[ks][4], vb[ks][5]}, p3 = {vb[ks][6], vb[ks][7]};
+      n0 = __builtin_amdgcn_fdot2_f32_bf16(p0, p0, n0, false);
+      n1 = __builtin_amdgcn_fdot2_f32_bf16(p1, p1, n1, false);
+      n0 = __builtin_amdgcn_fdot2_f32_bf16(p2, p2, n0, false);
+      n1 = __builtin_amdgcn_fdot2_f32_bf16(p3, p3, n1, false);
+    }
+    float nvj = n0 + n1;
+    {
+      auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(nvj), __float_as_uint(nvj), false, false);
+      nvj = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
+    }
+    double acc = 0.0;
+    if (ONEBLOCK) {
+      block_terms(0, qa1, aa1, kb, vb, nvj, (int)tok, acc);
+    } else {
+      for (int b = 0; b < nb; ++b) {
+        bf16x8 qa[8], aa[8];
+        load_rows(b, qa, aa);
+        block_terms(b, qa, aa, kb, vb, nvj, (int)tok, acc);
+      }
+    }
+    // lanes l and l + 32 hold the same token's two halves of the rows: every
+    // lane forms (lower half) + (upper half) in that order
+    const uint64_t bits = (uint64_t)__double_as_longlong(acc);
+    const auto lo = __builtin_amdgcn_permlane32_swap((uint32_t)bits, (uint32_t)bits, false, false);
+    const auto hi = __builtin_amdgcn_permlane32_swap((uint32_t)(bits >> 32), (uint32_t)(bits >> 32), false, false);
+    const double d0 = __longlong_as_double((long long)(((uint64_t)hi[0] << 32) | lo[0]));
+    const double d1 = __longlong_as_double((long long)(((uint64_t)hi[1] << 32) | lo[1]));
+    const double total = d0 + d1;
+    if (h == 0 && tok < A.n) S[tok] += total * invG;
+  }
+}
+
+__global__ void k_dec_zero(double* p, int64_t count) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < count) p[i] = 0.0;
+}
+
+__global__ void k_dec_tof32(const double* S64, float* out, int64_t n, int64_t n_max, int Hkv) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= (int64_t)Hkv * n) return;
+  const int64_t g = i / n, j = i % n;
+  out[i] = (float)S64[g * n_max + j];
+}
+
+}  // namespace
+
+// ---------------------------------------------------------------------------- launchers
+
+DecState carve_decode_state(void* base, int64_t n_max, int32_t w, int32_t Hq, int32_t Hkv) {
+  DecState S{};
+  size_t off = 0;
+  char* b = (char*)base;
+  auto take = [&](size_t bytes) -> void* {
+    void* p = b ? (void*)(b + off) : nullptr;
+    off = (off + bytes + 255) / 256 * 256;
+    return p;
+  };
+  const int G = Hq / Hkv;
+  const size_t rows = (size_t)Hkv * (w + 1) * G;
+  S.S64 = (double*)take(sizeof(double) * (size_t)Hkv * n_max);
+  S.T.q = (uint16_t*)take(2 * rows * HD);
+  S.T.a = (float*)take(4 * rows * HD);
+  S.T.a_bf = (uint16_t*)take(2 * rows * HD);
+  S.T.m = (float*)take(4 * rows);
+  S.T.L = (float*)take(4 * rows);
+  S.T.R = (float*)take(4 * rows);
+  S.T.cstar = (float*)take(4 * rows);
+  S.T.bias = (float*)take(4 * rows);
+  S.T.cinit = (float*)take(4 * rows);
+  S.T.jstar = (int32_t*)take(4 * rows);
+  S.nch = (int)((n_max + kStatsTok - 1) / kStatsTok);
+  S.part = (float*)take(sizeof(float) * (size_t)S.nch * Hkv * G * kDecPart);
+  // MFMA row statistics of the first window, sized for n_max (its buffers do
+  // not grow with a shorter cache); its S and select scratch serve the select
+  const Shape sh{n_max, w, Hq, Hkv, HD};
+  S.ws_base = take(carve_workspace(nullptr, sh, true).bytes);
+  S.bytes = off;
+  return S;
+}
+
+hipError_t launch_decode_contrib(const void* k, const void* v, int64_t n, int64_t n_max, int32_t w, int G,
+                                 int32_t Hkv, const DecState& S, int mode, hipStream_t st) {
+  const float c2 = kLog2e / sqrtf((float)HD);
+  const int nent = mode == 0 ? w : 2;
+  const int per = kContribRows / G;  // window entries per launch
+  const dim3 grid((unsigned)((n + kTokPerWg - 1) / kTokPerWg), Hkv);
+  for (int e0 = 0; e0 < nent; e0 += per) {
+    const int e1 = e0 + per < nent ? e0 + per : nent;
+    ContribArgs a{(const uint16_t*)k, (const uint16_t*)v, S.T, S.S64, n, n_max, w, G, mode, e0, e1, c2};
+    if ((e1 - e0) * G <= 32)
+      k_dec_contrib<true><<<grid, 256, 0, st>>>(a);
+    else
+      k_dec_contrib<false><<<grid, 256, 0, st>>>(a);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_decode_init(const void* q, const void* k, const void* v, int64_t n, int64_t n_max, int32_t w,
+                              int32_t Hq, int32_t Hkv, const DecState& S, int32_t* status, hipStream_t st) {
+  const Shape sh{n, w, Hq, Hkv, HD};
+  Workspace ws = carve_workspace(S.ws_base, sh, true);
+  ws.status = status;
+  FoldInfo fold{};
+  hipError_t e = launch_mfma_rowstats(q, k, v, sh, n_max, ws, st, &fold);
+  if (e != hipSuccess) return e;
+  const int64_t rows = (int64_t)Hq * w;
+  LoadArgs la{(const uint16_t*)q, ws.rs, S.T, S.S64, n, n_max, w, Hq, Hkv};
+  k_dec_load<<<(unsigned)((rows + 3) / 4), 256, 0, st>>>(la);
+  StarInitArgs sa{fold, S.T, S.S64, n, n_max, w, status};
+  k_dec_star_init<<<Hkv, HD, 0, st>>>(sa);
+  return launch_decode_contrib(k, v, n, n_max, w, Hq / Hkv, Hkv, S, 0, st);
+}
+
+hipError_t launch_decode_step(const void* q_new, const void* k, const void* v, int64_t n, int64_t n_max,
+                              int32_t w, int32_t Hq, int32_t Hkv, const DecState& S, int32_t* status,
+                              hipStream_t st) {
+  const int G = Hq / Hkv;
+  const float c2 = kLog2e / sqrtf((float)HD);
+  const int nch = (int)((n + kStatsTok - 1) / kStatsTok);
+  for (int r0 = 0; r0 < G; r0 += kRowBatch) {
+    const int nr = G - r0 < kRowBatch ? G - r0 : kRowBatch;
+    StatsArgs a{(const uint16_t*)q_new, (const uint16_t*)k, (const uint16_t*)v, S.part, n, n_max, G, Hkv, nch,
+                r0, nr, c2};
+    k_dec_stats<<<dim3(nch, Hkv), 256, 0, st>>>(a);
+  }
+  DMergeArgs ma{S.part, (const uint16_t*)q_new, S.T, n, G, Hkv, w, nch, status};
+  k_dec_merge<<<(unsigned)((Hkv * G + 3) / 4), 256, 0, st>>>(ma);
+  hipError_t e = launch_decode_contrib(k, v, n, n_max, w, G, Hkv, S, 1, st);
+  if (e != hipSuccess) return e;
+  StarStepArgs sa{(const uint16_t*)v, S.T, S.S64, n, n_max, w, G, 1, status};
+  k_dec_star<<<Hkv, HD, 0, st>>>(sa);
+  return hipGetLastError();
+}
+
+hipError_t launch_decode_rebuild(const void* k, const void* v, int64_t n, int64_t n_max, int32_t w, int32_t Hq,
+                                 int32_t Hkv, const DecState& S, int32_t* status, hipStream_t st) {
+  const int G = Hq / Hkv;
+  const int64_t cnt = (int64_t)Hkv * n_max;
+  k_dec_zero<<<(unsigned)((cnt + 255) / 256), 256, 0, st>>>(S.S64, cnt);
+  StarStepArgs sa{(const uint16_t*)v, S.T, S.S64, n, n_max, w, G, 0, status};
+  k_dec_star<<<Hkv, HD, 0, st>>>(sa);
+  return launch_decode_contrib(k, v, n, n_max, w, G, Hkv, S, 0, st);
+}
+
+hipError_t launch_decode_scores(const DecState& S, int64_t n, int64_t n_max, int32_t Hkv, float* out,
+                                hipStream_t st) {
+  const int64_t tot = (int64_t)Hkv * n;
+  k_dec_tof32<<<(unsigned)((tot + 255) / 256), 256, 0, st>>>(S.S64, out, n, n_max, Hkv);
+  return hipGetLastError();
+}
+
+hipError_t launch_decode_select(const DecState& S, int64_t n, int64_t n_max, int32_t w, int32_t Hq, int32_t Hkv,
+                                int32_t pool_kernel, int64_t n_evict, float* out_scores, int64_t* out_idx,
+                                int32_t* status, hipStream_t st) {
+  const Shape sh{n_max, w, Hq, Hkv, HD};
+  Workspace ws = carve_workspace(S.ws_base, sh, true);  // S [Hkv][n] and select scratch for n <= n_max
+  hipError_t e = launch_decode_scores(S, n, n_max, Hkv, ws.S, st);
+  if (e == hipSuccess) e = launch_init(ws.status, nullptr, ws.sel, Hkv, st);
+  if (e == hipSuccess)
+    e = launch_select(ws.S, n, w, Hkv, pool_kernel, n_evict, out_scores, out_idx, status, nullptr, ws.sel, st);
+  return e;
+}
+
+}  // namespace dropkv

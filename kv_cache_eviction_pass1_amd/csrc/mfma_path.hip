@@ -186,6 +186,7 @@ struct P1Args {
   const uint16_t* k;
   const uint16_t* v;
   int64_t n;
+  int64_t ld;  // token rows per KV head in k and v (>= n)
   int w, Rg, nw, tiles_per_chunk, Hkv;
   float c2;          // log2(e) / sqrt(d)
   float* part;       // [chunk][Hkv*Rg][PSTRIDE]
@@ -411,8 +412,8 @@ __global__ __launch_bounds__(NW * 64) void k_pass1(P1Args A) {
   if (t1 > A.n) t1 = A.n;
   const int ntiles = (int)((t1 - t0 + TT - 1) / TT);
   const int nclean = clean_tiles(A.n, A.w, t0, ntiles);
-  const uint16_t* kh = A.k + (size_t)g * A.n * HD;
-  const uint16_t* vh = A.v + (size_t)g * A.n * HD;
+  const uint16_t* kh = A.k + (size_t)g * A.ld * HD;
+  const uint16_t* vh = A.v + (size_t)g * A.ld * HD;
   float* nvh = A.nv + (size_t)g * A.n;
   const int64_t pos = A.n - A.w + ((row_ok ? row : 0) % A.w);
   const float c2 = A.c2;
@@ -509,6 +510,7 @@ struct MergeArgs {
   const uint16_t* k;
   const float* part;
   int64_t n;
+  int64_t ld;  // token rows per KV head in k (>= n)
   int w, Rg, Hkv, nchunks;
   float c2, inv_sqrt_d;
   RowStats rs;
@@ -596,7 +598,7 @@ __global__ __launch_bounds__(256) void k_merge(MergeArgs M) {
     float x = -INFINITY;
     if (lane < 32 && tok <= pos && tok >= 0) {
       const uint16_t* qr = M.q + (size_t)row * HD;
-      const uint16_t* kr = M.k + ((size_t)g * M.n + tok) * HD;
+      const uint16_t* kr = M.k + ((size_t)g * M.ld + tok) * HD;
       float acc = 0.f;
       for (int c = 0; c < HD; ++c) acc = fmaf(bf16_to_f32(qr[c]), bf16_to_f32(kr[c]), acc);
       x = acc;
@@ -631,6 +633,7 @@ struct FixArgs {
   const uint16_t* k;
   const uint16_t* v;
   int64_t n;
+  int64_t ld;  // token rows per KV head in k and v (>= n)
   int w, Rg, Hkv;
   float c2;
   RowStats rs;
@@ -661,7 +664,7 @@ __device__ __forceinline__ void fixup_chunk(const FixArgs& F, int c, int g) {
     __syncthreads();
     if (tid < HD) {
       qs[tid] = bf16_to_f32(F.q[row * HD + tid]);
-      vstar[tid] = bf16_to_f32(F.v[((size_t)g * F.n + js) * HD + tid]);
+      vstar[tid] = bf16_to_f32(F.v[((size_t)g * F.ld + js) * HD + tid]);
     }
     __syncthreads();
     float sp = 0.f, ps = 0.f, Dacc = 0.f;
@@ -670,7 +673,7 @@ __device__ __forceinline__ void fixup_chunk(const FixArgs& F, int c, int g) {
       const int64_t j = b + tid;
       float p = 0.f;
       if (j < hi) {
-        const uint16_t* kr = F.k + ((size_t)g * F.n + j) * HD;
+        const uint16_t* kr = F.k + ((size_t)g * F.ld + j) * HD;
         float acc = 0.f;
         for (int cc = 0; cc < HD; ++cc) acc = fmaf(qs[cc], bf16_to_f32(kr[cc]), acc);
         p = __builtin_amdgcn_exp2f(fmaf(acc, F.c2, -bias));
@@ -681,7 +684,7 @@ __device__ __forceinline__ void fixup_chunk(const FixArgs& F, int c, int g) {
       __syncthreads();
       const int cnt = (int)((hi - b) < T ? (hi - b) : T);
       for (int t = sub; t < cnt; t += T / HD) {
-        const float vv = bf16_to_f32(F.v[((size_t)g * F.n + b + t) * HD + dim]);
+        const float vv = bf16_to_f32(F.v[((size_t)g * F.ld + b + t) * HD + dim]);
         Dacc = fmaf(ptile[t], vv - vstar[dim], Dacc);
       }
       __syncthreads();
@@ -1242,7 +1245,7 @@ hipError_t launch_mfma_path(const void* q, const void* k, const void* v, const S
   float* Spart = p.nrg2 > 1 ? (float*)take(sizeof(float) * (size_t)p.nrg2 * s.Hkv * s.n) : ws.S;
   const float c2 = kLog2e / sqrtf((float)HD);
 
-  P1Args a1{(const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v, s.n, s.w, p.Rg, p.nw,
+  P1Args a1{(const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v, s.n, s.n, s.w, p.Rg, p.nw,
             p.tpc1, s.Hkv, c2, ws.part, nv, ws.status, flagcount, (uint32_t*)ws.sel,
             (int64_t)select_zero_words(s.Hkv)};
   record_stage(se, "start", st);
@@ -1256,12 +1259,12 @@ hipError_t launch_mfma_path(const void* q, const void* k, const void* v, const S
     }
   }
   record_stage(se, "pass1", st);
-  MergeArgs am{(const uint16_t*)q, (const uint16_t*)k, ws.part, s.n, s.w, p.Rg, s.Hkv, p.nch1,
+  MergeArgs am{(const uint16_t*)q, (const uint16_t*)k, ws.part, s.n, s.n, s.w, p.Rg, s.Hkv, p.nch1,
                c2, 1.0f / sqrtf((float)HD), ws.rs, flagcount, ws.status};
   const int64_t rows = (int64_t)s.Hkv * p.Rg;
   k_merge<<<(unsigned)((rows + 3) / 4), 256, 0, st>>>(am);
   record_stage(se, "merge", st);
-  FixArgs af{(const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v, s.n, s.w, p.Rg, s.Hkv, c2,
+  FixArgs af{(const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v, s.n, s.n, s.w, p.Rg, s.Hkv, c2,
              ws.rs, flagcount, fx};
   if (p.nw2 < 2) {  // wider workgroups run the fix-up inside pass 2
     k_fixup<<<dim3(FXC, s.Hkv), 256, 0, st>>>(af);
@@ -1293,6 +1296,35 @@ hipError_t launch_mfma_path(const void* q, const void* k, const void* v, const S
   return hipGetLastError();
 }
 
+hipError_t launch_mfma_rowstats(const void* q, const void* k, const void* v, const Shape& s, int64_t ld,
+                                const Workspace& ws, hipStream_t st, FoldInfo* fold) {
+  const Plan p = make_plan(s);
+  char* extra = (char*)ws.extra;
+  auto take = [&](size_t bytes) { char* r = extra; extra += (bytes + 255) / 256 * 256; return r; };
+  float* nv = (float*)take(sizeof(float) * (size_t)s.Hkv * s.n);
+  float* fx = (float*)take(sizeof(float) * (size_t)FXC * s.Hkv * p.Rg * FXSTRIDE);
+  const float c2 = kLog2e / sqrtf((float)HD);
+  P1Args a1{(const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v, s.n, ld, s.w, p.Rg, p.nw,
+            p.tpc1, s.Hkv, c2, ws.part, nv, ws.status, ws.flagcount, (uint32_t*)ws.sel,
+            (int64_t)select_zero_words(s.Hkv)};
+  const dim3 grid1(p.nch1, p.nrg, s.Hkv);
+  switch (p.nw) {
+    case 8: k_pass1<8><<<grid1, 512, 0, st>>>(a1); break;
+    case 4: k_pass1<4><<<grid1, 256, 0, st>>>(a1); break;
+    case 2: k_pass1<2><<<grid1, 128, 0, st>>>(a1); break;
+    default: k_pass1<1><<<grid1, 64, 0, st>>>(a1); break;
+  }
+  MergeArgs am{(const uint16_t*)q, (const uint16_t*)k, ws.part, s.n, ld, s.w, p.Rg, s.Hkv, p.nch1,
+               c2, 1.0f / sqrtf((float)HD), ws.rs, ws.flagcount, ws.status};
+  const int64_t rows = (int64_t)s.Hkv * p.Rg;
+  k_merge<<<(unsigned)((rows + 3) / 4), 256, 0, st>>>(am);
+  FixArgs af{(const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v, s.n, ld, s.w, p.Rg, s.Hkv, c2,
+             ws.rs, ws.flagcount, fx};
+  k_fixup<<<dim3(FXC, s.Hkv), 256, 0, st>>>(af);
+  *fold = FoldInfo{ws.flagcount, ws.rs, fx, s.Hkv, p.Rg, FXC, FXSTRIDE, HD, 1.0f / (float)s.G()};
+  return hipGetLastError();
+}
+
 hipError_t launch_mfma_from_stats(const void* q, const void* k, const void* v, const Shape& s,
                                   const Workspace& ws, hipStream_t st, const float* m,
                                   const float* rest, const int32_t* argmax, const float* a,
@@ -1310,7 +1342,7 @@ hipError_t launch_mfma_from_stats(const void* q, const void* k, const void* v, c
   const int64_t rows = (int64_t)s.Hkv * p.Rg;
   ImportArgs ai{m, rest, argmax, a, s.n, rows, p.Rg, ws.rs, flagcount, ws.status};
   k_import<<<(unsigned)((rows + 3) / 4), 256, 0, st>>>(ai);
-  FixArgs af{(const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v, s.n, s.w, p.Rg, s.Hkv, c2,
+  FixArgs af{(const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v, s.n, s.n, s.w, p.Rg, s.Hkv, c2,
              ws.rs, flagcount, fx};
   if (p.nw2 < 2) k_fixup<<<dim3(FXC, s.Hkv), 256, 0, st>>>(af);
   P2Args a2{(const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v, s.n, s.w, p.Rg, p.nw2,

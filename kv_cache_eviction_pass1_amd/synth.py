@@ -194,6 +194,35 @@ def make_gaussian_case(Hq: int, Hkv: int, d: int, n: int, window: int, *,
                 dtype=dtype, needle_pos=needle_pos)
 
 
+def make_decode_case(Hq: int, Hkv: int, d: int, n_total: int, *, seeds=(42, 43, 44),
+                     sink: bool = True, needles: int = 0, sink_scale: float = 3.0,
+                     needle_scale: float = 2.5):
+    """A cache grown token by token: query rows of every position and the keys
+    and values, bf16 bit patterns, q_all [Hq][n_total][d], k, v [Hkv][n_total][d].
+
+    N(0,1) draws (Q, K, V from one PCG64 stream each); per KV head the sink
+    (key 0) and `needles` keys at positions drawn from [1, n_total // 2) on the
+    K stream point along the normalised mean of the group's queries, as in
+    make_gaussian_case. Rounded to bf16 once, last.
+    """
+    if Hq % Hkv:
+        raise ValueError("Hq must be a multiple of Hkv")
+    rq, rk, rv = (np.random.default_rng(s) for s in seeds)
+    q = _normal(rq, (Hq, n_total, d))
+    k = _normal(rk, (Hkv, n_total, d))
+    v = _normal(rv, (Hkv, n_total, d))
+    G = Hq // Hkv
+    for g in range(Hkv):
+        mu = q[g * G:(g + 1) * G].reshape(-1, d).astype(np.float64).mean(axis=0)
+        u = (mu / np.linalg.norm(mu)).astype(np.float32)
+        if sink:
+            k[g, 0] = np.float32(sink_scale * math.sqrt(d)) * u
+        if needles:
+            pos = rk.choice(n_total // 2 - 1, size=needles, replace=False) + 1
+            k[g, pos] = np.float32(needle_scale * math.sqrt(d)) * u
+    return bf16_round_bits(q), bf16_round_bits(k), bf16_round_bits(v)
+
+
 def make_case(cfg: Config, *, layer: int = 0, b: int = 0, dtype: Optional[str] = None,
               one_stream_seed: Optional[int] = None, n: Optional[int] = None) -> Case:
     """Inputs of one sequence of a named workload (optionally another n/dtype)."""

@@ -1,0 +1,148 @@
+"""Decode-time rescoring on the GPU (dropkv_decode_*) against the oracle.
+
+The cache grows token by token from a scored prefix; after the first scoring
+and after every checked step, the kept raw score must match the oracle's
+score of the grown cache computed from scratch (relative 2e-2, bf16 inputs),
+including after more steps than the window holds (every prefix row has left).
+The fp64 score kept incrementally must equal a rebuild from the stored window
+rows to fp64 rounding (the subtracted terms are bit for bit the added ones),
+re-eviction must equal the select stage on the same raw score and the oracle's
+eviction where the gap rule allows, and invalid calls / singular rows are
+reported.
+"""
+
+import numpy as np
+import pytest
+
+import oracle
+import kv_cache_eviction_pass1_amd as K
+from kv_cache_eviction_pass1_amd import synth
+from parity import RTOL, check_evictions, max_rel_err
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.fail("GPU tests need a GPU")
+    K.load_library()
+    yield
+
+
+def _dev(bits):
+    return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16).copy()).view(torch.bfloat16).cuda()
+
+
+def _setup(Hq, Hkv, n0, w, steps, n_max, needles=4, seeds=(42, 43, 44)):
+    d = 128
+    q_all, k, v = synth.make_decode_case(Hq, Hkv, d, n0 + steps, seeds=seeds, needles=needles)
+    kc = torch.zeros((Hkv, n_max, d), dtype=torch.bfloat16, device="cuda")
+    vc = torch.zeros_like(kc)
+    kc[:, : n0 + steps] = _dev(k)
+    vc[:, : n0 + steps] = _dev(v)
+    sc = K.DecodeScorer(n_max=n_max, window=w, Hq=Hq, Hkv=Hkv, d=d)
+    sc.init(_dev(q_all[:, n0 - w:n0]).contiguous(), kc, vc, n0)
+    return sc, q_all, k, v, kc, vc
+
+
+def _ref(q_all, k, v, n, w, Hq, Hkv):
+    return oracle.decode_scratch(q_all[:, n - w:n], k, v, n=n, window=w, Hq=Hq, Hkv=Hkv, d=128, dtype="bf16")
+
+
+@pytest.mark.parametrize("Hq,Hkv,n0,w,steps,n_max,check_every", [
+    (8, 2, 200, 16, 21, 256, 7),     # G = 4: more steps than the window holds
+    (28, 4, 300, 8, 10, 320, 5),     # G = 7 (Qwen-like group)
+    (4, 4, 97, 1, 4, 101, 2),        # G = 1, window of one row, ragged n
+    (16, 2, 1030, 40, 3, 1100, 3),   # G = 8, n across the 1024-token workgroup edge
+])
+def test_decode_matches_oracle(Hq, Hkv, n0, w, steps, n_max, check_every):
+    sc, q_all, k, v, kc, vc = _setup(Hq, Hkv, n0, w, steps, n_max)
+    S0 = sc.raw_scores().cpu().numpy()
+    sc.check()
+    err = max_rel_err(S0, _ref(q_all, k, v, n0, w, Hq, Hkv))
+    assert err <= RTOL["bf16"], f"after init: {err}"
+    for s in range(steps):
+        sc.step(_dev(q_all[:, n0 + s]).contiguous(), kc, vc)
+        if (s + 1) % check_every == 0 or s + 1 == steps:
+            n = n0 + s + 1
+            S = sc.raw_scores().cpu().numpy()
+            sc.check()
+            err = max_rel_err(S, _ref(q_all, k, v, n, w, Hq, Hkv))
+            assert err <= RTOL["bf16"], f"after {s + 1} steps: {err}"
+    S64 = sc.raw_scores_f64().cpu().numpy()
+    S32 = sc.raw_scores().cpu().numpy()
+    np.testing.assert_array_equal(S32, S64.astype(np.float32))
+
+
+@pytest.mark.parametrize("Hq,Hkv,n0,w,steps", [(8, 2, 300, 12, 30), (28, 4, 200, 6, 9)])
+def test_incremental_equals_rebuild(Hq, Hkv, n0, w, steps):
+    sc, q_all, k, v, kc, vc = _setup(Hq, Hkv, n0, w, steps, n0 + steps + 5, needles=8)
+    for s in range(steps):
+        sc.step(_dev(q_all[:, n0 + s]).contiguous(), kc, vc)
+    inc = sc.raw_scores_f64().cpu().numpy().copy()
+    sc.rebuild(kc, vc)
+    reb = sc.raw_scores_f64().cpu().numpy()
+    sc.check()
+    scale = np.abs(reb).max()
+    assert scale > 0
+    # terms of departed rows cancel exactly; what remains is fp64 summation order
+    assert np.abs(inc - reb).max() <= 1e-12 * scale
+    big = np.abs(reb) > 1e-6 * scale
+    rel = np.abs(inc[big] - reb[big]) / np.abs(reb[big])
+    assert rel.max() <= 1e-9, rel.max()
+
+
+def test_reevict_matches_select_and_oracle():
+    Hq, Hkv, n0, w, steps = 8, 2, 400, 16, 20
+    sc, q_all, k, v, kc, vc = _setup(Hq, Hkv, n0, w, steps, 512, needles=6)
+    for s in range(steps):
+        sc.step(_dev(q_all[:, n0 + s]).contiguous(), kc, vc)
+    n = n0 + steps
+    ne = n - w - 37
+    scores, idx = sc.select(pool_kernel=7, n_evict=ne)
+    sc.check()
+    raw = sc.raw_scores()
+    s2, i2 = K.select(raw, window=w, pool_kernel=7, n_evict=ne)
+    np.testing.assert_array_equal(scores.cpu().numpy(), s2.cpu().numpy())
+    np.testing.assert_array_equal(idx.cpu().numpy(), i2.cpu().numpy())
+    ref = oracle.dropkv_oracle(q_all[:, n - w:n], k[:, :n], v[:, :n], n=n, window=w, Hq=Hq, Hkv=Hkv, d=128,
+                               pool_kernel=7, n_evict=ne, dtype="bf16")
+    assert max_rel_err(scores.cpu().numpy(), ref["P"]) <= RTOL["bf16"]
+    exact, jac = check_evictions(scores.cpu().numpy(), idx.cpu().numpy(), ref["P"], ref["S"], ref["evict"], ne,
+                                 RTOL["bf16"])
+    print(f"exact heads {exact}/{Hkv}, jaccard {jac}")
+
+
+def test_decode_rejects_invalid_calls():
+    Hq, Hkv, w = 8, 2, 4
+    with pytest.raises(K.DropKVInvalidError):
+        K.DecodeScorer(n_max=64, window=w, Hq=Hq, Hkv=Hkv, d=64)
+    sc, q_all, k, v, kc, vc = _setup(Hq, Hkv, 40, w, 1, 41)
+    sc.step(_dev(q_all[:, 40]).contiguous(), kc, vc)  # fills the cache: n == n_max
+    with pytest.raises(K.DropKVInvalidError):
+        sc.step(_dev(q_all[:, 40]).contiguous(), kc, vc)  # n would exceed n_max
+    lib = K.load_library()
+    # init needs window < n; a step needs n >= window + 2; a small state is rejected
+    q = _dev(q_all[:, 36:40]).contiguous()
+    assert lib.dropkv_decode_init(q.data_ptr(), kc.data_ptr(), vc.data_ptr(), w, 41, w, Hq, Hkv, 128,
+                                  sc.state.data_ptr(), sc.state.numel(), sc.status.data_ptr(), None) == K.binding.ERR_INVALID
+    assert lib.dropkv_decode_step(q.data_ptr(), kc.data_ptr(), vc.data_ptr(), w + 1, 41, w, Hq, Hkv, 128,
+                                  sc.state.data_ptr(), sc.state.numel(), sc.status.data_ptr(), None) == K.binding.ERR_INVALID
+    assert lib.dropkv_decode_init(q.data_ptr(), kc.data_ptr(), vc.data_ptr(), 40, 41, w, Hq, Hkv, 128,
+                                  sc.state.data_ptr(), 1024, sc.status.data_ptr(), None) == K.binding.ERR_INVALID
+
+
+def test_decode_reports_singular_new_row():
+    Hq, Hkv, n0, w = 8, 2, 64, 4
+    sc, q_all, k, v, kc, vc = _setup(Hq, Hkv, n0, w, 1, 80, needles=0)
+    sc.check()
+    qn = q_all[:, n0].copy()
+    qf = synth.bf16_bits_to_float32(qn[1]).astype(np.float64)
+    planted = (200.0 * qf / np.linalg.norm(qf)).astype(np.float32)
+    kc[0, 9] = _dev(synth.bf16_round_bits(planted))  # query head 1's logit gap is ~200: rest mass << 2^-24
+    sc.step(_dev(qn).contiguous(), kc, vc)
+    with pytest.raises(K.DropKVSingularError):
+        sc.check()
