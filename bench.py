@@ -333,6 +333,51 @@ def main():
             "score_plus_compact_ms": round(ms_per_step + c_ms, 4),
         }
 
+    # Decode-time rescoring on the same layer: the prefix scored once (init),
+    # then one step per appended token (the new position's rows added, the
+    # leaving rows subtracted), then a re-eviction on the kept score. The
+    # layer's tensors stand in for the grown cache (head stride = n); the query
+    # rows of the appended positions are the layer's window rows in turn.
+    if args.workload == "llama_128k" and K.uses_mfma(dcode, case.d) and not args.no_extras:
+        dsteps = 64
+        n0 = case.n - dsteps
+        dec = K.DecodeScorer(n_max=case.n, window=case.window, Hq=case.Hq, Hkv=case.Hkv, d=case.d, device=dev)
+        qrows = [q[:, i % case.window].contiguous() for i in range(dsteps)]
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        for _ in range(3):
+            dec.init(q, k, v, n0)
+        e0.record()
+        dec.init(q, k, v, n0)
+        e1.record()
+        torch.cuda.synchronize()
+        init_ms = e0.elapsed_time(e1)
+        for i in range(dsteps // 2):  # warm-up steps, then the state is scored again
+            dec.step(qrows[i], k, v)
+        dec.init(q, k, v, n0)
+        torch.cuda.synchronize()
+        e0.record()
+        for i in range(dsteps):
+            dec.step(qrows[i], k, v)
+        e1.record()
+        torch.cuda.synchronize()
+        step_ms = e0.elapsed_time(e1) / dsteps
+        e0.record()
+        dec.select(pool_kernel=cfg.pool_kernel, n_evict=n_evict)
+        e1.record()
+        torch.cuda.synchronize()
+        sel_ms = e0.elapsed_time(e1)
+        dec.check()
+        step_bytes = 4 * case.Hkv * case.n * case.d * 2  # K and V read by the statistics and the terms kernels
+        rec["decode"] = {
+            "workload": "same layer grown by 64 tokens from n - 64, window 64",
+            "init_ms": round(init_ms, 4), "step_ms": round(step_ms, 4), "select_ms": round(sel_ms, 4),
+            "step_alg_bytes": step_bytes,
+            "step_achieved_GBs": round(step_bytes / (step_ms * 1e-3) / 1e9, 1),
+            "step_frac": round(step_bytes / (step_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+            "full_rescore_ms": round(ms_per_step, 4),
+        }
+        del dec
+
     if not args.no_cpu_baseline:
         import oracle
         ncores = len(os.sched_getaffinity(0))

@@ -20,8 +20,9 @@
 //   k_dec_stats / k_dec_merge  new rows' attention: max logit, exact rest mass
 //       R = sum_{j != argmax} 2^{x_j - m}, argmax, a (VALU; 16 lanes per token)
 //   k_dec_contrib  signed terms r^2 ||a - v_j||^2 of a list of rows for every
-//       token (X = Q K^T and C = a V^T on MFMA, one wave per 32 tokens, K and V
-//       read straight into the MFMA operands), added into the fp64 score
+//       token (X = Q K^T and C = a V^T on 16x16x32 MFMA, 16-token subtiles per
+//       wave, K and V read straight into the MFMA operands, 64 contiguous
+//       bytes per token and load), added into the fp64 score
 //   k_dec_star     argmax terms of rows with p_max > 1/2 (kept per row, so the
 //       exact value added is the one later removed) and the commit of the new
 //       rows into the window's ring of row slots
@@ -33,19 +34,16 @@ namespace dropkv {
 namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
 constexpr int HD = 128;
 constexpr int kRowBatch = 8;       // new rows per k_dec_stats launch
 constexpr int kDecPart = HD + 4;   // floats per stats partial (A[128], m, R, j*, pad)
 constexpr int kContribRows = 1024; // rows per k_dec_contrib launch (LDS tables)
-constexpr int kTokPerWg = 1024;    // tokens per k_dec_contrib workgroup (4 waves x 8 subtiles)
+constexpr int kOpRows = 64;        // rows whose MFMA operands k_dec_contrib stages in LDS
+constexpr int kOpStride = HD + 8;  // bf16 per staged operand row (272 bytes)
+constexpr int kTokPerWg = 512;     // tokens per k_dec_contrib workgroup (4 waves x 8 subtiles of 16)
 constexpr int kStatsTok = 2048;    // tokens per k_dec_stats workgroup
-
-__device__ __forceinline__ f32x16 mfma(bf16x8 a, bf16x8 b, f32x16 c) {
-  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
-}
 
 __device__ __forceinline__ uint16_t rne_bf16(float x) {
   uint32_t b = __float_as_uint(x);
@@ -282,11 +280,13 @@ __device__ __forceinline__ void on_merge(OnState& s1, float (&A1)[8], OnState s2
 // 8(l%16) .. +7, so a wave instruction reads 4 whole token rows), rows held
 // in registers; the 16 lane groups of the workgroup are merged through lane
 // shuffles and LDS into one partial per row.
+template <int NR>
 __global__ __launch_bounds__(256) void k_dec_stats(StatsArgs A) {
   const int chunk = blockIdx.x, g = blockIdx.y;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int li = lane & 15, grp = lane >> 4;
-  const int nr = A.nr;
+  constexpr int nr = NR;  // rows of this launch (compile-time, so the row loops unroll)
+  constexpr int kStatsUnroll = NR <= 4 ? 4 : 2;  // 16-token groups per round of loads (two rounds in flight)
   const int64_t t0 = (int64_t)chunk * kStatsTok;
   int64_t t1 = t0 + kStatsTok;
   if (t1 > A.n) t1 = A.n;
@@ -307,41 +307,71 @@ __global__ __launch_bounds__(256) void k_dec_stats(StatsArgs A) {
   }
   const uint16_t* kh = A.k + (size_t)g * A.n_max * HD;
   const uint16_t* vh = A.v + (size_t)g * A.n_max * HD;
-  for (int64_t tb = t0; tb < t1; tb += 16) {
-    const int64_t tok = tb + wave * 4 + grp;
-    const bool ok = tok < t1;
-    const int64_t tr = ok ? tok : t1 - 1;
-    const uint4 ku = *(const uint4*)(kh + tr * HD + 8 * li);
-    const uint4 vu = *(const uint4*)(vh + tr * HD + 8 * li);
-    const uint32_t kw[4] = {ku.x, ku.y, ku.z, ku.w};
-    const uint32_t vw[4] = {vu.x, vu.y, vu.z, vu.w};
-    float vf[8];
+  // kStatsUnroll groups of 16 tokens per round, all their loads issued first;
+  // offsets are 32-bit within the chunk (at most kStatsTok rows of 256 bytes)
+  const char* kc = (const char*)(kh + t0 * HD);
+  const char* vc = (const char*)(vh + t0 * HD);
+  const int nt = (int)(t1 - t0);
+  const int lo = wave * 4 + grp;  // this lane group's token within each group of 16
+  auto load = [&](int tb, uint4 (&ku)[kStatsUnroll], uint4 (&vu)[kStatsUnroll]) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      vf[2 * i] = __uint_as_float(vw[i] << 16);
-      vf[2 * i + 1] = __uint_as_float(vw[i] & 0xffff0000u);
+    for (int u = 0; u < kStatsUnroll; ++u) {
+      int tr = tb + 16 * u + lo;
+      tr = tr < nt ? tr : nt - 1;
+      const uint32_t off = (uint32_t)tr * (HD * 2) + 16u * (uint32_t)li;
+      ku[u] = *(const uint4*)(kc + off);
+      vu[u] = *(const uint4*)(vc + off);
     }
+  };
+  auto process = [&](int tb, const uint4 (&ku)[kStatsUnroll], const uint4 (&vu)[kStatsUnroll]) {
 #pragma unroll
-    for (int r = 0; r < kRowBatch; ++r) {
-      if (r >= nr) break;
-      float d = 0.f;
+    for (int u = 0; u < kStatsUnroll; ++u) {
+      const int tl = tb + 16 * u + lo;
+      const bool ok = tl < nt;
+      const uint32_t kw[4] = {ku[u].x, ku[u].y, ku[u].z, ku[u].w};
+      const uint32_t vw[4] = {vu[u].x, vu[u].y, vu[u].z, vu[u].w};
+      float vf[8];
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
-        d = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, q[r][i]), __builtin_bit_cast(bf16x2, kw[i]),
-                                            d, false);
-      const float x = row16_sum(d) * A.c2;
-      if (!ok) continue;
-      const float mx = fmaxf(st[r].m, x);
-      const float so = __builtin_amdgcn_exp2f(st[r].m - mx);  // 0 while the state is empty
-      const float e = __builtin_amdgcn_exp2f(x - mx);
-      const bool gt = x > st[r].m;
-      st[r].R = gt ? (st[r].R + 1.0f) * so : st[r].R + e;
-      if (st[r].m == -INFINITY) st[r].R = 0.f;
-      st[r].j = gt ? (int)tok : st[r].j;
-      st[r].m = mx;
+      for (int i = 0; i < 4; ++i) {
+        vf[2 * i] = __uint_as_float(vw[i] << 16);
+        vf[2 * i + 1] = __uint_as_float(vw[i] & 0xffff0000u);
+      }
 #pragma unroll
-      for (int i = 0; i < 8; ++i) acc[r][i] = fmaf(acc[r][i], so, e * vf[i]);
+      for (int r = 0; r < kRowBatch; ++r) {
+        if (r >= nr) break;
+        float d = 0.f;
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          d = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, q[r][i]), __builtin_bit_cast(bf16x2, kw[i]),
+                                              d, false);
+        // branch-free update; a token past the chunk leaves the state as it is
+        const float x = ok ? row16_sum(d) * A.c2 : -INFINITY;
+        const float mx = fmaxf(st[r].m, x);
+        const float so = st[r].m == mx ? 1.0f : __builtin_amdgcn_exp2f(st[r].m - mx);  // 0 from an empty state
+        const float e = ok ? __builtin_amdgcn_exp2f(x - mx) : 0.0f;
+        const bool gt = x > st[r].m;
+        st[r].R = gt ? (st[r].R + 1.0f) * so : st[r].R + e;
+        st[r].j = gt ? (int)(t0 + tl) : st[r].j;
+        st[r].m = mx;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) acc[r][i] = fmaf(acc[r][i], so, e * vf[i]);
+      }
     }
+  };
+  // rounds of kStatsUnroll groups of 16 tokens; the next round's loads are in
+  // flight while this one is processed
+  constexpr int kRound = 16 * kStatsUnroll;
+  uint4 k0[kStatsUnroll], v0[kStatsUnroll], k1[kStatsUnroll], v1[kStatsUnroll];
+  int tb = 0;
+  if (tb < nt) load(tb, k0, v0);
+  while (tb < nt) {
+    if (tb + kRound < nt) load(tb + kRound, k1, v1);
+    process(tb, k0, v0);
+    tb += kRound;
+    if (tb >= nt) break;
+    if (tb + kRound < nt) load(tb + kRound, k0, v0);
+    process(tb, k1, v1);
+    tb += kRound;
   }
   // merge the four lane groups of the wave (lanes li, li + 16, li + 32, li + 48)
 #pragma unroll
@@ -428,23 +458,54 @@ __global__ __launch_bounds__(256) void k_dec_merge(DMergeArgs A) {
   const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
   if (row >= (int64_t)A.Hkv * A.G) return;
   const int g = (int)(row / A.G), h = (int)(row % A.G);
-  float m = -INFINITY, R = 0.f, a0 = 0.f, a1 = 0.f;
-  int j = -1;
-  for (int c = 0; c < A.nch; ++c) {
-    const float* o = A.part + (((size_t)c * A.Hkv + g) * A.G + h) * kDecPart;
-    const float m2 = o[HD], R2 = o[HD + 1];
-    const int j2 = __float_as_int(o[HD + 2]);
-    const float2 a2 = *(const float2*)(o + 2 * lane);
-    if (m2 == -INFINITY) continue;
-    if (m == -INFINITY) { m = m2; R = R2; j = j2; a0 = a2.x; a1 = a2.y; continue; }
-    const bool win1 = m > m2 || (m == m2 && j < j2);
-    const float mx = fmaxf(m, m2);
-    const float f1 = __builtin_amdgcn_exp2f(m - mx), f2 = __builtin_amdgcn_exp2f(m2 - mx);
-    R = win1 ? R + (R2 + 1.0f) * f2 : R2 + (R + 1.0f) * f1;
-    j = win1 ? j : j2;
-    m = mx;
-    a0 = a0 * f1 + a2.x * f2;
-    a1 = a1 * f1 + a2.y * f2;
+  auto part = [&](int c) { return A.part + (((size_t)c * A.Hkv + g) * A.G + h) * kDecPart; };
+  // the largest chunk maximum, and the lowest chunk attaining it (whose argmax is then the lowest)
+  float m = -INFINITY;
+  int cw = -1;
+  for (int c0 = 0; c0 < A.nch; c0 += 64) {
+    const int c = c0 + lane;
+    const float mc = c < A.nch ? part(c)[HD] : -INFINITY;
+    float wm = mc;
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) wm = fmaxf(wm, __shfl_xor(wm, o, 64));
+    if (wm > m) {
+      m = wm;
+      cw = c0 + __ffsll((long long)__builtin_amdgcn_ballot_w64(mc == wm)) - 1;
+    }
+  }
+  // R = R_winner + sum over the other chunks of (R_c + 1) 2^{m_c - m}: no term is subtracted
+  float R = 0.f;
+  for (int c0 = 0; c0 < A.nch; c0 += 64) {
+    const int c = c0 + lane;
+    float t = 0.f;
+    if (c < A.nch && m != -INFINITY) {
+      const float* o = part(c);
+      const float mc = o[HD];
+      t = c == cw ? o[HD + 1] : (mc == -INFINITY ? 0.f : (o[HD + 1] + 1.0f) * __builtin_amdgcn_exp2f(mc - m));
+    }
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) t += __shfl_xor(t, o, 64);
+    R += t;
+  }
+  const int j = cw >= 0 ? __float_as_int(part(cw)[HD + 2]) : -1;
+  // A = sum_c A_c 2^{m_c - m}, lane = 2 dims, sixteen chunks' loads in flight
+  float a0 = 0.f, a1 = 0.f;
+  for (int c0 = 0; c0 < A.nch; c0 += 16) {
+    float2 av[16];
+    float sv[16];
+#pragma unroll
+    for (int u = 0; u < 16; ++u) {
+      const int c = c0 + u < A.nch ? c0 + u : A.nch - 1;
+      const float* o = part(c);
+      av[u] = *(const float2*)(o + 2 * lane);
+      const float mc = o[HD];
+      sv[u] = (c0 + u < A.nch && mc != -INFINITY && m != -INFINITY) ? __builtin_amdgcn_exp2f(mc - m) : 0.f;
+    }
+#pragma unroll
+    for (int u = 0; u < 16; ++u) {
+      a0 = fmaf(av[u].x, sv[u], a0);
+      a1 = fmaf(av[u].y, sv[u], a1);
+    }
   }
   const float L = 1.0f + R;
   const float x0 = a0 / L, x1 = a1 / L;
@@ -497,30 +558,69 @@ __device__ __forceinline__ void entry_of(const ContribArgs& A, int e, int& slot,
   }
 }
 
-// Operand layout (32x32x16 bf16 MFMA): lane l holds row / token l%32 and, at
-// step ks, dims 64 (l/32) + 8 ks .. +7 (a fixed permutation of the 128 dims,
-// the same for every operand, so each lane's loads are 128 contiguous bytes).
-__device__ __forceinline__ int opdim(int lane, int ks) { return 64 * (lane >> 5) + 8 * ks; }
+typedef float f32x4 __attribute__((ext_vector_type(4)));
 
-// Per (chunk of kTokPerWg tokens, KV head): each wave takes 32-token subtiles;
-// per subtile and 32-row block X = Q K^T and C = a V^T - ||a||^2/2 on MFMA,
-// then per (row, token) the term r^2 ||a - v_j||^2 with r = p / (1 - p), for
-// tokens the row sees other than its kept argmax, summed with the row's sign
-// in fp64 and added to the score.
-template <bool ONEBLOCK>
+// Operand layout (16x16x32 bf16 MFMA): lane l holds row / token l%16 and, at
+// step ks, dims 32 ks + 8 (l/16) .. +7, so the four lanes of a token read 64
+// adjacent bytes of its row and one load instruction covers 16 rows x 64 B.
+// The result gives lane l token l%16 and rows 4 (l/16) + i, i = 0..3.
+__device__ __forceinline__ int opoff(int lane, int ks) { return 64 * ks + 16 * (lane >> 4); }  // bytes
+
+__device__ __forceinline__ f32x4 mfma16(bf16x8 a, bf16x8 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+// sum over the four 16-lane rows (lanes l, l^16, l^32, l^48), the same
+// order in every lane: (row0 + row1) + (row2 + row3)
+__device__ __forceinline__ float rows4_sum(float x) {
+  auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  const float y = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(y), __float_as_uint(y), false, false);
+  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+}
+__device__ __forceinline__ double rows4_sum(double x) {
+  const uint64_t u = (uint64_t)__double_as_longlong(x);
+  auto lo = __builtin_amdgcn_permlane16_swap((uint32_t)u, (uint32_t)u, false, false);
+  auto hi = __builtin_amdgcn_permlane16_swap((uint32_t)(u >> 32), (uint32_t)(u >> 32), false, false);
+  const double y = __longlong_as_double((long long)(((uint64_t)hi[0] << 32) | lo[0])) +
+                   __longlong_as_double((long long)(((uint64_t)hi[1] << 32) | lo[1]));
+  const uint64_t w = (uint64_t)__double_as_longlong(y);
+  auto lo2 = __builtin_amdgcn_permlane32_swap((uint32_t)w, (uint32_t)w, false, false);
+  auto hi2 = __builtin_amdgcn_permlane32_swap((uint32_t)(w >> 32), (uint32_t)(w >> 32), false, false);
+  return __longlong_as_double((long long)(((uint64_t)hi2[0] << 32) | lo2[0])) +
+         __longlong_as_double((long long)(((uint64_t)hi2[1] << 32) | lo2[1]));
+}
+
+// Per (chunk of kTokPerWg tokens, KV head): each wave takes 16-token
+// subtiles; per subtile and 16-row block X = Q K^T and C = a V^T - ||a||^2/2
+// on MFMA, then per (row, token) the term r^2 ||a - v_j||^2 with
+// r = p / (1 - p), for tokens the row sees other than its kept argmax,
+// summed with the row's sign in fp64 and added to the score. Every element's
+// value depends only on its row's stored state and its token, whatever else
+// shares the block, so a row's terms are the same in every launch.
+template <bool LDSOP>
 __global__ __launch_bounds__(256) void k_dec_contrib(ContribArgs A) {
   const int chunk = blockIdx.x, g = blockIdx.y;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int h = lane >> 5, l32 = lane & 31;
+  const int q4 = lane >> 4, l16 = lane & 15;
   const int nrows = (A.e1 - A.e0) * A.G;
-  const int nb = (nrows + 31) / 32;
+  const int nb = (nrows + 15) / 16;
   __shared__ __attribute__((aligned(16))) float s_bias[kContribRows];
   __shared__ __attribute__((aligned(16))) float s_cinit[kContribRows];
   __shared__ __attribute__((aligned(16))) float s_sign[kContribRows];
   __shared__ __attribute__((aligned(16))) int s_pos[kContribRows];
   __shared__ __attribute__((aligned(16))) int s_js[kContribRows];
   __shared__ int64_t s_row[kContribRows];
-  for (int rr = threadIdx.x; rr < nb * 32; rr += blockDim.x) {
+  // per-token sums of this chunk, added to the score once every subtile is done
+  // (a read-modify-write per subtile would wait for the prefetched loads too)
+  __shared__ double s_tot[kTokPerWg];
+  // LDSOP: the rows' query and a operands staged in LDS (rows padded to 272
+  // bytes, so 16 rows read at one column hit distinct banks); otherwise they
+  // are read from global memory per block and subtile (many rows: the first
+  // window). LDS reads keep the loads of the next subtiles in flight, which a
+  // global read here would wait for (vector loads complete in order).
+  __shared__ __attribute__((aligned(16))) uint16_t s_op[LDSOP ? 2 * kOpRows : 1][kOpStride];
+  for (int rr = threadIdx.x; rr < nb * 16; rr += blockDim.x) {
     if (rr < nrows) {
       int slot;
       int64_t pos;
@@ -543,44 +643,80 @@ __global__ __launch_bounds__(256) void k_dec_contrib(ContribArgs A) {
     }
   }
   __syncthreads();
-  const uint16_t* kh = A.k + (size_t)g * A.n_max * HD;
-  const uint16_t* vh = A.v + (size_t)g * A.n_max * HD;
+  if constexpr (LDSOP) {
+    for (int i = threadIdx.x; i < nb * 16 * 32; i += blockDim.x) {
+      const int rr = i >> 5, c = i & 31;  // 32 chunks of 16 bytes: q then a_bf
+      const int64_t r = s_row[rr];
+      uint4 u = make_uint4(0, 0, 0, 0);
+      if (r >= 0) u = *(const uint4*)((const char*)((c < 16 ? A.T.q : A.T.a_bf) + r * HD) + 16 * (c & 15));
+      *(uint4*)((char*)&s_op[(c < 16 ? 0 : kOpRows) + rr][0] + 16 * (c & 15)) = u;
+    }
+    __syncthreads();
+  }
+  const int64_t t0 = (int64_t)chunk * kTokPerWg;
   const double invG = 1.0 / (double)A.G;
   double* S = A.S64 + (size_t)g * A.n_max;
-  const int64_t t0 = (int64_t)chunk * kTokPerWg;
+  // 32-bit byte offsets within the workgroup's chunk (at most kTokPerWg rows)
+  const char* kc = (const char*)(A.k + ((size_t)g * A.n_max + t0) * HD);
+  const char* vc = (const char*)(A.v + ((size_t)g * A.n_max + t0) * HD);
+  const int nt = (int)((A.n - t0) < kTokPerWg ? (A.n - t0) : kTokPerWg);
+  constexpr int NSUB = kTokPerWg / 16;
 
-  auto load_rows = [&](int b, bf16x8 (&qa)[8], bf16x8 (&aa)[8]) {
-    const int64_t r = s_row[32 * b + l32];
+  auto valid = [&](int sub) { return sub < NSUB && sub * 16 < nt; };
+  auto load_kv = [&](int sub, bf16x8 (&kb)[4], bf16x8 (&vb)[4]) {
+    int tr = sub * 16 + l16;
+    tr = tr < nt ? tr : nt - 1;
 #pragma unroll
-    for (int ks = 0; ks < 8; ++ks) {
-      if (r >= 0) {
-        qa[ks] = *(const bf16x8*)(A.T.q + r * HD + opdim(lane, ks));
-        aa[ks] = *(const bf16x8*)(A.T.a_bf + r * HD + opdim(lane, ks));
-      } else {
-        qa[ks] = bf16x8{};
-        aa[ks] = bf16x8{};
-      }
+    for (int ks = 0; ks < 4; ++ks) {
+      const uint32_t off = (uint32_t)tr * (HD * 2) + (uint32_t)opoff(lane, ks);
+      kb[ks] = *(const bf16x8*)(kc + off);
+      vb[ks] = *(const bf16x8*)(vc + off);
     }
   };
-  // signed fp64 sum of the block's 16 terms of this lane's token
-  auto block_terms = [&](int b, const bf16x8 (&qa)[8], const bf16x8 (&aa)[8], const bf16x8 (&kb)[8],
-                         const bf16x8 (&vb)[8], float nvj, int tok, double& acc) {
-    f32x16 X = {}, C;
+  auto process = [&](int sub, const bf16x8 (&kb)[4], const bf16x8 (&vb)[4]) {
+    const int tok = (int)t0 + sub * 16 + l16;
+    // ||v_j||^2: exact bf16 squares, fp32 sums over this lane's 32 dims, then the token's four lanes
+    float n0 = 0.f, n1 = 0.f;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const float4 c4 = *(const float4*)(&s_cinit[32 * b + 8 * j + 4 * h]);
-      C[4 * j] = c4.x;
-      C[4 * j + 1] = c4.y;
-      C[4 * j + 2] = c4.z;
-      C[4 * j + 3] = c4.w;
+    for (int ks = 0; ks < 4; ++ks) {
+      const bf16x2 p0 = {vb[ks][0], vb[ks][1]}, p1 = {vb[ks][2], vb[ks][3]};
+      const bf16x2 p2 = {vb[ks][4], vb[ks][5]}, p3 = {vb[ks][6], vb[ks][7]};
+      n0 = __builtin_amdgcn_fdot2_f32_bf16(p0, p0, n0, false);
+      n1 = __builtin_amdgcn_fdot2_f32_bf16(p1, p1, n1, false);
+      n0 = __builtin_amdgcn_fdot2_f32_bf16(p2, p2, n0, false);
+      n1 = __builtin_amdgcn_fdot2_f32_bf16(p3, p3, n1, false);
     }
+    const float nvj = rows4_sum(n0 + n1);
+    double acc = 0.0;
+    for (int b = 0; b < nb; ++b) {
+      // the block's query and a operands
+      bf16x8 qa[4], aa[4];
+      if constexpr (LDSOP) {
 #pragma unroll
-    for (int ks = 0; ks < 8; ++ks) X = mfma(qa[ks], kb[ks], X);
+        for (int ks = 0; ks < 4; ++ks) {
+          qa[ks] = *(const bf16x8*)((const char*)&s_op[16 * b + l16][0] + opoff(lane, ks));
+          aa[ks] = *(const bf16x8*)((const char*)&s_op[kOpRows + 16 * b + l16][0] + opoff(lane, ks));
+        }
+      } else {
+        const int64_t r = s_row[16 * b + l16];
 #pragma unroll
-    for (int ks = 0; ks < 8; ++ks) C = mfma(aa[ks], vb[ks], C);
+        for (int ks = 0; ks < 4; ++ks) {
+          if (r >= 0) {
+            qa[ks] = *(const bf16x8*)((const char*)(A.T.q + r * HD) + opoff(lane, ks));
+            aa[ks] = *(const bf16x8*)((const char*)(A.T.a_bf + r * HD) + opoff(lane, ks));
+          } else {
+            qa[ks] = bf16x8{};
+            aa[ks] = bf16x8{};
+          }
+        }
+      }
+      const int base = 16 * b + 4 * q4;  // this lane's four rows
+      const float4 c4 = *(const float4*)(&s_cinit[base]);
+      f32x4 X = {}, C = {c4.x, c4.y, c4.z, c4.w};
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int base = 32 * b + 8 * j + 4 * h;
+      for (int ks = 0; ks < 4; ++ks) X = mfma16(qa[ks], kb[ks], X);
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) C = mfma16(aa[ks], vb[ks], C);
       const float4 bi = *(const float4*)(&s_bias[base]);
       const float4 sg = *(const float4*)(&s_sign[base]);
       const int4 ps = *(const int4*)(&s_pos[base]);
@@ -589,67 +725,38 @@ __global__ __launch_bounds__(256) void k_dec_contrib(ContribArgs A) {
       const int pv[4] = {ps.x, ps.y, ps.z, ps.w}, jv[4] = {js.x, js.y, js.z, js.w};
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const int vv = 4 * j + i;
-        float c = 0.f;
-        if (tok <= pv[i] && tok != jv[i]) {
-          const float p = __builtin_amdgcn_exp2f(fmaf(X[vv], A.c2, -bv[i]));
-          const float r = p * __builtin_amdgcn_rcpf(1.0f - p);
-          c = r * r * fmaxf(fmaf(-2.0f, C[vv], nvj), 0.0f);
-        }
-        acc += (double)(sv[i] * c);
+        // branch-free: tokens the row does not see, and its kept argmax, get 0
+        const float p = __builtin_amdgcn_exp2f(fmaf(X[i], A.c2, -bv[i]));
+        const float rr = p * __builtin_amdgcn_rcpf(1.0f - p);
+        const float c = rr * rr * fmaxf(fmaf(-2.0f, C[i], nvj), 0.0f);
+        acc += (double)((tok <= pv[i] && tok != jv[i]) ? sv[i] * c : 0.0f);
       }
     }
+    const double total = rows4_sum(acc);
+    if (q4 == 0) s_tot[sub * 16 + l16] = total;
   };
-
-  bf16x8 qa1[8], aa1[8];
-  if (ONEBLOCK) load_rows(0, qa1, aa1);
-  for (int sub = wave; sub < kTokPerWg / 32; sub += 4) {
-    const int64_t tb = t0 + (int64_t)sub * 32;
-    if (tb >= A.n) break;
-    int64_t tok = tb + l32;
-    const int64_t tr = tok < A.n ? tok : A.n - 1;
-    bf16x8 kb[8], vb[8];
-#pragma unroll
-    for (int ks = 0; ks < 8; ++ks) {
-      kb[ks] = *(const bf16x8*)(kh + tr * HD + opdim(lane, ks));
-      vb[ks] = *(const bf16x8*)(vh + tr * HD + opdim(lane, ks));
-    }
-    // ||v_j||^2: exact bf16 squares, fp32 sums over this lane's 64 dims, then the pair
-    float n0 = 0.f, n1 = 0.f;
-#pragma unroll
-    for (int ks = 0; ks < 8; ++ks) {
-      const bf16x2 p0 = {vb[ks][0], vb[ks][1]}, p1 = {vb[ks][2], vb[ks][3]};
-      const bf16x2 p2 = {vb[ks][4], vb[ks][5]}, p3 = {vb[ks][6], vb[ks][7]};
-      n0 = __builtin_amdgcn_fdot2_f32_bf16(p0, p0, n0, false);
-      n1 = __builtin_amdgcn_fdot2_f32_bf16(p1, p1, n1, false);
-      n0 = __builtin_amdgcn_fdot2_f32_bf16(p2, p2, n0, false);
-      n1 = __builtin_amdgcn_fdot2_f32_bf16(p3, p3, n1, false);
-    }
-    float nvj = n0 + n1;
-    {
-      auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(nvj), __float_as_uint(nvj), false, false);
-      nvj = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
-    }
-    double acc = 0.0;
-    if (ONEBLOCK) {
-      block_terms(0, qa1, aa1, kb, vb, nvj, (int)tok, acc);
-    } else {
-      for (int b = 0; b < nb; ++b) {
-        bf16x8 qa[8], aa[8];
-        load_rows(b, qa, aa);
-        block_terms(b, qa, aa, kb, vb, nvj, (int)tok, acc);
-      }
-    }
-    // lanes l and l + 32 hold the same token's two halves of the rows: every
-    // lane forms (lower half) + (upper half) in that order
-    const uint64_t bits = (uint64_t)__double_as_longlong(acc);
-    const auto lo = __builtin_amdgcn_permlane32_swap((uint32_t)bits, (uint32_t)bits, false, false);
-    const auto hi = __builtin_amdgcn_permlane32_swap((uint32_t)(bits >> 32), (uint32_t)(bits >> 32), false, false);
-    const double d0 = __longlong_as_double((long long)(((uint64_t)hi[0] << 32) | lo[0]));
-    const double d1 = __longlong_as_double((long long)(((uint64_t)hi[1] << 32) | lo[1]));
-    const double total = d0 + d1;
-    if (h == 0 && tok < A.n) S[tok] += total * invG;
+  // subtiles wave, wave + 4, ...: the next two subtiles' K and V are in
+  // flight while one is processed (three register buffers in rotation)
+  bf16x8 kb[3][4], vb[3][4];
+  int sub = wave;
+  if (valid(sub)) load_kv(sub, kb[0], vb[0]);
+  if (valid(sub + 4)) load_kv(sub + 4, kb[1], vb[1]);
+  while (true) {
+    if (!valid(sub)) break;
+    if (valid(sub + 8)) load_kv(sub + 8, kb[2], vb[2]);
+    process(sub, kb[0], vb[0]);
+    sub += 4;
+    if (!valid(sub)) break;
+    if (valid(sub + 8)) load_kv(sub + 8, kb[0], vb[0]);
+    process(sub, kb[1], vb[1]);
+    sub += 4;
+    if (!valid(sub)) break;
+    if (valid(sub + 8)) load_kv(sub + 8, kb[1], vb[1]);
+    process(sub, kb[2], vb[2]);
+    sub += 4;
   }
+  __syncthreads();
+  for (int i = threadIdx.x; i < nt; i += blockDim.x) S[t0 + i] += s_tot[i] * invG;
 }
 
 __global__ void k_dec_zero(double* p, int64_t count) {
@@ -709,7 +816,7 @@ hipError_t launch_decode_contrib(const void* k, const void* v, int64_t n, int64_
   for (int e0 = 0; e0 < nent; e0 += per) {
     const int e1 = e0 + per < nent ? e0 + per : nent;
     ContribArgs a{(const uint16_t*)k, (const uint16_t*)v, S.T, S.S64, n, n_max, w, G, mode, e0, e1, c2};
-    if ((e1 - e0) * G <= 32)
+    if ((e1 - e0) * G <= kOpRows)
       k_dec_contrib<true><<<grid, 256, 0, st>>>(a);
     else
       k_dec_contrib<false><<<grid, 256, 0, st>>>(a);
@@ -743,7 +850,17 @@ hipError_t launch_decode_step(const void* q_new, const void* k, const void* v, i
     const int nr = G - r0 < kRowBatch ? G - r0 : kRowBatch;
     StatsArgs a{(const uint16_t*)q_new, (const uint16_t*)k, (const uint16_t*)v, S.part, n, n_max, G, Hkv, nch,
                 r0, nr, c2};
-    k_dec_stats<<<dim3(nch, Hkv), 256, 0, st>>>(a);
+    const dim3 grid(nch, Hkv);
+    switch (nr) {
+      case 1: k_dec_stats<1><<<grid, 256, 0, st>>>(a); break;
+      case 2: k_dec_stats<2><<<grid, 256, 0, st>>>(a); break;
+      case 3: k_dec_stats<3><<<grid, 256, 0, st>>>(a); break;
+      case 4: k_dec_stats<4><<<grid, 256, 0, st>>>(a); break;
+      case 5: k_dec_stats<5><<<grid, 256, 0, st>>>(a); break;
+      case 6: k_dec_stats<6><<<grid, 256, 0, st>>>(a); break;
+      case 7: k_dec_stats<7><<<grid, 256, 0, st>>>(a); break;
+      default: k_dec_stats<8><<<grid, 256, 0, st>>>(a); break;
+    }
   }
   DMergeArgs ma{S.part, (const uint16_t*)q_new, S.T, n, G, Hkv, w, nch, status};
   k_dec_merge<<<(unsigned)((Hkv * G + 3) / 4), 256, 0, st>>>(ma);
