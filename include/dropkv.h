@@ -253,8 +253,9 @@ int dropkv_compact(int32_t dtype, const void* k, const void* v, int64_t n, int32
  * or pointer checks) or DROPKV_ERR_DEVICE. Device-side findings go to the
  * caller's device int32 `d_status` as DROPKV_STATUS_* bits: a window row whose
  * rest mass is <= 2^-24 (SINGULAR) or non-finite values (NONFINITE) make S
- * unspecified until the next init. Limits: window >= 1, Hq a multiple of Hkv,
- * n_max < 2^31. Calls on one state must not overlap.
+ * unspecified until the next init. Limits: window >= 1, Hq a multiple of Hkv
+ * with at most 16 query heads per KV head, n_max < 2^31. Calls on one state
+ * must not overlap.
  */
 size_t dropkv_decode_state_bytes(int64_t n_max, int32_t window, int32_t Hq, int32_t Hkv, int32_t d);
 

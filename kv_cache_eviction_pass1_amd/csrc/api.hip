@@ -179,6 +179,7 @@ int check_decode(int64_t n, int64_t need_n, int64_t n_max, int32_t window, int32
   if (d != 128) return fail(DROPKV_ERR_INVALID, "decode rescoring needs bf16 inputs with d = 128");
   if (window < 1) return fail(DROPKV_ERR_INVALID, "need window >= 1");
   if (Hq < 1 || Hkv < 1 || Hq % Hkv != 0) return fail(DROPKV_ERR_INVALID, "need Hq a positive multiple of Hkv >= 1");
+  if (Hq / Hkv > 16) return fail(DROPKV_ERR_INVALID, "decode rescoring takes at most 16 query heads per KV head");
   if (n_max > ((int64_t)1 << 31) - 1) return fail(DROPKV_ERR_INVALID, "n_max must fit in int32 token indices");
   if (n < need_n || n > n_max) return fail(DROPKV_ERR_INVALID, "token count out of range for this call (see dropkv.h)");
   if ((double)Hkv * (double)n_max * 128.0 > 1e15 || (double)Hq * window > 1e8)
@@ -589,7 +590,7 @@ int dropkv_compact(int32_t dtype, const void* k, const void* v, int64_t n, int32
 }
 
 size_t dropkv_decode_state_bytes(int64_t n_max, int32_t window, int32_t Hq, int32_t Hkv, int32_t d) {
-  if (d != 128 || window < 1 || Hq < 1 || Hkv < 1 || Hq % Hkv != 0 || n_max < 2 ||
+  if (d != 128 || window < 1 || Hq < 1 || Hkv < 1 || Hq % Hkv != 0 || Hq / Hkv > 16 || n_max < 2 ||
       n_max > ((int64_t)1 << 31) - 1)
     return 0;
   return carve_decode_state(nullptr, n_max, window, Hq, Hkv).bytes;

@@ -18,14 +18,16 @@
 //
 // Kernels (bf16, d = 128):
 //   k_dec_stats / k_dec_merge  new rows' attention: max logit, exact rest mass
-//       R = sum_{j != argmax} 2^{x_j - m}, argmax, a (VALU; 16 lanes per token)
+//       R = sum_{j != argmax} 2^{x_j - m}, argmax, a (VALU; 8 lanes per token);
+//       the merge also stores the rows and moves the argmax terms (below)
 //   k_dec_contrib  signed terms r^2 ||a - v_j||^2 of a list of rows for every
 //       token (X = Q K^T and C = a V^T on 16x16x32 MFMA, 16-token subtiles per
 //       wave, K and V read straight into the MFMA operands, 64 contiguous
 //       bytes per token and load), added into the fp64 score
-//   k_dec_star     argmax terms of rows with p_max > 1/2 (kept per row, so the
-//       exact value added is the one later removed) and the commit of the new
-//       rows into the window's ring of row slots
+//   argmax terms of rows with p_max > 1/2 are scored apart and kept per row,
+//       so the exact value added is the one later removed. The rows live in a
+//       ring of w + 1 slots per KV head (position p in slot p mod (w + 1)), so
+//       the appended position never shares a slot with the one leaving.
 // The first window comes from the MFMA pass 1 + merge + argmax fix-up.
 #include "dropkv_common.h"
 
@@ -63,10 +65,9 @@ __device__ __forceinline__ float row16_sum(float x) {
 
 // ---------------------------------------------------------------------------- row table
 
-// Row table index of query head h (of KV head g's G) in slot `slot` (slot w
-// is the staging slot of the position being appended).
-__device__ __forceinline__ int64_t trow(int g, int slot, int h, int w, int G) {
-  return ((int64_t)g * (w + 1) + slot) * G + h;
+// Row table index of query head h (of KV head g's G) at cache position pos.
+__device__ __forceinline__ int64_t trow(int g, int64_t pos, int h, int w, int G) {
+  return ((int64_t)g * (w + 1) + pos % (w + 1)) * G + h;
 }
 
 // State derived from (m, L, a) once, when a row is stored: a in bf16 for the
@@ -96,7 +97,7 @@ struct LoadArgs {
   int w, Hq, Hkv;
 };
 
-// Window rows of the first scoring into their slots (slot = position mod w),
+// Window rows of the first scoring into their slots (slot = position mod (w + 1)),
 // and the fp64 score cleared. One wave per row; the score is cleared by a
 // grid-stride loop.
 __global__ __launch_bounds__(256) void k_dec_load(LoadArgs A) {
@@ -112,7 +113,7 @@ __global__ __launch_bounds__(256) void k_dec_load(LoadArgs A) {
   const int h = (int)(row / A.w), i = (int)(row % A.w);
   const int g = h / G, hl = h % G;
   const int64_t pos = A.n - A.w + i;
-  const int64_t r = trow(g, (int)(pos % A.w), hl, A.w, G);
+  const int64_t r = trow(g, pos, hl, A.w, G);
   *(uint32_t*)(A.T.q + r * HD + 2 * lane) = *(const uint32_t*)(A.q + row * HD + 2 * lane);
   *(float2*)(A.T.a + r * HD + 2 * lane) = *(const float2*)(A.rs.a + row * HD + 2 * lane);
   const float m = A.rs.m[row], L = A.rs.L[row];
@@ -154,7 +155,7 @@ __global__ __launch_bounds__(HD) void k_dec_star_init(StarInitArgs A) {
     const int js = A.f.rs.jstar[row];
     if (threadIdx.x == 0) {
       const int hl = rr / A.w, i = rr % A.w;
-      const int64_t r = trow(g, (int)((A.n - A.w + i) % A.w), hl, A.w, G);
+      const int64_t r = trow(g, A.n - A.w + i, hl, A.w, G);
       if (js < 0 || js >= A.n) {
         atomicOr(A.status, kStatusNonFinite);
       } else if (bits) {
@@ -168,73 +169,24 @@ __global__ __launch_bounds__(HD) void k_dec_star_init(StarInitArgs A) {
   }
 }
 
-struct StarStepArgs {
-  const uint16_t* v;  // [Hkv][n_max][d]
+struct StarAllArgs {
   DecRows T;
   double* S64;
   int64_t n, n_max;
   int w, G;
-  int commit;         // 1: step (new rows in the staging slot, commit them); 0: rebuild (all slots)
-  int32_t* status;
 };
 
-// One block per KV head. Step: the new rows' argmax terms (rows with R < 1:
-// ||a - v_j*||^2 / R^2, computed directly) are added and kept, the leaving
-// rows' kept terms are subtracted, then the new rows replace the leaving ones
-// in their slot. Rebuild: every window slot's kept term is added.
-__global__ __launch_bounds__(HD) void k_dec_star(StarStepArgs A) {
-  const int g = blockIdx.x, tid = threadIdx.x;
-  __shared__ float red[HD];
-  const double invG = 1.0 / (double)A.G;
+// Rebuild: every window row's kept argmax term added, in row order. One thread per KV head.
+__global__ void k_dec_star_all(StarAllArgs A) {
+  const int g = blockIdx.x;
+  if (threadIdx.x != 0) return;
   double* S = A.S64 + (size_t)g * A.n_max;
-  if (!A.commit) {
-    for (int slot = 0; slot < A.w; ++slot)
-      for (int h = 0; h < A.G; ++h) {
-        const int64_t r = trow(g, slot, h, A.w, A.G);
-        const int js = A.T.jstar[r];
-        if (tid == 0 && js >= 0 && js < A.n) S[js] += (double)A.T.cstar[r] * invG;
-      }
-    return;
-  }
-  const int so = (int)((A.n - 1) % A.w);  // slot of the leaving rows, and of the new ones after the commit
-  for (int h = 0; h < A.G; ++h) {
-    const int64_t rn = trow(g, A.w, h, A.w, A.G);
-    const int js = A.T.jstar[rn];  // uniform
-    if (js >= 0) {
-      const float d = A.T.a[rn * HD + tid] - bf16_to_f32(A.v[((size_t)g * A.n_max + js) * HD + tid]);
-      const float dist = block_sum<HD>(d * d, red);
-      if (tid == 0) {
-        const float R = A.T.R[rn];
-        const float val = dist / (R * R);
-        A.T.cstar[rn] = val;
-        S[js] += (double)val * invG;
-      }
-    } else if (tid == 0) {
-      A.T.cstar[rn] = 0.f;
+  for (int i = 0; i < A.w; ++i)
+    for (int h = 0; h < A.G; ++h) {
+      const int64_t r = trow(g, A.n - A.w + i, h, A.w, A.G);
+      const int js = A.T.jstar[r];
+      if (js >= 0 && js < A.n) S[js] += (double)A.T.cstar[r] / (double)A.G;
     }
-    if (tid == 0) {
-      const int64_t ro = trow(g, so, h, A.w, A.G);
-      const int jo = A.T.jstar[ro];
-      if (jo >= 0 && jo < A.n) S[jo] -= (double)A.T.cstar[ro] * invG;
-    }
-  }
-  __syncthreads();
-  // commit: staging rows into the leaving rows' slot
-  for (int h = 0; h < A.G; ++h) {
-    const int64_t rn = trow(g, A.w, h, A.w, A.G), ro = trow(g, so, h, A.w, A.G);
-    A.T.q[ro * HD + tid] = A.T.q[rn * HD + tid];
-    A.T.a[ro * HD + tid] = A.T.a[rn * HD + tid];
-    A.T.a_bf[ro * HD + tid] = A.T.a_bf[rn * HD + tid];
-    if (tid == 0) {
-      A.T.m[ro] = A.T.m[rn];
-      A.T.L[ro] = A.T.L[rn];
-      A.T.R[ro] = A.T.R[rn];
-      A.T.jstar[ro] = A.T.jstar[rn];
-      A.T.cstar[ro] = A.T.cstar[rn];
-      A.T.bias[ro] = A.T.bias[rn];
-      A.T.cinit[ro] = A.T.cinit[rn];
-    }
-  }
 }
 
 // ---------------------------------------------------------------------------- new rows
@@ -257,13 +209,14 @@ struct OnState {
   int j;
 };
 
-// (m1, R1, j1, A1) merged with (m2, R2, j2, A2); A is the caller's (8 dims per lane)
-__device__ __forceinline__ void on_merge(OnState& s1, float (&A1)[8], OnState s2, const float (&A2)[8]) {
+// (m1, R1, j1, A1) merged with (m2, R2, j2, A2); A holds the lane's D dims
+template <int D>
+__device__ __forceinline__ void on_merge(OnState& s1, float (&A1)[D], OnState s2, const float (&A2)[D]) {
   if (s2.m == -INFINITY) return;
   if (s1.m == -INFINITY) {
     s1 = s2;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) A1[i] = A2[i];
+    for (int i = 0; i < D; ++i) A1[i] = A2[i];
     return;
   }
   const bool win1 = s1.m > s2.m || (s1.m == s2.m && s1.j < s2.j);
@@ -273,139 +226,167 @@ __device__ __forceinline__ void on_merge(OnState& s1, float (&A1)[8], OnState s2
   s1.j = win1 ? s1.j : s2.j;
   s1.m = mx;
 #pragma unroll
-  for (int i = 0; i < 8; ++i) A1[i] = A1[i] * f1 + A2[i] * f2;
+  for (int i = 0; i < D; ++i) A1[i] = A1[i] * f1 + A2[i] * f2;
 }
 
-// Per (token chunk, KV head): 16 lanes per token (lane l%16 holds dims
-// 8(l%16) .. +7, so a wave instruction reads 4 whole token rows), rows held
-// in registers; the 16 lane groups of the workgroup are merged through lane
-// shuffles and LDS into one partial per row.
+// sum over the 8 lanes of a DPP half-row, result in every lane of it
+__device__ __forceinline__ float row8_sum(float x) {
+  x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0xB1, 0xf, 0xf, false));   // quad_perm 1,0,3,2
+  x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x4E, 0xf, 0xf, false));   // quad_perm 2,3,0,1
+  x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x141, 0xf, 0xf, false));  // row_half_mirror
+  return x;
+}
+
+// Per (token chunk, KV head): 8 lanes per token (lane l%8 holds dims
+// 8(l%8) .. +7 and 64 + 8(l%8) .. +7, so each load instruction reads 8 token
+// rows x 128 contiguous bytes), rows held in registers. Each lane group keeps
+// its rows' state against a lazy reference mref (log2 units): estar = 2^{m -
+// mref} of the current maximum m, R' = sum over its other tokens of
+// 2^{x - mref} (a new maximum moves the old one's weight into R', so nothing
+// is ever subtracted) and acc = sum 2^{x - mref} v; the reference moves only
+// when a logit exceeds it by more than 2^8. The eight lane groups and four
+// waves are then merged into one partial per row, relative to m.
 template <int NR>
 __global__ __launch_bounds__(256) void k_dec_stats(StatsArgs A) {
   const int chunk = blockIdx.x, g = blockIdx.y;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int li = lane & 15, grp = lane >> 4;
-  constexpr int nr = NR;  // rows of this launch (compile-time, so the row loops unroll)
-  constexpr int kStatsUnroll = NR <= 4 ? 4 : 2;  // 16-token groups per round of loads (two rounds in flight)
+  const int li = lane & 7, grp = lane >> 3;
+  constexpr int U = NR <= 2 ? 4 : (NR <= 4 ? 2 : 1);  // 32-token groups per round of loads (two rounds in flight)
+  constexpr float kRef = 8.0f;
   const int64_t t0 = (int64_t)chunk * kStatsTok;
   int64_t t1 = t0 + kStatsTok;
   if (t1 > A.n) t1 = A.n;
-  uint32_t q[kRowBatch][4];
+  uint32_t q[NR][8];
 #pragma unroll
-  for (int r = 0; r < kRowBatch; ++r) {
-    const int rr = r < nr ? r : 0;
-    const uint4 u = *(const uint4*)(A.qn + ((size_t)(g * A.G + A.r0 + rr)) * HD + 8 * li);
-    q[r][0] = u.x; q[r][1] = u.y; q[r][2] = u.z; q[r][3] = u.w;
+  for (int r = 0; r < NR; ++r) {
+    const uint16_t* qr = A.qn + ((size_t)(g * A.G + A.r0 + r)) * HD;
+    const uint4 u0 = *(const uint4*)(qr + 8 * li), u1 = *(const uint4*)(qr + 64 + 8 * li);
+    q[r][0] = u0.x; q[r][1] = u0.y; q[r][2] = u0.z; q[r][3] = u0.w;
+    q[r][4] = u1.x; q[r][5] = u1.y; q[r][6] = u1.z; q[r][7] = u1.w;
   }
-  OnState st[kRowBatch];
-  float acc[kRowBatch][8];
+  float mref[NR], m[NR], estar[NR], Rp[NR], acc[NR][16];
+  int jst[NR];
 #pragma unroll
-  for (int r = 0; r < kRowBatch; ++r) {
-    st[r] = OnState{-INFINITY, 0.f, -1};
+  for (int r = 0; r < NR; ++r) {
+    mref[r] = -INFINITY; m[r] = -INFINITY; estar[r] = 0.f; Rp[r] = 0.f; jst[r] = -1;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) acc[r][i] = 0.f;
+    for (int i = 0; i < 16; ++i) acc[r][i] = 0.f;
   }
-  const uint16_t* kh = A.k + (size_t)g * A.n_max * HD;
-  const uint16_t* vh = A.v + (size_t)g * A.n_max * HD;
-  // kStatsUnroll groups of 16 tokens per round, all their loads issued first;
-  // offsets are 32-bit within the chunk (at most kStatsTok rows of 256 bytes)
-  const char* kc = (const char*)(kh + t0 * HD);
-  const char* vc = (const char*)(vh + t0 * HD);
+  const char* kc = (const char*)(A.k + ((size_t)g * A.n_max + t0) * HD);
+  const char* vc = (const char*)(A.v + ((size_t)g * A.n_max + t0) * HD);
   const int nt = (int)(t1 - t0);
-  const int lo = wave * 4 + grp;  // this lane group's token within each group of 16
-  auto load = [&](int tb, uint4 (&ku)[kStatsUnroll], uint4 (&vu)[kStatsUnroll]) {
+  const int lo = wave * 8 + grp;  // this lane group's token within each group of 32
+  auto load = [&](int tb, uint4 (&k0)[U], uint4 (&k1)[U], uint4 (&v0)[U], uint4 (&v1)[U]) {
 #pragma unroll
-    for (int u = 0; u < kStatsUnroll; ++u) {
-      int tr = tb + 16 * u + lo;
+    for (int u = 0; u < U; ++u) {
+      int tr = tb + 32 * u + lo;
       tr = tr < nt ? tr : nt - 1;
       const uint32_t off = (uint32_t)tr * (HD * 2) + 16u * (uint32_t)li;
-      ku[u] = *(const uint4*)(kc + off);
-      vu[u] = *(const uint4*)(vc + off);
+      k0[u] = *(const uint4*)(kc + off);
+      k1[u] = *(const uint4*)(kc + off + 128);
+      v0[u] = *(const uint4*)(vc + off);
+      v1[u] = *(const uint4*)(vc + off + 128);
     }
   };
-  auto process = [&](int tb, const uint4 (&ku)[kStatsUnroll], const uint4 (&vu)[kStatsUnroll]) {
+  auto process = [&](int tb, const uint4 (&k0)[U], const uint4 (&k1)[U], const uint4 (&v0)[U],
+                     const uint4 (&v1)[U]) {
 #pragma unroll
-    for (int u = 0; u < kStatsUnroll; ++u) {
-      const int tl = tb + 16 * u + lo;
+    for (int u = 0; u < U; ++u) {
+      const int tl = tb + 32 * u + lo;
       const bool ok = tl < nt;
-      const uint32_t kw[4] = {ku[u].x, ku[u].y, ku[u].z, ku[u].w};
-      const uint32_t vw[4] = {vu[u].x, vu[u].y, vu[u].z, vu[u].w};
-      float vf[8];
+      const uint32_t kw[8] = {k0[u].x, k0[u].y, k0[u].z, k0[u].w, k1[u].x, k1[u].y, k1[u].z, k1[u].w};
+      const uint32_t vw[8] = {v0[u].x, v0[u].y, v0[u].z, v0[u].w, v1[u].x, v1[u].y, v1[u].z, v1[u].w};
+      float vf[16];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
+      for (int i = 0; i < 8; ++i) {
         vf[2 * i] = __uint_as_float(vw[i] << 16);
         vf[2 * i + 1] = __uint_as_float(vw[i] & 0xffff0000u);
       }
 #pragma unroll
-      for (int r = 0; r < kRowBatch; ++r) {
-        if (r >= nr) break;
+      for (int r = 0; r < NR; ++r) {
         float d = 0.f;
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
+        for (int i = 0; i < 8; ++i)
           d = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, q[r][i]), __builtin_bit_cast(bf16x2, kw[i]),
                                               d, false);
-        // branch-free update; a token past the chunk leaves the state as it is
-        const float x = ok ? row16_sum(d) * A.c2 : -INFINITY;
-        const float mx = fmaxf(st[r].m, x);
-        const float so = st[r].m == mx ? 1.0f : __builtin_amdgcn_exp2f(st[r].m - mx);  // 0 from an empty state
-        const float e = ok ? __builtin_amdgcn_exp2f(x - mx) : 0.0f;
-        const bool gt = x > st[r].m;
-        st[r].R = gt ? (st[r].R + 1.0f) * so : st[r].R + e;
-        st[r].j = gt ? (int)(t0 + tl) : st[r].j;
-        st[r].m = mx;
+        const float x = ok ? row8_sum(d) * A.c2 : -INFINITY;
+        // move the reference when a logit passes it by more than 2^8 (rare; a wave decision)
+        if (__builtin_amdgcn_ballot_w64(x > mref[r] + kRef)) {
+          const bool mv = x > mref[r] + kRef;
+          const float nref = mv ? x : mref[r];
+          const float f = mv ? __builtin_amdgcn_exp2f(mref[r] - nref) : 1.0f;  // 0 from an empty state
+          Rp[r] *= f;
+          estar[r] *= f;
 #pragma unroll
-        for (int i = 0; i < 8; ++i) acc[r][i] = fmaf(acc[r][i], so, e * vf[i]);
+          for (int i = 0; i < 16; ++i) acc[r][i] *= f;
+          mref[r] = nref;
+        }
+        const float e = ok ? __builtin_amdgcn_exp2f(x - mref[r]) : 0.f;
+        const bool gt = x > m[r];
+        Rp[r] += gt ? estar[r] : e;
+        estar[r] = gt ? e : estar[r];
+        jst[r] = gt ? (int)(t0 + tl) : jst[r];
+        m[r] = gt ? x : m[r];
+#pragma unroll
+        for (int i = 0; i < 16; ++i) acc[r][i] = fmaf(e, vf[i], acc[r][i]);
       }
     }
   };
-  // rounds of kStatsUnroll groups of 16 tokens; the next round's loads are in
-  // flight while this one is processed
-  constexpr int kRound = 16 * kStatsUnroll;
-  uint4 k0[kStatsUnroll], v0[kStatsUnroll], k1[kStatsUnroll], v1[kStatsUnroll];
+  constexpr int kRound = 32 * U;
+  uint4 ka0[U], ka1[U], va0[U], va1[U], kb0[U], kb1[U], vb0[U], vb1[U];
   int tb = 0;
-  if (tb < nt) load(tb, k0, v0);
+  if (tb < nt) load(tb, ka0, ka1, va0, va1);
   while (tb < nt) {
-    if (tb + kRound < nt) load(tb + kRound, k1, v1);
-    process(tb, k0, v0);
+    if (tb + kRound < nt) load(tb + kRound, kb0, kb1, vb0, vb1);
+    process(tb, ka0, ka1, va0, va1);
     tb += kRound;
     if (tb >= nt) break;
-    if (tb + kRound < nt) load(tb + kRound, k0, v0);
-    process(tb, k1, v1);
+    if (tb + kRound < nt) load(tb + kRound, ka0, ka1, va0, va1);
+    process(tb, kb0, kb1, vb0, vb1);
     tb += kRound;
   }
-  // merge the four lane groups of the wave (lanes li, li + 16, li + 32, li + 48)
+  // state relative to m: R = R' / estar, A = acc / estar (estar = 2^{m - mref} >= 2^-8... > 0)
+  OnState st[NR];
 #pragma unroll
-  for (int r = 0; r < kRowBatch; ++r) {
-    if (r >= nr) break;
+  for (int r = 0; r < NR; ++r) {
+    const float inv = m[r] == -INFINITY ? 0.f : 1.0f / estar[r];
+    st[r] = OnState{m[r], Rp[r] * inv, jst[r]};
 #pragma unroll
-    for (int o = 16; o < 64; o <<= 1) {
+    for (int i = 0; i < 16; ++i) acc[r][i] *= inv;
+  }
+  // merge the eight lane groups of the wave (lanes li + 8 k), lower group first
+#pragma unroll
+  for (int r = 0; r < NR; ++r) {
+#pragma unroll
+    for (int o = 8; o < 64; o <<= 1) {
       OnState s2{__shfl_xor(st[r].m, o, 64), __shfl_xor(st[r].R, o, 64), __shfl_xor(st[r].j, o, 64)};
-      float a2[8];
+      float a2[16];
 #pragma unroll
-      for (int i = 0; i < 8; ++i) a2[i] = __shfl_xor(acc[r][i], o, 64);
-      // both lanes of a pair merge in the same order (lower lane group first), so they agree bit for bit
+      for (int i = 0; i < 16; ++i) a2[i] = __shfl_xor(acc[r][i], o, 64);
       if (lane & o) {
         OnState s1 = s2;
-        float a1[8];
+        float a1[16];
 #pragma unroll
-        for (int i = 0; i < 8; ++i) a1[i] = a2[i];
-        on_merge(s1, a1, st[r], acc[r]);
+        for (int i = 0; i < 16; ++i) a1[i] = a2[i];
+        on_merge<16>(s1, a1, st[r], acc[r]);
         st[r] = s1;
 #pragma unroll
-        for (int i = 0; i < 8; ++i) acc[r][i] = a1[i];
+        for (int i = 0; i < 16; ++i) acc[r][i] = a1[i];
       } else {
-        on_merge(st[r], acc[r], s2, a2);
+        on_merge<16>(st[r], acc[r], s2, a2);
       }
     }
   }
-  // then the four waves, in wave order
-  __shared__ float ws[4][kRowBatch][kDecPart];
+  // then the four waves, in wave order; dims of lane li: 8 li + (0..7), 64 + 8 li + (0..7)
+  __shared__ float ws[4][NR][kDecPart];
   if (grp == 0) {
 #pragma unroll
-    for (int r = 0; r < kRowBatch; ++r) {
-      if (r >= nr) break;
+    for (int r = 0; r < NR; ++r) {
 #pragma unroll
-      for (int i = 0; i < 8; ++i) ws[wave][r][8 * li + i] = acc[r][i];
+      for (int i = 0; i < 8; ++i) {
+        ws[wave][r][8 * li + i] = acc[r][i];
+        ws[wave][r][64 + 8 * li + i] = acc[r][8 + i];
+      }
       if (li == 0) {
         ws[wave][r][HD] = st[r].m;
         ws[wave][r][HD + 1] = st[r].R;
@@ -416,22 +397,30 @@ __global__ __launch_bounds__(256) void k_dec_stats(StatsArgs A) {
   __syncthreads();
   if (wave == 0 && grp == 0) {
 #pragma unroll
-    for (int r = 0; r < kRowBatch; ++r) {
-      if (r >= nr) break;
+    for (int r = 0; r < NR; ++r) {
       OnState s1{ws[0][r][HD], ws[0][r][HD + 1], __float_as_int(ws[0][r][HD + 2])};
-      float a1[8];
+      float a1[16];
 #pragma unroll
-      for (int i = 0; i < 8; ++i) a1[i] = ws[0][r][8 * li + i];
+      for (int i = 0; i < 8; ++i) {
+        a1[i] = ws[0][r][8 * li + i];
+        a1[8 + i] = ws[0][r][64 + 8 * li + i];
+      }
       for (int wv = 1; wv < 4; ++wv) {
         OnState s2{ws[wv][r][HD], ws[wv][r][HD + 1], __float_as_int(ws[wv][r][HD + 2])};
-        float a2[8];
+        float a2[16];
 #pragma unroll
-        for (int i = 0; i < 8; ++i) a2[i] = ws[wv][r][8 * li + i];
-        on_merge(s1, a1, s2, a2);
+        for (int i = 0; i < 8; ++i) {
+          a2[i] = ws[wv][r][8 * li + i];
+          a2[8 + i] = ws[wv][r][64 + 8 * li + i];
+        }
+        on_merge<16>(s1, a1, s2, a2);
       }
       float* o = A.part + (((size_t)chunk * A.Hkv + g) * A.G + A.r0 + r) * kDecPart;
 #pragma unroll
-      for (int i = 0; i < 8; ++i) o[8 * li + i] = a1[i];
+      for (int i = 0; i < 8; ++i) {
+        o[8 * li + i] = a1[i];
+        o[64 + 8 * li + i] = a1[8 + i];
+      }
       if (li == 0) {
         o[HD] = s1.m;
         o[HD + 1] = s1.R;
@@ -444,87 +433,116 @@ __global__ __launch_bounds__(256) void k_dec_stats(StatsArgs A) {
 struct DMergeArgs {
   const float* part;
   const uint16_t* qn;
+  const uint16_t* v;  // [Hkv][n_max][d]
   DecRows T;
-  int64_t n;
+  double* S64;
+  int64_t n, n_max;
   int G, Hkv, w, nch;
   int32_t* status;
 };
 
-// One wave per new row: the chunk partials merged in chunk order, the row
-// stored in the staging slot (query, a, m, L = 1 + R, R, argmax of rows with
-// R < 1, derived state). Rejects R <= 2^-24 (singular) and non-finite rows.
-__global__ __launch_bounds__(256) void k_dec_merge(DMergeArgs A) {
-  const int lane = threadIdx.x & 63;
-  const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (row >= (int64_t)A.Hkv * A.G) return;
-  const int g = (int)(row / A.G), h = (int)(row % A.G);
-  auto part = [&](int c) { return A.part + (((size_t)c * A.Hkv + g) * A.G + h) * kDecPart; };
-  // the largest chunk maximum, and the lowest chunk attaining it (whose argmax is then the lowest)
-  float m = -INFINITY;
-  int cw = -1;
-  for (int c0 = 0; c0 < A.nch; c0 += 64) {
-    const int c = c0 + lane;
-    const float mc = c < A.nch ? part(c)[HD] : -INFINITY;
-    float wm = mc;
+// One block per KV head, one wave per new row: the chunk partials merged
+// (chunks across lanes; R = R_winner + sum over the other chunks of
+// (R_c + 1) 2^{m_c - m}, so nothing is subtracted), the row stored in its
+// slot (query, a, m, L = 1 + R, R, the argmax of rows with R < 1, derived
+// state). Then, in row order, the argmax terms: added for the new rows with
+// R < 1 (||a - v_j*||^2 / R^2, computed directly) and removed for the rows
+// leaving the window (their kept value). Rejects R <= 2^-24 (singular) and
+// non-finite rows.
+__global__ __launch_bounds__(1024) void k_dec_merge(DMergeArgs A) {
+  const int g = blockIdx.x, h = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  __shared__ float s_val[64];
+  __shared__ int s_js[64];
+  if (h < A.G) {
+    auto part = [&](int c) { return A.part + (((size_t)c * A.Hkv + g) * A.G + h) * kDecPart; };
+    float m = -INFINITY, R = 0.f, a0 = 0.f, a1 = 0.f;
+    int j = -1;
+    for (int c0 = 0; c0 < A.nch; c0 += 32) {
+      // this group of up to 32 chunks (lane = chunk): every load issued before any is used
+      const int cn = A.nch - c0 < 32 ? A.nch - c0 : 32;
+      const int c = c0 + (lane < cn ? lane : cn - 1);
+      const float mc = lane < cn ? part(c)[HD] : -INFINITY;
+      const float Rc = part(c)[HD + 1];
+      const int jc = __float_as_int(part(c)[HD + 2]);
+      float2 av[32];
 #pragma unroll
-    for (int o = 32; o > 0; o >>= 1) wm = fmaxf(wm, __shfl_xor(wm, o, 64));
-    if (wm > m) {
-      m = wm;
-      cw = c0 + __ffsll((long long)__builtin_amdgcn_ballot_w64(mc == wm)) - 1;
+      for (int u = 0; u < 32; ++u) av[u] = *(const float2*)(part(c0 + (u < cn ? u : cn - 1)) + 2 * lane);
+      float gm = mc;
+#pragma unroll
+      for (int o = 32; o > 0; o >>= 1) gm = fmaxf(gm, __shfl_xor(gm, o, 64));
+      const int cw = __ffsll((long long)__builtin_amdgcn_ballot_w64(mc == gm)) - 1;  // lowest chunk at the max
+      // this group's state relative to its own max gm
+      float t = (lane == cw || mc == -INFINITY) ? (lane == cw ? Rc : 0.f)
+                                                : (Rc + 1.0f) * __builtin_amdgcn_exp2f(mc - gm);
+#pragma unroll
+      for (int o = 32; o > 0; o >>= 1) t += __shfl_xor(t, o, 64);
+      const int jg = __shfl(jc, cw, 64);
+      float g0 = 0.f, g1 = 0.f;
+#pragma unroll
+      for (int u = 0; u < 32; ++u) {
+        const float mu = __shfl(mc, u, 64);
+        const float su = (u < cn && mu != -INFINITY) ? __builtin_amdgcn_exp2f(mu - gm) : 0.f;
+        g0 = fmaf(av[u].x, su, g0);
+        g1 = fmaf(av[u].y, su, g1);
+      }
+      // fold the group into the running state (groups in chunk order)
+      if (gm != -INFINITY) {
+        if (m == -INFINITY) {
+          m = gm; R = t; j = jg; a0 = g0; a1 = g1;
+        } else {
+          const bool win1 = m >= gm;  // earlier chunks hold lower indices
+          const float mx = fmaxf(m, gm);
+          const float f1 = __builtin_amdgcn_exp2f(m - mx), f2 = __builtin_amdgcn_exp2f(gm - mx);
+          R = win1 ? R + (t + 1.0f) * f2 : t + (R + 1.0f) * f1;
+          j = win1 ? j : jg;
+          a0 = a0 * f1 + g0 * f2;
+          a1 = a1 * f1 + g1 * f2;
+          m = mx;
+        }
+      }
+    }
+    const float L = 1.0f + R;
+    const float x0 = a0 / L, x1 = a1 / L;
+    const int64_t r = trow(g, A.n - 1, h, A.w, A.G);
+    *(float2*)(A.T.a + r * HD + 2 * lane) = make_float2(x0, x1);
+    *(uint32_t*)(A.T.q + r * HD + 2 * lane) = *(const uint32_t*)(A.qn + ((size_t)g * A.G + h) * HD + 2 * lane);
+    bool bad = !finite_f(m) || !finite_f(R) || !finite_f(x0) || !finite_f(x1);
+    bad = __builtin_amdgcn_ballot_w64(bad) != 0;
+    const float m_nat = m / kLog2e;
+    const int js = (!bad && R < 1.0f && j >= 0 && j < A.n) ? j : -1;
+    float val = 0.f;
+    if (js >= 0) {  // the argmax term, without cancellation
+      const uint32_t vv = *(const uint32_t*)(A.v + ((size_t)g * A.n_max + js) * HD + 2 * lane);
+      const float d0 = x0 - __uint_as_float(vv << 16), d1 = x1 - __uint_as_float(vv & 0xffff0000u);
+      float dist = fmaf(d0, d0, d1 * d1);
+#pragma unroll
+      for (int o = 32; o > 0; o >>= 1) dist += __shfl_xor(dist, o, 64);
+      val = dist / (R * R);
+    }
+    if (lane == 0) {
+      A.T.m[r] = m_nat;
+      A.T.L[r] = L;
+      A.T.R[r] = R;
+      A.T.jstar[r] = js;
+      A.T.cstar[r] = val;
+      s_val[h] = val;
+      s_js[h] = js;
+      if (bad) atomicOr(A.status, kStatusNonFinite);
+      else if (R <= kSingularRest) atomicOr(A.status, kStatusSingular);
+    }
+    derive_row(A.T, r, m_nat, L, lane);
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    double* S = A.S64 + (size_t)g * A.n_max;
+    const double invG = 1.0 / (double)A.G;
+    for (int hh = 0; hh < A.G; ++hh) {
+      if (s_js[hh] >= 0) S[s_js[hh]] += (double)s_val[hh] * invG;
+      const int64_t ro = trow(g, A.n - 1 - A.w, hh, A.w, A.G);  // leaving row
+      const int jo = A.T.jstar[ro];
+      if (jo >= 0 && jo < A.n) S[jo] -= (double)A.T.cstar[ro] * invG;
     }
   }
-  // R = R_winner + sum over the other chunks of (R_c + 1) 2^{m_c - m}: no term is subtracted
-  float R = 0.f;
-  for (int c0 = 0; c0 < A.nch; c0 += 64) {
-    const int c = c0 + lane;
-    float t = 0.f;
-    if (c < A.nch && m != -INFINITY) {
-      const float* o = part(c);
-      const float mc = o[HD];
-      t = c == cw ? o[HD + 1] : (mc == -INFINITY ? 0.f : (o[HD + 1] + 1.0f) * __builtin_amdgcn_exp2f(mc - m));
-    }
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) t += __shfl_xor(t, o, 64);
-    R += t;
-  }
-  const int j = cw >= 0 ? __float_as_int(part(cw)[HD + 2]) : -1;
-  // A = sum_c A_c 2^{m_c - m}, lane = 2 dims, sixteen chunks' loads in flight
-  float a0 = 0.f, a1 = 0.f;
-  for (int c0 = 0; c0 < A.nch; c0 += 16) {
-    float2 av[16];
-    float sv[16];
-#pragma unroll
-    for (int u = 0; u < 16; ++u) {
-      const int c = c0 + u < A.nch ? c0 + u : A.nch - 1;
-      const float* o = part(c);
-      av[u] = *(const float2*)(o + 2 * lane);
-      const float mc = o[HD];
-      sv[u] = (c0 + u < A.nch && mc != -INFINITY && m != -INFINITY) ? __builtin_amdgcn_exp2f(mc - m) : 0.f;
-    }
-#pragma unroll
-    for (int u = 0; u < 16; ++u) {
-      a0 = fmaf(av[u].x, sv[u], a0);
-      a1 = fmaf(av[u].y, sv[u], a1);
-    }
-  }
-  const float L = 1.0f + R;
-  const float x0 = a0 / L, x1 = a1 / L;
-  const int64_t r = trow(g, A.w, h, A.w, A.G);
-  *(float2*)(A.T.a + r * HD + 2 * lane) = make_float2(x0, x1);
-  *(uint32_t*)(A.T.q + r * HD + 2 * lane) = *(const uint32_t*)(A.qn + row * HD + 2 * lane);
-  bool bad = !finite_f(m) || !finite_f(R) || !finite_f(x0) || !finite_f(x1);
-  bad = __builtin_amdgcn_ballot_w64(bad) != 0;
-  const float m_nat = m / kLog2e;
-  if (lane == 0) {
-    A.T.m[r] = m_nat;
-    A.T.L[r] = L;
-    A.T.R[r] = R;
-    A.T.jstar[r] = (!bad && R < 1.0f) ? j : -1;
-    A.T.cstar[r] = 0.f;
-    if (bad) atomicOr(A.status, kStatusNonFinite);
-    else if (R <= kSingularRest) atomicOr(A.status, kStatusSingular);
-  }
-  derive_row(A.T, r, m_nat, L, lane);
 }
 
 // ---------------------------------------------------------------------------- signed terms
@@ -542,17 +560,14 @@ struct ContribArgs {
 };
 
 // Row rr of this launch's list (per KV head): entry e = rr / G, query head rr % G.
-__device__ __forceinline__ void entry_of(const ContribArgs& A, int e, int& slot, int64_t& pos, float& sign) {
+__device__ __forceinline__ void entry_of(const ContribArgs& A, int e, int64_t& pos, float& sign) {
   if (A.mode == 0) {
     pos = A.n - A.w + e;
-    slot = (int)(pos % A.w);
     sign = 1.0f;
   } else if (e == 0) {
-    slot = A.w;
     pos = A.n - 1;
     sign = 1.0f;
   } else {
-    slot = (int)((A.n - 1) % A.w);
     pos = A.n - 1 - A.w;
     sign = -1.0f;
   }
@@ -622,11 +637,10 @@ __global__ __launch_bounds__(256) void k_dec_contrib(ContribArgs A) {
   __shared__ __attribute__((aligned(16))) uint16_t s_op[LDSOP ? 2 * kOpRows : 1][kOpStride];
   for (int rr = threadIdx.x; rr < nb * 16; rr += blockDim.x) {
     if (rr < nrows) {
-      int slot;
       int64_t pos;
       float sign;
-      entry_of(A, A.e0 + rr / A.G, slot, pos, sign);
-      const int64_t r = trow(g, slot, rr % A.G, A.w, A.G);
+      entry_of(A, A.e0 + rr / A.G, pos, sign);
+      const int64_t r = trow(g, pos, rr % A.G, A.w, A.G);
       s_row[rr] = r;
       s_bias[rr] = A.T.bias[r];
       s_cinit[rr] = A.T.cinit[r];
@@ -862,13 +876,10 @@ hipError_t launch_decode_step(const void* q_new, const void* k, const void* v, i
       default: k_dec_stats<8><<<grid, 256, 0, st>>>(a); break;
     }
   }
-  DMergeArgs ma{S.part, (const uint16_t*)q_new, S.T, n, G, Hkv, w, nch, status};
-  k_dec_merge<<<(unsigned)((Hkv * G + 3) / 4), 256, 0, st>>>(ma);
-  hipError_t e = launch_decode_contrib(k, v, n, n_max, w, G, Hkv, S, 1, st);
-  if (e != hipSuccess) return e;
-  StarStepArgs sa{(const uint16_t*)v, S.T, S.S64, n, n_max, w, G, 1, status};
-  k_dec_star<<<Hkv, HD, 0, st>>>(sa);
-  return hipGetLastError();
+  DMergeArgs ma{S.part, (const uint16_t*)q_new, (const uint16_t*)v, S.T, S.S64, n, n_max, G, Hkv, w, nch,
+                status};
+  k_dec_merge<<<Hkv, 64 * G, 0, st>>>(ma);
+  return launch_decode_contrib(k, v, n, n_max, w, G, Hkv, S, 1, st);
 }
 
 hipError_t launch_decode_rebuild(const void* k, const void* v, int64_t n, int64_t n_max, int32_t w, int32_t Hq,
@@ -876,8 +887,9 @@ hipError_t launch_decode_rebuild(const void* k, const void* v, int64_t n, int64_
   const int G = Hq / Hkv;
   const int64_t cnt = (int64_t)Hkv * n_max;
   k_dec_zero<<<(unsigned)((cnt + 255) / 256), 256, 0, st>>>(S.S64, cnt);
-  StarStepArgs sa{(const uint16_t*)v, S.T, S.S64, n, n_max, w, G, 0, status};
-  k_dec_star<<<Hkv, HD, 0, st>>>(sa);
+  StarAllArgs sa{S.T, S.S64, n, n_max, w, G};
+  k_dec_star_all<<<Hkv, 64, 0, st>>>(sa);
+  (void)status;
   return launch_decode_contrib(k, v, n, n_max, w, G, Hkv, S, 0, st);
 }
 

@@ -125,10 +125,10 @@ int mfma_chunks(const Shape& s);
 size_t mfma_extra_bytes(const Shape& s);
 
 // Decode-time rescoring state (decode.hip), carved from one caller-owned
-// allocation. The window's rows live in a ring of w slots per KV head (the row
-// at position p in slot p mod w) plus a staging slot w for the position being
-// appended; row index ((g * (w + 1) + slot) * G + h) for query head h of KV
-// head g's G.
+// allocation. The window's rows live in a ring of w + 1 slots per KV head (the
+// row at position p in slot p mod (w + 1), so the position being appended and
+// the one leaving the window never share a slot); row index
+// ((g * (w + 1) + slot) * G + h) for query head h of KV head g's G.
 struct DecRows {
   uint16_t* q;      // [rows][128] query (bf16)
   float* a;         // [rows][128] attention output
@@ -154,8 +154,8 @@ DecState carve_decode_state(void* base, int64_t n_max, int32_t w, int32_t Hq, in
 // Clears *status first. k, v: [Hkv][n_max][128] bf16 holding n tokens.
 hipError_t launch_decode_init(const void* q, const void* k, const void* v, int64_t n, int64_t n_max, int32_t w,
                               int32_t Hq, int32_t Hkv, const DecState& S, int32_t* status, hipStream_t st);
-// One appended token (n counts it): new rows' statistics, signed terms of the
-// new and the leaving rows, argmax terms, commit. ORs status bits.
+// One appended token (n counts it): new rows' statistics and argmax terms,
+// signed terms of the new and the leaving rows. ORs status bits.
 hipError_t launch_decode_step(const void* q_new, const void* k, const void* v, int64_t n, int64_t n_max,
                               int32_t w, int32_t Hq, int32_t Hkv, const DecState& S, int32_t* status,
                               hipStream_t st);
