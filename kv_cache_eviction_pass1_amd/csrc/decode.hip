@@ -41,8 +41,7 @@ typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 constexpr int HD = 128;
 constexpr int kRowBatch = 8;       // new rows per k_dec_stats launch
 constexpr int kDecPart = HD + 4;   // floats per stats partial (A[128], m, R, j*, pad)
-constexpr int kContribRows = 1024; // rows per k_dec_contrib launch (LDS tables)
-constexpr int kOpRows = 64;        // rows whose MFMA operands k_dec_contrib stages in LDS
+constexpr int kContribRows = 64;   // rows per k_dec_contrib launch (operands and tables in LDS)
 constexpr int kOpStride = HD + 8;  // bf16 per staged operand row (272 bytes)
 constexpr int kTokPerWg = 512;     // tokens per k_dec_contrib workgroup (4 waves x 8 subtiles of 16)
 constexpr int kStatsTok = 2048;    // tokens per k_dec_stats workgroup
@@ -613,7 +612,6 @@ __device__ __forceinline__ double rows4_sum(double x) {
 // summed with the row's sign in fp64 and added to the score. Every element's
 // value depends only on its row's stored state and its token, whatever else
 // shares the block, so a row's terms are the same in every launch.
-template <bool LDSOP>
 __global__ __launch_bounds__(256) void k_dec_contrib(ContribArgs A) {
   const int chunk = blockIdx.x, g = blockIdx.y;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -629,12 +627,11 @@ __global__ __launch_bounds__(256) void k_dec_contrib(ContribArgs A) {
   // per-token sums of this chunk, added to the score once every subtile is done
   // (a read-modify-write per subtile would wait for the prefetched loads too)
   __shared__ double s_tot[kTokPerWg];
-  // LDSOP: the rows' query and a operands staged in LDS (rows padded to 272
-  // bytes, so 16 rows read at one column hit distinct banks); otherwise they
-  // are read from global memory per block and subtile (many rows: the first
-  // window). LDS reads keep the loads of the next subtiles in flight, which a
-  // global read here would wait for (vector loads complete in order).
-  __shared__ __attribute__((aligned(16))) uint16_t s_op[LDSOP ? 2 * kOpRows : 1][kOpStride];
+  // the rows' query and a operands, staged in LDS (rows padded to 272 bytes,
+  // so 16 rows read at one column hit distinct banks): reading them from
+  // global memory here would wait for the loads of the next subtiles too
+  // (vector loads complete in order)
+  __shared__ __attribute__((aligned(16))) uint16_t s_op[2 * kContribRows][kOpStride];
   for (int rr = threadIdx.x; rr < nb * 16; rr += blockDim.x) {
     if (rr < nrows) {
       int64_t pos;
@@ -657,16 +654,14 @@ __global__ __launch_bounds__(256) void k_dec_contrib(ContribArgs A) {
     }
   }
   __syncthreads();
-  if constexpr (LDSOP) {
-    for (int i = threadIdx.x; i < nb * 16 * 32; i += blockDim.x) {
-      const int rr = i >> 5, c = i & 31;  // 32 chunks of 16 bytes: q then a_bf
-      const int64_t r = s_row[rr];
-      uint4 u = make_uint4(0, 0, 0, 0);
-      if (r >= 0) u = *(const uint4*)((const char*)((c < 16 ? A.T.q : A.T.a_bf) + r * HD) + 16 * (c & 15));
-      *(uint4*)((char*)&s_op[(c < 16 ? 0 : kOpRows) + rr][0] + 16 * (c & 15)) = u;
-    }
-    __syncthreads();
+  for (int i = threadIdx.x; i < nb * 16 * 32; i += blockDim.x) {
+    const int rr = i >> 5, c = i & 31;  // 32 chunks of 16 bytes: q then a_bf
+    const int64_t r = s_row[rr];
+    uint4 u = make_uint4(0, 0, 0, 0);
+    if (r >= 0) u = *(const uint4*)((const char*)((c < 16 ? A.T.q : A.T.a_bf) + r * HD) + 16 * (c & 15));
+    *(uint4*)((char*)&s_op[(c < 16 ? 0 : kContribRows) + rr][0] + 16 * (c & 15)) = u;
   }
+  __syncthreads();
   const int64_t t0 = (int64_t)chunk * kTokPerWg;
   const double invG = 1.0 / (double)A.G;
   double* S = A.S64 + (size_t)g * A.n_max;
@@ -705,24 +700,10 @@ __global__ __launch_bounds__(256) void k_dec_contrib(ContribArgs A) {
     for (int b = 0; b < nb; ++b) {
       // the block's query and a operands
       bf16x8 qa[4], aa[4];
-      if constexpr (LDSOP) {
 #pragma unroll
-        for (int ks = 0; ks < 4; ++ks) {
-          qa[ks] = *(const bf16x8*)((const char*)&s_op[16 * b + l16][0] + opoff(lane, ks));
-          aa[ks] = *(const bf16x8*)((const char*)&s_op[kOpRows + 16 * b + l16][0] + opoff(lane, ks));
-        }
-      } else {
-        const int64_t r = s_row[16 * b + l16];
-#pragma unroll
-        for (int ks = 0; ks < 4; ++ks) {
-          if (r >= 0) {
-            qa[ks] = *(const bf16x8*)((const char*)(A.T.q + r * HD) + opoff(lane, ks));
-            aa[ks] = *(const bf16x8*)((const char*)(A.T.a_bf + r * HD) + opoff(lane, ks));
-          } else {
-            qa[ks] = bf16x8{};
-            aa[ks] = bf16x8{};
-          }
-        }
+      for (int ks = 0; ks < 4; ++ks) {
+        qa[ks] = *(const bf16x8*)((const char*)&s_op[16 * b + l16][0] + opoff(lane, ks));
+        aa[ks] = *(const bf16x8*)((const char*)&s_op[kContribRows + 16 * b + l16][0] + opoff(lane, ks));
       }
       const int base = 16 * b + 4 * q4;  // this lane's four rows
       const float4 c4 = *(const float4*)(&s_cinit[base]);
@@ -825,15 +806,12 @@ hipError_t launch_decode_contrib(const void* k, const void* v, int64_t n, int64_
                                  int32_t Hkv, const DecState& S, int mode, hipStream_t st) {
   const float c2 = kLog2e / sqrtf((float)HD);
   const int nent = mode == 0 ? w : 2;
-  const int per = kContribRows / G;  // window entries per launch
+  const int per = kContribRows / G;  // window entries per launch (G <= 16)
   const dim3 grid((unsigned)((n + kTokPerWg - 1) / kTokPerWg), Hkv);
   for (int e0 = 0; e0 < nent; e0 += per) {
     const int e1 = e0 + per < nent ? e0 + per : nent;
     ContribArgs a{(const uint16_t*)k, (const uint16_t*)v, S.T, S.S64, n, n_max, w, G, mode, e0, e1, c2};
-    if ((e1 - e0) * G <= kOpRows)
-      k_dec_contrib<true><<<grid, 256, 0, st>>>(a);
-    else
-      k_dec_contrib<false><<<grid, 256, 0, st>>>(a);
+    k_dec_contrib<<<grid, 256, 0, st>>>(a);
   }
   return hipGetLastError();
 }
