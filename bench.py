@@ -10,7 +10,10 @@ when the timed region starts.
 Prints one JSON line: scored tokens/s for the layer, the dominant kernel's
 achieved HBM bandwidth against MI355X's 8 TB/s (per-kernel HIP events on the
 library's stream), and the fp64 CPU oracle timed on a bounded sample of the
-same workload (one KV head) as a reported baseline.
+same workload (one KV head) as a reported baseline. After the timed steps it
+also times, apart from `value`: scoring from given row statistics, the
+Qwen2.5-7B-shaped 28-layer sweep, cache compaction and decode-time rescoring
+(first window, per appended token, re-eviction).
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
 """
@@ -46,7 +49,8 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extras", action="store_true",
                     help="time only the headline step: skip the scoring-from-statistics, "
-                         "Qwen2.5-7B sweep and cache-compaction timings that follow it")
+                         "Qwen2.5-7B sweep, cache-compaction and decode-rescoring timings that "
+                         "follow it")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain device copy of 512 MiB (3 times): the reference kernel "
                          "that scales rocprofv3 FETCH_SIZE / WRITE_SIZE to bytes")
