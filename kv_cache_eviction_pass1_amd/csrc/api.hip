@@ -1,6 +1,7 @@
 // C-ABI entry points of libdropkv: validation, workspace, dispatch, status.
 #include "../../include/dropkv.h"
 #include "dropkv_common.h"
+#include "decode_state.h"
 
 #include <cstdio>
 #include <cstring>

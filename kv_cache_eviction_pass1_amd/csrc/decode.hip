@@ -30,6 +30,7 @@
 //       the appended position never shares a slot with the one leaving.
 // The first window comes from the MFMA pass 1 + merge + argmax fix-up.
 #include "dropkv_common.h"
+#include "decode_state.h"
 
 namespace dropkv {
 
