@@ -42,7 +42,8 @@ typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 constexpr int HD = 128;
 constexpr int kRowBatch = 8;       // new rows per k_dec_stats launch
 constexpr int kDecPart = HD + 4;   // floats per stats partial (A[128], m, R, j*, pad)
-constexpr int kContribRows = 64;   // rows per k_dec_contrib launch (operands and tables in LDS)
+constexpr int kContribRows = 64;   // rows per k_dec_contrib launch in a step (operands and tables in LDS)
+constexpr int kInitRows = 128;     // rows per launch when a whole window is scored (76 KB of LDS: two workgroups per CU)
 constexpr int kOpStride = HD + 8;  // bf16 per staged operand row (272 bytes)
 constexpr int kTokPerWg = 512;     // tokens per k_dec_contrib workgroup (4 waves x 8 subtiles of 16)
 constexpr int kStatsTok = 2048;    // tokens per k_dec_stats workgroup
@@ -613,18 +614,19 @@ __device__ __forceinline__ double rows4_sum(double x) {
 // summed with the row's sign in fp64 and added to the score. Every element's
 // value depends only on its row's stored state and its token, whatever else
 // shares the block, so a row's terms are the same in every launch.
+template <int ROWS>
 __global__ __launch_bounds__(256) void k_dec_contrib(ContribArgs A) {
   const int chunk = blockIdx.x, g = blockIdx.y;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int q4 = lane >> 4, l16 = lane & 15;
   const int nrows = (A.e1 - A.e0) * A.G;
   const int nb = (nrows + 15) / 16;
-  __shared__ __attribute__((aligned(16))) float s_bias[kContribRows];
-  __shared__ __attribute__((aligned(16))) float s_cinit[kContribRows];
-  __shared__ __attribute__((aligned(16))) float s_sign[kContribRows];
-  __shared__ __attribute__((aligned(16))) int s_pos[kContribRows];
-  __shared__ __attribute__((aligned(16))) int s_js[kContribRows];
-  __shared__ int64_t s_row[kContribRows];
+  __shared__ __attribute__((aligned(16))) float s_bias[ROWS];
+  __shared__ __attribute__((aligned(16))) float s_cinit[ROWS];
+  __shared__ __attribute__((aligned(16))) float s_sign[ROWS];
+  __shared__ __attribute__((aligned(16))) int s_pos[ROWS];
+  __shared__ __attribute__((aligned(16))) int s_js[ROWS];
+  __shared__ int64_t s_row[ROWS];
   // per-token sums of this chunk, added to the score once every subtile is done
   // (a read-modify-write per subtile would wait for the prefetched loads too)
   __shared__ double s_tot[kTokPerWg];
@@ -632,7 +634,7 @@ __global__ __launch_bounds__(256) void k_dec_contrib(ContribArgs A) {
   // so 16 rows read at one column hit distinct banks): reading them from
   // global memory here would wait for the loads of the next subtiles too
   // (vector loads complete in order)
-  __shared__ __attribute__((aligned(16))) uint16_t s_op[2 * kContribRows][kOpStride];
+  __shared__ __attribute__((aligned(16))) uint16_t s_op[2 * ROWS][kOpStride];
   for (int rr = threadIdx.x; rr < nb * 16; rr += blockDim.x) {
     if (rr < nrows) {
       int64_t pos;
@@ -660,7 +662,7 @@ __global__ __launch_bounds__(256) void k_dec_contrib(ContribArgs A) {
     const int64_t r = s_row[rr];
     uint4 u = make_uint4(0, 0, 0, 0);
     if (r >= 0) u = *(const uint4*)((const char*)((c < 16 ? A.T.q : A.T.a_bf) + r * HD) + 16 * (c & 15));
-    *(uint4*)((char*)&s_op[(c < 16 ? 0 : kContribRows) + rr][0] + 16 * (c & 15)) = u;
+    *(uint4*)((char*)&s_op[(c < 16 ? 0 : ROWS) + rr][0] + 16 * (c & 15)) = u;
   }
   __syncthreads();
   const int64_t t0 = (int64_t)chunk * kTokPerWg;
@@ -704,7 +706,7 @@ __global__ __launch_bounds__(256) void k_dec_contrib(ContribArgs A) {
 #pragma unroll
       for (int ks = 0; ks < 4; ++ks) {
         qa[ks] = *(const bf16x8*)((const char*)&s_op[16 * b + l16][0] + opoff(lane, ks));
-        aa[ks] = *(const bf16x8*)((const char*)&s_op[kContribRows + 16 * b + l16][0] + opoff(lane, ks));
+        aa[ks] = *(const bf16x8*)((const char*)&s_op[ROWS + 16 * b + l16][0] + opoff(lane, ks));
       }
       const int base = 16 * b + 4 * q4;  // this lane's four rows
       const float4 c4 = *(const float4*)(&s_cinit[base]);
@@ -807,12 +809,18 @@ hipError_t launch_decode_contrib(const void* k, const void* v, int64_t n, int64_
                                  int32_t Hkv, const DecState& S, int mode, hipStream_t st) {
   const float c2 = kLog2e / sqrtf((float)HD);
   const int nent = mode == 0 ? w : 2;
-  const int per = kContribRows / G;  // window entries per launch (G <= 16)
+  // a step's 2G rows fit one small launch; a whole window takes launches of
+  // up to kInitRows rows: fewer K/V reads than 64-row launches, while two
+  // workgroups still fit a CU (256-row launches, one per CU, were slower)
+  const int per = (mode == 0 ? kInitRows : kContribRows) / G;  // window entries per launch (G <= 16)
   const dim3 grid((unsigned)((n + kTokPerWg - 1) / kTokPerWg), Hkv);
   for (int e0 = 0; e0 < nent; e0 += per) {
     const int e1 = e0 + per < nent ? e0 + per : nent;
     ContribArgs a{(const uint16_t*)k, (const uint16_t*)v, S.T, S.S64, n, n_max, w, G, mode, e0, e1, c2};
-    k_dec_contrib<<<grid, 256, 0, st>>>(a);
+    if (mode == 0)
+      k_dec_contrib<kInitRows><<<grid, 256, 0, st>>>(a);
+    else
+      k_dec_contrib<kContribRows><<<grid, 256, 0, st>>>(a);
   }
   return hipGetLastError();
 }

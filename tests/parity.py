@@ -77,3 +77,36 @@ def check_evictions(gpu_scores, gpu_idx, ref_P, ref_S, ref_idx, n_evict, rtol):
             assert np.array_equal(gpu_idx[g], ref), f"head {g}: evicted set differs from the oracle's"
             exact += 1
     return exact, jac
+
+
+def sample_tokens(case, g, rng, n_random=96, chunk=4096):
+    n, w = case.n, case.window
+    picks = [0, 1, 2, n - w - 1, n - w, n - w + 1, n - 2, n - 1]
+    picks += [c for b in range(chunk, n, chunk) for c in (b - 1, b)]
+    if case.needle_pos is not None:
+        picks += [int(p) for p in case.needle_pos[g]]
+    picks += [int(t) for t in rng.choice(n, size=n_random, replace=False)]
+    return np.unique(np.clip(np.asarray(picks), 0, n - 1))
+
+
+def check_sampled(case, g, pool, S_gpu, P_gpu, rng):
+    """Raw and pooled scores of head g on sampled tokens, against the oracle."""
+    G, n, w = case.group, case.n, case.window
+    half = pool // 2
+    toks = sample_tokens(case, g, rng)
+    need = np.unique(np.clip((toks[:, None] + np.arange(-half, half + 1)[None, :]).ravel(), 0, n - 1))
+    q = oracle.as_f64(case.q, case.dtype)
+    k = oracle.as_f64(case.k, case.dtype)
+    v = oracle.as_f64(case.v, case.dtype)
+    hs = oracle.head_scores(q, k, v, g, G, n, w, tokens=need)
+    S_ref = dict(zip(need.tolist(), hs["S"].tolist()))
+    ref_S = np.array([S_ref[int(t)] for t in toks])
+    ref_P = np.array([max(S_ref[int(u)] for u in range(max(0, t - half), min(n, t + half + 1)))
+                      for t in toks])
+    ref_P = np.where(toks >= n - w, np.inf, ref_P)
+    rtol = RTOL[case.dtype]
+    e_S = max_rel_err(S_gpu[g, toks], ref_S)
+    e_P = max_rel_err(P_gpu[g, toks], ref_P)
+    assert e_S <= rtol, f"head {g}: sampled raw scores rel err {e_S:.3e}"
+    assert e_P <= rtol, f"head {g}: sampled pooled scores rel err {e_P:.3e}"
+    return e_S, e_P

@@ -3,7 +3,8 @@
 The cache grows token by token from a scored prefix; after the first scoring
 and after every checked step, the kept raw score must match the oracle's
 score of the grown cache computed from scratch (relative 2e-2, bf16 inputs),
-including after more steps than the window holds (every prefix row has left).
+including after more steps than the window holds (every prefix row has left),
+and at the full 128K layer in the benchmark's launch configuration.
 The fp64 score kept incrementally must equal a rebuild from the stored window
 rows to fp64 rounding (the subtracted terms are bit for bit the added ones),
 re-eviction must equal the select stage on the same raw score and the oracle's
@@ -17,7 +18,7 @@ import pytest
 import oracle
 import kv_cache_eviction_pass1_amd as K
 from kv_cache_eviction_pass1_amd import synth
-from parity import RTOL, check_evictions, max_rel_err
+from parity import RTOL, check_evictions, check_sampled, max_rel_err, own_bottom_k, to_torch
 
 pytestmark = pytest.mark.gpu
 
@@ -146,3 +147,44 @@ def test_decode_reports_singular_new_row():
     sc.step(_dev(qn).contiguous(), kc, vc)
     with pytest.raises(K.DropKVSingularError):
         sc.check()
+
+
+def test_decode_full_layer_sampled():
+    """The 128K Llama layer reached by decode steps, sized as the benchmark runs them:
+    scored at n - 64 with 64 other window rows, then 64 appended positions whose
+    query rows are the layer's window rows. The kept score is then the layer's
+    score: against the oracle on sampled tokens (sink, needles, chunk edges,
+    window edge, random), and against the scoring pass on every token."""
+    cfg = synth.CONFIGS["llama_128k"]
+    case = synth.make_case(cfg)
+    n, w, Hq, Hkv, d = case.n, case.window, case.Hq, case.Hkv, case.d
+    q, k, v = to_torch(case)
+    rng = np.random.default_rng(77)
+    scale = float(synth.bf16_bits_to_float32(case.q).std())
+    first = synth.bf16_round_bits((rng.standard_normal((Hq, w, d)) * scale).astype(np.float32))
+    print(f"[decode full] llama_128k n={n} w={w}: init at n - {w}, {w} steps", flush=True)
+    sc = K.DecodeScorer(n_max=n, window=w, Hq=Hq, Hkv=Hkv, d=d)
+    sc.init(_dev(first).contiguous(), k, v, n - w)
+    for i in range(w):
+        sc.step(q[:, i].contiguous(), k, v)
+    ne = cfg.n_evicts()[0]
+    P, idx = sc.select(pool_kernel=cfg.pool_kernel, n_evict=ne)
+    sc.check()
+    S = sc.raw_scores().cpu().numpy()
+    P, idx = P.cpu().numpy(), idx.cpu().numpy()
+    for g in (0, 5):
+        e_S, e_P = check_sampled(case, g, cfg.pool_kernel, S, P, rng)
+        print(f"[decode full] head {g}: sampled rel err S {e_S:.2e}, P {e_P:.2e}", flush=True)
+    S_main = K.raw_scores(q, k, v).cpu().numpy()
+    # each is within RTOL of the exact score
+    assert max_rel_err(S, S_main) <= 2 * RTOL["bf16"]
+    assert np.all(np.isinf(P[:, n - w:])) and np.all(np.isfinite(P[:, : n - w]))
+    for g in range(Hkv):
+        assert np.array_equal(idx[g], own_bottom_k(P[g], ne)), f"head {g}: not its own bottom-k"
+    P_main, idx_main = K.select(torch.from_numpy(S_main).cuda(), window=w, pool_kernel=cfg.pool_kernel,
+                                n_evict=ne)
+    idx_main = idx_main.cpu().numpy()
+    for g in range(Hkv):
+        inter = np.intersect1d(idx[g], idx_main[g]).size
+        jac = inter / (2 * ne - inter)
+        assert jac > 0.99, f"head {g}: evicted set overlap with the scoring pass {jac:.4f}"

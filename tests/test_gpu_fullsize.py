@@ -14,7 +14,7 @@ import pytest
 import oracle
 import kv_cache_eviction_pass1_amd as K
 from kv_cache_eviction_pass1_amd import synth
-from parity import RTOL, check_evictions, max_rel_err, own_bottom_k, to_torch
+from parity import RTOL, check_evictions, check_sampled, max_rel_err, own_bottom_k, to_torch
 
 pytestmark = pytest.mark.gpu
 
@@ -40,39 +40,6 @@ def _run_ex(case, pool, n_evict):
     torch.cuda.synchronize()
     assert int(st.item()) == 0, f"device status {int(st.item())}"
     return scores.cpu().numpy(), idx.cpu().numpy(), S.cpu().numpy()
-
-
-def _sample_tokens(case, g, rng, n_random=96, chunk=4096):
-    n, w = case.n, case.window
-    picks = [0, 1, 2, n - w - 1, n - w, n - w + 1, n - 2, n - 1]
-    picks += [c for b in range(chunk, n, chunk) for c in (b - 1, b)]
-    if case.needle_pos is not None:
-        picks += [int(p) for p in case.needle_pos[g]]
-    picks += [int(t) for t in rng.choice(n, size=n_random, replace=False)]
-    return np.unique(np.clip(np.asarray(picks), 0, n - 1))
-
-
-def _check_sampled(case, g, pool, S_gpu, P_gpu, rng):
-    """Raw and pooled scores of head g on sampled tokens, against the oracle."""
-    G, n, w = case.group, case.n, case.window
-    half = pool // 2
-    toks = _sample_tokens(case, g, rng)
-    need = np.unique(np.clip((toks[:, None] + np.arange(-half, half + 1)[None, :]).ravel(), 0, n - 1))
-    q = oracle.as_f64(case.q, case.dtype)
-    k = oracle.as_f64(case.k, case.dtype)
-    v = oracle.as_f64(case.v, case.dtype)
-    hs = oracle.head_scores(q, k, v, g, G, n, w, tokens=need)
-    S_ref = dict(zip(need.tolist(), hs["S"].tolist()))
-    ref_S = np.array([S_ref[int(t)] for t in toks])
-    ref_P = np.array([max(S_ref[int(u)] for u in range(max(0, t - half), min(n, t + half + 1)))
-                      for t in toks])
-    ref_P = np.where(toks >= n - w, np.inf, ref_P)
-    rtol = RTOL[case.dtype]
-    e_S = max_rel_err(S_gpu[g, toks], ref_S)
-    e_P = max_rel_err(P_gpu[g, toks], ref_P)
-    assert e_S <= rtol, f"head {g}: sampled raw scores rel err {e_S:.3e}"
-    assert e_P <= rtol, f"head {g}: sampled pooled scores rel err {e_P:.3e}"
-    return e_S, e_P
 
 
 def _check_protection_and_own_bottom_k(case, P, idx, n_evict):
@@ -112,7 +79,7 @@ def test_llama_128k_headline_layer():
     _check_protection_and_own_bottom_k(case, P, idx, ne)
     rng = np.random.default_rng(2024)
     for g in (3, 7):
-        _check_sampled(case, g, cfg.pool_kernel, S, P, rng)
+        check_sampled(case, g, cfg.pool_kernel, S, P, rng)
     # head 0 in full: scores and the exact evicted set
     ref = oracle.dropkv_oracle(case.q, case.k, case.v, n=case.n, window=case.window, Hq=case.Hq,
                                Hkv=case.Hkv, d=case.d, pool_kernel=cfg.pool_kernel, n_evict=ne,
@@ -133,4 +100,4 @@ def test_qwen_128k_layer_sampled():
     _check_protection_and_own_bottom_k(case, P, idx, ne)
     rng = np.random.default_rng(2025)
     for g in (0, 3):
-        _check_sampled(case, g, cfg.pool_kernel, S, P, rng)
+        check_sampled(case, g, cfg.pool_kernel, S, P, rng)
