@@ -13,7 +13,8 @@ library's stream), and the fp64 CPU oracle timed on a bounded sample of the
 same workload (one KV head) as a reported baseline. After the timed steps it
 also times, apart from `value`: scoring from given row statistics, the
 Qwen2.5-7B-shaped 28-layer sweep, cache compaction and decode-time rescoring
-(first window, per appended token, re-eviction).
+(first window, per appended token in the two-pass and the single-pass form,
+the flush of pending terms, re-eviction).
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
 """
@@ -365,6 +366,25 @@ def main():
         e1.record()
         torch.cuda.synchronize()
         step_ms = e0.elapsed_time(e1) / dsteps
+        # the same 64 appended tokens with single-pass steps (one read of the
+        # cache per token; the newest position's terms wait for the next step),
+        # then the flush that adds the last step's pending terms
+        dec.init(q, k, v, n0)
+        for i in range(dsteps // 2):
+            dec.step(qrows[i], k, v, deferred=True)
+        dec.init(q, k, v, n0)
+        torch.cuda.synchronize()
+        e0.record()
+        for i in range(dsteps):
+            dec.step(qrows[i], k, v, deferred=True)
+        e1.record()
+        torch.cuda.synchronize()
+        step1_ms = e0.elapsed_time(e1) / dsteps
+        e0.record()
+        dec.flush()
+        e1.record()
+        torch.cuda.synchronize()
+        flush_ms = e0.elapsed_time(e1)
         for _ in range(3):
             dec.select(pool_kernel=cfg.pool_kernel, n_evict=n_evict)
         e0.record()
@@ -375,12 +395,18 @@ def main():
         sel_ms = e0.elapsed_time(e1) / 10
         dec.check()
         step_bytes = 4 * case.Hkv * case.n * case.d * 2  # K and V read by the statistics and the terms kernels
+        step1_bytes = step_bytes // 2  # K and V read once
         rec["decode"] = {
             "workload": "same layer grown by 64 tokens from n - 64, window 64",
             "init_ms": round(init_ms, 4), "step_ms": round(step_ms, 4), "select_ms": round(sel_ms, 4),
             "step_alg_bytes": step_bytes,
             "step_achieved_GBs": round(step_bytes / (step_ms * 1e-3) / 1e9, 1),
             "step_frac": round(step_bytes / (step_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+            "single_pass_step_ms": round(step1_ms, 4),
+            "single_pass_alg_bytes": step1_bytes,
+            "single_pass_achieved_GBs": round(step1_bytes / (step1_ms * 1e-3) / 1e9, 1),
+            "single_pass_frac": round(step1_bytes / (step1_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+            "flush_ms": round(flush_ms, 4),
             "full_rescore_ms": round(ms_per_step, 4),
         }
         del dec

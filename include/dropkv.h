@@ -68,8 +68,14 @@ typedef enum {
 enum { DROPKV_BF16 = 0, DROPKV_F32 = 1 };
 
 /* Bits of the device status word written by dropkv_score_ex (and, for
- * DROPKV_STATUS_BAD_INDEX, by dropkv_compact). */
-enum { DROPKV_STATUS_SINGULAR = 1, DROPKV_STATUS_NONFINITE = 2, DROPKV_STATUS_BAD_INDEX = 4 };
+ * DROPKV_STATUS_BAD_INDEX, by dropkv_compact; DROPKV_STATUS_PENDING, by
+ * dropkv_decode_select after dropkv_decode_step_deferred). */
+enum {
+  DROPKV_STATUS_SINGULAR = 1,
+  DROPKV_STATUS_NONFINITE = 2,
+  DROPKV_STATUS_BAD_INDEX = 4,
+  DROPKV_STATUS_PENDING = 8
+};
 
 /* Flags for dropkv_score_ex. */
 enum {
@@ -273,8 +279,32 @@ int dropkv_decode_step(const void* q_new, const void* k, const void* v, int64_t 
                        int32_t window, int32_t Hq, int32_t Hkv, int32_t d, void* state, size_t state_bytes,
                        int32_t* d_status, void* stream);
 
+/* One appended token in a single pass over the cache (dropkv_decode_step
+ * reads K and V twice: once for the new rows' statistics, then for their
+ * terms). Arguments, limits and errors as dropkv_decode_step. The pass computes
+ * the new position's row statistics, subtracts the terms of the rows leaving
+ * the window and adds those of the rows a previous deferred step left pending;
+ * the new rows' terms (which need their finished statistics) stay pending.
+ * Their argmax terms are added at once. So after this call S lacks the
+ * newest position's non-argmax terms until the next step of either form (a
+ * two-pass step adds them), dropkv_decode_flush or dropkv_decode_rebuild;
+ * dropkv_decode_select ORs DROPKV_STATUS_PENDING into d_status when called in
+ * that state (its result is then that of the incomplete S), and
+ * dropkv_decode_scores returns the incomplete S. With more than 8 query heads
+ * per KV head this call runs the two-pass step (nothing is left pending). */
+int dropkv_decode_step_deferred(const void* q_new, const void* k, const void* v, int64_t n, int64_t n_max,
+                                int32_t window, int32_t Hq, int32_t Hkv, int32_t d, void* state, size_t state_bytes,
+                                int32_t* d_status, void* stream);
+
+/* Add the terms a deferred step left pending (none: nothing changes; the
+ * call still launches two small kernels). k, v, n as for the step that left
+ * them. */
+int dropkv_decode_flush(const void* k, const void* v, int64_t n, int64_t n_max, int32_t window, int32_t Hq,
+                        int32_t Hkv, int32_t d, void* state, size_t state_bytes, void* stream);
+
 /* Recompute S from the window rows kept in the state (no new statistics):
- * equal to the incrementally kept S up to fp64 rounding. ORs status bits. */
+ * equal to the incrementally kept S up to fp64 rounding. Nothing stays
+ * pending afterwards. ORs status bits. */
 int dropkv_decode_rebuild(const void* k, const void* v, int64_t n, int64_t n_max, int32_t window, int32_t Hq,
                           int32_t Hkv, int32_t d, void* state, size_t state_bytes, int32_t* d_status,
                           void* stream);

@@ -17,7 +17,7 @@ LIB_PATH = os.path.join(_HERE, "libdropkv.so")
 
 OK, ERR_INVALID, ERR_SINGULAR, ERR_NONFINITE, ERR_DEVICE = 0, -1, -2, -3, -4
 BF16, F32 = 0, 1
-STATUS_SINGULAR, STATUS_NONFINITE, STATUS_BAD_INDEX = 1, 2, 4
+STATUS_SINGULAR, STATUS_NONFINITE, STATUS_BAD_INDEX, STATUS_PENDING = 1, 2, 4, 8
 FLAG_GENERIC = 1
 FLAG_STAGE_LOG = 2
 
@@ -45,6 +45,8 @@ SIGNATURES = {
     "dropkv_decode_state_bytes": (_sz, [_i64, _i32, _i32, _i32, _i32]),
     "dropkv_decode_init": (_i32, [_p, _p, _p, _i64, _i64, _i32, _i32, _i32, _i32, _p, _sz, _p, _p]),
     "dropkv_decode_step": (_i32, [_p, _p, _p, _i64, _i64, _i32, _i32, _i32, _i32, _p, _sz, _p, _p]),
+    "dropkv_decode_step_deferred": (_i32, [_p, _p, _p, _i64, _i64, _i32, _i32, _i32, _i32, _p, _sz, _p, _p]),
+    "dropkv_decode_flush": (_i32, [_p, _p, _i64, _i64, _i32, _i32, _i32, _i32, _p, _sz, _p]),
     "dropkv_decode_rebuild": (_i32, [_p, _p, _i64, _i64, _i32, _i32, _i32, _i32, _p, _sz, _p, _p]),
     "dropkv_decode_scores": (_i32, [_p, _sz, _i64, _i64, _i32, _i32, _i32, _i32, _p, _p]),
     "dropkv_decode_select": (_i32, [_p, _sz, _i64, _i64, _i32, _i32, _i32, _i32, _i32, _i64, _p, _p, _p,
@@ -307,7 +309,9 @@ class DecodeScorer:
     first n token rows of each head are valid; the scorer owns the device
     state (sized for n_max) and a device status word. Calls are asynchronous
     on the current stream; check() synchronises and raises on a recorded
-    singular / non-finite row.
+    singular / non-finite row. After step(..., deferred=True) the newest
+    position's terms are pending; the reading calls (raw_scores,
+    raw_scores_f64, select) flush them first with the k, v of that step.
     """
 
     def __init__(self, *, n_max: int, window: int, Hq: int, Hkv: int, d: int, device=None):
@@ -320,6 +324,7 @@ class DecodeScorer:
         self.state = torch.empty(nbytes, dtype=torch.uint8, device=device or "cuda")
         self.status = torch.zeros(1, dtype=torch.int32, device=self.state.device)
         self.n = 0
+        self._pending_kv = None  # (k, v) of a deferred step whose terms are not in S yet
 
     def _kv(self, k, v):
         torch = _torch()
@@ -340,28 +345,46 @@ class DecodeScorer:
                                            self.state.data_ptr(), self.state.numel(), self.status.data_ptr(),
                                            _stream_handle(stream)))
         self.n = n
+        self._pending_kv = None
 
-    def step(self, q_new, k, v, stream=None):
-        """Append one token: its key and value are already at row self.n of k and v; q_new [Hq, d]."""
+    def step(self, q_new, k, v, stream=None, *, deferred: bool = False):
+        """Append one token: its key and value are already at row self.n of k and v; q_new [Hq, d].
+
+        deferred=True takes the single-pass step (one read of the cache): the
+        new position's terms stay pending until the next step, a flush or a
+        reading call.
+        """
         self._kv(k, v)
         if tuple(q_new.shape) != (self.Hq, self.d) or q_new.dtype != k.dtype or not q_new.is_contiguous():
             raise DropKVInvalidError(ERR_INVALID, "q_new must be contiguous bf16 [Hq, d]")
         n = self.n + 1
-        _raise(self.lib.dropkv_decode_step(q_new.data_ptr(), k.data_ptr(), v.data_ptr(), n, *self._args(),
-                                           self.state.data_ptr(), self.state.numel(), self.status.data_ptr(),
-                                           _stream_handle(stream)))
+        fn = self.lib.dropkv_decode_step_deferred if deferred else self.lib.dropkv_decode_step
+        _raise(fn(q_new.data_ptr(), k.data_ptr(), v.data_ptr(), n, *self._args(), self.state.data_ptr(),
+                  self.state.numel(), self.status.data_ptr(), _stream_handle(stream)))
         self.n = n
+        self._pending_kv = (k, v) if deferred else None
+
+    def flush(self, stream=None):
+        """Add the terms a deferred step left pending (no-op if none)."""
+        if self._pending_kv is None:
+            return
+        k, v = self._pending_kv
+        _raise(self.lib.dropkv_decode_flush(k.data_ptr(), v.data_ptr(), self.n, *self._args(),
+                                            self.state.data_ptr(), self.state.numel(), _stream_handle(stream)))
+        self._pending_kv = None
 
     def rebuild(self, k, v, stream=None):
-        """Recompute the kept score from the stored window rows."""
+        """Recompute the kept score from the stored window rows (nothing stays pending)."""
         self._kv(k, v)
         _raise(self.lib.dropkv_decode_rebuild(k.data_ptr(), v.data_ptr(), self.n, *self._args(),
                                               self.state.data_ptr(), self.state.numel(), self.status.data_ptr(),
                                               _stream_handle(stream)))
+        self._pending_kv = None
 
     def raw_scores(self, stream=None):
         """The kept raw score as fp32 [Hkv, n]."""
         torch = _torch()
+        self.flush(stream)
         out = torch.empty((self.Hkv, self.n), dtype=torch.float32, device=self.state.device)
         _raise(self.lib.dropkv_decode_scores(self.state.data_ptr(), self.state.numel(), self.n, *self._args(),
                                              out.data_ptr(), _stream_handle(stream)))
@@ -370,12 +393,14 @@ class DecodeScorer:
     def raw_scores_f64(self):
         """The kept fp64 score [Hkv, n] (a view into the state: S64 comes first in its layout)."""
         torch = _torch()
+        self.flush()
         S64 = self.state[: 8 * self.Hkv * self.n_max].view(torch.float64).view(self.Hkv, self.n_max)
         return S64[:, : self.n]
 
     def select(self, *, pool_kernel: int, n_evict: int, stream=None):
         """Re-eviction on the kept score: (pooled scores [Hkv, n], evict_idx [Hkv, n_evict])."""
         torch = _torch()
+        self.flush(stream)
         scores = torch.empty((self.Hkv, self.n), dtype=torch.float32, device=self.state.device)
         idx = torch.empty((self.Hkv, max(n_evict, 0)), dtype=torch.int64, device=self.state.device)
         _raise(self.lib.dropkv_decode_select(self.state.data_ptr(), self.state.numel(), self.n, *self._args(),

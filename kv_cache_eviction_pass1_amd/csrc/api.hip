@@ -623,6 +623,31 @@ int dropkv_decode_step(const void* q_new, const void* k, const void* v, int64_t 
   return DROPKV_OK;
 }
 
+int dropkv_decode_step_deferred(const void* q_new, const void* k, const void* v, int64_t n, int64_t n_max,
+                                int32_t window, int32_t Hq, int32_t Hkv, int32_t d, void* state, size_t state_bytes,
+                                int32_t* d_status, void* stream) {
+  g_last_error.clear();
+  if (int rc = check_decode(n, (int64_t)window + 2, n_max, window, Hq, Hkv, d, state, state_bytes)) return rc;
+  if (int rc = check_inputs(q_new, k, v)) return rc;
+  if (!d_status || !is_device_ptr(d_status)) return fail(DROPKV_ERR_INVALID, "d_status must be a device pointer");
+  const DecState S = carve_decode_state(state, n_max, window, Hq, Hkv);
+  hipError_t e =
+      launch_decode_step_deferred(q_new, k, v, n, n_max, window, Hq, Hkv, S, d_status, (hipStream_t)stream);
+  if (e != hipSuccess) return fail_hip(e, "decode deferred step");
+  return DROPKV_OK;
+}
+
+int dropkv_decode_flush(const void* k, const void* v, int64_t n, int64_t n_max, int32_t window, int32_t Hq,
+                        int32_t Hkv, int32_t d, void* state, size_t state_bytes, void* stream) {
+  g_last_error.clear();
+  if (int rc = check_decode(n, (int64_t)window + 1, n_max, window, Hq, Hkv, d, state, state_bytes)) return rc;
+  if (!k || !v || !is_device_ptr(k) || !is_device_ptr(v)) return fail(DROPKV_ERR_INVALID, "k and v must be device pointers");
+  const DecState S = carve_decode_state(state, n_max, window, Hq, Hkv);
+  hipError_t e = launch_decode_flush(k, v, n, n_max, window, Hq, Hkv, S, (hipStream_t)stream);
+  if (e != hipSuccess) return fail_hip(e, "decode flush");
+  return DROPKV_OK;
+}
+
 int dropkv_decode_rebuild(const void* k, const void* v, int64_t n, int64_t n_max, int32_t window, int32_t Hq,
                           int32_t Hkv, int32_t d, void* state, size_t state_bytes, int32_t* d_status,
                           void* stream) {
@@ -642,7 +667,7 @@ int dropkv_decode_scores(const void* state, size_t state_bytes, int64_t n, int64
   if (int rc = check_decode(n, (int64_t)window + 1, n_max, window, Hq, Hkv, d, state, state_bytes)) return rc;
   if (!out_S || !is_device_ptr(out_S)) return fail(DROPKV_ERR_INVALID, "out_S must be a device pointer");
   const DecState S = carve_decode_state(const_cast<void*>(state), n_max, window, Hq, Hkv);
-  hipError_t e = launch_decode_scores(S, n, n_max, Hkv, out_S, (hipStream_t)stream);
+  hipError_t e = launch_decode_scores(S, n, n_max, Hkv, out_S, nullptr, (hipStream_t)stream);
   if (e != hipSuccess) return fail_hip(e, "decode scores");
   return DROPKV_OK;
 }

@@ -96,6 +96,7 @@ struct LoadArgs {
   double* S64;
   int64_t n, n_max;
   int w, Hq, Hkv;
+  int64_t* pend;
 };
 
 // Window rows of the first scoring into their slots (slot = position mod (w + 1)),
@@ -109,6 +110,7 @@ __global__ __launch_bounds__(256) void k_dec_load(LoadArgs A) {
     for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < tot; i += (int64_t)gridDim.x * blockDim.x)
       A.S64[i] = 0.0;
   }
+  if (blockIdx.x == 0 && threadIdx.x == 0) A.pend[0] = -1;
   const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
   if (row >= (int64_t)A.Hq * A.w) return;
   const int h = (int)(row / A.w), i = (int)(row % A.w);
@@ -238,165 +240,154 @@ __device__ __forceinline__ float row8_sum(float x) {
   return x;
 }
 
-// Per (token chunk, KV head): 8 lanes per token (lane l%8 holds dims
-// 8(l%8) .. +7 and 64 + 8(l%8) .. +7, so each load instruction reads 8 token
-// rows x 128 contiguous bytes), rows held in registers. Each lane group keeps
-// its rows' state against a lazy reference mref (log2 units): estar = 2^{m -
-// mref} of the current maximum m, R' = sum over its other tokens of
-// 2^{x - mref} (a new maximum moves the old one's weight into R', so nothing
-// is ever subtracted) and acc = sum 2^{x - mref} v; the reference moves only
-// when a logit exceeds it by more than 2^8. The eight lane groups and four
-// waves are then merged into one partial per row, relative to m.
+// One lane's share of NR rows' online state (dims 8 li .. +7 and 64 + 8 li ..
+// +7 of lane li of its 8-lane group, one token per group at a time), kept
+// against a lazy reference mref (log2 units): estar = 2^{m - mref} of the
+// current maximum m, R' = sum over its other tokens of 2^{x - mref} (a new
+// maximum moves the old one's weight into R', so nothing is ever subtracted)
+// and acc = sum 2^{x - mref} v; the reference moves only when a logit exceeds
+// it by more than 2^8.
 template <int NR>
-__global__ __launch_bounds__(256) void k_dec_stats(StatsArgs A) {
-  const int chunk = blockIdx.x, g = blockIdx.y;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int li = lane & 7, grp = lane >> 3;
-  constexpr int U = NR <= 2 ? 4 : (NR <= 4 ? 2 : 1);  // 32-token groups per round of loads (two rounds in flight)
-  constexpr float kRef = 8.0f;
-  const int64_t t0 = (int64_t)chunk * kStatsTok;
-  int64_t t1 = t0 + kStatsTok;
-  if (t1 > A.n) t1 = A.n;
+struct StatsLane {
   uint32_t q[NR][8];
-#pragma unroll
-  for (int r = 0; r < NR; ++r) {
-    const uint16_t* qr = A.qn + ((size_t)(g * A.G + A.r0 + r)) * HD;
-    const uint4 u0 = *(const uint4*)(qr + 8 * li), u1 = *(const uint4*)(qr + 64 + 8 * li);
-    q[r][0] = u0.x; q[r][1] = u0.y; q[r][2] = u0.z; q[r][3] = u0.w;
-    q[r][4] = u1.x; q[r][5] = u1.y; q[r][6] = u1.z; q[r][7] = u1.w;
-  }
   float mref[NR], m[NR], estar[NR], Rp[NR], acc[NR][16];
   int jst[NR];
+};
+
+// query rows r0 .. r0 + NR - 1 of KV head g (qn: [Hq][d] bf16), empty state
+template <int NR>
+__device__ __forceinline__ void stats_begin(StatsLane<NR>& L, const uint16_t* qn, int g, int G, int r0, int li) {
 #pragma unroll
   for (int r = 0; r < NR; ++r) {
-    mref[r] = -INFINITY; m[r] = -INFINITY; estar[r] = 0.f; Rp[r] = 0.f; jst[r] = -1;
+    const uint16_t* qr = qn + ((size_t)(g * G + r0 + r)) * HD;
+    const uint4 u0 = *(const uint4*)(qr + 8 * li), u1 = *(const uint4*)(qr + 64 + 8 * li);
+    L.q[r][0] = u0.x; L.q[r][1] = u0.y; L.q[r][2] = u0.z; L.q[r][3] = u0.w;
+    L.q[r][4] = u1.x; L.q[r][5] = u1.y; L.q[r][6] = u1.z; L.q[r][7] = u1.w;
+    L.mref[r] = -INFINITY; L.m[r] = -INFINITY; L.estar[r] = 0.f; L.Rp[r] = 0.f; L.jst[r] = -1;
 #pragma unroll
-    for (int i = 0; i < 16; ++i) acc[r][i] = 0.f;
+    for (int i = 0; i < 16; ++i) L.acc[r][i] = 0.f;
   }
-  const char* kc = (const char*)(A.k + ((size_t)g * A.n_max + t0) * HD);
-  const char* vc = (const char*)(A.v + ((size_t)g * A.n_max + t0) * HD);
-  const int nt = (int)(t1 - t0);
-  const int lo = wave * 8 + grp;  // this lane group's token within each group of 32
-  auto load = [&](int tb, uint4 (&k0)[U], uint4 (&k1)[U], uint4 (&v0)[U], uint4 (&v1)[U]) {
+}
+
+// U tokens (global indices tok[u]; ok[u] = inside the cache) into every row's
+// state, in token order. kw / vw: this lane's 16 dims of k and v of each token
+// as bf16 pairs. All U x NR logits are formed first (independent dot-product
+// chains), then the state updates run token by token, so the result is that
+// of feeding the tokens one at a time. Wave-uniform control flow: every lane
+// of the wave calls it together.
+template <int NR, int U>
+__device__ __forceinline__ void stats_tokens(StatsLane<NR>& L, const uint32_t (&kw)[U][8],
+                                             const uint32_t (&vw)[U][8], const bool (&ok)[U], const int (&tok)[U],
+                                             float c2) {
+  constexpr float kRef = 8.0f;
+  float x[U][NR];
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-      int tr = tb + 32 * u + lo;
-      tr = tr < nt ? tr : nt - 1;
-      const uint32_t off = (uint32_t)tr * (HD * 2) + 16u * (uint32_t)li;
-      k0[u] = *(const uint4*)(kc + off);
-      k1[u] = *(const uint4*)(kc + off + 128);
-      v0[u] = *(const uint4*)(vc + off);
-      v1[u] = *(const uint4*)(vc + off + 128);
-    }
-  };
-  auto process = [&](int tb, const uint4 (&k0)[U], const uint4 (&k1)[U], const uint4 (&v0)[U],
-                     const uint4 (&v1)[U]) {
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int tl = tb + 32 * u + lo;
-      const bool ok = tl < nt;
-      const uint32_t kw[8] = {k0[u].x, k0[u].y, k0[u].z, k0[u].w, k1[u].x, k1[u].y, k1[u].z, k1[u].w};
-      const uint32_t vw[8] = {v0[u].x, v0[u].y, v0[u].z, v0[u].w, v1[u].x, v1[u].y, v1[u].z, v1[u].w};
-      float vf[16];
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        vf[2 * i] = __uint_as_float(vw[i] << 16);
-        vf[2 * i + 1] = __uint_as_float(vw[i] & 0xffff0000u);
-      }
-#pragma unroll
-      for (int r = 0; r < NR; ++r) {
-        float d = 0.f;
-#pragma unroll
-        for (int i = 0; i < 8; ++i)
-          d = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, q[r][i]), __builtin_bit_cast(bf16x2, kw[i]),
-                                              d, false);
-        const float x = ok ? row8_sum(d) * A.c2 : -INFINITY;
-        // move the reference when a logit passes it by more than 2^8 (rare; a wave decision)
-        if (__builtin_amdgcn_ballot_w64(x > mref[r] + kRef)) {
-          const bool mv = x > mref[r] + kRef;
-          const float nref = mv ? x : mref[r];
-          const float f = mv ? __builtin_amdgcn_exp2f(mref[r] - nref) : 1.0f;  // 0 from an empty state
-          Rp[r] *= f;
-          estar[r] *= f;
-#pragma unroll
-          for (int i = 0; i < 16; ++i) acc[r][i] *= f;
-          mref[r] = nref;
-        }
-        const float e = ok ? __builtin_amdgcn_exp2f(x - mref[r]) : 0.f;
-        const bool gt = x > m[r];
-        Rp[r] += gt ? estar[r] : e;
-        estar[r] = gt ? e : estar[r];
-        jst[r] = gt ? (int)(t0 + tl) : jst[r];
-        m[r] = gt ? x : m[r];
-#pragma unroll
-        for (int i = 0; i < 16; ++i) acc[r][i] = fmaf(e, vf[i], acc[r][i]);
-      }
-    }
-  };
-  constexpr int kRound = 32 * U;
-  uint4 ka0[U], ka1[U], va0[U], va1[U], kb0[U], kb1[U], vb0[U], vb1[U];
-  int tb = 0;
-  if (tb < nt) load(tb, ka0, ka1, va0, va1);
-  while (tb < nt) {
-    if (tb + kRound < nt) load(tb + kRound, kb0, kb1, vb0, vb1);
-    process(tb, ka0, ka1, va0, va1);
-    tb += kRound;
-    if (tb >= nt) break;
-    if (tb + kRound < nt) load(tb + kRound, ka0, ka1, va0, va1);
-    process(tb, kb0, kb1, vb0, vb1);
-    tb += kRound;
-  }
-  // state relative to m: R = R' / estar, A = acc / estar (estar = 2^{m - mref} >= 2^-8... > 0)
-  OnState st[NR];
-#pragma unroll
-  for (int r = 0; r < NR; ++r) {
-    const float inv = m[r] == -INFINITY ? 0.f : 1.0f / estar[r];
-    st[r] = OnState{m[r], Rp[r] * inv, jst[r]};
-#pragma unroll
-    for (int i = 0; i < 16; ++i) acc[r][i] *= inv;
-  }
-  // merge the eight lane groups of the wave (lanes li + 8 k), lower group first
-#pragma unroll
-  for (int r = 0; r < NR; ++r) {
-#pragma unroll
-    for (int o = 8; o < 64; o <<= 1) {
-      OnState s2{__shfl_xor(st[r].m, o, 64), __shfl_xor(st[r].R, o, 64), __shfl_xor(st[r].j, o, 64)};
-      float a2[16];
-#pragma unroll
-      for (int i = 0; i < 16; ++i) a2[i] = __shfl_xor(acc[r][i], o, 64);
-      if (lane & o) {
-        OnState s1 = s2;
-        float a1[16];
-#pragma unroll
-        for (int i = 0; i < 16; ++i) a1[i] = a2[i];
-        on_merge<16>(s1, a1, st[r], acc[r]);
-        st[r] = s1;
-#pragma unroll
-        for (int i = 0; i < 16; ++i) acc[r][i] = a1[i];
-      } else {
-        on_merge<16>(st[r], acc[r], s2, a2);
-      }
-    }
-  }
-  // then the four waves, in wave order; dims of lane li: 8 li + (0..7), 64 + 8 li + (0..7)
-  __shared__ float ws[4][NR][kDecPart];
-  if (grp == 0) {
+  for (int u = 0; u < U; ++u) {
 #pragma unroll
     for (int r = 0; r < NR; ++r) {
+      float d = 0.f;
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        ws[wave][r][8 * li + i] = acc[r][i];
-        ws[wave][r][64 + 8 * li + i] = acc[r][8 + i];
+      for (int i = 0; i < 8; ++i)
+        d = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, L.q[r][i]),
+                                            __builtin_bit_cast(bf16x2, kw[u][i]), d, false);
+      x[u][r] = ok[u] ? row8_sum(d) * c2 : -INFINITY;
+    }
+  }
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    float vf[16];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      vf[2 * i] = __uint_as_float(vw[u][i] << 16);
+      vf[2 * i + 1] = __uint_as_float(vw[u][i] & 0xffff0000u);
+    }
+#pragma unroll
+    for (int r = 0; r < NR; ++r) {
+      const float xr = x[u][r];
+      // move the reference when a logit passes it by more than 2^8 (rare; a wave decision)
+      if (__builtin_amdgcn_ballot_w64(xr > L.mref[r] + kRef)) {
+        const bool mv = xr > L.mref[r] + kRef;
+        const float nref = mv ? xr : L.mref[r];
+        const float f = mv ? __builtin_amdgcn_exp2f(L.mref[r] - nref) : 1.0f;  // 0 from an empty state
+        L.Rp[r] *= f;
+        L.estar[r] *= f;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) L.acc[r][i] *= f;
+        L.mref[r] = nref;
       }
-      if (li == 0) {
-        ws[wave][r][HD] = st[r].m;
-        ws[wave][r][HD + 1] = st[r].R;
-        ws[wave][r][HD + 2] = __int_as_float(st[r].j);
+      const float e = ok[u] ? __builtin_amdgcn_exp2f(xr - L.mref[r]) : 0.f;
+      const bool gt = xr > L.m[r];
+      L.Rp[r] += gt ? L.estar[r] : e;
+      L.estar[r] = gt ? e : L.estar[r];
+      L.jst[r] = gt ? tok[u] : L.jst[r];
+      L.m[r] = gt ? xr : L.m[r];
+#pragma unroll
+      for (int i = 0; i < 16; ++i) L.acc[r][i] = fmaf(e, vf[i], L.acc[r][i]);
+    }
+  }
+}
+
+// The workgroup's partial per row (relative to its m) into out[r * kDecPart]:
+// the eight lane groups of each of the four statistics waves (swave 0..3)
+// merged (lower group first), then the four waves in order through ws. Every
+// thread of the workgroup calls it (active: the lane belongs to a statistics
+// wave); ends with the partials written (no trailing barrier).
+template <int NR>
+__device__ __forceinline__ void stats_finish(StatsLane<NR>& L, float (*ws)[NR][kDecPart], float* out, int lane,
+                                             int swave, bool active) {
+  const int li = lane & 7, grp = lane >> 3;
+  const int wave = swave;
+  if (active) {
+    // state relative to m: R = R' / estar, A = acc / estar (estar = 2^{m - mref} >= 2^-8... > 0)
+    OnState st[NR];
+  #pragma unroll
+    for (int r = 0; r < NR; ++r) {
+      const float inv = L.m[r] == -INFINITY ? 0.f : 1.0f / L.estar[r];
+      st[r] = OnState{L.m[r], L.Rp[r] * inv, L.jst[r]};
+  #pragma unroll
+      for (int i = 0; i < 16; ++i) L.acc[r][i] *= inv;
+    }
+  #pragma unroll
+    for (int r = 0; r < NR; ++r) {
+  #pragma unroll
+      for (int o = 8; o < 64; o <<= 1) {
+        OnState s2{__shfl_xor(st[r].m, o, 64), __shfl_xor(st[r].R, o, 64), __shfl_xor(st[r].j, o, 64)};
+        float a2[16];
+  #pragma unroll
+        for (int i = 0; i < 16; ++i) a2[i] = __shfl_xor(L.acc[r][i], o, 64);
+        if (lane & o) {
+          OnState s1 = s2;
+          float a1[16];
+  #pragma unroll
+          for (int i = 0; i < 16; ++i) a1[i] = a2[i];
+          on_merge<16>(s1, a1, st[r], L.acc[r]);
+          st[r] = s1;
+  #pragma unroll
+          for (int i = 0; i < 16; ++i) L.acc[r][i] = a1[i];
+        } else {
+          on_merge<16>(st[r], L.acc[r], s2, a2);
+        }
+      }
+    }
+    // then the four waves, in wave order; dims of lane li: 8 li + (0..7), 64 + 8 li + (0..7)
+    if (grp == 0) {
+  #pragma unroll
+      for (int r = 0; r < NR; ++r) {
+  #pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          ws[wave][r][8 * li + i] = L.acc[r][i];
+          ws[wave][r][64 + 8 * li + i] = L.acc[r][8 + i];
+        }
+        if (li == 0) {
+          ws[wave][r][HD] = st[r].m;
+          ws[wave][r][HD + 1] = st[r].R;
+          ws[wave][r][HD + 2] = __int_as_float(st[r].j);
+        }
       }
     }
   }
   __syncthreads();
-  if (wave == 0 && grp == 0) {
+  if (active && wave == 0 && grp == 0) {
 #pragma unroll
     for (int r = 0; r < NR; ++r) {
       OnState s1{ws[0][r][HD], ws[0][r][HD + 1], __float_as_int(ws[0][r][HD + 2])};
@@ -416,7 +407,7 @@ __global__ __launch_bounds__(256) void k_dec_stats(StatsArgs A) {
         }
         on_merge<16>(s1, a1, s2, a2);
       }
-      float* o = A.part + (((size_t)chunk * A.Hkv + g) * A.G + A.r0 + r) * kDecPart;
+      float* o = out + (size_t)r * kDecPart;
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
         o[8 * li + i] = a1[i];
@@ -431,6 +422,73 @@ __global__ __launch_bounds__(256) void k_dec_stats(StatsArgs A) {
   }
 }
 
+// Per (token chunk, KV head): 8 lanes per token (lane l%8 holds dims
+// 8(l%8) .. +7 and 64 + 8(l%8) .. +7, so each load instruction reads 8 token
+// rows x 128 contiguous bytes), rows held in registers (StatsLane); the eight
+// lane groups and four waves are then merged into one partial per row,
+// relative to m.
+template <int NR>
+__global__ __launch_bounds__(256) void k_dec_stats(StatsArgs A) {
+  const int chunk = blockIdx.x, g = blockIdx.y;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int li = lane & 7, grp = lane >> 3;
+  constexpr int U = NR <= 2 ? 4 : (NR <= 4 ? 2 : 1);  // 32-token groups per round of loads (two rounds in flight)
+  const int64_t t0 = (int64_t)chunk * kStatsTok;
+  int64_t t1 = t0 + kStatsTok;
+  if (t1 > A.n) t1 = A.n;
+  StatsLane<NR> L;
+  stats_begin<NR>(L, A.qn, g, A.G, A.r0, li);
+  const char* kc = (const char*)(A.k + ((size_t)g * A.n_max + t0) * HD);
+  const char* vc = (const char*)(A.v + ((size_t)g * A.n_max + t0) * HD);
+  const int nt = (int)(t1 - t0);
+  const int lo = wave * 8 + grp;  // this lane group's token within each group of 32
+  auto load = [&](int tb, uint4 (&k0)[U], uint4 (&k1)[U], uint4 (&v0)[U], uint4 (&v1)[U]) {
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      int tr = tb + 32 * u + lo;
+      tr = tr < nt ? tr : nt - 1;
+      const uint32_t off = (uint32_t)tr * (HD * 2) + 16u * (uint32_t)li;
+      k0[u] = *(const uint4*)(kc + off);
+      k1[u] = *(const uint4*)(kc + off + 128);
+      v0[u] = *(const uint4*)(vc + off);
+      v1[u] = *(const uint4*)(vc + off + 128);
+    }
+  };
+  auto process = [&](int tb, const uint4 (&k0)[U], const uint4 (&k1)[U], const uint4 (&v0)[U],
+                     const uint4 (&v1)[U]) {
+    uint32_t kw[U][8], vw[U][8];
+    bool ok[U];
+    int tok[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int tl = tb + 32 * u + lo;
+      ok[u] = tl < nt;
+      tok[u] = (int)(t0 + tl);
+      const uint4 a0 = k0[u], a1 = k1[u], b0 = v0[u], b1 = v1[u];
+      kw[u][0] = a0.x; kw[u][1] = a0.y; kw[u][2] = a0.z; kw[u][3] = a0.w;
+      kw[u][4] = a1.x; kw[u][5] = a1.y; kw[u][6] = a1.z; kw[u][7] = a1.w;
+      vw[u][0] = b0.x; vw[u][1] = b0.y; vw[u][2] = b0.z; vw[u][3] = b0.w;
+      vw[u][4] = b1.x; vw[u][5] = b1.y; vw[u][6] = b1.z; vw[u][7] = b1.w;
+    }
+    stats_tokens<NR, U>(L, kw, vw, ok, tok, A.c2);
+  };
+  constexpr int kRound = 32 * U;
+  uint4 ka0[U], ka1[U], va0[U], va1[U], kb0[U], kb1[U], vb0[U], vb1[U];
+  int tb = 0;
+  if (tb < nt) load(tb, ka0, ka1, va0, va1);
+  while (tb < nt) {
+    if (tb + kRound < nt) load(tb + kRound, kb0, kb1, vb0, vb1);
+    process(tb, ka0, ka1, va0, va1);
+    tb += kRound;
+    if (tb >= nt) break;
+    if (tb + kRound < nt) load(tb + kRound, ka0, ka1, va0, va1);
+    process(tb, kb0, kb1, vb0, vb1);
+    tb += kRound;
+  }
+  __shared__ float ws[4][NR][kDecPart];
+  stats_finish<NR>(L, ws, A.part + (((size_t)chunk * A.Hkv + g) * A.G + A.r0) * kDecPart, lane, wave, true);
+}
+
 struct DMergeArgs {
   const float* part;
   const uint16_t* qn;
@@ -440,6 +498,8 @@ struct DMergeArgs {
   int64_t n, n_max;
   int G, Hkv, w, nch;
   int32_t* status;
+  int64_t* pend;  // [2], see ContribArgs
+  int deferred;   // 1: the new rows' terms are left pending (single-pass step)
 };
 
 // One block per KV head, one wave per new row: the chunk partials merged
@@ -534,6 +594,16 @@ __global__ __launch_bounds__(1024) void k_dec_merge(DMergeArgs A) {
     derive_row(A.T, r, m_nat, L, lane);
   }
   __syncthreads();
+  if (threadIdx.x == 0 && g == 0) {
+    // pending rows: a single-pass step leaves the new position's terms
+    // pending; a two-pass step adds them, and any left by an earlier step
+    if (A.deferred) {
+      A.pend[0] = A.n - 1;
+    } else {
+      A.pend[1] = A.pend[0];
+      A.pend[0] = -1;
+    }
+  }
   if (threadIdx.x == 0) {
     double* S = A.S64 + (size_t)g * A.n_max;
     const double invG = 1.0 / (double)A.G;
@@ -555,22 +625,40 @@ struct ContribArgs {
   double* S64;        // [Hkv][n_max]
   int64_t n, n_max;
   int w, G;
-  int mode;           // 0: window entries e0 .. e1-1 (rows at n - w + e); 1: step (new rows +, leaving rows -)
-  int e0, e1;
+  int mode;           // which rows: see entry_of
+  int e0, e1;         // mode 0: window entries e0 .. e1 - 1
   float c2;           // log2(e) / sqrt(d)
+  const int64_t* pend;  // [2]: position whose terms are pending, position to add in this launch (-1: none)
 };
 
-// Row rr of this launch's list (per KV head): entry e = rr / G, query head rr % G.
-__device__ __forceinline__ void entry_of(const ContribArgs& A, int e, int64_t& pos, float& sign) {
+// The launch's row list, per KV head: entry e holds the G query rows of one
+// position. Mode 0 (a whole window): positions n - w + e for e in [e0, e1), +.
+// Mode 1 (step): n - 1 (+), n - 1 - w (-), then pend[1] (+) if there is one.
+// Mode 2 (flush): pend[1] (+) if there is one. Mode 3 (single-pass step):
+// n - 1 - w (-), then pend[0] (+) if there is one. pp is the mode's pending
+// position (read once per thread); one outside the rows the ring still holds
+// (positions n - 1 - w .. n - 1) counts as none, so a state used before its
+// init cannot send the row lookups out of the table.
+__device__ __forceinline__ int64_t pending_of(const ContribArgs& A) {
+  const int64_t pp = (A.mode == 1 || A.mode == 2) ? A.pend[1] : (A.mode == 3 ? A.pend[0] : -1);
+  return (pp >= A.n - 1 - A.w && pp < A.n) ? pp : -1;
+}
+__device__ __forceinline__ int entry_count(const ContribArgs& A, int64_t pp) {
+  const int has = pp >= 0 ? 1 : 0;
+  return A.mode == 0 ? A.e1 - A.e0 : (A.mode == 1 ? 2 + has : (A.mode == 2 ? has : 1 + has));
+}
+__device__ __forceinline__ void entry_of(const ContribArgs& A, int64_t pp, int e, int64_t& pos, float& sign) {
+  sign = 1.0f;
   if (A.mode == 0) {
-    pos = A.n - A.w + e;
-    sign = 1.0f;
-  } else if (e == 0) {
-    pos = A.n - 1;
-    sign = 1.0f;
+    pos = A.n - A.w + A.e0 + e;
+  } else if (A.mode == 1) {
+    pos = e == 0 ? A.n - 1 : (e == 1 ? A.n - 1 - A.w : pp);
+    sign = e == 1 ? -1.0f : 1.0f;
+  } else if (A.mode == 2) {
+    pos = pp;
   } else {
-    pos = A.n - 1 - A.w;
-    sign = -1.0f;
+    pos = e == 0 ? A.n - 1 - A.w : pp;
+    sign = e == 0 ? -1.0f : 1.0f;
   }
 }
 
@@ -607,64 +695,192 @@ __device__ __forceinline__ double rows4_sum(double x) {
          __longlong_as_double((long long)(((uint64_t)hi2[1] << 32) | lo2[1]));
 }
 
-// Per (chunk of kTokPerWg tokens, KV head): each wave takes 16-token
-// subtiles; per subtile and 16-row block X = Q K^T and C = a V^T - ||a||^2/2
-// on MFMA, then per (row, token) the term r^2 ||a - v_j||^2 with
-// r = p / (1 - p), for tokens the row sees other than its kept argmax,
-// summed with the row's sign in fp64 and added to the score. Every element's
-// value depends only on its row's stored state and its token, whatever else
-// shares the block, so a row's terms are the same in every launch.
+// A launch's rows in LDS: exponent bias, C's start value, sign, position,
+// kept argmax and slot per row, and the query and a operands (rows padded to
+// 272 bytes, so 16 rows read at one column hit distinct banks). Reading the
+// operands from global memory inside the token loop would wait for the loads
+// of the next subtiles too (vector loads complete in order).
 template <int ROWS>
-__global__ __launch_bounds__(256) void k_dec_contrib(ContribArgs A) {
-  const int chunk = blockIdx.x, g = blockIdx.y;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int q4 = lane >> 4, l16 = lane & 15;
-  const int nrows = (A.e1 - A.e0) * A.G;
+struct ContribLds {
+  float bias[ROWS], cinit[ROWS], sign[ROWS];
+  int pos[ROWS], js[ROWS];
+  int64_t row[ROWS];
+  uint16_t op[2 * ROWS][kOpStride];
+};
+
+// Fill L with the launch's rows of KV head g (padding rows up to a multiple of
+// 16: p = 0); returns the number of 16-row blocks. Called by every thread;
+// ends with a barrier.
+template <int ROWS>
+__device__ __forceinline__ int contrib_stage(const ContribArgs& A, ContribLds<ROWS>& L, int g) {
+  const int64_t pp = pending_of(A);
+  const int nrows = entry_count(A, pp) * A.G;
   const int nb = (nrows + 15) / 16;
-  __shared__ __attribute__((aligned(16))) float s_bias[ROWS];
-  __shared__ __attribute__((aligned(16))) float s_cinit[ROWS];
-  __shared__ __attribute__((aligned(16))) float s_sign[ROWS];
-  __shared__ __attribute__((aligned(16))) int s_pos[ROWS];
-  __shared__ __attribute__((aligned(16))) int s_js[ROWS];
-  __shared__ int64_t s_row[ROWS];
-  // per-token sums of this chunk, added to the score once every subtile is done
-  // (a read-modify-write per subtile would wait for the prefetched loads too)
-  __shared__ double s_tot[kTokPerWg];
-  // the rows' query and a operands, staged in LDS (rows padded to 272 bytes,
-  // so 16 rows read at one column hit distinct banks): reading them from
-  // global memory here would wait for the loads of the next subtiles too
-  // (vector loads complete in order)
-  __shared__ __attribute__((aligned(16))) uint16_t s_op[2 * ROWS][kOpStride];
   for (int rr = threadIdx.x; rr < nb * 16; rr += blockDim.x) {
     if (rr < nrows) {
       int64_t pos;
       float sign;
-      entry_of(A, A.e0 + rr / A.G, pos, sign);
+      entry_of(A, pp, rr / A.G, pos, sign);
       const int64_t r = trow(g, pos, rr % A.G, A.w, A.G);
-      s_row[rr] = r;
-      s_bias[rr] = A.T.bias[r];
-      s_cinit[rr] = A.T.cinit[r];
-      s_sign[rr] = sign;
-      s_pos[rr] = (int)pos;
-      s_js[rr] = A.T.jstar[r];
-    } else {  // padding rows: p = 0
-      s_row[rr] = -1;
-      s_bias[rr] = INFINITY;
-      s_cinit[rr] = 0.f;
-      s_sign[rr] = 0.f;
-      s_pos[rr] = -1;
-      s_js[rr] = -1;
+      L.row[rr] = r;
+      L.bias[rr] = A.T.bias[r];
+      L.cinit[rr] = A.T.cinit[r];
+      L.sign[rr] = sign;
+      L.pos[rr] = (int)pos;
+      L.js[rr] = A.T.jstar[r];
+    } else {
+      L.row[rr] = -1;
+      L.bias[rr] = INFINITY;
+      L.cinit[rr] = 0.f;
+      L.sign[rr] = 0.f;
+      L.pos[rr] = -1;
+      L.js[rr] = -1;
     }
   }
   __syncthreads();
   for (int i = threadIdx.x; i < nb * 16 * 32; i += blockDim.x) {
     const int rr = i >> 5, c = i & 31;  // 32 chunks of 16 bytes: q then a_bf
-    const int64_t r = s_row[rr];
+    const int64_t r = L.row[rr];
     uint4 u = make_uint4(0, 0, 0, 0);
     if (r >= 0) u = *(const uint4*)((const char*)((c < 16 ? A.T.q : A.T.a_bf) + r * HD) + 16 * (c & 15));
-    *(uint4*)((char*)&s_op[(c < 16 ? 0 : ROWS) + rr][0] + 16 * (c & 15)) = u;
+    *(uint4*)((char*)&L.op[(c < 16 ? 0 : ROWS) + rr][0] + 16 * (c & 15)) = u;
   }
   __syncthreads();
+  return nb;
+}
+
+// One 16-row block as a lane holds it: the query and a operands of row l%16
+// and C's start value, exponent bias, sign, position and kept argmax of its
+// four rows 4 (l/16) + i.
+struct BlockRegs {
+  bf16x8 qa[4], aa[4];
+  float cinit[4], bias[4], sign[4];
+  int pos[4], js[4];
+};
+
+// ||v_j||^2 of this lane's token: exact bf16 squares, fp32 sums over the
+// lane's 32 dims, then over the token's four lanes (same order in each).
+__device__ __forceinline__ float token_vnorm(const bf16x8 (&vb)[4]) {
+  float n0 = 0.f, n1 = 0.f;
+#pragma unroll
+  for (int ks = 0; ks < 4; ++ks) {
+    const bf16x2 p0 = {vb[ks][0], vb[ks][1]}, p1 = {vb[ks][2], vb[ks][3]};
+    const bf16x2 p2 = {vb[ks][4], vb[ks][5]}, p3 = {vb[ks][6], vb[ks][7]};
+    n0 = __builtin_amdgcn_fdot2_f32_bf16(p0, p0, n0, false);
+    n1 = __builtin_amdgcn_fdot2_f32_bf16(p1, p1, n1, false);
+    n0 = __builtin_amdgcn_fdot2_f32_bf16(p2, p2, n0, false);
+    n1 = __builtin_amdgcn_fdot2_f32_bf16(p3, p3, n1, false);
+  }
+  return rows4_sum(n0 + n1);
+}
+
+// The signed terms of one block for this lane's token tok (row l%16 of a
+// 16-token subtile), added to acc in row order: X = Q K^T and
+// C = a V^T - ||a||^2/2 on MFMA, then per (row, token) r^2 ||a - v_j||^2 with
+// r = p / (1 - p), for tokens the row sees other than its kept argmax. Every
+// element's value depends only on its row's stored state and its token,
+// whatever else shares the block or the launch, so a row's terms are the same
+// bit for bit in every kernel that uses this.
+__device__ __forceinline__ void block_terms(const BlockRegs& B, const bf16x8 (&kb)[4], const bf16x8 (&vb)[4],
+                                            float nvj, int tok, float c2, double& acc) {
+  f32x4 X = {}, C = {B.cinit[0], B.cinit[1], B.cinit[2], B.cinit[3]};
+#pragma unroll
+  for (int ks = 0; ks < 4; ++ks) X = mfma16(B.qa[ks], kb[ks], X);
+#pragma unroll
+  for (int ks = 0; ks < 4; ++ks) C = mfma16(B.aa[ks], vb[ks], C);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    // branch-free: tokens the row does not see, and its kept argmax, get 0
+    const float p = __builtin_amdgcn_exp2f(fmaf(X[i], c2, -B.bias[i]));
+    const float rr = p * __builtin_amdgcn_rcpf(1.0f - p);
+    const float c = rr * rr * fmaxf(fmaf(-2.0f, C[i], nvj), 0.0f);
+    acc += (double)((tok <= B.pos[i] && tok != B.js[i]) ? B.sign[i] * c : 0.0f);
+  }
+}
+
+// The signed terms of token tok over the staged rows, summed in fp64 in a
+// fixed order (blocks, then rows); the sum is returned in all four lanes of
+// the token.
+template <int ROWS>
+__device__ __forceinline__ double contrib_token(const ContribLds<ROWS>& L, int nb, const bf16x8 (&kb)[4],
+                                                const bf16x8 (&vb)[4], int tok, int lane, float c2) {
+  const int q4 = lane >> 4, l16 = lane & 15;
+  const float nvj = token_vnorm(vb);
+  double acc = 0.0;
+  for (int b = 0; b < nb; ++b) {
+    BlockRegs B;
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      B.qa[ks] = *(const bf16x8*)((const char*)&L.op[16 * b + l16][0] + opoff(lane, ks));
+      B.aa[ks] = *(const bf16x8*)((const char*)&L.op[ROWS + 16 * b + l16][0] + opoff(lane, ks));
+    }
+    const int base = 16 * b + 4 * q4;  // this lane's four rows
+    const float4 c4 = *(const float4*)(&L.cinit[base]);
+    const float4 bi = *(const float4*)(&L.bias[base]);
+    const float4 sg = *(const float4*)(&L.sign[base]);
+    const int4 ps = *(const int4*)(&L.pos[base]);
+    const int4 js = *(const int4*)(&L.js[base]);
+    B.cinit[0] = c4.x; B.cinit[1] = c4.y; B.cinit[2] = c4.z; B.cinit[3] = c4.w;
+    B.bias[0] = bi.x; B.bias[1] = bi.y; B.bias[2] = bi.z; B.bias[3] = bi.w;
+    B.sign[0] = sg.x; B.sign[1] = sg.y; B.sign[2] = sg.z; B.sign[3] = sg.w;
+    B.pos[0] = ps.x; B.pos[1] = ps.y; B.pos[2] = ps.z; B.pos[3] = ps.w;
+    B.js[0] = js.x; B.js[1] = js.y; B.js[2] = js.z; B.js[3] = js.w;
+    block_terms(B, kb, vb, nvj, tok, c2, acc);
+  }
+  return rows4_sum(acc);
+}
+
+// The first 16 rows of a launch's list straight into registers (for a list
+// of at most 16 rows; padding rows as contrib_stage makes them).
+__device__ __forceinline__ void load_block_regs(const ContribArgs& A, int g, int lane, BlockRegs& B) {
+  const int64_t pp = pending_of(A);
+  const int nrows = entry_count(A, pp) * A.G;
+  auto locate = [&](int rr, int64_t& r, int64_t& pos, float& sign) {
+    if (rr >= nrows) return false;
+    entry_of(A, pp, rr / A.G, pos, sign);
+    r = trow(g, pos, rr % A.G, A.w, A.G);
+    return true;
+  };
+  int64_t r, pos;
+  float sign;
+  const bool ok = locate(lane & 15, r, pos, sign);
+#pragma unroll
+  for (int ks = 0; ks < 4; ++ks) {
+    B.qa[ks] = ok ? *(const bf16x8*)((const char*)(A.T.q + r * HD) + opoff(lane, ks)) : bf16x8{};
+    B.aa[ks] = ok ? *(const bf16x8*)((const char*)(A.T.a_bf + r * HD) + opoff(lane, ks)) : bf16x8{};
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    if (locate(4 * (lane >> 4) + i, r, pos, sign)) {
+      B.cinit[i] = A.T.cinit[r];
+      B.bias[i] = A.T.bias[r];
+      B.sign[i] = sign;
+      B.pos[i] = (int)pos;
+      B.js[i] = A.T.jstar[r];
+    } else {
+      B.cinit[i] = 0.f;
+      B.bias[i] = INFINITY;
+      B.sign[i] = 0.f;
+      B.pos[i] = -1;
+      B.js[i] = -1;
+    }
+  }
+}
+
+// Per (chunk of kTokPerWg tokens, KV head): each wave takes 16-token
+// subtiles (wave, wave + 4, ...) with K and V read straight into the MFMA
+// operands, the next two subtiles' loads in flight while one is processed.
+template <int ROWS>
+__global__ __launch_bounds__(256) void k_dec_contrib(ContribArgs A) {
+  const int chunk = blockIdx.x, g = blockIdx.y;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int q4 = lane >> 4, l16 = lane & 15;
+  __shared__ __attribute__((aligned(16))) ContribLds<ROWS> cl;
+  // per-token sums of this chunk, added to the score once every subtile is done
+  // (a read-modify-write per subtile would wait for the prefetched loads too)
+  __shared__ double s_tot[kTokPerWg];
+  const int nb = contrib_stage<ROWS>(A, cl, g);
+  if (nb == 0) return;
   const int64_t t0 = (int64_t)chunk * kTokPerWg;
   const double invG = 1.0 / (double)A.G;
   double* S = A.S64 + (size_t)g * A.n_max;
@@ -686,55 +902,9 @@ __global__ __launch_bounds__(256) void k_dec_contrib(ContribArgs A) {
     }
   };
   auto process = [&](int sub, const bf16x8 (&kb)[4], const bf16x8 (&vb)[4]) {
-    const int tok = (int)t0 + sub * 16 + l16;
-    // ||v_j||^2: exact bf16 squares, fp32 sums over this lane's 32 dims, then the token's four lanes
-    float n0 = 0.f, n1 = 0.f;
-#pragma unroll
-    for (int ks = 0; ks < 4; ++ks) {
-      const bf16x2 p0 = {vb[ks][0], vb[ks][1]}, p1 = {vb[ks][2], vb[ks][3]};
-      const bf16x2 p2 = {vb[ks][4], vb[ks][5]}, p3 = {vb[ks][6], vb[ks][7]};
-      n0 = __builtin_amdgcn_fdot2_f32_bf16(p0, p0, n0, false);
-      n1 = __builtin_amdgcn_fdot2_f32_bf16(p1, p1, n1, false);
-      n0 = __builtin_amdgcn_fdot2_f32_bf16(p2, p2, n0, false);
-      n1 = __builtin_amdgcn_fdot2_f32_bf16(p3, p3, n1, false);
-    }
-    const float nvj = rows4_sum(n0 + n1);
-    double acc = 0.0;
-    for (int b = 0; b < nb; ++b) {
-      // the block's query and a operands
-      bf16x8 qa[4], aa[4];
-#pragma unroll
-      for (int ks = 0; ks < 4; ++ks) {
-        qa[ks] = *(const bf16x8*)((const char*)&s_op[16 * b + l16][0] + opoff(lane, ks));
-        aa[ks] = *(const bf16x8*)((const char*)&s_op[ROWS + 16 * b + l16][0] + opoff(lane, ks));
-      }
-      const int base = 16 * b + 4 * q4;  // this lane's four rows
-      const float4 c4 = *(const float4*)(&s_cinit[base]);
-      f32x4 X = {}, C = {c4.x, c4.y, c4.z, c4.w};
-#pragma unroll
-      for (int ks = 0; ks < 4; ++ks) X = mfma16(qa[ks], kb[ks], X);
-#pragma unroll
-      for (int ks = 0; ks < 4; ++ks) C = mfma16(aa[ks], vb[ks], C);
-      const float4 bi = *(const float4*)(&s_bias[base]);
-      const float4 sg = *(const float4*)(&s_sign[base]);
-      const int4 ps = *(const int4*)(&s_pos[base]);
-      const int4 js = *(const int4*)(&s_js[base]);
-      const float bv[4] = {bi.x, bi.y, bi.z, bi.w}, sv[4] = {sg.x, sg.y, sg.z, sg.w};
-      const int pv[4] = {ps.x, ps.y, ps.z, ps.w}, jv[4] = {js.x, js.y, js.z, js.w};
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        // branch-free: tokens the row does not see, and its kept argmax, get 0
-        const float p = __builtin_amdgcn_exp2f(fmaf(X[i], A.c2, -bv[i]));
-        const float rr = p * __builtin_amdgcn_rcpf(1.0f - p);
-        const float c = rr * rr * fmaxf(fmaf(-2.0f, C[i], nvj), 0.0f);
-        acc += (double)((tok <= pv[i] && tok != jv[i]) ? sv[i] * c : 0.0f);
-      }
-    }
-    const double total = rows4_sum(acc);
+    const double total = contrib_token<ROWS>(cl, nb, kb, vb, (int)t0 + sub * 16 + l16, lane, A.c2);
     if (q4 == 0) s_tot[sub * 16 + l16] = total;
   };
-  // subtiles wave, wave + 4, ...: the next two subtiles' K and V are in
-  // flight while one is processed (three register buffers in rotation)
   bf16x8 kb[3][4], vb[3][4];
   int sub = wave;
   if (valid(sub)) load_kv(sub, kb[0], vb[0]);
@@ -757,13 +927,248 @@ __global__ __launch_bounds__(256) void k_dec_contrib(ContribArgs A) {
   for (int i = threadIdx.x; i < nt; i += blockDim.x) S[t0 + i] += s_tot[i] * invG;
 }
 
-__global__ void k_dec_zero(double* p, int64_t count) {
-  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (i < count) p[i] = 0.0;
+// ---------------------------------------------------------------------------- single-pass step
+
+typedef __attribute__((address_space(3))) void lds_void;
+typedef __attribute__((address_space(1))) const void gbl_cvoid;
+
+constexpr int kTileTok = 64;                    // tokens per LDS tile
+constexpr int kTileBytes = kTileTok * HD * 2;   // 16 KiB per tensor
+constexpr int kFusedRows = 16;                  // staged rows: leaving G + pending G (G <= 8)
+constexpr int kTileBufs = 4;                    // LDS tile buffers: three tiles in flight
+
+// Chunk permutation of token row t inside a tile: a bijection on t mod 16, so
+// the 16 rows of a subtile read at one logical column hit 16 distinct 16-byte
+// bank groups.
+__device__ __forceinline__ int tswz(int t) { return ((t & 3) << 2) | ((t >> 2) & 3); }
+
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
 }
 
-__global__ void k_dec_tof32(const double* S64, float* out, int64_t n, int64_t n_max, int Hkv) {
+// Workgroup barrier ordering LDS traffic only (tile loads still in flight are
+// waited for with wait_vmcnt first).
+__device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
+// Direct-to-LDS loads of token rows [tok0, tok0 + 64) of one head (rows at or
+// past n repeat row n - 1; consumers mask them): wave instruction i = wave + 4 j
+// fills tile bytes 1024 i .. +1023, lane l the 16-byte chunk (l % 16) of row
+// 4 i + l / 16 with the row's logical chunk (l % 16) ^ tswz(row).
+__device__ __forceinline__ void dec_issue_tile(const uint16_t* head, int64_t tok0, int64_t n, char* lds, int wave,
+                                               int lane) {
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int inst = wave + 4 * j;
+    const int row = inst * 4 + (lane >> 4);
+    const int c = (lane & 15) ^ tswz(row);
+    int64_t tok = tok0 + row;
+    if (tok >= n) tok = n - 1;
+    __builtin_amdgcn_global_load_lds((gbl_cvoid*)(head + tok * HD + c * 8), (lds_void*)(lds + inst * 1024), 16, 0, 0);
+  }
+}
+
+// The statistics share of one 64-token LDS tile for lane group (swave, grp):
+// tokens 32 u + 8 swave + grp, u = 0, 1 (the token order of k_dec_stats).
+template <int NR>
+__device__ __forceinline__ void stats_tile(StatsLane<NR>& L, const char* kt, const char* vt, int swave, int grp,
+                                           int li, int t, int64_t t0, int nt, float c2) {
+  uint32_t kw[2][8], vw[2][8];
+  bool ok[2];
+  int tok[2];
+#pragma unroll
+  for (int u = 0; u < 2; ++u) {
+    const int row = 32 * u + swave * 8 + grp;
+    const int tl = t * kTileTok + row;
+    ok[u] = tl < nt;
+    tok[u] = (int)(t0 + tl);
+    const int o0 = row * 256 + ((li ^ tswz(row)) << 4), o1 = row * 256 + (((8 + li) ^ tswz(row)) << 4);
+    const uint4 k0 = *(const uint4*)(kt + o0), k1 = *(const uint4*)(kt + o1);
+    const uint4 v0 = *(const uint4*)(vt + o0), v1 = *(const uint4*)(vt + o1);
+    kw[u][0] = k0.x; kw[u][1] = k0.y; kw[u][2] = k0.z; kw[u][3] = k0.w;
+    kw[u][4] = k1.x; kw[u][5] = k1.y; kw[u][6] = k1.z; kw[u][7] = k1.w;
+    vw[u][0] = v0.x; vw[u][1] = v0.y; vw[u][2] = v0.z; vw[u][3] = v0.w;
+    vw[u][4] = v1.x; vw[u][5] = v1.y; vw[u][6] = v1.z; vw[u][7] = v1.w;
+  }
+  stats_tokens<NR, 2>(L, kw, vw, ok, tok, c2);
+}
+
+struct FusedArgs {
+  StatsArgs s;    // the new position's rows (r0 = 0, nr = G)
+  ContribArgs c;  // mode 3: leaving rows and the pending rows
+};
+
+// One step in one pass over K and V (per chunk of kStatsTok tokens, KV head):
+// 64-token tiles of K and V land in LDS (four buffers, three tiles in flight);
+// per tile every lane group takes two tokens of the new rows' statistics
+// (StatsLane, as k_dec_stats) and every wave one 16-token subtile of terms of
+// the leaving rows (-) and of the rows whose terms the previous step left
+// pending (+) (contrib_token, as k_dec_contrib). The new rows' terms need
+// their full statistics, so they stay pending until the next step or a flush.
+template <int NR>
+__global__ __launch_bounds__(256) void k_dec_fused(FusedArgs F) {
+  const int chunk = blockIdx.x, g = blockIdx.y;
+  const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int li = lane & 7, grp = lane >> 3, q4 = lane >> 4, l16 = lane & 15;
+  __shared__ __attribute__((aligned(1024))) char kbuf[kTileBufs][kTileBytes];
+  __shared__ __attribute__((aligned(1024))) char vbuf[kTileBufs][kTileBytes];
+  __shared__ __attribute__((aligned(16))) ContribLds<kFusedRows> cl;
+  __shared__ double s_tot[kStatsTok];
+  static_assert(4 * NR * kDecPart * sizeof(float) <= sizeof(kbuf), "stats merge space");
+  const int nb = contrib_stage<kFusedRows>(F.c, cl, g);
+  StatsLane<NR> L;
+  stats_begin<NR>(L, F.s.qn, g, F.s.G, 0, li);
+  const int64_t n = F.s.n;
+  const int64_t t0 = (int64_t)chunk * kStatsTok;
+  const int nt = (int)((n - t0) < kStatsTok ? (n - t0) : kStatsTok);
+  const int ntiles = (nt + kTileTok - 1) / kTileTok;
+  const uint16_t* kh = F.s.k + (size_t)g * F.s.n_max * HD;
+  const uint16_t* vh = F.s.v + (size_t)g * F.s.n_max * HD;
+  const float c2 = F.s.c2;
+  for (int t = 0; t < kTileBufs - 1 && t < ntiles; ++t) {
+    dec_issue_tile(kh, t0 + (int64_t)t * kTileTok, n, kbuf[t], wave, lane);
+    dec_issue_tile(vh, t0 + (int64_t)t * kTileTok, n, vbuf[t], wave, lane);
+  }
+  for (int t = 0; t < ntiles; ++t) {
+    // per wave 8 loads per tile, in issue order: the loads of the (at most
+    // two) later tiles in flight may be outstanding once tile t has landed
+    if (t + 2 < ntiles) wait_vmcnt<16>(); else if (t + 1 < ntiles) wait_vmcnt<8>(); else wait_vmcnt<0>();
+    lds_barrier();  // tile t visible to every wave; tile t - 1's buffers are free
+    if (t + 3 < ntiles) {
+      const int b3 = (t + 3) % kTileBufs;
+      dec_issue_tile(kh, t0 + (int64_t)(t + 3) * kTileTok, n, kbuf[b3], wave, lane);
+      dec_issue_tile(vh, t0 + (int64_t)(t + 3) * kTileTok, n, vbuf[b3], wave, lane);
+    }
+    const char* kt = kbuf[t % kTileBufs];
+    const char* vt = vbuf[t % kTileBufs];
+    stats_tile<NR>(L, kt, vt, wave, grp, li, t, t0, nt, c2);
+    {
+      const int row = 16 * wave + l16;
+      bf16x8 kb[4], vb[4];
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) {
+        const int o = row * 256 + (((4 * ks + q4) ^ tswz(row)) << 4);
+        kb[ks] = *(const bf16x8*)(kt + o);
+        vb[ks] = *(const bf16x8*)(vt + o);
+      }
+      const double total = contrib_token<kFusedRows>(cl, nb, kb, vb, (int)t0 + t * kTileTok + row, lane, c2);
+      if (q4 == 0) s_tot[t * kTileTok + row] = total;
+    }
+  }
+  lds_barrier();  // every wave is done with the tiles: their space takes the stats merge
+  stats_finish<NR>(L, reinterpret_cast<float (*)[NR][kDecPart]>(&kbuf[0][0]),
+                   F.s.part + (((size_t)chunk * F.s.Hkv + g) * F.s.G) * kDecPart, lane, wave, true);
+  double* S = F.c.S64 + (size_t)g * F.c.n_max;
+  const double invG = 1.0 / (double)F.c.G;
+  for (int i = threadIdx.x; i < nt; i += blockDim.x) S[t0 + i] += s_tot[i] * invG;
+}
+
+// Rebuild: the score cleared; nothing stays pending (the rebuild scores every window row).
+// The single-pass step with eight waves (two per SIMD), for at most four
+// rows per position (the register budget of 512 threads; the leaving and
+// pending rows then make one 16-row block, held in registers). Waves 4-7
+// load the 64-token tiles into LDS (five buffers, all of LDS: four tiles in
+// flight) and take the new rows' statistics (two tokens per lane group and
+// tile, in the token order of k_dec_stats); waves 0-3 take the terms of one
+// 16-token subtile each and add them to the score with fp64 atomic adds (one
+// per token and launch, so the order does not matter), so they never wait
+// for tile loads of their own and each SIMD interleaves an MFMA-heavy and a
+// VALU-heavy wave.
+template <int NR>
+__global__ __launch_bounds__(512) void k_dec_fused8(FusedArgs F) {
+  static_assert(NR <= 4, "register budget");
+  constexpr int NB = 5;
+  const int chunk = blockIdx.x, g = blockIdx.y;
+  const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int li = lane & 7, grp = lane >> 3, l16 = lane & 15, q4 = lane >> 4;
+  const bool stats_wave = wave >= 4;
+  const int swave = wave & 3;
+  __shared__ __attribute__((aligned(1024))) char kbuf[NB][kTileBytes];
+  __shared__ __attribute__((aligned(1024))) char vbuf[NB][kTileBytes];
+  static_assert(4 * NR * kDecPart * sizeof(float) <= sizeof(kbuf), "stats merge space");
+  BlockRegs B;
+  load_block_regs(F.c, g, lane, B);
+  StatsLane<NR> L;
+  stats_begin<NR>(L, F.s.qn, g, F.s.G, 0, li);
+  const int64_t n = F.s.n;
+  const int64_t t0 = (int64_t)chunk * kStatsTok;
+  const int nt = (int)((n - t0) < kStatsTok ? (n - t0) : kStatsTok);
+  const int ntiles = (nt + kTileTok - 1) / kTileTok;
+  const uint16_t* kh = F.s.k + (size_t)g * F.s.n_max * HD;
+  const uint16_t* vh = F.s.v + (size_t)g * F.s.n_max * HD;
+  const float c2 = F.s.c2;
+  double* S = F.c.S64 + (size_t)g * F.c.n_max;
+  const double invG = 1.0 / (double)F.c.G;
+  // tile loads, statistics waves only: per tensor 16 wave loads of 1 KiB, wave 4 + s issues s, s + 4, s + 8, s + 12
+  auto issue = [&](int64_t tok0, char* kd, char* vd) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int inst = swave + 4 * j;
+      const int row = inst * 4 + (lane >> 4);
+      const int c = (lane & 15) ^ tswz(row);
+      int64_t tok = tok0 + row;
+      if (tok >= n) tok = n - 1;
+      __builtin_amdgcn_global_load_lds((gbl_cvoid*)(kh + tok * HD + c * 8), (lds_void*)(kd + inst * 1024), 16, 0, 0);
+      __builtin_amdgcn_global_load_lds((gbl_cvoid*)(vh + tok * HD + c * 8), (lds_void*)(vd + inst * 1024), 16, 0, 0);
+    }
+  };
+  if (stats_wave)
+    for (int t = 0; t < NB - 1 && t < ntiles; ++t) issue(t0 + (int64_t)t * kTileTok, kbuf[t], vbuf[t]);
+  for (int t = 0; t < ntiles; ++t) {
+    if (stats_wave) {
+      // 8 loads per tile: the loads of the (at most three) later tiles in flight may be outstanding
+      const int ahead = ntiles - 1 - t;
+      if (ahead >= 3) wait_vmcnt<24>(); else if (ahead == 2) wait_vmcnt<16>(); else if (ahead == 1) wait_vmcnt<8>();
+      else wait_vmcnt<0>();
+    }
+    lds_barrier();  // tile t visible to every wave; tile t - 1's buffers are free
+    const char* kt = kbuf[t % NB];
+    const char* vt = vbuf[t % NB];
+    if (stats_wave) {
+      if (t + NB - 1 < ntiles) {
+        const int b = (t + NB - 1) % NB;
+        issue(t0 + (int64_t)(t + NB - 1) * kTileTok, kbuf[b], vbuf[b]);
+      }
+      stats_tile<NR>(L, kt, vt, swave, grp, li, t, t0, nt, c2);
+    } else {
+      const int row = 16 * wave + l16;
+      bf16x8 kb[4], vb[4];
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) {
+        const int o = row * 256 + (((4 * ks + q4) ^ tswz(row)) << 4);
+        kb[ks] = *(const bf16x8*)(kt + o);
+        vb[ks] = *(const bf16x8*)(vt + o);
+      }
+      const int tok = (int)t0 + t * kTileTok + row;
+      double acc = 0.0;
+      block_terms(B, kb, vb, token_vnorm(vb), tok, c2, acc);
+      const double total = rows4_sum(acc);
+      if (q4 == 0 && tok < n) atomicAdd(&S[tok], total * invG);
+    }
+  }
+  lds_barrier();  // every wave is done with the tiles: their space takes the stats merge
+  stats_finish<NR>(L, reinterpret_cast<float (*)[NR][kDecPart]>(&kbuf[0][0]),
+                   F.s.part + (((size_t)chunk * F.s.Hkv + g) * F.s.G) * kDecPart, lane, swave, stats_wave);
+}
+
+__global__ void k_dec_zero(double* p, int64_t count, int64_t* pend) {
   const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < count) p[i] = 0.0;
+  if (i == 0) pend[0] = -1;
+}
+
+// Flush: the pending position becomes the one this launch adds.
+__global__ void k_dec_pend_take(int64_t* pend) {
+  pend[1] = pend[0];
+  pend[0] = -1;
+}
+
+// The kept score to fp32; reports (when status is given) terms still pending.
+__global__ void k_dec_tof32(const double* S64, float* out, int64_t n, int64_t n_max, int Hkv, const int64_t* pend,
+                            int32_t* status) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i == 0 && status != nullptr && pend[0] >= 0) atomicOr(status, kStatusPending);
   if (i >= (int64_t)Hkv * n) return;
   const int64_t g = i / n, j = i % n;
   out[i] = (float)S64[g * n_max + j];
@@ -795,6 +1200,7 @@ DecState carve_decode_state(void* base, int64_t n_max, int32_t w, int32_t Hq, in
   S.T.bias = (float*)take(4 * rows);
   S.T.cinit = (float*)take(4 * rows);
   S.T.jstar = (int32_t*)take(4 * rows);
+  S.pend = (int64_t*)take(2 * sizeof(int64_t));
   S.nch = (int)((n_max + kStatsTok - 1) / kStatsTok);
   S.part = (float*)take(sizeof(float) * (size_t)S.nch * Hkv * G * kDecPart);
   // MFMA row statistics of the first window, sized for n_max (its buffers do
@@ -808,19 +1214,20 @@ DecState carve_decode_state(void* base, int64_t n_max, int32_t w, int32_t Hq, in
 hipError_t launch_decode_contrib(const void* k, const void* v, int64_t n, int64_t n_max, int32_t w, int G,
                                  int32_t Hkv, const DecState& S, int mode, hipStream_t st) {
   const float c2 = kLog2e / sqrtf((float)HD);
-  const int nent = mode == 0 ? w : 2;
-  // a step's 2G rows fit one small launch; a whole window takes launches of
-  // up to kInitRows rows: fewer K/V reads than 64-row launches, while two
-  // workgroups still fit a CU (256-row launches, one per CU, were slower)
-  const int per = (mode == 0 ? kInitRows : kContribRows) / G;  // window entries per launch (G <= 16)
   const dim3 grid((unsigned)((n + kTokPerWg - 1) / kTokPerWg), Hkv);
-  for (int e0 = 0; e0 < nent; e0 += per) {
-    const int e1 = e0 + per < nent ? e0 + per : nent;
-    ContribArgs a{(const uint16_t*)k, (const uint16_t*)v, S.T, S.S64, n, n_max, w, G, mode, e0, e1, c2};
-    if (mode == 0)
-      k_dec_contrib<kInitRows><<<grid, 256, 0, st>>>(a);
-    else
-      k_dec_contrib<kContribRows><<<grid, 256, 0, st>>>(a);
+  if (mode != 0) {  // a step's (at most 3G <= 48) or a flush's rows: one launch
+    ContribArgs a{(const uint16_t*)k, (const uint16_t*)v, S.T, S.S64, n, n_max, w, G, mode, 0, 0, c2, S.pend};
+    k_dec_contrib<kContribRows><<<grid, 256, 0, st>>>(a);
+    return hipGetLastError();
+  }
+  // a whole window: launches of up to kInitRows rows, fewer K/V reads than
+  // 64-row launches while two workgroups still fit a CU (256-row launches,
+  // one per CU, were slower)
+  const int per = kInitRows / G;  // window entries per launch (G <= 16)
+  for (int e0 = 0; e0 < w; e0 += per) {
+    const int e1 = e0 + per < w ? e0 + per : w;
+    ContribArgs a{(const uint16_t*)k, (const uint16_t*)v, S.T, S.S64, n, n_max, w, G, 0, e0, e1, c2, S.pend};
+    k_dec_contrib<kInitRows><<<grid, 256, 0, st>>>(a);
   }
   return hipGetLastError();
 }
@@ -834,7 +1241,7 @@ hipError_t launch_decode_init(const void* q, const void* k, const void* v, int64
   hipError_t e = launch_mfma_rowstats(q, k, v, sh, n_max, ws, st, &fold);
   if (e != hipSuccess) return e;
   const int64_t rows = (int64_t)Hq * w;
-  LoadArgs la{(const uint16_t*)q, ws.rs, S.T, S.S64, n, n_max, w, Hq, Hkv};
+  LoadArgs la{(const uint16_t*)q, ws.rs, S.T, S.S64, n, n_max, w, Hq, Hkv, S.pend};
   k_dec_load<<<(unsigned)((rows + 3) / 4), 256, 0, st>>>(la);
   StarInitArgs sa{fold, S.T, S.S64, n, n_max, w, status};
   k_dec_star_init<<<Hkv, HD, 0, st>>>(sa);
@@ -864,16 +1271,50 @@ hipError_t launch_decode_step(const void* q_new, const void* k, const void* v, i
     }
   }
   DMergeArgs ma{S.part, (const uint16_t*)q_new, (const uint16_t*)v, S.T, S.S64, n, n_max, G, Hkv, w, nch,
-                status};
+                status, S.pend, 0};
   k_dec_merge<<<Hkv, 64 * G, 0, st>>>(ma);
   return launch_decode_contrib(k, v, n, n_max, w, G, Hkv, S, 1, st);
+}
+
+hipError_t launch_decode_step_deferred(const void* q_new, const void* k, const void* v, int64_t n, int64_t n_max,
+                                       int32_t w, int32_t Hq, int32_t Hkv, const DecState& S, int32_t* status,
+                                       hipStream_t st) {
+  const int G = Hq / Hkv;
+  if (G > kRowBatch) return launch_decode_step(q_new, k, v, n, n_max, w, Hq, Hkv, S, status, st);
+  const float c2 = kLog2e / sqrtf((float)HD);
+  const int nch = (int)((n + kStatsTok - 1) / kStatsTok);
+  FusedArgs f{StatsArgs{(const uint16_t*)q_new, (const uint16_t*)k, (const uint16_t*)v, S.part, n, n_max, G, Hkv,
+                        nch, 0, G, c2},
+              ContribArgs{(const uint16_t*)k, (const uint16_t*)v, S.T, S.S64, n, n_max, w, G, 3, 0, 0, c2,
+                          S.pend}};
+  const dim3 grid(nch, Hkv);
+  switch (G) {
+    case 1: k_dec_fused8<1><<<grid, 512, 0, st>>>(f); break;
+    case 2: k_dec_fused8<2><<<grid, 512, 0, st>>>(f); break;
+    case 3: k_dec_fused8<3><<<grid, 512, 0, st>>>(f); break;
+    case 4: k_dec_fused8<4><<<grid, 512, 0, st>>>(f); break;
+    case 5: k_dec_fused<5><<<grid, 256, 0, st>>>(f); break;
+    case 6: k_dec_fused<6><<<grid, 256, 0, st>>>(f); break;
+    case 7: k_dec_fused<7><<<grid, 256, 0, st>>>(f); break;
+    default: k_dec_fused<8><<<grid, 256, 0, st>>>(f); break;
+  }
+  DMergeArgs ma{S.part, (const uint16_t*)q_new, (const uint16_t*)v, S.T, S.S64, n, n_max, G, Hkv, w, nch,
+                status, S.pend, 1};
+  k_dec_merge<<<Hkv, 64 * G, 0, st>>>(ma);
+  return hipGetLastError();
+}
+
+hipError_t launch_decode_flush(const void* k, const void* v, int64_t n, int64_t n_max, int32_t w, int32_t Hq,
+                               int32_t Hkv, const DecState& S, hipStream_t st) {
+  k_dec_pend_take<<<1, 1, 0, st>>>(S.pend);
+  return launch_decode_contrib(k, v, n, n_max, w, Hq / Hkv, Hkv, S, 2, st);
 }
 
 hipError_t launch_decode_rebuild(const void* k, const void* v, int64_t n, int64_t n_max, int32_t w, int32_t Hq,
                                  int32_t Hkv, const DecState& S, int32_t* status, hipStream_t st) {
   const int G = Hq / Hkv;
   const int64_t cnt = (int64_t)Hkv * n_max;
-  k_dec_zero<<<(unsigned)((cnt + 255) / 256), 256, 0, st>>>(S.S64, cnt);
+  k_dec_zero<<<(unsigned)((cnt + 255) / 256), 256, 0, st>>>(S.S64, cnt, S.pend);
   StarAllArgs sa{S.T, S.S64, n, n_max, w, G};
   k_dec_star_all<<<Hkv, 64, 0, st>>>(sa);
   (void)status;
@@ -881,9 +1322,9 @@ hipError_t launch_decode_rebuild(const void* k, const void* v, int64_t n, int64_
 }
 
 hipError_t launch_decode_scores(const DecState& S, int64_t n, int64_t n_max, int32_t Hkv, float* out,
-                                hipStream_t st) {
+                                int32_t* status, hipStream_t st) {
   const int64_t tot = (int64_t)Hkv * n;
-  k_dec_tof32<<<(unsigned)((tot + 255) / 256), 256, 0, st>>>(S.S64, out, n, n_max, Hkv);
+  k_dec_tof32<<<(unsigned)((tot + 255) / 256), 256, 0, st>>>(S.S64, out, n, n_max, Hkv, S.pend, status);
   return hipGetLastError();
 }
 
@@ -892,7 +1333,7 @@ hipError_t launch_decode_select(const DecState& S, int64_t n, int64_t n_max, int
                                 int32_t* status, hipStream_t st) {
   const Shape sh{n_max, w, Hq, Hkv, HD};
   Workspace ws = carve_workspace(S.ws_base, sh, true);  // S [Hkv][n] and select scratch for n <= n_max
-  hipError_t e = launch_decode_scores(S, n, n_max, Hkv, ws.S, st);
+  hipError_t e = launch_decode_scores(S, n, n_max, Hkv, ws.S, status, st);
   if (e == hipSuccess) e = launch_init(ws.status, nullptr, ws.sel, Hkv, st);
   if (e == hipSuccess)
     e = launch_select(ws.S, n, w, Hkv, pool_kernel, n_evict, out_scores, out_idx, status, nullptr, ws.sel, st);

@@ -9,7 +9,9 @@ The fp64 score kept incrementally must equal a rebuild from the stored window
 rows to fp64 rounding (the subtracted terms are bit for bit the added ones),
 re-eviction must equal the select stage on the same raw score and the oracle's
 eviction where the gap rule allows, and invalid calls / singular rows are
-reported.
+reported. The single-pass (deferred) step must give the two-pass step's score
+once its pending terms are flushed, in any mix with two-pass steps, flushes
+and rebuilds.
 """
 
 import numpy as np
@@ -149,7 +151,8 @@ def test_decode_reports_singular_new_row():
         sc.check()
 
 
-def test_decode_full_layer_sampled():
+@pytest.mark.parametrize("deferred", [False, True])
+def test_decode_full_layer_sampled(deferred):
     """The 128K Llama layer reached by decode steps, sized as the benchmark runs them:
     scored at n - 64 with 64 other window rows, then 64 appended positions whose
     query rows are the layer's window rows. The kept score is then the layer's
@@ -162,11 +165,11 @@ def test_decode_full_layer_sampled():
     rng = np.random.default_rng(77)
     scale = float(synth.bf16_bits_to_float32(case.q).std())
     first = synth.bf16_round_bits((rng.standard_normal((Hq, w, d)) * scale).astype(np.float32))
-    print(f"[decode full] llama_128k n={n} w={w}: init at n - {w}, {w} steps", flush=True)
+    print(f"[decode full] llama_128k n={n} w={w}: init at n - {w}, {w} steps, deferred={deferred}", flush=True)
     sc = K.DecodeScorer(n_max=n, window=w, Hq=Hq, Hkv=Hkv, d=d)
     sc.init(_dev(first).contiguous(), k, v, n - w)
     for i in range(w):
-        sc.step(q[:, i].contiguous(), k, v)
+        sc.step(q[:, i].contiguous(), k, v, deferred=deferred)
     ne = cfg.n_evicts()[0]
     P, idx = sc.select(pool_kernel=cfg.pool_kernel, n_evict=ne)
     sc.check()
@@ -188,3 +191,97 @@ def test_decode_full_layer_sampled():
         inter = np.intersect1d(idx[g], idx_main[g]).size
         jac = inter / (2 * ne - inter)
         assert jac > 0.99, f"head {g}: evicted set overlap with the scoring pass {jac:.4f}"
+
+
+def _scorers(Hq, Hkv, n0, w, steps, n_max, needles=4):
+    """Two scorers on the same grown cache, both initialised at n0."""
+    a, q_all, k, v, kc, vc = _setup(Hq, Hkv, n0, w, steps, n_max, needles=needles)
+    b = K.DecodeScorer(n_max=n_max, window=w, Hq=Hq, Hkv=Hkv, d=128)
+    b.init(_dev(q_all[:, n0 - w:n0]).contiguous(), kc, vc, n0)
+    return a, b, q_all, k, v, kc, vc
+
+
+def _close_f64(x, y, rel):
+    x, y = x.raw_scores_f64().cpu().numpy(), y.raw_scores_f64().cpu().numpy()
+    scale = np.abs(y).max()
+    assert scale > 0
+    err = np.abs(x - y).max() / scale
+    assert err <= rel, err
+    return err
+
+
+@pytest.mark.parametrize("Hq,Hkv,n0,w,steps,n_max", [
+    (8, 2, 300, 12, 20, 330),     # G = 4, more steps than the window holds
+    (28, 4, 2100, 6, 9, 2200),    # G = 7, two statistics chunks and a ragged tile
+    (4, 4, 97, 1, 5, 110),        # G = 1, window of one row: the pending row is the one leaving
+    (16, 2, 130, 20, 4, 140),     # G = 8, the largest group of the single pass
+    (16, 1, 90, 5, 3, 100),       # G = 16: the deferred call takes the two-pass step
+])
+def test_deferred_steps_match_two_pass(Hq, Hkv, n0, w, steps, n_max):
+    a, b, q_all, k, v, kc, vc = _scorers(Hq, Hkv, n0, w, steps, n_max)
+    for s in range(steps):
+        qn = _dev(q_all[:, n0 + s]).contiguous()
+        a.step(qn, kc, vc, deferred=True)
+        b.step(qn, kc, vc)
+    a.check(), b.check()
+    n = n0 + steps
+    # the new rows' statistics take the same arithmetic in both forms; the terms too
+    err = _close_f64(a, b, 1e-9)
+    print(f"deferred vs two-pass: {err:.2e}")
+    assert max_rel_err(a.raw_scores().cpu().numpy(), _ref(q_all, k, v, n, w, Hq, Hkv)) <= RTOL["bf16"]
+    assert int(a.status.item()) & K.binding.STATUS_PENDING == 0
+
+
+def test_deferred_mixed_with_two_pass_flush_and_rebuild():
+    Hq, Hkv, n0, w, steps = 8, 2, 260, 10, 24
+    a, b, q_all, k, v, kc, vc = _scorers(Hq, Hkv, n0, w, steps, 300, needles=6)
+    plan = "DDTDFDDRTDDDTTDFFDDRDDTD"  # D deferred, T two-pass, F flush after a deferred step, R rebuild
+    assert len(plan) == steps
+    for s, op in enumerate(plan):
+        qn = _dev(q_all[:, n0 + s]).contiguous()
+        a.step(qn, kc, vc, deferred=op in "DFR")
+        if op == "F":
+            a.flush()
+            a.flush()  # nothing left: a no-op
+        if op == "R":
+            a.rebuild(kc, vc)
+        b.step(qn, kc, vc)
+        if s % 6 == 5:
+            a.check()
+            n = n0 + s + 1
+            assert max_rel_err(a.raw_scores().cpu().numpy(), _ref(q_all, k, v, n, w, Hq, Hkv)) <= RTOL["bf16"]
+            _close_f64(a, b, 1e-9)
+    a.check(), b.check()
+    _close_f64(a, b, 1e-9)
+    a.rebuild(kc, vc)
+    _close_f64(a, b, 1e-9)
+
+
+def test_select_reports_pending_terms():
+    """The C entry points: select on a state with pending terms flags it; a flush clears it."""
+    Hq, Hkv, n0, w = 8, 2, 200, 8
+    sc, q_all, k, v, kc, vc = _setup(Hq, Hkv, n0, w, 2, 210)
+    lib = K.load_library()
+    args = (sc.n_max, w, Hq, Hkv, 128)
+    stream = torch.cuda.current_stream().cuda_stream
+    qn = _dev(q_all[:, n0]).contiguous()
+    assert lib.dropkv_decode_step_deferred(qn.data_ptr(), kc.data_ptr(), vc.data_ptr(), n0 + 1, *args,
+                                           sc.state.data_ptr(), sc.state.numel(), sc.status.data_ptr(), stream) == 0
+    n = n0 + 1
+    out = torch.empty((Hkv, n), dtype=torch.float32, device="cuda")
+    idx = torch.empty((Hkv, 10), dtype=torch.int64, device="cuda")
+    assert lib.dropkv_decode_select(sc.state.data_ptr(), sc.state.numel(), n, *args, 3, 10, out.data_ptr(),
+                                    idx.data_ptr(), sc.status.data_ptr(), stream) == 0
+    assert int(sc.status.item()) == K.binding.STATUS_PENDING
+    partial = out.clone()
+    sc.status.zero_()
+    assert lib.dropkv_decode_flush(kc.data_ptr(), vc.data_ptr(), n, *args, sc.state.data_ptr(), sc.state.numel(),
+                                   stream) == 0
+    assert lib.dropkv_decode_select(sc.state.data_ptr(), sc.state.numel(), n, *args, 3, 10, out.data_ptr(),
+                                    idx.data_ptr(), sc.status.data_ptr(), stream) == 0
+    assert int(sc.status.item()) == 0
+    ref = oracle.dropkv_oracle(q_all[:, n - w:n], k[:, :n], v[:, :n], n=n, window=w, Hq=Hq, Hkv=Hkv, d=128,
+                               pool_kernel=3, n_evict=10, dtype="bf16")
+    assert max_rel_err(out.cpu().numpy(), ref["P"]) <= RTOL["bf16"]
+    # before the flush the newest position's terms were missing
+    assert max_rel_err(partial.cpu().numpy(), ref["P"]) > RTOL["bf16"]
