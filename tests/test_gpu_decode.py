@@ -215,6 +215,8 @@ def _close_f64(x, y, rel):
     (28, 4, 2100, 6, 9, 2200),    # G = 7, two statistics chunks and a ragged tile
     (4, 4, 97, 1, 5, 110),        # G = 1, window of one row: the pending row is the one leaving
     (16, 2, 130, 20, 4, 140),     # G = 8, the largest group of the single pass
+    (6, 2, 150, 7, 5, 160),       # G = 3: the rows split 2 + 1 between the waves of a SIMD
+    (4, 2, 120, 3, 4, 130),       # G = 2
     (16, 1, 90, 5, 3, 100),       # G = 16: the deferred call takes the two-pass step
 ])
 def test_deferred_steps_match_two_pass(Hq, Hkv, n0, w, steps, n_max):
