@@ -24,6 +24,11 @@
 //       token (X = Q K^T and C = a V^T on 16x16x32 MFMA, 16-token subtiles per
 //       wave, K and V read straight into the MFMA operands, 64 contiguous
 //       bytes per token and load), added into the fp64 score
+//   k_dec_fused8 / k_dec_fused  the single-pass step: one read of K and V
+//       through LDS tiles feeds both the new rows' statistics (as
+//       k_dec_stats) and the terms of the leaving rows and of the rows the
+//       previous single-pass step left pending (as k_dec_contrib); the new
+//       rows' terms stay pending until the next step, a flush or a rebuild
 //   argmax terms of rows with p_max > 1/2 are scored apart and kept per row,
 //       so the exact value added is the one later removed. The rows live in a
 //       ring of w + 1 slots per KV head (position p in slot p mod (w + 1)), so
