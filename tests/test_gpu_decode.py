@@ -151,21 +151,24 @@ def test_decode_reports_singular_new_row():
         sc.check()
 
 
-@pytest.mark.parametrize("deferred", [False, True])
-def test_decode_full_layer_sampled(deferred):
-    """The 128K Llama layer reached by decode steps, sized as the benchmark runs them:
+@pytest.mark.parametrize("workload,deferred", [("llama_128k", False), ("llama_128k", True),
+                                               ("qwen_128k_sweep", True)])
+def test_decode_full_layer_sampled(workload, deferred):
+    """A 128K layer reached by decode steps, sized as the benchmark runs them:
     scored at n - 64 with 64 other window rows, then 64 appended positions whose
     query rows are the layer's window rows. The kept score is then the layer's
     score: against the oracle on sampled tokens (sink, needles, chunk edges,
-    window edge, random), and against the scoring pass on every token."""
-    cfg = synth.CONFIGS["llama_128k"]
+    window edge, random), and against the scoring pass on every token. The
+    Qwen-shaped layer (G = 7) takes the single-pass kernel for five to eight
+    rows per position."""
+    cfg = synth.CONFIGS[workload]
     case = synth.make_case(cfg)
     n, w, Hq, Hkv, d = case.n, case.window, case.Hq, case.Hkv, case.d
     q, k, v = to_torch(case)
     rng = np.random.default_rng(77)
     scale = float(synth.bf16_bits_to_float32(case.q).std())
     first = synth.bf16_round_bits((rng.standard_normal((Hq, w, d)) * scale).astype(np.float32))
-    print(f"[decode full] llama_128k n={n} w={w}: init at n - {w}, {w} steps, deferred={deferred}", flush=True)
+    print(f"[decode full] {workload} n={n} w={w}: init at n - {w}, {w} steps, deferred={deferred}", flush=True)
     sc = K.DecodeScorer(n_max=n, window=w, Hq=Hq, Hkv=Hkv, d=d)
     sc.init(_dev(first).contiguous(), k, v, n - w)
     for i in range(w):
@@ -175,7 +178,7 @@ def test_decode_full_layer_sampled(deferred):
     sc.check()
     S = sc.raw_scores().cpu().numpy()
     P, idx = P.cpu().numpy(), idx.cpu().numpy()
-    for g in (0, 5):
+    for g in (0, Hkv - 1):
         e_S, e_P = check_sampled(case, g, cfg.pool_kernel, S, P, rng)
         print(f"[decode full] head {g}: sampled rel err S {e_S:.2e}, P {e_P:.2e}", flush=True)
     S_main = K.raw_scores(q, k, v).cpu().numpy()
