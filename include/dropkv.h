@@ -252,8 +252,9 @@ int dropkv_compact(int32_t dtype, const void* k, const void* v, int64_t n, int32
  * (head stride n_max token rows), of which the first n rows of each head are
  * valid; q is [Hq][window][d] (the last `window` positions' query rows, head
  * major), q_new [Hq][d] (the appended position's query rows). The caller owns
- * `state`: device memory of dropkv_decode_state_bytes(...) bytes, 256-byte
- * aligned, used only through these calls (layout: fp64 S [Hkv][n_max] first,
+ * `state`: device memory of dropkv_decode_state_bytes(...) bytes (hipMalloc'd,
+ * not managed memory: the single-pass step adds to it with fp64 atomics),
+ * 256-byte aligned, used only through these calls (layout: fp64 S [Hkv][n_max] first,
  * then the window's rows). All calls are asynchronous on `stream` and return
  * DROPKV_OK once enqueued, DROPKV_ERR_INVALID (nothing launched: shape, count
  * or pointer checks) or DROPKV_ERR_DEVICE. Device-side findings go to the

@@ -185,8 +185,13 @@ int check_decode(int64_t n, int64_t need_n, int64_t n_max, int32_t window, int32
   if (n < need_n || n > n_max) return fail(DROPKV_ERR_INVALID, "token count out of range for this call (see dropkv.h)");
   if ((double)Hkv * (double)n_max * 128.0 > 1e15 || (double)Hq * window > 1e8)
     return fail(DROPKV_ERR_INVALID, "shape too large");
-  if (!state || ((uintptr_t)state & 255) || !is_device_ptr(state))
-    return fail(DROPKV_ERR_INVALID, "state must be a 256-byte aligned device pointer");
+  hipPointerAttribute_t attr;
+  const bool plain_device = state && hipPointerGetAttributes(&attr, state) == hipSuccess &&
+                            attr.type == hipMemoryTypeDevice;
+  if (!plain_device) (void)hipGetLastError();
+  // not managed memory: the single-pass step updates the score with fp64 atomic adds
+  if (!state || ((uintptr_t)state & 255) || !plain_device)
+    return fail(DROPKV_ERR_INVALID, "state must be a 256-byte aligned device pointer (device memory, not managed)");
   if (carve_decode_state(nullptr, n_max, window, Hq, Hkv).bytes > state_bytes)
     return fail(DROPKV_ERR_INVALID, "state too small (dropkv_decode_state_bytes)");
   return DROPKV_OK;

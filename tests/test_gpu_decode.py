@@ -136,6 +136,17 @@ def test_decode_rejects_invalid_calls():
                                   sc.state.data_ptr(), sc.state.numel(), sc.status.data_ptr(), None) == K.binding.ERR_INVALID
     assert lib.dropkv_decode_init(q.data_ptr(), kc.data_ptr(), vc.data_ptr(), 40, 41, w, Hq, Hkv, 128,
                                   sc.state.data_ptr(), 1024, sc.status.data_ptr(), None) == K.binding.ERR_INVALID
+    # a state in managed memory is refused (the single-pass step uses fp64 atomics on it)
+    import ctypes
+    hip = ctypes.CDLL("libamdhip64.so")
+    ptr = ctypes.c_void_p()
+    nbytes = sc.state.numel()
+    assert hip.hipMallocManaged(ctypes.byref(ptr), ctypes.c_size_t(nbytes), ctypes.c_uint(1)) == 0
+    try:
+        assert lib.dropkv_decode_init(q.data_ptr(), kc.data_ptr(), vc.data_ptr(), 40, 41, w, Hq, Hkv, 128,
+                                      ptr.value, nbytes, sc.status.data_ptr(), None) == K.binding.ERR_INVALID
+    finally:
+        hip.hipFree(ptr)
 
 
 def test_decode_reports_singular_new_row():
