@@ -78,25 +78,6 @@ __device__ __forceinline__ float pair_sum(float x) {
   return __uint_as_float(s[0]) + __uint_as_float(s[1]);
 }
 
-// ||v_j||^2 of token l%32 of a subtile from the V operand of C = a V^T (lane l
-// holds dims 16ks + 8(l/32) .. +7 of that token): two-term bf16 dot products
-// (exact squares, fp32 sums) over the lane's half of the dims, plus the other
-// half-lane's. Used when no ||v||^2 array from pass 1 exists.
-__device__ __forceinline__ float vnorm_from_operand(const bf16x8 (&vb)[8]) {
-  typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-  float a0 = 0.f, a1 = 0.f;
-#pragma unroll
-  for (int ks = 0; ks < 8; ++ks) {
-    const bf16x2 p0 = {vb[ks][0], vb[ks][1]}, p1 = {vb[ks][2], vb[ks][3]};
-    const bf16x2 p2 = {vb[ks][4], vb[ks][5]}, p3 = {vb[ks][6], vb[ks][7]};
-    a0 = __builtin_amdgcn_fdot2_f32_bf16(p0, p0, a0, false);
-    a1 = __builtin_amdgcn_fdot2_f32_bf16(p1, p1, a1, false);
-    a0 = __builtin_amdgcn_fdot2_f32_bf16(p2, p2, a0, false);
-    a1 = __builtin_amdgcn_fdot2_f32_bf16(p3, p3, a1, false);
-  }
-  return pair_sum(a0 + a1);
-}
-
 __device__ __forceinline__ bf16x8 ld16(const char* p) { return *(const bf16x8*)p; }
 
 // Wait until this wave's direct-to-LDS loads have landed, then barrier: after
@@ -960,8 +941,10 @@ __device__ __forceinline__ void p2_values(const float (&y2)[16], const f32x16& C
 
 // One 32-token subtile of the pass-2 fast path for this wave's 32 rows:
 // returns this wave's share of the score of token l%32 (valid in lanes < 32).
+// NVC (||v_j||^2 not known yet): returns the share of sum r^2 C and leaves
+// that of sum r^2 in *q2out; the workgroup folds ||v_j||^2 in later.
 template <bool MASK, bool NVC>
-__device__ __forceinline__ float p2_sub(const char* kt, const char* vt, float nvj, const LdsOff& off,
+__device__ __forceinline__ float p2_sub(const char* kt, const char* vt, float nvj, float* q2out, const LdsOff& off,
                                         const bf16x8 (&qa)[8], const bf16x8 (&aa)[8],
                                         const float (&nb2)[16], const float (&cinit)[16], float c2x2,
                                         int64_t tok, int rbase, int w) {
@@ -972,7 +955,6 @@ __device__ __forceinline__ float p2_sub(const char* kt, const char* vt, float nv
   for (int ks = 0; ks < 8; ++ks) vb[ks] = ld16(vt + off.k[ks]);
   // all sixteen operand reads in flight before the first MFMA waits on one
   __builtin_amdgcn_sched_barrier(0);
-  if constexpr (NVC) nvj = vnorm_from_operand(vb);
   f32x16 X = {}, C;
 #pragma unroll
   for (int i = 0; i < 16; ++i) C[i] = cinit[i];
@@ -1003,11 +985,18 @@ __device__ __forceinline__ float p2_sub(const char* kt, const char* vt, float nv
     p2_values<kTierSquare>(y2, C, q1, q2);
   }
   // this wave's rows: sum r^2 (||a||^2 - 2 a.v + ||v||^2) = ||v||^2 q2 - 2 q1
-  return pair_sum(fmaf(nvj, q2, -2.0f * q1));
+  if constexpr (NVC) {
+    *q2out = pair_sum(q2);
+    return pair_sum(q1);
+  } else {
+    return pair_sum(fmaf(nvj, q2, -2.0f * q1));
+  }
 }
 
-// NVC: ||v_j||^2 comes from the V operands in registers instead of the array
-// pass 1 writes (the path that starts from given row statistics).
+// NVC: ||v_j||^2 is computed from the tile in LDS, once per workgroup and
+// token (tile_vnorms), instead of read from the array pass 1 writes (the path
+// that starts from given row statistics); the waves' shares of sum r^2 C and
+// sum r^2 are reduced separately and ||v_j||^2 is folded in per token.
 template <int NW, bool NVC>
 __global__ __launch_bounds__(NW * 64) void k_pass2(P2Args P, FixArgs F) {
   if (NW >= 2 && blockIdx.x >= gridDim.x - (NW >= 2 ? FXC : 0)) {
@@ -1020,6 +1009,7 @@ __global__ __launch_bounds__(NW * 64) void k_pass2(P2Args P, FixArgs F) {
   __shared__ __attribute__((aligned(1024))) char kbuf[3][TILE_BYTES];
   __shared__ __attribute__((aligned(1024))) char vbuf[3][TILE_BYTES];
   __shared__ float red3[3][NW][TT];
+  __shared__ float red3b[NVC ? 3 : 1][NW][TT];  // NVC: the waves' shares of sum r^2 per token
   __shared__ float nvbuf[3][TT];
   constexpr int kDmaPerTile = 32 / NW + (NVC ? 0 : 1);  // direct-to-LDS instructions per wave per tile
   const int chunk = blockIdx.x, rg = blockIdx.y, g = blockIdx.z;
@@ -1110,8 +1100,37 @@ __global__ __launch_bounds__(NW * 64) void k_pass2(P2Args P, FixArgs F) {
       if (tok < t1) {
         float sacc = 0.f;
         for (int wv = 0; wv < nwa; ++wv) sacc += red[wv][threadIdx.x];
+        if constexpr (NVC) {  // sacc = sum r^2 C; ||v_j||^2 and sum r^2 from the tile's buffers
+          const int b = tl % 3;
+          float s2 = 0.f;
+          for (int wv = 0; wv < nwa; ++wv) s2 += red3b[b][wv][threadIdx.x];
+          sacc = fmaf(nvbuf[b][threadIdx.x], s2, -2.0f * sacc);
+        }
         Sout[tok] = fmaxf(sacc, 0.0f) * P.invG;
       }
+    }
+  };
+  // NVC: ||v_j||^2 of tile t's 64 tokens into nvbuf[t % 3], shared by the
+  // waves (8 lanes per token, 16 dims each); read by combine(t) after the
+  // barrier at tile t + 1
+  auto tile_vnorms = [&](int t) {
+    const char* vt = vbuf[t % 3];
+    const int li = lane & 7;
+    for (int tk = wave * 8 + (lane >> 3); tk < TT; tk += NW * 8) {
+      const bf16x8 x0 = ld16(vt + toff(tk, 8 * li)), x1 = ld16(vt + toff(tk, 64 + 8 * li));
+      typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+      float a0 = 0.f, a1 = 0.f;
+#pragma unroll
+      for (int i = 0; i < 8; i += 2) {
+        const bf16x2 p0 = {x0[i], x0[i + 1]}, p1 = {x1[i], x1[i + 1]};
+        a0 = __builtin_amdgcn_fdot2_f32_bf16(p0, p0, a0, false);
+        a1 = __builtin_amdgcn_fdot2_f32_bf16(p1, p1, a1, false);
+      }
+      float a = a0 + a1;
+      a += __shfl_xor(a, 1, 64);
+      a += __shfl_xor(a, 2, 64);
+      a += __shfl_xor(a, 4, 64);
+      if (li == 0) nvbuf[t % 3][tk] = a;
     }
   };
   auto head = [&](int t, const float (*red_prev)[TT], char* kn, char* vn, float* nvn) {
@@ -1131,12 +1150,18 @@ __global__ __launch_bounds__(NW * 64) void k_pass2(P2Args P, FixArgs F) {
     constexpr int B = decltype(bc)::value;
     constexpr int N2 = (B + 2) % 3;
     head(t, red3[N2], kbuf[N2], vbuf[N2], nvbuf[N2]);
+    if constexpr (NVC) tile_vnorms(t);
     if (active) {
 #pragma unroll
       for (int sub = 0; sub < 2; ++sub) {
+        float q2s = 0.f;
         const float sw = p2_sub<false, NVC>(kbuf[B] + sub * 32 * 256, vbuf[B] + sub * 32 * 256,
-                                       nvbuf[B][sub * 32 + l32], off, qa, aa, nb2, cinit, c2x2, 0, rbase, P.w);
-        if (h == 0) red3[B][wave][sub * 32 + l32] = sw;
+                                       NVC ? 0.f : nvbuf[B][sub * 32 + l32], &q2s, off, qa, aa, nb2, cinit, c2x2,
+                                       0, rbase, P.w);
+        if (h == 0) {
+          red3[B][wave][sub * 32 + l32] = sw;
+          if constexpr (NVC) red3b[B][wave][sub * 32 + l32] = q2s;
+        }
       }
     }
   };
@@ -1149,13 +1174,19 @@ __global__ __launch_bounds__(NW * 64) void k_pass2(P2Args P, FixArgs F) {
   for (; t < ntiles; ++t) {  // at most two clean tiles, then the masked tail
     const int b = t % 3, nb = (t + 2) % 3;
     head(t, red3[nb], kbuf[nb], vbuf[nb], nvbuf[nb]);
+    if constexpr (NVC) tile_vnorms(t);
     if (active) {
 #pragma unroll
       for (int sub = 0; sub < 2; ++sub) {
         const int64_t tok = tok_rel0 + (int64_t)t * TT + sub * 32;
+        float q2s = 0.f;
         const float sw = p2_sub<true, NVC>(kbuf[b] + sub * 32 * 256, vbuf[b] + sub * 32 * 256,
-                                      nvbuf[b][sub * 32 + l32], off, qa, aa, nb2, cinit, c2x2, tok, rbase, P.w);
-        if (h == 0) red3[b][wave][sub * 32 + l32] = sw;
+                                      NVC ? 0.f : nvbuf[b][sub * 32 + l32], &q2s, off, qa, aa, nb2, cinit, c2x2,
+                                      tok, rbase, P.w);
+        if (h == 0) {
+          red3[b][wave][sub * 32 + l32] = sw;
+          if constexpr (NVC) red3b[b][wave][sub * 32 + l32] = q2s;
+        }
       }
     }
   }
