@@ -60,6 +60,7 @@ def _ref(q_all, k, v, n, w, Hq, Hkv):
     (28, 4, 300, 8, 10, 320, 5),     # G = 7 (Qwen-like group)
     (4, 4, 97, 1, 4, 101, 2),        # G = 1, window of one row, ragged n
     (16, 2, 1030, 40, 3, 1100, 3),   # G = 8, n across the 1024-token workgroup edge
+    (8, 2, 600, 130, 3, 640, 3),     # G = 4, w = 130: the window takes five 128-row launches, the last ragged
 ])
 def test_decode_matches_oracle(Hq, Hkv, n0, w, steps, n_max, check_every):
     sc, q_all, k, v, kc, vc = _setup(Hq, Hkv, n0, w, steps, n_max)
@@ -229,8 +230,9 @@ def _close_f64(x, y, rel):
     (28, 4, 2100, 6, 9, 2200),    # G = 7, two statistics chunks and a ragged tile
     (4, 4, 97, 1, 5, 110),        # G = 1, window of one row: the pending row is the one leaving
     (16, 2, 130, 20, 4, 140),     # G = 8, the largest group of the single pass
-    (6, 2, 150, 7, 5, 160),       # G = 3: the rows split 2 + 1 between the waves of a SIMD
+    (6, 2, 150, 7, 5, 160),       # G = 3
     (4, 2, 120, 3, 4, 130),       # G = 2
+    (8, 2, 600, 130, 4, 640),     # G = 4 with a long window (rows leave from five init launches)
     (16, 1, 90, 5, 3, 100),       # G = 16: the deferred call takes the two-pass step
 ])
 def test_deferred_steps_match_two_pass(Hq, Hkv, n0, w, steps, n_max):
