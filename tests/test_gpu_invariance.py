@@ -87,3 +87,27 @@ def test_doubling_values_quadruples_decode_scores(deferred):
     np.testing.assert_array_equal(S2, 4.0 * S1)
     np.testing.assert_array_equal(P2, 4.0 * P1)
     np.testing.assert_array_equal(i2, i1)
+
+
+@pytest.mark.parametrize("workload,n,dtype", [("llama_4k", 2500, "bf16"), ("tiny", 300, "f32")])
+def test_reversing_kv_heads_reverses_outputs(workload, n, dtype):
+    """Each KV head's score depends only on its own K/V and query group: listing
+    the heads (with their groups) in reverse order must reverse the outputs bit
+    for bit. A head-stride or group-offset mistake breaks this."""
+    cfg = synth.CONFIGS[workload]
+    case = synth.make_case(cfg, n=n, dtype=dtype)
+    G = case.Hq // case.Hkv
+    qr = case.q.reshape(case.Hkv, G, *case.q.shape[1:])[::-1].reshape(case.q.shape)
+    rev = dataclasses.replace(case, q=np.ascontiguousarray(qr), k=np.ascontiguousarray(case.k[::-1]),
+                              v=np.ascontiguousarray(case.v[::-1]))
+    ne = (n - case.window) // 3
+    outs = []
+    for c in (case, rev):
+        q, k, v = to_torch(c)
+        S = K.raw_scores(q, k, v).cpu().numpy()
+        P, idx = K.score(q, k, v, pool_kernel=cfg.pool_kernel, n_evict=ne)
+        outs.append((S, P.cpu().numpy(), idx.cpu().numpy()))
+    (S1, P1, i1), (S2, P2, i2) = outs
+    np.testing.assert_array_equal(S2, S1[::-1])
+    np.testing.assert_array_equal(P2, P1[::-1])
+    np.testing.assert_array_equal(i2, i1[::-1])
