@@ -52,6 +52,7 @@ constexpr int kInitRows = 128;     // rows per launch when a whole window is sco
 constexpr int kOpStride = HD + 8;  // bf16 per staged operand row (272 bytes)
 constexpr int kTokPerWg = 512;     // tokens per k_dec_contrib workgroup (4 waves x 8 subtiles of 16)
 constexpr int kStatsTok = 2048;    // tokens per k_dec_stats workgroup
+constexpr int kNumCUs = 256;       // MI355X compute units (one k_dec_fused8 workgroup each at long contexts)
 
 __device__ __forceinline__ uint16_t rne_bf16(float x) {
   uint32_t b = __float_as_uint(x);
@@ -1002,6 +1003,7 @@ __device__ __forceinline__ void stats_tile(StatsLane<NR>& L, const char* kt, con
 struct FusedArgs {
   StatsArgs s;    // the new position's rows (r0 = 0, nr = G)
   ContribArgs c;  // mode 3: leaving rows and the pending rows
+  int chunk_tok;  // tokens per workgroup (k_dec_fused8: a multiple of 64, >= kStatsTok)
 };
 
 // One step in one pass over K and V (per chunk of kStatsTok tokens, KV head):
@@ -1075,7 +1077,9 @@ __global__ __launch_bounds__(256) void k_dec_fused(FusedArgs F) {
 // pending rows then make one 16-row block, held in registers). Waves 4-7
 // load the 64-token tiles into LDS (five buffers, all of LDS: four tiles in
 // flight) and take the new rows' statistics (two tokens per lane group and
-// tile, in the token order of k_dec_stats); waves 0-3 take the terms of one
+// tile, in the token order of k_dec_stats; with the same chunks the
+// statistics are those of k_dec_stats bit for bit, with the longer chunks of
+// long contexts they agree to fp32 rounding); waves 0-3 take the terms of one
 // 16-token subtile each and add them to the score with fp64 atomic adds (one
 // per token and launch, so the order does not matter), so they never wait
 // for tile loads of their own and each SIMD interleaves an MFMA-heavy and a
@@ -1097,8 +1101,8 @@ __global__ __launch_bounds__(512) void k_dec_fused8(FusedArgs F) {
   StatsLane<NR> L;
   stats_begin<NR>(L, F.s.qn, g, F.s.G, 0, li);
   const int64_t n = F.s.n;
-  const int64_t t0 = (int64_t)chunk * kStatsTok;
-  const int nt = (int)((n - t0) < kStatsTok ? (n - t0) : kStatsTok);
+  const int64_t t0 = (int64_t)chunk * F.chunk_tok;
+  const int nt = (int)((n - t0) < F.chunk_tok ? (n - t0) : F.chunk_tok);
   const int ntiles = (nt + kTileTok - 1) / kTileTok;
   const uint16_t* kh = F.s.k + (size_t)g * F.s.n_max * HD;
   const uint16_t* vh = F.s.v + (size_t)g * F.s.n_max * HD;
@@ -1287,11 +1291,21 @@ hipError_t launch_decode_step_deferred(const void* q_new, const void* k, const v
   const int G = Hq / Hkv;
   if (G > kRowBatch) return launch_decode_step(q_new, k, v, n, n_max, w, Hq, Hkv, S, status, st);
   const float c2 = kLog2e / sqrtf((float)HD);
-  const int nch = (int)((n + kStatsTok - 1) / kStatsTok);
+  // k_dec_fused8 (one workgroup per CU by LDS): chunks sized so that the grid
+  // is about one wave of workgroups (no second round with its pipeline refill
+  // and tail), never below kStatsTok (the partials buffer holds n_max /
+  // kStatsTok chunks); k_dec_fused keeps kStatsTok (its per-token sums sit in LDS)
+  int64_t chunk_tok = kStatsTok;
+  if (G <= 4) {
+    const int64_t per = ((n * Hkv + kNumCUs - 1) / kNumCUs + 63) / 64 * 64;
+    if (per > chunk_tok) chunk_tok = per;
+  }
+  const int nch = (int)((n + chunk_tok - 1) / chunk_tok);
   FusedArgs f{StatsArgs{(const uint16_t*)q_new, (const uint16_t*)k, (const uint16_t*)v, S.part, n, n_max, G, Hkv,
                         nch, 0, G, c2},
               ContribArgs{(const uint16_t*)k, (const uint16_t*)v, S.T, S.S64, n, n_max, w, G, 3, 0, 0, c2,
-                          S.pend}};
+                          S.pend},
+              (int)chunk_tok};
   const dim3 grid(nch, Hkv);
   switch (G) {
     case 1: k_dec_fused8<1><<<grid, 512, 0, st>>>(f); break;
