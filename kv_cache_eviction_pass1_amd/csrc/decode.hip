@@ -50,7 +50,10 @@ constexpr int kDecPart = HD + 4;   // floats per stats partial (A[128], m, R, j*
 constexpr int kContribRows = 64;   // rows per k_dec_contrib launch in a step (operands and tables in LDS)
 constexpr int kInitRows = 128;     // rows per launch when a whole window is scored (76 KB of LDS: two workgroups per CU)
 constexpr int kOpStride = HD + 8;  // bf16 per staged operand row (272 bytes)
-constexpr int kTokPerWg = 512;     // tokens per k_dec_contrib workgroup (4 waves x 8 subtiles of 16)
+// tokens per k_dec_contrib workgroup: 512 for a step's few rows (4 waves x 8
+// subtiles of 16), 1024 for whole-window launches (their 128 rows keep each
+// workgroup busy longer, and fewer workgroups stage the rows: 7% faster)
+constexpr int tok_per_wg(int rows) { return rows > 64 ? 1024 : 512; }
 constexpr int kStatsTok = 2048;    // tokens per k_dec_stats workgroup
 constexpr int kNumCUs = 256;       // MI355X compute units (one k_dec_fused8 workgroup each at long contexts)
 
@@ -873,11 +876,12 @@ __device__ __forceinline__ void load_block_regs(const ContribArgs& A, int g, int
   }
 }
 
-// Per (chunk of kTokPerWg tokens, KV head): each wave takes 16-token
+// Per (chunk of tok_per_wg(ROWS) tokens, KV head): each wave takes 16-token
 // subtiles (wave, wave + 4, ...) with K and V read straight into the MFMA
 // operands, the next two subtiles' loads in flight while one is processed.
 template <int ROWS>
 __global__ __launch_bounds__(256) void k_dec_contrib(ContribArgs A) {
+  constexpr int kTokPerWg = tok_per_wg(ROWS);
   const int chunk = blockIdx.x, g = blockIdx.y;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int q4 = lane >> 4, l16 = lane & 15;
@@ -1223,8 +1227,8 @@ DecState carve_decode_state(void* base, int64_t n_max, int32_t w, int32_t Hq, in
 hipError_t launch_decode_contrib(const void* k, const void* v, int64_t n, int64_t n_max, int32_t w, int G,
                                  int32_t Hkv, const DecState& S, int mode, hipStream_t st) {
   const float c2 = kLog2e / sqrtf((float)HD);
-  const dim3 grid((unsigned)((n + kTokPerWg - 1) / kTokPerWg), Hkv);
   if (mode != 0) {  // a step's (at most 3G <= 48) or a flush's rows: one launch
+    const dim3 grid((unsigned)((n + tok_per_wg(kContribRows) - 1) / tok_per_wg(kContribRows)), Hkv);
     ContribArgs a{(const uint16_t*)k, (const uint16_t*)v, S.T, S.S64, n, n_max, w, G, mode, 0, 0, c2, S.pend};
     k_dec_contrib<kContribRows><<<grid, 256, 0, st>>>(a);
     return hipGetLastError();
@@ -1233,6 +1237,7 @@ hipError_t launch_decode_contrib(const void* k, const void* v, int64_t n, int64_
   // 64-row launches while two workgroups still fit a CU (256-row launches,
   // one per CU, were slower)
   const int per = kInitRows / G;  // window entries per launch (G <= 16)
+  const dim3 grid((unsigned)((n + tok_per_wg(kInitRows) - 1) / tok_per_wg(kInitRows)), Hkv);
   for (int e0 = 0; e0 < w; e0 += per) {
     const int e1 = e0 + per < w ? e0 + per : w;
     ContribArgs a{(const uint16_t*)k, (const uint16_t*)v, S.T, S.S64, n, n_max, w, G, 0, e0, e1, c2, S.pend};
