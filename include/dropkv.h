@@ -61,7 +61,8 @@ typedef enum {
   DROPKV_ERR_INVALID = -1,   /* bad argument: nothing launched */
   DROPKV_ERR_SINGULAR = -2,  /* a window row has a probability that rounds to 1 */
   DROPKV_ERR_NONFINITE = -3, /* NaN/inf in the inputs or the scores */
-  DROPKV_ERR_DEVICE = -4     /* HIP runtime error */
+  DROPKV_ERR_DEVICE = -4,    /* HIP runtime error */
+  DROPKV_ERR_NEGATIVE = -5   /* dropkv_select only: a given raw score is negative */
 } dropkv_status;
 
 /* Element type of q, k, v. */
@@ -74,7 +75,8 @@ enum {
   DROPKV_STATUS_SINGULAR = 1,
   DROPKV_STATUS_NONFINITE = 2,
   DROPKV_STATUS_BAD_INDEX = 4,
-  DROPKV_STATUS_PENDING = 8
+  DROPKV_STATUS_PENDING = 8,
+  DROPKV_STATUS_NEGATIVE = 16 /* dropkv_select: a given raw score S[g][j] < 0 */
 };
 
 /* Flags for dropkv_score_ex. */
@@ -140,9 +142,21 @@ int dropkv_row_stats(int32_t dtype, const void* q, const void* k, const void* v,
                      void* stream);
 
 /*
+ * The same export under the name of the boundary's stage list: pass-1
+ * statistics of bf16 inputs, i.e. dropkv_row_stats(DROPKV_BF16, ..., flags = 0).
+ * out_rest is R (the rest mass) as defined there. Synchronous.
+ */
+int dropkv_pass1_stats(const void* q, const void* k, const void* v, int64_t n, int32_t window,
+                       int32_t Hq, int32_t Hkv, int32_t d, float* out_m, float* out_rest,
+                       int32_t* out_argmax, float* out_a, void* stream);
+
+/*
  * The pooling, protection and selection stage alone, on caller-given raw
- * scores S [Hkv][n] (non-negative fp32): writes out_scores and out_evict_idx
- * exactly as dropkv_score does. Synchronous; NONFINITE if S holds NaN/inf.
+ * scores S [Hkv][n] (fp32): writes out_scores and out_evict_idx exactly as
+ * dropkv_score does. DropKV scores are sums of squared norms, so S must be
+ * non-negative (-0.0 counts as 0): a negative entry makes the call return
+ * DROPKV_ERR_NEGATIVE (found on the device; the outputs are then
+ * unspecified). Synchronous; NONFINITE if S holds NaN/inf.
  */
 int dropkv_select(const float* S, int64_t n, int32_t window, int32_t Hkv, int32_t pool_kernel,
                   int64_t n_evict, float* out_scores, int64_t* out_evict_idx, void* stream);
@@ -328,6 +342,9 @@ int dropkv_uses_mfma(int32_t dtype, int32_t d);
 
 /* Human-readable description of the calling thread's most recent error ("" if none). */
 const char* dropkv_last_error(void);
+
+/* The same text under the boundary's second name for it. */
+const char* dropkv_last_error_string(void);
 
 /* Library version string. */
 const char* dropkv_version(void);

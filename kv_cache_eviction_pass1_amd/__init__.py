@@ -8,9 +8,9 @@ load the library; the first call does, and fails loudly if it is not built.
 
 from .binding import (  # noqa: F401
     BF16, F32, FLAG_GENERIC, FLAG_STAGE_LOG, STATUS_BAD_INDEX, STATUS_NONFINITE, STATUS_SINGULAR,
-    DecodeScorer, DropKVError,
+    STATUS_NEGATIVE, DecodeScorer, DropKVError, DropKVNegativeScoreError,
     DropKVInvalidError, DropKVNonFiniteError, DropKVNotBuiltError, DropKVSingularError, LIB_PATH,
-    compact, load_library, raw_scores, row_stats, score, score_ex, score_from_stats, select,
+    compact, load_library, pass1_stats, raw_scores, row_stats, score, score_ex, score_from_stats, select,
     stage_log, stage_times,
     uses_mfma,
     version,
@@ -18,7 +18,8 @@ from .binding import (  # noqa: F401
 )
 
 __all__ = [
-    "score", "score_ex", "score_from_stats", "raw_scores", "row_stats", "select", "compact", "DecodeScorer",
+    "score", "score_ex", "score_from_stats", "raw_scores", "row_stats", "pass1_stats", "select", "compact",
+    "DecodeScorer", "DropKVNegativeScoreError", "STATUS_NEGATIVE",
     "stage_times", "stage_log",
     "workspace_bytes",
     "uses_mfma",

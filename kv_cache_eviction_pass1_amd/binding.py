@@ -15,9 +15,9 @@ from typing import Optional, Tuple
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libdropkv.so")
 
-OK, ERR_INVALID, ERR_SINGULAR, ERR_NONFINITE, ERR_DEVICE = 0, -1, -2, -3, -4
+OK, ERR_INVALID, ERR_SINGULAR, ERR_NONFINITE, ERR_DEVICE, ERR_NEGATIVE = 0, -1, -2, -3, -4, -5
 BF16, F32 = 0, 1
-STATUS_SINGULAR, STATUS_NONFINITE, STATUS_BAD_INDEX, STATUS_PENDING = 1, 2, 4, 8
+STATUS_SINGULAR, STATUS_NONFINITE, STATUS_BAD_INDEX, STATUS_PENDING, STATUS_NEGATIVE = 1, 2, 4, 8, 16
 FLAG_GENERIC = 1
 FLAG_STAGE_LOG = 2
 
@@ -33,6 +33,7 @@ SIGNATURES = {
     "dropkv_raw_scores": (_i32, [_i32, _p, _p, _p, _i64, _i32, _i32, _i32, _i32, _p, _u32, _p]),
     "dropkv_row_stats": (_i32, [_i32, _p, _p, _p, _i64, _i32, _i32, _i32, _i32, _p, _p, _p, _p,
                                 _u32, _p]),
+    "dropkv_pass1_stats": (_i32, [_p, _p, _p, _i64, _i32, _i32, _i32, _i32, _p, _p, _p, _p, _p]),
     "dropkv_select": (_i32, [_p, _i64, _i32, _i32, _i32, _i64, _p, _p, _p]),
     "dropkv_stage_times": (_i32, [_i32, _p, _p, _p, _i64, _i32, _i32, _i32, _i32, _i32, _i64, _p,
                                   _p, _u32, _p, _p, _i32, _p, _p]),
@@ -53,6 +54,7 @@ SIGNATURES = {
                                     _p]),
     "dropkv_uses_mfma": (_i32, [_i32, _i32]),
     "dropkv_last_error": (_c.c_char_p, []),
+    "dropkv_last_error_string": (_c.c_char_p, []),
     "dropkv_version": (_c.c_char_p, []),
 }
 
@@ -72,6 +74,10 @@ class DropKVSingularError(DropKVError):
 
 
 class DropKVNonFiniteError(DropKVError):
+    pass
+
+
+class DropKVNegativeScoreError(DropKVError, ValueError):
     pass
 
 
@@ -103,7 +109,8 @@ def _raise(code: int):
         return
     msg = load_library().dropkv_last_error().decode(errors="replace")
     cls = {ERR_INVALID: DropKVInvalidError, ERR_SINGULAR: DropKVSingularError,
-           ERR_NONFINITE: DropKVNonFiniteError}.get(code, DropKVError)
+           ERR_NONFINITE: DropKVNonFiniteError,
+           ERR_NEGATIVE: DropKVNegativeScoreError}.get(code, DropKVError)
     raise cls(code, msg)
 
 
@@ -217,8 +224,25 @@ def row_stats(q, k, v, *, flags: int = 0, stream=None):
     return m, rest, arg, a
 
 
+def pass1_stats(q, k, v, *, stream=None):
+    """bf16 inputs: the same per-row statistics as row_stats, through dropkv_pass1_stats."""
+    torch = _torch()
+    lib = load_library()
+    Hq, Hkv, d, n, w = _shapes(q, k, v)
+    rows = Hq * w
+    m = torch.empty(rows, dtype=torch.float32, device=q.device)
+    rest = torch.empty(rows, dtype=torch.float32, device=q.device)
+    arg = torch.empty(rows, dtype=torch.int32, device=q.device)
+    a = torch.empty((rows, d), dtype=torch.float32, device=q.device)
+    rc = lib.dropkv_pass1_stats(q.data_ptr(), k.data_ptr(), v.data_ptr(), n, w, Hq, Hkv, d, m.data_ptr(),
+                                rest.data_ptr(), arg.data_ptr(), a.data_ptr(), _stream_handle(stream))
+    _raise(rc)
+    return m, rest, arg, a
+
+
 def select(S, *, window: int, pool_kernel: int, n_evict: int, stream=None):
-    """Pool, protect and select on given raw scores S [Hkv, n] (fp32 GPU tensor)."""
+    """Pool, protect and select on given raw scores S [Hkv, n] (fp32 GPU tensor, >= 0;
+    a negative entry raises DropKVNegativeScoreError)."""
     torch = _torch()
     lib = load_library()
     Hkv, n = S.shape

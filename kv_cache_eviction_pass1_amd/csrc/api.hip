@@ -132,6 +132,7 @@ int status_to_code(int32_t st_word) {
   if (st_word & kStatusSingular)
     return fail(DROPKV_ERR_SINGULAR, "a window row has a probability that rounds to 1 (singular)");
   if (st_word & kStatusNonFinite) return fail(DROPKV_ERR_NONFINITE, "non-finite inputs or scores");
+  if (st_word & kStatusNegative) return fail(DROPKV_ERR_NEGATIVE, "negative raw score given to select");
   return DROPKV_OK;
 }
 
@@ -412,6 +413,13 @@ int dropkv_row_stats(int32_t dtype, const void* q, const void* k, const void* v,
   return sync_status(ws, st);
 }
 
+int dropkv_pass1_stats(const void* q, const void* k, const void* v, int64_t n, int32_t window,
+                       int32_t Hq, int32_t Hkv, int32_t d, float* out_m, float* out_rest,
+                       int32_t* out_argmax, float* out_a, void* stream) {
+  return dropkv_row_stats(DROPKV_BF16, q, k, v, n, window, Hq, Hkv, d, out_m, out_rest, out_argmax, out_a, 0u,
+                          stream);
+}
+
 int dropkv_select(const float* S, int64_t n, int32_t window, int32_t Hkv, int32_t pool_kernel,
                   int64_t n_evict, float* out_scores, int64_t* out_evict_idx, void* stream) {
   g_last_error.clear();
@@ -432,7 +440,7 @@ int dropkv_select(const float* S, int64_t n, int32_t window, int32_t Hkv, int32_
   hipError_t e = launch_init(ws.status, nullptr, ws.sel, Hkv, st);
   if (e == hipSuccess)
     e = launch_select(S, n, window, Hkv, pool_kernel, n_evict, out_scores, out_evict_idx, ws.status, nullptr,
-                      ws.sel, st);
+                      ws.sel, st, /*reject_negative=*/true);
   if (e != hipSuccess) return fail_hip(e, "select");
   return sync_status(ws, st);
 }
@@ -697,6 +705,8 @@ int dropkv_decode_select(void* state, size_t state_bytes, int64_t n, int64_t n_m
 int dropkv_uses_mfma(int32_t dtype, int32_t d) { return mfma_supported(dtype, d) ? 1 : 0; }
 
 const char* dropkv_last_error(void) { return g_last_error.c_str(); }
+
+const char* dropkv_last_error_string(void) { return g_last_error.c_str(); }
 
 const char* dropkv_version(void) { return "dropkv-gfx950 0.1"; }
 

@@ -48,14 +48,30 @@ constexpr int HD = 128;
 constexpr int kRowBatch = 8;       // new rows per k_dec_stats launch
 constexpr int kDecPart = HD + 4;   // floats per stats partial (A[128], m, R, j*, pad)
 constexpr int kContribRows = 64;   // rows per k_dec_contrib launch in a step (operands and tables in LDS)
-constexpr int kInitRows = 128;     // rows per launch when a whole window is scored (76 KB of LDS: two workgroups per CU)
+constexpr int kInitRows = 128;     // rows per launch when a whole window is scored (two workgroups per CU: see below)
 constexpr int kOpStride = HD + 8;  // bf16 per staged operand row (272 bytes)
 // tokens per k_dec_contrib workgroup: 512 for a step's few rows (4 waves x 8
 // subtiles of 16), 1024 for whole-window launches (their 128 rows keep each
 // workgroup busy longer, and fewer workgroups stage the rows: 7% faster)
 constexpr int tok_per_wg(int rows) { return rows > 64 ? 1024 : 512; }
 constexpr int kStatsTok = 2048;    // tokens per k_dec_stats workgroup
-constexpr int kNumCUs = 256;       // MI355X compute units (one k_dec_fused8 workgroup each at long contexts)
+// The single-pass step runs k_dec_fused8 (chunks of chunk_tok >= kStatsTok
+// tokens) for groups of at most this many query heads per KV head, and
+// k_dec_fused (chunks of exactly kStatsTok) above it.
+constexpr int kFused8MaxG = 4;
+
+// Compute units of the current device (read once per device; 256 on MI355X).
+int device_cu_count() {
+  static int cached[64] = {};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (cached[dev] == 0) {
+    int cus = 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 1) cus = 256;
+    cached[dev] = cus;
+  }
+  return cached[dev];
+}
 
 __device__ __forceinline__ uint16_t rne_bf16(float x) {
   uint32_t b = __float_as_uint(x);
@@ -717,6 +733,12 @@ struct ContribLds {
   uint16_t op[2 * ROWS][kOpStride];
 };
 
+// k_dec_contrib<kInitRows> holds ContribLds<kInitRows> (71.5 KiB) and its
+// per-token fp64 sums (8 KiB): two of them must fit in the CU's 160 KiB of LDS
+// so that two workgroups share a CU.
+static_assert(2 * (sizeof(ContribLds<kInitRows>) + sizeof(double) * tok_per_wg(kInitRows)) <= 160 * 1024,
+              "whole-window contrib launches must keep two workgroups per CU");
+
 // Fill L with the launch's rows of KV head g (padding rows up to a multiple of
 // 16: p = 0); returns the number of 16-row blocks. Called by every thread;
 // ends with a barrier.
@@ -1301,8 +1323,9 @@ hipError_t launch_decode_step_deferred(const void* q_new, const void* k, const v
   // and tail), never below kStatsTok (the partials buffer holds n_max /
   // kStatsTok chunks); k_dec_fused keeps kStatsTok (its per-token sums sit in LDS)
   int64_t chunk_tok = kStatsTok;
-  if (G <= 4) {
-    const int64_t per = ((n * Hkv + kNumCUs - 1) / kNumCUs + 63) / 64 * 64;
+  if (G <= kFused8MaxG) {
+    const int64_t cus = device_cu_count();
+    const int64_t per = ((n * Hkv + cus - 1) / cus + 63) / 64 * 64;
     if (per > chunk_tok) chunk_tok = per;
   }
   const int nch = (int)((n + chunk_tok - 1) / chunk_tok);
@@ -1312,6 +1335,8 @@ hipError_t launch_decode_step_deferred(const void* q_new, const void* k, const v
                           S.pend},
               (int)chunk_tok};
   const dim3 grid(nch, Hkv);
+  static_assert(kFused8MaxG == 4, "the switch below sends G = 1..4 to k_dec_fused8");
+  if (G > kFused8MaxG && chunk_tok != kStatsTok) return hipErrorInvalidValue;  // k_dec_fused's chunks
   switch (G) {
     case 1: k_dec_fused8<1><<<grid, 512, 0, st>>>(f); break;
     case 2: k_dec_fused8<2><<<grid, 512, 0, st>>>(f); break;

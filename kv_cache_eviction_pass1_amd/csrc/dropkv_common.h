@@ -11,6 +11,7 @@ namespace dropkv {
 constexpr int kStatusSingular = 1;
 constexpr int kStatusNonFinite = 2;
 constexpr int kStatusBadIndex = 4;  // cache compaction: eviction list not increasing inside [0, n)
+constexpr int kStatusNegative = 16;  // select on given scores: some S[g][j] < 0
 
 // A window row is rejected when its rest mass R = sum_{j != argmax} exp(x_j - x_max)
 // is at most 2^-24: then 1/(1+R) rounds to 1 in binary32 (the singular-input rule).
@@ -81,9 +82,13 @@ struct FoldInfo {
   float invG;
 };
 
+// reject_negative: S comes from the caller (dropkv_select), and any S < 0
+// raises kStatusNegative; scores the library computed are >= 0 by
+// construction, up to fp64 rounding residue in decode-time rescoring, which
+// orders as +0.
 hipError_t launch_select(const float* S, int64_t n, int32_t w, int32_t Hkv, int32_t pool_kernel,
                          int64_t n_evict, float* out_scores, int64_t* out_idx, int32_t* status,
-                         const FoldInfo* fold, void* scratch, hipStream_t st);
+                         const FoldInfo* fold, void* scratch, hipStream_t st, bool reject_negative = false);
 size_t select_scratch_bytes(int64_t n, int32_t Hkv);
 // 32-bit words at the start of the select scratch that must be zero before a call.
 size_t select_zero_words(int32_t Hkv);

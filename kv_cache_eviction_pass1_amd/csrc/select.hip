@@ -65,6 +65,7 @@ struct SelArgs {
   uint32_t* wg_lt;    // [Hkv][kMaxWg]: the same, summed over each cand workgroup's segments
   int32_t* status;
   FoldInfo fold;      // argmax terms of flagged rows to add to S (flagcount null: none)
+  bool reject_negative;  // caller-given S: a negative entry raises kStatusNegative
 };
 
 __device__ __forceinline__ uint32_t score_key(float x) {
@@ -245,12 +246,15 @@ __global__ __launch_bounds__(kT) void k_sel_pool(SelArgs A) {
   }
   // token base + e * kT + threadIdx.x: consecutive threads, consecutive tokens
   float mx[kPer];
-  bool nf = false;
+  bool nf = false, neg = false;
   if (in_lds) {
 #pragma unroll
     for (int e = 0; e < kPer; ++e) {
       mx[e] = sS[half + e * kT + threadIdx.x];
-      if (base + e * kT + threadIdx.x < A.n && !finite_f(mx[e])) nf = true;  // max() would hide a NaN
+      if (base + e * kT + threadIdx.x < A.n) {
+        if (!finite_f(mx[e])) nf = true;  // max() would hide a NaN
+        if (mx[e] < 0.0f) neg = true;     // -0.0 passes: it orders as +0
+      }
     }
     // one window offset at a time: the kPer LDS reads of a step are independent
     for (int t = 0; t <= 2 * half; ++t) {
@@ -265,6 +269,7 @@ __global__ __launch_bounds__(kT) void k_sel_pool(SelArgs A) {
       if (j < A.n) {
         mx[e] = Sg[j];
         if (!finite_f(mx[e])) nf = true;
+        if (mx[e] < 0.0f) neg = true;
         const int64_t lo = j - half < 0 ? 0 : j - half;
         const int64_t hi = j + half >= A.n ? A.n - 1 : j + half;
         for (int64_t t = lo; t <= hi; ++t) mx[e] = fmaxf(mx[e], Sg[t]);
@@ -282,14 +287,15 @@ __global__ __launch_bounds__(kT) void k_sel_pool(SelArgs A) {
       key[e] = score_key(p);
     }
   }
-  if (nf) bad = 1;
+  if (nf) bad |= kStatusNonFinite;
+  if (neg && A.reject_negative) bad |= kStatusNegative;
   if (A.n_evict > 0) {
 #pragma unroll
     for (int e = 0; e < kPer; ++e)
       if (key[e] != 0xffffffffu) atomicAdd(&hist[key[e] >> 20], 1u);
   }
   __syncthreads();
-  if (threadIdx.x == 0 && bad) atomicOr(A.status, kStatusNonFinite);
+  if (threadIdx.x == 0 && bad) atomicOr(A.status, bad);
   if (A.n_evict <= 0) return;
   uint32_t* gh = A.hist + (size_t)g * kHistStride;
   for (int i = threadIdx.x; i < kBins1; i += kT)
@@ -614,7 +620,7 @@ hipError_t launch_init(int32_t* status, int32_t* flagcount, void* sel_scratch, i
 
 hipError_t launch_select(const float* S, int64_t n, int32_t w, int32_t Hkv, int32_t pool_kernel,
                          int64_t n_evict, float* out_scores, int64_t* out_idx, int32_t* status,
-                         const FoldInfo* fold, void* scratch, hipStream_t st) {
+                         const FoldInfo* fold, void* scratch, hipStream_t st, bool reject_negative) {
   const SelGeom q = sel_geom(n);
   if (fold && fold->flagcount && pool_kernel / 2 > kMaxHalo) {
     // the pool kernel reads S from global memory for such wide kernels: fold first
@@ -640,6 +646,7 @@ hipError_t launch_select(const float* S, int64_t n, int32_t w, int32_t Hkv, int3
   A.seg_lt = p.seg_lt;
   A.wg_lt = p.wg_lt;
   A.status = status;
+  A.reject_negative = reject_negative;
   if (fold) A.fold = *fold;
   k_sel_pool<<<dim3(A.nblk, Hkv), kT, 0, st>>>(A);
   if (n_evict > 0) {

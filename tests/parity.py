@@ -3,9 +3,12 @@
 Tolerances: relative 2e-2 on scores for bf16 inputs and 1e-5 for fp32
 inputs, on every finite entry; +inf entries (the protected window) must match
 exactly. Evicted sets must always be the bottom-n_evict of the GPU's own
-pooled scores under (score, index), and must equal the oracle's set exactly
-whenever no oracle score other than the boundary value lies within twice the
-tolerance of it.
+pooled scores under (score, index); they must equal the oracle's set exactly
+when the oracle's k-th / (k+1)-th gap exceeds twice the tolerance, or when no
+oracle score other than the boundary value lies within twice the tolerance of
+it; otherwise every index in which the two sets differ must have an oracle
+score within the band that the measured score error allows around the
+boundary value (check_evictions).
 """
 
 from __future__ import annotations
@@ -52,13 +55,45 @@ def own_bottom_k(scores_row, k):
     return np.sort(np.argsort(scores_row, kind="stable")[:k])
 
 
-def check_evictions(gpu_scores, gpu_idx, ref_P, ref_S, ref_idx, n_evict, rtol):
-    """Returns (n_exact_checked, jaccards). Asserts both eviction rules."""
+def symdiff_band(e):
+    """Relative band around the oracle's boundary value tau that every index
+    of the symmetric difference must fall in, when every GPU pooled score is
+    within relative e of the oracle's.
+
+    If |g_j - r_j| <= e r_j for all j, the k-th smallest GPU value lies in
+    [(1-e) tau, (1+e) tau]; an index the GPU evicts and the oracle keeps has
+    r_j >= tau and g_j <= (1+e) tau, so r_j <= tau (1+e)/(1-e); one the oracle
+    evicts and the GPU keeps has r_j <= tau and r_j >= tau (1-e)/(1+e).
+    """
+    return (1.0 - e) / (1.0 + e), (1.0 + e) / (1.0 - e)
+
+
+def check_evictions(gpu_scores, gpu_idx, ref_P, ref_S, ref_idx, n_evict, rtol, report=None):
+    """Returns (n_exact_checked, jaccards). Asserts, per KV head:
+
+    (a) the GPU set is the bottom-n_evict of the GPU's own pooled scores
+        under (score, index), strictly ascending;
+    (b) gap rule: when the oracle's sorted pooled scores satisfy
+        P_(k+1) - P_(k) > 2 rtol P_(k), the GPU set equals the oracle's;
+    (c) plateau rule: when no oracle value other than tau = P_(k) (raw or
+        pooled) lies within 2 rtol of tau, the GPU set equals the oracle's
+        (pooling plateaus copy tau bit for bit on both sides);
+    (d) always: every index in the symmetric difference has an oracle pooled
+        score inside symdiff_band(e) around tau, e being this head's
+        measured largest relative error of the pooled scores (e <= rtol, so
+        the band lies inside tau (1 +- 2 rtol) to first order), and the two
+        one-sided differences have equal size.
+    `report` (a dict) counts heads per rule: gap, plateau, band, sizes of
+    the symmetric differences.
+    """
     gpu_scores = np.asarray(gpu_scores)
     gpu_idx = np.asarray(gpu_idx)
     exact, jac = 0, []
-    n = gpu_scores.shape[1]
+    rep = report if report is not None else {}
+    for key in ("heads", "gap_exact", "plateau_exact", "band_checked", "symdiff_max", "band_used_max"):
+        rep.setdefault(key, 0)
     for g in range(gpu_scores.shape[0]):
+        rep["heads"] += 1
         if n_evict == 0:
             assert gpu_idx.shape[1] == 0
             continue
@@ -68,14 +103,45 @@ def check_evictions(gpu_scores, gpu_idx, ref_P, ref_S, ref_idx, n_evict, rtol):
         ref = ref_idx[g]
         inter = np.intersect1d(ref, gpu_idx[g]).size
         jac.append(inter / max(1, np.union1d(ref, gpu_idx[g]).size))
-        tau = np.sort(ref_P[g])[n_evict - 1]
+        srt = np.sort(ref_P[g])
+        tau = srt[n_evict - 1]
+        nxt = srt[n_evict] if n_evict < srt.size else np.inf
+        # (b) the k-th / (k+1)-th gap rule
+        if nxt - tau > 2 * rtol * tau:
+            assert np.array_equal(gpu_idx[g], ref), f"head {g}: evicted set differs (gap rule)"
+            rep["gap_exact"] += 1
+            exact += 1
+            continue
+        # (c) no other oracle value near tau
         band = 2 * rtol * abs(tau)
         near_P = np.abs(ref_P[g] - tau) <= band
         near_S = np.abs(ref_S[g] - tau) <= band
         ambiguous = np.any(near_P & (ref_P[g] != tau)) or np.any(near_S & (ref_S[g] != tau))
         if not ambiguous:
-            assert np.array_equal(gpu_idx[g], ref), f"head {g}: evicted set differs from the oracle's"
+            assert np.array_equal(gpu_idx[g], ref), f"head {g}: evicted set differs (plateau rule)"
+            rep["plateau_exact"] += 1
             exact += 1
+            continue
+        # (d) every difference lies where the measured score error allows
+        e = max_rel_err(gpu_scores[g], ref_P[g])
+        assert e <= rtol, f"head {g}: pooled scores rel err {e:.3e}"
+        lo, hi = symdiff_band(e)
+        only_gpu = np.setdiff1d(gpu_idx[g], ref)
+        only_ref = np.setdiff1d(ref, gpu_idx[g])
+        assert only_gpu.size == only_ref.size, f"head {g}: one-sided differences of unequal size"
+        diff = np.concatenate([only_gpu, only_ref])
+        if diff.size:
+            rv = ref_P[g][diff]
+            slack = 1e-12 * tau
+            bad = (rv < tau * lo - slack) | (rv > tau * hi + slack)
+            assert not np.any(bad), (
+                f"head {g}: {int(bad.sum())} differing indices outside the error band "
+                f"[{tau * lo:.6e}, {tau * hi:.6e}] (e = {e:.3e}), e.g. index {int(diff[bad][0])} "
+                f"with oracle score {float(rv[bad][0]):.6e}")
+            used = float(np.max(np.abs(rv / tau - 1.0)))
+            rep["band_used_max"] = max(rep["band_used_max"], used)
+        rep["band_checked"] += 1
+        rep["symdiff_max"] = max(rep["symdiff_max"], int(only_gpu.size))
     return exact, jac
 
 

@@ -45,10 +45,11 @@ def test_binding_covers_only_declared_symbols():
 def test_header_status_codes_match_binding():
     text = open(HEADER).read()
     for name, val in [("DROPKV_OK", 0), ("DROPKV_ERR_INVALID", -1), ("DROPKV_ERR_SINGULAR", -2),
-                      ("DROPKV_ERR_NONFINITE", -3), ("DROPKV_ERR_DEVICE", -4)]:
+                      ("DROPKV_ERR_NONFINITE", -3), ("DROPKV_ERR_DEVICE", -4),
+                      ("DROPKV_ERR_NEGATIVE", -5), ("DROPKV_STATUS_NEGATIVE", 16)]:
         assert re.search(rf"{name}\s*=\s*{val}\b", text), name
     assert (binding.OK, binding.ERR_INVALID, binding.ERR_SINGULAR, binding.ERR_NONFINITE,
-            binding.ERR_DEVICE) == (0, -1, -2, -3, -4)
+            binding.ERR_DEVICE, binding.ERR_NEGATIVE, binding.STATUS_NEGATIVE) == (0, -1, -2, -3, -4, -5, 16)
     assert re.search(r"DROPKV_BF16\s*=\s*0", text) and re.search(r"DROPKV_F32\s*=\s*1", text)
 
 
@@ -73,6 +74,14 @@ def test_invalid_arguments_rejected_before_any_device_call(lib, bad):
                           args["d"], args["pool_kernel"], args["n_evict"], None, None, None)
     assert rc == binding.ERR_INVALID
     assert lib.dropkv_last_error().decode()
+
+
+def test_boundary_aliases_share_the_error_text(lib):
+    rc = lib.dropkv_score(None, None, None, 22, 3, 4, 2, 8, 3, 7, None, None, None)
+    assert rc == binding.ERR_INVALID
+    assert lib.dropkv_last_error_string() == lib.dropkv_last_error() != b""
+    rc = lib.dropkv_pass1_stats(None, None, None, 22, 0, 4, 2, 128, None, None, None, None, None)
+    assert rc == binding.ERR_INVALID
 
 
 def test_null_pointers_rejected(lib):

@@ -12,6 +12,7 @@ import numpy as np
 import pytest
 
 import oracle
+from brute_force import brute_force_joint
 from oracle.joint import approx_ratio, joint_objective
 
 
@@ -33,6 +34,39 @@ def test_single_token_joint_objective_is_the_score(seed):
             J = joint_objective(q, k, v, g, G, s["n"], s["window"], [j])
             assert abs(J - S[j]) <= 1e-12 * max(S[j], 1e-300)
         assert joint_objective(q, k, v, g, G, s["n"], s["window"], []) == 0.0
+
+
+@pytest.mark.parametrize("seed", [0, 1, 2, 3])
+def test_joint_objective_of_sets_equals_literal_deletion(seed):
+    """|E| >= 2: the joint objective against removing the whole set literally
+    (brute force: re-softmax over the visible keys outside E), including sets
+    that hold every evictable token of a row's view but one."""
+    q, k, v, s = _case(seed)
+    G = s["Hq"] // s["Hkv"]
+    n, w = s["n"], s["window"]
+    rng = np.random.default_rng(1000 + seed)
+    sets = [sorted(rng.choice(n - w, size=size, replace=False).tolist()) for size in (2, 3, 5, 8)]
+    sets.append(list(range(n - w)))          # every evictable token
+    sets.append(list(range(1, n - w)))       # all but the first
+    sets.append([0, n - w - 1])              # both ends of the evictable range
+    for g in range(s["Hkv"]):
+        for E in sets:
+            J = joint_objective(q, k, v, g, G, n, w, E)
+            B = brute_force_joint(q, k, v, g, G, n, w, E)
+            assert abs(J - B) <= 1e-12 * max(B, 1e-300), (g, E, J, B)
+
+
+def test_joint_objective_is_not_additive():
+    """Removing two tokens together differs from the sum of removing each:
+    a check that the set objective really renormalises once over the rest."""
+    q, k, v, s = _case(7)
+    G = s["Hq"] // s["Hkv"]
+    n, w = s["n"], s["window"]
+    J12 = joint_objective(q, k, v, 0, G, n, w, [1, 2])
+    J1 = joint_objective(q, k, v, 0, G, n, w, [1])
+    J2 = joint_objective(q, k, v, 0, G, n, w, [2])
+    assert abs(J12 - (J1 + J2)) > 1e-6 * J12
+    assert abs(J12 - brute_force_joint(q, k, v, 0, G, n, w, [1, 2])) <= 1e-12 * J12
 
 
 @pytest.mark.parametrize("seed", range(4))

@@ -164,6 +164,31 @@ def test_select_matches_stable_argsort(n, w, k, ne):
     assert np.array_equal(idx, ev_ref)
 
 
+@pytest.mark.parametrize("where", [0, 4095, 9000])
+def test_select_rejects_negative_scores(where):
+    """Given raw scores must be >= 0 (sums of squared norms): a negative entry
+    anywhere is reported; -0.0 is accepted and orders as +0."""
+    n, w, k, ne = 9001, 16, 7, 500
+    rng = np.random.default_rng(where)
+    S = rng.random((2, n)).astype(np.float32)
+    S[1, where] = -1e-30
+    with pytest.raises(K.DropKVNegativeScoreError):
+        K.select(torch.from_numpy(S).cuda(), window=w, pool_kernel=k, n_evict=ne)
+    S[1, where] = -0.0
+    P_ref = oracle.protect_window(oracle.maxpool1d_same(np.abs(S.astype(np.float64)), k), w)
+    scores, idx = K.select(torch.from_numpy(S).cuda(), window=w, pool_kernel=k, n_evict=ne)
+    assert np.array_equal(idx.cpu().numpy(), oracle.evict_smallest(P_ref, ne))
+
+
+def test_pass1_stats_name_matches_row_stats():
+    case = synth.make_case(synth.CONFIGS["llama_4k"])
+    q, k, v = to_torch(case)
+    a = K.row_stats(q, k, v)
+    b = K.pass1_stats(q, k, v)
+    for x, y in zip(a, b):
+        assert torch.equal(x, y)
+
+
 # ------------------------------------------------------------ failure paths ---
 
 def test_singular_row_rejected():

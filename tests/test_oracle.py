@@ -350,3 +350,43 @@ def test_sampled_token_scores_equal_full():
     for g in range(kw["Hkv"]):
         part = oracle.head_scores(q, k, v, g, kw["Hq"] // kw["Hkv"], kw["n"], kw["window"], tokens=toks)
         assert np.allclose(part["S"], full["S"][g, toks], rtol=1e-14)
+
+
+# ------------------------------------------------------- input decoding, argmax ---
+
+def test_bf16_bits_to_f64_matches_torch_every_pattern():
+    """Every one of the 65536 bf16 bit patterns decodes to the value torch's
+    bfloat16 -> float64 conversion gives (NaN patterns to NaN)."""
+    torch = pytest.importorskip("torch")
+    bits = np.arange(1 << 16, dtype=np.uint32).astype(np.uint16)
+    ours = oracle.bf16_bits_to_f64(bits)
+    ref = torch.from_numpy(bits.view(np.int16).copy()).view(torch.bfloat16).to(torch.float64).numpy()
+    nan = np.isnan(ref)
+    assert np.array_equal(np.isnan(ours), nan)
+    assert np.array_equal(ours[~nan], ref[~nan])
+    # signed zeros keep their sign
+    assert np.array_equal(np.signbit(ours[~nan]), np.signbit(ref[~nan]))
+
+
+@pytest.mark.parametrize("first,second", [(3, 7), (5, 2), (0, 9)])
+def test_argmax_tie_goes_to_lowest_index(first, second):
+    """Two identical dominant keys: every row that sees both reports the lower
+    index as its argmax, and its rest mass counts the other copy in full (R >= 1)."""
+    rng = np.random.default_rng(77)
+    Hq, Hkv, d, n, w = 2, 1, 8, 12, 2
+    q = rng.standard_normal((Hq, w, d))
+    k = rng.standard_normal((Hkv, n, d)) * 0.2
+    v = rng.standard_normal((Hkv, n, d))
+    u = q.reshape(-1, d).mean(axis=0)
+    u /= np.linalg.norm(u)
+    k[0, first] = 4.0 * math.sqrt(d) * u
+    k[0, second] = k[0, first]  # bit-identical keys: bit-identical logits
+    st = oracle.head_row_stats(q, k, v, 0, Hq, n, w)
+    lo = min(first, second)
+    x = st["x"]
+    for r in range(Hq * w):
+        top = np.max(x[r])
+        if x[r, first] == top:  # the planted pair is the maximum of this row
+            assert st["jstar"][r] == lo
+            assert st["rest"][r] >= 1.0
+    assert np.any(x[:, first] == x.max(axis=1)), "plant must dominate at least one row"
