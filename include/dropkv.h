@@ -120,6 +120,35 @@ int dropkv_score_ex(int32_t dtype, const void* q, const void* k, const void* v, 
                     int64_t n_evict, float* out_scores, int64_t* out_evict_idx, void* workspace,
                     size_t workspace_bytes, int32_t* d_status, uint32_t flags, void* stream);
 
+/* Size of the static scratch array behind dropkv_score_noalloc, per GPU. */
+#define DROPKV_NOALLOC_SCRATCH_BYTES (64ull << 20)
+
+/*
+ * For callers that cannot allocate device memory: code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc. The same
+ * scoring as dropkv_score_ex (same kernels, same outputs, bit for bit), with
+ * all scratch in a library-owned static device array of
+ * DROPKV_NOALLOC_SCRATCH_BYTES (64 MiB; every GPU the library runs on holds
+ * one until the process ends) instead of a workspace argument. The caller
+ * passes inputs, outputs and d_status (a device int32 that the call clears
+ * and ORs DROPKV_STATUS_* bits into) as for dropkv_score_ex.
+ * A shape whose dropkv_workspace_bytes exceeds the array is rejected with
+ * DROPKV_ERR_INVALID before anything is launched (the 128K-token Llama-3.1-8B
+ * layer, 32 query / 8 KV heads, window 64, needs about 60 MiB);
+ * DROPKV_FLAG_STAGE_LOG is rejected too. The call makes no hipMalloc,
+ * hipFree or other allocating call; its first call on a device looks up the
+ * array's device address once. Every call on one GPU uses that GPU's one
+ * array, which keeps the previous call's contents (everything that must start
+ * at zero is cleared by the call's own first kernel): calls that overlap on
+ * one GPU (several streams or threads) race and must be serialised by the
+ * caller. Asynchronous: device-side errors are visible in *d_status after the
+ * stream completes.
+ */
+int dropkv_score_noalloc(int32_t dtype, const void* q, const void* k, const void* v, int64_t n,
+                         int32_t window, int32_t Hq, int32_t Hkv, int32_t d, int32_t pool_kernel,
+                         int64_t n_evict, float* out_scores, int64_t* out_evict_idx, int32_t* d_status,
+                         uint32_t flags, void* stream);
+
 /*
  * Stage export: the GQA-mean scores S [Hkv][n] (fp32) before pooling and
  * protection. Synchronous like dropkv_score (returns SINGULAR / NONFINITE).

@@ -30,6 +30,8 @@ SIGNATURES = {
     "dropkv_workspace_bytes": (_sz, [_i32, _i64, _i32, _i32, _i32, _i32]),
     "dropkv_score_ex": (_i32, [_i32, _p, _p, _p, _i64, _i32, _i32, _i32, _i32, _i32, _i64, _p, _p,
                                _p, _sz, _p, _u32, _p]),
+    "dropkv_score_noalloc": (_i32, [_i32, _p, _p, _p, _i64, _i32, _i32, _i32, _i32, _i32, _i64, _p, _p,
+                                    _p, _u32, _p]),
     "dropkv_raw_scores": (_i32, [_i32, _p, _p, _p, _i64, _i32, _i32, _i32, _i32, _p, _u32, _p]),
     "dropkv_row_stats": (_i32, [_i32, _p, _p, _p, _i64, _i32, _i32, _i32, _i32, _p, _p, _p, _p,
                                 _u32, _p]),
@@ -191,6 +193,23 @@ def score_ex(q, k, v, *, pool_kernel: int, n_evict: int, workspace, status, scor
                              evict_idx.data_ptr() if n_evict > 0 else None, workspace.data_ptr(),
                              workspace.numel() * workspace.element_size(), status.data_ptr(),
                              flags, _stream_handle(stream))
+    _raise(rc)
+    return scores, evict_idx
+
+
+NOALLOC_SCRATCH_BYTES = 64 << 20
+
+
+def score_noalloc(q, k, v, *, pool_kernel: int, n_evict: int, status, scores, evict_idx, flags: int = 0,
+                  stream=None):
+    """dropkv_score_noalloc: scratch in the library's static device array, outputs
+    and the device status word given by the caller (nothing is allocated here)."""
+    lib = load_library()
+    Hq, Hkv, d, n, w = _shapes(q, k, v)
+    rc = lib.dropkv_score_noalloc(_dtype_code(q), q.data_ptr(), k.data_ptr(), v.data_ptr(), n, w, Hq, Hkv, d,
+                                  pool_kernel, n_evict, scores.data_ptr(),
+                                  evict_idx.data_ptr() if n_evict > 0 else None, status.data_ptr(), flags,
+                                  _stream_handle(stream))
     _raise(rc)
     return scores, evict_idx
 

@@ -34,6 +34,35 @@ struct DeviceWs {
 std::mutex g_ws_mutex;
 std::unordered_map<int, DeviceWs> g_ws;
 
+// Scratch of dropkv_score_noalloc: one static device array, which every GPU
+// the library runs on holds (at its own address) until the process ends. In
+// host code `scratch` names a host-side stand-in, not device memory: kernels
+// and copies get the device address from hipGetSymbolAddress, looked up once
+// per device (with that device current) and kept in g_scratch_dev.
+constexpr size_t kNoAllocScratchBytes = (size_t)DROPKV_NOALLOC_SCRATCH_BYTES;
+__device__ __align__(256) unsigned char scratch[kNoAllocScratchBytes];
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mutex;
+void* g_scratch_dev[kMaxDevices] = {};
+
+// Device address of the current device's scratch array (no allocation).
+int noalloc_scratch(void** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail_hip(e, "hipGetDevice");
+  if (dev < 0 || dev >= kMaxDevices) return fail(DROPKV_ERR_DEVICE, "device index beyond the scratch table");
+  std::lock_guard<std::mutex> lock(g_scratch_mutex);
+  if (!g_scratch_dev[dev]) {
+    void* ptr = nullptr;
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return fail_hip(e, "hipGetSymbolAddress(scratch)");
+    if (!ptr || ((uintptr_t)ptr & 255)) return fail(DROPKV_ERR_DEVICE, "scratch array address not 256-byte aligned");
+    g_scratch_dev[dev] = ptr;
+  }
+  *out = g_scratch_dev[dev];
+  return DROPKV_OK;
+}
+
 // Stage log: event sets of up to kLogCalls logged dropkv_score_ex calls per device.
 constexpr int kLogCalls = 256;
 struct StageLog {
@@ -363,6 +392,37 @@ int dropkv_score_ex(int32_t dtype, const void* q, const void* k, const void* v, 
   if (e != hipSuccess) return fail_hip(e, "select");
   e = record_stage(se, "select", st);
   if (e != hipSuccess) return fail_hip(e, "stage event");
+  return DROPKV_OK;
+}
+
+int dropkv_score_noalloc(int32_t dtype, const void* q, const void* k, const void* v, int64_t n,
+                         int32_t window, int32_t Hq, int32_t Hkv, int32_t d, int32_t pool_kernel,
+                         int64_t n_evict, float* out_scores, int64_t* out_evict_idx, int32_t* d_status,
+                         uint32_t flags, void* stream) {
+  g_last_error.clear();
+  if (flags & DROPKV_FLAG_STAGE_LOG) return fail(DROPKV_ERR_INVALID, "the stage log is not available without allocation");
+  if (const char* m = validate(dtype, n, window, Hq, Hkv, d)) return fail(DROPKV_ERR_INVALID, m);
+  if (const char* m = validate_select(n, window, Hkv, pool_kernel, n_evict))
+    return fail(DROPKV_ERR_INVALID, m);
+  const Shape s{n, window, Hq, Hkv, d};
+  const bool mfma = use_mfma(dtype, d, flags);
+  if (carve_workspace(nullptr, s, mfma).bytes > kNoAllocScratchBytes)
+    return fail(DROPKV_ERR_INVALID, "shape needs more scratch than DROPKV_NOALLOC_SCRATCH_BYTES (use dropkv_score_ex)");
+  if (int rc = check_inputs(q, k, v)) return rc;
+  if (!out_scores || !is_device_ptr(out_scores)) return fail(DROPKV_ERR_INVALID, "out_scores must be a device pointer");
+  if (n_evict > 0 && (!out_evict_idx || !is_device_ptr(out_evict_idx)))
+    return fail(DROPKV_ERR_INVALID, "out_evict_idx must be a device pointer when n_evict > 0");
+  if (!d_status || !is_device_ptr(d_status)) return fail(DROPKV_ERR_INVALID, "d_status must be a device pointer");
+  void* base = nullptr;
+  if (int rc = noalloc_scratch(&base)) return rc;
+  Workspace ws = carve_workspace(base, s, mfma);
+  ws.status = d_status;  // cleared by the path's first kernel, like every buffer that must start at zero
+  hipStream_t st = (hipStream_t)stream;
+  FoldInfo fold{};
+  if (int rc = run_scores(dtype, q, k, v, s, ws, mfma, st, nullptr, &fold)) return rc;
+  hipError_t e = launch_select(ws.S, n, window, Hkv, pool_kernel, n_evict, out_scores, out_evict_idx,
+                               ws.status, &fold, ws.sel, st);
+  if (e != hipSuccess) return fail_hip(e, "select");
   return DROPKV_OK;
 }
 
