@@ -7,14 +7,19 @@ pool/protect/select) over one Llama-3.1-8B-shaped layer: 32 query heads,
 with a planted attention sink and 64 needle keys, already resident in HBM
 when the timed region starts.
 
-Prints one JSON line: scored tokens/s for the layer, the dominant kernel's
-achieved HBM bandwidth against MI355X's 8 TB/s (per-kernel HIP events on the
-library's stream), and the fp64 CPU oracle timed on a bounded sample of the
-same workload (one KV head) as a reported baseline. After the timed steps it
-also times, apart from `value`: scoring from given row statistics, the
-Qwen2.5-7B-shaped 28-layer sweep, cache compaction and decode-time rescoring
-(first window, per appended token in the two-pass and the single-pass form,
-the flush of pending terms, re-eviction).
+Prints one JSON line: scored tokens/s for the layer (K steps back to back
+with nothing else on the stream), the median and minimum per-step time (the
+same K steps again, each bracketed by events), the dominant kernel's achieved
+HBM bandwidth against MI355X's 8 TB/s (K more steps with the library's
+per-kernel stage log), and the fp64 CPU oracle timed on a bounded sample of
+the same workload (one KV head) as a reported baseline. After the timed
+steps it also times, apart from `value`: the 4K and 32K Llama-shaped layers
+(both 32K budgets), scoring from given row statistics, the Qwen2.5-7B-shaped
+28-layer sweep (with its layers (0, 0) and (1, 27) scored on their own
+seeds, checked against the oracle on one head each, and the oracle's time
+extrapolated to the whole sweep), cache compaction and decode-time
+rescoring (first window, per appended token in the two-pass and the
+single-pass form, the flush of pending terms, re-eviction).
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
 """
@@ -112,6 +117,70 @@ def counted_traffic(kernel):
     return int(vals[kernel])
 
 
+def step_times(torch, fn, reps):
+    """Median and minimum of `reps` calls of fn, each bracketed by events on the current stream."""
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+    for a, b in evs:
+        a.record()
+        fn()
+        b.record()
+    torch.cuda.synchronize()
+    ms = sorted(a.elapsed_time(b) for a, b in evs)
+    return {"median": float(np.median(ms)), "min": float(ms[0]), "mean": float(np.mean(ms))}
+
+
+def time_layer(torch, K, synth, name, dev, warmup, steps, n_evict=None):
+    """Whole-path steps on one more synthetic workload: ms per step (mean of
+    `steps` back-to-back steps after `warmup`), per-step median/min, the
+    per-kernel means from the stage log, and the HBM fractions."""
+    cfg = synth.CONFIGS[name]
+    case = synth.make_case(cfg)
+    ne = cfg.n_evicts()[0] if n_evict is None else n_evict
+    q, k, v = (torch.from_numpy(t.view(np.int16)).view(torch.bfloat16).to(dev).contiguous()
+               for t in (case.q, case.k, case.v))
+    ws = torch.empty(K.workspace_bytes(K.BF16, case.n, case.window, case.Hq, case.Hkv, case.d),
+                     dtype=torch.uint8, device=dev)
+    st = torch.zeros(1, dtype=torch.int32, device=dev)
+    sc = torch.empty((case.Hkv, case.n), dtype=torch.float32, device=dev)
+    ix = torch.empty((case.Hkv, ne), dtype=torch.int64, device=dev)
+
+    def step(flags=0):
+        K.score_ex(q, k, v, pool_kernel=cfg.pool_kernel, n_evict=ne, workspace=ws, status=st, scores=sc,
+                   evict_idx=ix, flags=flags)
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        step()
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) * 1e3 / steps
+    per = step_times(torch, step, steps)
+    K.stage_log()
+    for _ in range(steps):
+        step(K.FLAG_STAGE_LOG)
+    torch.cuda.synchronize()
+    _, stages = K.stage_log()
+    if int(st.item()) != 0:
+        raise SystemExit(f"device status {int(st.item())} on {name}")
+    stage_ms = {a: b for a, b in stages}
+    pass_bytes = case.Hkv * case.n * case.d * 2 * 2
+    dom = max((x for x in ("pass1", "pass2") if x in stage_ms), key=lambda x: stage_ms[x])
+    out = {
+        "workload": f"{name}: Hq {case.Hq}, Hkv {case.Hkv}, d {case.d}, n {case.n}, window {case.window}, "
+                    f"pool {cfg.pool_kernel}, evict {ne} per head",
+        "ms_per_step": round(ms, 4), "ms_per_step_median": round(per["median"], 4),
+        "ms_per_step_min": round(per["min"], 4),
+        "tokens_per_s": round(case.n / (ms * 1e-3), 1),
+        "step_hbm_frac": round(2 * pass_bytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+        "dominant_kernel": dom,
+        "dominant_kernel_hbm_frac": round(pass_bytes / (stage_ms[dom] * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+        "stages_ms": {a: round(b, 4) for a, b in stage_ms.items()},
+    }
+    del q, k, v, ws
+    return out
+
+
 def copy_calibration():
     import torch
     dev = torch.device("cuda:0")
@@ -172,14 +241,13 @@ def main():
     torch.cuda.synchronize()
     if int(status.item()) != 0:
         raise SystemExit(f"device status {int(status.item())} after warm-up")
-    K.stage_log()  # start the timed region with an empty stage log
 
-    # timed region: K whole-path steps, synchronised on both sides; every step
-    # records a HIP event after each kernel on the library's stream (no sync)
+    # timed region: K whole-path steps back to back, synchronised on both
+    # sides, nothing else on the stream (value and ms_per_step come from here)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for _ in range(args.steps):
-        step(K.FLAG_STAGE_LOG)
+        step()
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     st_word = int(status.item())
@@ -188,7 +256,16 @@ def main():
     ms_per_step = (t1 - t0) * 1e3 / args.steps
     tokens_per_s = case.n / (ms_per_step * 1e-3)
 
-    # per-kernel mean durations over the timed steps, from their HIP events
+    # per-step distribution: the same K steps again, each bracketed by events
+    # on the stream the library launches on (the current torch stream)
+    per_step = step_times(torch, step, args.steps)
+
+    # per-kernel mean durations: K more steps with the library's stage log (a
+    # HIP event after every kernel on its stream)
+    K.stage_log()  # empty the log
+    for _ in range(args.steps):
+        step(K.FLAG_STAGE_LOG)
+    torch.cuda.synchronize()
     logged, stages = K.stage_log()
     stage_ms = {name: ms for name, ms in stages}
     kv_bytes_per_pass = case.Hkv * case.n * case.d * 2 * 2  # K and V read once
@@ -237,11 +314,26 @@ def main():
         "mfma": {"alg_flop": flops,
                  "achieved_TFLOPs": round(flops / (ms_per_step * 1e-3) / 1e12, 1),
                  "frac": round(flops / (ms_per_step * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4)},
+        "ms_per_step_median": round(per_step["median"], 4),
+        "ms_per_step_min": round(per_step["min"], 4),
         "stages_ms": {k_: round(v_, 4) for k_, v_ in stage_ms.items()},
+        "workspace_bytes": int(ws.numel()),
         "path": "mfma" if K.uses_mfma(dcode, case.d) else "generic",
         "git": git_sha(),
         "device": torch.cuda.get_device_name(dev),
     }
+
+    # The shorter Llama-3.1-8B-shaped layers (4K; 32K at both budgets), timed
+    # the same way, apart from `value`.
+    if args.workload == "llama_128k" and not args.no_extras:
+        c3 = synth.CONFIGS["llama_32k"]
+        rec["workloads"] = {
+            "llama_4k": time_layer(torch, K, synth, "llama_4k", dev, args.warmup, args.steps),
+            "llama_32k_keep5": time_layer(torch, K, synth, "llama_32k", dev, args.warmup, args.steps,
+                                          c3.n_evicts()[0]),
+            "llama_32k_keep20": time_layer(torch, K, synth, "llama_32k", dev, args.warmup, args.steps,
+                                           c3.n_evicts()[1]),
+        }
 
     # Scoring from given row statistics (no pass 1; the step a prefill kernel's
     # statistics would allow), timed apart from the scoring steps above.
@@ -309,6 +401,19 @@ def main():
             "mfma_TFLOPs": round(q_flop / (q_ms * 1e-3) / 1e12, 1),
             "mfma_frac": round(q_flop / (q_ms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),
         }
+        # the sweep's sampled layers with their own seeds, (sequence, layer) = (0, 0)
+        # and (1, 27): scored once each here, checked against the oracle below
+        qwen_layers = {}
+        for b_, l_ in ((0, 0), (1, 27)):
+            lc = synth.make_case(qcfg, layer=l_, b=b_)
+            lq, lk, lv = (to_dev(t).contiguous() for t in (lc.q, lc.k, lc.v))
+            K.score_ex(lq, lk, lv, pool_kernel=qcfg.pool_kernel, n_evict=qne, workspace=qws, status=qst,
+                       scores=qsc, evict_idx=qix)
+            torch.cuda.synchronize()
+            if int(qst.item()) != 0:
+                raise SystemExit(f"device status {int(qst.item())} on Qwen layer {(b_, l_)}")
+            qwen_layers[(b_, l_)] = (lc, qsc.cpu().numpy(), qix.cpu().numpy())
+            del lq, lk, lv
         del qq, qk, qv, qws
 
     # Cache compaction (the step after scoring), timed apart from the scoring
@@ -450,6 +555,36 @@ def main():
         }
         rec["parity_sample"] = {"head": head, "max_rel_err": rel, "evict_set_equal": same_set,
                                 "jaccard": round(float(jac), 6)}
+        if args.workload == "llama_128k" and not args.no_extras:
+            # the Qwen2.5-7B-shaped sweep: the oracle on KV head 0 of the two
+            # sampled layers, extrapolated to all heads and all 56 calls
+            qcfg = synth.CONFIGS["qwen_128k_sweep"]
+            qne = qcfg.n_evicts()[0]
+            times, checks = [], []
+            for (b_, l_), (lc, qsc_np, qix_np) in qwen_layers.items():
+                t_q = time.perf_counter()
+                qref = oracle.dropkv_oracle(lc.q, lc.k, lc.v, n=lc.n, window=lc.window, Hq=lc.Hq,
+                                            Hkv=lc.Hkv, d=lc.d, pool_kernel=qcfg.pool_kernel, n_evict=qne,
+                                            dtype=lc.dtype, heads=[0])
+                times.append(time.perf_counter() - t_q)
+                Pq = qref["P"][0]
+                fq = np.isfinite(Pq)
+                rq = float(np.max(np.abs(qsc_np[0][fq].astype(np.float64) - Pq[fq]) / np.abs(Pq[fq])))
+                jq = (np.intersect1d(qix_np[0], qref["evict"][0]).size
+                      / np.union1d(qix_np[0], qref["evict"][0]).size)
+                checks.append({"seq": b_, "layer": l_, "head": 0, "max_rel_err": rq,
+                               "jaccard": round(float(jq), 6)})
+            t_head = float(np.mean(times))
+            calls = qcfg.layers * qcfg.batch
+            rec["qwen_sweep"]["cpu_baseline_extrapolated"] = {
+                "value": round(qcfg.n / (t_head * qcfg.Hkv), 2), "unit": "tokens/s",
+                "cores": blas_threads or ncores, "kind": "oracle",
+                "sweep_s": round(t_head * qcfg.Hkv * calls, 1),
+                "sample": (f"fp64 numpy oracle on KV head 0 of {qcfg.Hkv} of (sequence, layer) = (0, 0) and "
+                           f"(1, 27), {t_head:.1f} s per head, extrapolated x{qcfg.Hkv} heads x{calls} calls "
+                           f"(EXTRAPOLATED, not run in full)"),
+            }
+            rec["qwen_sweep"]["parity_sample"] = checks
     line = json.dumps(rec)
     print(line, flush=True)
     if args.out:
