@@ -37,6 +37,7 @@ __all__ = [
     "n_evict_for_keep_pct",
     "make_case",
     "make_gaussian_case",
+    "prefill_queries",
 ]
 
 
@@ -231,3 +232,20 @@ def make_case(cfg: Config, *, layer: int = 0, b: int = 0, dtype: Optional[str] =
                               dtype=dtype or cfg.dtype, seeds=seeds,
                               one_stream_seed=one_stream_seed,
                               sink=cfg.sink, needles=cfg.needles)
+
+
+def prefill_queries(case: Case, seed: int) -> np.ndarray:
+    """Queries of every position for a prefill of `case`: [Hq][n][d].
+
+    The last `window` positions hold the case's own window queries; the
+    earlier positions are N(0,1) draws from their own PCG64 stream (`seed`),
+    rounded like the case's tensors (bf16 bit patterns or float32).
+    """
+    rng = np.random.default_rng(seed)
+    prefix = _normal(rng, (case.Hq, case.n - case.window, case.d))
+    if case.dtype == "bf16":
+        prefix = bf16_round_bits(prefix)
+    out = np.empty((case.Hq, case.n, case.d), dtype=case.q.dtype)
+    out[:, : case.n - case.window] = prefix
+    out[:, case.n - case.window:] = case.q
+    return out

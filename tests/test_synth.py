@@ -55,3 +55,13 @@ def test_budget_to_evict_count():
     assert synth.CONFIGS["llama_32k"].n_evicts() == (31130, 26215)
     assert synth.CONFIGS["llama_128k"].n_evicts() == (124519,)
     assert synth.CONFIGS["tiny"].n_evicts() == (7,)
+
+
+def test_prefill_queries_end_with_the_window_queries():
+    cfg = synth.CONFIGS["llama_4k"]
+    case = synth.make_case(cfg)
+    qa = synth.prefill_queries(case, seed=7)
+    assert qa.shape == (case.Hq, case.n, case.d) and qa.dtype == case.q.dtype
+    assert np.array_equal(qa[:, case.n - case.window:], case.q)
+    assert np.array_equal(qa, synth.prefill_queries(case, seed=7))
+    assert not np.array_equal(qa[:, :8], synth.prefill_queries(case, seed=8)[:, :8])
