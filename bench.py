@@ -363,6 +363,48 @@ def main():
             "evict_equal": bool(torch.equal(fs_ix, evict)),
         }
 
+    # Prefill attention at this layer's shape, handing the window rows'
+    # statistics to scoring (the producer of scoring from statistics): its
+    # kernel time and MFMA rate (causal: 4 d sum_pos (pos + 1) flops per query
+    # head), and prefill + scoring from its statistics against prefill + the
+    # two-pass scoring step.
+    if args.workload == "llama_128k" and K.uses_mfma(dcode, case.d) and not args.no_extras:
+        qa_np = synth.prefill_queries(case, seed=cfg.seeds[0] + 7)
+        q_all = torch.from_numpy(qa_np.view(np.int16)).view(torch.bfloat16).to(dev).contiguous()
+        del qa_np
+        o_buf = torch.empty((case.Hq, case.n, case.d), dtype=torch.bfloat16, device=dev)
+        pst = torch.zeros(1, dtype=torch.int32, device=dev)
+        outs = K.prefill_attention(q_all, k, v, window=case.window, status=pst, out_o=o_buf)
+        torch.cuda.synchronize()
+        reps = 3
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            outs = K.prefill_attention(q_all, k, v, window=case.window, status=pst, out_o=o_buf)
+        e1.record()
+        torch.cuda.synchronize()
+        if int(pst.item()) != 0:
+            raise SystemExit(f"prefill status {int(pst.item())}")
+        p_ms = e0.elapsed_time(e1) / reps
+        _, pm, prest, parg, pa = outs
+        pf_sc = torch.empty_like(scores)
+        pf_ix = torch.empty_like(evict)
+        K.score_from_stats(q, k, v, pm, prest, parg, pa, pool_kernel=cfg.pool_kernel, n_evict=n_evict,
+                           workspace=ws, status=status, scores=pf_sc, evict_idx=pf_ix)
+        torch.cuda.synchronize()
+        p_flop = 4 * case.d * case.Hq * case.n * (case.n + 1) // 2
+        rec["prefill"] = {
+            "workload": "causal prefill attention of the same layer (all 131072 positions, 32 query heads), "
+                        "window statistics handed to scoring",
+            "ms": round(p_ms, 3), "flop": p_flop,
+            "mfma_TFLOPs": round(p_flop / (p_ms * 1e-3) / 1e12, 1),
+            "mfma_frac": round(p_flop / (p_ms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),
+            "scores_from_prefill_stats_max_rel_diff": float(
+                (pf_sc - scores).abs().div(scores.abs().clamp_min(1e-30)).nan_to_num(0.0).max().item()),
+            "evict_equal_to_step": bool(torch.equal(pf_ix, evict)),
+        }
+        del q_all, o_buf, outs
+
     # The Qwen2.5-7B-shaped sweep (28 layers x 2 sequences of one 128K layer
     # shape, G = 7), back to back on one stream; MFMA-bound by its arithmetic
     # intensity. One generated layer's tensors serve every call (the throughput
@@ -415,6 +457,11 @@ def main():
             qwen_layers[(b_, l_)] = (lc, qsc.cpu().numpy(), qix.cpu().numpy())
             del lq, lk, lv
         del qq, qk, qv, qws
+
+    if "prefill" in rec and "from_stats" in rec:
+        rec["prefill"]["prefill_plus_scoring_from_stats_ms"] = round(
+            rec["prefill"]["ms"] + rec["from_stats"]["ms_per_step"], 3)
+        rec["prefill"]["prefill_plus_scoring_step_ms"] = round(rec["prefill"]["ms"] + ms_per_step, 3)
 
     # Cache compaction (the step after scoring), timed apart from the scoring
     # steps above: copies each head's kept rows of K and V into a compact cache.

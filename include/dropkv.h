@@ -253,6 +253,35 @@ int dropkv_score_from_stats_ex(const void* q, const void* k, const void* v, int6
                                size_t workspace_bytes, int32_t* d_status, void* stream);
 
 /*
+ * Prefill attention that hands over the scoring statistics (the step before
+ * scoring: a prefill pass has already attended the window rows, so scoring
+ * from its statistics reads K and V once instead of twice). For every query
+ * head h and position pos (keys 0..pos of KV head h / (Hq / Hkv) visible),
+ * p = softmax(K q / sqrt(d)) and o = sum_j p_j v_j (DropKV write-up, section
+ * 核心公式; the atlas summary of the paper, Experimental setup, names
+ * FlashAttention-2 as the basis of the paper's scorer). bf16 with d = 128 only;
+ * Hq / Hkv <= 32.
+ *   q_all      [Hq][n][d]        bf16, the queries of every position
+ *   k, v       [Hkv][n][d]       bf16
+ *   out_o      [Hq][n][d]        bf16, o of every position
+ * and for the last `window` positions, window row r = h * window + i at
+ * position n - window + i (the layout dropkv_score_from_stats reads):
+ *   out_m      [Hq*window]       fp32, largest logit x_max (x = q.k / sqrt(d))
+ *   out_rest   [Hq*window]       fp32, R = sum_{j != argmax} exp(x_j - x_max), formed
+ *                                as (sum_j exp(x_j - x_max)) - 1 (exact where R < 1 is
+ *                                not needed: scoring recomputes the argmax term then)
+ *   out_argmax [Hq*window]       int32, lowest index attaining x_max
+ *   out_a      [Hq*window][d]    fp32, o of the window rows
+ * All pointers are caller-owned device memory; every output is required.
+ * Asynchronous on `stream`: *d_status is cleared, then DROPKV_STATUS_NONFINITE
+ * is ORed in for non-finite statistics. DROPKV_ERR_INVALID before any launch
+ * for bad shapes or pointers.
+ */
+int dropkv_prefill_attention(const void* q_all, const void* k, const void* v, int64_t n, int32_t window,
+                             int32_t Hq, int32_t Hkv, int32_t d, void* out_o, float* out_m, float* out_rest,
+                             int32_t* out_argmax, float* out_a, int32_t* d_status, void* stream);
+
+/*
  * Cache compaction, the step after scoring (write-up section 代码映射与边界:
  * the scorer returns per-head eviction indices and the caller drops those
  * tokens from its cache). Copies the rows of k and v [Hkv][n][d] (dtype

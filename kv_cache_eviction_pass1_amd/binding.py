@@ -44,6 +44,8 @@ SIGNATURES = {
                                        _p, _p, _p, _p, _p]),
     "dropkv_score_from_stats_ex": (_i32, [_p, _p, _p, _i64, _i32, _i32, _i32, _i32, _i32, _i64, _p,
                                           _p, _p, _p, _p, _p, _p, _sz, _p, _p]),
+    "dropkv_prefill_attention": (_i32, [_p, _p, _p, _i64, _i32, _i32, _i32, _i32, _p, _p, _p, _p, _p, _p,
+                                        _p]),
     "dropkv_compact": (_i32, [_i32, _p, _p, _i64, _i32, _i32, _p, _i64, _p, _p, _p, _p]),
     "dropkv_decode_state_bytes": (_sz, [_i64, _i32, _i32, _i32, _i32]),
     "dropkv_decode_init": (_i32, [_p, _p, _p, _i64, _i64, _i32, _i32, _i32, _i32, _p, _sz, _p, _p]),
@@ -305,6 +307,38 @@ def score_from_stats(q, k, v, m, rest, argmax, a, *, pool_kernel: int, n_evict: 
         rc = lib.dropkv_score_from_stats(*ptrs, _stream_handle(stream))
     _raise(rc)
     return scores, evict_idx
+
+
+def prefill_attention(q_all, k, v, *, window: int, status=None, out_o=None, stream=None):
+    """Causal prefill attention of bf16 q_all [Hq, n, d] against k, v [Hkv, n, d]:
+    returns (o [Hq, n, d] bf16, m, rest, argmax, a) where the last four are the
+    window rows' statistics in the layout score_from_stats takes. Asynchronous:
+    `status` (int32 GPU tensor of one element, allocated if None) receives the
+    STATUS_* bits."""
+    torch = _torch()
+    lib = load_library()
+    if q_all.dim() != 3 or k.dim() != 3 or v.dim() != 3 or tuple(k.shape) != tuple(v.shape):
+        raise DropKVInvalidError(ERR_INVALID, "q_all must be [Hq, n, d], k and v [Hkv, n, d]")
+    Hq, n, d = q_all.shape
+    Hkv = k.shape[0]
+    if k.shape[1] != n or k.shape[2] != d:
+        raise DropKVInvalidError(ERR_INVALID, "q_all/k/v shapes disagree")
+    for t in (q_all, k, v):
+        if not t.is_cuda or not t.is_contiguous() or t.dtype != torch.bfloat16:
+            raise DropKVInvalidError(ERR_INVALID, "q_all, k, v must be contiguous bf16 GPU tensors")
+    dev = q_all.device
+    rows = Hq * window
+    o = out_o if out_o is not None else torch.empty((Hq, n, d), dtype=torch.bfloat16, device=dev)
+    m = torch.empty(rows, dtype=torch.float32, device=dev)
+    rest = torch.empty(rows, dtype=torch.float32, device=dev)
+    arg = torch.empty(rows, dtype=torch.int32, device=dev)
+    a = torch.empty((rows, d), dtype=torch.float32, device=dev)
+    st = status if status is not None else torch.zeros(1, dtype=torch.int32, device=dev)
+    rc = lib.dropkv_prefill_attention(q_all.data_ptr(), k.data_ptr(), v.data_ptr(), n, window, Hq, Hkv, d,
+                                      o.data_ptr(), m.data_ptr(), rest.data_ptr(), arg.data_ptr(), a.data_ptr(),
+                                      st.data_ptr(), _stream_handle(stream))
+    _raise(rc)
+    return o, m, rest, arg, a
 
 
 def compact(k, v, evict_idx, *, status=None, out_k=None, out_v=None, stream=None):

@@ -426,6 +426,23 @@ int dropkv_score_noalloc(int32_t dtype, const void* q, const void* k, const void
   return DROPKV_OK;
 }
 
+int dropkv_prefill_attention(const void* q_all, const void* k, const void* v, int64_t n, int32_t window,
+                             int32_t Hq, int32_t Hkv, int32_t d, void* out_o, float* out_m, float* out_rest,
+                             int32_t* out_argmax, float* out_a, int32_t* d_status, void* stream) {
+  g_last_error.clear();
+  if (const char* m = validate(DROPKV_BF16, n, window, Hq, Hkv, d)) return fail(DROPKV_ERR_INVALID, m);
+  if (!mfma_supported(DROPKV_BF16, d)) return fail(DROPKV_ERR_INVALID, "prefill attention needs bf16 inputs with d = 128");
+  if (Hq / Hkv > 32) return fail(DROPKV_ERR_INVALID, "prefill attention takes at most 32 query heads per KV head");
+  if (int rc = check_inputs(q_all, k, v)) return rc;
+  for (const void* p : {(const void*)out_o, (const void*)out_m, (const void*)out_rest, (const void*)out_argmax,
+                        (const void*)out_a, (const void*)d_status})
+    if (!p || !is_device_ptr(p)) return fail(DROPKV_ERR_INVALID, "outputs and d_status must be device pointers");
+  hipError_t e = launch_prefill(q_all, k, v, n, window, Hq, Hkv, out_o, out_m, out_rest, out_argmax, out_a,
+                                out_rest, out_argmax, d_status, (hipStream_t)stream);
+  if (e != hipSuccess) return fail_hip(e, "prefill attention");
+  return DROPKV_OK;
+}
+
 int dropkv_raw_scores(int32_t dtype, const void* q, const void* k, const void* v, int64_t n,
                       int32_t window, int32_t Hq, int32_t Hkv, int32_t d, float* out_S,
                       uint32_t flags, void* stream) {

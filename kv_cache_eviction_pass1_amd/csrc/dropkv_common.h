@@ -125,6 +125,13 @@ hipError_t launch_mfma_rowstats(const void* q, const void* k, const void* v, con
                                 const Workspace& ws, hipStream_t st, FoldInfo* fold);
 hipError_t launch_fold(const FoldInfo& fold, int64_t n, int32_t Hkv, float* S, int32_t* status,
                        hipStream_t st);
+// Prefill attention (bf16, d = 128; mfma_path.hip): O [Hq][n][d] for every
+// position and, for the last w positions (row r = h * w + i), the largest
+// logit m (natural units), the rest mass R, the argmax and the output a in
+// fp32. ws_L, ws_best: scratch of Hq * w floats / ints. Clears *status first.
+hipError_t launch_prefill(const void* q_all, const void* k, const void* v, int64_t n, int32_t w, int32_t Hq,
+                          int32_t Hkv, void* o, float* m, float* rest, int32_t* argmax, float* a, float* ws_L,
+                          int32_t* ws_best, int32_t* status, hipStream_t st);
 bool mfma_supported(int dtype, int d);
 int mfma_chunks(const Shape& s);
 size_t mfma_extra_bytes(const Shape& s);

@@ -1393,4 +1393,237 @@ hipError_t launch_mfma_from_stats(const void* q, const void* k, const void* v, c
   return hipGetLastError();
 }
 
+
+// ---------------------------------------------------------------------------- prefill attention
+//
+// Causal prefill attention of every position (the pass a prefill runs
+// anyway), which also hands over the window rows' statistics that scoring
+// from given statistics consumes (largest logit, rest mass, argmax, output),
+// so that scoring reads K and V once more instead of twice. DropKV write-up,
+// section 核心公式: p = softmax(K q / sqrt d), a = sum_j p_j v_j, each row
+// seeing keys 0..its position; the atlas summary (Experimental setup) names
+// FlashAttention-2 as the basis of the paper's scorer.
+//
+// One workgroup per (block of PB consecutive positions, KV head): its rows
+// are the G query heads of that KV head at those positions (row r: head
+// g G + r / PB, position p0 + r % PB), so each K/V tile read serves all G
+// heads. The workgroup streams K/V tiles 0 .. (p0 + PB - 1) / 64 through LDS
+// exactly as pass 1 does (the same tile routine: QK^T and PV on MFMA, online
+// softmax with a lazy reference), masks the diagonal tiles, and writes O in
+// bf16. Blocks are taken heaviest (last) first.
+
+namespace {
+
+struct PrefillArgs {
+  const uint16_t* q;  // [Hq][n][d]
+  const uint16_t* k;  // [Hkv][n][d]
+  const uint16_t* v;
+  int64_t n;
+  int w, G, PB, Rg, nblk, Hkv;
+  float c2, inv_sqrt_d;
+  uint16_t* o;         // [Hq][n][d] bf16
+  float* m;            // window row r = h * w + i: largest logit (natural units)
+  float* L;            // 1 + R relative to the largest logit
+  int32_t* best;       // 32-token block where the largest logit first occurs
+  float* a;            // [Hq * w][d] output in fp32
+};
+
+template <int NW>
+__global__ __launch_bounds__(NW * 64) void k_prefill(PrefillArgs A) {
+  __shared__ __attribute__((aligned(1024))) char kbuf[3][TILE_BYTES];
+  __shared__ __attribute__((aligned(1024))) char vbuf[3][TILE_BYTES];
+  constexpr int kDmaPerTile = 32 / NW;
+  const int blk = A.nblk - 1 - (int)blockIdx.x;  // heaviest first
+  const int g = blockIdx.y;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
+  const int h = lane >> 5, l32 = lane & 31;
+  const int64_t p0 = (int64_t)blk * A.PB;
+  const int row = wave * 32 + l32;
+  const int t = row / A.PB;
+  const int64_t pos = p0 + row % A.PB;
+  const bool row_ok = row < A.Rg && pos < A.n;
+  const bool active = wave * 32 < A.Rg;
+  int64_t nkeys = p0 + A.PB;  // keys 0 .. nkeys - 1 are visible to some row
+  if (nkeys > A.n) nkeys = A.n;
+  const int ntiles = (int)((nkeys + TT - 1) / TT);
+  const int nclean = (int)((p0 + 1) / TT) < ntiles ? (int)((p0 + 1) / TT) : ntiles;  // tiles every row sees whole
+  const uint16_t* kh = A.k + (size_t)g * A.n * HD;
+  const uint16_t* vh = A.v + (size_t)g * A.n * HD;
+  const int qh = g * A.G + (row_ok ? t : 0);
+  const float c2 = A.c2;
+  const LdsOff off = lds_offsets(lane);
+  const DmaOff<NW> doff = dma_offsets<NW>(wave, lane);
+
+  bf16x8 qb[8];
+  {
+    const uint16_t* qr = A.q + ((size_t)qh * A.n + (row_ok ? pos : 0)) * HD;
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks) {
+      bf16x8 tq = *(const bf16x8*)(qr + ks * 16 + h * 8);
+      if (!row_ok) tq = bf16x8{};
+      qb[ks] = tq;
+    }
+  }
+  P1State st{-INFINITY, -INFINITY, 0.f, -1};
+  f32x16 O[4];
+#pragma unroll
+  for (int db = 0; db < 4; ++db) O[db] = f32x16{};
+
+  if (ntiles > 0) {
+    issue_any<NW>(kh, 0, nkeys, kbuf[0], wave, lane, doff);
+    issue_any<NW>(vh, 0, nkeys, vbuf[0], wave, lane, doff);
+  }
+  if (ntiles > 1) {
+    issue_any<NW>(kh, TT, nkeys, kbuf[1], wave, lane, doff);
+    issue_any<NW>(vh, TT, nkeys, vbuf[1], wave, lane, doff);
+  }
+  // per tile and wave the only vector-memory ops are the tile loads, so
+  // `vmcnt <= one tile's loads` at the top of tile t + 1 means it has landed
+  auto head = [&](int tt, char* kn, char* vn) {
+    const int64_t tb = (int64_t)tt * TT;
+    if (tt + 1 < ntiles) wait_vmcnt<kDmaPerTile>(); else wait_vmcnt<0>();
+    lds_barrier();
+    if (tt + 2 < ntiles) {
+      issue_any<NW>(kh, tb + 2 * TT, nkeys, kn, wave, lane, doff);
+      issue_any<NW>(vh, tb + 2 * TT, nkeys, vn, wave, lane, doff);
+    }
+  };
+  auto clean = [&](auto bc, int tt) {
+    constexpr int B = decltype(bc)::value;
+    constexpr int N2 = (B + 2) % 3;
+    head(tt, kbuf[N2], vbuf[N2]);
+    if (active) p1_tile<false>(c2, kbuf[B], vbuf[B], (int64_t)tt * TT, off, lane, pos, qb, st, O);
+  };
+  int tt = 0;
+  for (; tt + 3 <= nclean; tt += 3) {
+    clean(IntC<0>{}, tt);
+    clean(IntC<1>{}, tt + 1);
+    clean(IntC<2>{}, tt + 2);
+  }
+  for (; tt < ntiles; ++tt) {  // at most two clean tiles, then the diagonal ones
+    const int b = tt % 3, nb = (tt + 2) % 3;
+    head(tt, kbuf[nb], vbuf[nb]);
+    if (active) p1_tile<true>(c2, kbuf[b], vbuf[b], (int64_t)tt * TT, off, lane, pos, qb, st, O);
+  }
+  if (!active) return;
+  const float l_tot = pair_sum(st.l);
+  if (!row_ok) return;
+  const float inv_l = 1.0f / l_tot;
+  // lane holds O^T rows d = 32 db + 8 i + 4 h + (0..3) of its row's column
+  uint16_t* orow = A.o + ((size_t)qh * A.n + pos) * HD;
+#pragma unroll
+  for (int db = 0; db < 4; ++db)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int d0 = 32 * db + 8 * i + 4 * h;
+      uint2 pk;
+      pk.x = (uint32_t)f32_to_bf16_rne(O[db][4 * i] * inv_l) | ((uint32_t)f32_to_bf16_rne(O[db][4 * i + 1] * inv_l) << 16);
+      pk.y = (uint32_t)f32_to_bf16_rne(O[db][4 * i + 2] * inv_l) |
+             ((uint32_t)f32_to_bf16_rne(O[db][4 * i + 3] * inv_l) << 16);
+      *(uint2*)(orow + d0) = pk;
+    }
+  if (pos >= A.n - A.w) {
+    const int64_t wr = (int64_t)qh * A.w + (pos - (A.n - A.w));
+    float* ar = A.a + wr * HD;
+#pragma unroll
+    for (int db = 0; db < 4; ++db)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        float4 ov = {O[db][4 * i] * inv_l, O[db][4 * i + 1] * inv_l, O[db][4 * i + 2] * inv_l,
+                     O[db][4 * i + 3] * inv_l};
+        *(float4*)(ar + 32 * db + 8 * i + 4 * h) = ov;
+      }
+    if (h == 0) {
+      A.m[wr] = st.m_true * A.inv_sqrt_d;
+      // l is relative to the reference exponent mref; L = l 2^(mref - x_max c)
+      A.L[wr] = l_tot * __builtin_amdgcn_exp2f(st.mref - st.m_true * c2);
+      A.best[wr] = st.best;
+    }
+  }
+}
+
+__global__ void k_zero_word(int32_t* p) {
+  if (threadIdx.x == 0) *p = 0;
+}
+
+struct PrefillArgmaxArgs {
+  const uint16_t* q;  // [Hq][n][d]
+  const uint16_t* k;
+  int64_t n;
+  int w, G, Hq;
+  const float* L;
+  const int32_t* best;
+  float* rest;        // out: R = L - 1
+  int32_t* argmax;    // out: lowest index attaining the largest logit (search in its 32-token block)
+  int32_t* status;
+};
+
+// One wave per window row: R from L, and the argmax inside the 32-token
+// block where the running maximum was set (logits recomputed in fp32 from the
+// bf16 inputs, lowest index on ties, as the merge of the scoring path does).
+__global__ __launch_bounds__(256) void k_prefill_argmax(PrefillArgmaxArgs P) {
+  const int lane = threadIdx.x & 63;
+  const int64_t wr = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (wr >= (int64_t)P.Hq * P.w) return;
+  const int qh = (int)(wr / P.w);
+  const int64_t pos = P.n - P.w + wr % P.w;
+  const int g = qh / P.G;
+  const int bt = P.best[wr];
+  const int64_t tok = (int64_t)bt * 32 + (lane & 31);
+  float x = -INFINITY;
+  if (lane < 32 && bt >= 0 && tok <= pos) {
+    const uint16_t* qr = P.q + ((size_t)qh * P.n + pos) * HD;
+    const uint16_t* kr = P.k + ((size_t)g * P.n + tok) * HD;
+    float acc = 0.f;
+    for (int c = 0; c < HD; ++c) acc = fmaf(bf16_to_f32(qr[c]), bf16_to_f32(kr[c]), acc);
+    x = acc;
+  }
+  int jt = (x == -INFINITY) ? 0x7fffffff : (int)tok;
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    const float xo = __shfl_xor(x, o, 64);
+    const int jo = __shfl_xor(jt, o, 64);
+    if (xo > x || (xo == x && jo < jt)) { x = xo; jt = jo; }
+  }
+  if (lane == 0) {
+    const float L = P.L[wr];
+    P.rest[wr] = L - 1.0f;
+    P.argmax[wr] = (jt == 0x7fffffff) ? -1 : jt;
+    if (!finite_f(L) || jt == 0x7fffffff) atomicOr(P.status, kStatusNonFinite);
+  }
+}
+
+}  // namespace
+
+// Prefill attention (bf16, d = 128): O for every position, and the window
+// rows' statistics m, R (rest), argmax and a. ws_L / ws_best (Hq * w each)
+// hold 1 + R and the 32-token block of the maximum between the two kernels;
+// they may be rest / argmax themselves (the second kernel converts each row
+// in place).
+hipError_t launch_prefill(const void* q_all, const void* k, const void* v, int64_t n, int32_t w, int32_t Hq,
+                          int32_t Hkv, void* o, float* m, float* rest, int32_t* argmax, float* a, float* ws_L,
+                          int32_t* ws_best, int32_t* status, hipStream_t st) {
+  const int G = Hq / Hkv;
+  int PB = (256 / G) / 32 * 32;  // positions per workgroup: G PB rows, at most 256
+  if (PB < 8) PB = 256 / G;
+  const int Rg = G * PB;
+  const int nblk = (int)((n + PB - 1) / PB);
+  int nw = MAXW;
+  while (nw > 1 && (nw / 2) * 32 >= Rg) nw /= 2;
+  PrefillArgs pa{(const uint16_t*)q_all, (const uint16_t*)k, (const uint16_t*)v, n, w, G, PB, Rg, nblk, Hkv,
+                 kLog2e / sqrtf((float)HD), 1.0f / sqrtf((float)HD), (uint16_t*)o, m, ws_L, ws_best, a};
+  k_zero_word<<<1, 64, 0, st>>>(status);  // the status word starts clear (a kernel, so the call can be captured)
+  const dim3 grid(nblk, Hkv);
+  switch (nw) {
+    case 8: k_prefill<8><<<grid, 512, 0, st>>>(pa); break;
+    case 4: k_prefill<4><<<grid, 256, 0, st>>>(pa); break;
+    case 2: k_prefill<2><<<grid, 128, 0, st>>>(pa); break;
+    default: k_prefill<1><<<grid, 64, 0, st>>>(pa); break;
+  }
+  PrefillArgmaxArgs pm{(const uint16_t*)q_all, (const uint16_t*)k, n, w, G, Hq, ws_L, ws_best, rest, argmax, status};
+  const int64_t rows = (int64_t)Hq * w;
+  k_prefill_argmax<<<(unsigned)((rows + 3) / 4), 256, 0, st>>>(pm);
+  return hipGetLastError();
+}
+
 }  // namespace dropkv
