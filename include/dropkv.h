@@ -76,7 +76,9 @@ enum {
   DROPKV_STATUS_NONFINITE = 2,
   DROPKV_STATUS_BAD_INDEX = 4,
   DROPKV_STATUS_PENDING = 8,
-  DROPKV_STATUS_NEGATIVE = 16 /* dropkv_select: a given raw score S[g][j] < 0 */
+  DROPKV_STATUS_NEGATIVE = 16, /* dropkv_select: a given raw score S[g][j] < 0 */
+  DROPKV_STATUS_BOUNDS = 32    /* checking build (libdropkv_debug.so) only: a device-side
+                                  bounds check failed; the call returns DROPKV_ERR_DEVICE */
 };
 
 /* Flags for dropkv_score_ex. */

@@ -13,7 +13,9 @@ import os
 from typing import Optional, Tuple
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "libdropkv.so")
+# DROPKV_LIBRARY may name one of the checking builds next to it
+# (libdropkv_debug.so, libdropkv_asan.so; see build.py) instead.
+LIB_PATH = os.environ.get("DROPKV_LIBRARY") or os.path.join(_HERE, "libdropkv.so")
 
 OK, ERR_INVALID, ERR_SINGULAR, ERR_NONFINITE, ERR_DEVICE, ERR_NEGATIVE = 0, -1, -2, -3, -4, -5
 BF16, F32 = 0, 1

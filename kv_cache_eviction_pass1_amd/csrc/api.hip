@@ -162,6 +162,7 @@ int status_to_code(int32_t st_word) {
     return fail(DROPKV_ERR_SINGULAR, "a window row has a probability that rounds to 1 (singular)");
   if (st_word & kStatusNonFinite) return fail(DROPKV_ERR_NONFINITE, "non-finite inputs or scores");
   if (st_word & kStatusNegative) return fail(DROPKV_ERR_NEGATIVE, "negative raw score given to select");
+  if (st_word & kStatusBounds) return fail(DROPKV_ERR_DEVICE, "a device-side bounds check failed (checking build)");
   return DROPKV_OK;
 }
 

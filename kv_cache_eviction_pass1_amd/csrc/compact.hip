@@ -168,6 +168,7 @@ __global__ __launch_bounds__(kT) void k_compact(CompactArgs A) {
           const int64_t so = (int64_t)rows[r] * A.row_bytes + (int64_t)c * (int64_t)sizeof(U);
           bk[u] = *(const U*)(src + so);
           const int64_t orow = base + r;
+          DKV_CHECK(rows[r] < (uint16_t)kCT && t0 + rows[r] < A.n, A.status);
           if (orow >= 0 && orow < A.n_keep) dst[u] = orow * A.row_bytes + (int64_t)c * (int64_t)sizeof(U);
         }
         r += dr;

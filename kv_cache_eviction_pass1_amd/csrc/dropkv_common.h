@@ -12,6 +12,21 @@ constexpr int kStatusSingular = 1;
 constexpr int kStatusNonFinite = 2;
 constexpr int kStatusBadIndex = 4;  // cache compaction: eviction list not increasing inside [0, n)
 constexpr int kStatusNegative = 16;  // select on given scores: some S[g][j] < 0
+constexpr int kStatusBounds = 32;    // checking build only: an index failed its bounds check
+
+// Bounds checks of the checking build (-DDROPKV_DEBUG): a failed check ORs
+// kStatusBounds into the call's status word (the access itself is left as it
+// is; the release build compiles the checks away).
+#ifdef DROPKV_DEBUG
+#define DKV_CHECK(cond, status)                                 \
+  do {                                                          \
+    if (!(cond)) atomicOr((status), ::dropkv::kStatusBounds);   \
+  } while (0)
+#else
+#define DKV_CHECK(cond, status) \
+  do {                          \
+  } while (0)
+#endif
 
 // A window row is rejected when its rest mass R = sum_{j != argmax} exp(x_j - x_max)
 // is at most 2^-24: then 1/(1+R) rounds to 1 in binary32 (the singular-input rule).

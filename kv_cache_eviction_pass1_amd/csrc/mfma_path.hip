@@ -229,7 +229,8 @@ __device__ __forceinline__ VnOff<NW> vn_offsets(int wave, int lane) {
 
 template <int NW>
 __device__ __forceinline__ void p1_vnorms(const char* vb, const VnOff<NW>& vo, float* nvtile, int64_t ntok,
-                                          int wave, int lane) {
+                                          int wave, int lane, int32_t* status) {
+  (void)status;
   typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
   float a0 = 0.f, a1 = 0.f;
 #pragma unroll
@@ -251,6 +252,7 @@ __device__ __forceinline__ void p1_vnorms(const char* vb, const VnOff<NW>& vo, f
   if (NW >= 8) acc += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(acc), 0x141, 0xf, 0xf, false));
   const int tt = wave * (TT / NW) + lane / NW;
   if (lane % NW == 0 && tt < ntok) nvtile[tt] = acc;
+  DKV_CHECK(tt < TT, status);
 }
 
 // Online-softmax state of one window row (one lane pair).
@@ -441,7 +443,7 @@ __global__ __launch_bounds__(NW * 64) void k_pass1(P1Args A) {
     const int64_t tb = t0 + (int64_t)t * TT;
     if (t + 1 < ntiles) wait_vmcnt<kDmaPerTile>(); else wait_vmcnt<0>();
     lds_barrier();  // tile t in LDS for every wave; tile t-1's buffer is free
-    if (rg == 0) p1_vnorms<NW>(vc, vno, nvh + tb, t1 - tb, wave, lane);
+    if (rg == 0) p1_vnorms<NW>(vc, vno, nvh + tb, t1 - tb, wave, lane, A.status);
     if (t + 2 < ntiles) {
       issue_any<NW>(kh, tb + 2 * TT, A.n, kn, wave, lane, doff);
       issue_any<NW>(vh, tb + 2 * TT, A.n, vn, wave, lane, doff);
@@ -467,6 +469,7 @@ __global__ __launch_bounds__(NW * 64) void k_pass1(P1Args A) {
   if (!active) return;
   const float l_tot = pair_sum(st.l);
   if (!row_ok) return;
+  DKV_CHECK(chunk < (int)gridDim.x && g < A.Hkv && row < A.Rg && t1 <= A.n, A.status);
   float* pr = A.part + ((size_t)chunk * A.Hkv * A.Rg + (size_t)g * A.Rg + row) * PSTRIDE;
   // lane holds O^T rows d = 32db + 8i + 4h + (0..3) of this row's column
 #pragma unroll
@@ -576,6 +579,7 @@ __global__ __launch_bounds__(256) void k_merge(MergeArgs M) {
     // lowest-index argmax inside the 32-token block where the running max was set
     const int64_t pos = M.n - M.w + (r % M.w);
     const int64_t tok = (int64_t)bt * 32 + (lane & 31);
+    DKV_CHECK(bt >= 0 && (int64_t)bt * 32 < M.n, M.status);
     float x = -INFINITY;
     if (lane < 32 && tok <= pos && tok >= 0) {
       const uint16_t* qr = M.q + (size_t)row * HD;
@@ -733,6 +737,7 @@ struct P2Args {
   const float* nv;
   const int32_t* flagcount;
   float* S;  // [rg][Hkv][n]
+  int32_t* status;
 };
 
 __device__ __forceinline__ void p2_tile(const P2Args& P, const char* kb, const char* vb,
@@ -830,6 +835,7 @@ __device__ __forceinline__ void p2_combine(const P2Args& P, float (*red)[TT][2],
         nvj = P.nv[(size_t)g * P.n + tok];
       }
       const float s = fmaxf(fmaf(nvj, T2, -2.0f * T1), 0.0f) * P.invG;
+      DKV_CHECK(tok < P.n, P.status);
       P.S[((size_t)blockIdx.y * P.Hkv + g) * P.n + tok] = s;
     }
   }
@@ -1106,6 +1112,7 @@ __global__ __launch_bounds__(NW * 64) void k_pass2(P2Args P, FixArgs F) {
           for (int wv = 0; wv < nwa; ++wv) s2 += red3b[b][wv][threadIdx.x];
           sacc = fmaf(nvbuf[b][threadIdx.x], s2, -2.0f * sacc);
         }
+        DKV_CHECK(tok < P.n, P.status);
         Sout[tok] = fmaxf(sacc, 0.0f) * P.invG;
       }
     }
@@ -1302,7 +1309,7 @@ hipError_t launch_mfma_path(const void* q, const void* k, const void* v, const S
     record_stage(se, "fixup", st);
   }
   P2Args a2{(const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v, s.n, s.w, p.Rg, p.nw2,
-            p.tpc2, s.Hkv, c2, 1.0f / (float)s.G(), ws.rs, nv, flagcount, Spart};
+            p.tpc2, s.Hkv, c2, 1.0f / (float)s.G(), ws.rs, nv, flagcount, Spart, ws.status};
   const dim3 grid2(p.nch2 + (p.nw2 >= 2 ? FXC : 0), p.nrg2, s.Hkv);
   switch (p.nw2) {
     case 8: k_pass2<8, false><<<grid2, 512, 0, st>>>(a2, af); break;
@@ -1377,7 +1384,7 @@ hipError_t launch_mfma_from_stats(const void* q, const void* k, const void* v, c
              ws.rs, flagcount, fx};
   if (p.nw2 < 2) k_fixup<<<dim3(FXC, s.Hkv), 256, 0, st>>>(af);
   P2Args a2{(const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v, s.n, s.w, p.Rg, p.nw2,
-            p.tpc2, s.Hkv, c2, 1.0f / (float)s.G(), ws.rs, nullptr, flagcount, Spart};
+            p.tpc2, s.Hkv, c2, 1.0f / (float)s.G(), ws.rs, nullptr, flagcount, Spart, ws.status};
   const dim3 grid2(p.nch2 + (p.nw2 >= 2 ? FXC : 0), p.nrg2, s.Hkv);
   switch (p.nw2) {
     case 8: k_pass2<8, true><<<grid2, 512, 0, st>>>(a2, af); break;
@@ -1426,6 +1433,7 @@ struct PrefillArgs {
   float* L;            // 1 + R relative to the largest logit
   int32_t* best;       // 32-token block where the largest logit first occurs
   float* a;            // [Hq * w][d] output in fp32
+  int32_t* status;
 };
 
 template <int NW>
@@ -1510,6 +1518,7 @@ __global__ __launch_bounds__(NW * 64) void k_prefill(PrefillArgs A) {
   if (!row_ok) return;
   const float inv_l = 1.0f / l_tot;
   // lane holds O^T rows d = 32 db + 8 i + 4 h + (0..3) of its row's column
+  DKV_CHECK(pos < A.n && qh < A.Hkv * A.G, A.status);
   uint16_t* orow = A.o + ((size_t)qh * A.n + pos) * HD;
 #pragma unroll
   for (int db = 0; db < 4; ++db)
@@ -1524,6 +1533,7 @@ __global__ __launch_bounds__(NW * 64) void k_prefill(PrefillArgs A) {
     }
   if (pos >= A.n - A.w) {
     const int64_t wr = (int64_t)qh * A.w + (pos - (A.n - A.w));
+    DKV_CHECK(wr >= 0 && wr < (int64_t)A.Hkv * A.G * A.w, A.status);
     float* ar = A.a + wr * HD;
 #pragma unroll
     for (int db = 0; db < 4; ++db)
@@ -1611,7 +1621,7 @@ hipError_t launch_prefill(const void* q_all, const void* k, const void* v, int64
   int nw = MAXW;
   while (nw > 1 && (nw / 2) * 32 >= Rg) nw /= 2;
   PrefillArgs pa{(const uint16_t*)q_all, (const uint16_t*)k, (const uint16_t*)v, n, w, G, PB, Rg, nblk, Hkv,
-                 kLog2e / sqrtf((float)HD), 1.0f / sqrtf((float)HD), (uint16_t*)o, m, ws_L, ws_best, a};
+                 kLog2e / sqrtf((float)HD), 1.0f / sqrtf((float)HD), (uint16_t*)o, m, ws_L, ws_best, a, status};
   k_zero_word<<<1, 64, 0, st>>>(status);  // the status word starts clear (a kernel, so the call can be captured)
   const dim3 grid(nblk, Hkv);
   switch (nw) {

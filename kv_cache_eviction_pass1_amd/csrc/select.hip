@@ -361,7 +361,10 @@ __global__ __launch_bounds__(kT) void k_sel_cand(SelArgs A) {
     auto emit_keys = [&](const uint32_t (&key)[kKeys], int64_t c0) {
 #pragma unroll
       for (int e = 0; e < kKeys; ++e)
-        if (key[e] != 0xffffffffu && (key[e] >> 20) == d1) cg[pos++] = make_uint2(key[e], (uint32_t)(c0 + e));
+        if (key[e] != 0xffffffffu && (key[e] >> 20) == d1) {
+          DKV_CHECK(pos < (uint32_t)A.n, A.status);
+          cg[pos++] = make_uint2(key[e], (uint32_t)(c0 + e));
+        }
     };
     emit_keys(key0, j0);
     for (int64_t c0 = j0 + kKeys; c0 < j1; c0 += kKeys) {
@@ -518,6 +521,7 @@ __global__ __launch_bounds__(kT) void k_sel_write(SelArgs A) {
           const uint32_t r = pos - base32;  // wraps above cnt32 if ever below base
           stg[(take && r < cnt32) ? r : (uint32_t)(kStage + threadIdx.x)] = q0 + k;
         } else {
+          DKV_CHECK(!take || pos < (uint32_t)A.n_evict, A.status);
           if (take && pos < (uint32_t)A.n_evict) og[pos] = (int64_t)(q0 + k);
         }
         pos += take ? 1u : 0u;
@@ -548,6 +552,7 @@ __global__ __launch_bounds__(kT) void k_sel_write(SelArgs A) {
 #pragma unroll
     for (int k = 0; k < kOutPer; ++k) {
       const uint32_t i = i0 + k * kT + threadIdx.x;
+      DKV_CHECK(i >= cnt32 || (int64_t)i < lim, A.status);
       if (i < cnt32 && (int64_t)i < lim) og[base + i] = (int64_t)v[k];
     }
   }
