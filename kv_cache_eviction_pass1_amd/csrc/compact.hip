@@ -8,29 +8,31 @@
 // j - #{evicted indices < j} of the head's output.
 //
 // One workgroup per (block of kCT tokens, KV head), reading the list only
-// where it needs it:
-//   - two waves find the list range [lo, hi) of the block's tokens with
-//     64-way searches (three or four rounds of 64 probes for 10^5 entries);
-//   - the block's evicted tokens become a bitmap in LDS, the kept tokens are
-//     ranked by a workgroup scan, and the block's rows land at output row
-//     (block start - lo) + rank;
-//   - the copy runs over (row, 16-byte unit) pairs, consecutive threads on
-//     consecutive units, so reads of a row and writes of the output are
-//     coalesced; K's rows first, then V's.
+// where it needs it, in two dependent rounds:
+//   - its kT threads read kT evenly spaced list entries; counting those below
+//     the block's first token t0 and below its end t1 brackets the two list
+//     positions lo = #{e < t0} and hi = #{e < t1} within one sample spacing
+//     each (sample i sits at position i * n_evict / kT);
+//   - the threads read the bracketed list range [A, B) once: the entries below
+//     t0 complete lo, those inside the block become a bitmap in LDS;
+//   - the kept tokens are ranked by a workgroup scan and land at output row
+//     (t0 - lo) + rank; the copy runs over (row, 16-byte unit) pairs,
+//     consecutive threads on consecutive units, K's and V's unit loaded
+//     together so that both streams are in flight.
 // Every workgroup also checks an equal share of the list (strictly increasing,
-// inside [0, n)); a bad list sets the status bit, and no write can leave the
-// output arrays whatever the list holds.
+// inside [0, n)); a bad list sets the status bit, and no read or write leaves
+// the list or the output arrays whatever the list holds.
 #include "dropkv_common.h"
 
 namespace dropkv {
 
 namespace {
 
-constexpr int kT = 256;    // threads per workgroup
+constexpr int kT = 512;    // threads per workgroup
 constexpr int kCT = 1024;  // tokens per workgroup
 constexpr int kPerT = kCT / kT;
-constexpr int kBatch = 16;  // copy units in flight per thread
-static_assert(kCT % kT == 0 && kCT % 32 == 0 && kPerT <= 32, "token blocking");
+constexpr int kBatch = 8;  // copy units in flight per thread and tensor
+static_assert(kCT % kT == 0 && kCT % 32 == 0 && kPerT <= 32 && 32 % kPerT == 0, "token blocking");
 
 struct CompactArgs {
   const char* k;
@@ -45,29 +47,6 @@ struct CompactArgs {
   int32_t* status;
 };
 
-// Lowest i in [0, len) with e[i] >= x (len if none) for a strictly increasing
-// list: each round the 64 lanes of the calling wave probe 64 evenly spaced
-// entries and keep the one gap where the comparison flips. For any list it
-// returns some index in [0, len] after at most ~log_64(len) + 2 rounds.
-__device__ int64_t lower_bound_wave(const int64_t* e, int64_t len, int64_t x) {
-  const int lane = threadIdx.x & 63;
-  int64_t lo = 0, hi = len;  // the answer lies in [lo, hi]
-  while (lo < hi) {
-    const int64_t step = (hi - lo + 63) / 64;
-    const int64_t p = lo + (int64_t)lane * step;
-    const bool less = p < hi && e[p] < x;
-    const int c = __popcll(__builtin_amdgcn_ballot_w64(less));
-    if (c == 0) {
-      hi = lo;  // e[lo] >= x
-    } else {
-      const int64_t nhi = lo + (int64_t)c * step;
-      lo = lo + (int64_t)(c - 1) * step + 1;
-      hi = nhi < hi ? nhi : hi;
-    }
-  }
-  return lo;
-}
-
 __device__ __forceinline__ uint32_t wave_incl_scan(uint32_t x) {
   x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x111, 0xf, 0xf, false);  // row_shr:1
   x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x112, 0xf, 0xf, false);  // row_shr:2
@@ -78,33 +57,33 @@ __device__ __forceinline__ uint32_t wave_incl_scan(uint32_t x) {
   return x;
 }
 
+// list position of sample i (i <= kT; sample kT stands for the end of the list)
+__device__ __forceinline__ int64_t sample_pos(int64_t ne, int i) { return (int64_t)i * ne / kT; }
+
 template <typename U>
 __global__ __launch_bounds__(kT) void k_compact(CompactArgs A) {
   const int b = blockIdx.x, g = blockIdx.y;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int64_t t0 = (int64_t)b * kCT;
   const int64_t t1 = (t0 + kCT < A.n) ? t0 + kCT : A.n;
-  const int64_t* e = A.e + (size_t)g * A.n_evict;
+  const int64_t ne = A.n_evict;
+  const int64_t* e = A.e + (size_t)g * ne;
   __shared__ uint32_t bits[kCT / 32];
   __shared__ uint16_t rows[kCT];
-  __shared__ int64_t sh_lo, sh_hi;
   __shared__ uint32_t wsum[kT / 64];
+  __shared__ uint32_t cnt[3];  // samples below t0, samples below t1, bracketed entries below t0
   __shared__ int bad;
   if (threadIdx.x < kCT / 32) bits[threadIdx.x] = 0u;
+  if (threadIdx.x < 3) cnt[threadIdx.x] = 0u;
   if (threadIdx.x == 0) bad = 0;
-  // the two ends of the block's list range, searched by two waves at once
-  if (wave == 0) {
-    const int64_t lo = lower_bound_wave(e, A.n_evict, t0);
-    if (lane == 0) sh_lo = lo;
-  } else if (wave == 1) {
-    const int64_t hi = lower_bound_wave(e, A.n_evict, t1);
-    if (lane == 0) sh_hi = hi;
-  }
+  // round 1: one list sample per thread, and this workgroup's share of the
+  // list check (all shares cover every adjacent pair once)
+  int64_t sv = INT64_MAX;
+  if (ne > 0) sv = e[sample_pos(ne, threadIdx.x)];
   {
-    // this workgroup's share of the list check (all shares cover every pair once)
-    const int64_t per = (A.n_evict + A.nblk - 1) / A.nblk;
+    const int64_t per = (ne + A.nblk - 1) / A.nblk;
     const int64_t i0 = (int64_t)b * per;
-    const int64_t i1 = (i0 + per < A.n_evict) ? i0 + per : A.n_evict;
+    const int64_t i1 = (i0 + per < ne) ? i0 + per : ne;
     bool badl = false;
     for (int64_t i = i0 + threadIdx.x; i < i1; i += kT) {
       const int64_t x = e[i];
@@ -113,10 +92,34 @@ __global__ __launch_bounds__(kT) void k_compact(CompactArgs A) {
     if (badl) bad = 1;
   }
   __syncthreads();
-  const int64_t lo = sh_lo, hi = sh_hi > sh_lo ? sh_hi : sh_lo;
-  for (int64_t i = lo + threadIdx.x; i < hi; i += kT) {
-    const int64_t x = e[i] - t0;
-    if (x >= 0 && x < t1 - t0) atomicOr(&bits[x >> 5], 1u << (x & 31));
+  {
+    const uint32_t c0 = __popcll(__builtin_amdgcn_ballot_w64(sv < t0));
+    const uint32_t c1 = __popcll(__builtin_amdgcn_ballot_w64(sv < t1));
+    if (lane == 0) {
+      if (c0) atomicAdd(&cnt[0], c0);
+      if (c1) atomicAdd(&cnt[1], c1);
+    }
+  }
+  __syncthreads();
+  // lo lies in [A0, pos(c0)], hi in [pos(c1 - 1) + 1, pos(c1)]: read [A0, B0)
+  const int c0 = (int)cnt[0], c1 = (int)cnt[1];
+  const int64_t A0 = c0 > 0 ? sample_pos(ne, c0 - 1) + 1 : 0;
+  const int64_t B0 = sample_pos(ne, c1);
+  uint32_t below = 0;
+  for (int64_t i = A0 + threadIdx.x; i < B0; i += kT) {
+    const int64_t x = e[i];
+    if (x < t0) {
+      ++below;
+    } else if (x < t1) {
+      const int64_t r = x - t0;
+      atomicOr(&bits[r >> 5], 1u << (r & 31));
+    }
+  }
+  {
+    // wave sum of `below` (a few entries per thread at most)
+    uint32_t wv = wave_incl_scan(below);
+    wv = (uint32_t)__builtin_amdgcn_readlane((int)wv, 63);
+    if (lane == 0 && wv) atomicAdd(&cnt[2], wv);
   }
   __syncthreads();
   // kept tokens of this block, ranked: thread t owns tokens kPerT*t .. +kPerT-1
@@ -126,11 +129,11 @@ __global__ __launch_bounds__(kT) void k_compact(CompactArgs A) {
 #pragma unroll
   for (int j = 0; j < kPerT; ++j)
     if (t0 + tok0 + j < t1 && !((word >> j) & 1u)) keep |= 1u << j;
-  const uint32_t cnt = __popc(keep);
-  const uint32_t incl = wave_incl_scan(cnt);
+  const uint32_t nk = __popc(keep);
+  const uint32_t incl = wave_incl_scan(nk);
   if (lane == 63) wsum[wave] = incl;
   __syncthreads();
-  uint32_t before = incl - cnt, total = 0;
+  uint32_t before = incl - nk, total = 0;
 #pragma unroll
   for (int w = 0; w < kT / 64; ++w) {
     const uint32_t s = wsum[w];
@@ -141,7 +144,8 @@ __global__ __launch_bounds__(kT) void k_compact(CompactArgs A) {
   for (int j = 0; j < kPerT; ++j)
     if ((keep >> j) & 1u) rows[before++] = (uint16_t)(tok0 + j);
   __syncthreads();
-  // kept tokens before this block: t0 - lo (exact for a valid list)
+  // kept tokens before this block: t0 - lo, lo = A0 + bracketed entries below t0
+  const int64_t lo = A0 + (int64_t)cnt[2];
   const int64_t base = t0 - lo;
   // (row, unit) pairs of this block: at most kCT * 4096 * 4 / 2 < 2^31
   const uint32_t upr = (uint32_t)A.upr;
@@ -151,37 +155,36 @@ __global__ __launch_bounds__(kT) void k_compact(CompactArgs A) {
   char* kd = A.ok + (size_t)g * A.n_keep * A.row_bytes;
   char* vd = A.ov + (size_t)g * A.n_keep * A.row_bytes;
   // unit i = r * upr + c; each thread walks i = threadIdx.x + m * kT, stepping
-  // (r, c) by (kT / upr, kT % upr) with a carry instead of dividing. K first,
-  // then V: two memory streams at a time instead of four.
+  // (r, c) by (kT / upr, kT % upr) with a carry instead of dividing
   const uint32_t dr = (uint32_t)kT / upr, dc = (uint32_t)kT % upr;
-  for (int tsr = 0; tsr < 2; ++tsr) {
-    const char* src = tsr ? vs : ks;
-    char* dstb = tsr ? vd : kd;
-    uint32_t r = threadIdx.x / upr, c = threadIdx.x % upr;
-    for (uint32_t i0 = threadIdx.x; i0 < units; i0 += (uint32_t)kT * kBatch) {
-      U bk[kBatch];
-      int64_t dst[kBatch];
+  uint32_t r = threadIdx.x / upr, c = threadIdx.x % upr;
+  for (uint32_t i0 = threadIdx.x; i0 < units; i0 += (uint32_t)kT * kBatch) {
+    U bk[kBatch], bv[kBatch];
+    int64_t dst[kBatch];
 #pragma unroll
-      for (int u = 0; u < kBatch; ++u) {
-        dst[u] = -1;
-        if (i0 + (uint32_t)u * kT < units) {
-          const int64_t so = (int64_t)rows[r] * A.row_bytes + (int64_t)c * (int64_t)sizeof(U);
-          bk[u] = *(const U*)(src + so);
-          const int64_t orow = base + r;
-          DKV_CHECK(rows[r] < (uint16_t)kCT && t0 + rows[r] < A.n, A.status);
-          if (orow >= 0 && orow < A.n_keep) dst[u] = orow * A.row_bytes + (int64_t)c * (int64_t)sizeof(U);
-        }
-        r += dr;
-        c += dc;
-        if (c >= upr) {
-          c -= upr;
-          ++r;
-        }
+    for (int u = 0; u < kBatch; ++u) {
+      dst[u] = -1;
+      if (i0 + (uint32_t)u * kT < units) {
+        const int64_t so = (int64_t)rows[r] * A.row_bytes + (int64_t)c * (int64_t)sizeof(U);
+        bk[u] = *(const U*)(ks + so);
+        bv[u] = *(const U*)(vs + so);
+        const int64_t orow = base + r;
+        DKV_CHECK(rows[r] < (uint16_t)kCT && t0 + rows[r] < A.n, A.status);
+        if (orow >= 0 && orow < A.n_keep) dst[u] = orow * A.row_bytes + (int64_t)c * (int64_t)sizeof(U);
       }
-#pragma unroll
-      for (int u = 0; u < kBatch; ++u)
-        if (dst[u] >= 0) *(U*)(dstb + dst[u]) = bk[u];
+      r += dr;
+      c += dc;
+      if (c >= upr) {
+        c -= upr;
+        ++r;
+      }
     }
+#pragma unroll
+    for (int u = 0; u < kBatch; ++u)
+      if (dst[u] >= 0) {
+        *(U*)(kd + dst[u]) = bk[u];
+        *(U*)(vd + dst[u]) = bv[u];
+      }
   }
   if (threadIdx.x == 0 && bad) atomicOr(A.status, kStatusBadIndex);
 }
