@@ -83,8 +83,9 @@ StageEvents* log_slot() {
   const int i = L.used;
   if (!L.created[i]) {
     // timing-only events: no system-scope fence (and its cache writeback) per record
-    for (int e = 0; e <= kMaxStages; ++e)
-      if (hipEventCreateWithFlags(&L.slot[i].ev[e], hipEventDisableSystemFence) != hipSuccess) return nullptr;
+    for (int e = 0; e < kMaxStages; ++e)
+      for (int b = 0; b < 2; ++b)
+        if (hipEventCreateWithFlags(&L.slot[i].ev[e][b], hipEventDisableSystemFence) != hipSuccess) return nullptr;
     L.created[i] = true;
   }
   L.slot[i].count = 0;
@@ -144,13 +145,13 @@ int run_scores(int dtype, const void* q, const void* k, const void* v, const Sha
   } else {
     e = launch_init(ws.status, ws.flagcount, ws.sel, s.Hkv, st);
     if (e != hipSuccess) return fail_hip(e, "init");
-    record_stage(se, "start", st);
+    (void)record_stage(se, "start", st);
     e = launch_generic_rows(dtype, q, k, v, s, ws, st);
     if (e != hipSuccess) return fail_hip(e, "generic row stats");
-    record_stage(se, "rows", st);
+    (void)record_stage(se, "rows", st);
     e = launch_generic_scores(dtype, q, k, v, s, ws, st);
     if (e != hipSuccess) return fail_hip(e, "generic scores");
-    record_stage(se, "scores", st);
+    (void)record_stage(se, "scores", st);
   }
   return DROPKV_OK;
 }
@@ -287,17 +288,13 @@ int score_sync(int dtype, const void* q, const void* k, const void* v, int64_t n
 // ----------------------------------------------------------------- stage events
 
 hipError_t record_stage(StageEvents* se, const char* name, hipStream_t st) {
-  if (!se || se->count > kMaxStages) return hipSuccess;
-  // ev[0] is the start marker; ev[i] (i >= 1) closes stage i-1
-  if (se->count == 0 && name && std::strcmp(name, "start") == 0) {
-    hipError_t e = hipEventRecord(se->ev[0], st);
-    se->count = 0;
-    return e;
-  }
-  if (se->count >= kMaxStages) return hipSuccess;
+  if (!se || se->count >= kMaxStages) return hipSuccess;
+  if (name && std::strcmp(name, "start") == 0) return hipEventRecord(se->ev[se->count][0], st);
+  // this marker closes the current stage and opens the next one
   se->names[se->count] = name;
-  hipError_t e = hipEventRecord(se->ev[se->count + 1], st);
+  hipError_t e = hipEventRecord(se->ev[se->count][1], st);
   se->count += 1;
+  if (e == hipSuccess && se->count < kMaxStages) e = hipEventRecord(se->ev[se->count][0], st);
   return e;
 }
 
@@ -389,10 +386,8 @@ int dropkv_score_ex(int32_t dtype, const void* q, const void* k, const void* v, 
   FoldInfo fold{};
   if (int rc = run_scores(dtype, q, k, v, s, ws, mfma, st, se, &fold)) return rc;
   hipError_t e = launch_select(ws.S, n, window, Hkv, pool_kernel, n_evict, out_scores, out_evict_idx,
-                               ws.status, &fold, ws.sel, st);
+                               ws.status, &fold, ws.sel, st, false, se);
   if (e != hipSuccess) return fail_hip(e, "select");
-  e = record_stage(se, "select", st);
-  if (e != hipSuccess) return fail_hip(e, "stage event");
   return DROPKV_OK;
 }
 
@@ -544,24 +539,24 @@ int dropkv_stage_times(int32_t dtype, const void* q, const void* k, const void* 
   if (int rc = get_workspace(carve_workspace(nullptr, s, mfma).bytes, &base)) return rc;
   Workspace ws = carve_workspace(base, s, mfma);
   StageEvents se{};
-  for (int i = 0; i <= kMaxStages; ++i) {
-    hipError_t e = hipEventCreateWithFlags(&se.ev[i], hipEventDisableSystemFence);
-    if (e != hipSuccess) return fail_hip(e, "hipEventCreateWithFlags");
-  }
+  for (int i = 0; i < kMaxStages; ++i)
+    for (int b = 0; b < 2; ++b) {
+      hipError_t e = hipEventCreateWithFlags(&se.ev[i][b], hipEventDisableSystemFence);
+      if (e != hipSuccess) return fail_hip(e, "hipEventCreateWithFlags");
+    }
   FoldInfo fold{};
   int rc = run_scores(dtype, q, k, v, s, ws, mfma, st, &se, &fold);
   if (rc == DROPKV_OK) {
     hipError_t e = launch_select(ws.S, n, window, Hkv, pool_kernel, n_evict, out_scores, out_evict_idx, ws.status,
-                                 &fold, ws.sel, st);
+                                 &fold, ws.sel, st, false, &se);
     if (e != hipSuccess) rc = fail_hip(e, "select");
-    else record_stage(&se, "select", st);
   }
   if (rc == DROPKV_OK) rc = sync_status(ws, st);
   if (rc == DROPKV_OK || rc == DROPKV_ERR_SINGULAR || rc == DROPKV_ERR_NONFINITE) {
     std::string names;
     for (int i = 0; i < se.count; ++i) {
       float ms = 0.f;
-      (void)hipEventElapsedTime(&ms, se.ev[i], se.ev[i + 1]);
+      (void)hipEventElapsedTime(&ms, se.ev[i][0], se.ev[i][1]);
       out_ms[i] = ms;
       names += se.names[i];
       names += (i + 1 < se.count) ? "," : "";
@@ -572,7 +567,8 @@ int dropkv_stage_times(int32_t dtype, const void* q, const void* k, const void* 
       out_names[names_bytes - 1] = 0;
     }
   }
-  for (int i = 0; i <= kMaxStages; ++i) (void)hipEventDestroy(se.ev[i]);
+  for (int i = 0; i < kMaxStages; ++i)
+    for (int b = 0; b < 2; ++b) (void)hipEventDestroy(se.ev[i][b]);
   return rc;
 }
 
@@ -597,7 +593,8 @@ int dropkv_stage_log(float* out_ms, char* out_names, int32_t names_bytes, int32_
     for (int i = 0; i < sc.count; ++i)
       if (std::strcmp(sc.names[i], s0.names[i]) != 0)
         return fail(DROPKV_ERR_INVALID, "logged calls ran different stages");
-    e = hipEventSynchronize(sc.ev[sc.count]);
+    if (sc.count == 0) continue;
+    e = hipEventSynchronize(sc.ev[sc.count - 1][1]);
     if (e != hipSuccess) return fail_hip(e, "hipEventSynchronize");
   }
   std::string names;
@@ -605,7 +602,7 @@ int dropkv_stage_log(float* out_ms, char* out_names, int32_t names_bytes, int32_
     double acc = 0.0;
     for (int c = 0; c < calls; ++c) {
       float ms = 0.f;
-      e = hipEventElapsedTime(&ms, L.slot[c].ev[i], L.slot[c].ev[i + 1]);
+      e = hipEventElapsedTime(&ms, L.slot[c].ev[i][0], L.slot[c].ev[i][1]);
       if (e != hipSuccess) return fail_hip(e, "hipEventElapsedTime");
       acc += ms;
     }

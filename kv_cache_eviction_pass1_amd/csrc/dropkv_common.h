@@ -2,6 +2,7 @@
 #pragma once
 
 #include <hip/hip_runtime.h>
+#include <hip/hip_ext.h>
 #include <stdint.h>
 #include <stddef.h>
 
@@ -101,21 +102,43 @@ struct FoldInfo {
 // raises kStatusNegative; scores the library computed are >= 0 by
 // construction, up to fp64 rounding residue in decode-time rescoring, which
 // orders as +0.
+struct StageEvents;
 hipError_t launch_select(const float* S, int64_t n, int32_t w, int32_t Hkv, int32_t pool_kernel,
                          int64_t n_evict, float* out_scores, int64_t* out_idx, int32_t* status,
-                         const FoldInfo* fold, void* scratch, hipStream_t st, bool reject_negative = false);
+                         const FoldInfo* fold, void* scratch, hipStream_t st, bool reject_negative = false,
+                         StageEvents* se = nullptr);
 size_t select_scratch_bytes(int64_t n, int32_t Hkv);
 // 32-bit words at the start of the select scratch that must be zero before a call.
 size_t select_zero_words(int32_t Hkv);
-// Stage timing: when `ev` is non-null, an event is recorded on the stream after
-// every kernel of the path; `names` receives the stage names (at most kMaxStages).
+// Stage timing. Stage i runs from ev[i][0] to ev[i][1]. Kernels launched
+// through stage_launch take these from their own dispatch (the begin time of
+// a stage's first kernel, the end time of its last), so timing adds no packet
+// between kernels; record_stage instead records marker events on the stream
+// (a stage then runs from the previous marker to its own).
 constexpr int kMaxStages = 12;
 struct StageEvents {
-  hipEvent_t ev[kMaxStages + 1];
+  hipEvent_t ev[kMaxStages][2];
   const char* names[kMaxStages];
   int count;
 };
 hipError_t record_stage(StageEvents* se, const char* name, hipStream_t st);
+// Roles of a kernel in its stage (bit 0: first kernel, bit 1: last kernel).
+enum { kStageMid = 0, kStageFirst = 1, kStageLast = 2, kStageOnly = 3 };
+// Launches `kern` on `st`; with se non-null the kernel's begin (kStageFirst) and
+// end (kStageLast) times become stage `name`'s events.
+template <typename F, typename... Args>
+hipError_t stage_launch(StageEvents* se, const char* name, int role, F kern, dim3 grid, dim3 block,
+                        hipStream_t st, Args... args) {
+  if (!se || se->count >= kMaxStages) {
+    hipLaunchKernelGGL(kern, grid, block, 0, st, args...);
+    return hipGetLastError();
+  }
+  hipEvent_t e0 = (role & kStageFirst) ? se->ev[se->count][0] : nullptr;
+  hipEvent_t e1 = (role & kStageLast) ? se->ev[se->count][1] : nullptr;
+  hipExtLaunchKernelGGL(kern, grid, block, 0, st, e0, e1, 0u, args...);
+  if (role & kStageLast) se->names[se->count++] = name;
+  return hipGetLastError();
+}
 // MFMA path up to raw scores. Pass 1 also clears the status word, the flag
 // counts and select_zero_words(Hkv) words of ws.sel (no separate init launch).
 // fold_in_select: leave the flagged rows' argmax terms out of ws.S and return

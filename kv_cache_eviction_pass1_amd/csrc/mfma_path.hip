@@ -1286,50 +1286,51 @@ hipError_t launch_mfma_path(const void* q, const void* k, const void* v, const S
   P1Args a1{(const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v, s.n, s.n, s.w, p.Rg, p.nw,
             p.tpc1, s.Hkv, c2, ws.part, nv, ws.status, flagcount, (uint32_t*)ws.sel,
             (int64_t)select_zero_words(s.Hkv)};
-  record_stage(se, "start", st);
+  hipError_t e;
   {
     const dim3 grid1(p.nch1, p.nrg, s.Hkv);
     switch (p.nw) {
-      case 8: k_pass1<8><<<grid1, 512, 0, st>>>(a1); break;
-      case 4: k_pass1<4><<<grid1, 256, 0, st>>>(a1); break;
-      case 2: k_pass1<2><<<grid1, 128, 0, st>>>(a1); break;
-      default: k_pass1<1><<<grid1, 64, 0, st>>>(a1); break;
+      case 8: e = stage_launch(se, "pass1", kStageOnly, k_pass1<8>, grid1, dim3(512), st, a1); break;
+      case 4: e = stage_launch(se, "pass1", kStageOnly, k_pass1<4>, grid1, dim3(256), st, a1); break;
+      case 2: e = stage_launch(se, "pass1", kStageOnly, k_pass1<2>, grid1, dim3(128), st, a1); break;
+      default: e = stage_launch(se, "pass1", kStageOnly, k_pass1<1>, grid1, dim3(64), st, a1); break;
     }
+    if (e != hipSuccess) return e;
   }
-  record_stage(se, "pass1", st);
   MergeArgs am{(const uint16_t*)q, (const uint16_t*)k, ws.part, s.n, s.n, s.w, p.Rg, s.Hkv, p.nch1,
                c2, 1.0f / sqrtf((float)HD), ws.rs, flagcount, ws.status};
   const int64_t rows = (int64_t)s.Hkv * p.Rg;
-  k_merge<<<(unsigned)((rows + 3) / 4), 256, 0, st>>>(am);
-  record_stage(se, "merge", st);
+  e = stage_launch(se, "merge", kStageOnly, k_merge, dim3((unsigned)((rows + 3) / 4)), dim3(256), st, am);
+  if (e != hipSuccess) return e;
   FixArgs af{(const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v, s.n, s.n, s.w, p.Rg, s.Hkv, c2,
              ws.rs, flagcount, fx};
   if (p.nw2 < 2) {  // wider workgroups run the fix-up inside pass 2
-    k_fixup<<<dim3(FXC, s.Hkv), 256, 0, st>>>(af);
-    record_stage(se, "fixup", st);
+    e = stage_launch(se, "fixup", kStageOnly, k_fixup, dim3(FXC, s.Hkv), dim3(256), st, af);
+    if (e != hipSuccess) return e;
   }
   P2Args a2{(const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v, s.n, s.w, p.Rg, p.nw2,
             p.tpc2, s.Hkv, c2, 1.0f / (float)s.G(), ws.rs, nv, flagcount, Spart, ws.status};
   const dim3 grid2(p.nch2 + (p.nw2 >= 2 ? FXC : 0), p.nrg2, s.Hkv);
   switch (p.nw2) {
-    case 8: k_pass2<8, false><<<grid2, 512, 0, st>>>(a2, af); break;
-    case 4: k_pass2<4, false><<<grid2, 256, 0, st>>>(a2, af); break;
-    case 2: k_pass2<2, false><<<grid2, 128, 0, st>>>(a2, af); break;
-    default: k_pass2<1, false><<<grid2, 64, 0, st>>>(a2, af); break;
+    case 8: e = stage_launch(se, "pass2", kStageOnly, k_pass2<8, false>, grid2, dim3(512), st, a2, af); break;
+    case 4: e = stage_launch(se, "pass2", kStageOnly, k_pass2<4, false>, grid2, dim3(256), st, a2, af); break;
+    case 2: e = stage_launch(se, "pass2", kStageOnly, k_pass2<2, false>, grid2, dim3(128), st, a2, af); break;
+    default: e = stage_launch(se, "pass2", kStageOnly, k_pass2<1, false>, grid2, dim3(64), st, a2, af); break;
   }
-  record_stage(se, "pass2", st);
+  if (e != hipSuccess) return e;
   if (p.nrg2 > 1) {
     const int64_t total = (int64_t)s.Hkv * s.n;
-    k_sum_rowgroups<<<(unsigned)((total + 255) / 256), 256, 0, st>>>(Spart, ws.S, total, p.nrg2);
-    record_stage(se, "rowgroup_sum", st);
+    e = stage_launch(se, "rowgroup_sum", kStageOnly, k_sum_rowgroups, dim3((unsigned)((total + 255) / 256)),
+                     dim3(256), st, (const float*)Spart, ws.S, total, p.nrg2);
+    if (e != hipSuccess) return e;
   }
   FoldInfo fi{flagcount, ws.rs, fx, s.Hkv, p.Rg, FXC, FXSTRIDE, HD, 1.0f / (float)s.G()};
   if (fold_in_select) {
     *fold = fi;
-  } else {
-    hipError_t e = launch_fold(fi, s.n, s.Hkv, ws.S, ws.status, st);
+  } else if (fi.flagcount) {
+    FoldArgs ao{fi, s.n, ws.S, ws.status};
+    e = stage_launch(se, "fold", kStageOnly, k_fold, dim3(s.Hkv), dim3(HD), st, ao);
     if (e != hipSuccess) return e;
-    record_stage(se, "fold", st);
   }
   return hipGetLastError();
 }

@@ -625,7 +625,8 @@ hipError_t launch_init(int32_t* status, int32_t* flagcount, void* sel_scratch, i
 
 hipError_t launch_select(const float* S, int64_t n, int32_t w, int32_t Hkv, int32_t pool_kernel,
                          int64_t n_evict, float* out_scores, int64_t* out_idx, int32_t* status,
-                         const FoldInfo* fold, void* scratch, hipStream_t st, bool reject_negative) {
+                         const FoldInfo* fold, void* scratch, hipStream_t st, bool reject_negative,
+                         StageEvents* se) {
   const SelGeom q = sel_geom(n);
   if (fold && fold->flagcount && pool_kernel / 2 > kMaxHalo) {
     // the pool kernel reads S from global memory for such wide kernels: fold first
@@ -653,13 +654,13 @@ hipError_t launch_select(const float* S, int64_t n, int32_t w, int32_t Hkv, int3
   A.status = status;
   A.reject_negative = reject_negative;
   if (fold) A.fold = *fold;
-  k_sel_pool<<<dim3(A.nblk, Hkv), kT, 0, st>>>(A);
-  if (n_evict > 0) {
-    const dim3 gs((q.nseg + kT - 1) / kT, Hkv);
-    k_sel_cand<<<gs, kT, 0, st>>>(A);
-    k_sel_write<<<gs, kT, 0, st>>>(A);
-  }
-  return hipGetLastError();
+  hipError_t e = stage_launch(se, "select", n_evict > 0 ? kStageFirst : kStageOnly, k_sel_pool,
+                              dim3(A.nblk, Hkv), dim3(kT), st, A);
+  if (e != hipSuccess || n_evict <= 0) return e;
+  const dim3 gs((q.nseg + kT - 1) / kT, Hkv);
+  e = stage_launch(se, "select", kStageMid, k_sel_cand, gs, dim3(kT), st, A);
+  if (e != hipSuccess) return e;
+  return stage_launch(se, "select", kStageLast, k_sel_write, gs, dim3(kT), st, A);
 }
 
 }  // namespace dropkv
