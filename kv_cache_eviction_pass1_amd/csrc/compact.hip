@@ -76,7 +76,7 @@ __global__ __launch_bounds__(kT) void k_compact(CompactArgs A) {
   if (threadIdx.x < kCT / 32) bits[threadIdx.x] = 0u;
   if (threadIdx.x < 3) cnt[threadIdx.x] = 0u;
   if (threadIdx.x == 0) bad = 0;
-  // round 1: one list sample per thread, and this workgroup's share of the
+  // first load round: one list sample per thread, and this workgroup's share of the
   // list check (all shares cover every adjacent pair once)
   int64_t sv = INT64_MAX;
   if (ne > 0) sv = e[sample_pos(ne, threadIdx.x)];
