@@ -150,7 +150,10 @@ def test_bitwise_repeatable():
                                       (40000, 64, 7, 30000),
                                       # segments of 24 keys: several load groups per segment and
                                       # workgroups with more evictions than their staging area
-                                      (300000, 64, 9, 250000)])
+                                      (300000, 64, 9, 250000),
+                                      # either side of the largest head selected inside one
+                                      # workgroup (32768 keys), and every evictable token evicted
+                                      (32768, 64, 7, 31130), (32769, 64, 7, 31131), (20000, 16, 3, 19984)])
 def test_select_matches_stable_argsort(n, w, k, ne):
     rng = np.random.default_rng(n + ne)
     S = rng.integers(0, 7, size=(3, n)).astype(np.float32) * np.float32(0.25)  # many exact ties
@@ -162,6 +165,17 @@ def test_select_matches_stable_argsort(n, w, k, ne):
     scores, idx = scores.cpu().numpy(), idx.cpu().numpy()
     assert np.array_equal(scores.astype(np.float64), P_ref)
     assert np.array_equal(idx, ev_ref)
+
+
+@pytest.mark.parametrize("n", [4096, 32768, 32769])
+def test_select_all_keys_tied(n):
+    """Every pooled score equal: tau is that value and the lowest indices are evicted."""
+    S = np.full((2, n), 0.5, np.float32)
+    ne = n // 2 + 3
+    scores, idx = K.select(torch.from_numpy(S).cuda(), window=8, pool_kernel=5, n_evict=ne)
+    P_ref = oracle.protect_window(oracle.maxpool1d_same(S.astype(np.float64), 5), 8)
+    assert np.array_equal(scores.cpu().numpy().astype(np.float64), P_ref)
+    assert np.array_equal(idx.cpu().numpy(), np.tile(np.arange(ne, dtype=np.int64), (2, 1)))
 
 
 @pytest.mark.parametrize("where", [0, 4095, 9000])
