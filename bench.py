@@ -261,7 +261,7 @@ def main():
     per_step = step_times(torch, step, args.steps)
 
     # per-kernel mean durations: K more steps with the library's stage log (a
-    # HIP event after every kernel on its stream)
+    # stage's begin and end from its kernels' own dispatch timestamps)
     K.stage_log()  # empty the log
     for _ in range(args.steps):
         step(K.FLAG_STAGE_LOG)

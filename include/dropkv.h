@@ -84,8 +84,10 @@ enum {
 /* Flags for dropkv_score_ex. */
 enum {
   DROPKV_FLAG_GENERIC = 1, /* force the plain-VALU path even where the MFMA path applies */
-  DROPKV_FLAG_STAGE_LOG = 2 /* dropkv_score_ex only: record a HIP event after every kernel of
-                               the call into the library's stage log (see dropkv_stage_log) */
+  DROPKV_FLAG_STAGE_LOG = 2 /* dropkv_score_ex only: record each stage's begin and end time
+                               (the dispatch timestamps of its first and last kernel on the
+                               MFMA path and the select stage) into the library's stage log
+                               (see dropkv_stage_log) */
 };
 
 /*
@@ -194,7 +196,8 @@ int dropkv_select(const float* S, int64_t n, int32_t window, int32_t Hkv, int32_
 
 /*
  * Measurement form of dropkv_score: runs the whole path once on `stream`
- * with a HIP event recorded after every kernel, synchronises, and writes the
+ * with each stage's begin and end time recorded (as DROPKV_FLAG_STAGE_LOG
+ * does), synchronises, and writes the
  * duration of each stage in milliseconds to out_ms[0..*out_count-1] (at most
  * 12 stages) and their comma-separated names to out_names (names_bytes
  * bytes, NUL-terminated; may be NULL). Outputs and return codes are those of

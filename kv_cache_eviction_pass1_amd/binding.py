@@ -498,7 +498,7 @@ class DecodeScorer:
 
 
 def stage_times(q, k, v, *, pool_kernel: int, n_evict: int, flags: int = 0, stream=None):
-    """One scoring call with a HIP event after every kernel.
+    """One scoring call with each stage's begin and end time recorded.
 
     Returns (scores, evict_idx, [(stage name, milliseconds), ...]).
     """
