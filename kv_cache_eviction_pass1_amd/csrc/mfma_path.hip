@@ -32,6 +32,7 @@
 // operand reads and the transposing 8-byte reads on gfx950's 64-bank LDS).
 #include "dropkv_common.h"
 
+#include <climits>
 #include <type_traits>
 
 namespace dropkv {
@@ -77,6 +78,10 @@ __device__ __forceinline__ float pair_sum(float x) {
   auto s = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
   return __uint_as_float(s[0]) + __uint_as_float(s[1]);
 }
+__device__ __forceinline__ int pair_min(int x) {
+  auto s = __builtin_amdgcn_permlane32_swap((unsigned)x, (unsigned)x, false, false);
+  return min((int)s[0], (int)s[1]);
+}
 
 __device__ __forceinline__ bf16x8 ld16(const char* p) { return *(const bf16x8*)p; }
 
@@ -95,6 +100,11 @@ __device__ __forceinline__ bf16x8 tr_pair(const char* p0, const char* p1) {
   u.h[0] = lo;
   u.h[1] = hi;
   return u.v;
+}
+
+// LDS byte address of a pointer into shared memory.
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)(size_t)(const __attribute__((address_space(3))) char*)p;
 }
 
 __device__ __forceinline__ uint16_t f32_to_bf16_rne(float x) {
@@ -202,6 +212,27 @@ __device__ __forceinline__ LdsOff lds_offsets(int lane) {
   return o;
 }
 
+// The same offsets with the transposing reads' LDS base folded in: v[i]
+// becomes the LDS byte address of element v[i] of the first V buffer at
+// vbase (p1_tile subtracts that base again in the pointer arithmetic, so the
+// reads stay derived from the buffer and the compiler still knows which
+// array they read: it does not wait for the tile loads in flight into the
+// other buffers). The V buffers follow the three K buffers, so the later
+// ones start beyond the 16-bit offset field of an LDS read; with their base
+// held in these registers (which the compiler must not split up again) every
+// buffer, subtile and step offset is an immediate of at most 44 KiB, and no
+// per-read address arithmetic is left in the loop.
+__device__ __forceinline__ LdsOff with_v_base(LdsOff o, const char* vbase) {
+  const uint32_t b = lds_addr(vbase);
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    int x = o.v[i] + (int)b;
+    asm volatile("" : "+v"(x));
+    o.v[i] = x;
+  }
+  return o;
+}
+
 // ||v_j||^2 of the tiles, computed by pass 1 while V sits in LDS: NW lanes
 // per token (wave w takes tokens (64/NW) w .. +64/NW-1), each squaring 128/NW
 // dims with two-term dot products (bf16 squares are exact, sums fp32), then
@@ -255,9 +286,15 @@ __device__ __forceinline__ void p1_vnorms(const char* vb, const VnOff<NW>& vo, f
   DKV_CHECK(tt < TT, status);
 }
 
-// Online-softmax state of one window row (one lane pair).
-//  m_true : largest logit seen so far (exact running max, for the merge);
-//  mref   : reference exponent (log2 domain) of l and O, i.e. l = sum 2^{x c - mref}.
+// Online-softmax state of one window row, held by the lane pair (l, l ^ 32)
+// that shares the row's column of X^T; each lane sees half of every subtile's
+// tokens.
+//  m_true : largest logit among this lane's tokens so far (exact; the two
+//           lanes are combined by p1_row_max at the end);
+//  best   : 32-token block of the first occurrence of m_true;
+//  mref   : reference exponent (log2 domain) of l and O, i.e. l = sum 2^{x c - mref},
+//           always equal in both lanes of the pair (O sums over both);
+//  nb     : -mref, or 0 while mref is -inf (no finite logit yet).
 // The reference only moves when a logit exceeds it by more than kLazy (a
 // factor 2^8 in p), so the O/l rescale runs a few times per chunk instead of
 // at every new maximum; p stays below 2^8, well inside bf16 and fp32 range.
@@ -265,19 +302,33 @@ constexpr float kLazy = 8.0f;
 
 struct P1State {
   float m_true, mref, l;
-  int best;  // 32-token block of the first occurrence of m_true
+  int best;
+  float nb;
 };
 
+// The row's largest logit and the first block holding it, from the two lanes
+// of the pair (lowest block among the lanes that attain it). All 64 lanes of
+// the wave must be active.
+__device__ __forceinline__ void p1_row_max(P1State& st) {
+  const float m = pair_max(st.m_true);
+  st.best = pair_min(st.m_true == m ? st.best : INT_MAX);
+  st.m_true = m;
+}
+
 // One 64-token tile of pass 1 for this wave's 32 rows (X^T layout: lane = row).
+// kb: the tile's K buffer; vb0: the first V buffer, whose LDS address
+// off.v already holds (with_v_base); vofs: byte offset of the tile's V buffer
+// from it.
 template <bool MASK>
-__device__ __forceinline__ void p1_tile(float c2, const char* kb, const char* vb, int64_t tokbase_tile,
+__device__ __forceinline__ void p1_tile(float c2, const char* kb, const char* vb0, int vofs, int64_t tokbase_tile,
                                         const LdsOff& off, int lane, int64_t pos,
                                         const bf16x8 (&qb)[8], P1State& st, f32x16 (&O)[4]) {
   const int h = lane >> 5;
+  const int vb0_addr = (int)lds_addr(vb0);
 #pragma unroll
   for (int sub = 0; sub < 2; ++sub) {
     const char* kt = kb + sub * 32 * 256;
-    const char* vt = vb + sub * 32 * 256;
+    const char* vt = vb0 + (vofs + sub * 32 * 256 - vb0_addr);
     bf16x8 ka[8];
 #pragma unroll
     for (int ks = 0; ks < 8; ++ks) ka[ks] = ld16(kt + off.k[ks]);
@@ -307,31 +358,35 @@ __device__ __forceinline__ void p1_tile(float c2, const char* kb, const char* vb
         if (tok > pos) x[vv] = -INFINITY;
       }
     }
-    float mx = fmaxf(fmaxf(x[0], x[1]), x[2]);
+    // this lane's running maximum over its own tokens (the chain starts from
+    // the running value, so no NaN quieting of the raw MFMA outputs is
+    // needed); the pair is combined only when the reference moves
+    float mx = fmaxf(fmaxf(st.m_true, x[0]), x[1]);
 #pragma unroll
-    for (int vv = 3; vv < 15; vv += 2) mx = fmaxf(fmaxf(mx, x[vv]), x[vv + 1]);
-    mx = pair_max(fmaxf(mx, x[15]));
+    for (int vv = 2; vv < 16; vv += 2) mx = fmaxf(fmaxf(mx, x[vv]), x[vv + 1]);
     if (mx > st.m_true) {
       st.m_true = mx;
       st.best = (int)(tokbase >> 5);
     }
     if (__builtin_amdgcn_ballot_w64(mx * c2 > st.mref + kLazy)) {
-      const float nref = st.m_true * c2;
+      const float nref = pair_max(st.m_true) * c2;  // the same in both lanes of the row
       if (nref > st.mref) {
         const float alpha = (st.mref == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(st.mref - nref);
         st.l *= alpha;
 #pragma unroll
         for (int db = 0; db < 4; ++db) O[db] *= alpha;
         st.mref = nref;
+        st.nb = -nref;
       }
     }
-    const float nb = (st.mref == -INFINITY) ? 0.f : -st.mref;
     float e[16];
-    float ls0 = 0.f, ls1 = 0.f;
+    e[0] = __builtin_amdgcn_exp2f(fmaf(x[0], c2, st.nb));
+    e[1] = __builtin_amdgcn_exp2f(fmaf(x[1], c2, st.nb));
+    float ls0 = e[0], ls1 = e[1];
 #pragma unroll
-    for (int vv = 0; vv < 16; vv += 2) {
-      e[vv] = __builtin_amdgcn_exp2f(fmaf(x[vv], c2, nb));
-      e[vv + 1] = __builtin_amdgcn_exp2f(fmaf(x[vv + 1], c2, nb));
+    for (int vv = 2; vv < 16; vv += 2) {
+      e[vv] = __builtin_amdgcn_exp2f(fmaf(x[vv], c2, st.nb));
+      e[vv + 1] = __builtin_amdgcn_exp2f(fmaf(x[vv + 1], c2, st.nb));
       ls0 += e[vv];
       ls1 += e[vv + 1];
     }
@@ -400,7 +455,7 @@ __global__ __launch_bounds__(NW * 64) void k_pass1(P1Args A) {
   float* nvh = A.nv + (size_t)g * A.n;
   const int64_t pos = A.n - A.w + ((row_ok ? row : 0) % A.w);
   const float c2 = A.c2;
-  const LdsOff off = lds_offsets(lane);
+  const LdsOff off = with_v_base(lds_offsets(lane), vbuf[0]);
   const DmaOff<NW> doff = dma_offsets<NW>(wave, lane);
   const VnOff<NW> vno = vn_offsets<NW>(wave, lane);
   {
@@ -423,7 +478,7 @@ __global__ __launch_bounds__(NW * 64) void k_pass1(P1Args A) {
       qb[ks] = t;
     }
   }
-  P1State st{-INFINITY, -INFINITY, 0.f, -1};
+  P1State st{-INFINITY, -INFINITY, 0.f, -1, 0.f};
   f32x16 O[4];
 #pragma unroll
   for (int db = 0; db < 4; ++db) O[db] = f32x16{};
@@ -453,7 +508,7 @@ __global__ __launch_bounds__(NW * 64) void k_pass1(P1Args A) {
     constexpr int B = decltype(bc)::value;
     constexpr int N2 = (B + 2) % 3;
     head(t, vbuf[B], kbuf[N2], vbuf[N2]);
-    if (active) p1_tile<false>(c2, kbuf[B], vbuf[B], t0 + (int64_t)t * TT, off, lane, pos, qb, st, O);
+    if (active) p1_tile<false>(c2, kbuf[B], vbuf[0], B * TILE_BYTES, t0 + (int64_t)t * TT, off, lane, pos, qb, st, O);
   };
   int t = 0;
   for (; t + 3 <= nclean; t += 3) {
@@ -464,10 +519,11 @@ __global__ __launch_bounds__(NW * 64) void k_pass1(P1Args A) {
   for (; t < ntiles; ++t) {  // at most two clean tiles, then the masked tail
     const int b = t % 3, nb = (t + 2) % 3;
     head(t, vbuf[b], kbuf[nb], vbuf[nb]);
-    if (active) p1_tile<true>(c2, kbuf[b], vbuf[b], t0 + (int64_t)t * TT, off, lane, pos, qb, st, O);
+    if (active) p1_tile<true>(c2, kbuf[b], vbuf[0], b * TILE_BYTES, t0 + (int64_t)t * TT, off, lane, pos, qb, st, O);
   }
   if (!active) return;
   const float l_tot = pair_sum(st.l);
+  p1_row_max(st);
   if (!row_ok) return;
   DKV_CHECK(chunk < (int)gridDim.x && g < A.Hkv && row < A.Rg && t1 <= A.n, A.status);
   float* pr = A.part + ((size_t)chunk * A.Hkv * A.Rg + (size_t)g * A.Rg + row) * PSTRIDE;
@@ -1460,7 +1516,7 @@ __global__ __launch_bounds__(NW * 64) void k_prefill(PrefillArgs A) {
   const uint16_t* vh = A.v + (size_t)g * A.n * HD;
   const int qh = g * A.G + (row_ok ? t : 0);
   const float c2 = A.c2;
-  const LdsOff off = lds_offsets(lane);
+  const LdsOff off = with_v_base(lds_offsets(lane), vbuf[0]);
   const DmaOff<NW> doff = dma_offsets<NW>(wave, lane);
 
   bf16x8 qb[8];
@@ -1473,7 +1529,7 @@ __global__ __launch_bounds__(NW * 64) void k_prefill(PrefillArgs A) {
       qb[ks] = tq;
     }
   }
-  P1State st{-INFINITY, -INFINITY, 0.f, -1};
+  P1State st{-INFINITY, -INFINITY, 0.f, -1, 0.f};
   f32x16 O[4];
 #pragma unroll
   for (int db = 0; db < 4; ++db) O[db] = f32x16{};
@@ -1501,7 +1557,7 @@ __global__ __launch_bounds__(NW * 64) void k_prefill(PrefillArgs A) {
     constexpr int B = decltype(bc)::value;
     constexpr int N2 = (B + 2) % 3;
     head(tt, kbuf[N2], vbuf[N2]);
-    if (active) p1_tile<false>(c2, kbuf[B], vbuf[B], (int64_t)tt * TT, off, lane, pos, qb, st, O);
+    if (active) p1_tile<false>(c2, kbuf[B], vbuf[0], B * TILE_BYTES, (int64_t)tt * TT, off, lane, pos, qb, st, O);
   };
   int tt = 0;
   for (; tt + 3 <= nclean; tt += 3) {
@@ -1512,10 +1568,11 @@ __global__ __launch_bounds__(NW * 64) void k_prefill(PrefillArgs A) {
   for (; tt < ntiles; ++tt) {  // at most two clean tiles, then the diagonal ones
     const int b = tt % 3, nb = (tt + 2) % 3;
     head(tt, kbuf[nb], vbuf[nb]);
-    if (active) p1_tile<true>(c2, kbuf[b], vbuf[b], (int64_t)tt * TT, off, lane, pos, qb, st, O);
+    if (active) p1_tile<true>(c2, kbuf[b], vbuf[0], b * TILE_BYTES, (int64_t)tt * TT, off, lane, pos, qb, st, O);
   }
   if (!active) return;
   const float l_tot = pair_sum(st.l);
+  p1_row_max(st);
   if (!row_ok) return;
   const float inv_l = 1.0f / l_tot;
   // lane holds O^T rows d = 32 db + 8 i + 4 h + (0..3) of its row's column
