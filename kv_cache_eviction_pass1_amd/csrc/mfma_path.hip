@@ -114,60 +114,60 @@ __device__ __forceinline__ uint16_t f32_to_bf16_rne(float x) {
   return (uint16_t)(b >> 16);
 }
 
-// Issue direct-to-LDS loads of one 64-token tile of one tensor: 16 wave
-// instructions of 1 KiB (4 token rows each), instruction wave + i*NW of NW waves.
-template <int NW>
-__device__ __forceinline__ void issue_tile(const uint16_t* __restrict__ head, int64_t tok0, int64_t n,
-                                           char* lds, int wave, int lane) {
-#pragma unroll
-  for (int i = 0; i < 16 / NW; ++i) {
-    const int inst = wave + i * NW;
-    const int row = inst * 4 + (lane >> 4);
-    const int c = (lane & 15) ^ swz(row);
-    int64_t tok = tok0 + row;
-    if (tok >= n) tok = n - 1;  // clamped rows are masked out by the consumers
-    const uint16_t* gp = head + tok * HD + c * 8;
-    __builtin_amdgcn_global_load_lds((gbl_cvoid*)gp, (lds_void*)(lds + inst * 1024), 16, 0, 0);
-  }
-}
-
-// Lane byte offsets of the direct-to-LDS loads of a full tile: load i of wave
-// `wave` fetches token rows 4 (wave + i NW) .. +3, lane l the 16-byte chunk
-// (l%16) ^ swz(row) of row 4 (wave + i NW) + l/16. They do not depend on the
-// tile, so a full tile needs one uniform base address and no per-lane math.
-// (Kept for NW >= 4 only: with fewer waves the offsets would occupy 8-16
-// registers, and those narrow workgroups recompute them per load instead.)
+// Lane byte offsets of the direct-to-LDS tile loads: load i of wave `wave`
+// fetches token rows 4 (wave + i NW) .. +3 of the tile, lane l the 16-byte
+// chunk (l%16) ^ swz(row) of row 4 (wave + i NW) + l/16. They do not depend
+// on the tile. (Kept for NW >= 4 only: with fewer waves the offsets would
+// occupy 8-16 registers, and those narrow workgroups recompute them per load.)
 template <int NW>
 struct DmaOff {
   static constexpr int kN = NW >= 4 ? 16 / NW : 1;
   uint32_t g[kN];
 };
 
+__device__ __forceinline__ uint32_t dma_offset(int inst, int lane) {
+  const int row = inst * 4 + (lane >> 4);
+  return (uint32_t)(row * 256 + (((lane & 15) ^ swz(row)) << 4));
+}
+
 template <int NW>
 __device__ __forceinline__ DmaOff<NW> dma_offsets(int wave, int lane) {
   DmaOff<NW> o;
 #pragma unroll
-  for (int i = 0; i < DmaOff<NW>::kN; ++i) {
-    const int row = (wave + i * NW) * 4 + (lane >> 4);
-    o.g[i] = (uint32_t)(row * 256 + (((lane & 15) ^ swz(row)) << 4));
-  }
+  for (int i = 0; i < DmaOff<NW>::kN; ++i) o.g[i] = dma_offset(wave + i * NW, lane);
   return o;
 }
 
-// Loads of tile [tok0, tok0 + 64): full tiles take the offset form, a tile
-// that runs past n clamps its rows (issue_tile).
+// Buffer descriptor of `bytes` bytes at p (a raw buffer: stride 0, 32-bit
+// data format); loads past `bytes` return zeros, and a direct-to-LDS load
+// writes those zeros.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t raw_rsrc(const void* p, int bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, bytes, 0x00020000);
+}
+
+// Direct-to-LDS loads of the 64-token tile of one tensor that starts at
+// token tok0: 16 wave instructions of 1 KiB (4 token rows each), instruction
+// wave + i*NW of NW waves. The descriptor covers the tile's `rows` valid rows
+// (64, or n - tok0 >= 1 on a ragged last tile), so the rows past n arrive as
+// zeros (masked by every consumer, and zero keeps 0 * V finite) and nothing
+// outside the tensor is read. Base, range and tile live in scalar registers:
+// a lane's only address is its 32-bit offset inside the tile.
 template <int NW>
-__device__ __forceinline__ void issue_any(const uint16_t* __restrict__ head, int64_t tok0, int64_t n,
-                                          char* lds, int wave, int lane, const DmaOff<NW>& o) {
-  if (NW >= 4 && tok0 + TT <= n) {
-    const char* base = (const char*)(head + tok0 * HD);
+__device__ __forceinline__ void issue_tile(const uint16_t* __restrict__ head, int64_t tok0, int rows, char* lds,
+                                           int wave, int lane, const DmaOff<NW>& o) {
+  const __amdgpu_buffer_rsrc_t r = raw_rsrc(head + tok0 * HD, rows * (HD * 2));
 #pragma unroll
-    for (int i = 0; i < DmaOff<NW>::kN; ++i)
-      __builtin_amdgcn_global_load_lds((gbl_cvoid*)(base + o.g[i]), (lds_void*)(lds + (wave + i * NW) * 1024),
-                                       16, 0, 0);
-  } else {
-    issue_tile<NW>(head, tok0, n, lds, wave, lane);
+  for (int i = 0; i < 16 / NW; ++i) {
+    const int inst = wave + i * NW;
+    const uint32_t off = NW >= 4 ? o.g[i < DmaOff<NW>::kN ? i : 0] : dma_offset(inst, lane);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)(lds + inst * 1024), 16, off, 0, 0, 0);
   }
+}
+
+// Valid rows of tile tl of a range [r0, r1) of tokens: 64 for the full tiles
+// 0 .. nfull - 1 (nfull = (r1 - r0) / 64, a scalar 32-bit test), else the rest.
+__device__ __forceinline__ int tile_rows(int tl, int nfull, int64_t r0, int64_t r1) {
+  return tl < nfull ? TT : (int)(r1 - (r0 + (int64_t)tl * TT));
 }
 
 // ---------------------------------------------------------------------------- pass 1
@@ -449,6 +449,7 @@ __global__ __launch_bounds__(NW * 64) void k_pass1(P1Args A) {
   int64_t t1 = t0 + (int64_t)A.tiles_per_chunk * TT;
   if (t1 > A.n) t1 = A.n;
   const int ntiles = (int)((t1 - t0 + TT - 1) / TT);
+  const int nfull = (int)((t1 - t0) / TT);  // tiles 0 .. nfull - 1 end at or before t1 <= n
   const int nclean = clean_tiles(A.n, A.w, t0, ntiles);
   const uint16_t* kh = A.k + (size_t)g * A.ld * HD;
   const uint16_t* vh = A.v + (size_t)g * A.ld * HD;
@@ -484,12 +485,12 @@ __global__ __launch_bounds__(NW * 64) void k_pass1(P1Args A) {
   for (int db = 0; db < 4; ++db) O[db] = f32x16{};
 
   if (ntiles > 0) {
-    issue_any<NW>(kh, t0, A.n, kbuf[0], wave, lane, doff);
-    issue_any<NW>(vh, t0, A.n, vbuf[0], wave, lane, doff);
+    issue_tile<NW>(kh, t0, tile_rows(0, nfull, t0, t1), kbuf[0], wave, lane, doff);
+    issue_tile<NW>(vh, t0, tile_rows(0, nfull, t0, t1), vbuf[0], wave, lane, doff);
   }
   if (ntiles > 1) {
-    issue_any<NW>(kh, t0 + TT, A.n, kbuf[1], wave, lane, doff);
-    issue_any<NW>(vh, t0 + TT, A.n, vbuf[1], wave, lane, doff);
+    issue_tile<NW>(kh, t0 + TT, tile_rows(1, nfull, t0, t1), kbuf[1], wave, lane, doff);
+    issue_tile<NW>(vh, t0 + TT, tile_rows(1, nfull, t0, t1), vbuf[1], wave, lane, doff);
   }
   // Per tile the vector-memory ops are, in issue order: the ||v||^2 store of
   // tile t, then the loads of tile t+2; so `vmcnt <= one tile's loads` at the
@@ -500,8 +501,8 @@ __global__ __launch_bounds__(NW * 64) void k_pass1(P1Args A) {
     lds_barrier();  // tile t in LDS for every wave; tile t-1's buffer is free
     if (rg == 0) p1_vnorms<NW>(vc, vno, nvh + tb, t1 - tb, wave, lane, A.status);
     if (t + 2 < ntiles) {
-      issue_any<NW>(kh, tb + 2 * TT, A.n, kn, wave, lane, doff);
-      issue_any<NW>(vh, tb + 2 * TT, A.n, vn, wave, lane, doff);
+      issue_tile<NW>(kh, tb + 2 * TT, tile_rows(t + 2, nfull, t0, t1), kn, wave, lane, doff);
+      issue_tile<NW>(vh, tb + 2 * TT, tile_rows(t + 2, nfull, t0, t1), vn, wave, lane, doff);
     }
   };
   auto clean = [&](auto bc, int t) {
@@ -963,11 +964,12 @@ __global__ __launch_bounds__(256) void k_import(ImportArgs I) {
 
 enum { kTierSquare = 0, kTierSeries = 1, kTierExact = 2 };
 
-// ||v||^2 of the 64 tokens of a tile into LDS (one 4-byte direct-to-LDS load per lane)
-__device__ __forceinline__ void issue_nv(const float* nvh, int64_t tok0, int64_t n, float* lds, int lane) {
-  int64_t tok = tok0 + lane;
-  if (tok >= n) tok = n - 1;
-  __builtin_amdgcn_global_load_lds((gbl_cvoid*)(nvh + tok), (lds_void*)lds, 4, 0, 0);
+// ||v||^2 of the 64 tokens of a tile into LDS: one 4-byte direct-to-LDS load
+// per lane, issued by one wave of the workgroup; `rows` valid tokens (the
+// rest arrive as zeros, as in issue_tile).
+__device__ __forceinline__ void issue_nv(const float* nvh, int64_t tok0, int rows, float* lds, int lane) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(raw_rsrc(nvh + tok0, rows * 4), (lds_void*)lds, 4, (uint32_t)lane * 4u, 0,
+                                           0, 0);
 }
 
 // Score terms of one subtile from y2 = 2 (x c - bias) = log2 p^2:
@@ -1073,18 +1075,22 @@ __global__ __launch_bounds__(NW * 64) void k_pass2(P2Args P, FixArgs F) {
   __shared__ float red3[3][NW][TT];
   __shared__ float red3b[NVC ? 3 : 1][NW][TT];  // NVC: the waves' shares of sum r^2 per token
   __shared__ float nvbuf[3][TT];
-  constexpr int kDmaPerTile = 32 / NW + (NVC ? 0 : 1);  // direct-to-LDS instructions per wave per tile
+  // direct-to-LDS instructions per tile: 32 / NW per wave for K and V, plus
+  // the ||v||^2 load in wave 0 (not in NVC mode)
+  constexpr int kDmaPerTile = 32 / NW;
   const int chunk = blockIdx.x, rg = blockIdx.y, g = blockIdx.z;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
   const int h = lane >> 5, l32 = lane & 31;
   const int rb = rg * NW + wave;
   const bool active = rb * 32 < P.Rg;
+  const bool nv_wave = !NVC && wave == 0;
   int nwa = (P.Rg - rg * NW * 32 + 31) / 32;  // active waves
   if (nwa > NW) nwa = NW;
   const int64_t t0 = (int64_t)chunk * P.tiles_per_chunk * TT;
   int64_t t1 = t0 + (int64_t)P.tiles_per_chunk * TT;
   if (t1 > P.n) t1 = P.n;
   const int ntiles = (int)((t1 - t0 + TT - 1) / TT);
+  const int nfull = (int)((t1 - t0) / TT);  // tiles 0 .. nfull - 1 end at or before t1 <= n
   const uint16_t* kh = P.k + (size_t)g * P.n * HD;
   const uint16_t* vh = P.v + (size_t)g * P.n * HD;
   const float* __restrict__ nvg = NVC ? nullptr : P.nv + (size_t)g * P.n;
@@ -1117,8 +1123,8 @@ __global__ __launch_bounds__(NW * 64) void k_pass2(P2Args P, FixArgs F) {
   }
 
   if (ntiles > 0) {
-    issue_tile<NW>(kh, t0, P.n, kbuf[0], wave, lane);
-    issue_tile<NW>(vh, t0, P.n, vbuf[0], wave, lane);
+    issue_tile<NW>(kh, t0, tile_rows(0, nfull, t0, t1), kbuf[0], wave, lane, doff);
+    issue_tile<NW>(vh, t0, tile_rows(0, nfull, t0, t1), vbuf[0], wave, lane, doff);
   }
 
   if (flagged) {
@@ -1129,8 +1135,10 @@ __global__ __launch_bounds__(NW * 64) void k_pass2(P2Args P, FixArgs F) {
       const int b = it & 1;
       tile_barrier();
       if (it + 1 < ntiles) {
-        issue_tile<NW>(kh, t0 + (int64_t)(it + 1) * TT, P.n, kbuf[b ^ 1], wave, lane);
-        issue_tile<NW>(vh, t0 + (int64_t)(it + 1) * TT, P.n, vbuf[b ^ 1], wave, lane);
+        issue_tile<NW>(kh, t0 + (int64_t)(it + 1) * TT, tile_rows(it + 1, nfull, t0, t1), kbuf[b ^ 1], wave, lane,
+                       doff);
+        issue_tile<NW>(vh, t0 + (int64_t)(it + 1) * TT, tile_rows(it + 1, nfull, t0, t1), vbuf[b ^ 1], wave, lane,
+                       doff);
       }
       p2_tile(P, kbuf[b], vbuf[b], t0 + (int64_t)it * TT, lane, active, rb, qa, aa, bias, cinit,
               true, g, red, wave);
@@ -1142,11 +1150,11 @@ __global__ __launch_bounds__(NW * 64) void k_pass2(P2Args P, FixArgs F) {
 
   // the fast path's only vector-memory loads are the direct-to-LDS tile loads
   // (K, V and ||v||^2), so `vmcnt <= one tile's loads` means the older tile landed
-  if (!NVC && ntiles > 0) issue_nv(nvg, t0, P.n, nvbuf[0], lane);
+  if (nv_wave && ntiles > 0) issue_nv(nvg, t0, tile_rows(0, nfull, t0, t1), nvbuf[0], lane);
   if (ntiles > 1) {
-    issue_any<NW>(kh, t0 + TT, P.n, kbuf[1], wave, lane, doff);
-    issue_any<NW>(vh, t0 + TT, P.n, vbuf[1], wave, lane, doff);
-    if (!NVC) issue_nv(nvg, t0 + TT, P.n, nvbuf[1], lane);
+    issue_tile<NW>(kh, t0 + TT, tile_rows(1, nfull, t0, t1), kbuf[1], wave, lane, doff);
+    issue_tile<NW>(vh, t0 + TT, tile_rows(1, nfull, t0, t1), vbuf[1], wave, lane, doff);
+    if (nv_wave) issue_nv(nvg, t0 + TT, tile_rows(1, nfull, t0, t1), nvbuf[1], lane);
   }
   const float c2x2 = 2.0f * P.c2;
   const LdsOff off = lds_offsets(lane);
@@ -1156,8 +1164,9 @@ __global__ __launch_bounds__(NW * 64) void k_pass2(P2Args P, FixArgs F) {
   const int rbase = rb * 32 + 4 * h;  // first row of this lane's 16 (masked tiles only)
   const int nclean = clean_tiles(P.n, P.w, t0, ntiles);
   // scores of tile t-1 (every wave wrote its partial before the barrier at tile t)
+  static_assert(TT == 64, "one wave combines a tile");
   auto combine = [&](int tl, const float (*red)[TT]) {
-    if (threadIdx.x < TT) {
+    if (wave == 0) {  // wave-uniform: the other waves skip it with a scalar branch
       const int64_t tok = t0 + (int64_t)tl * TT + threadIdx.x;
       if (tok < t1) {
         float sacc = 0.f;
@@ -1198,13 +1207,17 @@ __global__ __launch_bounds__(NW * 64) void k_pass2(P2Args P, FixArgs F) {
   };
   auto head = [&](int t, const float (*red_prev)[TT], char* kn, char* vn, float* nvn) {
     const int64_t tb = t0 + (int64_t)t * TT;
-    if (t + 1 < ntiles) wait_vmcnt<kDmaPerTile>(); else wait_vmcnt<0>();
+    if (t + 1 < ntiles) {
+      if (nv_wave) wait_vmcnt<kDmaPerTile + 1>(); else wait_vmcnt<kDmaPerTile>();
+    } else {
+      wait_vmcnt<0>();
+    }
     lds_barrier();  // tile t in LDS for every wave; tile t-1's buffer is free
     if (t >= 1) combine(t - 1, red_prev);
     if (t + 2 < ntiles) {
-      issue_any<NW>(kh, tb + 2 * TT, P.n, kn, wave, lane, doff);
-      issue_any<NW>(vh, tb + 2 * TT, P.n, vn, wave, lane, doff);
-      if (!NVC) issue_nv(nvg, tb + 2 * TT, P.n, nvn, lane);
+      issue_tile<NW>(kh, tb + 2 * TT, tile_rows(t + 2, nfull, t0, t1), kn, wave, lane, doff);
+      issue_tile<NW>(vh, tb + 2 * TT, tile_rows(t + 2, nfull, t0, t1), vn, wave, lane, doff);
+      if (nv_wave) issue_nv(nvg, tb + 2 * TT, tile_rows(t + 2, nfull, t0, t1), nvn, lane);
     }
   };
   // token offset of this lane's column relative to n - w, for the causal mask
@@ -1511,6 +1524,7 @@ __global__ __launch_bounds__(NW * 64) void k_prefill(PrefillArgs A) {
   int64_t nkeys = p0 + A.PB;  // keys 0 .. nkeys - 1 are visible to some row
   if (nkeys > A.n) nkeys = A.n;
   const int ntiles = (int)((nkeys + TT - 1) / TT);
+  const int nfull = (int)(nkeys / TT);  // tiles 0 .. nfull - 1 hold 64 keys each
   const int nclean = (int)((p0 + 1) / TT) < ntiles ? (int)((p0 + 1) / TT) : ntiles;  // tiles every row sees whole
   const uint16_t* kh = A.k + (size_t)g * A.n * HD;
   const uint16_t* vh = A.v + (size_t)g * A.n * HD;
@@ -1535,12 +1549,12 @@ __global__ __launch_bounds__(NW * 64) void k_prefill(PrefillArgs A) {
   for (int db = 0; db < 4; ++db) O[db] = f32x16{};
 
   if (ntiles > 0) {
-    issue_any<NW>(kh, 0, nkeys, kbuf[0], wave, lane, doff);
-    issue_any<NW>(vh, 0, nkeys, vbuf[0], wave, lane, doff);
+    issue_tile<NW>(kh, 0, tile_rows(0, nfull, 0, nkeys), kbuf[0], wave, lane, doff);
+    issue_tile<NW>(vh, 0, tile_rows(0, nfull, 0, nkeys), vbuf[0], wave, lane, doff);
   }
   if (ntiles > 1) {
-    issue_any<NW>(kh, TT, nkeys, kbuf[1], wave, lane, doff);
-    issue_any<NW>(vh, TT, nkeys, vbuf[1], wave, lane, doff);
+    issue_tile<NW>(kh, TT, tile_rows(1, nfull, 0, nkeys), kbuf[1], wave, lane, doff);
+    issue_tile<NW>(vh, TT, tile_rows(1, nfull, 0, nkeys), vbuf[1], wave, lane, doff);
   }
   // per tile and wave the only vector-memory ops are the tile loads, so
   // `vmcnt <= one tile's loads` at the top of tile t + 1 means it has landed
@@ -1549,8 +1563,8 @@ __global__ __launch_bounds__(NW * 64) void k_prefill(PrefillArgs A) {
     if (tt + 1 < ntiles) wait_vmcnt<kDmaPerTile>(); else wait_vmcnt<0>();
     lds_barrier();
     if (tt + 2 < ntiles) {
-      issue_any<NW>(kh, tb + 2 * TT, nkeys, kn, wave, lane, doff);
-      issue_any<NW>(vh, tb + 2 * TT, nkeys, vn, wave, lane, doff);
+      issue_tile<NW>(kh, tb + 2 * TT, tile_rows(tt + 2, nfull, 0, nkeys), kn, wave, lane, doff);
+      issue_tile<NW>(vh, tb + 2 * TT, tile_rows(tt + 2, nfull, 0, nkeys), vn, wave, lane, doff);
     }
   };
   auto clean = [&](auto bc, int tt) {
