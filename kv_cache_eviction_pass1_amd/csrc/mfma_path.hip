@@ -170,6 +170,15 @@ __device__ __forceinline__ int tile_rows(int tl, int nfull, int64_t r0, int64_t 
   return tl < nfull ? TT : (int)(r1 - (r0 + (int64_t)tl * TT));
 }
 
+// As tile_rows, and 0 for a tile past the last one (ntiles): loads through a
+// descriptor of zero range read nothing and write zeros. Loops that issue
+// their loads unconditionally this way give the compiler the same sequence
+// of memory operations on every path, so it can place its own waits for a
+// register loaded one tile ahead without draining the tile loads behind it.
+__device__ __forceinline__ int tile_rows_or0(int tl, int ntiles, int nfull, int64_t r0, int64_t r1) {
+  return tl < ntiles ? tile_rows(tl, nfull, r0, r1) : 0;
+}
+
 // ---------------------------------------------------------------------------- pass 1
 
 struct P1Args {
@@ -801,7 +810,7 @@ __device__ __forceinline__ void p2_tile(const P2Args& P, const char* kb, const c
                                         int64_t tokbase_tile, int lane, bool active, int rb,
                                         const bf16x8 (&qa)[8], const bf16x8 (&aa)[8],
                                         const float (&bias)[16], const float (&cinit)[16],
-                                        bool flagged, int g, float (*red)[TT][2], int wave) {
+                                        const int (&jst)[16], float (*red)[TT][2], int wave) {
   const int h = lane >> 5, l32 = lane & 31;
   if (!active) return;
 #pragma unroll
@@ -830,32 +839,17 @@ __device__ __forceinline__ void p2_tile(const P2Args& P, const char* kb, const c
         if (tok > pos) x[vv] = -INFINITY;
       }
     }
+    // some row of this KV head takes its argmax term from the fix-up: that
+    // (row, token) pair is left out here (jst[vv], -1 for none; n < 2^31)
     float t1 = 0.f, t2 = 0.f;
-    if (!flagged) {
 #pragma unroll
-      for (int vv = 0; vv < 16; ++vv) {
-        const float p = __builtin_amdgcn_exp2f(fmaf(x[vv], P.c2, -bias[vv]));
-        const float r = p * __builtin_amdgcn_rcpf(1.0f - p);
-        const float r2 = r * r;
-        t2 += r2;
-        t1 = fmaf(r2, cc[vv], t1);
-      }
-    } else {
-      // some row of this KV head takes its argmax term from the fix-up
-#pragma unroll
-      for (int vv = 0; vv < 16; ++vv) {
-        const int rr = rb * 32 + (vv >> 2) * 8 + 4 * h + (vv & 3);
-        bool skip = false;
-        if (rr < P.Rg) {
-          const int64_t row = (int64_t)g * P.Rg + rr;
-          skip = P.rs.flag[row] && (int64_t)P.rs.jstar[row] == tok;
-        }
-        const float p = skip ? 0.f : __builtin_amdgcn_exp2f(fmaf(x[vv], P.c2, -bias[vv]));
-        const float r = p * __builtin_amdgcn_rcpf(1.0f - p);
-        const float r2 = r * r;
-        t2 += r2;
-        t1 = fmaf(r2, cc[vv], t1);
-      }
+    for (int vv = 0; vv < 16; ++vv) {
+      const bool skip = jst[vv] == (int)tok;
+      const float p = skip ? 0.f : __builtin_amdgcn_exp2f(fmaf(x[vv], P.c2, -bias[vv]));
+      const float r = p * __builtin_amdgcn_rcpf(1.0f - p);
+      const float r2 = r * r;
+      t2 += r2;
+      t1 = fmaf(r2, cc[vv], t1);
     }
     t1 = pair_sum(t1);
     t2 = pair_sum(t2);
@@ -964,12 +958,17 @@ __global__ __launch_bounds__(256) void k_import(ImportArgs I) {
 
 enum { kTierSquare = 0, kTierSeries = 1, kTierExact = 2 };
 
-// ||v||^2 of the 64 tokens of a tile into LDS: one 4-byte direct-to-LDS load
-// per lane, issued by one wave of the workgroup; `rows` valid tokens (the
-// rest arrive as zeros, as in issue_tile).
-__device__ __forceinline__ void issue_nv(const float* nvh, int64_t tok0, int rows, float* lds, int lane) {
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(raw_rsrc(nvh + tok0, rows * 4), (lds_void*)lds, 4, (uint32_t)lane * 4u, 0,
-                                           0, 0);
+// ||v_j||^2 of this lane's two tokens (l32 and 32 + l32) of the tile at tok0,
+// which holds `rows` valid tokens (the rest read as zero): two 4-byte buffer
+// loads into registers. Pass 2 issues them one tile ahead, before the next
+// tile's K/V loads, so the wait for a tile's K/V also covers them (vector
+// memory operations complete in issue order).
+__device__ __forceinline__ float2 load_nv_pair(const float* nvh, int64_t tok0, int rows, int l32) {
+  const __amdgpu_buffer_rsrc_t r = raw_rsrc(nvh + tok0, rows * 4);
+  float2 o;
+  o.x = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r, (uint32_t)l32 * 4u, 0, 0));
+  o.y = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r, (uint32_t)l32 * 4u + 128u, 0, 0));
+  return o;
 }
 
 // Score terms of one subtile from y2 = 2 (x c - bias) = log2 p^2:
@@ -1070,20 +1069,25 @@ __global__ __launch_bounds__(NW * 64) void k_pass2(P2Args P, FixArgs F) {
     }
     return;
   }
-  __shared__ __attribute__((aligned(1024))) char kbuf[3][TILE_BYTES];
-  __shared__ __attribute__((aligned(1024))) char vbuf[3][TILE_BYTES];
+  // The three K and three V tile buffers are separate variables, not one
+  // [3][TILE_BYTES] array each: with a compile-time buffer index (the clean
+  // loop below is unrolled over the buffers) the compiler can then tell that
+  // a read of the current tile and the direct-to-LDS loads in flight into a
+  // later tile's buffer do not overlap, and places no wait for those loads
+  // before the read.
+  __shared__ __attribute__((aligned(1024))) char kbuf0[TILE_BYTES], kbuf1[TILE_BYTES], kbuf2[TILE_BYTES];
+  __shared__ __attribute__((aligned(1024))) char vbuf0[TILE_BYTES], vbuf1[TILE_BYTES], vbuf2[TILE_BYTES];
+  auto kbuf = [&](int i) -> char* { return i == 0 ? kbuf0 : (i == 1 ? kbuf1 : kbuf2); };
+  auto vbuf = [&](int i) -> char* { return i == 0 ? vbuf0 : (i == 1 ? vbuf1 : vbuf2); };
   __shared__ float red3[3][NW][TT];
   __shared__ float red3b[NVC ? 3 : 1][NW][TT];  // NVC: the waves' shares of sum r^2 per token
-  __shared__ float nvbuf[3][TT];
-  // direct-to-LDS instructions per tile: 32 / NW per wave for K and V, plus
-  // the ||v||^2 load in wave 0 (not in NVC mode)
-  constexpr int kDmaPerTile = 32 / NW;
+  __shared__ float nvbuf[NVC ? 3 : 1][TT];  // NVC: ||v_j||^2 of the tiles, formed in LDS
+  constexpr int kDmaPerTile = 32 / NW;  // direct-to-LDS instructions per wave and tile (K and V)
   const int chunk = blockIdx.x, rg = blockIdx.y, g = blockIdx.z;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
   const int h = lane >> 5, l32 = lane & 31;
   const int rb = rg * NW + wave;
   const bool active = rb * 32 < P.Rg;
-  const bool nv_wave = !NVC && wave == 0;
   int nwa = (P.Rg - rg * NW * 32 + 31) / 32;  // active waves
   if (nwa > NW) nwa = NW;
   const int64_t t0 = (int64_t)chunk * P.tiles_per_chunk * TT;
@@ -1123,39 +1127,51 @@ __global__ __launch_bounds__(NW * 64) void k_pass2(P2Args P, FixArgs F) {
   }
 
   if (ntiles > 0) {
-    issue_tile<NW>(kh, t0, tile_rows(0, nfull, t0, t1), kbuf[0], wave, lane, doff);
-    issue_tile<NW>(vh, t0, tile_rows(0, nfull, t0, t1), vbuf[0], wave, lane, doff);
+    issue_tile<NW>(kh, t0, tile_rows(0, nfull, t0, t1), kbuf(0), wave, lane, doff);
+    issue_tile<NW>(vh, t0, tile_rows(0, nfull, t0, t1), vbuf(0), wave, lane, doff);
   }
 
   if (flagged) {
     // per-tile path with the argmax exclusion of flagged rows (double-buffered)
     float (*red)[TT][2] = (float (*)[TT][2])&red3[0][0][0];
     static_assert(3 * NW * TT >= NW * TT * 2, "reduction buffer");
+    // per row of this lane: the token whose term the fix-up supplies (-1: none)
+    int jst[16];
+#pragma unroll
+    for (int vv = 0; vv < 16; ++vv) {
+      const int rr = rb * 32 + (vv >> 2) * 8 + 4 * h + (vv & 3);
+      jst[vv] = -1;
+      if (active && rr < P.Rg) {
+        const size_t row = (size_t)g * P.Rg + rr;
+        if (P.rs.flag[row]) jst[vv] = P.rs.jstar[row];
+      }
+    }
     for (int it = 0; it < ntiles; ++it) {
       const int b = it & 1;
       tile_barrier();
       if (it + 1 < ntiles) {
-        issue_tile<NW>(kh, t0 + (int64_t)(it + 1) * TT, tile_rows(it + 1, nfull, t0, t1), kbuf[b ^ 1], wave, lane,
+        issue_tile<NW>(kh, t0 + (int64_t)(it + 1) * TT, tile_rows(it + 1, nfull, t0, t1), kbuf(b ^ 1), wave, lane,
                        doff);
-        issue_tile<NW>(vh, t0 + (int64_t)(it + 1) * TT, tile_rows(it + 1, nfull, t0, t1), vbuf[b ^ 1], wave, lane,
+        issue_tile<NW>(vh, t0 + (int64_t)(it + 1) * TT, tile_rows(it + 1, nfull, t0, t1), vbuf(b ^ 1), wave, lane,
                        doff);
       }
-      p2_tile(P, kbuf[b], vbuf[b], t0 + (int64_t)it * TT, lane, active, rb, qa, aa, bias, cinit,
-              true, g, red, wave);
+      p2_tile(P, kbuf(b), vbuf(b), t0 + (int64_t)it * TT, lane, active, rb, qa, aa, bias, cinit, jst, red, wave);
       __syncthreads();
-      p2_combine<NVC>(P, red, nwa, t0 + (int64_t)it * TT, t1, g, vbuf[b]);
+      p2_combine<NVC>(P, red, nwa, t0 + (int64_t)it * TT, t1, g, vbuf(b));
     }
     return;
   }
 
-  // the fast path's only vector-memory loads are the direct-to-LDS tile loads
-  // (K, V and ||v||^2), so `vmcnt <= one tile's loads` means the older tile landed
-  if (nv_wave && ntiles > 0) issue_nv(nvg, t0, tile_rows(0, nfull, t0, t1), nvbuf[0], lane);
-  if (ntiles > 1) {
-    issue_tile<NW>(kh, t0 + TT, tile_rows(1, nfull, t0, t1), kbuf[1], wave, lane, doff);
-    issue_tile<NW>(vh, t0 + TT, tile_rows(1, nfull, t0, t1), vbuf[1], wave, lane, doff);
-    if (nv_wave) issue_nv(nvg, t0 + TT, tile_rows(1, nfull, t0, t1), nvbuf[1], lane);
-  }
+  // the fast path's vector-memory operations per tile are, in issue order:
+  // wave 0's score store, the next tile's ||v||^2 loads and the K/V loads of
+  // the tile after it, so `vmcnt <= one tile's K/V loads` at the top of tile t
+  // means tile t's K/V and ||v||^2 have landed
+  // ||v_j||^2 of this lane's tokens of the current tile and of the next one
+  // (the latter loaded one tile ahead; not in NVC mode)
+  float2 nv_cur = make_float2(0.f, 0.f), nv_next = make_float2(0.f, 0.f);
+  if (!NVC) nv_next = load_nv_pair(nvg, t0, tile_rows_or0(0, ntiles, nfull, t0, t1), l32);
+  issue_tile<NW>(kh, t0 + TT, tile_rows_or0(1, ntiles, nfull, t0, t1), kbuf(1), wave, lane, doff);
+  issue_tile<NW>(vh, t0 + TT, tile_rows_or0(1, ntiles, nfull, t0, t1), vbuf(1), wave, lane, doff);
   const float c2x2 = 2.0f * P.c2;
   const LdsOff off = lds_offsets(lane);
   float nb2[16];
@@ -1186,7 +1202,7 @@ __global__ __launch_bounds__(NW * 64) void k_pass2(P2Args P, FixArgs F) {
   // waves (8 lanes per token, 16 dims each); read by combine(t) after the
   // barrier at tile t + 1
   auto tile_vnorms = [&](int t) {
-    const char* vt = vbuf[t % 3];
+    const char* vt = vbuf(t % 3);
     const int li = lane & 7;
     for (int tk = wave * 8 + (lane >> 3); tk < TT; tk += NW * 8) {
       const bf16x8 x0 = ld16(vt + toff(tk, 8 * li)), x1 = ld16(vt + toff(tk, 64 + 8 * li));
@@ -1205,34 +1221,33 @@ __global__ __launch_bounds__(NW * 64) void k_pass2(P2Args P, FixArgs F) {
       if (li == 0) nvbuf[t % 3][tk] = a;
     }
   };
-  auto head = [&](int t, const float (*red_prev)[TT], char* kn, char* vn, float* nvn) {
+  // Every head issues the same loads (past the last tile with zero range, into
+  // a buffer nobody reads any more), so the wait at its top is the same too.
+  auto head = [&](int t, const float (*red_prev)[TT], char* kn, char* vn) {
     const int64_t tb = t0 + (int64_t)t * TT;
-    if (t + 1 < ntiles) {
-      if (nv_wave) wait_vmcnt<kDmaPerTile + 1>(); else wait_vmcnt<kDmaPerTile>();
-    } else {
-      wait_vmcnt<0>();
-    }
+    wait_vmcnt<kDmaPerTile>();
     lds_barrier();  // tile t in LDS for every wave; tile t-1's buffer is free
     if (t >= 1) combine(t - 1, red_prev);
-    if (t + 2 < ntiles) {
-      issue_tile<NW>(kh, tb + 2 * TT, tile_rows(t + 2, nfull, t0, t1), kn, wave, lane, doff);
-      issue_tile<NW>(vh, tb + 2 * TT, tile_rows(t + 2, nfull, t0, t1), vn, wave, lane, doff);
-      if (nv_wave) issue_nv(nvg, tb + 2 * TT, tile_rows(t + 2, nfull, t0, t1), nvn, lane);
+    if constexpr (!NVC) {
+      nv_cur = nv_next;
+      nv_next = load_nv_pair(nvg, tb + TT, tile_rows_or0(t + 1, ntiles, nfull, t0, t1), l32);
     }
+    issue_tile<NW>(kh, tb + 2 * TT, tile_rows_or0(t + 2, ntiles, nfull, t0, t1), kn, wave, lane, doff);
+    issue_tile<NW>(vh, tb + 2 * TT, tile_rows_or0(t + 2, ntiles, nfull, t0, t1), vn, wave, lane, doff);
   };
   // token offset of this lane's column relative to n - w, for the causal mask
   const int64_t tok_rel0 = t0 + l32 - (P.n - P.w);
   auto clean = [&](auto bc, int t) {
     constexpr int B = decltype(bc)::value;
     constexpr int N2 = (B + 2) % 3;
-    head(t, red3[N2], kbuf[N2], vbuf[N2], nvbuf[N2]);
+    head(t, red3[N2], kbuf(N2), vbuf(N2));
     if constexpr (NVC) tile_vnorms(t);
     if (active) {
 #pragma unroll
       for (int sub = 0; sub < 2; ++sub) {
         float q2s = 0.f;
-        const float sw = p2_sub<false, NVC>(kbuf[B] + sub * 32 * 256, vbuf[B] + sub * 32 * 256,
-                                       NVC ? 0.f : nvbuf[B][sub * 32 + l32], &q2s, off, qa, aa, nb2, cinit, c2x2,
+        const float sw = p2_sub<false, NVC>(kbuf(B) + sub * 32 * 256, vbuf(B) + sub * 32 * 256,
+                                       NVC ? 0.f : (sub ? nv_cur.y : nv_cur.x), &q2s, off, qa, aa, nb2, cinit, c2x2,
                                        0, rbase, P.w);
         if (h == 0) {
           red3[B][wave][sub * 32 + l32] = sw;
@@ -1249,15 +1264,15 @@ __global__ __launch_bounds__(NW * 64) void k_pass2(P2Args P, FixArgs F) {
   }
   for (; t < ntiles; ++t) {  // at most two clean tiles, then the masked tail
     const int b = t % 3, nb = (t + 2) % 3;
-    head(t, red3[nb], kbuf[nb], vbuf[nb], nvbuf[nb]);
+    head(t, red3[nb], kbuf(nb), vbuf(nb));
     if constexpr (NVC) tile_vnorms(t);
     if (active) {
 #pragma unroll
       for (int sub = 0; sub < 2; ++sub) {
         const int64_t tok = tok_rel0 + (int64_t)t * TT + sub * 32;
         float q2s = 0.f;
-        const float sw = p2_sub<true, NVC>(kbuf[b] + sub * 32 * 256, vbuf[b] + sub * 32 * 256,
-                                      NVC ? 0.f : nvbuf[b][sub * 32 + l32], &q2s, off, qa, aa, nb2, cinit, c2x2,
+        const float sw = p2_sub<true, NVC>(kbuf(b) + sub * 32 * 256, vbuf(b) + sub * 32 * 256,
+                                      NVC ? 0.f : (sub ? nv_cur.y : nv_cur.x), &q2s, off, qa, aa, nb2, cinit, c2x2,
                                       tok, rbase, P.w);
         if (h == 0) {
           red3[b][wave][sub * 32 + l32] = sw;
@@ -1266,6 +1281,7 @@ __global__ __launch_bounds__(NW * 64) void k_pass2(P2Args P, FixArgs F) {
       }
     }
   }
+  wait_vmcnt<0>();  // the zero-range loads of the last heads land before the LDS goes away
   __syncthreads();
   if (ntiles >= 1) combine(ntiles - 1, red3[(ntiles - 1) % 3]);
 }
