@@ -29,7 +29,7 @@ namespace dropkv {
 namespace {
 
 constexpr int kT = 512;    // threads per workgroup
-constexpr int kCT = 1024;  // tokens per workgroup
+constexpr int kCT = 4096;  // tokens per workgroup
 constexpr int kPerT = kCT / kT;
 constexpr int kBatch = 8;  // copy units in flight per thread and tensor
 static_assert(kCT % kT == 0 && kCT % 32 == 0 && kPerT <= 32 && 32 % kPerT == 0, "token blocking");

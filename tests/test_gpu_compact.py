@@ -1,7 +1,7 @@
 """Cache compaction on the GPU (dropkv_compact) against the oracle, bit for bit.
 
 Covers the three copy widths (16-, 4- and 2-byte units, chosen from the row
-size and the pointers' alignment), ragged token counts around the 1024-token
+size and the pointers' alignment), ragged token counts around the 4096-token
 block, empty and full eviction lists, invalid lists (status bit, and no write
 outside the outputs: guard rows around them stay untouched), and the
 score -> compact pipeline on a full-size layer.
@@ -91,7 +91,7 @@ def _run(k, v, ev, misalign=False):
 
 
 @pytest.mark.parametrize("dtype,d", [("bf16", 128), ("bf16", 7), ("f32", 3), ("f32", 64), ("bf16", 256)])
-@pytest.mark.parametrize("n", [1, 5, 1023, 1024, 1025, 3000])
+@pytest.mark.parametrize("n", [1, 5, 1025, 3000, 4095, 4096, 4097, 9000])
 def test_compact_matches_oracle(dtype, d, n):
     rng = np.random.default_rng(n * 31 + d)
     Hkv = 3
