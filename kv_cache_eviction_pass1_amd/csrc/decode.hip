@@ -962,7 +962,6 @@ __global__ __launch_bounds__(256) void k_dec_contrib(ContribArgs A) {
 // ---------------------------------------------------------------------------- single-pass step
 
 typedef __attribute__((address_space(3))) void lds_void;
-typedef __attribute__((address_space(1))) const void gbl_cvoid;
 
 constexpr int kTileTok = 64;                    // tokens per LDS tile
 constexpr int kTileBytes = kTileTok * HD * 2;   // 16 KiB per tensor
@@ -984,20 +983,23 @@ __device__ __forceinline__ void wait_vmcnt() {
 // waited for with wait_vmcnt first).
 __device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
 
-// Direct-to-LDS loads of token rows [tok0, tok0 + 64) of one head (rows at or
-// past n repeat row n - 1; consumers mask them): wave instruction i = wave + 4 j
-// fills tile bytes 1024 i .. +1023, lane l the 16-byte chunk (l % 16) of row
-// 4 i + l / 16 with the row's logical chunk (l % 16) ^ tswz(row).
+// Direct-to-LDS loads of token rows [tok0, tok0 + 64) of one head (tok0 < n):
+// wave instruction i = wave + 4 j fills tile bytes 1024 i .. +1023, lane l the
+// 16-byte chunk (l % 16) of row 4 i + l / 16 with the row's logical chunk
+// (l % 16) ^ tswz(row). The descriptor covers the rows before n only, so rows
+// at or past n arrive as zeros (the consumers mask them; zero keeps 0 * V
+// finite); base and range are scalar, a lane's address is its 32-bit offset
+// inside the tile.
 __device__ __forceinline__ void dec_issue_tile(const uint16_t* head, int64_t tok0, int64_t n, char* lds, int wave,
                                                int lane) {
+  const int left = (int)(n - tok0);  // n < 2^31
+  const __amdgpu_buffer_rsrc_t r = raw_rsrc(head + tok0 * HD, (left < kTileTok ? left : kTileTok) * (HD * 2));
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
     const int inst = wave + 4 * j;
     const int row = inst * 4 + (lane >> 4);
-    const int c = (lane & 15) ^ tswz(row);
-    int64_t tok = tok0 + row;
-    if (tok >= n) tok = n - 1;
-    __builtin_amdgcn_global_load_lds((gbl_cvoid*)(head + tok * HD + c * 8), (lds_void*)(lds + inst * 1024), 16, 0, 0);
+    const uint32_t off = (uint32_t)(row * (HD * 2) + (((lane & 15) ^ tswz(row)) << 4));
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)(lds + inst * 1024), 16, off, 0, 0, 0);
   }
 }
 
@@ -1137,16 +1139,8 @@ __global__ __launch_bounds__(512) void k_dec_fused8(FusedArgs F) {
   const double invG = 1.0 / (double)F.c.G;
   // tile loads, statistics waves only: per tensor 16 wave loads of 1 KiB, wave 4 + s issues s, s + 4, s + 8, s + 12
   auto issue = [&](int64_t tok0, char* kd, char* vd) {
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int inst = swave + 4 * j;
-      const int row = inst * 4 + (lane >> 4);
-      const int c = (lane & 15) ^ tswz(row);
-      int64_t tok = tok0 + row;
-      if (tok >= n) tok = n - 1;
-      __builtin_amdgcn_global_load_lds((gbl_cvoid*)(kh + tok * HD + c * 8), (lds_void*)(kd + inst * 1024), 16, 0, 0);
-      __builtin_amdgcn_global_load_lds((gbl_cvoid*)(vh + tok * HD + c * 8), (lds_void*)(vd + inst * 1024), 16, 0, 0);
-    }
+    dec_issue_tile(kh, tok0, n, kd, swave, lane);
+    dec_issue_tile(vh, tok0, n, vd, swave, lane);
   };
   if (stats_wave)
     for (int t = 0; t < NB - 1 && t < ntiles; ++t) issue(t0 + (int64_t)t * kTileTok, kbuf[t], vbuf[t]);

@@ -35,6 +35,14 @@ constexpr float kSingularRest = 5.9604644775390625e-08f;  // 2^-24
 
 constexpr float kLog2e = 1.4426950408889634f;
 
+// Buffer descriptor of `bytes` bytes at p (a raw buffer: stride 0, 32-bit
+// data format). Loads past `bytes` (the scalar offset included) return
+// zeros, and a direct-to-LDS load writes those zeros: a tile read through a
+// descriptor that covers only its valid rows needs no clamping.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t raw_rsrc(const void* p, int bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, bytes, 0x00020000);
+}
+
 // Per-window-row statistics, row index r = h * window + i (query head h, window row i).
 struct RowStats {
   float* m;         // largest logit x_max = max_j q.k_j / sqrt(d)  (natural units)

@@ -52,7 +52,6 @@ constexpr int FXC = 8;                   // token chunks of the fix-up pass
 constexpr int FXSTRIDE = HD + 2;         // floats per fix-up partial (sp, ps, D[128])
 
 typedef __attribute__((address_space(3))) void lds_void;
-typedef __attribute__((address_space(1))) const void gbl_cvoid;
 
 // Chunk permutation of token row t: a bijection on t mod 16 (16 consecutive
 // rows read with ds_read_b128 hit 16 distinct 16-byte bank groups) whose top
@@ -136,13 +135,6 @@ __device__ __forceinline__ DmaOff<NW> dma_offsets(int wave, int lane) {
 #pragma unroll
   for (int i = 0; i < DmaOff<NW>::kN; ++i) o.g[i] = dma_offset(wave + i * NW, lane);
   return o;
-}
-
-// Buffer descriptor of `bytes` bytes at p (a raw buffer: stride 0, 32-bit
-// data format); loads past `bytes` return zeros, and a direct-to-LDS load
-// writes those zeros.
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t raw_rsrc(const void* p, int bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, bytes, 0x00020000);
 }
 
 // Direct-to-LDS loads of the 64-token tile of one tensor that starts at
