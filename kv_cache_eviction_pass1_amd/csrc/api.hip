@@ -326,7 +326,7 @@ Workspace carve_workspace(void* base, const Shape& s, bool mfma) {
     ws.rs.na = (float*)take(sizeof(float) * rows);
     ws.rs.bias = (float*)take(sizeof(float) * rows);
     ws.nchunks = mfma_chunks(s);
-    ws.part = (float*)take(sizeof(float) * (size_t)ws.nchunks * rows * (size_t)(s.d + 4));
+    ws.part = (uint32_t*)take(sizeof(uint32_t) * (size_t)ws.nchunks * rows * (size_t)(s.d / 2 + 4));
     ws.extra = take(mfma_extra_bytes(s));
   }
   ws.bytes = off;

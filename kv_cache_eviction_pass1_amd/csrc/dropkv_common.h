@@ -62,7 +62,7 @@ struct Workspace {
   int32_t* status;  // OR of kStatus* bits
   float* S;         // [Hkv][n] GQA-mean raw scores
   RowStats rs;
-  float* part;      // pass-1 partials (MFMA path)
+  uint32_t* part;   // pass-1 partials (MFMA path): A in bf16, then m, l, best, mref
   void* extra;      // further MFMA-path buffers (see mfma_extra_bytes)
   void* sel;        // select-stage scratch (see select_scratch_bytes)
   int32_t* flagcount;  // [Hkv] rows per KV head whose argmax term comes from the fix-up

@@ -8,8 +8,8 @@
 //          K/V tiles through LDS. X^T = K Q^T and O^T += V^T P^T run on
 //          v_mfma_f32_32x32x16_bf16; the softmax is online (running max m,
 //          sum l = sum 2^{(x-m) c}) in fp32, so the w x n attention matrix is
-//          never stored. Writes per-chunk partials (m, l, A, tile of the max)
-//          and ||v_j||^2.
+//          never stored. Writes per-chunk partials (m, l, A rounded to bf16,
+//          tile of the max) and ||v_j||^2.
 //  merge   (k_merge)  combines the chunk partials per window row: m, l, a,
 //          a in bf16, ||a_bf16||^2, the exponent bias m c + log2 l so that
 //          p_j = 2^{x_j c - bias}, and flags rows with l < 2 (R < 1, i.e.
@@ -47,7 +47,7 @@ constexpr int HD = 128;                  // head dim of this path
 constexpr int TT = 64;                   // tokens per LDS tile
 constexpr int TILE_BYTES = TT * HD * 2;  // 16 KiB per tensor per tile
 constexpr int MAXW = 8;                  // waves per workgroup (row blocks of 32)
-constexpr int PSTRIDE = HD + 4;          // floats per pass-1 partial (A[128], m, l, best, mref)
+constexpr int PSTRIDE = HD / 2 + 4;      // 32-bit words per pass-1 partial (A[128] in bf16, m, l, best, mref)
 constexpr int FXC = 8;                   // token chunks of the fix-up pass
 constexpr int FXSTRIDE = HD + 2;         // floats per fix-up partial (sp, ps, D[128])
 
@@ -181,7 +181,7 @@ struct P1Args {
   int64_t ld;  // token rows per KV head in k and v (>= n)
   int w, Rg, nw, tiles_per_chunk, Hkv;
   float c2;          // log2(e) / sqrt(d)
-  float* part;       // [chunk][Hkv*Rg][PSTRIDE]
+  uint32_t* part;    // [chunk][Hkv*Rg][PSTRIDE]
   float* nv;         // [Hkv][n]
   int32_t* status;   // cleared here (read by later kernels only)
   int32_t* flagcount;  // [Hkv], cleared here
@@ -528,20 +528,25 @@ __global__ __launch_bounds__(NW * 64) void k_pass1(P1Args A) {
   p1_row_max(st);
   if (!row_ok) return;
   DKV_CHECK(chunk < (int)gridDim.x && g < A.Hkv && row < A.Rg && t1 <= A.n, A.status);
-  float* pr = A.part + ((size_t)chunk * A.Hkv * A.Rg + (size_t)g * A.Rg + row) * PSTRIDE;
-  // lane holds O^T rows d = 32db + 8i + 4h + (0..3) of this row's column
+  uint32_t* pr = A.part + ((size_t)chunk * A.Hkv * A.Rg + (size_t)g * A.Rg + row) * PSTRIDE;
+  // lane holds O^T rows d = 32db + 8i + 4h + (0..3) of this row's column; A
+  // is stored rounded to bf16 (nearest even), two dims per word: the merge
+  // rounds a to bf16 for pass 2 anyway, and the partials are read once
+  typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 #pragma unroll
   for (int db = 0; db < 4; ++db)
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      float4 o = {O[db][4 * i], O[db][4 * i + 1], O[db][4 * i + 2], O[db][4 * i + 3]};
-      *(float4*)(pr + 32 * db + 8 * i + 4 * h) = o;
+      const bf16x2 lo = {(__bf16)O[db][4 * i], (__bf16)O[db][4 * i + 1]};
+      const bf16x2 hi = {(__bf16)O[db][4 * i + 2], (__bf16)O[db][4 * i + 3]};
+      *(uint2*)(pr + 16 * db + 4 * i + 2 * h) =
+          make_uint2(__builtin_bit_cast(uint32_t, lo), __builtin_bit_cast(uint32_t, hi));
     }
   if (h == 0) {
-    pr[HD] = st.m_true;
-    pr[HD + 1] = l_tot;
-    pr[HD + 2] = __int_as_float(st.best);
-    pr[HD + 3] = st.mref;
+    pr[HD / 2] = __float_as_uint(st.m_true);
+    pr[HD / 2 + 1] = __float_as_uint(l_tot);
+    pr[HD / 2 + 2] = (uint32_t)st.best;
+    pr[HD / 2 + 3] = __float_as_uint(st.mref);
   }
 }
 
@@ -550,7 +555,7 @@ __global__ __launch_bounds__(NW * 64) void k_pass1(P1Args A) {
 struct MergeArgs {
   const uint16_t* q;
   const uint16_t* k;
-  const float* part;
+  const uint32_t* part;
   int64_t n;
   int64_t ld;  // token rows per KV head in k (>= n)
   int w, Rg, Hkv, nchunks;
@@ -568,21 +573,21 @@ __global__ __launch_bounds__(256) void k_merge(MergeArgs M) {
   if (row >= rows) return;
   const int g = (int)(row / M.Rg), r = (int)(row % M.Rg);
   const size_t cstride = (size_t)rows * PSTRIDE;
-  const float* prow = M.part + (size_t)row * PSTRIDE;
+  const uint32_t* prow = M.part + (size_t)row * PSTRIDE;
   // lane c (< 64) holds chunk c's (m, l, best); more chunks fold in 64 at a time
   float mx = -INFINITY;
   int bt = -1;
   for (int c0 = 0; c0 < M.nchunks; c0 += 64) {
     const int c = c0 + lane;
-    const float mc = c < M.nchunks ? prow[c * cstride + HD] : -INFINITY;
+    const float mc = c < M.nchunks ? __uint_as_float(prow[c * cstride + HD / 2]) : -INFINITY;
     float wm = mc;
 #pragma unroll
     for (int o = 32; o > 0; o >>= 1) wm = fmaxf(wm, __shfl_xor(wm, o, 64));
     if (wm > mx) {
       const unsigned long long hit = __builtin_amdgcn_ballot_w64(mc == wm);
       const int first = __ffsll((long long)hit) - 1;  // lowest chunk attaining the max
-      const float bf = c < M.nchunks ? prow[c * cstride + HD + 2] : 0.f;
-      bt = __float_as_int(__shfl(bf, first, 64));
+      const int bf = c < M.nchunks ? (int)prow[c * cstride + HD / 2 + 2] : 0;
+      bt = __shfl(bf, first, 64);
       mx = wm;
     }
   }
@@ -590,8 +595,8 @@ __global__ __launch_bounds__(256) void k_merge(MergeArgs M) {
   for (int c0 = 0; c0 < M.nchunks; c0 += 64) {
     const int c = c0 + lane;
     // chunk c holds l and A relative to its own reference exponent mref
-    const float rc = c < M.nchunks ? prow[c * cstride + HD + 3] : -INFINITY;
-    const float lc = c < M.nchunks ? prow[c * cstride + HD + 1] : 0.f;
+    const float rc = c < M.nchunks ? __uint_as_float(prow[c * cstride + HD / 2 + 3]) : -INFINITY;
+    const float lc = c < M.nchunks ? __uint_as_float(prow[c * cstride + HD / 2 + 1]) : 0.f;
     const float sc = (rc == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(rc - mx * M.c2);
     float lw = lc * sc;
 #pragma unroll
@@ -600,24 +605,24 @@ __global__ __launch_bounds__(256) void k_merge(MergeArgs M) {
     const int cn = (M.nchunks - c0) < 64 ? (M.nchunks - c0) : 64;
     int cc = 0;
     for (; cc + 16 <= cn; cc += 16) {  // sixteen chunk rows in flight
-      float2 av[16];
+      uint32_t av[16];
       float sv[16];
 #pragma unroll
       for (int u = 0; u < 16; ++u) {
-        av[u] = *(const float2*)(prow + (size_t)(c0 + cc + u) * cstride + 2 * lane);
+        av[u] = prow[(size_t)(c0 + cc + u) * cstride + lane];
         sv[u] = __shfl(sc, cc + u, 64);
       }
 #pragma unroll
       for (int u = 0; u < 16; ++u) {
-        a0 = fmaf(av[u].x, sv[u], a0);
-        a1 = fmaf(av[u].y, sv[u], a1);
+        a0 = fmaf(__uint_as_float(av[u] << 16), sv[u], a0);
+        a1 = fmaf(__uint_as_float(av[u] & 0xffff0000u), sv[u], a1);
       }
     }
     for (; cc < cn; ++cc) {
-      const float2 av = *(const float2*)(prow + (size_t)(c0 + cc) * cstride + 2 * lane);
+      const uint32_t av = prow[(size_t)(c0 + cc) * cstride + lane];
       const float sv = __shfl(sc, cc, 64);
-      a0 = fmaf(av.x, sv, a0);
-      a1 = fmaf(av.y, sv, a1);
+      a0 = fmaf(__uint_as_float(av << 16), sv, a0);
+      a1 = fmaf(__uint_as_float(av & 0xffff0000u), sv, a1);
     }
   }
   const float inv_l = 1.0f / l;
