@@ -1,10 +1,13 @@
 """Cache compaction on the GPU (dropkv_compact) against the oracle, bit for bit.
 
 Covers the three copy widths (16-, 4- and 2-byte units, chosen from the row
-size and the pointers' alignment), ragged token counts around the 4096-token
-block, empty and full eviction lists, invalid lists (status bit, and no write
-outside the outputs: guard rows around them stay untouched), and the
-score -> compact pipeline on a full-size layer.
+size and the pointers' alignment), ragged row counts around the 128-row
+output block, empty and full eviction lists, kept sets of every shape (spread
+out, in runs, all at the front, all at the back, at both ends around one long
+evicted run: the case whose block span holds more list entries than the
+kernel stages in LDS), invalid lists (status bit, and no write outside the
+outputs: guard rows around them stay untouched), and the score -> compact
+pipeline on a full-size layer.
 """
 
 import numpy as np
@@ -65,6 +68,13 @@ def _evict_lists(rng, Hkv, n, ne, kind):
             if e.size < ne:
                 rest = np.setdiff1d(np.arange(n), e)
                 e = np.sort(np.concatenate([e, rng.choice(rest, size=ne - e.size, replace=False)]))
+        elif kind == "front":  # keep the first tokens
+            e = np.arange(n - ne, n)
+        elif kind == "back":  # keep the last tokens
+            e = np.arange(0, ne)
+        elif kind == "ends":  # keep both ends, one evicted run between them
+            s0 = (n - ne) // 2
+            e = np.arange(s0, s0 + ne)
         else:  # every other token, from g
             e = np.arange(g % 2, n, 2)[:ne]
             if e.size < ne:
@@ -98,7 +108,8 @@ def test_compact_matches_oracle(dtype, d, n):
     tdt = torch.bfloat16 if dtype == "bf16" else torch.float32
     k = torch.randn(Hkv, n, d).to(tdt).cuda()
     v = torch.randn(Hkv, n, d).to(tdt).cuda()
-    for ne, kind in ((0, "random"), (n, "random"), (n // 2, "random"), (n - n // 7, "runs"), (n // 3, "alt")):
+    for ne, kind in ((0, "random"), (n, "random"), (n // 2, "random"), (n - n // 7, "runs"), (n // 3, "alt"),
+                     (n - n // 7, "front"), (n // 2, "back"), (n - n // 7, "ends")):
         ev = _evict_lists(rng, Hkv, n, ne, kind)
         print(f"[compact] {dtype} d={d} n={n} evict={ne} {kind}", flush=True)
         ok, ov, st, bufs = _run(k, v, ev)
