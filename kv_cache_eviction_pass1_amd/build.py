@@ -38,6 +38,11 @@ DEVICE_FLAGS = [
     f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-munsafe-fp-atomics", "-Wall", "-Wno-unused-function",
+    # Every global atomic here is issued by one lane. The compiler's atomic
+    # optimizer would still rewrite a uniform-address atomic into a wave
+    # reduction that waits for all outstanding memory operations right after
+    # it (vmcnt(0)), draining the tile loads in flight behind a tile claim.
+    "-mllvm", "-amdgpu-atomic-optimizer-strategy=None",
 ]
 # host code of the C ABI under AddressSanitizer; device code is unchanged
 ASAN_HOST_FLAGS = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fno-omit-frame-pointer",

@@ -118,6 +118,10 @@ hipError_t launch_select(const float* S, int64_t n, int32_t w, int32_t Hkv, int3
 size_t select_scratch_bytes(int64_t n, int32_t Hkv);
 // 32-bit words at the start of the select scratch that must be zero before a call.
 size_t select_zero_words(int32_t Hkv);
+// Spare words of that zeroed block, free for other kernels of the call:
+// select_spare_words(scratch, g)[i] for KV head g and i < kSelSpareWords.
+constexpr int kSelSpareWords = 15;
+uint32_t* select_spare_words(void* sel_scratch, int32_t g);
 // Stage timing. Stage i runs from ev[i][0] to ev[i][1]. Kernels launched
 // through stage_launch take these from their own dispatch (the begin time of
 // a stage's first kernel, the end time of its last), so timing adds no packet

@@ -801,6 +801,14 @@ struct P2Args {
   const int32_t* flagcount;
   float* S;  // [rg][Hkv][n]
   int32_t* status;
+  // Tile schedule of the fast path. ctr null: workgroup `chunk` takes tiles
+  // [chunk * tiles_per_chunk, ...) of its head. Otherwise it takes its static
+  // share [chunk * stat_tiles, (chunk + 1) * stat_tiles) and then claims
+  // tiles of the pool [pool0, tiles) one at a time from the counter
+  // ctr[g * ctr_stride + rg] (zero before the launch), so workgroups on
+  // faster CUs take more of them. The flagged path always takes static chunks.
+  uint32_t* ctr;
+  int ctr_stride, stat_tiles, pool0, tiles;
 };
 
 __device__ __forceinline__ void p2_tile(const P2Args& P, const char* kb, const char* vb,
@@ -1059,13 +1067,6 @@ __device__ __forceinline__ float p2_sub(const char* kt, const char* vt, float nv
 // sum r^2 are reduced separately and ||v_j||^2 is folded in per token.
 template <int NW, bool NVC>
 __global__ __launch_bounds__(NW * 64) void k_pass2(P2Args P, FixArgs F) {
-  if (NW >= 2 && blockIdx.x >= gridDim.x - (NW >= 2 ? FXC : 0)) {
-    // the argmax fix-up (independent of pass 2) runs as FXC extra workgroups per head
-    if constexpr (NW >= 2) {
-      if (blockIdx.y == 0) fixup_chunk<NW * 64>(F, blockIdx.x - (gridDim.x - FXC), blockIdx.z);
-    }
-    return;
-  }
   // The three K and three V tile buffers are separate variables, not one
   // [3][TILE_BYTES] array each: with a compile-time buffer index (the clean
   // loop below is unrolled over the buffers) the compiler can then tell that
@@ -1123,9 +1124,14 @@ __global__ __launch_bounds__(NW * 64) void k_pass2(P2Args P, FixArgs F) {
     }
   }
 
+  // the fast path's first tile: its static share starts at chunk * stat_tiles
+  const bool dyn = P.ctr != nullptr && !flagged;
+  const int gbase = dyn ? chunk * P.stat_tiles : chunk * P.tiles_per_chunk;
   if (ntiles > 0) {
-    issue_tile<NW>(kh, t0, tile_rows(0, nfull, t0, t1), kbuf(0), wave, lane, doff);
-    issue_tile<NW>(vh, t0, tile_rows(0, nfull, t0, t1), vbuf(0), wave, lane, doff);
+    const int64_t f0 = (int64_t)gbase * TT;
+    const int r0 = dyn ? (int)(P.n - f0 < TT ? P.n - f0 : TT) : tile_rows(0, nfull, t0, t1);
+    issue_tile<NW>(kh, f0, r0, kbuf(0), wave, lane, doff);
+    issue_tile<NW>(vh, f0, r0, vbuf(0), wave, lane, doff);
   }
 
   if (flagged) {
@@ -1156,41 +1162,72 @@ __global__ __launch_bounds__(NW * 64) void k_pass2(P2Args P, FixArgs F) {
       __syncthreads();
       p2_combine<NVC>(P, red, nwa, t0 + (int64_t)it * TT, t1, g, vbuf(b));
     }
+    // the argmax fix-up of this head's flagged rows (independent of pass 2):
+    // fix-up chunks chunk, chunk + gridDim.x, ... of row group 0's workgroups
+    if constexpr (NW >= 2) {
+      if (rg == 0) {
+        __syncthreads();
+        for (int c = chunk; c < FXC; c += gridDim.x) fixup_chunk<NW * 64>(F, c, g);
+      }
+    }
     return;
   }
 
-  // the fast path's vector-memory operations per tile are, in issue order:
-  // wave 0's score store, the next tile's ||v||^2 loads and the K/V loads of
-  // the tile after it, so `vmcnt <= one tile's K/V loads` at the top of tile t
-  // means tile t's K/V and ||v||^2 have landed
+  // The fast path's vector-memory operations per tile are, in issue order:
+  // wave 0's score store, the next tile's ||v||^2 loads, (wave 0, pooled
+  // tiles) the claim of a later tile and the K/V loads of the tile after
+  // next, so `vmcnt <= one tile's K/V loads` at the top of tile t means tile
+  // t's K/V and ||v||^2 and the claim issued one tile earlier have landed.
+  //
+  // The workgroup's tiles are its static share [gbase, static_end), then
+  // tiles claimed from the head's pool. The claim for a tile goes out at the
+  // top of the tile three places before it and reaches every wave through
+  // LDS at the top of the next tile, when that tile's loads are issued.
+  // Claims only grow, so a workgroup's tiles ascend; once a claim runs past
+  // the pool, its sequence ends. gp / g0 / g1: global tiles of local tiles
+  // t - 1, t, t + 1 (-1: none) before the top of tile t.
+  __shared__ int claim_slot[2];  // written at the top of tile t into slot t % 2: a wave still
+                                 // reading slot t % 2 blocks the next write there at barrier t + 1
+  const int static_end = gbase + (dyn ? P.stat_tiles : ntiles);
+  uint32_t* const ctrp = dyn ? P.ctr + (size_t)g * P.ctr_stride + rg : nullptr;
+  uint32_t pend = 0;  // wave 0, lane 0: the claim in flight
+  int gp = -1, g0 = ntiles > 0 ? gbase : -1, g1 = (gbase + 1 < static_end) ? gbase + 1 : -1;
+  // rows of global tile gt (0 for none: zero-range loads)
+  const int last_tile = P.tiles - 1;
+  const int last_rows = (int)(P.n - (int64_t)last_tile * TT);
+  auto trows = [&](int gt) -> int { return gt < 0 ? 0 : (gt == last_tile ? last_rows : TT); };
+  // local tile t + 3 is a pooled tile whose claim goes out at the top of t
+  // (g2: the global tile of local t + 2)
+  auto claims_next = [&](int g2) { return dyn && g2 >= 0 && g2 + 1 >= static_end; };
   // ||v_j||^2 of this lane's tokens of the current tile and of the next one
   // (the latter loaded one tile ahead; not in NVC mode)
   float2 nv_cur = make_float2(0.f, 0.f), nv_next = make_float2(0.f, 0.f);
-  if (!NVC) nv_next = load_nv_pair(nvg, t0, tile_rows_or0(0, ntiles, nfull, t0, t1), l32);
-  issue_tile<NW>(kh, t0 + TT, tile_rows_or0(1, ntiles, nfull, t0, t1), kbuf(1), wave, lane, doff);
-  issue_tile<NW>(vh, t0 + TT, tile_rows_or0(1, ntiles, nfull, t0, t1), vbuf(1), wave, lane, doff);
+  if (!NVC) nv_next = load_nv_pair(nvg, (int64_t)(g0 < 0 ? 0 : g0) * TT, trows(g0), l32);
+  issue_tile<NW>(kh, (int64_t)(g1 < 0 ? 0 : g1) * TT, trows(g1), kbuf(1), wave, lane, doff);
+  issue_tile<NW>(vh, (int64_t)(g1 < 0 ? 0 : g1) * TT, trows(g1), vbuf(1), wave, lane, doff);
   const float c2x2 = 2.0f * P.c2;
   const LdsOff off = lds_offsets(lane);
   float nb2[16];
 #pragma unroll
   for (int vv = 0; vv < 16; ++vv) nb2[vv] = -2.0f * bias[vv];
   const int rbase = rb * 32 + 4 * h;  // first row of this lane's 16 (masked tiles only)
-  const int nclean = clean_tiles(P.n, P.w, t0, ntiles);
+  // global tiles [0, ncg) end at or before the first window position: no row needs the mask
+  const int ncg = clean_tiles(P.n, P.w, 0, P.tiles);
   // scores of tile t-1 (every wave wrote its partial before the barrier at tile t)
   static_assert(TT == 64, "one wave combines a tile");
-  auto combine = [&](int tl, const float (*red)[TT]) {
+  auto combine = [&](int gt, const float (*red)[TT], int lt) {
     if (wave == 0) {  // wave-uniform: the other waves skip it with a scalar branch
-      const int64_t tok = t0 + (int64_t)tl * TT + threadIdx.x;
-      if (tok < t1) {
+      const int64_t tok = (int64_t)gt * TT + threadIdx.x;
+      if (tok < P.n) {
         float sacc = 0.f;
         for (int wv = 0; wv < nwa; ++wv) sacc += red[wv][threadIdx.x];
         if constexpr (NVC) {  // sacc = sum r^2 C; ||v_j||^2 and sum r^2 from the tile's buffers
-          const int b = tl % 3;
+          const int b = lt % 3;
           float s2 = 0.f;
           for (int wv = 0; wv < nwa; ++wv) s2 += red3b[b][wv][threadIdx.x];
           sacc = fmaf(nvbuf[b][threadIdx.x], s2, -2.0f * sacc);
         }
-        DKV_CHECK(tok < P.n, P.status);
+        DKV_CHECK(tok < P.n && gt < P.tiles, P.status);
         Sout[tok] = fmaxf(sacc, 0.0f) * P.invG;
       }
     }
@@ -1218,26 +1255,39 @@ __global__ __launch_bounds__(NW * 64) void k_pass2(P2Args P, FixArgs F) {
       if (li == 0) nvbuf[t % 3][tk] = a;
     }
   };
-  // Every head issues the same loads (past the last tile with zero range, into
-  // a buffer nobody reads any more), so the wait at its top is the same too.
-  auto head = [&](int t, const float (*red_prev)[TT], char* kn, char* vn) {
-    const int64_t tb = t0 + (int64_t)t * TT;
+  // Top of local tile t: every head issues the same loads (past the last tile
+  // with zero range, into a buffer nobody reads any more), so the wait at its
+  // top is the same too. Returns the global tile of local t + 2.
+  auto head = [&](int t, const float (*red_prev)[TT], char* kn, char* vn) -> int {
     wait_vmcnt<kDmaPerTile>();
+    const bool pooled2 = claims_next(g1);  // local t + 2 was claimed at the top of t - 1
+    if (pooled2 && wave == 0 && lane == 0) {
+      const uint32_t gt = (uint32_t)P.pool0 + pend;
+      claim_slot[t & 1] = gt < (uint32_t)P.tiles ? (int)gt : -1;
+    }
     lds_barrier();  // tile t in LDS for every wave; tile t-1's buffer is free
-    if (t >= 1) combine(t - 1, red_prev);
+    int g2 = -1;
+    if (pooled2) g2 = __builtin_amdgcn_readfirstlane(claim_slot[t & 1]);
+    else if (g1 >= 0 && g1 + 1 < static_end) g2 = g1 + 1;
+    if (gp >= 0) combine(gp, red_prev, t - 1);
     if constexpr (!NVC) {
       nv_cur = nv_next;
-      nv_next = load_nv_pair(nvg, tb + TT, tile_rows_or0(t + 1, ntiles, nfull, t0, t1), l32);
+      nv_next = load_nv_pair(nvg, (int64_t)(g1 < 0 ? 0 : g1) * TT, trows(g1), l32);
     }
-    issue_tile<NW>(kh, tb + 2 * TT, tile_rows_or0(t + 2, ntiles, nfull, t0, t1), kn, wave, lane, doff);
-    issue_tile<NW>(vh, tb + 2 * TT, tile_rows_or0(t + 2, ntiles, nfull, t0, t1), vn, wave, lane, doff);
+    if (claims_next(g2) && wave == 0 && lane == 0) pend = atomicAdd(ctrp, 1u);
+    issue_tile<NW>(kh, (int64_t)(g2 < 0 ? 0 : g2) * TT, trows(g2), kn, wave, lane, doff);
+    issue_tile<NW>(vh, (int64_t)(g2 < 0 ? 0 : g2) * TT, trows(g2), vn, wave, lane, doff);
+    return g2;
   };
-  // token offset of this lane's column relative to n - w, for the causal mask
-  const int64_t tok_rel0 = t0 + l32 - (P.n - P.w);
+  auto advance = [&](int g2) {
+    gp = g0;
+    g0 = g1;
+    g1 = g2;
+  };
   auto clean = [&](auto bc, int t) {
     constexpr int B = decltype(bc)::value;
     constexpr int N2 = (B + 2) % 3;
-    head(t, red3[N2], kbuf(N2), vbuf(N2));
+    const int g2 = head(t, red3[N2], kbuf(N2), vbuf(N2));
     if constexpr (NVC) tile_vnorms(t);
     if (active) {
 #pragma unroll
@@ -1252,21 +1302,26 @@ __global__ __launch_bounds__(NW * 64) void k_pass2(P2Args P, FixArgs F) {
         }
       }
     }
+    advance(g2);
   };
+  auto is_clean = [&]() { return g0 >= 0 && g0 < ncg; };
   int t = 0;
-  for (; t + 3 <= nclean; t += 3) {
-    clean(IntC<0>{}, t);
-    clean(IntC<1>{}, t + 1);
-    clean(IntC<2>{}, t + 2);
+  for (;;) {
+    if (!is_clean()) break;
+    clean(IntC<0>{}, t++);
+    if (!is_clean()) break;
+    clean(IntC<1>{}, t++);
+    if (!is_clean()) break;
+    clean(IntC<2>{}, t++);
   }
-  for (; t < ntiles; ++t) {  // at most two clean tiles, then the masked tail
+  for (; g0 >= 0; ++t) {  // the masked tail: tiles that reach into the window
     const int b = t % 3, nb = (t + 2) % 3;
-    head(t, red3[nb], kbuf(nb), vbuf(nb));
+    const int g2 = head(t, red3[nb], kbuf(nb), vbuf(nb));
     if constexpr (NVC) tile_vnorms(t);
     if (active) {
 #pragma unroll
       for (int sub = 0; sub < 2; ++sub) {
-        const int64_t tok = tok_rel0 + (int64_t)t * TT + sub * 32;
+        const int64_t tok = (int64_t)g0 * TT + sub * 32 + l32 - (P.n - P.w);
         float q2s = 0.f;
         const float sw = p2_sub<true, NVC>(kbuf(b) + sub * 32 * 256, vbuf(b) + sub * 32 * 256,
                                       NVC ? 0.f : (sub ? nv_cur.y : nv_cur.x), &q2s, off, qa, aa, nb2, cinit, c2x2,
@@ -1277,10 +1332,11 @@ __global__ __launch_bounds__(NW * 64) void k_pass2(P2Args P, FixArgs F) {
         }
       }
     }
+    advance(g2);
   }
   wait_vmcnt<0>();  // the zero-range loads of the last heads land before the LDS goes away
   __syncthreads();
-  if (ntiles >= 1) combine(ntiles - 1, red3[(ntiles - 1) % 3]);
+  if (gp >= 0) combine(gp, red3[(t - 1) % 3], t - 1);
 }
 
 // Sum of the row-group partial scores (only when a KV head has > 8 row blocks).
@@ -1296,6 +1352,7 @@ __global__ void k_sum_rowgroups(const float* __restrict__ Sp, float* __restrict_
 struct Plan {
   int Rg, RBt, nrg, nw, tiles, tpc1, nch1, tpc2, nch2;
   int nw2, nrg2;  // pass 2: waves per workgroup (1, 2 or 4; 64 rows each) and row groups
+  int stat2;      // pass 2: static tiles per workgroup of the pooled schedule (0: static chunks)
 };
 
 Plan make_plan(const Shape& s) {
@@ -1326,7 +1383,30 @@ Plan make_plan(const Shape& s) {
   if (p.nch2 < 1) p.nch2 = 1;
   p.tpc2 = (p.tiles + p.nch2 - 1) / p.nch2;
   p.nch2 = (p.tiles + p.tpc2 - 1) / p.tpc2;
+  // Pass 2 gives each workgroup three quarters of its even share and pools
+  // the rest: the clocks of the XCDs differ by several percent under this
+  // load, and with fixed chunks the slowest XCD sets the pass time. The
+  // pooled schedule needs >= 3 static tiles (its first claim goes out three
+  // tiles ahead) and one counter word per row group.
+  const int st = (p.tiles * 3 / 4) / p.nch2;
+  p.stat2 = (st >= 3 && p.nrg2 <= kSelSpareWords) ? st : 0;
   return p;
+}
+
+// The pooled schedule's fields of P2Args (counters in the select scratch's
+// spare words, zeroed before pass 2 by pass 1 or the init launch).
+void set_schedule(P2Args& a, const Plan& p, void* sel) {
+  a.tiles = p.tiles;
+  a.ctr = nullptr;
+  a.ctr_stride = 0;
+  a.stat_tiles = 0;
+  a.pool0 = 0;
+  if (p.stat2 > 0) {
+    a.ctr = select_spare_words(sel, 0);
+    a.ctr_stride = (int)(select_spare_words(sel, 1) - a.ctr);
+    a.stat_tiles = p.stat2;
+    a.pool0 = p.nch2 * p.stat2;
+  }
 }
 
 }  // namespace
@@ -1392,7 +1472,8 @@ hipError_t launch_mfma_path(const void* q, const void* k, const void* v, const S
   }
   P2Args a2{(const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v, s.n, s.w, p.Rg, p.nw2,
             p.tpc2, s.Hkv, c2, 1.0f / (float)s.G(), ws.rs, nv, flagcount, Spart, ws.status};
-  const dim3 grid2(p.nch2 + (p.nw2 >= 2 ? FXC : 0), p.nrg2, s.Hkv);
+  set_schedule(a2, p, ws.sel);
+  const dim3 grid2(p.nch2, p.nrg2, s.Hkv);
   switch (p.nw2) {
     case 8: e = stage_launch(se, "pass2", kStageOnly, k_pass2<8, false>, grid2, dim3(512), st, a2, af); break;
     case 4: e = stage_launch(se, "pass2", kStageOnly, k_pass2<4, false>, grid2, dim3(256), st, a2, af); break;
@@ -1468,7 +1549,8 @@ hipError_t launch_mfma_from_stats(const void* q, const void* k, const void* v, c
   if (p.nw2 < 2) k_fixup<<<dim3(FXC, s.Hkv), 256, 0, st>>>(af);
   P2Args a2{(const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v, s.n, s.w, p.Rg, p.nw2,
             p.tpc2, s.Hkv, c2, 1.0f / (float)s.G(), ws.rs, nullptr, flagcount, Spart, ws.status};
-  const dim3 grid2(p.nch2 + (p.nw2 >= 2 ? FXC : 0), p.nrg2, s.Hkv);
+  set_schedule(a2, p, ws.sel);
+  const dim3 grid2(p.nch2, p.nrg2, s.Hkv);
   switch (p.nw2) {
     case 8: k_pass2<8, true><<<grid2, 512, 0, st>>>(a2, af); break;
     case 4: k_pass2<4, true><<<grid2, 256, 0, st>>>(a2, af); break;

@@ -616,6 +616,12 @@ size_t select_scratch_bytes(int64_t n, int32_t Hkv) { return carve_sel(nullptr, 
 
 size_t select_zero_words(int32_t Hkv) { return (size_t)Hkv * kHistStride; }
 
+// the 15 words after each head's candidate count (kHistStride = bins + 16)
+static_assert(kHistStride - kBins1 - kBins2 - 1 >= kSelSpareWords, "spare words");
+uint32_t* select_spare_words(void* sel_scratch, int32_t g) {
+  return (uint32_t*)sel_scratch + (size_t)g * kHistStride + kBins1 + kBins2 + 1;
+}
+
 hipError_t launch_init(int32_t* status, int32_t* flagcount, void* sel_scratch, int32_t Hkv,
                        hipStream_t st) {
   // the histogram block sits first in the select scratch for every n

@@ -67,6 +67,13 @@ def test_from_stats_matches(n, w, Hq, Hkv):
     _compare(case, 7, (n - w) // 2, "shapes")
 
 
+def test_from_stats_pooled_tile_schedule():
+    """Scoring from statistics on a shape that takes pass 2's pooled schedule
+    (counters cleared by the init launch of this path)."""
+    case = synth.make_gaussian_case(32, 8, 128, 8229, 32, dtype="bf16", seeds=(8, 2, 29), sink=True, needles=16)
+    _compare(case, 7, 8229 - 411, "pooled schedule")
+
+
 def test_from_stats_row_groups():
     case = synth.make_gaussian_case(28, 4, 128, 3000, 64, dtype="bf16", seeds=(1, 2, 3), sink=True, needles=16)
     _compare(case, 7, 2500, "qwen row groups")

@@ -57,6 +57,16 @@ def test_mfma_tile_and_row_boundaries(n, w, Hq, Hkv):
     _compare(case, 7 if n > 16 else 3, ne, "bounds")
 
 
+@pytest.mark.parametrize("n,w,Hq,Hkv", [(8229, 32, 32, 8), (8292, 64, 28, 4), (65600, 32, 8, 1)])
+def test_mfma_pooled_tile_schedule(n, w, Hq, Hkv):
+    """Shapes long enough for pass 2's pooled schedule (static shares of three
+    quarters of the tiles, the rest claimed one tile at a time): a ragged last
+    tile and the masked window tiles sit in the pool; two row groups with
+    their own counters; one KV head over 256 workgroups."""
+    case = synth.make_gaussian_case(Hq, Hkv, 128, n, w, dtype="bf16", seeds=(n, w, Hq), sink=True, needles=16)
+    _compare(case, 7, n - n // 20, "pooled schedule")
+
+
 def test_mfma_row_groups_qwen_shape():
     """28 query heads over 4 KV heads with w = 64: 448 rows per KV head, two row groups."""
     case = synth.make_gaussian_case(28, 4, 128, 3000, 64, dtype="bf16", seeds=(42, 43, 44),
@@ -120,6 +130,19 @@ def test_mfma_flagged_rows_pool_widths(pool):
     gaps = [0.0, 2.0, 7.0, 8.0, 10.0, 13.0, 16.0, 20.0]
     case = _dominant_case(gaps, n=3000, seed=3)
     _compare(case, pool, 1500, f"flagged pool={pool}")
+
+
+@pytest.mark.parametrize("n", [300, 3000])
+def test_mfma_flagged_rows_wide_group(n):
+    """40 window rows per KV head (two row blocks): the argmax fix-up of the
+    flagged rows runs inside pass 2's workgroups, also when the head has fewer
+    tiles than fix-up chunks (n = 300: five workgroups cover eight chunks)."""
+    gaps = [0.0, 2.0, 7.0, 8.0, 10.0, 13.0, 16.0, 20.0] * 5
+    case = _dominant_case(gaps, n=n, w=20, G=2, seed=5)
+    ref = run_oracle(case, 3, 100)
+    rests = np.concatenate([st["rest"] for st in ref["stats"]])
+    assert rests.min() < 1e-5 and rests.max() > 1.0  # both kinds of rows present
+    _compare(case, 3, (n - 20) // 2, f"flagged wide n={n}")
 
 
 def test_mfma_singular_row_rejected():
