@@ -124,6 +124,22 @@ int dropkv_score_ex(int32_t dtype, const void* q, const void* k, const void* v, 
                     int64_t n_evict, float* out_scores, int64_t* out_evict_idx, void* workspace,
                     size_t workspace_bytes, int32_t* d_status, uint32_t flags, void* stream);
 
+/*
+ * dropkv_score_ex that also writes the kept token indices: out_keep_idx
+ * [Hkv][n - n_evict] int64 (device memory, caller-owned; may be NULL only
+ * when n_evict == n), per head the indices that out_evict_idx does not name
+ * (the protected window included), ascending. The select stage emits them
+ * alongside the evicted ones, for dropkv_compact_kept (write-up section
+ * 代码映射与边界: the caller drops the evicted tokens from its cache; a kept
+ * list is what a gather of the kept rows reads). Same limits, ownership,
+ * status word and asynchrony as dropkv_score_ex.
+ */
+int dropkv_score_keep_ex(int32_t dtype, const void* q, const void* k, const void* v, int64_t n,
+                         int32_t window, int32_t Hq, int32_t Hkv, int32_t d, int32_t pool_kernel,
+                         int64_t n_evict, float* out_scores, int64_t* out_evict_idx, int64_t* out_keep_idx,
+                         void* workspace, size_t workspace_bytes, int32_t* d_status, uint32_t flags,
+                         void* stream);
+
 /* Size of the static scratch array behind dropkv_score_noalloc, per GPU. */
 #define DROPKV_NOALLOC_SCRATCH_BYTES (64ull << 20)
 
@@ -308,6 +324,24 @@ int dropkv_prefill_attention(const void* q_all, const void* k, const void* v, in
 int dropkv_compact(int32_t dtype, const void* k, const void* v, int64_t n, int32_t Hkv, int32_t d,
                    const int64_t* evict_idx, int64_t n_evict, void* out_k, void* out_v,
                    int32_t* d_status, void* stream);
+
+/*
+ * Cache compaction from a kept list (as dropkv_score_keep_ex writes it):
+ * output row r of head g in out_k, out_v [Hkv][n_keep][d] is row
+ * keep_idx[g][r] of k, v [Hkv][n][d]; keep_idx [Hkv][n_keep] int64 must be
+ * strictly increasing inside [0, n) per head. Same result as dropkv_compact
+ * with the complementary eviction list, without searching that list.
+ * Limits: 1 <= n < 2^31, Hkv >= 1, 1 <= d <= 4096, 0 <= n_keep <= n; device
+ * pointers (keep_idx, out_k, out_v may be NULL when n_keep == 0); outputs must
+ * not overlap the inputs. Asynchronous on `stream`; ORs
+ * DROPKV_STATUS_BAD_INDEX into `d_status` (cleared by the caller) for a list
+ * that breaks the order or range (outputs then unspecified, no write outside
+ * out_k / out_v). Returns DROPKV_OK once enqueued, DROPKV_ERR_INVALID
+ * (nothing launched) or DROPKV_ERR_DEVICE.
+ */
+int dropkv_compact_kept(int32_t dtype, const void* k, const void* v, int64_t n, int32_t Hkv, int32_t d,
+                        const int64_t* keep_idx, int64_t n_keep, void* out_k, void* out_v,
+                        int32_t* d_status, void* stream);
 
 /*
  * Decode-time rescoring with a sliding observation window.

@@ -10,7 +10,7 @@ from .binding import (  # noqa: F401
     BF16, F32, FLAG_GENERIC, FLAG_STAGE_LOG, STATUS_BAD_INDEX, STATUS_NONFINITE, STATUS_SINGULAR,
     STATUS_NEGATIVE, DecodeScorer, DropKVError, DropKVNegativeScoreError,
     DropKVInvalidError, DropKVNonFiniteError, DropKVNotBuiltError, DropKVSingularError, LIB_PATH,
-    compact, load_library, pass1_stats, prefill_attention, raw_scores, row_stats, score, score_ex, score_from_stats, select,
+    compact, compact_kept, load_library, pass1_stats, prefill_attention, raw_scores, row_stats, score, score_ex, score_keep_ex, score_from_stats, select,
     stage_log, stage_times,
     uses_mfma,
     version,
@@ -18,7 +18,7 @@ from .binding import (  # noqa: F401
 )
 
 __all__ = [
-    "score", "score_ex", "score_from_stats", "raw_scores", "row_stats", "pass1_stats", "select", "compact",
+    "score", "score_ex", "score_keep_ex", "score_from_stats", "raw_scores", "row_stats", "pass1_stats", "select", "compact", "compact_kept",
     "DecodeScorer", "DropKVNegativeScoreError", "STATUS_NEGATIVE", "prefill_attention",
     "stage_times", "stage_log",
     "workspace_bytes",

@@ -32,6 +32,8 @@ SIGNATURES = {
     "dropkv_workspace_bytes": (_sz, [_i32, _i64, _i32, _i32, _i32, _i32]),
     "dropkv_score_ex": (_i32, [_i32, _p, _p, _p, _i64, _i32, _i32, _i32, _i32, _i32, _i64, _p, _p,
                                _p, _sz, _p, _u32, _p]),
+    "dropkv_score_keep_ex": (_i32, [_i32, _p, _p, _p, _i64, _i32, _i32, _i32, _i32, _i32, _i64, _p, _p,
+                                    _p, _p, _sz, _p, _u32, _p]),
     "dropkv_score_noalloc": (_i32, [_i32, _p, _p, _p, _i64, _i32, _i32, _i32, _i32, _i32, _i64, _p, _p,
                                     _p, _u32, _p]),
     "dropkv_raw_scores": (_i32, [_i32, _p, _p, _p, _i64, _i32, _i32, _i32, _i32, _p, _u32, _p]),
@@ -49,6 +51,7 @@ SIGNATURES = {
     "dropkv_prefill_attention": (_i32, [_p, _p, _p, _i64, _i32, _i32, _i32, _i32, _p, _p, _p, _p, _p, _p,
                                         _p]),
     "dropkv_compact": (_i32, [_i32, _p, _p, _i64, _i32, _i32, _p, _i64, _p, _p, _p, _p]),
+    "dropkv_compact_kept": (_i32, [_i32, _p, _p, _i64, _i32, _i32, _p, _i64, _p, _p, _p, _p]),
     "dropkv_decode_state_bytes": (_sz, [_i64, _i32, _i32, _i32, _i32]),
     "dropkv_decode_init": (_i32, [_p, _p, _p, _i64, _i64, _i32, _i32, _i32, _i32, _p, _sz, _p, _p]),
     "dropkv_decode_step": (_i32, [_p, _p, _p, _i64, _i64, _i32, _i32, _i32, _i32, _p, _sz, _p, _p]),
@@ -199,6 +202,30 @@ def score_ex(q, k, v, *, pool_kernel: int, n_evict: int, workspace, status, scor
                              flags, _stream_handle(stream))
     _raise(rc)
     return scores, evict_idx
+
+
+def score_keep_ex(q, k, v, *, pool_kernel: int, n_evict: int, workspace, status, scores=None,
+                  evict_idx=None, keep_idx=None, flags: int = 0, stream=None):
+    """score_ex that also returns the kept token indices [Hkv, n - n_evict] (int64,
+    ascending per head: the complement of evict_idx). Returns (scores, evict_idx, keep_idx)."""
+    torch = _torch()
+    lib = load_library()
+    Hq, Hkv, d, n, w = _shapes(q, k, v)
+    if scores is None:
+        scores = torch.empty((Hkv, n), dtype=torch.float32, device=q.device)
+    if evict_idx is None:
+        evict_idx = torch.empty((Hkv, max(n_evict, 0)), dtype=torch.int64, device=q.device)
+    n_keep = n - n_evict
+    if keep_idx is None:
+        keep_idx = torch.empty((Hkv, max(n_keep, 0)), dtype=torch.int64, device=q.device)
+    rc = lib.dropkv_score_keep_ex(_dtype_code(q), q.data_ptr(), k.data_ptr(), v.data_ptr(), n, w, Hq,
+                                  Hkv, d, pool_kernel, n_evict, scores.data_ptr(),
+                                  evict_idx.data_ptr() if n_evict > 0 else None,
+                                  keep_idx.data_ptr() if n_keep > 0 else None, workspace.data_ptr(),
+                                  workspace.numel() * workspace.element_size(), status.data_ptr(),
+                                  flags, _stream_handle(stream))
+    _raise(rc)
+    return scores, evict_idx, keep_idx
 
 
 NOALLOC_SCRATCH_BYTES = 64 << 20
@@ -378,6 +405,43 @@ def compact(k, v, evict_idx, *, status=None, out_k=None, out_v=None, stream=None
     _raise(rc)
     if sync and int(status.item()) & STATUS_BAD_INDEX:
         raise DropKVInvalidError(ERR_INVALID, "evict_idx is not strictly increasing inside [0, n)")
+    return out_k, out_v
+
+
+def compact_kept(k, v, keep_idx, *, status=None, out_k=None, out_v=None, stream=None):
+    """Cache compaction from a kept list: out_k, out_v [Hkv, n_keep, d] = the rows
+    keep_idx [Hkv, n_keep] (int64, strictly increasing per head) of k, v [Hkv, n, d].
+
+    With `status` (a device int32 tensor, cleared by the caller) the call is
+    asynchronous and ORs STATUS_BAD_INDEX into it for an invalid list; without
+    it the call synchronises and raises DropKVInvalidError for one.
+    """
+    torch = _torch()
+    lib = load_library()
+    if k.dim() != 3 or tuple(v.shape) != tuple(k.shape) or k.dtype != v.dtype:
+        raise DropKVInvalidError(ERR_INVALID, "k and v must both be [Hkv, n, d] of one dtype")
+    for t in (k, v, keep_idx):
+        if not t.is_cuda or not t.is_contiguous():
+            raise DropKVInvalidError(ERR_INVALID, "k, v and keep_idx must be contiguous GPU tensors")
+    Hkv, n, d = k.shape
+    if keep_idx.dtype != torch.int64 or keep_idx.dim() != 2 or keep_idx.shape[0] != Hkv:
+        raise DropKVInvalidError(ERR_INVALID, "keep_idx must be int64 [Hkv, n_keep]")
+    n_keep = keep_idx.shape[1]
+    if out_k is None:
+        out_k = torch.empty((Hkv, n_keep, d), dtype=k.dtype, device=k.device)
+    if out_v is None:
+        out_v = torch.empty((Hkv, n_keep, d), dtype=k.dtype, device=k.device)
+    sync = status is None
+    if sync:
+        status = torch.zeros(1, dtype=torch.int32, device=k.device)
+    rc = lib.dropkv_compact_kept(_dtype_code(k), k.data_ptr(), v.data_ptr(), n, Hkv, d,
+                                 keep_idx.data_ptr() if n_keep > 0 else None, n_keep,
+                                 out_k.data_ptr() if n_keep > 0 else None,
+                                 out_v.data_ptr() if n_keep > 0 else None, status.data_ptr(),
+                                 _stream_handle(stream))
+    _raise(rc)
+    if sync and int(status.item()) & STATUS_BAD_INDEX:
+        raise DropKVInvalidError(ERR_INVALID, "keep_idx is not strictly increasing inside [0, n)")
     return out_k, out_v
 
 

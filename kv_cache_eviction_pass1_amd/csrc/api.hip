@@ -391,6 +391,39 @@ int dropkv_score_ex(int32_t dtype, const void* q, const void* k, const void* v, 
   return DROPKV_OK;
 }
 
+int dropkv_score_keep_ex(int32_t dtype, const void* q, const void* k, const void* v, int64_t n,
+                         int32_t window, int32_t Hq, int32_t Hkv, int32_t d, int32_t pool_kernel,
+                         int64_t n_evict, float* out_scores, int64_t* out_evict_idx, int64_t* out_keep_idx,
+                         void* workspace, size_t workspace_bytes, int32_t* d_status, uint32_t flags,
+                         void* stream) {
+  g_last_error.clear();
+  if (n_evict < n && (!out_keep_idx || !is_device_ptr(out_keep_idx)))
+    return fail(DROPKV_ERR_INVALID, "out_keep_idx must be a device pointer when tokens are kept");
+  if (const char* m = validate(dtype, n, window, Hq, Hkv, d)) return fail(DROPKV_ERR_INVALID, m);
+  if (const char* m = validate_select(n, window, Hkv, pool_kernel, n_evict))
+    return fail(DROPKV_ERR_INVALID, m);
+  if (int rc = check_inputs(q, k, v)) return rc;
+  if (!out_scores || !is_device_ptr(out_scores)) return fail(DROPKV_ERR_INVALID, "out_scores must be a device pointer");
+  if (n_evict > 0 && (!out_evict_idx || !is_device_ptr(out_evict_idx)))
+    return fail(DROPKV_ERR_INVALID, "out_evict_idx must be a device pointer when n_evict > 0");
+  if (!workspace || ((uintptr_t)workspace & 255) || !is_device_ptr(workspace))
+    return fail(DROPKV_ERR_INVALID, "workspace must be a 256-byte aligned device pointer");
+  if (!d_status || !is_device_ptr(d_status)) return fail(DROPKV_ERR_INVALID, "d_status must be a device pointer");
+  const Shape s{n, window, Hq, Hkv, d};
+  const bool mfma = use_mfma(dtype, d, flags);
+  Workspace ws = carve_workspace(workspace, s, mfma);
+  if (ws.bytes > workspace_bytes) return fail(DROPKV_ERR_INVALID, "workspace too small");
+  ws.status = d_status;
+  hipStream_t st = (hipStream_t)stream;
+  StageEvents* se = (flags & DROPKV_FLAG_STAGE_LOG) ? log_slot() : nullptr;
+  FoldInfo fold{};
+  if (int rc = run_scores(dtype, q, k, v, s, ws, mfma, st, se, &fold)) return rc;
+  hipError_t e = launch_select(ws.S, n, window, Hkv, pool_kernel, n_evict, out_scores, out_evict_idx,
+                               ws.status, &fold, ws.sel, st, false, se, out_keep_idx);
+  if (e != hipSuccess) return fail_hip(e, "select");
+  return DROPKV_OK;
+}
+
 int dropkv_score_noalloc(int32_t dtype, const void* q, const void* k, const void* v, int64_t n,
                          int32_t window, int32_t Hq, int32_t Hkv, int32_t d, int32_t pool_kernel,
                          int64_t n_evict, float* out_scores, int64_t* out_evict_idx, int32_t* d_status,
@@ -675,6 +708,26 @@ int dropkv_compact(int32_t dtype, const void* k, const void* v, int64_t n, int32
   hipError_t e = launch_compact(dtype, k, v, n, Hkv, d, evict_idx, n_evict, out_k, out_v, d_status,
                                 (hipStream_t)stream);
   if (e != hipSuccess) return fail_hip(e, "compact");
+  return DROPKV_OK;
+}
+
+int dropkv_compact_kept(int32_t dtype, const void* k, const void* v, int64_t n, int32_t Hkv, int32_t d,
+                        const int64_t* keep_idx, int64_t n_keep, void* out_k, void* out_v,
+                        int32_t* d_status, void* stream) {
+  g_last_error.clear();
+  if (dtype != DROPKV_BF16 && dtype != DROPKV_F32) return fail(DROPKV_ERR_INVALID, "dtype must be DROPKV_BF16 or DROPKV_F32");
+  if (n < 1 || n > ((int64_t)1 << 31) - 1) return fail(DROPKV_ERR_INVALID, "need 1 <= n < 2^31");
+  if (Hkv < 1 || d < 1 || d > 4096) return fail(DROPKV_ERR_INVALID, "need Hkv >= 1 and 1 <= d <= 4096");
+  if (n_keep < 0 || n_keep > n) return fail(DROPKV_ERR_INVALID, "need 0 <= n_keep <= n");
+  if (!k || !v || !is_device_ptr(k) || !is_device_ptr(v)) return fail(DROPKV_ERR_INVALID, "k and v must be device pointers");
+  if (n_keep > 0 && (!keep_idx || !is_device_ptr(keep_idx)))
+    return fail(DROPKV_ERR_INVALID, "keep_idx must be a device pointer when n_keep > 0");
+  if (n_keep > 0 && (!out_k || !out_v || !is_device_ptr(out_k) || !is_device_ptr(out_v)))
+    return fail(DROPKV_ERR_INVALID, "out_k and out_v must be device pointers when n_keep > 0");
+  if (!d_status || !is_device_ptr(d_status)) return fail(DROPKV_ERR_INVALID, "d_status must be a device pointer");
+  hipError_t e = launch_compact_kept(dtype, k, v, n, Hkv, d, keep_idx, n_keep, out_k, out_v, d_status,
+                                     (hipStream_t)stream);
+  if (e != hipSuccess) return fail_hip(e, "compact_kept");
   return DROPKV_OK;
 }
 

@@ -22,7 +22,10 @@
 //     block's span) is searched in global memory instead.
 // The copy then runs over (row, 16-byte unit) pairs, consecutive threads on
 // consecutive units, K's and V's unit loaded together so that both streams
-// are in flight, and stored with non-temporal stores. Every workgroup also checks an equal share of the list
+// are in flight, and stored with non-temporal stores. (A kept list, which
+// the select stage can emit, makes the source rows plain list entries:
+// k_compact_kept needs one round of list reads before the copy.) Every
+// workgroup also checks an equal share of the list
 // (strictly increasing, inside [0, n)); a bad list sets the status bit, and no
 // read or write leaves the list or the output arrays whatever the list holds.
 #include "dropkv_common.h"
@@ -63,6 +66,51 @@ __device__ __forceinline__ int64_t fval(const int64_t* e, int64_t i, int64_t n) 
   int64_t x = e[i];
   x = x < 0 ? 0 : (x >= n ? n - 1 : x);
   return x - i;
+}
+
+// Copies the block's output rows [r0, r1) of head g from the token rows
+// src[0 .. r1 - r0) (in LDS) of K and V.
+template <typename U>
+__device__ __forceinline__ void copy_rows(const CompactArgs& A, const int32_t* src, int g, int64_t r0,
+                                          int64_t r1) {
+  // (row, unit) pairs of this block: at most kR * 4096 * 4 / 2 units
+  const uint32_t upr = (uint32_t)A.upr;
+  const uint32_t units = (uint32_t)(r1 > r0 ? r1 - r0 : 0) * upr;
+  const char* ks = A.k + (size_t)g * A.n * A.row_bytes;
+  const char* vs = A.v + (size_t)g * A.n * A.row_bytes;
+  char* kd = A.ok + ((size_t)g * A.n_keep + r0) * A.row_bytes;
+  char* vd = A.ov + ((size_t)g * A.n_keep + r0) * A.row_bytes;
+  // unit i = r * upr + c; each thread walks i = threadIdx.x + m * kT, stepping
+  // (r, c) by (kT / upr, kT % upr) with a carry instead of dividing
+  const uint32_t dr = (uint32_t)kT / upr, dc = (uint32_t)kT % upr;
+  uint32_t r = threadIdx.x / upr, c = threadIdx.x % upr;
+  for (uint32_t i0 = threadIdx.x; i0 < units; i0 += (uint32_t)kT * kBatch) {
+    U bk[kBatch], bv[kBatch];
+    int64_t dst[kBatch];
+#pragma unroll
+    for (int u = 0; u < kBatch; ++u) {
+      dst[u] = -1;
+      if (i0 + (uint32_t)u * kT < units) {
+        const int64_t so = (int64_t)src[r] * A.row_bytes + (int64_t)c * (int64_t)sizeof(U);
+        bk[u] = *(const U*)(ks + so);
+        bv[u] = *(const U*)(vs + so);
+        dst[u] = (int64_t)r * A.row_bytes + (int64_t)c * (int64_t)sizeof(U);
+      }
+      r += dr;
+      c += dc;
+      if (c >= upr) {
+        c -= upr;
+        ++r;
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < kBatch; ++u)
+      if (dst[u] >= 0) {
+        // written once, read by a later call: no need to keep them in the L2
+        __builtin_nontemporal_store(bk[u], (U*)(kd + dst[u]));
+        __builtin_nontemporal_store(bv[u], (U*)(vd + dst[u]));
+      }
+  }
 }
 
 template <typename U>
@@ -151,47 +199,37 @@ __global__ __launch_bounds__(kT) void k_compact(CompactArgs A) {
     src[threadIdx.x] = (int32_t)t;
   }
   __syncthreads();
-  // (row, unit) pairs of this block: at most kR * 4096 * 4 / 2 units
-  const uint32_t upr = (uint32_t)A.upr;
-  const uint32_t units = (uint32_t)(r1 > r0 ? r1 - r0 : 0) * upr;
-  const char* ks = A.k + (size_t)g * A.n * A.row_bytes;
-  const char* vs = A.v + (size_t)g * A.n * A.row_bytes;
-  char* kd = A.ok + ((size_t)g * A.n_keep + r0) * A.row_bytes;
-  char* vd = A.ov + ((size_t)g * A.n_keep + r0) * A.row_bytes;
-  // unit i = r * upr + c; each thread walks i = threadIdx.x + m * kT, stepping
-  // (r, c) by (kT / upr, kT % upr) with a carry instead of dividing
-  const uint32_t dr = (uint32_t)kT / upr, dc = (uint32_t)kT % upr;
-  uint32_t r = threadIdx.x / upr, c = threadIdx.x % upr;
-  for (uint32_t i0 = threadIdx.x; i0 < units; i0 += (uint32_t)kT * kBatch) {
-    U bk[kBatch], bv[kBatch];
-    int64_t dst[kBatch];
-#pragma unroll
-    for (int u = 0; u < kBatch; ++u) {
-      dst[u] = -1;
-      if (i0 + (uint32_t)u * kT < units) {
-        const int64_t so = (int64_t)src[r] * A.row_bytes + (int64_t)c * (int64_t)sizeof(U);
-        bk[u] = *(const U*)(ks + so);
-        bv[u] = *(const U*)(vs + so);
-        dst[u] = (int64_t)r * A.row_bytes + (int64_t)c * (int64_t)sizeof(U);
-      }
-      r += dr;
-      c += dc;
-      if (c >= upr) {
-        c -= upr;
-        ++r;
-      }
-    }
-#pragma unroll
-    for (int u = 0; u < kBatch; ++u)
-      if (dst[u] >= 0) {
-        // written once, read by a later call: no need to keep them in the L2
-        __builtin_nontemporal_store(bk[u], (U*)(kd + dst[u]));
-        __builtin_nontemporal_store(bv[u], (U*)(vd + dst[u]));
-      }
-  }
+  copy_rows<U>(A, src, g, r0, r1);
   if (threadIdx.x == 0 && bad) atomicOr(A.status, kStatusBadIndex);
 }
 
+
+// From a kept list: output row r0 + i of head g is token keep[g][r0 + i].
+// Each thread checks its entry against the one before it (strictly
+// increasing inside [0, n)); a bad entry sets the status bit and is clamped,
+// so no read leaves the K/V arrays whatever the list holds.
+template <typename U>
+__global__ __launch_bounds__(kT) void k_compact_kept(CompactArgs A) {
+  const int b = blockIdx.x, g = blockIdx.y;
+  const int64_t r0 = (int64_t)b * kR;
+  const int64_t r1 = (r0 + kR < A.n_keep) ? r0 + kR : A.n_keep;
+  const int64_t* kl = A.e + (size_t)g * A.n_keep;
+  __shared__ int32_t src[kR];
+  __shared__ int bad;
+  if (threadIdx.x == 0) bad = 0;
+  __syncthreads();
+  if ((int64_t)threadIdx.x < r1 - r0) {
+    const int64_t r = r0 + threadIdx.x;
+    int64_t t = kl[r];
+    const int64_t prev = r > 0 ? kl[r - 1] : -1;
+    if (t < 0 || t >= A.n || t <= prev) bad = 1;
+    t = t < 0 ? 0 : (t >= A.n ? A.n - 1 : t);
+    src[threadIdx.x] = (int32_t)t;
+  }
+  __syncthreads();
+  copy_rows<U>(A, src, g, r0, r1);
+  if (threadIdx.x == 0 && bad) atomicOr(A.status, kStatusBadIndex);
+}
 }  // namespace
 
 hipError_t launch_compact(int dtype, const void* k, const void* v, int64_t n, int32_t Hkv, int32_t d,
@@ -225,6 +263,44 @@ hipError_t launch_compact(int dtype, const void* k, const void* v, int64_t n, in
   } else {
     A.upr = (int32_t)(A.row_bytes / 2);
     k_compact<uint16_t><<<grid, kT, 0, st>>>(A);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace dropkv
+
+namespace dropkv {
+
+hipError_t launch_compact_kept(int dtype, const void* k, const void* v, int64_t n, int32_t Hkv, int32_t d,
+                               const int64_t* keep_idx, int64_t n_keep, void* out_k, void* out_v,
+                               int32_t* status, hipStream_t st) {
+  if (n_keep <= 0) return hipSuccess;
+  CompactArgs A{};
+  A.k = (const char*)k;
+  A.v = (const char*)v;
+  A.ok = (char*)out_k;
+  A.ov = (char*)out_v;
+  A.e = keep_idx;
+  A.n = n;
+  A.n_evict = n - n_keep;
+  A.n_keep = n_keep;
+  A.row_bytes = (int64_t)d * (dtype == 0 ? 2 : 4);
+  A.nblk = (int32_t)((n_keep + kR - 1) / kR);
+  A.status = status;
+  auto aligned = [&](size_t a) {
+    return A.row_bytes % (int64_t)a == 0 && (uintptr_t)k % a == 0 && (uintptr_t)v % a == 0 &&
+           (uintptr_t)out_k % a == 0 && (uintptr_t)out_v % a == 0;
+  };
+  const dim3 grid(A.nblk, Hkv);
+  if (aligned(16)) {
+    A.upr = (int32_t)(A.row_bytes / 16);
+    k_compact_kept<u32x4><<<grid, kT, 0, st>>>(A);
+  } else if (aligned(4)) {
+    A.upr = (int32_t)(A.row_bytes / 4);
+    k_compact_kept<uint32_t><<<grid, kT, 0, st>>>(A);
+  } else {
+    A.upr = (int32_t)(A.row_bytes / 2);
+    k_compact_kept<uint16_t><<<grid, kT, 0, st>>>(A);
   }
   return hipGetLastError();
 }

@@ -88,6 +88,12 @@ Workspace carve_workspace(void* ws_base, const Shape& s, bool mfma);
 hipError_t launch_compact(int dtype, const void* k, const void* v, int64_t n, int32_t Hkv, int32_t d,
                           const int64_t* evict_idx, int64_t n_evict, void* out_k, void* out_v,
                           int32_t* status, hipStream_t st);
+// The same from the kept list keep_idx [Hkv][n_keep] (ascending per head):
+// output row r of head g is row keep_idx[g][r]; kStatusBadIndex for a list
+// that is not strictly increasing inside [0, n).
+hipError_t launch_compact_kept(int dtype, const void* k, const void* v, int64_t n, int32_t Hkv, int32_t d,
+                               const int64_t* keep_idx, int64_t n_keep, void* out_k, void* out_v,
+                               int32_t* status, hipStream_t st);
 // Zeroes the status word, flagcount[Hkv] (may be null) and the select scratch.
 hipError_t launch_init(int32_t* status, int32_t* flagcount, void* sel_scratch, int32_t Hkv,
                        hipStream_t st);
@@ -114,7 +120,7 @@ struct StageEvents;
 hipError_t launch_select(const float* S, int64_t n, int32_t w, int32_t Hkv, int32_t pool_kernel,
                          int64_t n_evict, float* out_scores, int64_t* out_idx, int32_t* status,
                          const FoldInfo* fold, void* scratch, hipStream_t st, bool reject_negative = false,
-                         StageEvents* se = nullptr);
+                         StageEvents* se = nullptr, int64_t* keep_idx = nullptr);
 size_t select_scratch_bytes(int64_t n, int32_t Hkv);
 // 32-bit words at the start of the select scratch that must be zero before a call.
 size_t select_zero_words(int32_t Hkv);

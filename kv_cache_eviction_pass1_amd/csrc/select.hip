@@ -66,6 +66,7 @@ struct SelArgs {
   int32_t* status;
   FoldInfo fold;      // argmax terms of flagged rows to add to S (flagcount null: none)
   bool reject_negative;  // caller-given S: a negative entry raises kStatusNegative
+  int64_t* keep;      // [Hkv][n - n_evict]: the kept token indices, ascending (null: not written)
 };
 
 __device__ __forceinline__ uint32_t score_key(float x) {
@@ -510,12 +511,20 @@ __global__ __launch_bounds__(kT) void k_sel_write(SelArgs A) {
     if (s >= A.nseg) return;
     uint32_t eqb = tot_eq + epre;
     uint32_t pos = tot_lt + lpre + (eqb < need32 ? eqb : need32);
+    int64_t* kg = A.keep ? A.keep + (size_t)g * (size_t)(A.n - A.n_evict) : nullptr;
+    const uint32_t n_keep32 = (uint32_t)(A.n - A.n_evict);
     auto emit_keys = [&](const uint32_t (&key)[kKeys], uint32_t q0) {
 #pragma unroll
       for (int k = 0; k < kKeys; ++k) {
         const bool eq = key[k] == tau;
         const bool take = key[k] < tau || (eq && eqb < need32);
         eqb += eq ? 1u : 0u;
+        if (kg && !take && key[k] != 0xffffffffu) {
+          // a kept token j lands at j - #{evicted tokens below j} = j - pos
+          const uint32_t kp = q0 + k - pos;
+          DKV_CHECK(kp < n_keep32, A.status);
+          if (kp < n_keep32) kg[kp] = (int64_t)(q0 + k);
+        }
         if constexpr (decltype(to_lds)::value) {
           // no branch: a key not taken is written to this thread's spare slot
           const uint32_t r = pos - base32;  // wraps above cnt32 if ever below base
@@ -568,6 +577,12 @@ __global__ void k_init(int32_t* status, int32_t* flagcount, uint32_t* hist) {
     if (flagcount) flagcount[g] = 0;
     if (g == 0) *status = 0;
   }
+}
+
+// Every token kept (n_evict = 0): the kept list is 0 .. n - 1 for each head.
+__global__ void k_keep_all(int64_t* keep, int64_t n, int32_t Hkv) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n * Hkv) keep[i] = i % n;
 }
 
 struct SelGeom {
@@ -632,7 +647,7 @@ hipError_t launch_init(int32_t* status, int32_t* flagcount, void* sel_scratch, i
 hipError_t launch_select(const float* S, int64_t n, int32_t w, int32_t Hkv, int32_t pool_kernel,
                          int64_t n_evict, float* out_scores, int64_t* out_idx, int32_t* status,
                          const FoldInfo* fold, void* scratch, hipStream_t st, bool reject_negative,
-                         StageEvents* se) {
+                         StageEvents* se, int64_t* keep_idx) {
   const SelGeom q = sel_geom(n);
   if (fold && fold->flagcount && pool_kernel / 2 > kMaxHalo) {
     // the pool kernel reads S from global memory for such wide kernels: fold first
@@ -659,9 +674,15 @@ hipError_t launch_select(const float* S, int64_t n, int32_t w, int32_t Hkv, int3
   A.wg_lt = p.wg_lt;
   A.status = status;
   A.reject_negative = reject_negative;
+  A.keep = keep_idx;
   if (fold) A.fold = *fold;
   hipError_t e = stage_launch(se, "select", n_evict > 0 ? kStageFirst : kStageOnly, k_sel_pool,
                               dim3(A.nblk, Hkv), dim3(kT), st, A);
+  if (e == hipSuccess && n_evict <= 0 && keep_idx) {
+    const int64_t total = n * Hkv;
+    k_keep_all<<<(unsigned)((total + 255) / 256), 256, 0, st>>>(keep_idx, n, Hkv);
+    e = hipGetLastError();
+  }
   if (e != hipSuccess || n_evict <= 0) return e;
   const dim3 gs((q.nseg + kT - 1) / kT, Hkv);
   e = stage_launch(se, "select", kStageMid, k_sel_cand, gs, dim3(kT), st, A);

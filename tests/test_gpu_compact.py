@@ -7,7 +7,10 @@ out, in runs, all at the front, all at the back, at both ends around one long
 evicted run: the case whose block span holds more list entries than the
 kernel stages in LDS), invalid lists (status bit, and no write outside the
 outputs: guard rows around them stay untouched), and the score -> compact
-pipeline on a full-size layer.
+pipeline on a full-size layer. The kept-list form (dropkv_compact_kept, fed
+by the kept list dropkv_score_keep_ex writes) is checked the same way: against
+the oracle's compaction of the complementary eviction list, on invalid lists,
+and score -> compact on the 32K layer.
 """
 
 import numpy as np
@@ -183,3 +186,104 @@ def test_score_then_compact_full_layer():
     assert np.array_equal(_bits(ok), rk.view(np.int16)) and np.array_equal(_bits(ov), rv.view(np.int16))
     # the protected window is always kept, at the end of every head
     assert np.array_equal(_bits(ok)[:, -case.window:], case.k[:, -case.window:].view(np.int16))
+
+
+def _keep_lists(ev, n):
+    """Per head the token indices an eviction list does not name, ascending."""
+    return np.stack([np.setdiff1d(np.arange(n), e) for e in ev]).astype(np.int64) if len(ev) else \
+        np.zeros((0, n), np.int64)
+
+
+def _run_kept(k, v, keep):
+    Hkv, n, d = k.shape
+    n_keep = keep.shape[1]
+    bufs, (ok, ov) = _guarded_outputs(Hkv, n_keep, d, k.dtype, k.device)
+    st = torch.zeros(1, dtype=torch.int32, device=k.device)
+    K.compact_kept(k, v, torch.from_numpy(np.ascontiguousarray(keep)).to(k.device), status=st, out_k=ok, out_v=ov)
+    torch.cuda.synchronize()
+    return ok, ov, int(st.item()), bufs
+
+
+@pytest.mark.parametrize("dtype,d", [("bf16", 128), ("bf16", 7), ("f32", 3)])
+@pytest.mark.parametrize("n", [1, 1025, 4097, 9000])
+def test_compact_kept_matches_oracle(dtype, d, n):
+    """dropkv_compact_kept on the complement of each eviction list gives the
+    oracle's compaction of that list, bit for bit."""
+    rng = np.random.default_rng(n * 7 + d)
+    Hkv = 3
+    tdt = torch.bfloat16 if dtype == "bf16" else torch.float32
+    k = torch.randn(Hkv, n, d).to(tdt).cuda()
+    v = torch.randn(Hkv, n, d).to(tdt).cuda()
+    for ne, kind in ((0, "random"), (n, "random"), (n // 2, "random"), (n - n // 7, "runs"),
+                     (n - n // 7, "front"), (n // 2, "back"), (n - n // 7, "ends")):
+        ev = _evict_lists(rng, Hkv, n, ne, kind)
+        keep = _keep_lists(ev, n)
+        print(f"[compact_kept] {dtype} d={d} n={n} keep={n - ne} {kind}", flush=True)
+        ok, ov, st, bufs = _run_kept(k, v, keep)
+        assert st == 0
+        rk, rv = oracle.compact_cache(_bits(k), _bits(v), ev)
+        assert np.array_equal(_bits(ok), rk) and np.array_equal(_bits(ov), rv)
+        _check_guards(bufs, Hkv, n - ne, d)
+
+
+@pytest.mark.parametrize("bad", ["unsorted", "duplicate", "too_large", "negative"])
+def test_compact_kept_bad_lists_flagged_and_contained(bad):
+    Hkv, n, d = 2, 3000, 16
+    k = torch.randn(Hkv, n, d).cuda()
+    v = torch.randn(Hkv, n, d).cuda()
+    keep = _keep_lists(_evict_lists(np.random.default_rng(4), Hkv, n, 1000, "random"), n)
+    if bad == "unsorted":
+        keep[1, 10], keep[1, 500] = keep[1, 500], keep[1, 10]
+    elif bad == "duplicate":
+        keep[0, 700] = keep[0, 699]
+    elif bad == "too_large":
+        keep[1, -1] = n + 5
+    else:
+        keep[0, 0] = -3
+    print(f"[compact_kept] bad list: {bad}", flush=True)
+    ok, ov, st, bufs = _run_kept(k, v, keep)
+    assert st & K.STATUS_BAD_INDEX
+    _check_guards(bufs, Hkv, keep.shape[1], d)
+    with pytest.raises(K.DropKVInvalidError):
+        K.compact_kept(k, v, torch.from_numpy(keep).cuda())
+
+
+@pytest.mark.parametrize("n,w,Hq,Hkv,ne", [(3000, 16, 8, 2, 1500), (3000, 16, 8, 2, 0), (3000, 16, 8, 2, 2984),
+                                          (65, 1, 4, 2, 30), (4161, 17, 6, 2, 4000)])
+def test_score_keep_list_is_the_complement(n, w, Hq, Hkv, ne):
+    """dropkv_score_keep_ex: the same scores and evicted sets as dropkv_score_ex,
+    and per head a kept list that is exactly the complement, ascending."""
+    case = synth.make_gaussian_case(Hq, Hkv, 128, n, w, dtype="bf16", seeds=(n, w, ne), sink=True, needles=8)
+    to_t = lambda a: torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).cuda()
+    q, k, v = to_t(case.q), to_t(case.k), to_t(case.v)
+    ws = torch.empty(K.workspace_bytes(K.BF16, n, w, Hq, Hkv, 128), dtype=torch.uint8, device="cuda")
+    st = torch.zeros(1, dtype=torch.int32, device="cuda")
+    print(f"[score_keep] n={n} w={w} Hq={Hq} Hkv={Hkv} evict={ne}", flush=True)
+    s0, i0 = K.score_ex(q, k, v, pool_kernel=7, n_evict=ne, workspace=ws, status=st)
+    s1, i1, kp = K.score_keep_ex(q, k, v, pool_kernel=7, n_evict=ne, workspace=ws, status=st)
+    torch.cuda.synchronize()
+    assert int(st.item()) == 0
+    assert torch.equal(s0, s1) and torch.equal(i0, i1)
+    assert kp.shape == (Hkv, n - ne)
+    assert np.array_equal(kp.cpu().numpy(), _keep_lists(i1.cpu().numpy(), n))
+
+
+def test_score_keep_then_compact_kept_full_layer():
+    """Score the 32K Llama layer with its kept list, then compact from it: the
+    same cache as compaction from the eviction list."""
+    cfg = synth.CONFIGS["llama_32k"]
+    case = synth.make_case(cfg)
+    to_t = lambda a: torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).cuda()
+    q, k, v = to_t(case.q), to_t(case.k), to_t(case.v)
+    ne = cfg.n_evicts()[0]
+    ws = torch.empty(K.workspace_bytes(K.BF16, case.n, case.window, case.Hq, case.Hkv, case.d),
+                     dtype=torch.uint8, device="cuda")
+    st = torch.zeros(1, dtype=torch.int32, device="cuda")
+    print(f"[compact_kept] score -> compact_kept llama_32k evict={ne}", flush=True)
+    _, idx, keep = K.score_keep_ex(q, k, v, pool_kernel=cfg.pool_kernel, n_evict=ne, workspace=ws, status=st)
+    ok1, ov1 = K.compact_kept(k, v, keep)
+    ok0, ov0 = K.compact(k, v, idx)
+    torch.cuda.synchronize()
+    assert int(st.item()) == 0
+    assert torch.equal(ok0, ok1) and torch.equal(ov0, ov1)
+    assert np.array_equal(keep.cpu().numpy(), _keep_lists(idx.cpu().numpy(), case.n))
