@@ -94,3 +94,17 @@ def test_package_import_does_not_require_gpu():
     # importing and loading the library work without a GPU; compute calls would raise
     assert callable(K.score) and callable(K.score_ex)
     assert ctypes.sizeof(ctypes.c_void_p) == 8
+
+
+def test_kept_list_entry_points_reject_bad_arguments_on_the_host(lib):
+    # scoring with the kept list: a missing kept-list output while tokens are kept
+    rc = lib.dropkv_score_keep_ex(0, None, None, None, 22, 3, 4, 2, 8, 3, 7, None, None, None, None, 0, None, 0,
+                                  None)
+    assert rc == binding.ERR_INVALID
+    assert b"out_keep_idx" in lib.dropkv_last_error()
+    # compaction from a kept list: bad dtype, more kept tokens than tokens, bad sizes
+    assert lib.dropkv_compact_kept(7, None, None, 100, 2, 8, None, 10, None, None, None, None) == binding.ERR_INVALID
+    assert lib.dropkv_compact_kept(0, None, None, 100, 2, 8, None, 101, None, None, None, None) == binding.ERR_INVALID
+    assert b"n_keep" in lib.dropkv_last_error()
+    assert lib.dropkv_compact_kept(0, None, None, 100, 0, 8, None, 10, None, None, None, None) == binding.ERR_INVALID
+    assert lib.dropkv_compact_kept(0, None, None, 0, 2, 8, None, 0, None, None, None, None) == binding.ERR_INVALID
