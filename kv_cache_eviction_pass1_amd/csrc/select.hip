@@ -35,7 +35,7 @@ namespace {
 // 512 threads: two waves per SIMD hide part of the latency of these short,
 // one-pass kernels (one workgroup per CU at the 128K shape)
 constexpr int kT = 512;            // threads per workgroup (pool, cand, write)
-constexpr int kChunk = 4096;       // pool: elements per workgroup
+constexpr int kChunk = 2048;       // pool: elements per workgroup (two workgroups per CU at the 128K layer: 1 us less than 4096)
 constexpr int kPer = kChunk / kT;  // pool: elements per thread
 constexpr int kKeys = 8;           // cand / write: keys per load group (segments are multiples of it)
 constexpr int kMaxHalo = 512;      // pooling halo held in LDS (larger kernels read global memory)
