@@ -1180,14 +1180,16 @@ __global__ __launch_bounds__(NW * 64) void k_pass2(P2Args P, FixArgs F) {
   // t's K/V and ||v||^2 and the claim issued one tile earlier have landed.
   //
   // The workgroup's tiles are its static share [gbase, static_end), then
-  // tiles claimed from the head's pool. The claim for a tile goes out at the
-  // top of the tile three places before it and reaches every wave through
-  // LDS at the top of the next tile, when that tile's loads are issued.
-  // Claims only grow, so a workgroup's tiles ascend; once a claim runs past
-  // the pool, its sequence ends. gp / g0 / g1: global tiles of local tiles
-  // t - 1, t, t + 1 (-1: none) before the top of tile t.
-  __shared__ int claim_slot[2];  // written at the top of tile t into slot t % 2: a wave still
-                                 // reading slot t % 2 blocks the next write there at barrier t + 1
+  // tiles claimed from the head's pool. The claim for local tile u goes out
+  // (wave 0, one lane) at the top of tile u - 3; its answer reaches every
+  // wave through LDS at the top of tile u - 2, where tile u's loads are
+  // issued. Claims only grow, so a workgroup's tiles ascend; once a claim
+  // runs past the pool, its sequence ends. gp / g0 / g1: global tiles of
+  // local tiles t - 1, t, t + 1 (-1: none) before the top of tile t.
+  // claim_slot[t % 2] is written before barrier t and read after it; the
+  // next write to that slot (top of t + 2) follows barrier t + 1, which every
+  // reader has reached.
+  __shared__ int claim_slot[2];
   const int static_end = gbase + (dyn ? P.stat_tiles : ntiles);
   uint32_t* const ctrp = dyn ? P.ctr + (size_t)g * P.ctr_stride + rg : nullptr;
   uint32_t pend = 0;  // wave 0, lane 0: the claim in flight
