@@ -153,7 +153,11 @@ def test_bitwise_repeatable():
                                       (300000, 64, 9, 250000),
                                       # either side of the largest head selected inside one
                                       # workgroup (32768 keys), and every evictable token evicted
-                                      (32768, 64, 7, 31130), (32769, 64, 7, 31131), (20000, 16, 3, 19984)])
+                                      (32768, 64, 7, 31130), (32769, 64, 7, 31131), (20000, 16, 3, 19984),
+                                      # either side of the heads selected by one workgroup in LDS
+                                      # (<= 4096 keys, pooling half-width <= 32)
+                                      (4096, 64, 7, 3000), (4096, 16, 65, 4000), (4096, 16, 67, 100),
+                                      (4095, 32, 1, 4063), (22, 3, 3, 7)])
 def test_select_matches_stable_argsort(n, w, k, ne):
     rng = np.random.default_rng(n + ne)
     S = rng.integers(0, 7, size=(3, n)).astype(np.float32) * np.float32(0.25)  # many exact ties
@@ -178,11 +182,12 @@ def test_select_all_keys_tied(n):
     assert np.array_equal(idx.cpu().numpy(), np.tile(np.arange(ne, dtype=np.int64), (2, 1)))
 
 
-@pytest.mark.parametrize("where", [0, 4095, 9000])
-def test_select_rejects_negative_scores(where):
+@pytest.mark.parametrize("n,where", [(9001, 0), (9001, 4095), (9001, 9000), (4000, 0), (4000, 3999)])
+def test_select_rejects_negative_scores(n, where):
     """Given raw scores must be >= 0 (sums of squared norms): a negative entry
-    anywhere is reported; -0.0 is accepted and orders as +0."""
-    n, w, k, ne = 9001, 16, 7, 500
+    anywhere is reported; -0.0 is accepted and orders as +0 (on the
+    three-kernel stage and on the one-workgroup stage of short heads)."""
+    w, k, ne = 16, 7, 500
     rng = np.random.default_rng(where)
     S = rng.random((2, n)).astype(np.float32)
     S[1, where] = -1e-30
@@ -192,6 +197,16 @@ def test_select_rejects_negative_scores(where):
     P_ref = oracle.protect_window(oracle.maxpool1d_same(np.abs(S.astype(np.float64)), k), w)
     scores, idx = K.select(torch.from_numpy(S).cuda(), window=w, pool_kernel=k, n_evict=ne)
     assert np.array_equal(idx.cpu().numpy(), oracle.evict_smallest(P_ref, ne))
+
+
+@pytest.mark.parametrize("n", [4000, 9000])
+def test_select_reports_nan_scores(n):
+    """A NaN among given raw scores is reported (pooling would otherwise hide
+    it), on both select stages."""
+    S = np.random.default_rng(n).random((2, n)).astype(np.float32)
+    S[1, n // 2] = np.nan
+    with pytest.raises(K.DropKVNonFiniteError):
+        K.select(torch.from_numpy(S).cuda(), window=16, pool_kernel=7, n_evict=100)
 
 
 def test_pass1_stats_name_matches_row_stats():
